@@ -1,0 +1,220 @@
+"""fp64 CPU oracle for the fused GEMM-epilogue and back-to-back GEMM path.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package. The GPU library
+(``b2bgemm_stage_stream_amd``) never imports it, and the two share no code: no
+kernels, headers, helpers or constants. The only common dependency is ``gen``,
+which draws the seeded inputs and holds none of this arithmetic.
+
+Source of the method: the pith.science review of arXiv 2608.03537, "ComFuse:
+Fusing Complex Memory-Intensive Subgraphs with Compute-Intensive Kernels For
+Modern GPU Architectures" (cited below as "ComFuse review"). The page names the
+operators (MatMul followed by elementwise ops, softmax, LayerNorm, RMSNorm;
+GEMM + elementwise/reduction + GEMM) but prints none of their formulas, so the
+oracle is the plain textbook definition of each, evaluated unfused in float64
+on the exact stored input values. Fusion and tiling change these results only
+by rounding order: per the ComFuse review ("Circularity Check"), Eq. (1) only
+bounds which tiles a reduction has to wait for, and Eqs. (3)-(5) cut the second
+contraction into segments whose sum is the whole product. So the plain
+definition is the oracle.
+
+Readings where the page is silent (each is listed with its reason in the design
+notes of this repository):
+  * epilogue order: alpha * P, + bias[n], + residual[m, n], activation, row
+    operation, affine, cast;
+  * LayerNorm uses the biased (1/N) variance and eps inside the square root;
+    RMSNorm is x / sqrt(mean(x^2) + eps) * w; softmax subtracts the row max;
+  * in the back-to-back GEMM the second contraction takes its left operand in
+    bf16: ``round_bf16(F(S))`` for elementwise F, and for the softmax
+    ``round_bf16(2**(t - c))`` with ``t = log2(e) * S`` and an integer
+    stabiliser ``c = ceil(max_row t)``, divided by the row sum of the unrounded
+    ``2**(t - c)``. The result does not depend on which integer c is used.
+    The unrounded result (``round_operand=False``) is available beside it.
+
+Parity pins (tests/test_oracle_pins.py) tie every function here to exact
+rational / 40-digit decimal brute force on tiny shapes, closed forms and
+invariants, not to this code.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "widen_bf16", "round_bf16", "matmul", "elementwise_stage", "relu",
+    "row_softmax", "layer_norm", "rms_norm", "gemm_epilogue",
+    "softmax_bf16_operand", "b2bgemm",
+]
+
+_LOG2E = 1.0 / math.log(2.0)
+
+
+# --------------------------------------------------------------------------- storage
+
+def widen_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64, exactly.
+
+    A bf16 value is the upper 16 bits of an IEEE binary32 value.
+    """
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bf16 value, ties to even.
+
+    bf16 keeps 8 significant bits and binary32's exponent range: normal values
+    are m * 2**e with 8-bit m; below 2**-126 the spacing is fixed at 2**-133;
+    results of magnitude 2**128 or more overflow to infinity.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                                   # x = m * 2**e, 0.5 <= |m| < 1
+    r = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)         # np.rint: half to even
+    tiny = np.abs(x) < 2.0 ** -126
+    r = np.where(tiny, np.ldexp(np.rint(np.ldexp(x, 133)), -133), r)
+    r = np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, x), r)
+    return r
+
+
+# --------------------------------------------------------------------------- GEMM + stage 1
+
+def matmul(A: np.ndarray, B: np.ndarray) -> np.ndarray:
+    """P = A . B in float64 (ComFuse review, "Core claim": the GEMM output P that
+    is tiled into T_{m,n}). Leading dims broadcast as batches."""
+    return np.matmul(np.asarray(A, np.float64), np.asarray(B, np.float64))
+
+
+def relu(x: np.ndarray) -> np.ndarray:
+    return np.maximum(x, 0.0)
+
+
+def elementwise_stage(P: np.ndarray, alpha: float = 1.0, bias: Optional[np.ndarray] = None,
+                      residual: Optional[np.ndarray] = None, act: str = "none") -> np.ndarray:
+    """Elementwise nodes that stream over the accumulator tile before the first
+    reduction (ComFuse review, "What carries the argument"): scale, bias per
+    output column n, residual add, activation."""
+    X = float(alpha) * P
+    if bias is not None:
+        X = X + np.asarray(bias, np.float64)[..., None, :]
+    if residual is not None:
+        X = X + np.asarray(residual, np.float64)
+    if act == "relu":
+        X = relu(X)
+    elif act != "none":
+        raise ValueError(f"unknown activation {act!r}")
+    return X
+
+
+# --------------------------------------------------------------------------- row reductions
+
+def row_softmax(X: np.ndarray) -> np.ndarray:
+    """Softmax over the last axis (a single-axis reduction over the strip that
+    shares row index m; ComFuse review, "If this is right")."""
+    mx = X.max(axis=-1, keepdims=True)
+    e = np.exp(X - mx)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def layer_norm(X: np.ndarray, gamma: Optional[np.ndarray], beta: Optional[np.ndarray],
+               eps: float) -> np.ndarray:
+    """LayerNorm over the last axis (ComFuse review, Fig. 3 "MatMul +
+    LayerNorm"): two-pass mean and biased variance, eps inside the root."""
+    mu = X.mean(axis=-1, keepdims=True)
+    d = X - mu
+    var = (d * d).mean(axis=-1, keepdims=True)
+    Y = d / np.sqrt(var + float(eps))
+    if gamma is not None:
+        Y = Y * np.asarray(gamma, np.float64)
+    if beta is not None:
+        Y = Y + np.asarray(beta, np.float64)
+    return Y
+
+
+def rms_norm(X: np.ndarray, weight: Optional[np.ndarray], eps: float) -> np.ndarray:
+    """RMSNorm over the last axis (ComFuse review, Fig. 2 "Data Flow in MatMul +
+    RMSNorm Subgraph"): x / sqrt(mean(x^2) + eps) * w."""
+    ms = (X * X).mean(axis=-1, keepdims=True)
+    Y = X / np.sqrt(ms + float(eps))
+    if weight is not None:
+        Y = Y * np.asarray(weight, np.float64)
+    return Y
+
+
+def gemm_epilogue(A: np.ndarray, B: np.ndarray, *, alpha: float = 1.0,
+                  bias: Optional[np.ndarray] = None, residual: Optional[np.ndarray] = None,
+                  act: str = "none", row_op: str = "none", gamma: Optional[np.ndarray] = None,
+                  beta: Optional[np.ndarray] = None, eps: float = 0.0) -> np.ndarray:
+    """GEMM followed by its memory-intensive epilogue, unfused, in float64.
+
+    Stage-Stream order (ComFuse review, "What carries the argument": elementwise
+    nodes stream, a reduction is a stage boundary): alpha, bias, residual,
+    activation, then one row operation with its affine parameters.
+    ``row_op`` is "none", "softmax", "layernorm" or "rmsnorm"; ``gamma`` is the
+    RMSNorm weight when row_op is "rmsnorm".
+    """
+    X = elementwise_stage(matmul(A, B), alpha, bias, residual, act)
+    if row_op == "none":
+        return X
+    if row_op == "softmax":
+        return row_softmax(X)
+    if row_op == "layernorm":
+        return layer_norm(X, gamma, beta, eps)
+    if row_op == "rmsnorm":
+        return rms_norm(X, gamma, eps)
+    raise ValueError(f"unknown row_op {row_op!r}")
+
+
+# --------------------------------------------------------------------------- back-to-back GEMM
+
+def softmax_bf16_operand(S: np.ndarray):
+    """Row softmax of S split into a bf16 numerator operand and a float64
+    denominator: returns (round_bf16(2**(t - c)), sum(2**(t - c))) with
+    t = log2(e) * S and c = ceil(max_row t), an integer. Dividing the second
+    GEMM's result by the denominator gives softmax(S) . B1 with the operand in
+    bf16. Because c is an integer and rounding commutes with scaling by a power
+    of two, the quotient does not depend on the integer chosen."""
+    t = S * _LOG2E
+    c = np.ceil(t.max(axis=-1, keepdims=True))
+    pt = np.exp2(t - c)
+    return round_bf16(pt), pt.sum(axis=-1, keepdims=True)
+
+
+def b2bgemm(A: np.ndarray, B0: np.ndarray, B1: np.ndarray, *, alpha: float = 1.0,
+            bias: Optional[np.ndarray] = None, act: str = "none", row_op: str = "none",
+            b0_layout: str = "kl", round_operand: bool = True) -> np.ndarray:
+    """Back-to-back GEMM O = F(alpha * A . B0 + bias) . B1 (ComFuse review,
+    Referee Report major comment 2, paper Sec. IV-A and Eqs. (2)-(5); the
+    intermediate S is an [M, L] matrix, L being the page's N1).
+
+    ``B0`` is [K, L] (``b0_layout="kl"``) or [L, K] (``"lk"``, e.g. attention
+    keys). F is the activation (``act``) and optionally a row softmax
+    (``row_op="softmax"``). With ``round_operand`` the left operand of the second
+    GEMM is rounded to bf16 as described in the module docstring; without it
+    the whole computation stays in float64. Leading dims broadcast as batches;
+    batches are evaluated one at a time to bound memory.
+    """
+    A = np.asarray(A, np.float64)
+    B0 = np.asarray(B0, np.float64)
+    B1 = np.asarray(B1, np.float64)
+    if b0_layout == "lk":
+        B0 = np.swapaxes(B0, -1, -2)
+    elif b0_layout != "kl":
+        raise ValueError(f"unknown b0_layout {b0_layout!r}")
+    if A.ndim == 3:
+        return np.stack([
+            b2bgemm(A[i], B0[i] if B0.ndim == 3 else B0, B1[i] if B1.ndim == 3 else B1,
+                    alpha=alpha, bias=bias, act=act, row_op=row_op, b0_layout="kl",
+                    round_operand=round_operand)
+            for i in range(A.shape[0])])
+    S = elementwise_stage(matmul(A, B0), alpha, bias, None, act)
+    if row_op == "softmax":
+        if round_operand:
+            num, den = softmax_bf16_operand(S)
+            return matmul(num, B1) / den
+        return matmul(row_softmax(S), B1)
+    if row_op != "none":
+        raise ValueError(f"row_op {row_op!r} is not supported between two GEMMs")
+    Pm = round_bf16(S) if round_operand else S
+    return matmul(Pm, B1)

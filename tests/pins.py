@@ -1,0 +1,314 @@
+"""Pins of the fp64 oracle: each check raises AssertionError when the oracle
+disagrees with exact arithmetic, a closed form or an invariant.
+
+They are plain functions so that ``test_oracle_pins.py`` runs them against the
+oracle and ``test_oracle_mutations.py`` runs them against deliberately broken
+copies of it (a mutation must make at least one pin fail).
+"""
+from __future__ import annotations
+
+import math
+from decimal import Decimal
+from fractions import Fraction
+
+import numpy as np
+
+import exact as X
+
+
+def _bf16_values(rng, shape, scale=1.0):
+    """Random bf16-representable float64 values (8 significant bits)."""
+    z = rng.standard_normal(shape) * scale
+    m, e = np.frexp(z)
+    return np.ldexp(np.round(np.ldexp(m, 8)), e - 8)
+
+
+def _close_dec(got, want, rtol=1e-13, atol=1e-15):
+    got = float(got)
+    want = float(want)
+    assert abs(got - want) <= atol + rtol * abs(want), (got, want)
+
+
+# --------------------------------------------------------------------------- storage
+
+def pin_round_bf16(o):
+    one = 1.0
+    # ties go to the even neighbour
+    assert o.round_bf16(np.array([one + 2.0 ** -8]))[0] == one
+    assert o.round_bf16(np.array([one + 3 * 2.0 ** -8]))[0] == one + 2.0 ** -6
+    assert o.round_bf16(np.array([-(one + 2.0 ** -8)]))[0] == -one
+    # just above a tie rounds up
+    assert o.round_bf16(np.array([one + 2.0 ** -8 + 2.0 ** -30]))[0] == one + 2.0 ** -7
+    # random values over a wide exponent range, against exact rational rounding
+    rng = np.random.default_rng(11)
+    vals = np.concatenate([
+        rng.standard_normal(300),
+        rng.standard_normal(100) * 1e-3,
+        rng.standard_normal(100) * 1e30,
+        rng.standard_normal(50) * 2.0 ** -128,      # bf16 subnormal range
+        np.array([0.0, 2.0 ** -126, 2.0 ** -133, 1.5 * 2.0 ** -133, 3.0e38]),
+    ])
+    got = o.round_bf16(vals)
+    for v, g in zip(vals, got):
+        want = X.round_bf16_exact(Fraction(float(v)))
+        assert Fraction(float(g)) == want, (v, g, float(want))
+
+
+def pin_widen_bf16(o):
+    bits = np.array([0x3F80, 0xC000, 0x3F81, 0x0000, 0x8000, 0x7F7F, 0x0001], dtype=np.uint16)
+    want = [1.0, -2.0, 1.0 + 2.0 ** -7, 0.0, -0.0, (2.0 - 2.0 ** -7) * 2.0 ** 127, 2.0 ** -133]
+    got = o.widen_bf16(bits)
+    assert list(got) == want, (got, want)
+
+
+# --------------------------------------------------------------------------- GEMM and stage 1
+
+def pin_matmul_exact(o):
+    rng = np.random.default_rng(1)
+    for (m, k, n) in [(4, 4, 4), (3, 5, 2), (1, 7, 1), (5, 1, 3), (2, 3, 6)]:
+        A = _bf16_values(rng, (m, k))
+        B = _bf16_values(rng, (k, n))
+        P = o.matmul(A, B)
+        assert P.shape == (m, n)
+        E = X.mm(X.mat(A), X.mat(B))
+        for i in range(m):
+            for j in range(n):
+                mag = sum((abs(X.F(A[i, p]) * X.F(B[p, j])) for p in range(k)), Fraction(0))
+                bound = k * 2.0 ** -52 * float(mag)
+                assert abs(Fraction(float(P[i, j])) - E[i][j]) <= Fraction(bound), (m, k, n, i, j)
+    # K = 1: the outer product, exactly
+    a = _bf16_values(rng, (6, 1))
+    b = _bf16_values(rng, (1, 5))
+    assert np.array_equal(o.matmul(a, b), a[:, 0][:, None] * b[0][None, :])
+
+
+def pin_stage1_exact(o):
+    rng = np.random.default_rng(2)
+    m, k, n = 3, 4, 5
+    A = _bf16_values(rng, (m, k))
+    B = _bf16_values(rng, (k, n))
+    bias = _bf16_values(rng, (n,))
+    R = _bf16_values(rng, (m, n))
+    alpha = 0.375
+    P = o.matmul(A, B)
+    for act in ("none", "relu"):
+        Y = o.elementwise_stage(P, alpha, bias, R, act)
+        E = X.mm(X.mat(A), X.mat(B))
+        for i in range(m):
+            for j in range(n):
+                v = Fraction(alpha) * E[i][j] + X.F(bias[j]) + X.F(R[i, j])
+                if act == "relu" and v < 0:
+                    v = Fraction(0)
+                assert abs(Fraction(float(Y[i, j])) - v) <= Fraction(1, 2 ** 48), (act, i, j)
+
+
+# --------------------------------------------------------------------------- row operations
+
+def pin_softmax(o):
+    rng = np.random.default_rng(3)
+    Xm = rng.standard_normal((6, 9)) * 3
+    Y = o.row_softmax(Xm)
+    assert np.all(np.abs(Y.sum(-1) - 1) <= 9 * 1e-15)
+    # invariant to a per-row shift
+    assert np.allclose(o.row_softmax(Xm + rng.standard_normal((6, 1)) * 50), Y, rtol=1e-12, atol=0)
+    # constant row -> 1/N
+    assert np.allclose(o.row_softmax(np.full((2, 7), 3.25)), 1.0 / 7, rtol=1e-15, atol=0)
+    # two columns -> logistic of the difference
+    a, b = 1.3, -0.4
+    y = o.row_softmax(np.array([[a, b]]))[0]
+    assert math.isclose(y[0], 1 / (1 + math.exp(b - a)), rel_tol=1e-15)
+    assert math.isclose(y[1], 1 / (1 + math.exp(a - b)), rel_tol=1e-15)
+    # large logits must not overflow (max subtraction)
+    big = np.array([[1000.0, 999.0, 990.0]])
+    yb = o.row_softmax(big)
+    want = X.softmax_row([Fraction(v) for v in big[0]])
+    for g, w in zip(yb[0], want):
+        _close_dec(g, w)
+    # 40-digit brute force on a 4x5 block
+    Z = rng.standard_normal((4, 5)) * 2
+    YZ = o.row_softmax(Z)
+    for i in range(4):
+        for g, w in zip(YZ[i], X.softmax_row([X.F(v) for v in Z[i]])):
+            _close_dec(g, w)
+
+
+def pin_layernorm(o):
+    rng = np.random.default_rng(4)
+    Xm = rng.standard_normal((5, 8)) * 2 + 3
+    for eps in (1e-5, 0.5):
+        Y = o.layer_norm(Xm, None, None, eps)
+        assert np.all(np.abs(Y.mean(-1)) <= 1e-14)
+        for i in range(5):
+            xs = [X.F(v) for v in Xm[i]]
+            mu = sum(xs, Fraction(0)) / len(xs)
+            var = sum(((x - mu) ** 2 for x in xs), Fraction(0)) / len(xs)
+            want = float(var / (var + X.F(eps)))        # variance after normalising
+            got = float(np.mean(Y[i] ** 2))
+            assert math.isclose(got, want, rel_tol=1e-13), (eps, got, want)
+    gamma = rng.standard_normal(8)
+    beta = rng.standard_normal(8)
+    # constant row -> beta
+    Yc = o.layer_norm(np.full((2, 8), -4.5), gamma, beta, 1e-5)
+    assert np.allclose(Yc, beta[None, :], rtol=0, atol=1e-15)
+    # [a, -a] -> [-1, 1] * a / sqrt(a^2 + eps) * gamma + beta
+    a, eps = 0.75, 0.01
+    y2 = o.layer_norm(np.array([[-a, a]]), gamma[:2], beta[:2], eps)[0]
+    s = a / math.sqrt(a * a + eps)
+    assert math.isclose(y2[0], -s * gamma[0] + beta[0], rel_tol=1e-14)
+    assert math.isclose(y2[1], s * gamma[1] + beta[1], rel_tol=1e-14)
+    # 40-digit brute force with the affine step
+    Z = rng.standard_normal((3, 6))
+    g6, b6 = gamma[:6], beta[:6]
+    YZ = o.layer_norm(Z, g6, b6, 1e-5)
+    for i in range(3):
+        for g, w in zip(YZ[i], X.layernorm_row([X.F(v) for v in Z[i]], 1e-5, g6, b6)):
+            _close_dec(g, w, rtol=1e-12, atol=1e-14)
+
+
+def pin_rmsnorm(o):
+    rng = np.random.default_rng(5)
+    Xm = rng.standard_normal((5, 8)) * 1.7
+    for eps in (1e-6, 0.25):
+        Y = o.rms_norm(Xm, None, eps)
+        for i in range(5):
+            xs = [X.F(v) for v in Xm[i]]
+            ms = sum((x * x for x in xs), Fraction(0)) / len(xs)
+            want = float(ms / (ms + X.F(eps)))
+            assert math.isclose(float(np.mean(Y[i] ** 2)), want, rel_tol=1e-13)
+    w = rng.standard_normal(8)
+    c, eps = -1.25, 1e-3
+    Yc = o.rms_norm(np.full((1, 8), c), w, eps)[0]
+    assert np.allclose(Yc, c / math.sqrt(c * c + eps) * w, rtol=1e-14, atol=0)
+    Z = rng.standard_normal((3, 7))
+    YZ = o.rms_norm(Z, w[:7], 1e-6)
+    for i in range(3):
+        for g, ww in zip(YZ[i], X.rmsnorm_row([X.F(v) for v in Z[i]], 1e-6, w[:7])):
+            _close_dec(g, ww, rtol=1e-12, atol=1e-14)
+
+
+def pin_gemm_epilogue_composition(o):
+    """Every row operation composed with bias + residual + ReLU, against brute force."""
+    rng = np.random.default_rng(6)
+    m, k, n = 3, 4, 6
+    A = _bf16_values(rng, (m, k))
+    B = _bf16_values(rng, (k, n))
+    bias = _bf16_values(rng, (n,))
+    R = _bf16_values(rng, (m, n))
+    g = 1 + 0.1 * _bf16_values(rng, (n,))
+    be = 0.1 * _bf16_values(rng, (n,))
+    alpha = 1.5
+    E = X.mm(X.mat(A), X.mat(B))
+    Xf = [[max(Fraction(alpha) * E[i][j] + X.F(bias[j]) + X.F(R[i, j]), Fraction(0))
+           for j in range(n)] for i in range(m)]
+    for row_op in ("none", "softmax", "layernorm", "rmsnorm"):
+        Y = o.gemm_epilogue(A, B, alpha=alpha, bias=bias, residual=R, act="relu",
+                            row_op=row_op, gamma=g, beta=be, eps=1e-5)
+        for i in range(m):
+            if row_op == "none":
+                want = [X.D(v) for v in Xf[i]]
+            elif row_op == "softmax":
+                want = X.softmax_row(Xf[i])
+            elif row_op == "layernorm":
+                want = X.layernorm_row(Xf[i], 1e-5, g, be)
+            else:
+                want = X.rmsnorm_row(Xf[i], 1e-5, g)
+            for gv, wv in zip(Y[i], want):
+                _close_dec(gv, wv, rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------------------- back-to-back GEMM
+
+def pin_b2b_relu(o):
+    rng = np.random.default_rng(7)
+    m, k, l, n = 4, 3, 5, 4
+    A = _bf16_values(rng, (m, k))
+    B0 = _bf16_values(rng, (k, l))
+    B1 = _bf16_values(rng, (l, n))
+    bias = _bf16_values(rng, (l,))
+    alpha = 0.5
+    O = o.b2bgemm(A, B0, B1, alpha=alpha, bias=bias, act="relu")
+    S = X.mm(X.mat(A), X.mat(B0))
+    Pm = [[X.round_bf16_exact(max(Fraction(alpha) * S[i][j] + X.F(bias[j]), Fraction(0)))
+           for j in range(l)] for i in range(m)]
+    E = X.mm(Pm, X.mat(B1))
+    for i in range(m):
+        for j in range(n):
+            assert abs(Fraction(float(O[i, j])) - E[i][j]) <= Fraction(1, 2 ** 45), (i, j)
+    # unrounded operand: exact relu(S) . B1
+    Ou = o.b2bgemm(A, B0, B1, alpha=alpha, bias=bias, act="relu", round_operand=False)
+    Pu = [[max(Fraction(alpha) * S[i][j] + X.F(bias[j]), Fraction(0)) for j in range(l)]
+          for i in range(m)]
+    Eu = X.mm(Pu, X.mat(B1))
+    for i in range(m):
+        for j in range(n):
+            assert abs(Fraction(float(Ou[i, j])) - Eu[i][j]) <= Fraction(1, 2 ** 45)
+    # B1 = identity: the output is the rounded intermediate itself
+    Oi = o.b2bgemm(A, B0, np.eye(l), alpha=alpha, bias=bias, act="relu")
+    for i in range(m):
+        for j in range(l):
+            assert Fraction(float(Oi[i, j])) == Pm[i][j]
+    # [L, K] storage of B0 gives the same result
+    assert np.array_equal(o.b2bgemm(A, B0.T.copy(), B1, alpha=alpha, bias=bias, act="relu",
+                                    b0_layout="lk"), O)
+
+
+def _softmax_operand_bruteforce(srow):
+    """Decimal brute force of the bf16-operand softmax for one row of S (Fractions)."""
+    log2e = X.CTX.divide(Decimal(1), X.LN2)
+    ts = [X.CTX.multiply(X.D(s), log2e) for s in srow]
+    c = max(ts).to_integral_value(rounding="ROUND_CEILING")
+    pts = [X.dexp(X.CTX.multiply(X.CTX.subtract(t, c), X.LN2)) for t in ts]
+    num = [X.round_bf16_exact(X.dec_to_frac(p)) for p in pts]
+    den = sum(pts, Decimal(0))
+    return num, den
+
+
+def pin_b2b_softmax(o):
+    rng = np.random.default_rng(8)
+    m, k, l, n = 4, 6, 7, 5
+    A = _bf16_values(rng, (m, k), 2.0)
+    B0 = _bf16_values(rng, (l, k), 2.0)        # keys stored [L, K]
+    B1 = _bf16_values(rng, (l, n))
+    alpha = 0.125
+    O = o.b2bgemm(A, B0, B1, alpha=alpha, row_op="softmax", b0_layout="lk")
+    S = X.mm(X.mat(A), [list(r) for r in zip(*X.mat(B0))])
+    for i in range(m):
+        num, den = _softmax_operand_bruteforce([Fraction(alpha) * s for s in S[i]])
+        for j in range(n):
+            acc = sum((num[p] * X.F(B1[p, j]) for p in range(l)), Fraction(0))
+            _close_dec(O[i, j], X.CTX.divide(X.D(acc), den), rtol=1e-12, atol=1e-14)
+    # unrounded operand: softmax(S) . B1
+    Ou = o.b2bgemm(A, B0, B1, alpha=alpha, row_op="softmax", b0_layout="lk", round_operand=False)
+    for i in range(m):
+        p = X.softmax_row([Fraction(alpha) * s for s in S[i]])
+        for j in range(n):
+            want = sum((X.CTX.multiply(p[q], X.D(X.F(B1[q, j]))) for q in range(l)), Decimal(0))
+            _close_dec(Ou[i, j], want, rtol=1e-12, atol=1e-14)
+    # B1 = identity: the rows are round_bf16(p~) / l, within 2**-8 of softmax(S)
+    Oi = o.b2bgemm(A, B0, np.eye(l), alpha=alpha, row_op="softmax", b0_layout="lk")
+    Ps = o.row_softmax(alpha * o.matmul(A, B0.T))
+    assert np.all(np.abs(Oi - Ps) <= 2.0 ** -8 * Ps + 1e-300)
+    assert np.all(np.abs(Oi.sum(-1) - 1) <= 2.0 ** -8)
+    # integer stabiliser: the largest numerator of each row lies in (1/2, 1] and
+    # every numerator is a bf16 value
+    num, den = o.softmax_bf16_operand(alpha * o.matmul(A, B0.T))
+    mx = num.max(-1)
+    assert np.all((mx > 0.5) & (mx <= 1.0))
+    assert np.array_equal(o.round_bf16(num), num)
+    # batched input equals per-batch evaluation
+    Ab = np.stack([A, A[::-1]])
+    B0b = np.stack([B0, B0 * 0.5])
+    B1b = np.stack([B1, -B1])
+    Ob = o.b2bgemm(Ab, B0b, B1b, alpha=alpha, row_op="softmax", b0_layout="lk")
+    assert np.array_equal(Ob[1], o.b2bgemm(A[::-1], B0 * 0.5, -B1, alpha=alpha,
+                                           row_op="softmax", b0_layout="lk"))
+
+
+ALL_PINS = [pin_round_bf16, pin_widen_bf16, pin_matmul_exact, pin_stage1_exact, pin_softmax,
+            pin_layernorm, pin_rmsnorm, pin_gemm_epilogue_composition, pin_b2b_relu,
+            pin_b2b_softmax]
+
+
+def run_all(o):
+    for p in ALL_PINS:
+        p(o)

@@ -1,0 +1,74 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that
+the pins reject every one of them. This shows the pins are strong enough to
+catch a dropped term, a wrong sign or index, or a transposed operand."""
+import os
+import types
+
+import pytest
+
+import pins
+
+ORACLE_SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                          "oracle", "__init__.py")
+
+MUTATIONS = {
+    "layernorm_unbiased_variance": [(
+        "var = (d * d).mean(axis=-1, keepdims=True)",
+        "var = (d * d).sum(axis=-1, keepdims=True) / (X.shape[-1] - 1)")],
+    "layernorm_eps_outside_root": [(
+        "Y = d / np.sqrt(var + float(eps))", "Y = d / (np.sqrt(var) + float(eps))")],
+    "layernorm_drops_beta": [(
+        "Y = Y + np.asarray(beta, np.float64)", "Y = Y")],
+    "rmsnorm_drops_eps": [("Y = X / np.sqrt(ms + float(eps))", "Y = X / np.sqrt(ms)")],
+    "rmsnorm_centres_rows": [(
+        "ms = (X * X).mean(axis=-1, keepdims=True)",
+        "ms = ((X - X.mean(axis=-1, keepdims=True)) ** 2).mean(axis=-1, keepdims=True)")],
+    "softmax_without_max_shift": [("e = np.exp(X - mx)", "e = np.exp(X)")],
+    "bias_per_row": [(
+        "X = X + np.asarray(bias, np.float64)[..., None, :]",
+        "X = X + np.asarray(bias, np.float64)[..., :, None]")],
+    "alpha_dropped": [("X = float(alpha) * P", "X = P")],
+    "residual_after_activation": [
+        ("        X = X + np.asarray(residual, np.float64)\n", "        pass\n"),
+        ("        X = relu(X)\n", "        X = relu(X)\n    if residual is not None:\n"
+                                "        X = X + np.asarray(residual, np.float64)\n")],
+    "matmul_transposed_b": [(
+        "return np.matmul(np.asarray(A, np.float64), np.asarray(B, np.float64))",
+        "return np.matmul(np.asarray(A, np.float64), np.swapaxes(np.asarray(B, np.float64), -1, -2))")],
+    "round_ties_away_from_zero": [(
+        "np.rint(np.ldexp(m, 8))", "np.trunc(np.ldexp(m, 8) + np.copysign(0.5, m))")],
+    "round_to_seven_bits": [(
+        "r = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)", "r = np.ldexp(np.rint(np.ldexp(m, 7)), e - 7)")],
+    "widen_wrong_shift": [(".astype(np.uint32) << 16", ".astype(np.uint32) << 15")],
+    "softmax_operand_real_stabiliser": [(
+        "c = np.ceil(t.max(axis=-1, keepdims=True))", "c = t.max(axis=-1, keepdims=True)")],
+    "softmax_operand_rounded_denominator": [(
+        "return round_bf16(pt), pt.sum(axis=-1, keepdims=True)",
+        "r = round_bf16(pt)\n    return r, r.sum(axis=-1, keepdims=True)")],
+    "b2b_operand_not_rounded": [("Pm = round_bf16(S) if round_operand else S", "Pm = S")],
+    "b2b_keys_layout_ignored": [("B0 = np.swapaxes(B0, -1, -2)", "B0 = B0")],
+    "b2b_relu_dropped": [(
+        "S = elementwise_stage(matmul(A, B0), alpha, bias, None, act)",
+        "S = elementwise_stage(matmul(A, B0), alpha, bias, None, 'none')")],
+}
+
+
+def _mutant(edits):
+    src = open(ORACLE_SRC).read()
+    for old, new in edits:
+        assert src.count(old) == 1, f"mutation anchor not found exactly once: {old!r}"
+        src = src.replace(old, new)
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src, "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name):
+    mod = _mutant(MUTATIONS[name])
+    with pytest.raises((AssertionError, ValueError)):
+        pins.run_all(mod)
+
+
+def test_unmutated_copy_passes():
+    pins.run_all(_mutant([]))

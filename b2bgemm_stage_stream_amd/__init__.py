@@ -1,0 +1,239 @@
+"""Python binding of the gfx950 fused GEMM-epilogue / back-to-back GEMM library.
+
+Thin ctypes marshalling over the C ABI in ``include/cf.h`` (``libcf.so`` built
+from ``csrc/`` by ``build_lib.py``). The functions keep the C names; they take
+torch tensors only to read device pointers, strides and the current HIP
+stream. Every computation runs in the library's kernels: there is no fallback,
+and importing this package fails loudly when ``libcf.so`` is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcf.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      "`python -m b2bgemm_stage_stream_amd.build_lib` (or __graft_entry__.build())")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# ----------------------------------------------------------------------------- C types
+CF_OK, CF_ERR_INVALID_ARGUMENT, CF_ERR_UNSUPPORTED, CF_ERR_WORKSPACE, CF_ERR_NO_DEVICE, \
+    CF_ERR_HIP, CF_ERR_DEVICE_TIMEOUT = range(7)
+CF_F32, CF_BF16 = 0, 1
+ACT = {"none": 0, "relu": 1}
+ROW_OP = {"none": 0, "softmax": 1, "layernorm": 2, "rmsnorm": 3}
+
+
+class cf_epilogue(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("alpha", ctypes.c_float),
+        ("bias", ctypes.c_void_p),
+        ("residual", ctypes.c_void_p),
+        ("ld_residual", ctypes.c_int64),
+        ("residual_dtype", ctypes.c_int),
+        ("vec_dtype", ctypes.c_int),
+        ("act", ctypes.c_int),
+        ("row_op", ctypes.c_int),
+        ("gamma", ctypes.c_void_p),
+        ("beta", ctypes.c_void_p),
+        ("eps", ctypes.c_float),
+    ]
+
+
+_i64, _vp, _int, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+_EPI_P = ctypes.POINTER(cf_epilogue)
+
+_lib.cf_epilogue_init.argtypes = [_EPI_P]
+_lib.cf_epilogue_init.restype = None
+_lib.cf_gemm_epilogue_workspace_size.argtypes = [_i64, _i64, _i64, _EPI_P]
+_lib.cf_gemm_epilogue_workspace_size.restype = _sz
+_lib.cf_workspace_init.argtypes = [_vp, _sz, _vp]
+_lib.cf_workspace_init.restype = _int
+_lib.cf_workspace_status.argtypes = [_vp, _vp]
+_lib.cf_workspace_status.restype = _int
+_lib.cf_gemm_epilogue.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _int, _int, _vp, _i64, _int,
+                                  _EPI_P, _vp, _sz, _vp]
+_lib.cf_gemm_epilogue.restype = _int
+_lib.cf_b2bgemm.argtypes = [_i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _int,
+                            _vp, _i64, _i64, _vp, _i64, _i64, _int, _int, _EPI_P, _vp]
+_lib.cf_b2bgemm.restype = _int
+_lib.cf_status_string.argtypes = [_int]
+_lib.cf_status_string.restype = ctypes.c_char_p
+_lib.cf_last_hip_error.argtypes = []
+_lib.cf_last_hip_error.restype = _int
+_lib.cf_version.argtypes = []
+_lib.cf_version.restype = ctypes.c_char_p
+_lib.cf_set_exchange_timeout_us.argtypes = [ctypes.c_uint64]
+_lib.cf_set_exchange_timeout_us.restype = ctypes.c_uint64
+
+EXPORTED = ["cf_epilogue_init", "cf_gemm_epilogue_workspace_size", "cf_workspace_init",
+            "cf_workspace_status", "cf_gemm_epilogue", "cf_b2bgemm", "cf_status_string",
+            "cf_last_hip_error", "cf_version", "cf_set_exchange_timeout_us"]
+
+
+class CfError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.cf_status_string(status).decode()
+        if status == CF_ERR_HIP:
+            msg += f" (hipError {_lib.cf_last_hip_error()})"
+        super().__init__(f"{where}: {msg}")
+
+
+def _check(status: int, where: str):
+    if status != CF_OK:
+        raise CfError(status, where)
+
+
+# ----------------------------------------------------------------------------- helpers
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return CF_F32
+    if t.dtype == torch.bfloat16:
+        return CF_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ld(t) -> int:
+    """Leading dimension (row stride in elements) of a row-major 2-D (or batched) tensor."""
+    if t.dim() < 2:
+        raise ValueError("expected a matrix")
+    if t.stride(-1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    return t.stride(-2)
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def make_epilogue(*, alpha: float = 1.0, bias=None, residual=None, act: str = "none",
+                  row_op: str = "none", gamma=None, beta=None, eps: float = 0.0) -> cf_epilogue:
+    """cf_epilogue descriptor from tensors (bias/gamma/beta share one dtype)."""
+    e = cf_epilogue()
+    _lib.cf_epilogue_init(ctypes.byref(e))
+    e.alpha = float(alpha)
+    e.act = ACT[act]
+    e.row_op = ROW_OP[row_op]
+    e.eps = float(eps)
+    vecs = [v for v in (bias, gamma, beta) if v is not None]
+    if vecs:
+        codes = {_dtype_code(v) for v in vecs}
+        if len(codes) != 1:
+            raise TypeError("bias, gamma and beta must share one dtype")
+        e.vec_dtype = codes.pop()
+        for v in vecs:
+            if not v.is_contiguous():
+                raise ValueError("bias/gamma/beta must be contiguous")
+    e.bias, e.gamma, e.beta = _ptr(bias), _ptr(gamma), _ptr(beta)
+    if residual is not None:
+        e.residual = residual.data_ptr()
+        e.ld_residual = _ld(residual)
+        e.residual_dtype = _dtype_code(residual)
+    return e
+
+
+# ----------------------------------------------------------------------------- C entry points
+def cf_version() -> str:
+    return _lib.cf_version().decode()
+
+
+def cf_status_string(status: int) -> str:
+    return _lib.cf_status_string(status).decode()
+
+
+def cf_set_exchange_timeout_us(us: int) -> int:
+    return int(_lib.cf_set_exchange_timeout_us(int(us)))
+
+
+def cf_gemm_epilogue_workspace_size(M: int, N: int, K: int, epi: Optional[cf_epilogue] = None) -> int:
+    return int(_lib.cf_gemm_epilogue_workspace_size(M, N, K, ctypes.byref(epi) if epi else None))
+
+
+def cf_workspace_init(ws, stream=None) -> None:
+    _check(_lib.cf_workspace_init(ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)),
+           "cf_workspace_init")
+
+
+def cf_workspace_status(ws, stream=None) -> int:
+    """CF_OK, or CF_ERR_DEVICE_TIMEOUT if a strip exchange timed out (synchronises the stream)."""
+    return int(_lib.cf_workspace_status(ws.data_ptr(), _stream(stream)))
+
+
+def cf_gemm_epilogue(A, B, C, *, b_is_nk: bool = False, epi: Optional[cf_epilogue] = None,
+                     workspace=None, stream=None, **epi_kwargs) -> None:
+    """C = epilogue(A . B) in one kernel. A [M, K]; B [K, N] (or [N, K] with
+    b_is_nk); C [M, N]. The epilogue is ``epi`` or built from keyword
+    arguments (alpha, bias, residual, act, row_op, gamma, beta, eps)."""
+    if epi is None:
+        epi = make_epilogue(**epi_kwargs)
+    elif epi_kwargs:
+        raise TypeError("pass either epi or epilogue keywords")
+    M, K = A.shape
+    N = B.shape[0] if b_is_nk else B.shape[1]
+    if C.shape != (M, N):
+        raise ValueError(f"C must be [{M}, {N}]")
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
+                                                           workspace.numel() * workspace.element_size())
+    _check(_lib.cf_gemm_epilogue(M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), int(b_is_nk),
+                                 _dtype_code(A), C.data_ptr(), _ld(C), _dtype_code(C), ctypes.byref(epi),
+                                 ws_ptr, ws_bytes, _stream(stream)), "cf_gemm_epilogue")
+
+
+def cf_b2bgemm(A, B0, B1, O, *, b0_is_lk: bool = False, epi: Optional[cf_epilogue] = None,
+               stream=None, **epi_kwargs) -> None:
+    """O = F(alpha * A . B0 + bias) . B1 in one kernel per batch. A [batch, M, K]
+    (or [M, K]); B0 [batch, K, L] or [batch, L, K] with b0_is_lk (a 2-D B0/B1 is
+    shared by all batches); B1 [batch, L, N]; O [batch, M, N]."""
+    if epi is None:
+        epi = make_epilogue(**epi_kwargs)
+    elif epi_kwargs:
+        raise TypeError("pass either epi or epilogue keywords")
+
+    def batched(t):
+        return (t.shape[0], t.stride(0)) if t.dim() == 3 else (None, 0)
+
+    batch, sa = batched(A)
+    if batch is None:
+        batch = 1
+    M, K = A.shape[-2:]
+    L = B0.shape[-2] if b0_is_lk else B0.shape[-1]
+    N = B1.shape[-1]
+    _, sb0 = batched(B0)
+    _, sb1 = batched(B1)
+    _, so = batched(O)
+    _check(_lib.cf_b2bgemm(batch, M, K, L, N, A.data_ptr(), _ld(A), sa, B0.data_ptr(), _ld(B0), sb0,
+                           int(b0_is_lk), B1.data_ptr(), _ld(B1), sb1, O.data_ptr(), _ld(O), so,
+                           _dtype_code(A), _dtype_code(O), ctypes.byref(epi), _stream(stream)),
+           "cf_b2bgemm")
+
+
+class Workspace:
+    """A cleared device workspace that grows on demand (device memory from torch)."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int, stream=None):
+        import torch
+        if nbytes == 0:
+            return None
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(max(nbytes, 4096), dtype=torch.uint8, device=self.device)
+            cf_workspace_init(self.buf, stream)
+        return self.buf

@@ -1,0 +1,328 @@
+// C ABI of the library (declared in include/cf.h): argument validation, launch
+// planning and dispatch. Every argument check runs before the first HIP call.
+#include "cf.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "cf_launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+std::atomic<uint64_t> g_timeout_us{2000000};
+
+struct DeviceInfo {
+  bool valid = false;
+  int cus = 0;
+  int wallclock_khz = 0;
+};
+std::mutex g_dev_mu;
+DeviceInfo g_dev[64];
+
+cf_status hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return CF_ERR_HIP;
+}
+
+// Current device and its properties; CF_ERR_NO_DEVICE when none is visible.
+cf_status current_device(int* dev_out, DeviceInfo* info) {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) return CF_ERR_NO_DEVICE;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= 64) return CF_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  if (!g_dev[dev].valid) {
+    DeviceInfo d;
+    if ((e = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return hip_fail(e);
+    if ((e = hipDeviceGetAttribute(&d.wallclock_khz, hipDeviceAttributeWallClockRate, dev)) != hipSuccess) return hip_fail(e);
+    if (d.wallclock_khz <= 0) d.wallclock_khz = 100000;
+    d.valid = true;
+    g_dev[dev] = d;
+  }
+  *dev_out = dev;
+  *info = g_dev[dev];
+  return CF_OK;
+}
+
+bool is_dtype(int d) { return d == CF_F32 || d == CF_BF16; }
+size_t dsize(cf_dtype d) { return d == CF_F32 ? 4 : 2; }
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Bytes spanned by `rows` rows of leading dimension ld (elements of size es),
+// padded by `pad_rows` rows so that out-of-range tile rows stay below 2^31.
+bool fits31(int64_t rows, int64_t pad_rows, int64_t ld, size_t es) {
+  const long double b = (long double)(rows + pad_rows) * (long double)ld * (long double)es;
+  return b < 2147483648.0L;
+}
+
+constexpr int64_t kTile = 256;
+
+struct GemmPlan {
+  int64_t tiles_n = 0, strips = 0, tiles = 0;
+  bool exchange = false;
+  size_t ws_bytes = 0;
+};
+
+GemmPlan plan_gemm(int64_t M, int64_t N, const cf_epilogue* epi) {
+  GemmPlan g;
+  g.tiles_n = (N + kTile - 1) / kTile;
+  g.strips = (M + kTile - 1) / kTile;
+  g.tiles = g.tiles_n * g.strips;
+  g.exchange = epi && epi->row_op != CF_ROW_NONE && g.tiles_n > 1;
+  if (g.exchange) {
+    const size_t slots = (size_t)g.strips * (size_t)g.tiles_n * (size_t)kTile * 2 * sizeof(uint64_t);
+    g.ws_bytes = cf::kWsHeaderBytes + ((slots + 255) / 256) * 256;
+  }
+  return g;
+}
+
+cf_status check_epilogue(const cf_epilogue* epi, int64_t N, bool allow_row_ops_norm, bool allow_residual) {
+  if (!epi) return CF_OK;
+  if (epi->struct_size != sizeof(cf_epilogue)) return CF_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(epi->alpha) || !std::isfinite(epi->eps) || epi->eps < 0.0f) return CF_ERR_INVALID_ARGUMENT;
+  if (epi->act != CF_ACT_NONE && epi->act != CF_ACT_RELU) return CF_ERR_INVALID_ARGUMENT;
+  if (epi->row_op < CF_ROW_NONE || epi->row_op > CF_ROW_RMSNORM) return CF_ERR_INVALID_ARGUMENT;
+  if (!is_dtype(epi->vec_dtype) || !is_dtype(epi->residual_dtype)) return CF_ERR_INVALID_ARGUMENT;
+  const size_t vs = dsize(epi->vec_dtype);
+  if ((epi->bias && !aligned(epi->bias, vs)) || (epi->gamma && !aligned(epi->gamma, vs)) ||
+      (epi->beta && !aligned(epi->beta, vs)))
+    return CF_ERR_INVALID_ARGUMENT;
+  if (epi->residual) {
+    if (!allow_residual) return CF_ERR_UNSUPPORTED;
+    if (epi->ld_residual < N || epi->ld_residual < 1) return CF_ERR_INVALID_ARGUMENT;
+    if (!aligned(epi->residual, dsize(epi->residual_dtype))) return CF_ERR_INVALID_ARGUMENT;
+  }
+  if (!allow_row_ops_norm) {
+    if (epi->row_op == CF_ROW_LAYERNORM || epi->row_op == CF_ROW_RMSNORM) return CF_ERR_UNSUPPORTED;
+    if (epi->gamma || epi->beta) return CF_ERR_UNSUPPORTED;
+  }
+  return CF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void cf_epilogue_init(cf_epilogue* epi) {
+  if (!epi) return;
+  std::memset(epi, 0, sizeof(*epi));
+  epi->struct_size = sizeof(cf_epilogue);
+  epi->alpha = 1.0f;
+  epi->residual_dtype = CF_BF16;
+  epi->vec_dtype = CF_BF16;
+  epi->act = CF_ACT_NONE;
+  epi->row_op = CF_ROW_NONE;
+  epi->eps = 0.0f;
+}
+
+size_t cf_gemm_epilogue_workspace_size(int64_t M, int64_t N, int64_t K, const cf_epilogue* epi) {
+  (void)K;
+  if (M <= 0 || N <= 0) return 0;
+  return plan_gemm(M, N, epi).ws_bytes;
+}
+
+cf_status cf_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws || !aligned(ws, 256) || ws_bytes < cf::kWsHeaderBytes) return CF_ERR_WORKSPACE;
+  int dev;
+  DeviceInfo info;
+  cf_status st = current_device(&dev, &info);
+  if (st != CF_OK) return st;
+  hipError_t e = cf::launch_workspace_clear(ws, ws_bytes & ~(size_t)3, (hipStream_t)stream);
+  return e == hipSuccess ? CF_OK : hip_fail(e);
+}
+
+cf_status cf_workspace_status(const void* ws, void* stream) {
+  if (!ws || !aligned(ws, 256)) return CF_ERR_WORKSPACE;
+  int dev;
+  DeviceInfo info;
+  cf_status st = current_device(&dev, &info);
+  if (st != CF_OK) return st;
+  uint32_t err = 0;
+  hipError_t e = hipMemcpyAsync(&err, (const uint32_t*)ws + cf::kHdrError, sizeof(err), hipMemcpyDeviceToHost,
+                                (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e);
+  if ((e = hipStreamSynchronize((hipStream_t)stream)) != hipSuccess) return hip_fail(e);
+  return err ? CF_ERR_DEVICE_TIMEOUT : CF_OK;
+}
+
+cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                           int64_t ldb, int b_is_nk, cf_dtype ab_dtype, void* C, int64_t ldc, cf_dtype c_dtype,
+                           const cf_epilogue* epi, void* ws, size_t ws_bytes, void* stream) {
+  // ---- argument checks (no HIP calls)
+  if (M < 0 || N < 0 || K < 0) return CF_ERR_INVALID_ARGUMENT;
+  if (!is_dtype(ab_dtype) || !is_dtype(c_dtype)) return CF_ERR_INVALID_ARGUMENT;
+  if (b_is_nk != 0 && b_is_nk != 1) return CF_ERR_INVALID_ARGUMENT;
+  cf_status st = check_epilogue(epi, N, true, true);
+  if (st != CF_OK) return st;
+  if (M == 0 || N == 0) return CF_OK;
+  const size_t es = dsize(ab_dtype), cs = dsize(c_dtype);
+  if (!C || ldc < N) return CF_ERR_INVALID_ARGUMENT;
+  if (K > 0) {
+    if (!A || !B || lda < K) return CF_ERR_INVALID_ARGUMENT;
+    if (ldb < (b_is_nk ? K : N)) return CF_ERR_INVALID_ARGUMENT;
+    if (!aligned(A, es) || !aligned(B, es)) return CF_ERR_INVALID_ARGUMENT;
+  }
+  if (!aligned(C, cs)) return CF_ERR_INVALID_ARGUMENT;
+  if (M > INT32_MAX - kTile || N > INT32_MAX - kTile || K > INT32_MAX - kTile) return CF_ERR_UNSUPPORTED;
+  // 32-bit buffer offsets: every operand (plus one tile of padding) below 2 GiB
+  if (!fits31(M, kTile, ldc, cs)) return CF_ERR_UNSUPPORTED;
+  if (K > 0) {
+    if (!fits31(M, kTile, lda, es)) return CF_ERR_UNSUPPORTED;
+    if (b_is_nk ? !fits31(N, kTile, ldb, es) : !fits31(K, 64, ldb, es)) return CF_ERR_UNSUPPORTED;
+  }
+  const cf_dtype rdt = (epi && epi->residual) ? epi->residual_dtype : CF_BF16;
+  if (epi && epi->residual && !fits31(M, kTile, epi->ld_residual, dsize(rdt))) return CF_ERR_UNSUPPORTED;
+  const int row_op = epi ? (int)epi->row_op : 0;
+  if (row_op != CF_ROW_NONE && N > 65536) return CF_ERR_UNSUPPORTED;
+
+  const GemmPlan plan = plan_gemm(M, N, epi);
+  if (plan.exchange) {
+    if (!ws || !aligned(ws, 256) || ws_bytes < plan.ws_bytes) return CF_ERR_WORKSPACE;
+  }
+
+  // fast path: 16-byte accesses everywhere, whole column tiles, bf16 (or no) residual
+  const int64_t ce = ab_dtype == CF_F32 ? 4 : 8;
+  bool vec = (N % kTile == 0) && (K % ce == 0) && (lda % ce == 0) && (ldb % ce == 0) && (ldc % 8 == 0) &&
+             aligned(A, 16) && aligned(B, 16) && aligned(C, 16);
+  if (epi && epi->residual)
+    vec = vec && epi->residual_dtype == CF_BF16 && epi->ld_residual % 8 == 0 && aligned(epi->residual, 16);
+
+  // ---- device
+  int dev;
+  DeviceInfo info;
+  if ((st = current_device(&dev, &info)) != CF_OK) return st;
+
+  cf::GemmEpilogueParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.A = A;
+  p.B = B;
+  p.C = C;
+  p.bias = epi ? epi->bias : nullptr;
+  p.residual = epi ? epi->residual : nullptr;
+  p.gamma = epi ? epi->gamma : nullptr;
+  p.beta = epi ? epi->beta : nullptr;
+  p.lda = (uint32_t)(K > 0 ? lda : 0);
+  p.ldb = (uint32_t)(K > 0 ? ldb : 0);
+  p.ldc = (uint32_t)ldc;
+  p.ldr = (uint32_t)(p.residual ? epi->ld_residual : 0);
+  p.a_bytes = (uint32_t)(K > 0 ? (uint64_t)M * lda * es : 0);
+  p.b_bytes = (uint32_t)(K > 0 ? (uint64_t)(b_is_nk ? N : K) * ldb * es : 0);
+  p.c_bytes = (uint32_t)((uint64_t)M * ldc * cs);
+  p.r_bytes = (uint32_t)(p.residual ? (uint64_t)M * epi->ld_residual * dsize(rdt) : 0);
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.tiles_n = (int)plan.tiles_n;
+  p.tiles = (int)plan.tiles;
+  p.alpha = epi ? epi->alpha : 1.0f;
+  p.eps = epi ? epi->eps : 0.0f;
+  p.act = epi ? (int)epi->act : 0;
+  p.row_op = row_op;
+  p.c_f32 = c_dtype == CF_F32;
+  p.vec_f32 = epi ? epi->vec_dtype == CF_F32 : 0;
+  p.res_f32 = rdt == CF_F32;
+  if (plan.exchange) {
+    p.ws_hdr = (uint32_t*)ws;
+    p.ws_slots = (uint64_t*)((char*)ws + cf::kWsHeaderBytes);
+  }
+  p.spin_ticks = g_timeout_us.load() * (uint64_t)info.wallclock_khz / 1000u;
+
+  const bool in_f32 = ab_dtype == CF_F32;
+  const int per_cu = cf::gemm_epilogue_blocks_per_cu(p, in_f32, b_is_nk != 0, vec);
+  if (per_cu <= 0) return hip_fail(hipGetLastError());
+  const int64_t cap = (int64_t)per_cu * info.cus;
+  int64_t grid;
+  if (plan.exchange) {
+    // every strip must be processed by co-resident workgroups in one round
+    if (plan.tiles_n > cap) return CF_ERR_UNSUPPORTED;
+    grid = std::min<int64_t>(plan.tiles, (cap / plan.tiles_n) * plan.tiles_n);
+  } else {
+    grid = std::min<int64_t>(plan.tiles, cap);
+  }
+  hipError_t e = cf::launch_gemm_epilogue(p, in_f32, b_is_nk != 0, vec, (int)grid, (hipStream_t)stream);
+  return e == hipSuccess ? CF_OK : hip_fail(e);
+}
+
+cf_status cf_b2bgemm(int64_t batch, int64_t M, int64_t K, int64_t L, int64_t N, const void* A, int64_t lda,
+                     int64_t sa, const void* B0, int64_t ldb0, int64_t sb0, int b0_is_lk, const void* B1,
+                     int64_t ldb1, int64_t sb1, void* O, int64_t ldo, int64_t so, cf_dtype in_dtype,
+                     cf_dtype out_dtype, const cf_epilogue* mid, void* stream) {
+  if (batch < 0 || M < 0 || K < 0 || L < 0 || N < 0) return CF_ERR_INVALID_ARGUMENT;
+  if (!is_dtype(in_dtype) || !is_dtype(out_dtype)) return CF_ERR_INVALID_ARGUMENT;
+  if (b0_is_lk != 0 && b0_is_lk != 1) return CF_ERR_INVALID_ARGUMENT;
+  if (sa < 0 || sb0 < 0 || sb1 < 0 || so < 0) return CF_ERR_INVALID_ARGUMENT;
+  cf_status st = check_epilogue(mid, L, false, false);
+  if (st != CF_OK) return st;
+  if (batch == 0 || M == 0 || N == 0) return CF_OK;
+  if (!A || !B0 || !B1 || !O) return CF_ERR_INVALID_ARGUMENT;
+  if (lda < K || ldb0 < (b0_is_lk ? K : L) || ldb1 < N || ldo < N) return CF_ERR_INVALID_ARGUMENT;
+  if (in_dtype != CF_BF16) return CF_ERR_UNSUPPORTED;
+  const size_t os = dsize(out_dtype);
+  if (!aligned(A, 16) || !aligned(B0, 16) || !aligned(B1, 16) || !aligned(O, os)) return CF_ERR_UNSUPPORTED;
+  if (lda % 8 || ldb0 % 8 || ldb1 % 8 || sa % 8 || sb0 % 8 || sb1 % 8) return CF_ERR_UNSUPPORTED;
+  if (mid && mid->bias && mid->vec_dtype != CF_BF16 && mid->vec_dtype != CF_F32) return CF_ERR_INVALID_ARGUMENT;
+  if (batch > INT32_MAX || M > INT32_MAX || L > INT32_MAX || K > INT32_MAX || N > INT32_MAX) return CF_ERR_UNSUPPORTED;
+
+  cf::B2bParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.A = A;
+  p.B0 = B0;
+  p.B1 = B1;
+  p.O = O;
+  p.bias = mid ? mid->bias : nullptr;
+  p.lda = (uint32_t)lda;
+  p.ldb0 = (uint32_t)ldb0;
+  p.ldb1 = (uint32_t)ldb1;
+  p.ldo = (uint32_t)ldo;
+  p.sa = (uint64_t)sa;
+  p.sb0 = (uint64_t)sb0;
+  p.sb1 = (uint64_t)sb1;
+  p.so = (uint64_t)so;
+  p.batch = (int)batch;
+  p.M = (int)M;
+  p.K = (int)K;
+  p.L = (int)L;
+  p.N = (int)N;
+  p.alpha = mid ? mid->alpha : 1.0f;
+  p.act = mid ? (int)mid->act : 0;
+  p.row_op = mid ? (int)mid->row_op : 0;
+  p.out_f32 = out_dtype == CF_F32;
+  p.bias_f32 = (mid && mid->vec_dtype == CF_F32) ? 1 : 0;
+  p.b0_lk = b0_is_lk;
+  if (!cf::b2b_supported(p)) return CF_ERR_UNSUPPORTED;
+
+  int dev;
+  DeviceInfo info;
+  if ((st = current_device(&dev, &info)) != CF_OK) return st;
+  hipError_t e = cf::launch_b2b(p, (hipStream_t)stream);
+  return e == hipSuccess ? CF_OK : hip_fail(e);
+}
+
+const char* cf_status_string(cf_status s) {
+  switch (s) {
+    case CF_OK: return "CF_OK";
+    case CF_ERR_INVALID_ARGUMENT: return "CF_ERR_INVALID_ARGUMENT";
+    case CF_ERR_UNSUPPORTED: return "CF_ERR_UNSUPPORTED";
+    case CF_ERR_WORKSPACE: return "CF_ERR_WORKSPACE";
+    case CF_ERR_NO_DEVICE: return "CF_ERR_NO_DEVICE";
+    case CF_ERR_HIP: return "CF_ERR_HIP";
+    case CF_ERR_DEVICE_TIMEOUT: return "CF_ERR_DEVICE_TIMEOUT";
+  }
+  return "CF_ERR_UNKNOWN";
+}
+
+int cf_last_hip_error(void) { return g_last_hip_error; }
+
+const char* cf_version(void) { return "cf 0.1.0 (gfx950)"; }
+
+uint64_t cf_set_exchange_timeout_us(uint64_t us) { return g_timeout_us.exchange(us); }
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// Kernel parameter blocks and launchers (host <-> kernel interface, internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cf {
+
+// Workspace header words (uint32 index into the header); the header is
+// kWsHeaderBytes long and followed by the partial-statistics slots.
+enum : int { kHdrEpoch = 0, kHdrDone = 32, kHdrError = 64 };
+constexpr size_t kWsHeaderBytes = 512;
+
+// Output tile of one workgroup in the GEMM + epilogue kernel.
+constexpr int kGemmBM = 256;
+constexpr int kGemmBN = 256;
+
+struct GemmEpilogueParams {
+  const void* A;
+  const void* B;
+  void* C;
+  const void* bias;
+  const void* residual;
+  const void* gamma;
+  const void* beta;
+  uint32_t lda, ldb, ldc, ldr;   // elements
+  uint32_t a_bytes, b_bytes, c_bytes, r_bytes;   // extents for the buffer range checks
+  int M, N, K;
+  int tiles_n;       // column tiles per row strip
+  int tiles;         // total output tiles
+  float alpha, eps;
+  int act;           // cf_act
+  int row_op;        // cf_row_op
+  int c_f32;         // 1: fp32 output, 0: bf16
+  int vec_f32;       // dtype of bias/gamma/beta: 1 fp32, 0 bf16
+  int res_f32;       // dtype of residual
+  uint32_t* ws_hdr;  // workspace header (NULL when tiles_n == 1 or no row op)
+  uint64_t* ws_slots;
+  uint64_t spin_ticks;   // wall-clock ticks a strip wait may take
+};
+
+// Launches the persistent kernel. in_f32: fp32 inputs (else bf16); b_nk: B
+// stored [N, K]; vec (fast path): 16-byte accesses allowed, N a multiple of
+// 256 and the residual (if any) bf16.
+hipError_t launch_gemm_epilogue(const GemmEpilogueParams& p, bool in_f32, bool b_nk, bool vec,
+                                int grid, hipStream_t stream);
+
+// Workgroups of the GEMM + epilogue kernel that fit on one compute unit.
+int gemm_epilogue_blocks_per_cu(const GemmEpilogueParams& p, bool in_f32, bool b_nk, bool vec);
+
+hipError_t launch_workspace_clear(void* ws, size_t bytes, hipStream_t stream);
+
+struct B2bParams {
+  const void* A;
+  const void* B0;
+  const void* B1;
+  void* O;
+  const void* bias;     // [L] or NULL
+  uint32_t lda, ldb0, ldb1, ldo;
+  uint64_t sa, sb0, sb1, so;   // batch strides, elements
+  int batch, M, K, L, N;
+  float alpha;
+  int act;
+  int row_op;
+  int out_f32;
+  int bias_f32;
+  int b0_lk;
+};
+
+hipError_t launch_b2b(const B2bParams& p, hipStream_t stream);
+// Returns false when (K, N, row_op, ...) has no kernel instantiation.
+bool b2b_supported(const B2bParams& p);
+
+}  // namespace cf

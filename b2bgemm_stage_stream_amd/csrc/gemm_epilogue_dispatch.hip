@@ -1,0 +1,59 @@
+// Host-side selection and launch of the GEMM + epilogue kernel instantiations,
+// and the workspace clear kernel.
+#include "cf_launch.h"
+
+namespace cf {
+
+#define CF_DECL_PARTS(F, N)                      \
+  const void* cf_ge_kernels_##F##_##N##_0(int);  \
+  const void* cf_ge_kernels_##F##_##N##_1(int);  \
+  const void* cf_ge_kernels_##F##_##N##_2(int);  \
+  const void* cf_ge_kernels_##F##_##N##_3(int);  \
+  const void* cf_ge_kernels_##F##_##N##_4(int);
+CF_DECL_PARTS(0, 0)
+CF_DECL_PARTS(0, 1)
+CF_DECL_PARTS(1, 0)
+CF_DECL_PARTS(1, 1)
+
+typedef const void* (*PartFn)(int);
+static const PartFn kParts[2][2][5] = {
+    {{cf_ge_kernels_0_0_0, cf_ge_kernels_0_0_1, cf_ge_kernels_0_0_2, cf_ge_kernels_0_0_3, cf_ge_kernels_0_0_4},
+     {cf_ge_kernels_0_1_0, cf_ge_kernels_0_1_1, cf_ge_kernels_0_1_2, cf_ge_kernels_0_1_3, cf_ge_kernels_0_1_4}},
+    {{cf_ge_kernels_1_0_0, cf_ge_kernels_1_0_1, cf_ge_kernels_1_0_2, cf_ge_kernels_1_0_3, cf_ge_kernels_1_0_4},
+     {cf_ge_kernels_1_1_0, cf_ge_kernels_1_1_1, cf_ge_kernels_1_1_2, cf_ge_kernels_1_1_3, cf_ge_kernels_1_1_4}}};
+
+static const void* pick(const GemmEpilogueParams& p, bool in_f32, bool b_nk, bool vec) {
+  const int part = vec ? p.row_op : 4;
+  return kParts[in_f32][b_nk][part]((p.bias != nullptr || p.residual != nullptr) ? 1 : 0);
+}
+
+int gemm_epilogue_blocks_per_cu(const GemmEpilogueParams& p, bool in_f32, bool b_nk, bool vec) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pick(p, in_f32, b_nk, vec), 256, 0) != hipSuccess)
+    return 0;
+  return n;
+}
+
+hipError_t launch_gemm_epilogue(const GemmEpilogueParams& p, bool in_f32, bool b_nk, bool vec, int grid,
+                                hipStream_t stream) {
+  void* args[] = {(void*)&p};
+  return hipLaunchKernel(pick(p, in_f32, b_nk, vec), dim3(grid), dim3(256), args, 0, stream);
+}
+
+// Clears a workspace with a fill kernel (no hipMemsetAsync, so the call can be
+// captured in a graph).
+__global__ void workspace_clear_kernel(uint32_t* ws, size_t words) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (size_t)gridDim.x * blockDim.x)
+    ws[i] = 0u;
+}
+
+hipError_t launch_workspace_clear(void* ws, size_t bytes, hipStream_t stream) {
+  const size_t words = bytes / 4;
+  const size_t want = (words + 255) / 256;
+  const int blocks = (int)(want < 1024 ? want : 1024);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(workspace_clear_kernel, dim3(blocks), dim3(256), 0, stream, (uint32_t*)ws, words);
+  return hipGetLastError();
+}
+
+}  // namespace cf

@@ -1,0 +1,29 @@
+// One instantiation unit of the GEMM + epilogue kernel. Compiled once per
+// (input dtype, B layout, part): CF_IN_F32 in {0, 1}, CF_B_NK in {0, 1},
+// CF_PART in {0, 1, 2, 3} (fast path for row op CF_PART, with and without
+// bias/residual) or 4 (general path). Splitting the instantiations lets them
+// compile in parallel.
+#include "gemm_epilogue_kernel.hpp"
+
+#if !defined(CF_IN_F32) || !defined(CF_B_NK) || !defined(CF_PART)
+#error "CF_IN_F32, CF_B_NK and CF_PART must be defined"
+#endif
+
+#define CF_JOIN2(a, b) a##b
+#define CF_JOIN(a, b) CF_JOIN2(a, b)
+#define CF_FN CF_JOIN(cf_ge_kernels_, CF_JOIN(CF_IN_F32, CF_JOIN(_, CF_JOIN(CF_B_NK, CF_JOIN(_, CF_PART)))))
+
+namespace cf {
+
+// Kernel entry of this unit; `pre` selects the bias/residual variant.
+const void* CF_FN(int pre) {
+#if CF_PART < 4
+  if (pre) return (const void*)&gemm_epilogue_kernel<CF_IN_F32 != 0, CF_B_NK != 0, true, CF_PART, true>;
+  return (const void*)&gemm_epilogue_kernel<CF_IN_F32 != 0, CF_B_NK != 0, true, CF_PART, false>;
+#else
+  (void)pre;
+  return (const void*)&gemm_epilogue_kernel<CF_IN_F32 != 0, CF_B_NK != 0, false, 0, false>;
+#endif
+}
+
+}  // namespace cf

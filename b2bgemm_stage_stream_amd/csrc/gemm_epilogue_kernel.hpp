@@ -1,0 +1,683 @@
+// Persistent GEMM + epilogue kernel for gfx950 (Stage-Stream execution).
+// Template definitions; instantiated by gemm_epilogue_inst.hip.
+//
+// Method: ComFuse review (pith.science review of arXiv 2608.03537), "What
+// carries the argument" and Fig. 3/Fig. 4: the accumulator tiles of P = A.B
+// stream through the elementwise epilogue nodes while still on chip; a row
+// reduction is a stage boundary resolved by a three-level aggregation. By the
+// review's reading of Eq. (1) (Referee Report, major comment 1) a reduction
+// over the columns of row m only needs the tiles T_{m,n} that share m.
+//
+// MI355X design:
+//  * one workgroup (4 waves) owns a 256x256 output tile; each wave a 128x128
+//    quarter held as 4x4 fp32 32x32 MFMA accumulators (256 AGPRs per lane);
+//  * operands go HBM -> VGPR -> LDS (double buffered, 2 x 64 KiB), B is
+//    transposed on the way in when stored [K, N], and the tiles use an XOR
+//    swizzle of their 16-byte chunks; MFMA src0 is the B tile and src1 the A
+//    tile, so each lane's accumulator registers all belong to one output row m
+//    (lane & 31) and the row reduction is mostly in-lane;
+//  * reduction level 1: in-lane over 64 registers, then across the two lane
+//    halves with v_permlane32_swap; level 2: the two waves that share rows
+//    merge through LDS; level 3: the workgroups of one row strip exchange
+//    per-row partial statistics through an epoch-tagged workspace in device
+//    memory (the pages use distributed shared memory inside a thread block
+//    cluster; gfx950 has no clusters, so this goes through L2/MALL);
+//  * the grid is persistent and never larger than the number of co-resident
+//    workgroups, and it is a multiple of the strip width, so every strip is
+//    processed by simultaneously resident workgroups in one round;
+//  * the partial statistics are merged in a fixed order, so all workgroups of
+//    a strip compute bit-identical row statistics and results are
+//    deterministic.
+// P itself is never written to memory.
+#pragma once
+
+#include "cf_device.hpp"
+#include "cf_launch.h"
+
+#include <type_traits>
+
+namespace cf {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowBytes = 128;                   // one LDS tile row: 8 chunks of 16 bytes
+constexpr int kTileBytes = kGemmBM * kRowBytes;  // 32 KiB per operand tile (BM == BN)
+
+template <bool kF32> struct In;
+template <> struct In<false> { static constexpr int kChunk = 8; static constexpr int kSize = 2; };
+template <> struct In<true>  { static constexpr int kChunk = 4; static constexpr int kSize = 4; };
+
+__device__ inline uint32_t swz(int row, int chunk) { return (uint32_t)(row * kRowBytes + ((chunk ^ (row & 7)) << 4)); }
+
+// ----------------------------------------------------------------------------- operand loads
+// Global -> registers for one k-tile (BK = 8 chunks of 16 bytes) of a [rows][k]
+// operand (A, or B stored [N, K]). Thread t covers chunk (t & 7) of rows
+// (t >> 3) + 32 i. `off` is this thread's byte offset of row (t >> 3), chunk
+// (t & 7) at k-tile start; rows past the end of the buffer read as zero (buffer
+// range check); chunks past K are zeroed here (only in the last k-tile).
+template <bool kF32, bool kVec>
+__device__ inline void load_rowmajor(u32x4_t (&regs)[8], __amdgpu_buffer_rsrc_t rs, uint32_t off,
+                                     uint32_t row_step, int kc, int K, uint32_t ld, uint32_t row0, int tid) {
+  if constexpr (kVec) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) regs[i] = buf_load_b128(rs, off + (uint32_t)i * row_step);
+    if (kc >= K) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) regs[i] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+  } else {
+    constexpr int S = In<kF32>::kSize;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t row = row0 + (uint32_t)((tid >> 3) + 32 * i);
+      u32x4_t v;
+      if constexpr (kF32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t x = buf_load_b32(rs, (row * ld + (uint32_t)(kc + e)) * S);
+          v[e] = (kc + e < K) ? x : 0u;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t lo = buf_load_b16(rs, (row * ld + (uint32_t)(kc + 2 * e)) * S);
+          const uint32_t hi = buf_load_b16(rs, (row * ld + (uint32_t)(kc + 2 * e + 1)) * S);
+          v[e] = ((kc + 2 * e < K) ? lo : 0u) | ((kc + 2 * e + 1 < K) ? (hi << 16) : 0u);
+        }
+      }
+      regs[i] = v;
+    }
+  }
+}
+
+__device__ inline void store_rowmajor(const u32x4_t (&regs)[8], uint8_t* tile, int tid) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    *(u32x4_t*)(tile + swz((tid >> 3) + 32 * i, tid & 7)) = regs[i];
+}
+
+// B stored [K, N]: load a k-tile x 256 columns, to be transposed into the LDS
+// tile [n][k]. bf16: thread t owns the 8x8 block (k: 8*(t>>5) + i, n: 8*(t&31) + j).
+// fp32: thread t owns two 4x4 blocks (k: 4*((t>>6) + 4*b) + i, n: 4*(t&63) + j).
+// `off` is the byte offset of (k-tile start + first k of the thread, first n of
+// the thread). Rows k >= K read as zero (range check); columns >= N hold
+// values of other columns and only reach output columns that are never stored
+// and are excluded from the row statistics.
+template <bool kF32, bool kVec>
+__device__ inline void load_kn(u32x4_t (&regs)[8], __amdgpu_buffer_rsrc_t rs, uint32_t off,
+                               uint32_t ldbytes, int n, int N) {
+  constexpr int S = In<kF32>::kSize;
+  if constexpr (kVec) {
+    if constexpr (!kF32) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) regs[i] = buf_load_b128(rs, off + (uint32_t)i * ldbytes);
+    } else {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) regs[4 * b + i] = buf_load_b128(rs, off + (uint32_t)(16 * b + i) * ldbytes);
+    }
+  } else {
+    constexpr int R = kF32 ? 4 : 8;      // k rows per block
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t ro = off + (uint32_t)((kF32 ? 16 * (i / 4) + (i % 4) : i)) * ldbytes;
+      u32x4_t v;
+      if constexpr (kF32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t x = buf_load_b32(rs, ro + (uint32_t)e * S);
+          v[e] = (n + e < N) ? x : 0u;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t lo = buf_load_b16(rs, ro + (uint32_t)(2 * e) * S);
+          const uint32_t hi = buf_load_b16(rs, ro + (uint32_t)(2 * e + 1) * S);
+          v[e] = ((n + 2 * e < N) ? lo : 0u) | ((n + 2 * e + 1 < N) ? (hi << 16) : 0u);
+        }
+      }
+      regs[i] = v;
+      (void)R;
+    }
+  }
+}
+
+template <bool kF32>
+__device__ inline void store_kn(const u32x4_t (&regs)[8], uint8_t* tile, int tid) {
+  if constexpr (!kF32) {
+    const int ng = tid & 31, kg = tid >> 5;
+    // regs[i] holds k = 8kg + i, columns n = 8ng + 2d, 8ng + 2d + 1 in dword d.
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int d = j >> 1;
+      u32x4_t o;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t a = regs[2 * p][d], b = regs[2 * p + 1][d];
+        o[p] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+      }
+      *(u32x4_t*)(tile + swz(ng * 8 + j, kg)) = o;
+    }
+  } else {
+    const int ng = tid & 63;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int kg = (tid >> 6) + 4 * b;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x4_t o;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) o[p] = regs[4 * b + p][j];
+        *(u32x4_t*)(tile + swz(ng * 4 + j, kg)) = o;
+      }
+    }
+  }
+}
+
+template <bool kF32>
+__device__ inline void mfma(f32x16_t& acc, const u32x4_t& src0, const u32x4_t& src1) {
+  if constexpr (!kF32) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, src0),
+                                                  __builtin_bit_cast(bf16x8_t, src1), acc, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(src0[j]), __uint_as_float(src1[j]),
+                                                 acc, 0, 0, 0);
+  }
+}
+
+// ----------------------------------------------------------------------------- epilogue helpers
+__device__ inline float load_vec(const void* p, int n, int is_f32) {
+  return is_f32 ? ((const float*)p)[n] : bf16_to_f32(((const uint16_t*)p)[n]);
+}
+
+// Strip exchange word: low 32 bits value, high 32 bits epoch tag. Agent-scope
+// atomics make each word visible across XCDs without an L2-wide flush, and the
+// tag in the same word makes every value self-validating.
+__device__ inline void publish(uint64_t* slot, float v, uint32_t tag) {
+  const uint64_t w = ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v);
+  __hip_atomic_store(slot, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Bounded wait for a peer's word; on timeout records it and returns 0.
+__device__ inline float wait_for(const uint64_t* slot, uint32_t tag, uint64_t t0, uint64_t limit,
+                                 bool& timed_out) {
+  for (;;) {
+    const uint64_t w = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)(w >> 32) == tag) return __uint_as_float((uint32_t)w);
+    if (timed_out || wall_clock64() - t0 > limit) {
+      timed_out = true;
+      return 0.0f;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------------------- epilogue
+// Accumulator layout: acc[mb][nb][4q + e] of a lane belongs to output element
+//   (m0 + ml, n0 + nl + e),  ml = wm*128 + mb*32 + (lane & 31),
+//   nl = wn*128 + nb*32 + 8q + 4h,  h = lane >> 5.
+// All 16 accumulator registers a lane holds in one column block nb of one
+// row block mb belong to the same output row, so the row reduction is in-lane
+// (64 values per row block), then across the two lane halves.
+//
+// The epilogue streams over the accumulators (which stay in AGPRs) once per
+// pass, recomputing the elementwise stage x = act(alpha * P + bias + R) each
+// time instead of writing it back. Each group of 4 accumulators is read with
+// an asm v_accvgpr_read whose extra input is a value computed from the
+// previous group; this keeps the reads in stream order so that only a few
+// accumulators live in VGPRs at a time.
+//
+// LDS use after the main loop (the operand tiles are dead by then):
+constexpr int kResStride = 528;                  // bytes per staged residual row (256 bf16 + 16 B pad)
+constexpr int kOffVec = 256 * kResStride;        // bias, gamma, beta: [3][256] f32
+constexpr int kOffWpart = kOffVec + 3 * 1024;    // [2][256] float2: partial per wave column
+constexpr int kOffRstat = kOffWpart + 4096;      // [256] float2: final row statistics
+constexpr int kLdsEpilogue = kOffRstat + 2048;
+
+// Four accumulators of block `blk`, registers 4q..4q+3, read into VGPRs after
+// `tok` is available.
+template <int Q>
+__device__ inline void acc_read4(const f32x16_t& blk, float tok, float (&v)[4]) {
+  asm("v_accvgpr_read_b32 %0, %4\n\tv_accvgpr_read_b32 %1, %5\n\t"
+      "v_accvgpr_read_b32 %2, %6\n\tv_accvgpr_read_b32 %3, %7"
+      : "=v"(v[0]), "=v"(v[1]), "=v"(v[2]), "=v"(v[3])
+      : "a"(blk[4 * Q]), "a"(blk[4 * Q + 1]), "a"(blk[4 * Q + 2]), "a"(blk[4 * Q + 3]), "v"(tok));
+}
+
+// (n, mean, M2) merge of two partial statistics (Chan et al.'s pairwise update).
+__device__ inline void chan_merge(float& n, float& mean, float& m2, float nb, float meanb, float m2b) {
+  const float nn = n + nb;
+  if (nn > 0.0f) {
+    const float d = meanb - mean;
+    mean = mean + d * (nb / nn);
+    m2 = m2 + m2b + d * d * (n * nb / nn);
+  }
+  n = nn;
+}
+
+// Values of the two lane halves: .x from lane (l & 31), .y from lane (l | 32).
+__device__ inline float2 halves(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// ROW: 0 none, 1 softmax, 2 LayerNorm, 3 RMSNorm (cf_row_op).
+// kFast: N is a multiple of 256, 16-byte accesses are allowed and the residual
+// (if any) is bf16; otherwise every column is masked against N.
+// kPre: a bias or a residual is present.
+template <int ROW, bool kFast, bool kPre>
+__device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueParams& p, uint8_t* smem,
+                                int strip, int tn, uint32_t tag, bool& timed_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, r32 = lane & 31;
+  const int m0 = strip * kGemmBM, n0 = tn * kGemmBN;
+  const __amdgpu_buffer_rsrc_t rsC = make_rsrc(p.C, p.c_bytes);
+
+  float* vbias = (float*)(smem + kOffVec);
+  float* vgamma = vbias + 256;
+  float* vbeta = vgamma + 256;
+  float2* wpart = (float2*)(smem + kOffWpart);
+  float2* rstat = (float2*)(smem + kOffRstat);
+  {
+    const int n = n0 + tid;
+    const bool ok = n < p.N;
+    vbias[tid] = (p.bias && ok) ? load_vec(p.bias, n, p.vec_f32) : 0.0f;
+    vgamma[tid] = (p.gamma && ok) ? load_vec(p.gamma, n, p.vec_f32) : 1.0f;
+    vbeta[tid] = (p.beta && ok) ? load_vec(p.beta, n, p.vec_f32) : 0.0f;
+  }
+  const bool has_res = p.residual != nullptr;
+  const __amdgpu_buffer_rsrc_t rsR = make_rsrc(p.residual, has_res ? p.r_bytes : 0u);
+  if (kFast && has_res) {
+    // stage the bf16 residual tile [256][256] in LDS with coalesced 16-byte loads;
+    // rows >= M read as zero
+    const int c = tid & 31;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      u32x4_t v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = (tid >> 5) + 8 * (8 * b + i);
+        v[i] = buf_load_b128(rsR, ((uint32_t)(m0 + row) * p.ldr + (uint32_t)(n0 + c * 8)) * 2);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = (tid >> 5) + 8 * (8 * b + i);
+        *(u32x4_t*)(smem + row * kResStride + c * 16) = v[i];
+      }
+    }
+  }
+  __syncthreads();
+
+  const float alpha = p.alpha;
+  const float floor_v = p.act == 1 ? 0.0f : -INFINITY;   // ReLU as max with a floor
+  const int ncol = p.N - (n0 + wn * 128 + 4 * h);          // element (c = nb*32 + 8q + e) valid iff c < ncol
+
+  // x for the 4 columns of group (mb, nb, q); tok orders the accumulator reads
+  auto xgroup = [&](int mb, int nb, auto qc, float tok, float (&x)[4]) {
+    constexpr int q = decltype(qc)::value;
+    const int nl = wn * 128 + nb * 32 + 8 * q + 4 * h;
+    f32x4_t bv = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (kPre) bv = *(const f32x4_t*)(vbias + nl);
+    float rv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (kPre && has_res) {
+      const int ml = wm * 128 + mb * 32 + r32;
+      if constexpr (kFast) {
+        const u32x2_t w = *(const u32x2_t*)(smem + ml * kResStride + nl * 2);
+        rv[0] = bf16lo(w[0]); rv[1] = bf16hi(w[0]); rv[2] = bf16lo(w[1]); rv[3] = bf16hi(w[1]);
+      } else {
+        const uint32_t rs = p.res_f32 ? 4 : 2;
+        const uint32_t base = ((uint32_t)(m0 + ml) * p.ldr + (uint32_t)(n0 + nl)) * rs;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t off = (nb * 32 + 8 * q + e < ncol) ? base + (uint32_t)e * rs : kOutOfRange;
+          rv[e] = p.res_f32 ? __uint_as_float(buf_load_b32(rsR, off)) : bf16_to_f32(buf_load_b16(rsR, off));
+        }
+      }
+    }
+    float v[4];
+    acc_read4<q>(acc[mb][nb], tok, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = fmaxf(__builtin_fmaf(alpha, v[e], bv[e]) + rv[e], floor_v);
+  };
+  using Q0 = std::integral_constant<int, 0>;
+  using Q1 = std::integral_constant<int, 1>;
+  using Q2 = std::integral_constant<int, 2>;
+  using Q3 = std::integral_constant<int, 3>;
+  // visit the 16 groups of row block mb in order: f(nb, qc, ...)
+  auto for_groups = [&](auto&& f) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) { f(nb, Q0{}); f(nb, Q1{}); f(nb, Q2{}); f(nb, Q3{}); }
+  };
+  auto valid = [&](int nb, int q, int e) { return kFast || (nb * 32 + 8 * q + e < ncol); };
+
+  float tok = 0.0f;
+  if constexpr (ROW != 0) {
+    const int cnt_w = min(max(p.N - (n0 + wn * 128), 0), 128);
+    // ---- reduction levels 1 and 2 (in-lane, lane halves, then the two waves sharing rows)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      float a = 0.0f, b = 0.0f;
+      if constexpr (ROW == 1) {
+        float mx = -INFINITY;
+        for_groups([&](int nb, auto qc) {
+          float x[4];
+          xgroup(mb, nb, qc, tok, x);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mx = valid(nb, decltype(qc)::value, e) ? fmaxf(mx, x[e]) : mx;
+          tok = mx;
+        });
+        mx = max_halves(mx);
+        const float mxs = (mx == -INFINITY) ? 0.0f : mx * kLog2e;
+        float s = 0.0f;
+        for_groups([&](int nb, auto qc) {
+          float x[4];
+          xgroup(mb, nb, qc, tok, x);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float ex = fast_exp2(__builtin_fmaf(x[e], kLog2e, -mxs));
+            s += valid(nb, decltype(qc)::value, e) ? ex : 0.0f;
+          }
+          tok = s;
+        });
+        a = mx;
+        b = sum_halves(s);
+      } else if constexpr (ROW == 2) {
+        // shifted sums about K (a value of this lane's row), then Chan merges
+        float K = 0.0f, s1 = 0.0f, s2 = 0.0f, cnt = 0.0f;
+        bool first = true;
+        for_groups([&](int nb, auto qc) {
+          float x[4];
+          xgroup(mb, nb, qc, tok, x);
+          if (first) { K = valid(nb, 0, 0) ? x[0] : 0.0f; first = false; }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool ok = valid(nb, decltype(qc)::value, e);
+            const float d = ok ? x[e] - K : 0.0f;
+            s1 += d;
+            s2 = __builtin_fmaf(d, d, s2);
+            if constexpr (!kFast) cnt += ok ? 1.0f : 0.0f;
+          }
+          tok = s2;
+        });
+        if constexpr (kFast) cnt = 64.0f;
+        float mean = cnt > 0.0f ? K + s1 / cnt : 0.0f;
+        float m2 = cnt > 0.0f ? fmaxf(s2 - s1 * (s1 / cnt), 0.0f) : 0.0f;
+        const float2 hn = halves(cnt), hm = halves(mean), hq = halves(m2);
+        float n = hn.x, mm = hm.x, q2 = hq.x;
+        chan_merge(n, mm, q2, hn.y, hm.y, hq.y);
+        a = mm;
+        b = q2;
+        (void)cnt_w;
+      } else {
+        float s2 = 0.0f;
+        for_groups([&](int nb, auto qc) {
+          float x[4];
+          xgroup(mb, nb, qc, tok, x);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float xx = valid(nb, decltype(qc)::value, e) ? x[e] : 0.0f;
+            s2 = __builtin_fmaf(xx, xx, s2);
+          }
+          tok = s2;
+        });
+        a = sum_halves(s2);
+      }
+      if (h == 0) wpart[wn * 256 + wm * 128 + mb * 32 + r32] = make_float2(a, b);
+    }
+    __syncthreads();
+
+    // ---- one thread per row: merge the two wave partials, then (reduction
+    // level 3) exchange with the other column tiles of the strip and merge all
+    // of them in tile order
+    {
+      const int ml = tid;
+      const bool row_ok = m0 + ml < p.M;
+      const float2 w0 = wpart[ml], w1 = wpart[256 + ml];
+      const int c0 = min(max(p.N - n0, 0), 128), c1 = min(max(p.N - n0 - 128, 0), 128);
+      float a, b;
+      if constexpr (ROW == 1) {
+        a = fmaxf(w0.x, w1.x);
+        b = w0.y * fast_exp2((w0.x - a) * kLog2e) + (c1 > 0 ? w1.y * fast_exp2((w1.x - a) * kLog2e) : 0.0f);
+      } else if constexpr (ROW == 2) {
+        float n = (float)c0;
+        a = w0.x;
+        b = w0.y;
+        chan_merge(n, a, b, (float)c1, w1.x, w1.y);
+      } else {
+        a = w0.x + w1.x;
+        b = 0.0f;
+      }
+      if (p.ws_hdr != nullptr && row_ok) {
+        uint64_t* slots = p.ws_slots + (size_t)strip * p.tiles_n * 512 + 2 * ml;
+        publish(slots + (size_t)tn * 512, a, tag);
+        publish(slots + (size_t)tn * 512 + 1, b, tag);
+        const uint64_t t0 = wall_clock64();
+        if constexpr (ROW == 1) {
+          float M = -INFINITY, S = 0.0f;
+          for (int tt = 0; tt < p.tiles_n; ++tt) {
+            float ma = a, sb = b;
+            if (tt != tn) {
+              ma = wait_for(slots + (size_t)tt * 512, tag, t0, p.spin_ticks, timed_out);
+              sb = wait_for(slots + (size_t)tt * 512 + 1, tag, t0, p.spin_ticks, timed_out);
+            }
+            const float Mn = fmaxf(M, ma);
+            S = S * fast_exp2((M - Mn) * kLog2e) + sb * fast_exp2((ma - Mn) * kLog2e);
+            M = Mn;
+          }
+          a = M;
+          b = S;
+        } else if constexpr (ROW == 2) {
+          float n = 0.0f, mean = 0.0f, m2 = 0.0f;
+          for (int tt = 0; tt < p.tiles_n; ++tt) {
+            float ma = a, mq = b;
+            if (tt != tn) {
+              ma = wait_for(slots + (size_t)tt * 512, tag, t0, p.spin_ticks, timed_out);
+              mq = wait_for(slots + (size_t)tt * 512 + 1, tag, t0, p.spin_ticks, timed_out);
+            }
+            chan_merge(n, mean, m2, (float)min(kGemmBN, p.N - tt * kGemmBN), ma, mq);
+          }
+          a = mean;
+          b = m2;
+        } else {
+          float s = 0.0f;
+          for (int tt = 0; tt < p.tiles_n; ++tt)
+            s += (tt == tn) ? a : wait_for(slots + (size_t)tt * 512, tag, t0, p.spin_ticks, timed_out);
+          a = s;
+        }
+      }
+      float2 st;
+      if constexpr (ROW == 1) st = make_float2(a * kLog2e, 1.0f / b);
+      else if constexpr (ROW == 2) st = make_float2(a, rsqrtf(b / (float)p.N + p.eps));
+      else st = make_float2(rsqrtf(a / (float)p.N + p.eps), 0.0f);
+      rstat[ml] = st;
+    }
+    __syncthreads();
+  }
+
+  // ---- stage 2: normalise, affine, cast, store
+  auto store_pass = [&](auto f32c) {
+    constexpr bool kOutF32 = decltype(f32c)::value;
+    constexpr uint32_t es = kOutF32 ? 4u : 2u;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int ml = wm * 128 + mb * 32 + r32;
+      const float2 st = ROW != 0 ? rstat[ml] : make_float2(0.f, 0.f);
+      const uint32_t rowoff = ((uint32_t)(m0 + ml) * p.ldc + (uint32_t)(n0 + wn * 128 + 4 * h)) * es;
+      for_groups([&](int nb, auto qc) {
+        constexpr int q = decltype(qc)::value;
+        const int c = nb * 32 + 8 * q;
+        const int nl = wn * 128 + c + 4 * h;
+        float x[4], y[4];
+        xgroup(mb, nb, qc, tok, x);
+        if constexpr (ROW == 2 || ROW == 3) {
+          const f32x4_t g = *(const f32x4_t*)(vgamma + nl);
+          const f32x4_t be = *(const f32x4_t*)(vbeta + nl);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (ROW == 2) y[e] = __builtin_fmaf((x[e] - st.x) * st.y, g[e], be[e]);
+            else y[e] = x[e] * st.x * g[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (ROW == 1) y[e] = fast_exp2(__builtin_fmaf(x[e], kLog2e, -st.x)) * st.y;
+            else y[e] = x[e];
+          }
+        }
+        tok = y[3];
+        if constexpr (kOutF32) {
+          if constexpr (kFast) {
+            const u32x4_t v = {__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3])};
+            buf_store_b128(v, rsC, rowoff + (uint32_t)c * 4);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              buf_store_b32(__float_as_uint(y[e]), rsC, (c + e < ncol) ? rowoff + (uint32_t)(c + e) * 4 : kOutOfRange);
+          }
+        } else {
+          if constexpr (kFast) {
+            const u32x2_t v = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+            buf_store_b64(v, rsC, rowoff + (uint32_t)c * 2);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              buf_store_b16((uint16_t)f32_to_bf16(y[e]), rsC, (c + e < ncol) ? rowoff + (uint32_t)(c + e) * 2 : kOutOfRange);
+          }
+        }
+      });
+    }
+  };
+  if (p.c_f32) store_pass(std::true_type{});
+  else store_pass(std::false_type{});
+}
+
+// kVec (fast path): vector loads, N a multiple of 256, bf16 or no residual; the
+// epilogue is then specialised on kRow (cf_row_op) and kPre (bias/residual
+// present). The general path (kVec false) dispatches on p.row_op at run time.
+template <bool kF32, bool kBnk, bool kVec, int kRow, bool kPre>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
+void gemm_epilogue_kernel(GemmEpilogueParams p) {
+  constexpr int kLdsBytes = 4 * kTileBytes > kLdsEpilogue ? 4 * kTileBytes : kLdsEpilogue;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
+  constexpr int BK = 8 * In<kF32>::kChunk;
+  constexpr int S = In<kF32>::kSize;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, r32 = lane & 31;
+
+  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.A, p.a_bytes);
+  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(p.B, p.b_bytes);
+
+  const bool exchange = p.ws_hdr != nullptr;
+  uint32_t tag = 0;
+  if (exchange) tag = __hip_atomic_load(p.ws_hdr + kHdrEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  bool timed_out = false;
+
+  const int KT = (p.K + BK - 1) / BK;
+
+  for (int tile = blockIdx.x; tile < p.tiles; tile += gridDim.x) {
+    const int strip = tile / p.tiles_n, tn = tile - strip * p.tiles_n;
+    const int m0 = strip * kGemmBM, n0 = tn * kGemmBN;
+
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{0};
+
+    // ------------------------------------------------------------------ main loop
+    u32x4_t ra[8], rb[8];
+    // per-thread byte offsets at k = 0 and the per-k-tile steps
+    const uint32_t a_off0 = ((uint32_t)(m0 + (tid >> 3)) * p.lda + (uint32_t)((tid & 7) * In<kF32>::kChunk)) * S;
+    const uint32_t a_rstep = 32u * p.lda * S;
+    uint32_t b_off0, b_rstep, b_kstep;
+    int b_n = 0;
+    if constexpr (kBnk) {
+      b_off0 = ((uint32_t)(n0 + (tid >> 3)) * p.ldb + (uint32_t)((tid & 7) * In<kF32>::kChunk)) * S;
+      b_rstep = 32u * p.ldb * S;
+      b_kstep = BK * S;
+    } else {
+      b_n = n0 + (kF32 ? (tid & 63) * 4 : (tid & 31) * 8);
+      const int kr = kF32 ? (tid >> 6) * 4 : (tid >> 5) * 8;
+      b_off0 = ((uint32_t)kr * p.ldb + (uint32_t)b_n) * S;
+      b_rstep = p.ldb * S;
+      b_kstep = (uint32_t)BK * p.ldb * S;
+    }
+    auto load_tile = [&](int kt) {
+      const int k0 = kt * BK;
+      const int kc = k0 + (tid & 7) * In<kF32>::kChunk;
+      load_rowmajor<kF32, kVec>(ra, rsA, a_off0 + (uint32_t)k0 * S, a_rstep, kc, p.K, p.lda, (uint32_t)m0, tid);
+      if constexpr (kBnk) load_rowmajor<kF32, kVec>(rb, rsB, b_off0 + (uint32_t)k0 * S, b_rstep, kc, p.K, p.ldb, (uint32_t)n0, tid);
+      else load_kn<kF32, kVec>(rb, rsB, b_off0 + (uint32_t)kt * b_kstep, b_rstep, b_n, p.N);
+    };
+    auto store_tile = [&](int buf) {
+      uint8_t* ta = smem + buf * kTileBytes;
+      store_rowmajor(ra, ta, tid);
+      if constexpr (kBnk) store_rowmajor(rb, ta + 2 * kTileBytes, tid);
+      else store_kn<kF32>(rb, ta + 2 * kTileBytes, tid);
+    };
+
+    if (KT > 0) {
+      load_tile(0);
+      store_tile(0);
+      __syncthreads();
+    }
+    // LDS layout: A0 @0, A1 @32K, B0 @64K, B1 @96K
+    const uint32_t a_rd = (uint32_t)((wm * 128 + r32) * kRowBytes);
+    const uint32_t b_rd = (uint32_t)(2 * kTileBytes + (wn * 128 + r32) * kRowBytes);
+    for (int kt = 0; kt < KT; ++kt) {
+      const uint32_t bufoff = (uint32_t)(kt & 1) * kTileBytes;
+      if (kt + 1 < KT) load_tile(kt + 1);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint32_t coff = (uint32_t)((((2 * kk + h) ^ (lane & 7))) << 4) + bufoff;
+        u32x4_t af[4], bfr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bfr[i] = *(const u32x4_t*)(smem + b_rd + coff + i * 32 * kRowBytes);
+          af[i] = *(const u32x4_t*)(smem + a_rd + coff + i * 32 * kRowBytes);
+        }
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) mfma<kF32>(acc[mb][nb], bfr[nb], af[mb]);
+      }
+      if (kt + 1 < KT) store_tile((kt + 1) & 1);
+      __syncthreads();
+    }
+
+    // ------------------------------------------------------------------ epilogue
+    if constexpr (kVec) {
+      epilogue<kRow, true, kPre>(acc, p, smem, strip, tn, tag, timed_out);
+    } else {
+      switch (p.row_op) {
+        case 1: epilogue<1, false, true>(acc, p, smem, strip, tn, tag, timed_out); break;
+        case 2: epilogue<2, false, true>(acc, p, smem, strip, tn, tag, timed_out); break;
+        case 3: epilogue<3, false, true>(acc, p, smem, strip, tn, tag, timed_out); break;
+        default: epilogue<0, false, true>(acc, p, smem, strip, tn, tag, timed_out); break;
+      }
+    }
+    __syncthreads();   // the next tile's operand stores reuse this LDS
+  }
+
+  if (exchange) {
+    if (timed_out) __hip_atomic_fetch_or(p.ws_hdr + kHdrError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (tid == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(p.ws_hdr + kHdrDone, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      if (prev == gridDim.x - 1) {
+        __hip_atomic_store(p.ws_hdr + kHdrDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.ws_hdr + kHdrEpoch, tag, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+}
+
+}  // namespace cf

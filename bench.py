@@ -1,0 +1,234 @@
+"""Benchmark of the fused GEMM + epilogue (and back-to-back GEMM) kernels on one
+MI355X.
+
+One step = one fused kernel call over the whole workload (inputs already
+resident in HBM). Prints one JSON line:
+  value      algorithmic GEMM TFLOP/s of the workload (2*M*N*K per GEMM)
+  roofline   the same kernel against the bf16 dense MFMA peak, with the mean
+             kernel time from HIP events on the launch stream
+  cpu_baseline  the fp64 oracle timed on the host cores on a bounded row sample
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused GEMM+epilogue TFLOP/s, % bf16 MFMA peak, intermediate HBM bytes (=0)"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (published)
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (published)
+HBM_GBPS = 8000.0
+
+DEFAULT_WORKLOAD = "c2_gemm_layernorm"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="measured HBM bytes per launch (written from rocprofv3 counters)")
+    return ap.parse_args()
+
+
+def flops_of(w) -> float:
+    d = w.dims
+    if w.kind == "gemm_epilogue":
+        return 2.0 * d["M"] * d["N"] * d["K"]
+    return 2.0 * d["batch"] * d["M"] * (d["K"] * d["L"] + d["L"] * d["N"])
+
+
+def bytes_of(w) -> float:
+    """Algorithmic HBM bytes: every input read once, the output written once."""
+    import gen
+    tot = 0.0
+    for t in w.tensors:
+        tot += np.prod(w.shape(t)) * (2 if t.dtype == "bf16" else 4)
+    d = w.dims
+    out_es = 4 if w.params.get("out_dtype") == "f32" else 2
+    if w.kind == "gemm_epilogue":
+        tot += d["M"] * d["N"] * out_es
+    else:
+        tot += d["batch"] * d["M"] * d["N"] * out_es
+    return float(tot)
+
+
+def make_call(w, dev, torch, cf):
+    """Device tensors + a closure launching one fused kernel on the current stream."""
+    p = w.params
+    out_dt = torch.float32 if p.get("out_dtype") == "f32" else torch.bfloat16
+    stream = torch.cuda.current_stream()
+    if w.kind == "gemm_epilogue":
+        d = w.dims
+        e = cf.make_epilogue(alpha=p["alpha"], bias=dev.get("bias"), residual=dev.get("residual"),
+                             act=p["act"], row_op=p["row_op"], gamma=dev.get("gamma", dev.get("weight")),
+                             beta=dev.get("beta"), eps=p.get("eps", 0.0))
+        nbytes = cf.cf_gemm_epilogue_workspace_size(d["M"], d["N"], d["K"], e)
+        ws = cf.Workspace("cuda").get(nbytes)
+        C = torch.empty(d["M"], d["N"], dtype=out_dt, device="cuda")
+
+        def call():
+            cf.cf_gemm_epilogue(dev["A"], dev["B"], C, epi=e, workspace=ws, stream=stream)
+        return call, C, ws, nbytes
+    d = w.dims
+    e = cf.make_epilogue(alpha=p["alpha"], act=p["act"], row_op=p["row_op"])
+    O = torch.empty(d["batch"], d["M"], d["N"], dtype=out_dt, device="cuda")
+    lk = p["b0_layout"] == "lk"
+
+    def call():
+        cf.cf_b2bgemm(dev["A"], dev["B0"], dev["B1"], O, b0_is_lk=lk, epi=e, stream=stream)
+    return call, O, None, 0
+
+
+def cpu_baseline(w, raw, target_s: float):
+    """The fp64 oracle on a bounded sample of rows (rows are independent)."""
+    import oracle
+    ncores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    p = w.params
+    d = w.dims
+
+    def widen(name):
+        t = next(t for t in w.tensors if t.name == name)
+        return oracle.widen_bf16(raw[name]) if t.dtype == "bf16" else raw[name].astype(np.float64)
+
+    if w.kind == "gemm_epilogue":
+        B = widen("B")
+        vec = {k: widen(k) for k in ("bias", "gamma", "beta", "weight") if k in raw}
+
+        def run(rows):
+            A = widen("A")[:rows] if rows < d["M"] else widen("A")
+            R = widen("residual")[:rows] if "residual" in raw else None
+            oracle.gemm_epilogue(A, B, alpha=p["alpha"], bias=vec.get("bias"), residual=R, act=p["act"],
+                                 row_op=p["row_op"], gamma=vec.get("gamma", vec.get("weight")),
+                                 beta=vec.get("beta"), eps=p.get("eps", 0.0))
+        unit_flops = 2.0 * d["N"] * d["K"]          # per row
+        total_units = d["M"]
+        what = "rows of the output"
+    else:
+        A, B0, B1 = widen("A"), widen("B0"), widen("B1")
+
+        def run(rows):   # rows = number of (batch) problems
+            oracle.b2bgemm(A[:rows], B0[:rows] if B0.shape[0] > 1 else B0, B1[:rows] if B1.shape[0] > 1 else B1,
+                           alpha=p["alpha"], act=p["act"], row_op=p["row_op"], b0_layout=p["b0_layout"])
+        if d["batch"] > 1:
+            unit_flops = 2.0 * d["M"] * (d["K"] * d["L"] + d["L"] * d["N"])
+            total_units = d["batch"]
+            what = "independent (batch, head) problems"
+        else:
+            # single batch: sample rows of A
+            A0 = A
+
+            def run(rows):  # noqa: F811
+                oracle.b2bgemm(A0[:, :rows], B0, B1, alpha=p["alpha"], act=p["act"], row_op=p["row_op"],
+                               b0_layout=p["b0_layout"])
+            unit_flops = 2.0 * (d["K"] * d["L"] + d["L"] * d["N"])
+            total_units = d["M"]
+            what = "rows of the output"
+    # calibrate on a small sample, then time the bounded sample
+    n0 = max(1, min(total_units, 64))
+    t = time.perf_counter()
+    run(n0)
+    t0 = time.perf_counter() - t
+    n = int(min(total_units, max(n0, n0 * target_s / max(t0, 1e-6))))
+    t = time.perf_counter()
+    run(n)
+    dt = time.perf_counter() - t
+    tflops = n * unit_flops / dt / 1e12
+    return {"value": tflops, "unit": "TFLOP/s", "cores": ncores, "kind": "oracle",
+            "sample": f"{n} of {total_units} {what} of the same workload, fp64, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (every box here has one GPU)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import b2bgemm_stage_stream_amd as cf
+    import gen
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+    w = gen.workload(args.workload)
+    raw = gen.make(w, seed=args.seed)
+
+    def to_dev(a, dtype):
+        if dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    dev = {t.name: to_dev(raw[t.name], t.dtype) for t in w.tensors}
+    call, out, ws, ws_bytes = make_call(w, dev, torch, cf)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    start_ev = torch.cuda.Event(enable_timing=True)
+    end_ev = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start_ev.record()
+    for _ in range(args.steps):
+        call()
+    end_ev.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if ws is not None and cf.cf_workspace_status(ws) != cf.CF_OK:
+        raise SystemExit("strip exchange timed out during the benchmark")
+    kernel_ms = start_ev.elapsed_time(end_ev) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    flops = flops_of(w)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    in_f32 = any(t.dtype == "f32" for t in w.tensors if t.name == "A")
+    peak = PEAK_F32_TFLOPS if in_f32 else PEAK_BF16_TFLOPS
+    traffic = None
+    if os.path.exists(args.traffic):
+        try:
+            traffic = json.load(open(args.traffic)).get(args.workload)
+        except (OSError, ValueError):
+            traffic = None
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if in_f32 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, **w.dims, "out_dtype": w.params.get("out_dtype")},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic},
+        "kernel_ms": round(kernel_ms, 4),
+        "algorithmic_bytes": bytes_of(w),
+        "intermediate_hbm_bytes": 0,
+        "workspace_bytes": ws_bytes,
+    }
+    if not args.no_cpu_baseline:
+        del dev, out
+        line["cpu_baseline"] = cpu_baseline(w, raw, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,176 @@
+/*
+ * cf.h -- C ABI of the MI355X (gfx950) fused GEMM-epilogue and back-to-back
+ * GEMM library.
+ *
+ * Method: ComFuse's Stage-Stream execution model and B2BGEMM schedule, as
+ * described on the pith.science review of arXiv 2608.03537, "ComFuse: Fusing
+ * Complex Memory-Intensive Subgraphs with Compute-Intensive Kernels For Modern
+ * GPU Architectures" (cited as "ComFuse review" below).
+ *
+ * Conventions for every entry point:
+ *   - Every matrix is row-major; leading dimensions (ld*) and batch strides are
+ *     in elements. Pointers are device pointers owned by the caller; the
+ *     library never allocates, frees or synchronises the caller's memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Each call only enqueues work on that stream and returns at once.
+ *   - Argument and descriptor errors are detected on the host before any HIP
+ *     call and return a status; nothing is launched then. No call aborts or
+ *     throws across this ABI.
+ *   - Results are deterministic: the same inputs give bit-identical outputs
+ *     (all cross-workgroup merges run in a fixed order).
+ *   - Fast paths need 16-byte aligned base pointers and leading dimensions,
+ *     K and N that are multiples of 8 elements (bf16) or 4 (f32); other shapes
+ *     and alignments are accepted and run on element-wise load paths.
+ */
+#ifndef CF_H_
+#define CF_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CF_OK = 0,
+  CF_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size/stride, bad enum      */
+  CF_ERR_UNSUPPORTED = 2,      /* legal but not implemented combination         */
+  CF_ERR_WORKSPACE = 3,        /* workspace missing, too small or misaligned    */
+  CF_ERR_NO_DEVICE = 4,        /* no HIP device is visible                      */
+  CF_ERR_HIP = 5,              /* a HIP runtime call failed; see cf_last_hip_error */
+  CF_ERR_DEVICE_TIMEOUT = 6    /* a strip exchange wait hit its time limit      */
+} cf_status;
+
+typedef enum { CF_F32 = 0, CF_BF16 = 1 } cf_dtype;
+
+typedef enum { CF_ACT_NONE = 0, CF_ACT_RELU = 1 } cf_act;
+
+/* Row operation that forms the Stage-Stream stage boundary: a reduction over
+ * the output columns n of one row m (ComFuse review, "Core claim" and Referee
+ * Report major comment 1 on Eq. (1): such a reduction needs only the tiles
+ * T_{m,n} that share m). */
+typedef enum {
+  CF_ROW_NONE = 0,
+  CF_ROW_SOFTMAX = 1,   /* y = exp(x - max_n x) / sum_n exp(x - max_n x)                 */
+  CF_ROW_LAYERNORM = 2, /* y = (x - mean) / sqrt(var + eps) * gamma[n] + beta[n]; var is
+                           the biased (1/N) variance; gamma/beta optional (NULL = 1 / 0) */
+  CF_ROW_RMSNORM = 3    /* y = x / sqrt(mean_n x^2 + eps) * gamma[n]; gamma optional     */
+} cf_row_op;
+
+/* Epilogue descriptor. The stages run in this fixed order on the fp32
+ * accumulator of P = A.B (ComFuse review, "What carries the argument":
+ * elementwise nodes stream over the accumulator fragments, the reduction is a
+ * stage boundary):
+ *   1. x = alpha * P
+ *   2. x += bias[n]                (if bias != NULL)
+ *   3. x += residual[m, n]         (if residual != NULL)
+ *   4. x = act(x)
+ *   5. row operation (row_op), with gamma/beta/eps
+ *   6. cast to the output dtype (round to nearest even for bf16) and store.
+ * bias, gamma and beta are vectors of N elements of dtype `vec_dtype`;
+ * residual is an [M, N] matrix of dtype `residual_dtype` with leading
+ * dimension ld_residual. */
+typedef struct cf_epilogue {
+  uint32_t struct_size;     /* must be sizeof(cf_epilogue)                        */
+  float alpha;
+  const void* bias;
+  const void* residual;
+  int64_t ld_residual;
+  cf_dtype residual_dtype;
+  cf_dtype vec_dtype;       /* dtype of bias, gamma and beta                      */
+  cf_act act;
+  cf_row_op row_op;
+  const void* gamma;
+  const void* beta;
+  float eps;
+} cf_epilogue;
+
+/* Fills *epi with the identity epilogue (alpha 1, no bias/residual/act/row op). */
+void cf_epilogue_init(cf_epilogue* epi);
+
+/* Bytes of device workspace cf_gemm_epilogue needs for this problem. Zero when
+ * no exchange between workgroups is needed (no row operation, or N fits in one
+ * 256-column tile). The workspace holds the per-strip partial row statistics
+ * (level 3 of the review's three-level reduction, Fig. 4), a launch counter and
+ * an error word. */
+size_t cf_gemm_epilogue_workspace_size(int64_t M, int64_t N, int64_t K, const cf_epilogue* epi);
+
+/* Clears a workspace (enqueued on `stream`). Must be called once after the
+ * workspace is allocated and before its first use; a workspace may then be
+ * reused by any number of calls of any shape on one stream at a time. Calls
+ * that share a workspace on different streams concurrently race.
+ * ws must be 256-byte aligned and ws_bytes >= 4096. */
+cf_status cf_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Reads the workspace error word (blocking copy; call after the stream has
+ * synchronised). Returns CF_ERR_DEVICE_TIMEOUT if a strip exchange wait timed
+ * out since the last cf_workspace_init (outputs of that call are invalid),
+ * otherwise CF_OK. */
+cf_status cf_workspace_status(const void* ws, void* stream);
+
+/* C[M,N] = epilogue(A[M,K] . B) -- one fused kernel; P is never written to
+ * memory (ComFuse review, "The pith" and "If this is right": the MatMul's output
+ * tiles flow into the normalisation while still on chip).
+ *   A       [M, K] with leading dimension lda, dtype ab_dtype.
+ *   B       [K, N] (b_is_nk = 0) or [N, K] (b_is_nk = 1, the nn.Linear weight
+ *           layout) with leading dimension ldb, dtype ab_dtype.
+ *   C       [M, N] with leading dimension ldc, dtype c_dtype. Must not overlap
+ *           the inputs.
+ *   ab_dtype CF_BF16 (bf16 MFMA, fp32 accumulation) or CF_F32 (fp32 MFMA).
+ *   epi     epilogue descriptor (NULL = identity).
+ *   ws      workspace of at least cf_gemm_epilogue_workspace_size() bytes,
+ *           cleared once by cf_workspace_init(); may be NULL when that size is 0.
+ * M, N or K may be 0 (nothing is launched when M or N is 0; K = 0 gives P = 0).
+ * Row operations need N <= 65536. */
+cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K,
+                           const void* A, int64_t lda,
+                           const void* B, int64_t ldb, int b_is_nk, cf_dtype ab_dtype,
+                           void* C, int64_t ldc, cf_dtype c_dtype,
+                           const cf_epilogue* epi, void* ws, size_t ws_bytes, void* stream);
+
+/* Back-to-back GEMM, one fused kernel per call (ComFuse review, Referee Report
+ * major comment 2, paper Sec. IV-A, Eqs. (2)-(5); Fig. 5):
+ *   S = alpha * A . B0 (+ bias[l]),  P = F(S),  O = P . B1
+ * for each of `batch` independent problems. The intermediate S/P [M, L] stays
+ * in registers and LDS and is never written to memory.
+ *   A   [M, K], leading dimension lda, batch stride sa.
+ *   B0  [K, L] (b0_is_lk = 0) or [L, K] (b0_is_lk = 1, e.g. attention keys),
+ *       leading dimension ldb0, batch stride sb0 (0 = shared by all batches).
+ *   B1  [L, N], leading dimension ldb1, batch stride sb1 (0 = shared).
+ *   O   [M, N], leading dimension ldo, batch stride so.
+ *   mid epilogue on S: alpha, bias (vector of L), act, and row_op in
+ *       {CF_ROW_NONE, CF_ROW_SOFTMAX}; residual/gamma/beta must be NULL.
+ * The second GEMM takes P in bf16 (the MFMA operand type); for the softmax the
+ * operand is round(2^(t - c)) with t = log2(e) * S and an integer per-row c,
+ * and the row sum used for normalisation is taken before rounding.
+ * in_dtype must be CF_BF16; out_dtype CF_BF16 or CF_F32.
+ * Supported sizes: K, N in {16, 32, 64, 128} (softmax: K, N in {64, 128});
+ * any M, L and batch. */
+cf_status cf_b2bgemm(int64_t batch, int64_t M, int64_t K, int64_t L, int64_t N,
+                     const void* A, int64_t lda, int64_t sa,
+                     const void* B0, int64_t ldb0, int64_t sb0, int b0_is_lk,
+                     const void* B1, int64_t ldb1, int64_t sb1,
+                     void* O, int64_t ldo, int64_t so,
+                     cf_dtype in_dtype, cf_dtype out_dtype, const cf_epilogue* mid,
+                     void* stream);
+
+/* Human-readable name of a status. Never NULL. */
+const char* cf_status_string(cf_status s);
+
+/* hipError_t of the last failing HIP call made by this thread (0 if none). */
+int cf_last_hip_error(void);
+
+/* Library version string. */
+const char* cf_version(void);
+
+/* Upper bound, in microseconds, of each strip-exchange wait (default 2e6).
+ * A wait that exceeds it records CF_ERR_DEVICE_TIMEOUT in the workspace and
+ * lets the kernel finish. Returns the previous value. */
+uint64_t cf_set_exchange_timeout_us(uint64_t us);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CF_H_ */

@@ -1,0 +1,191 @@
+"""GPU parity of cf_gemm_epilogue (the Stage-Stream GEMM + epilogue kernel)
+against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU-only hosts, never run there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import b2bgemm_stage_stream_amd as cf   # noqa: E402
+import oracle                           # noqa: E402
+import parity as P                      # noqa: E402
+
+_WS = cf.Workspace()
+
+
+def run(A, B, out_dtype, *, b_is_nk=False, **epi):
+    M = A.shape[0]
+    N = B.shape[0] if b_is_nk else B.shape[1]
+    e = cf.make_epilogue(**epi)
+    ws = _WS.get(cf.cf_gemm_epilogue_workspace_size(M, N, A.shape[1], e))
+    C = torch.empty(M, N, dtype=out_dtype, device="cuda")
+    cf.cf_gemm_epilogue(A, B, C, b_is_nk=b_is_nk, epi=e, workspace=ws)
+    torch.cuda.synchronize()
+    if ws is not None:
+        assert cf.cf_workspace_status(ws) == cf.CF_OK
+    return C
+
+
+def oracle_of(w, ref, rows=None):
+    p = w.params
+    sl = (lambda x: x) if rows is None else (lambda x: x[rows])
+    return oracle.gemm_epilogue(
+        sl(ref["A"]), ref["B"], alpha=p["alpha"], bias=ref.get("bias"),
+        residual=None if "residual" not in ref else sl(ref["residual"]), act=p["act"],
+        row_op=p["row_op"], gamma=ref.get("gamma", ref.get("weight")), beta=ref.get("beta"),
+        eps=p.get("eps", 0.0))
+
+
+def epi_of(w, dev):
+    p = w.params
+    return dict(alpha=p["alpha"], bias=dev.get("bias"), residual=dev.get("residual"), act=p["act"],
+                row_op=p["row_op"], gamma=dev.get("gamma", dev.get("weight")), beta=dev.get("beta"),
+                eps=p.get("eps", 0.0))
+
+
+def check_bf16_workload(w, dev, ref, what):
+    R = oracle_of(w, ref)
+    c32 = run(dev["A"], dev["B"], torch.float32, **epi_of(w, dev))
+    r, m = P.assert_close(P.gpu_to_f64(c32), R, P.REL_F_BF16, P.MAX_ABS_BF16, what + " f32-out")
+    c16 = run(dev["A"], dev["B"], torch.bfloat16, **epi_of(w, dev))
+    P.assert_bf16_consistent(c16, c32, R, what + " bf16-out")
+    print(f"{what}: relF {r:.2e} maxabs {m:.2e}", flush=True)
+
+
+# ---------------------------------------------------------------------------- fp32 path (C1)
+
+def test_c1_softmax_f32_full_size():
+    w, dev, ref = P.inputs("c1_gemm_bias_softmax_f32", seed=0)
+    R = oracle_of(w, ref)
+    C = run(dev["A"], dev["B"], torch.float32, **epi_of(w, dev))
+    r, m = P.assert_close(P.gpu_to_f64(C), R, P.REL_F_F32, P.MAX_ABS_F32, "C1")
+    assert np.allclose(P.gpu_to_f64(C).sum(1), 1.0, atol=1e-5)
+    print(f"C1 relF {r:.2e} maxabs {m:.2e}")
+
+
+def test_c1_softmax_large_logits():
+    # logits scaled x100 exercise the max subtraction
+    w, dev, ref = P.inputs("c1_gemm_bias_softmax_f32", seed=1)
+    A = dev["A"] * 100.0
+    R = oracle.gemm_epilogue(ref["A"] * 100.0, ref["B"], bias=ref["bias"], row_op="softmax")
+    C = run(A, dev["B"], torch.float32, bias=dev["bias"], row_op="softmax")
+    P.assert_close(P.gpu_to_f64(C), R, P.REL_F_F32, P.MAX_ABS_F32, "C1 x100")
+
+
+@pytest.mark.parametrize("row_op", ["none", "softmax", "layernorm", "rmsnorm"])
+def test_f32_row_ops_multi_tile(row_op):
+    # fp32 inputs, N spanning several column tiles (strip exchange), ragged M
+    w, dev, ref = P.inputs("c1_gemm_bias_softmax_f32", seed=2, M=300, N=768, K=96)
+    g = torch.linspace(0.5, 1.5, 768, device="cuda")
+    b = torch.linspace(-0.2, 0.2, 768, device="cuda")
+    R = oracle.gemm_epilogue(ref["A"], ref["B"], bias=ref["bias"], row_op=row_op,
+                             gamma=P.gpu_to_f64(g), beta=P.gpu_to_f64(b), eps=1e-5, act="relu")
+    C = run(dev["A"], dev["B"], torch.float32, bias=dev["bias"], row_op=row_op, gamma=g, beta=b,
+            eps=1e-5, act="relu")
+    P.assert_close(P.gpu_to_f64(C), R, P.REL_F_F32 * 10, P.MAX_ABS_F32 * 10, f"f32 {row_op}")
+
+
+# ---------------------------------------------------------------------------- bf16 path
+
+def test_c2_layernorm_reduced():
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=0, M=512, K=1024)
+    check_bf16_workload(w, dev, ref, "C2 512x4096x1024")
+
+
+def test_c3_residual_rmsnorm_reduced():
+    w, dev, ref = P.inputs("c3_gemm_residual_rmsnorm", seed=0, M=384, K=1088)
+    check_bf16_workload(w, dev, ref, "C3 384x4096x1088")
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_c2_seeds(seed):
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=seed, M=256, N=1024, K=512)
+    check_bf16_workload(w, dev, ref, f"C2 seed {seed}")
+
+
+@pytest.mark.parametrize("row_op", ["none", "softmax", "layernorm", "rmsnorm"])
+@pytest.mark.parametrize("shape", [(33, 65, 17), (300, 520, 200), (257, 256, 64), (4, 4, 4), (1, 1000, 9)])
+def test_ragged_general_path(row_op, shape):
+    M, N, K = shape
+    w, dev, ref = P.inputs("c3_gemm_residual_rmsnorm", seed=3, M=M, N=N, K=K)
+    bias = torch.linspace(-0.3, 0.3, N, device="cuda").to(torch.bfloat16)
+    gamma = dev["weight"]
+    beta = (torch.linspace(-0.1, 0.1, N, device="cuda")).to(torch.bfloat16)
+    R = oracle.gemm_epilogue(ref["A"], ref["B"], alpha=0.5, bias=P.gpu_to_f64(bias), residual=ref["residual"],
+                             act="relu", row_op=row_op, gamma=ref["weight"], beta=P.gpu_to_f64(beta), eps=1e-5)
+    kw = dict(alpha=0.5, bias=bias, residual=dev["residual"], act="relu", row_op=row_op, gamma=gamma,
+              beta=beta, eps=1e-5)
+    c32 = run(dev["A"], dev["B"], torch.float32, **kw)
+    P.assert_close(P.gpu_to_f64(c32), R, P.REL_F_BF16, P.MAX_ABS_BF16, f"ragged {shape} {row_op}")
+    c16 = run(dev["A"], dev["B"], torch.bfloat16, **kw)
+    P.assert_bf16_consistent(c16, c32, R, f"ragged {shape} {row_op} bf16")
+
+
+@pytest.mark.parametrize("row_op", ["layernorm", "softmax"])
+def test_b_nk_layout(row_op):
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=4, M=256, N=512, K=256)
+    Bt = dev["B"].t().contiguous()          # [N, K]
+    R = oracle.gemm_epilogue(ref["A"], ref["B"], row_op=row_op, gamma=ref["gamma"], beta=ref["beta"], eps=1e-5)
+    C = run(dev["A"], Bt, torch.float32, b_is_nk=True, row_op=row_op, gamma=dev["gamma"], beta=dev["beta"],
+            eps=1e-5)
+    P.assert_close(P.gpu_to_f64(C), R, P.REL_F_BF16, P.MAX_ABS_BF16, f"B [N,K] {row_op}")
+
+
+def test_fp32_residual_unaligned_ld():
+    w, dev, ref = P.inputs("c3_gemm_residual_rmsnorm", seed=5, M=64, N=512, K=128)
+    R32 = torch.randn(64, 520, device="cuda")[:, :512]      # fp32 residual, ld 520
+    R = oracle.gemm_epilogue(ref["A"], ref["B"], residual=P.gpu_to_f64(R32), row_op="rmsnorm",
+                             gamma=ref["weight"], eps=1e-6)
+    C = run(dev["A"], dev["B"], torch.float32, residual=R32, row_op="rmsnorm", gamma=dev["weight"], eps=1e-6)
+    P.assert_close(P.gpu_to_f64(C), R, P.REL_F_BF16, P.MAX_ABS_BF16, "fp32 residual")
+
+
+def test_k_zero_and_empty():
+    A = torch.zeros(8, 0, dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros(0, 16, dtype=torch.bfloat16, device="cuda")
+    bias = torch.arange(16, dtype=torch.float32, device="cuda")
+    C = run(A, B, torch.float32, bias=bias)
+    assert torch.equal(C, bias.expand(8, 16))
+    E = torch.empty(0, 16, dtype=torch.float32, device="cuda")
+    cf.cf_gemm_epilogue(torch.zeros(0, 4, dtype=torch.bfloat16, device="cuda"),
+                        torch.zeros(4, 16, dtype=torch.bfloat16, device="cuda"), E)
+
+
+# ---------------------------------------------------------------------------- structure
+
+def test_deterministic_and_row_local():
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=6, M=512, N=2048, K=256)
+    kw = epi_of(w, dev)
+    c1 = run(dev["A"], dev["B"], torch.bfloat16, **kw)
+    c2 = run(dev["A"], dev["B"], torch.bfloat16, **kw)
+    assert torch.equal(c1.view(torch.int16), c2.view(torch.int16)), "not deterministic"
+    # Eq. (1) locality: changing row 77 of A changes no other output row
+    A2 = dev["A"].clone()
+    A2[77] = -A2[77] * 2
+    c3 = run(A2, dev["B"], torch.bfloat16, **kw)
+    diff = (c3.view(torch.int16) != c1.view(torch.int16)).any(dim=1).cpu().numpy()
+    assert diff[77] and diff.sum() == 1
+
+
+# ---------------------------------------------------------------------------- full sizes, sampled rows
+
+@pytest.mark.parametrize("name", ["c2_gemm_layernorm", "c3_gemm_residual_rmsnorm"])
+def test_full_size_sampled_rows(name):
+    w, dev, ref = P.inputs(name, seed=0)
+    rows = np.random.default_rng(0).choice(w.dims["M"], 48, replace=False)
+    rows = np.concatenate([rows, [0, w.dims["M"] - 1]])
+    R = oracle_of(w, ref, rows)
+    kw = epi_of(w, dev)
+    c32 = run(dev["A"], dev["B"], torch.float32, **kw)
+    got = P.gpu_to_f64(c32[torch.as_tensor(rows, device="cuda")])
+    r, m = P.assert_close(got, R, P.REL_F_BF16, P.MAX_ABS_BF16, f"{name} full size, sampled rows")
+    del c32
+    c16 = run(dev["A"], dev["B"], torch.bfloat16, **kw)
+    g16 = P.gpu_to_f64(c16[torch.as_tensor(rows, device="cuda")])
+    P.assert_bf16_within(g16, R, f"{name} full size bf16")
+    # every row of a LayerNorm/RMSNorm output is finite
+    assert torch.isfinite(c16.float()).all()
+    print(f"{name} full: relF {r:.2e} maxabs {m:.2e}", flush=True)

@@ -51,14 +51,28 @@ def _compile(src, obj, defs):
     return obj
 
 
-def build(jobs: int | None = None, verbose: bool = True) -> str:
-    """Compile every unit and link libcf.so. Always rebuilds."""
+def _stale(obj: str) -> bool:
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    deps = [os.path.join(CSRC, f) for f in os.listdir(CSRC)] + [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE)]
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+def build(jobs: int | None = None, verbose: bool = True, force: bool = True) -> str:
+    """Compile the units and link libcf.so. With force=False only units older
+    than a source or header are recompiled."""
     os.makedirs(BUILD, exist_ok=True)
     units = _units()
+    if not force:
+        objs_all = [u[1] for u in units]
+        units = [u for u in units if _stale(u[1])]
     jobs = jobs or min(16, os.cpu_count() or 4)
     with cf_futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         futs = [ex.submit(_compile, *u) for u in units]
         objs = [f.result() for f in futs]
+    if not force:
+        objs = objs_all
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -71,4 +85,4 @@ def build(jobs: int | None = None, verbose: bool = True) -> str:
 
 
 if __name__ == "__main__":
-    build()
+    build(force="--incremental" not in sys.argv)

@@ -247,6 +247,22 @@ cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K, const void* A, int64
   } else {
     grid = std::min<int64_t>(plan.tiles, cap);
   }
+  // XCD rectangles: a round of `grid` tiles is (grid / tiles_n) strips x
+  // tiles_n columns; split it into 8 equal a x b rectangles with a + b minimal.
+  if (grid % 8 == 0 && grid % plan.tiles_n == 0) {
+    const int64_t S = grid / plan.tiles_n, per = grid / 8;
+    int64_t best = 0;
+    for (int64_t a = 1; a <= S; ++a) {
+      if (S % a || per % a) continue;
+      const int64_t b = per / a;
+      if (plan.tiles_n % b || (S / a) * (plan.tiles_n / b) != 8) continue;
+      if (!best || a + b < best + per / best) best = a;
+    }
+    if (best) {
+      p.xcd_a = (int)best;
+      p.xcd_b = (int)(per / best);
+    }
+  }
   hipError_t e = cf::launch_gemm_epilogue(p, in_f32, b_is_nk != 0, vec, (int)grid, (hipStream_t)stream);
   return e == hipSuccess ? CF_OK : hip_fail(e);
 }

@@ -28,6 +28,7 @@ struct GemmEpilogueParams {
   int M, N, K;
   int tiles_n;       // column tiles per row strip
   int tiles;         // total output tiles
+  int xcd_a, xcd_b;  // per-XCD rectangle of a round (strips x columns); 0: plain order
   float alpha, eps;
   int act;           // cf_act
   int row_op;        // cf_row_op

@@ -97,8 +97,9 @@ __device__ inline void store_rowmajor(const u32x4_t (&regs)[8], uint8_t* tile, i
 }
 
 // B stored [K, N]: load a k-tile x 256 columns, to be transposed into the LDS
-// tile [n][k]. bf16: thread t owns the 8x8 block (k: 8*(t>>5) + i, n: 8*(t&31) + j).
-// fp32: thread t owns two 4x4 blocks (k: 4*((t>>6) + 4*b) + i, n: 4*(t&63) + j).
+// tile [n][k]. bf16: thread t owns the 8x8 block (k: 8*(t&7) + i, n: 8*(t>>3) + j),
+// so the 8 lanes that share an LDS row write its 8 distinct 16-byte chunks.
+// fp32: thread t owns two 4x4 blocks (k: 4*((t&3) + 4*b) + i, n: 4*(t>>2) + j).
 // `off` is the byte offset of (k-tile start + first k of the thread, first n of
 // the thread). Rows k >= K read as zero (range check); columns >= N hold
 // values of other columns and only reach output columns that are never stored
@@ -146,7 +147,7 @@ __device__ inline void load_kn(u32x4_t (&regs)[8], __amdgpu_buffer_rsrc_t rs, ui
 template <bool kF32>
 __device__ inline void store_kn(const u32x4_t (&regs)[8], uint8_t* tile, int tid) {
   if constexpr (!kF32) {
-    const int ng = tid & 31, kg = tid >> 5;
+    const int ng = tid >> 3, kg = tid & 7;
     // regs[i] holds k = 8kg + i, columns n = 8ng + 2d, 8ng + 2d + 1 in dword d.
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -160,10 +161,10 @@ __device__ inline void store_kn(const u32x4_t (&regs)[8], uint8_t* tile, int tid
       *(u32x4_t*)(tile + swz(ng * 8 + j, kg)) = o;
     }
   } else {
-    const int ng = tid & 63;
+    const int ng = tid >> 2;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const int kg = (tid >> 6) + 4 * b;
+      const int kg = (tid & 3) + 4 * b;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         u32x4_t o;
@@ -582,7 +583,19 @@ void gemm_epilogue_kernel(GemmEpilogueParams p) {
 
   const int KT = (p.K + BK - 1) / BK;
 
-  for (int tile = blockIdx.x; tile < p.tiles; tile += gridDim.x) {
+  for (int base = 0; base < p.tiles; base += gridDim.x) {
+    // Tile of this round. Workgroups are dispatched round-robin over the 8
+    // XCDs (workgroup w on XCD w % 8); in a full round each XCD takes an
+    // xcd_a x xcd_b rectangle of (strip, column) tiles so that its workgroups
+    // share A strips and B panels in that XCD's L2.
+    int tile = base + (int)blockIdx.x;
+    if (p.xcd_a > 0 && base + (int)gridDim.x <= p.tiles) {
+      const int x = (int)blockIdx.x & 7, i = (int)blockIdx.x >> 3;
+      const int rects_n = p.tiles_n / p.xcd_b;
+      const int rx = x / rects_n, ry = x - rx * rects_n;
+      tile = (base / p.tiles_n + rx * p.xcd_a + i / p.xcd_b) * p.tiles_n + ry * p.xcd_b + i % p.xcd_b;
+    }
+    if (tile >= p.tiles) break;
     const int strip = tile / p.tiles_n, tn = tile - strip * p.tiles_n;
     const int m0 = strip * kGemmBM, n0 = tn * kGemmBN;
 
@@ -604,8 +617,8 @@ void gemm_epilogue_kernel(GemmEpilogueParams p) {
       b_rstep = 32u * p.ldb * S;
       b_kstep = BK * S;
     } else {
-      b_n = n0 + (kF32 ? (tid & 63) * 4 : (tid & 31) * 8);
-      const int kr = kF32 ? (tid >> 6) * 4 : (tid >> 5) * 8;
+      b_n = n0 + (kF32 ? (tid >> 2) * 4 : (tid >> 3) * 8);
+      const int kr = kF32 ? (tid & 3) * 4 : (tid & 7) * 8;
       b_off0 = ((uint32_t)kr * p.ldb + (uint32_t)b_n) * S;
       b_rstep = p.ldb * S;
       b_kstep = (uint32_t)BK * p.ldb * S;
@@ -624,32 +637,40 @@ void gemm_epilogue_kernel(GemmEpilogueParams p) {
       else store_kn<kF32>(rb, ta + 2 * kTileBytes, tid);
     };
 
+    // Software pipeline over k-tiles: while the MFMAs consume tile kt from one
+    // LDS buffer, tile kt+1 (already in registers) is written to the other
+    // buffer and tile kt+2 is fetched from memory into registers.
     if (KT > 0) {
       load_tile(0);
       store_tile(0);
+      if (KT > 1) load_tile(1);
       __syncthreads();
     }
     // LDS layout: A0 @0, A1 @32K, B0 @64K, B1 @96K
     const uint32_t a_rd = (uint32_t)((wm * 128 + r32) * kRowBytes);
     const uint32_t b_rd = (uint32_t)(2 * kTileBytes + (wn * 128 + r32) * kRowBytes);
+    auto read_frags = [&](u32x4_t (&af)[4], u32x4_t (&bfr)[4], uint32_t bufoff, int kk) {
+      const uint32_t coff = (uint32_t)((((2 * kk + h) ^ (lane & 7))) << 4) + bufoff;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bfr[i] = *(const u32x4_t*)(smem + b_rd + coff + i * 32 * kRowBytes);
+        af[i] = *(const u32x4_t*)(smem + a_rd + coff + i * 32 * kRowBytes);
+      }
+    };
     for (int kt = 0; kt < KT; ++kt) {
       const uint32_t bufoff = (uint32_t)(kt & 1) * kTileBytes;
-      if (kt + 1 < KT) load_tile(kt + 1);
+      u32x4_t af[2][4], bfr[2][4];
+      read_frags(af[0], bfr[0], bufoff, 0);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const uint32_t coff = (uint32_t)((((2 * kk + h) ^ (lane & 7))) << 4) + bufoff;
-        u32x4_t af[4], bfr[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          bfr[i] = *(const u32x4_t*)(smem + b_rd + coff + i * 32 * kRowBytes);
-          af[i] = *(const u32x4_t*)(smem + a_rd + coff + i * 32 * kRowBytes);
-        }
+        if (kk < 3) read_frags(af[(kk + 1) & 1], bfr[(kk + 1) & 1], bufoff, kk + 1);
+        if (kk == 1 && kt + 1 < KT) store_tile((kt + 1) & 1);
+        if (kk == 2 && kt + 2 < KT) load_tile(kt + 2);
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb) mfma<kF32>(acc[mb][nb], bfr[nb], af[mb]);
+          for (int nb = 0; nb < 4; ++nb) mfma<kF32>(acc[mb][nb], bfr[kk & 1][nb], af[kk & 1][mb]);
       }
-      if (kt + 1 < KT) store_tile((kt + 1) & 1);
       __syncthreads();
     }
 

@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--plain", action="store_true",
+                    help="diagnostic: same GEMM with the identity epilogue (not the headline workload)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per launch (written from rocprofv3 counters)")
@@ -164,6 +166,10 @@ def main():
     sys.path.insert(0, os.path.join(ROOT, "tests"))
 
     w = gen.workload(args.workload)
+    if args.plain:
+        import dataclasses
+        w = dataclasses.replace(w, params={**w.params, "row_op": "none", "act": "none"},
+                                tensors=tuple(t for t in w.tensors if t.name in ("A", "B", "B0", "B1")))
     raw = gen.make(w, seed=args.seed)
 
     def to_dev(a, dtype):
@@ -216,7 +222,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32" if in_f32 else "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, **w.dims, "out_dtype": w.params.get("out_dtype")},
+        "config": {"workload": w.name + ("/identity-epilogue" if args.plain else ""), **w.dims,
+                   "out_dtype": w.params.get("out_dtype")},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic},
         "kernel_ms": round(kernel_ms, 4),

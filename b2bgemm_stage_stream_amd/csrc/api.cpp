@@ -313,6 +313,7 @@ cf_status cf_b2bgemm(int64_t batch, int64_t M, int64_t K, int64_t L, int64_t N, 
   p.out_f32 = out_dtype == CF_F32;
   p.bias_f32 = (mid && mid->vec_dtype == CF_F32) ? 1 : 0;
   p.b0_lk = b0_is_lk;
+  p.o_vec = aligned(O, 16) && ldo % 4 == 0 && so % 4 == 0;
   if (!cf::b2b_supported(p)) return CF_ERR_UNSUPPORTED;
 
   int dev;

@@ -66,6 +66,7 @@ struct B2bParams {
   int out_f32;
   int bias_f32;
   int b0_lk;
+  int o_vec;     // O base, ldo and batch stride allow 4-element vector stores
 };
 
 hipError_t launch_b2b(const B2bParams& p, hipStream_t stream);

@@ -1,0 +1,168 @@
+"""GPU parity of cf_b2bgemm (back-to-back GEMM, intermediate kept on chip)
+against the fp64 oracle, through the C ABI.
+
+The oracle mirrors the one rounding the fused kernel must make: the second
+GEMM's left operand in bf16 (round_operand=True). The unrounded oracle is
+checked too, against a bar derived from that rounding (bf16 unit roundoff
+2^-9 on every operand element gives a relative Frobenius error of order 1e-3;
+the bar is 1e-2)."""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU-only hosts, never run there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import b2bgemm_stage_stream_amd as cf   # noqa: E402
+import oracle                           # noqa: E402
+import parity as P                      # noqa: E402
+
+REL_F_UNROUNDED = 1e-2
+
+
+def run(A, B0, B1, out_dtype, *, b0_is_lk, **epi):
+    batch = A.shape[0] if A.dim() == 3 else 1
+    M = A.shape[-2]
+    N = B1.shape[-1]
+    O = torch.empty(batch, M, N, dtype=out_dtype, device="cuda")   # ld = N (element stores when N % 4)
+    cf.cf_b2bgemm(A, B0, B1, O, b0_is_lk=b0_is_lk, **epi)
+    torch.cuda.synchronize()
+    return O
+
+
+def check(dev, ref, *, lk, what, alpha=1.0, act="none", row_op="none", bias=None, bias_ref=None):
+    kw = dict(alpha=alpha, act=act, row_op=row_op, bias=bias)
+    R = oracle.b2bgemm(ref["A"], ref["B0"], ref["B1"], alpha=alpha, act=act, row_op=row_op, bias=bias_ref,
+                       b0_layout="lk" if lk else "kl")
+    o32 = run(dev["A"], dev["B0"], dev["B1"], torch.float32, b0_is_lk=lk, **kw)
+    g = P.gpu_to_f64(o32)
+    r, m = P.assert_close(g, R, P.REL_F_BF16, P.MAX_ABS_BF16, what + " f32-out")
+    Ru = oracle.b2bgemm(ref["A"], ref["B0"], ref["B1"], alpha=alpha, act=act, row_op=row_op, bias=bias_ref,
+                        b0_layout="lk" if lk else "kl", round_operand=False)
+    ru, _ = P.metrics(g, Ru)
+    assert ru <= REL_F_UNROUNDED, f"{what}: relF vs unrounded oracle {ru:.3e}"
+    o16 = run(dev["A"], dev["B0"], dev["B1"], torch.bfloat16, b0_is_lk=lk, **kw)
+    P.assert_bf16_consistent(o16, o32, R, what + " bf16-out")
+    print(f"{what}: relF {r:.2e} maxabs {m:.2e} (unrounded oracle relF {ru:.2e})", flush=True)
+    return o32
+
+
+# ---------------------------------------------------------------------------- the two workloads
+
+def test_c4_mlp_relu_reduced():
+    w, dev, ref = P.inputs("c4_b2b_mlp_relu", seed=0, M=2048)
+    check(dev, ref, lk=False, act="relu", what="C4 2048 rows")
+
+
+def test_c5_attention_reduced():
+    w, dev, ref = P.inputs("c5_b2b_attention", seed=0, batch=4, M=256, L=256)
+    check(dev, ref, lk=True, alpha=0.125, row_op="softmax", what="C5 4x256x256")
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_c5_seeds(seed):
+    w, dev, ref = P.inputs("c5_b2b_attention", seed=seed, batch=2, M=128, L=512)
+    check(dev, ref, lk=True, alpha=0.125, row_op="softmax", what=f"C5 seed {seed}")
+
+
+def test_c5_large_logits():
+    # logits of several hundred exercise the integer stabiliser's rescaling
+    w, dev, ref = P.inputs("c5_b2b_attention", seed=3, batch=2, M=64, L=320)
+    dev["A"] = (dev["A"].float() * 6).to(torch.bfloat16)
+    ref["A"] = P.gpu_to_f64(dev["A"])
+    check(dev, ref, lk=True, alpha=0.125, row_op="softmax", what="C5 x6 logits")
+
+
+# ---------------------------------------------------------------------------- shapes and layouts
+
+def padded(t: torch.Tensor) -> torch.Tensor:
+    """Same values with the row length padded to a multiple of 8 elements (a
+    strided view, as the library's 16-byte aligned leading dimensions need)."""
+    n = t.shape[-1]
+    buf = torch.zeros(*t.shape[:-1], (n + 7) // 8 * 8, dtype=t.dtype, device=t.device)
+    buf[..., :n] = t
+    return buf[..., :n]
+
+
+@pytest.mark.parametrize("lk", [False, True])
+@pytest.mark.parametrize("row_op,act", [("none", "relu"), ("none", "none"), ("softmax", "none")])
+@pytest.mark.parametrize("shape", [(1, 77, 40, 100, 50), (3, 130, 16, 64, 32), (2, 5, 128, 200, 128),
+                                   (1, 1, 9, 1, 3), (2, 300, 64, 192, 64)])
+def test_shapes(lk, row_op, act, shape):
+    # scaled like the workloads (S and O of order one): alpha = K^-1/2, B1 / L^1/2
+    batch, M, K, L, N = shape
+    w, dev, ref = P.inputs("c5_b2b_attention", seed=4, batch=batch, M=M, K=K, L=L, N=N)
+    dev["B1"] = (dev["B1"].float() / np.sqrt(L)).to(torch.bfloat16)
+    ref["B1"] = P.gpu_to_f64(dev["B1"])
+    if not lk:   # B0 given as [K, L]
+        dev["B0"] = dev["B0"].transpose(1, 2).contiguous()
+        ref["B0"] = np.ascontiguousarray(np.swapaxes(ref["B0"], 1, 2))
+    dev = {k: padded(v) for k, v in dev.items()}
+    check(dev, ref, lk=lk, alpha=1.0 / np.sqrt(K), act=act, row_op=row_op,
+          what=f"{shape} {row_op}/{act} lk={lk}")
+
+
+def test_bias_and_shared_weights():
+    # a 2-D B0/B1 is shared by every batch; bias per column of S
+    w, dev, ref = P.inputs("c4_b2b_mlp_relu", seed=5, batch=3, M=96, K=32, L=96, N=64)
+    bias = torch.linspace(-0.5, 0.5, 96, device="cuda").to(torch.bfloat16)
+    B0, B1 = dev["B0"][0], dev["B1"][0]
+    R = oracle.b2bgemm(ref["A"], ref["B0"][0], ref["B1"][0], alpha=0.5, act="relu", bias=P.gpu_to_f64(bias))
+    O = torch.empty(3, 96, 64, dtype=torch.float32, device="cuda")
+    cf.cf_b2bgemm(dev["A"], B0, B1, O, alpha=0.5, act="relu", bias=bias)
+    torch.cuda.synchronize()
+    P.assert_close(P.gpu_to_f64(O), R, P.REL_F_BF16, P.MAX_ABS_BF16, "bias, shared weights")
+
+
+def test_identity_b1_matches_single_gemm_epilogue():
+    # B1 = I: O is round_bf16(relu(S)), the single-GEMM epilogue followed by bf16 rounding
+    w, dev, ref = P.inputs("c4_b2b_mlp_relu", seed=6, M=256, K=64, L=64, N=64)
+    eye = torch.eye(64, dtype=torch.bfloat16, device="cuda")
+    O = run(dev["A"], dev["B0"], eye[None], torch.float32, b0_is_lk=False, act="relu")
+    C = torch.empty(256, 64, dtype=torch.bfloat16, device="cuda")
+    cf.cf_gemm_epilogue(dev["A"][0], dev["B0"][0], C, act="relu")
+    torch.cuda.synchronize()
+    assert torch.equal(O[0], C.float())
+
+
+def test_identity_v_softmax():
+    # V = I: rows are round_bf16(p~) / l, within 2^-8 of softmax(S)
+    w, dev, ref = P.inputs("c5_b2b_attention", seed=7, batch=2, M=64, L=64, N=64)
+    eye = torch.eye(64, dtype=torch.bfloat16, device="cuda").expand(2, 64, 64).contiguous()
+    O = run(dev["A"], dev["B0"], eye, torch.float32, b0_is_lk=True, alpha=0.125, row_op="softmax")
+    S = 0.125 * np.matmul(ref["A"], np.swapaxes(ref["B0"], 1, 2))
+    Ps = oracle.row_softmax(S)
+    assert np.all(np.abs(P.gpu_to_f64(O) - Ps) <= 2.0 ** -8 * Ps + 1e-6)
+
+
+def test_deterministic():
+    w, dev, ref = P.inputs("c5_b2b_attention", seed=8, batch=4, M=128, L=256)
+    a = run(dev["A"], dev["B0"], dev["B1"], torch.bfloat16, b0_is_lk=True, alpha=0.125, row_op="softmax")
+    b = run(dev["A"], dev["B0"], dev["B1"], torch.bfloat16, b0_is_lk=True, alpha=0.125, row_op="softmax")
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------- full sizes, sampled
+
+def test_c4_full_size_sampled_rows():
+    w, dev, ref = P.inputs("c4_b2b_mlp_relu", seed=0)
+    O = run(dev["A"], dev["B0"], dev["B1"], torch.float32, b0_is_lk=False, act="relu")
+    rows = np.sort(np.random.default_rng(1).choice(w.dims["M"], 2048, replace=False))
+    R = oracle.b2bgemm(ref["A"][:, rows], ref["B0"], ref["B1"], act="relu")
+    got = P.gpu_to_f64(O[:, torch.as_tensor(rows, device="cuda")])
+    r, m = P.assert_close(got, R, P.REL_F_BF16, P.MAX_ABS_BF16, "C4 full size, sampled rows")
+    print(f"C4 full: relF {r:.2e} maxabs {m:.2e}", flush=True)
+
+
+def test_c5_full_size_sampled_heads():
+    w, dev, ref = P.inputs("c5_b2b_attention", seed=0)
+    O = run(dev["A"], dev["B0"], dev["B1"], torch.float32, b0_is_lk=True, alpha=0.125, row_op="softmax")
+    heads = np.array([0, 1, 255, 511])
+    R = oracle.b2bgemm(ref["A"][heads], ref["B0"][heads], ref["B1"][heads], alpha=0.125, row_op="softmax",
+                       b0_layout="lk")
+    got = P.gpu_to_f64(O[torch.as_tensor(heads, device="cuda")])
+    r, m = P.assert_close(got, R, P.REL_F_BF16, P.MAX_ABS_BF16, "C5 full size, sampled heads")
+    assert torch.isfinite(O).all()
+    print(f"C5 full: relF {r:.2e} maxabs {m:.2e}", flush=True)

@@ -44,7 +44,32 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM bytes per launch (written from rocprofv3 counters)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="calibration: time a plain device copy of MIB MiB (for the byte counters)")
     return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources: measured traffic is valid only for the kernels it was taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "b2bgemm_stage_stream_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def copy_probe(mib: int, steps: int):
+    """A plain copy of a known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_each_way": n * 4, "steps": steps}), flush=True)
 
 
 def flops_of(w) -> float:
@@ -156,6 +181,9 @@ def cpu_baseline(w, raw, target_s: float):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe, args.steps)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (every box here has one GPU)",
               file=sys.stderr)
@@ -204,9 +232,11 @@ def main():
     in_f32 = any(t.dtype == "f32" for t in w.tensors if t.name == "A")
     peak = PEAK_F32_TFLOPS if in_f32 else PEAK_BF16_TFLOPS
     traffic = None
-    if os.path.exists(args.traffic):
+    if os.path.exists(args.traffic) and not args.plain:
         try:
-            traffic = json.load(open(args.traffic)).get(args.workload)
+            rec = json.load(open(args.traffic))
+            if rec.get("kernel_source_hash") == kernel_source_hash():
+                traffic = rec.get("bytes_per_launch", {}).get(args.workload)
         except (OSError, ValueError):
             traffic = None
     line = {

@@ -189,6 +189,176 @@ __device__ inline void mfma(f32x16_t& acc, const u32x4_t& src0, const u32x4_t& s
   }
 }
 
+// ----------------------------------------------------------------------------- bf16 streaming main loop
+// bf16 operands, whole 16-byte accesses and K a multiple of 32: the operands go
+// straight from memory into LDS (buffer_load_dwordx4 ... lds, no VGPR staging)
+// through a ring of kStages stages of 32 k each, so the loads of a stage are
+// issued about kStages - 1.5 stages before the MFMAs consume it.
+//
+// Stage layout (32 KiB): A [256 m][64 B] then B. B given [N, K] is stored like
+// A ([256 n][64 B]); B given [K, N] stays [32 k][512 B] and the MFMA operand is
+// read with ds_read_b64_tr_b16, which hands lane i of each 16-lane group the
+// column i of the 4 x 16 block whose 8-byte row pieces the group addressed.
+//
+// One load instruction of a wave fills 1 KiB of LDS contiguously (lane l at
+// +16 l), so the bank swizzle is applied on the global side: lane l loads the
+// logical 16-byte chunk that belongs at its physical position.
+//  * 64-byte rows: physical chunk = logical ^ swz64(row); conflict free for the
+//    MFMA reads whether the LDS serves 8 or 16 lanes of a 16-byte read per cycle.
+//  * 512-byte B rows: physical chunk = logical ^ swz512(k); the 4 rows a 16-lane
+//    transposed read touches land in distinct banks.
+constexpr int kStageK = 32;
+constexpr int kStages = 4;
+constexpr int kStageBytes = 2 * kGemmBM * kStageK * 2;   // A + B, 32 KiB
+constexpr int kStageB = kGemmBM * kStageK * 2;           // offset of B in a stage
+static_assert(kStages * kStageBytes <= 160 * 1024, "LDS ring exceeds 160 KiB");
+
+__device__ inline int swz64(int row) { return (((row >> 1) ^ (row >> 3)) & 1) | ((row >> 1) & 2); }
+__device__ inline int swz512(int k) { const int j = k & 3; return (2 * j) ^ (4 * j); }
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// Raw buffer descriptor words (as make_rsrc builds them) for the asm loads below.
+__device__ inline u32x4_t rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+// 16 bytes per lane from memory straight into LDS at m0 + 16 * lane. Issued
+// from asm so that the compiler neither tracks nor waits for these loads: the
+// ring below orders them explicitly with s_waitcnt vmcnt and s_barrier.
+__device__ inline void lds_dma16(uint32_t lds_addr, u32x4_t rs, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds_addr), "v"(voff), "s"(rs) : "memory", "m0");
+}
+// s_waitcnt with lgkmcnt(0) and vmcnt(n), expcnt left open (gfx9 encoding).
+template <int N>
+__device__ inline void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+__device__ inline u32x2_t lds_read_tr16(const uint8_t* p) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                         (__attribute__((address_space(3))) i16x4_t*)(lds_u8*)p));
+}
+
+// `tid` is threadIdx.x passed through an opaque copy made per output tile, so
+// that the per-lane offsets below are computed per tile instead of being
+// hoisted out of the persistent loop (where they would be spilled and reloaded
+// inside the k loop).
+template <bool kBnk>
+__device__ inline void mainloop_stream(f32x16_t (&acc)[4][4], const GemmEpilogueParams& p, uint8_t* smem,
+                                       int m0, int n0, int tid) {
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, r32 = lane & 31;
+  const int KT = p.K / kStageK;
+  const u32x4_t rsA = rsrc_words(p.A, p.a_bytes), rsB = rsrc_words(p.B, p.b_bytes);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)smem;
+
+  // Global byte offsets (stage 0) of this thread's four A and four B pieces.
+  // Load i of wave w fills LDS block q = 4w + i (1 KiB).
+  uint32_t ga[4], gb[4];
+  {
+    const int ra = lane >> 2, ca = (lane & 3) ^ swz64(lane >> 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * (4 * wave + i) + ra;
+      ga[i] = ((uint32_t)(m0 + row) * p.lda + (uint32_t)(8 * ca)) * 2u;
+      if constexpr (kBnk) {
+        gb[i] = ((uint32_t)(n0 + row) * p.ldb + (uint32_t)(8 * ca)) * 2u;
+      } else {
+        const int kr = 2 * (4 * wave + i) + (lane >> 5);
+        const int cb = (lane & 31) ^ swz512(kr);
+        gb[i] = ((uint32_t)kr * p.ldb + (uint32_t)(n0 + 8 * cb)) * 2u;
+      }
+    }
+  }
+  const uint32_t a_step = kStageK * 2u;
+  const uint32_t b_step = kBnk ? kStageK * 2u : (uint32_t)kStageK * p.ldb * 2u;
+  auto issue = [&](int kt) {
+    const uint32_t st = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(lds0 + (uint32_t)((kt % kStages) * kStageBytes + wave * 4096)));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_dma16(st + i * 1024, rsA, ga[i] + (uint32_t)kt * a_step);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_dma16(st + kStageB + i * 1024, rsB, gb[i] + (uint32_t)kt * b_step);
+  };
+
+  // Per-lane LDS read offsets within a stage. A (and B [N, K]): row r of the
+  // wave's quarter, logical chunk 2 kk + h.
+  const int sa = swz64(r32);
+  const uint32_t a_rd[2] = {(uint32_t)((wm * 128 + r32) * 64 + 16 * ((0 + h) ^ sa)),
+                            (uint32_t)((wm * 128 + r32) * 64 + 16 * ((2 + h) ^ sa))};
+  const uint32_t bn_rd[2] = {(uint32_t)(kStageB + (wn * 128 + r32) * 64 + 16 * ((0 + h) ^ sa)),
+                             (uint32_t)(kStageB + (wn * 128 + r32) * 64 + 16 * ((2 + h) ^ sa))};
+  // B [K, N], transposed reads: lane = 16 g + i reads row kk*16 + 8(g>>1) +
+  // 4 half + i/4, columns wn*128 + nb*32 + 16(g&1) + 4(i&3) .. +3.
+  uint32_t bt_rd[4];
+  {
+    const int g = lane >> 4, i = lane & 15;
+    const int f = swz512(i >> 2);
+    const int c = 2 * (g & 1) + ((i & 3) >> 1);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int phys = wn * 16 + ((nb * 4 + c) ^ f);
+      bt_rd[nb] = (uint32_t)(kStageB + (8 * (g >> 1) + (i >> 2)) * 512 + 16 * phys + 8 * (i & 1));
+    }
+  }
+  auto read_frags = [&](u32x4_t (&af)[4], u32x4_t (&bfr)[4], const uint8_t* st, int kk) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[i] = *(const u32x4_t*)(st + a_rd[kk] + i * 32 * 64);
+    if constexpr (kBnk) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bfr[i] = *(const u32x4_t*)(st + bn_rd[kk] + i * 32 * 64);
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const u32x2_t lo = lds_read_tr16(st + bt_rd[nb] + kk * 16 * 512);
+        const u32x2_t hi = lds_read_tr16(st + bt_rd[nb] + kk * 16 * 512 + 4 * 512);
+        bfr[nb] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+      }
+    }
+  };
+  auto mma = [&](const u32x4_t (&af)[4], const u32x4_t (&bfr)[4]) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) mfma<false>(acc[mb][nb], bfr[nb], af[mb]);
+  };
+
+  if (KT == 0) return;
+  // Earlier vector memory operations of this workgroup (the previous tile's
+  // stores) complete first, so that vmcnt counts only this ring's loads.
+  __builtin_amdgcn_s_waitcnt(0);
+#pragma unroll
+  for (int s = 0; s < kStages; ++s)
+    if (s < KT) issue(s);
+  if (KT >= kStages) wait_vm_lgkm0<(kStages - 1) * 8>();
+  else __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  u32x4_t af[2][4], bfr[2][4];
+  read_frags(af[0], bfr[0], smem, 0);
+  for (int kt = 0; kt + 1 < KT; ++kt) {
+    read_frags(af[1], bfr[1], smem + (kt % kStages) * kStageBytes, 1);
+    mma(af[0], bfr[0]);
+    // stage kt + 1 complete in every thread; all reads of stage kt done
+    asm volatile("" ::: "memory");
+    if (kt + kStages - 1 < KT) wait_vm_lgkm0<(kStages - 2) * 8>();
+    else __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + kStages < KT) issue(kt + kStages);   // refills the buffer of stage kt
+    read_frags(af[0], bfr[0], smem + ((kt + 1) % kStages) * kStageBytes, 0);
+    mma(af[1], bfr[1]);
+  }
+  read_frags(af[1], bfr[1], smem + ((KT - 1) % kStages) * kStageBytes, 1);
+  mma(af[0], bfr[0]);
+  mma(af[1], bfr[1]);
+}
+
 // ----------------------------------------------------------------------------- epilogue helpers
 __device__ inline float load_vec(const void* p, int n, int is_f32) {
   return is_f32 ? ((const float*)p)[n] : bf16_to_f32(((const uint16_t*)p)[n]);
@@ -564,7 +734,8 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
 template <bool kF32, bool kBnk, bool kVec, int kRow, bool kPre>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void gemm_epilogue_kernel(GemmEpilogueParams p) {
-  constexpr int kLdsBytes = 4 * kTileBytes > kLdsEpilogue ? 4 * kTileBytes : kLdsEpilogue;
+  constexpr int kLdsMain = 4 * kTileBytes > kStages * kStageBytes ? 4 * kTileBytes : kStages * kStageBytes;
+  constexpr int kLdsBytes = kLdsMain > kLdsEpilogue ? kLdsMain : kLdsEpilogue;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
   constexpr int BK = 8 * In<kF32>::kChunk;
   constexpr int S = In<kF32>::kSize;
@@ -606,6 +777,17 @@ void gemm_epilogue_kernel(GemmEpilogueParams p) {
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{0};
 
     // ------------------------------------------------------------------ main loop
+    bool streamed = false;
+    if constexpr (!kF32 && kVec) {
+      if (p.K % kStageK == 0) {
+        int tid_t;
+        asm volatile("" : "=v"(tid_t) : "0"((int)threadIdx.x));
+        mainloop_stream<kBnk>(acc, p, smem, m0, n0, tid_t);
+        __syncthreads();   // the epilogue reuses the LDS ring
+        streamed = true;
+      }
+    }
+    if (!streamed) {
     u32x4_t ra[8], rb[8];
     // per-thread byte offsets at k = 0 and the per-k-tile steps
     const uint32_t a_off0 = ((uint32_t)(m0 + (tid >> 3)) * p.lda + (uint32_t)((tid & 7) * In<kF32>::kChunk)) * S;
@@ -672,6 +854,7 @@ void gemm_epilogue_kernel(GemmEpilogueParams p) {
           for (int nb = 0; nb < 4; ++nb) mfma<kF32>(acc[mb][nb], bfr[kk & 1][nb], af[kk & 1][mb]);
       }
       __syncthreads();
+    }
     }
 
     // ------------------------------------------------------------------ epilogue

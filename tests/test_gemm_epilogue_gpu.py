@@ -134,6 +134,20 @@ def test_b_nk_layout(row_op):
     P.assert_close(P.gpu_to_f64(C), R, P.REL_F_BF16, P.MAX_ABS_BF16, f"B [N,K] {row_op}")
 
 
+@pytest.mark.parametrize("b_is_nk", [False, True])
+@pytest.mark.parametrize("K", [32, 40, 96, 128, 160, 264, 1056])
+def test_k_depths_both_layouts(K, b_is_nk):
+    # K a multiple of 32: operands stream through the LDS stage ring (1, 3, 4, 5
+    # and 33 stages: fewer, as many and more than the ring holds); K = 40 and
+    # 264 (multiples of 8 only) take the register-staged loop. M = 300 leaves a
+    # ragged last row strip.
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=7, M=300, N=512, K=K)
+    B = dev["B"].t().contiguous() if b_is_nk else dev["B"]
+    R = oracle_of(w, ref)
+    C = run(dev["A"], B, torch.float32, b_is_nk=b_is_nk, **epi_of(w, dev))
+    P.assert_close(P.gpu_to_f64(C), R, P.REL_F_BF16, P.MAX_ABS_BF16, f"K={K} nk={b_is_nk}")
+
+
 def test_fp32_residual_unaligned_ld():
     w, dev, ref = P.inputs("c3_gemm_residual_rmsnorm", seed=5, M=64, N=512, K=128)
     R32 = torch.randn(64, 520, device="cuda")[:, :512]      # fp32 residual, ld 520

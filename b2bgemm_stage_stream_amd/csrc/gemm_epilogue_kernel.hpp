@@ -192,8 +192,9 @@ __device__ inline void mfma(f32x16_t& acc, const u32x4_t& src0, const u32x4_t& s
 // ----------------------------------------------------------------------------- bf16 streaming main loop
 // bf16 operands, whole 16-byte accesses and K a multiple of 32: the operands go
 // straight from memory into LDS (buffer_load_dwordx4 ... lds, no VGPR staging)
-// through a ring of kStages stages of 32 k each, so the loads of a stage are
-// issued about kStages - 1.5 stages before the MFMAs consume it.
+// through a ring of kStages stages of 32 k each; the loads of a stage are
+// issued between kStages - 2 and kStages - 1 iterations before the MFMAs
+// consume it.
 //
 // Stage layout (32 KiB): A [256 m][64 B] then B. B given [N, K] is stored like
 // A ([256 n][64 B]); B given [K, N] stays [32 k][512 B] and the MFMA operand is
@@ -246,18 +247,27 @@ __device__ inline u32x2_t lds_read_tr16(const uint8_t* p) {
 // that the per-lane offsets below are computed per tile instead of being
 // hoisted out of the persistent loop (where they would be spilled and reloaded
 // inside the k loop).
+//
+// Schedule of iteration kt (stage kt in LDS, 32 k = two k16 steps):
+//   phase A: 16 MFMAs of step 0, the fragment reads of step 1, and the four A
+//            loads of stage kt + kStages - 1 (one per 4 MFMAs);
+//   wait until stage kt + 1 has landed, barrier;
+//   phase B: 16 MFMAs of step 1, the fragment reads of step 0 of stage kt + 1,
+//            and the four B loads of stage kt + kStages - 1.
+// Stage kt + kStages - 1 goes into the buffer of stage kt - 1, whose last reads
+// finished before the previous barrier, so the refill of a stage spreads over a
+// whole iteration. Loads of stages past the end use an out-of-range offset
+// (nothing is fetched) so that every iteration issues the same number of loads
+// and the vmcnt thresholds stay constant.
 template <bool kBnk>
 __device__ inline void mainloop_stream(f32x16_t (&acc)[4][4], const GemmEpilogueParams& p, uint8_t* smem,
-                                       int m0, int n0, int tid) {
+                                        int m0, int n0, int tid) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1, h = lane >> 5, r32 = lane & 31;
   const int KT = p.K / kStageK;
   const u32x4_t rsA = rsrc_words(p.A, p.a_bytes), rsB = rsrc_words(p.B, p.b_bytes);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)smem;
-
-  // Global byte offsets (stage 0) of this thread's four A and four B pieces.
-  // Load i of wave w fills LDS block q = 4w + i (1 KiB).
   uint32_t ga[4], gb[4];
   {
     const int ra = lane >> 2, ca = (lane & 3) ^ swz64(lane >> 2);
@@ -276,24 +286,19 @@ __device__ inline void mainloop_stream(f32x16_t (&acc)[4][4], const GemmEpilogue
   }
   const uint32_t a_step = kStageK * 2u;
   const uint32_t b_step = kBnk ? kStageK * 2u : (uint32_t)kStageK * p.ldb * 2u;
-  auto issue = [&](int kt) {
+  // load j (0..3 A, 4..7 B) of stage s; stages past the end read out of range
+  auto dma = [&](int s, int j) {
     const uint32_t st = (uint32_t)__builtin_amdgcn_readfirstlane(
-        (int)(lds0 + (uint32_t)((kt % kStages) * kStageBytes + wave * 4096)));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lds_dma16(st + i * 1024, rsA, ga[i] + (uint32_t)kt * a_step);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lds_dma16(st + kStageB + i * 1024, rsB, gb[i] + (uint32_t)kt * b_step);
+        (int)(lds0 + (uint32_t)((s % kStages) * kStageBytes + wave * 4096)));
+    const bool ok = s < KT;
+    if (j < 4) lds_dma16(st + j * 1024, rsA, ok ? ga[j] + (uint32_t)s * a_step : kOutOfRange);
+    else lds_dma16(st + kStageB + (j - 4) * 1024, rsB, ok ? gb[j - 4] + (uint32_t)s * b_step : kOutOfRange);
   };
-
-  // Per-lane LDS read offsets within a stage. A (and B [N, K]): row r of the
-  // wave's quarter, logical chunk 2 kk + h.
   const int sa = swz64(r32);
   const uint32_t a_rd[2] = {(uint32_t)((wm * 128 + r32) * 64 + 16 * ((0 + h) ^ sa)),
                             (uint32_t)((wm * 128 + r32) * 64 + 16 * ((2 + h) ^ sa))};
   const uint32_t bn_rd[2] = {(uint32_t)(kStageB + (wn * 128 + r32) * 64 + 16 * ((0 + h) ^ sa)),
                              (uint32_t)(kStageB + (wn * 128 + r32) * 64 + 16 * ((2 + h) ^ sa))};
-  // B [K, N], transposed reads: lane = 16 g + i reads row kk*16 + 8(g>>1) +
-  // 4 half + i/4, columns wn*128 + nb*32 + 16(g&1) + 4(i&3) .. +3.
   uint32_t bt_rd[4];
   {
     const int g = lane >> 4, i = lane & 15;
@@ -305,58 +310,74 @@ __device__ inline void mainloop_stream(f32x16_t (&acc)[4][4], const GemmEpilogue
       bt_rd[nb] = (uint32_t)(kStageB + (8 * (g >> 1) + (i >> 2)) * 512 + 16 * phys + 8 * (i & 1));
     }
   }
-  auto read_frags = [&](u32x4_t (&af)[4], u32x4_t (&bfr)[4], const uint8_t* st, int kk) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) af[i] = *(const u32x4_t*)(st + a_rd[kk] + i * 32 * 64);
+  // fragment reads of one k16 step as a sequence of ops, B first:
+  //  !kBnk: ops 0..7 B halves (nb = op/2), 8..11 A;  kBnk: 0..3 B, 4..7 A
+  constexpr int kOps = kBnk ? 8 : 12;
+  struct Frags { u32x4_t a[4]; u32x2_t blo[4], bhi[4]; u32x4_t b[4]; };
+  auto read_op = [&](Frags& f, const uint8_t* st, int kk, int op) {
     if constexpr (kBnk) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bfr[i] = *(const u32x4_t*)(st + bn_rd[kk] + i * 32 * 64);
+      if (op < 4) f.b[op] = *(const u32x4_t*)(st + bn_rd[kk] + op * 32 * 64);
+      else f.a[op - 4] = *(const u32x4_t*)(st + a_rd[kk] + (op - 4) * 32 * 64);
     } else {
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const u32x2_t lo = lds_read_tr16(st + bt_rd[nb] + kk * 16 * 512);
-        const u32x2_t hi = lds_read_tr16(st + bt_rd[nb] + kk * 16 * 512 + 4 * 512);
-        bfr[nb] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+      if (op < 8) {
+        const int nb = op >> 1;
+        const uint8_t* q = st + bt_rd[nb] + kk * 16 * 512 + (op & 1) * 4 * 512;
+        if (op & 1) f.bhi[nb] = lds_read_tr16(q); else f.blo[nb] = lds_read_tr16(q);
+      } else {
+        f.a[op - 8] = *(const u32x4_t*)(st + a_rd[kk] + (op - 8) * 32 * 64);
       }
     }
   };
-  auto mma = [&](const u32x4_t (&af)[4], const u32x4_t (&bfr)[4]) {
+  auto bfrag = [&](const Frags& f, int nb) -> u32x4_t {
+    if constexpr (kBnk) return f.b[nb];
+    else return u32x4_t{f.blo[nb][0], f.blo[nb][1], f.bhi[nb][0], f.bhi[nb][1]};
+  };
+  // one phase: 16 MFMAs on `use`, the kOps reads of `nxt` (if st_rd) and 4 DMAs
+  auto phase = [&](auto rd, const Frags& use, Frags& nxt, const uint8_t* st_rd, int kk_rd, int s_dma, int j0) {
+    constexpr bool kRead = decltype(rd)::value;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int g = 0; g < 4; ++g) {
+      dma(s_dma, j0 + g);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) mfma<false>(acc[mb][nb], bfr[nb], af[mb]);
+      for (int nb = 0; nb < 4; ++nb) {
+        mfma<false>(acc[g][nb], bfrag(use, nb), use.a[g]);
+        constexpr int per = kOps / 4;
+        if (kRead && nb < per) read_op(nxt, st_rd, kk_rd, g * per + nb);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   if (KT == 0) return;
-  // Earlier vector memory operations of this workgroup (the previous tile's
-  // stores) complete first, so that vmcnt counts only this ring's loads.
   __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
-  for (int s = 0; s < kStages; ++s)
-    if (s < KT) issue(s);
-  if (KT >= kStages) wait_vm_lgkm0<(kStages - 1) * 8>();
-  else __builtin_amdgcn_s_waitcnt(0);
+  for (int s = 0; s < kStages - 1; ++s)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dma(s, j);
+  wait_vm_lgkm0<(kStages - 2) * 8>();
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 
-  u32x4_t af[2][4], bfr[2][4];
-  read_frags(af[0], bfr[0], smem, 0);
+  Frags f0, f1;
+#pragma unroll
+  for (int op = 0; op < kOps; ++op) read_op(f0, smem, 0, op);
   for (int kt = 0; kt + 1 < KT; ++kt) {
-    read_frags(af[1], bfr[1], smem + (kt % kStages) * kStageBytes, 1);
-    mma(af[0], bfr[0]);
-    // stage kt + 1 complete in every thread; all reads of stage kt done
+    // phase A: MFMAs of (kt, k16 step 0); reads of (kt, step 1); A loads of stage kt + kStages - 1
+    phase(std::true_type{}, f0, f1, smem + (kt % kStages) * kStageBytes, 1, kt + kStages - 1, 0);
     asm volatile("" ::: "memory");
-    if (kt + kStages - 1 < KT) wait_vm_lgkm0<(kStages - 2) * 8>();
-    else __builtin_amdgcn_s_waitcnt(0);
+    wait_vm_lgkm0<(kStages - 3) * 8 + 4>();     // stage kt + 1 complete
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (kt + kStages < KT) issue(kt + kStages);   // refills the buffer of stage kt
-    read_frags(af[0], bfr[0], smem + ((kt + 1) % kStages) * kStageBytes, 0);
-    mma(af[1], bfr[1]);
+    // phase B: MFMAs of (kt, step 1); reads of (kt + 1, step 0); B loads of stage kt + kStages - 1
+    phase(std::true_type{}, f1, f0, smem + ((kt + 1) % kStages) * kStageBytes, 0, kt + kStages - 1, 4);
   }
-  read_frags(af[1], bfr[1], smem + ((KT - 1) % kStages) * kStageBytes, 1);
-  mma(af[0], bfr[0]);
-  mma(af[1], bfr[1]);
+  {
+    const int kt = KT - 1;
+    phase(std::true_type{}, f0, f1, smem + (kt % kStages) * kStageBytes, 1, kt + kStages - 1, 0);
+    phase(std::false_type{}, f1, f0, smem, 0, kt + kStages - 1, 4);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
 }
 
 // ----------------------------------------------------------------------------- epilogue helpers

@@ -393,20 +393,6 @@ __device__ inline void publish(uint64_t* slot, float v, uint32_t tag) {
   __hip_atomic_store(slot, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Bounded wait for a peer's word; on timeout records it and returns 0.
-__device__ inline float wait_for(const uint64_t* slot, uint32_t tag, uint64_t t0, uint64_t limit,
-                                 bool& timed_out) {
-  for (;;) {
-    const uint64_t w = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((uint32_t)(w >> 32) == tag) return __uint_as_float((uint32_t)w);
-    if (timed_out || wall_clock64() - t0 > limit) {
-      timed_out = true;
-      return 0.0f;
-    }
-    __builtin_amdgcn_s_sleep(2);
-  }
-}
-
 }  // namespace
 
 // ----------------------------------------------------------------------------- epilogue
@@ -648,40 +634,71 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
       if (p.ws_hdr != nullptr && row_ok) {
         uint64_t* slots = p.ws_slots + (size_t)strip * p.tiles_n * 512 + 2 * ml;
         publish(slots + (size_t)tn * 512, a, tag);
-        publish(slots + (size_t)tn * 512 + 1, b, tag);
+        if constexpr (ROW != 3) publish(slots + (size_t)tn * 512 + 1, b, tag);
         const uint64_t t0 = wall_clock64();
-        if constexpr (ROW == 1) {
-          float M = -INFINITY, S = 0.0f;
-          for (int tt = 0; tt < p.tiles_n; ++tt) {
-            float ma = a, sb = b;
-            if (tt != tn) {
-              ma = wait_for(slots + (size_t)tt * 512, tag, t0, p.spin_ticks, timed_out);
-              sb = wait_for(slots + (size_t)tt * 512 + 1, tag, t0, p.spin_ticks, timed_out);
-            }
-            const float Mn = fmaxf(M, ma);
-            S = S * fast_exp2((M - Mn) * kLog2e) + sb * fast_exp2((ma - Mn) * kLog2e);
-            M = Mn;
+        // The peers' words are fetched 8 column tiles at a time with all loads
+        // in flight together, and the words not yet published are polled again
+        // together. The merge then runs in tile order, so every workgroup of
+        // the strip computes bit-identical statistics.
+        float ra = 0.0f, rb = 0.0f, rn = 0.0f;
+        if constexpr (ROW == 1) ra = -INFINITY;
+        for (int tb = 0; tb < p.tiles_n; tb += 8) {
+          float va[8], vb[8];
+          uint32_t need = 0;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            va[j] = a;
+            vb[j] = b;
+            if (tb + j < p.tiles_n && tb + j != tn) need |= 1u << j;
           }
-          a = M;
-          b = S;
-        } else if constexpr (ROW == 2) {
-          float n = 0.0f, mean = 0.0f, m2 = 0.0f;
-          for (int tt = 0; tt < p.tiles_n; ++tt) {
-            float ma = a, mq = b;
-            if (tt != tn) {
-              ma = wait_for(slots + (size_t)tt * 512, tag, t0, p.spin_ticks, timed_out);
-              mq = wait_for(slots + (size_t)tt * 512 + 1, tag, t0, p.spin_ticks, timed_out);
+          while (need) {
+            uint64_t wa[8], wb[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              wa[j] = wb[j] = 0;
+              if (need & (1u << j)) {
+                wa[j] = __hip_atomic_load(slots + (size_t)(tb + j) * 512, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if constexpr (ROW != 3)
+                  wb[j] = __hip_atomic_load(slots + (size_t)(tb + j) * 512 + 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+              }
             }
-            chan_merge(n, mean, m2, (float)min(kGemmBN, p.N - tt * kGemmBN), ma, mq);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const bool ok = (uint32_t)(wa[j] >> 32) == tag && (ROW == 3 || (uint32_t)(wb[j] >> 32) == tag);
+              if ((need & (1u << j)) && ok) {
+                va[j] = __uint_as_float((uint32_t)wa[j]);
+                vb[j] = __uint_as_float((uint32_t)wb[j]);
+                need &= ~(1u << j);
+              }
+            }
+            if (!need) break;
+            if (timed_out || wall_clock64() - t0 > p.spin_ticks) {   // recorded; the values are not used
+              timed_out = true;
+#pragma unroll
+              for (int j = 0; j < 8; ++j)
+                if (need & (1u << j)) va[j] = vb[j] = 0.0f;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(2);
           }
-          a = mean;
-          b = m2;
-        } else {
-          float s = 0.0f;
-          for (int tt = 0; tt < p.tiles_n; ++tt)
-            s += (tt == tn) ? a : wait_for(slots + (size_t)tt * 512, tag, t0, p.spin_ticks, timed_out);
-          a = s;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int tt = tb + j;
+            if (tt >= p.tiles_n) break;
+            if constexpr (ROW == 1) {
+              const float Mn = fmaxf(ra, va[j]);
+              rb = rb * fast_exp2((ra - Mn) * kLog2e) + vb[j] * fast_exp2((va[j] - Mn) * kLog2e);
+              ra = Mn;
+            } else if constexpr (ROW == 2) {
+              chan_merge(rn, ra, rb, (float)min(kGemmBN, p.N - tt * kGemmBN), va[j], vb[j]);
+            } else {
+              ra += va[j];
+            }
+          }
         }
+        a = ra;
+        b = rb;
       }
       float2 st;
       if constexpr (ROW == 1) st = make_float2(a * kLog2e, 1.0f / b);

@@ -411,11 +411,14 @@ __device__ inline void publish(uint64_t* slot, float v, uint32_t tag) {
 // accumulators live in VGPRs at a time.
 //
 // LDS use after the main loop (the operand tiles are dead by then):
-constexpr int kResStride = 528;                  // bytes per staged residual row (256 bf16 + 16 B pad)
-constexpr int kOffVec = 256 * kResStride;        // bias, gamma, beta: [3][256] f32
+// the small arrays come first so that every per-group access is a base
+// register plus an immediate offset below 64 KiB
+constexpr int kOffVec = 0;                       // bias, gamma, beta: [3][256] f32
 constexpr int kOffWpart = kOffVec + 3 * 1024;    // [2][256] float2: partial per wave column
 constexpr int kOffRstat = kOffWpart + 4096;      // [256] float2: final row statistics
-constexpr int kLdsEpilogue = kOffRstat + 2048;
+constexpr int kOffRes = kOffRstat + 2048;        // staged residual tile
+constexpr int kResStride = 528;                  // bytes per staged residual row (256 bf16 + 16 B pad)
+constexpr int kLdsEpilogue = kOffRes + 256 * kResStride;
 
 // Four accumulators of block `blk`, registers 4q..4q+3, read into VGPRs after
 // `tok` is available.
@@ -450,8 +453,8 @@ __device__ inline float2 halves(float v) {
 // kPre: a bias or a residual is present.
 template <int ROW, bool kFast, bool kPre>
 __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueParams& p, uint8_t* smem,
-                                int strip, int tn, uint32_t tag, bool& timed_out) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+                                int strip, int tn, uint32_t tag, bool& timed_out, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, r32 = lane & 31;
   const int m0 = strip * kGemmBM, n0 = tn * kGemmBN;
@@ -486,7 +489,7 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int row = (tid >> 5) + 8 * (8 * b + i);
-        *(u32x4_t*)(smem + row * kResStride + c * 16) = v[i];
+        *(u32x4_t*)(smem + kOffRes + row * kResStride + c * 16) = v[i];
       }
     }
   }
@@ -495,18 +498,24 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
   const float alpha = p.alpha;
   const float floor_v = p.act == 1 ? 0.0f : -INFINITY;   // ReLU as max with a floor
   const int ncol = p.N - (n0 + wn * 128 + 4 * h);          // element (c = nb*32 + 8q + e) valid iff c < ncol
+  // Per-lane LDS bases: every per-group access below is one of these plus a
+  // compile-time offset (below 64 KiB, so it folds into the instruction).
+  const float* vb_lane = vbias + wn * 128 + 4 * h;
+  const float* vg_lane = vgamma + wn * 128 + 4 * h;
+  const float* ve_lane = vbeta + wn * 128 + 4 * h;
+  uint8_t* res_lane = smem + kOffRes + (wm * 128 + r32) * kResStride + (wn * 128 + 4 * h) * 2;
 
   // x for the 4 columns of group (mb, nb, q); tok orders the accumulator reads
   auto xgroup = [&](int mb, int nb, auto qc, float tok, float (&x)[4]) {
     constexpr int q = decltype(qc)::value;
     const int nl = wn * 128 + nb * 32 + 8 * q + 4 * h;
     f32x4_t bv = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (kPre) bv = *(const f32x4_t*)(vbias + nl);
+    if constexpr (kPre) bv = *(const f32x4_t*)(vb_lane + nb * 32 + 8 * q);
     float rv[4] = {0.f, 0.f, 0.f, 0.f};
     if (kPre && has_res) {
       const int ml = wm * 128 + mb * 32 + r32;
       if constexpr (kFast) {
-        const u32x2_t w = *(const u32x2_t*)(smem + ml * kResStride + nl * 2);
+        const u32x2_t w = *(const u32x2_t*)(res_lane + mb * 32 * kResStride + (nb * 32 + 8 * q) * 2);
         rv[0] = bf16lo(w[0]); rv[1] = bf16hi(w[0]); rv[2] = bf16lo(w[1]); rv[3] = bf16hi(w[1]);
       } else {
         const uint32_t rs = p.res_f32 ? 4 : 2;
@@ -521,7 +530,10 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
     float v[4];
     acc_read4<q>(acc[mb][nb], tok, v);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = fmaxf(__builtin_fmaf(alpha, v[e], bv[e]) + rv[e], floor_v);
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (kPre) x[e] = fmaxf(__builtin_fmaf(alpha, v[e], bv[e]) + rv[e], floor_v);
+      else x[e] = fmaxf(alpha * v[e], floor_v);
+    }
   };
   using Q0 = std::integral_constant<int, 0>;
   using Q1 = std::integral_constant<int, 1>;
@@ -725,8 +737,8 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
         float x[4], y[4];
         xgroup(mb, nb, qc, tok, x);
         if constexpr (ROW == 2 || ROW == 3) {
-          const f32x4_t g = *(const f32x4_t*)(vgamma + nl);
-          const f32x4_t be = *(const f32x4_t*)(vbeta + nl);
+          const f32x4_t g = *(const f32x4_t*)(vg_lane + c);
+          const f32x4_t be = *(const f32x4_t*)(ve_lane + c);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             if constexpr (ROW == 2) y[e] = __builtin_fmaf((x[e] - st.x) * st.y, g[e], be[e]);
@@ -751,8 +763,10 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
           }
         } else {
           if constexpr (kFast) {
+            // staged in LDS (over this element's staged residual, which this
+            // lane has just read) and written out by whole rows below
             const u32x2_t v = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-            buf_store_b64(v, rsC, rowoff + (uint32_t)c * 2);
+            *(u32x2_t*)(res_lane + mb * 32 * kResStride + c * 2) = v;
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -762,8 +776,23 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
       });
     }
   };
-  if (p.c_f32) store_pass(std::true_type{});
-  else store_pass(std::false_type{});
+  if (p.c_f32) {
+    store_pass(std::true_type{});
+  } else {
+    store_pass(std::false_type{});
+    if constexpr (kFast) {
+      // bf16 tile [256][256] from LDS to C: each wave store covers two whole
+      // 512-byte row segments; rows >= M fall outside the buffer and are dropped
+      __syncthreads();
+      const int c = tid & 31;
+#pragma unroll 8
+      for (int i = 0; i < 32; ++i) {
+        const int row = (tid >> 5) + 8 * i;
+        const u32x4_t v = *(const u32x4_t*)(smem + kOffRes + row * kResStride + c * 16);
+        buf_store_b128(v, rsC, ((uint32_t)(m0 + row) * p.ldc + (uint32_t)(n0 + c * 8)) * 2u);
+      }
+    }
+  }
 }
 
 // kVec (fast path): vector loads, N a multiple of 256, bf16 or no residual; the
@@ -815,11 +844,14 @@ void gemm_epilogue_kernel(GemmEpilogueParams p) {
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{0};
 
     // ------------------------------------------------------------------ main loop
+    // threadIdx.x through an opaque copy per tile: per-lane offsets derived
+    // from it are recomputed per tile rather than hoisted out of the
+    // persistent loop and spilled
+    int tid_t;
+    asm volatile("" : "=v"(tid_t) : "0"((int)threadIdx.x));
     bool streamed = false;
     if constexpr (!kF32 && kVec) {
       if (p.K % kStageK == 0) {
-        int tid_t;
-        asm volatile("" : "=v"(tid_t) : "0"((int)threadIdx.x));
         mainloop_stream<kBnk>(acc, p, smem, m0, n0, tid_t);
         __syncthreads();   // the epilogue reuses the LDS ring
         streamed = true;
@@ -897,13 +929,13 @@ void gemm_epilogue_kernel(GemmEpilogueParams p) {
 
     // ------------------------------------------------------------------ epilogue
     if constexpr (kVec) {
-      epilogue<kRow, true, kPre>(acc, p, smem, strip, tn, tag, timed_out);
+      epilogue<kRow, true, kPre>(acc, p, smem, strip, tn, tag, timed_out, tid_t);
     } else {
       switch (p.row_op) {
-        case 1: epilogue<1, false, true>(acc, p, smem, strip, tn, tag, timed_out); break;
-        case 2: epilogue<2, false, true>(acc, p, smem, strip, tn, tag, timed_out); break;
-        case 3: epilogue<3, false, true>(acc, p, smem, strip, tn, tag, timed_out); break;
-        default: epilogue<0, false, true>(acc, p, smem, strip, tn, tag, timed_out); break;
+        case 1: epilogue<1, false, true>(acc, p, smem, strip, tn, tag, timed_out, tid_t); break;
+        case 2: epilogue<2, false, true>(acc, p, smem, strip, tn, tag, timed_out, tid_t); break;
+        case 3: epilogue<3, false, true>(acc, p, smem, strip, tn, tag, timed_out, tid_t); break;
+        default: epilogue<0, false, true>(acc, p, smem, strip, tn, tag, timed_out, tid_t); break;
       }
     }
     __syncthreads();   // the next tile's operand stores reuse this LDS

@@ -451,7 +451,8 @@ __device__ inline float2 halves(float v) {
 // kFast: N is a multiple of 256, 16-byte accesses are allowed and the residual
 // (if any) is bf16; otherwise every column is masked against N.
 // kPre: a bias or a residual is present.
-template <int ROW, bool kFast, bool kPre>
+// kId: alpha == 1 and no activation, so the elementwise stage is P (+ bias + R).
+template <int ROW, bool kFast, bool kPre, bool kId>
 __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueParams& p, uint8_t* smem,
                                 int strip, int tn, uint32_t tag, bool& timed_out, int tid) {
   const int lane = tid & 63, wave = tid >> 6;
@@ -506,11 +507,14 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
   uint8_t* res_lane = smem + kOffRes + (wm * 128 + r32) * kResStride + (wn * 128 + 4 * h) * 2;
 
   // x for the 4 columns of group (mb, nb, q); tok orders the accumulator reads
-  auto xgroup = [&](int mb, int nb, auto qc, float tok, float (&x)[4]) {
+  // bias of the 4 columns of group (nb, q)
+  auto bias4 = [&](int nb, int q) -> f32x4_t {
+    if constexpr (kPre) return *(const f32x4_t*)(vb_lane + nb * 32 + 8 * q);
+    else return f32x4_t{0.f, 0.f, 0.f, 0.f};
+  };
+  auto xgroup = [&](int mb, int nb, auto qc, const f32x4_t& bv, float tok, float (&x)[4]) {
     constexpr int q = decltype(qc)::value;
     const int nl = wn * 128 + nb * 32 + 8 * q + 4 * h;
-    f32x4_t bv = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (kPre) bv = *(const f32x4_t*)(vb_lane + nb * 32 + 8 * q);
     float rv[4] = {0.f, 0.f, 0.f, 0.f};
     if (kPre && has_res) {
       const int ml = wm * 128 + mb * 32 + r32;
@@ -531,7 +535,9 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
     acc_read4<q>(acc[mb][nb], tok, v);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if constexpr (kPre) x[e] = fmaxf(__builtin_fmaf(alpha, v[e], bv[e]) + rv[e], floor_v);
+      if constexpr (kId && kPre) x[e] = (v[e] + bv[e]) + rv[e];
+      else if constexpr (kId) x[e] = v[e];
+      else if constexpr (kPre) x[e] = fmaxf(__builtin_fmaf(alpha, v[e], bv[e]) + rv[e], floor_v);
       else x[e] = fmaxf(alpha * v[e], floor_v);
     }
   };
@@ -557,7 +563,7 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
         float mx = -INFINITY;
         for_groups([&](int nb, auto qc) {
           float x[4];
-          xgroup(mb, nb, qc, tok, x);
+          xgroup(mb, nb, qc, bias4(nb, decltype(qc)::value), tok, x);
 #pragma unroll
           for (int e = 0; e < 4; ++e) mx = valid(nb, decltype(qc)::value, e) ? fmaxf(mx, x[e]) : mx;
           tok = mx;
@@ -567,7 +573,7 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
         float s = 0.0f;
         for_groups([&](int nb, auto qc) {
           float x[4];
-          xgroup(mb, nb, qc, tok, x);
+          xgroup(mb, nb, qc, bias4(nb, decltype(qc)::value), tok, x);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float ex = fast_exp2(__builtin_fmaf(x[e], kLog2e, -mxs));
@@ -583,7 +589,7 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
         bool first = true;
         for_groups([&](int nb, auto qc) {
           float x[4];
-          xgroup(mb, nb, qc, tok, x);
+          xgroup(mb, nb, qc, bias4(nb, decltype(qc)::value), tok, x);
           if (first) { K = valid(nb, 0, 0) ? x[0] : 0.0f; first = false; }
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -608,7 +614,7 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
         float s2 = 0.0f;
         for_groups([&](int nb, auto qc) {
           float x[4];
-          xgroup(mb, nb, qc, tok, x);
+          xgroup(mb, nb, qc, bias4(nb, decltype(qc)::value), tok, x);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float xx = valid(nb, decltype(qc)::value, e) ? x[e] : 0.0f;
@@ -722,44 +728,46 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
   }
 
   // ---- stage 2: normalise, affine, cast, store
+  // Column group outer, row block inner: the per-column vectors are read
+  // from LDS once per group and reused by the 4 row blocks.
   auto store_pass = [&](auto f32c) {
     constexpr bool kOutF32 = decltype(f32c)::value;
     constexpr uint32_t es = kOutF32 ? 4u : 2u;
+    float2 st[4];
+    uint32_t rowoff[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const int ml = wm * 128 + mb * 32 + r32;
-      const float2 st = ROW != 0 ? rstat[ml] : make_float2(0.f, 0.f);
-      const uint32_t rowoff = ((uint32_t)(m0 + ml) * p.ldc + (uint32_t)(n0 + wn * 128 + 4 * h)) * es;
-      for_groups([&](int nb, auto qc) {
-        constexpr int q = decltype(qc)::value;
-        const int c = nb * 32 + 8 * q;
-        const int nl = wn * 128 + c + 4 * h;
+      st[mb] = ROW != 0 ? rstat[ml] : make_float2(0.f, 0.f);
+      rowoff[mb] = ((uint32_t)(m0 + ml) * p.ldc + (uint32_t)(n0 + wn * 128 + 4 * h)) * es;
+    }
+    for_groups([&](int nb, auto qc) {
+      constexpr int q = decltype(qc)::value;
+      const int c = nb * 32 + 8 * q;
+      const f32x4_t bv = bias4(nb, q);
+      f32x4_t g = {1.f, 1.f, 1.f, 1.f}, be = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (ROW == 2 || ROW == 3) g = *(const f32x4_t*)(vg_lane + c);
+      if constexpr (ROW == 2) be = *(const f32x4_t*)(ve_lane + c);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
         float x[4], y[4];
-        xgroup(mb, nb, qc, tok, x);
-        if constexpr (ROW == 2 || ROW == 3) {
-          const f32x4_t g = *(const f32x4_t*)(vg_lane + c);
-          const f32x4_t be = *(const f32x4_t*)(ve_lane + c);
+        xgroup(mb, nb, qc, bv, tok, x);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if constexpr (ROW == 2) y[e] = __builtin_fmaf((x[e] - st.x) * st.y, g[e], be[e]);
-            else y[e] = x[e] * st.x * g[e];
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if constexpr (ROW == 1) y[e] = fast_exp2(__builtin_fmaf(x[e], kLog2e, -st.x)) * st.y;
-            else y[e] = x[e];
-          }
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (ROW == 2) y[e] = __builtin_fmaf((x[e] - st[mb].x) * st[mb].y, g[e], be[e]);
+          else if constexpr (ROW == 3) y[e] = x[e] * st[mb].x * g[e];
+          else if constexpr (ROW == 1) y[e] = fast_exp2(__builtin_fmaf(x[e], kLog2e, -st[mb].x)) * st[mb].y;
+          else y[e] = x[e];
         }
         tok = y[3];
         if constexpr (kOutF32) {
           if constexpr (kFast) {
             const u32x4_t v = {__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3])};
-            buf_store_b128(v, rsC, rowoff + (uint32_t)c * 4);
+            buf_store_b128(v, rsC, rowoff[mb] + (uint32_t)c * 4);
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              buf_store_b32(__float_as_uint(y[e]), rsC, (c + e < ncol) ? rowoff + (uint32_t)(c + e) * 4 : kOutOfRange);
+              buf_store_b32(__float_as_uint(y[e]), rsC, (c + e < ncol) ? rowoff[mb] + (uint32_t)(c + e) * 4 : kOutOfRange);
           }
         } else {
           if constexpr (kFast) {
@@ -770,11 +778,11 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              buf_store_b16((uint16_t)f32_to_bf16(y[e]), rsC, (c + e < ncol) ? rowoff + (uint32_t)(c + e) * 2 : kOutOfRange);
+              buf_store_b16((uint16_t)f32_to_bf16(y[e]), rsC, (c + e < ncol) ? rowoff[mb] + (uint32_t)(c + e) * 2 : kOutOfRange);
           }
         }
-      });
-    }
+      }
+    });
   };
   if (p.c_f32) {
     store_pass(std::true_type{});
@@ -929,13 +937,14 @@ void gemm_epilogue_kernel(GemmEpilogueParams p) {
 
     // ------------------------------------------------------------------ epilogue
     if constexpr (kVec) {
-      epilogue<kRow, true, kPre>(acc, p, smem, strip, tn, tag, timed_out, tid_t);
+      if (p.alpha == 1.0f && p.act == 0) epilogue<kRow, true, kPre, true>(acc, p, smem, strip, tn, tag, timed_out, tid_t);
+      else epilogue<kRow, true, kPre, false>(acc, p, smem, strip, tn, tag, timed_out, tid_t);
     } else {
       switch (p.row_op) {
-        case 1: epilogue<1, false, true>(acc, p, smem, strip, tn, tag, timed_out, tid_t); break;
-        case 2: epilogue<2, false, true>(acc, p, smem, strip, tn, tag, timed_out, tid_t); break;
-        case 3: epilogue<3, false, true>(acc, p, smem, strip, tn, tag, timed_out, tid_t); break;
-        default: epilogue<0, false, true>(acc, p, smem, strip, tn, tag, timed_out, tid_t); break;
+        case 1: epilogue<1, false, true, false>(acc, p, smem, strip, tn, tag, timed_out, tid_t); break;
+        case 2: epilogue<2, false, true, false>(acc, p, smem, strip, tn, tag, timed_out, tid_t); break;
+        case 3: epilogue<3, false, true, false>(acc, p, smem, strip, tn, tag, timed_out, tid_t); break;
+        default: epilogue<0, false, true, false>(acc, p, smem, strip, tn, tag, timed_out, tid_t); break;
       }
     }
     __syncthreads();   // the next tile's operand stores reuse this LDS

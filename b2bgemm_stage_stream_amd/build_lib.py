@@ -31,7 +31,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 def _units():
     """(source, object, extra defines) for every translation unit."""
     units = []
-    for f in ("api.cpp", "gemm_epilogue_dispatch.hip", "b2b.hip"):
+    for f in ("api.cpp", "gemm_epilogue_dispatch.hip", "b2b.hip", "b2b_stream.hip"):
         units.append((os.path.join(CSRC, f), os.path.join(BUILD, os.path.splitext(f)[0] + ".o"), []))
     for in_f32 in (0, 1):
         for b_nk in (0, 1):

@@ -405,7 +405,8 @@ bool b2b_supported(const B2bParams& p) {
 }
 
 hipError_t launch_b2b(const B2bParams& p, hipStream_t stream) {
-  const void* k = pick(p);
+  const void* ks = b2b_stream_pick(p);
+  const void* k = ks ? ks : pick(p);
   if (!k) return hipErrorNotSupported;
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t e;
@@ -414,7 +415,9 @@ hipError_t launch_b2b(const B2bParams& p, hipStream_t stream) {
   if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, 0)) != hipSuccess) return e;
   const long tiles = (long)p.batch * ((p.M + kBM - 1) / kBM);
   const long cap = (long)(per_cu > 0 ? per_cu : 1) * cus;
-  const int grid = (int)(tiles < cap ? tiles : cap);
+  long g = tiles < cap ? tiles : cap;
+  if (ks && g >= 8) g -= g % 8;   // the streamed kernel maps workgroups to XCDs in groups of 8
+  const int grid = (int)g;
   void* args[] = {(void*)&p};
   return hipLaunchKernel(k, dim3(grid), dim3(kThreads), args, 0, stream);
 }

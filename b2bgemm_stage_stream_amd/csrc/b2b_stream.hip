@@ -1,0 +1,378 @@
+// Back-to-back GEMM for gfx950, exact shapes: O = F(alpha * A.B0 + bias) . B1
+// with K and N in {64, 128} and L a multiple of 64 (bf16 operands).
+//
+// Method: ComFuse review (pith.science review of arXiv 2608.03537), Referee
+// Report major comment 2 (paper Sec. IV-A, Eqs. (2)-(5)) and Fig. 5: S = A.B0 is
+// transformed tile by tile and consumed by the second GEMM from on-chip
+// storage, the contraction over L accumulated segment by segment. One
+// workgroup owns 128 rows of A (4 waves x 32) and walks all of L in 64-wide
+// segments; O stays in registers. The segment arithmetic (operand swap, P
+// packed from the GEMM1 accumulators in the permuted l order, power-of-two
+// online-softmax stabiliser) is the one of the general kernel in b2b.hip.
+//
+// What differs from the general kernel, for speed:
+//  * the B0 and B1 segments go from memory straight into an LDS ring of
+//    kStages segments (buffer_load_dwordx4 ... lds), refilled one segment per
+//    iteration with explicit vmcnt waits; no VGPR staging, no transposes;
+//  * B1 stays [l][n] in LDS and GEMM2 reads B1^T with ds_read_b64_tr_b16;
+//    B0 given [K][L] likewise stays [k][l] and GEMM1 reads it transposed;
+//  * at most 256 registers per lane, so two workgroups share a CU and one
+//    wave's softmax (VALU, exp) overlaps the other's MFMAs;
+//  * with per-batch B0/B1 (attention heads) the row tiles of one batch entry
+//    run on one XCD, so its B0/B1 segments are fetched into that XCD's L2 once;
+//  * B0/B1 shared by the whole batch and no longer than the ring stay
+//    resident in LDS for all the tiles a workgroup processes.
+#include "cf_device.hpp"
+#include "cf_launch.h"
+
+namespace cf {
+namespace {
+
+constexpr int kTBM = 128;     // rows of A per tile
+constexpr int kTLC = 64;      // L segment
+constexpr int kTThreads = 256;
+
+template <int KS, int NB>
+struct TCfg {
+  static constexpr int K = 16 * KS, N = 32 * NB;
+  static constexpr int kB0Bytes = kTLC * K * 2;
+  static constexpr int kB1Bytes = kTLC * N * 2;
+  static constexpr int kStage = kB0Bytes + kB1Bytes;
+  static constexpr int kStages = 4 * kStage <= 80 * 1024 ? 4 : 3 * kStage <= 80 * 1024 ? 3 : 2;
+  static constexpr int kLds = kStages * kStage;
+  static constexpr int kB0Blocks = kB0Bytes / 1024;              // 1 KiB DMA blocks
+  static constexpr int kLoads = kStage / (kTThreads * 16);       // DMA loads per thread per segment
+};
+
+// XOR swizzles of the 16-byte chunks of an LDS row (physical = logical ^ f):
+// conflict free for the access patterns below whether the LDS serves 128 or
+// 256 bytes per cycle.
+__device__ inline int swz_rows128(int r) { return (r & 7) ^ ((r >> 3) & 1); }   // 16-B row reads, 128-B rows
+__device__ inline int swz_rows256(int r) { return r & 15; }                     // 16-B row reads, 256-B rows
+__device__ inline int swz_tr128(int r) { return 2 * (r & 3); }                  // transposed reads, 128-B rows
+__device__ inline int swz_tr256(int r) { return (2 * (r & 3)) ^ (4 * (r & 3)); }  // transposed reads, 256-B rows
+
+}  // namespace
+
+template <int KS, int NB, bool kSoftmax, bool kB0LK>
+__global__ __attribute__((amdgpu_flat_work_group_size(kTThreads, kTThreads), amdgpu_waves_per_eu(2, 2)))
+void b2b_stream_kernel(B2bParams p) {
+  using C = TCfg<KS, NB>;
+  constexpr int NS = C::kStages;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::kLds];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, r32 = lane & 31;
+  const int mtiles = (p.M + kTBM - 1) / kTBM;
+  const int nchunks = p.L / kTLC;
+  const float scale = kSoftmax ? p.alpha * kLog2e : p.alpha;
+  const float floor_v = p.act == 1 ? 0.0f : -INFINITY;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)smem;
+
+  // ---- DMA plan: load i of wave w fills 1 KiB block q = 4 i + w of a stage
+  // (B0 blocks first). Per load: global byte offset at segment 0 (batch entry
+  // base excluded), the per-segment step, and the region.
+  uint32_t goff[C::kLoads], gstep[C::kLoads];
+  bool is_b0[C::kLoads];
+#pragma unroll
+  for (int i = 0; i < C::kLoads; ++i) {
+    const int q = 4 * i + wave;
+    is_b0[i] = q < C::kB0Blocks;
+    if (q < C::kB0Blocks) {
+      if constexpr (kB0LK) {            // rows l of K * 2 bytes
+        constexpr int cpr = C::K / 8, rpb = 1024 / (C::K * 2);
+        const int row = q * rpb + lane / cpr, ph = lane % cpr;
+        const int lg = ph ^ (C::K == 64 ? swz_rows128(row) : swz_rows256(row));
+        goff[i] = ((uint32_t)row * p.ldb0 + (uint32_t)(8 * lg)) * 2u;
+        gstep[i] = (uint32_t)kTLC * p.ldb0 * 2u;
+      } else {                          // rows k of 64 l (128 bytes)
+        const int row = q * 8 + lane / 8, ph = lane % 8;
+        const int lg = ph ^ swz_tr128(row);
+        goff[i] = ((uint32_t)row * p.ldb0 + (uint32_t)(8 * lg)) * 2u;
+        gstep[i] = kTLC * 2u;
+      }
+    } else {                            // B1 rows l of N * 2 bytes
+      constexpr int cpr = C::N / 8, rpb = 1024 / (C::N * 2);
+      const int qb = q - C::kB0Blocks;
+      const int row = qb * rpb + lane / cpr, ph = lane % cpr;
+      const int lg = ph ^ (C::N == 64 ? swz_tr128(row) : swz_tr256(row));
+      goff[i] = ((uint32_t)row * p.ldb1 + (uint32_t)(8 * lg)) * 2u;
+      gstep[i] = (uint32_t)kTLC * p.ldb1 * 2u;
+    }
+  }
+
+  // ---- LDS read offsets (within a stage)
+  // GEMM1 operand B0^T rows l = lb*32 + r32, k-slots 8h..8h+7 of step ks
+  uint32_t b0_rd[kB0LK ? KS : 2];
+  if constexpr (kB0LK) {
+    constexpr int RB = C::K * 2;
+    const int f = C::K == 64 ? swz_rows128(r32) : swz_rows256(r32);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) b0_rd[ks] = (uint32_t)(r32 * RB + 16 * ((2 * ks + h) ^ f));
+  } else {
+    // [k][l]: lane 16g + i reads row ks*16 + 8(g>>1) + 4 half + i/4, columns
+    // lb*32 + 16(g&1) + 4(i&3) .. +3; one base per lb
+    const int g = lane >> 4, i = lane & 15;
+    const int f = swz_tr128(i >> 2);
+    const int c = 2 * (g & 1) + ((i & 3) >> 1);
+#pragma unroll
+    for (int lb = 0; lb < 2; ++lb)
+      b0_rd[lb] = (uint32_t)((8 * (g >> 1) + (i >> 2)) * 128 + 16 * ((4 * lb + c) ^ f) + 8 * (i & 1));
+  }
+  // GEMM2 operand B1^T rows n = nb*32 + (lane & 31), k-slots = l in the
+  // permuted order: half 0 reads rows c16*16 + 4h + 0..3, half 1 rows +8
+  uint32_t b1_rd[NB];
+  {
+    constexpr int RB = C::N * 2;
+    const int g = lane >> 4, i = lane & 15;
+    const int f = C::N == 64 ? swz_tr128(i >> 2) : swz_tr256(i >> 2);
+    const int c = 2 * (g & 1) + ((i & 3) >> 1);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      b1_rd[nb] = (uint32_t)(C::kB0Bytes + (4 * (g >> 1) + (i >> 2)) * RB + 16 * ((4 * nb + c) ^ f) + 8 * (i & 1));
+  }
+
+  auto issue = [&](int s, const u32x4_t& rs0, const u32x4_t& rs1) {
+    const uint32_t st = (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(lds0 + (uint32_t)((s % NS) * C::kStage + wave * 1024)));
+    const bool ok = s < nchunks;
+#pragma unroll
+    for (int i = 0; i < C::kLoads; ++i)
+      lds_dma16(st + i * 4096, is_b0[i] ? rs0 : rs1, ok ? goff[i] + (uint32_t)s * gstep[i] : kOutOfRange);
+  };
+
+  // one segment: GEMM1, F, GEMM2 on stage buffer st
+  auto segment = [&](const uint8_t* st, int lc, const u32x4_t (&af)[KS], f32x16_t (&oacc)[NB], float& cst,
+                     float& lsum) {
+    f32x16_t sacc[2];
+#pragma unroll
+    for (int lb = 0; lb < 2; ++lb) {
+      sacc[lb] = f32x16_t{0};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4_t bf;
+        if constexpr (kB0LK) {
+          bf = *(const u32x4_t*)(st + b0_rd[ks] + lb * 32 * C::K * 2);
+        } else {
+          const u32x2_t lo = lds_read_tr16(st + b0_rd[lb] + ks * 16 * 128);
+          const u32x2_t hi = lds_read_tr16(st + b0_rd[lb] + ks * 16 * 128 + 4 * 128);
+          bf = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        }
+        sacc[lb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bf),
+                                                            __builtin_bit_cast(bf16x8_t, af[ks]), sacc[lb], 0, 0, 0);
+      }
+    }
+    // F: register r of block lb holds l = lc*64 + lb*32 + 8(r>>2) + 4h + (r&3)
+    u32x4_t pf[4];
+    if constexpr (kSoftmax) {
+      // row extreme of S (of alpha*S for the stabiliser): max for alpha >= 0, min otherwise
+      float mx;
+      if (scale >= 0.0f) {
+        mx = -INFINITY;
+#pragma unroll
+        for (int lb = 0; lb < 2; ++lb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[lb][r]);
+        mx = max_halves(mx);
+      } else {
+        mx = INFINITY;
+#pragma unroll
+        for (int lb = 0; lb < 2; ++lb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fminf(mx, sacc[lb][r]);
+        mx = min_halves(mx);
+      }
+      const float cn = fmaxf(cst, ceilf(mx * scale));
+      if (cn > cst && cst != -INFINITY) {
+        const int sh = (int)(cst - cn);          // exact power-of-two rescale
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[nb][r] = __builtin_amdgcn_ldexpf(oacc[nb][r], sh);
+        lsum = __builtin_amdgcn_ldexpf(lsum, sh);
+      }
+      cst = cn;
+#pragma unroll
+      for (int lb = 0; lb < 2; ++lb) {
+        float e[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          e[r] = fast_exp2(__builtin_fmaf(sacc[lb][r], scale, -cn));
+          lsum += e[r];
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) pf[2 * lb + c][q] = pack_bf16x2(e[8 * c + 2 * q], e[8 * c + 2 * q + 1]);
+      }
+    } else {
+#pragma unroll
+      for (int lb = 0; lb < 2; ++lb) {
+        float x[16];
+        if (p.bias) {
+          const int lbase = lc * kTLC + lb * 32 + 4 * h;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int l = lbase + 8 * (r >> 2) + (r & 3);
+            const float bv = p.bias_f32 ? ((const float*)p.bias)[l] : bf16_to_f32(((const uint16_t*)p.bias)[l]);
+            x[r] = fmaxf(__builtin_fmaf(sacc[lb][r], scale, bv), floor_v);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) x[r] = fmaxf(sacc[lb][r] * scale, floor_v);
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) pf[2 * lb + c][q] = pack_bf16x2(x[8 * c + 2 * q], x[8 * c + 2 * q + 1]);
+      }
+    }
+    // GEMM2 over the four 16-wide slices of the segment
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const u32x2_t lo = lds_read_tr16(st + b1_rd[nb] + c * 16 * C::N * 2);
+        const u32x2_t hi = lds_read_tr16(st + b1_rd[nb] + c * 16 * C::N * 2 + 8 * C::N * 2);
+        const u32x4_t vf = {lo[0], lo[1], hi[0], hi[1]};
+        oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf),
+                                                            __builtin_bit_cast(bf16x8_t, pf[c]), oacc[nb], 0, 0, 0);
+      }
+  };
+
+  // ---- B0/B1 shared by the batch and no longer than the ring: load once
+  const bool shared = p.batch == 1 || (p.sb0 == 0 && p.sb1 == 0);
+  const bool resident = shared && nchunks <= NS;
+  if (resident) {
+    const u32x4_t rs0 = rsrc_words(p.B0, (uint32_t)((size_t)(kB0LK ? p.L : C::K) * p.ldb0 * 2));
+    const u32x4_t rs1 = rsrc_words(p.B1, (uint32_t)((size_t)p.L * p.ldb1 * 2));
+#pragma unroll
+    for (int s = 0; s < NS; ++s) issue(s, rs0, rs1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+
+  // ---- tile schedule: with per-batch B0/B1 and a batch that is a multiple of
+  // 8, batch entry b is handled by the workgroups of XCD b % 8 (workgroup w
+  // runs on XCD w % 8); otherwise tiles go round robin
+  const int G = (int)gridDim.x;
+  const bool by_xcd = !shared && mtiles > 1 && (p.batch & 7) == 0 && (G & 7) == 0;
+  const int x = (int)blockIdx.x & 7;
+  const int per_x = by_xcd ? (x < p.batch ? (p.batch - x + 7) / 8 : 0) * mtiles : p.batch * mtiles;
+  const int e0 = by_xcd ? (int)blockIdx.x >> 3 : (int)blockIdx.x;
+  const int estep = by_xcd ? G >> 3 : G;
+
+  for (int e = e0; e < per_x; e += estep) {
+    int b, mt;
+    if (by_xcd) {
+      b = x + 8 * (e / mtiles);
+      mt = e % mtiles;
+    } else {
+      b = e / mtiles;
+      mt = e % mtiles;
+    }
+    const int m0 = mt * kTBM;
+    const uint16_t* Ab = (const uint16_t*)p.A + (size_t)b * p.sa;
+    const __amdgpu_buffer_rsrc_t rsA = make_rsrc(Ab, (uint32_t)((size_t)p.M * p.lda * 2));
+    const u32x4_t rs0 = rsrc_words((const uint16_t*)p.B0 + (size_t)b * p.sb0,
+                                   (uint32_t)((size_t)(kB0LK ? p.L : C::K) * p.ldb0 * 2));
+    const u32x4_t rs1 = rsrc_words((const uint16_t*)p.B1 + (size_t)b * p.sb1, (uint32_t)((size_t)p.L * p.ldb1 * 2));
+
+    if (!resident) {
+#pragma unroll
+      for (int s = 0; s < NS - 1; ++s) issue(s, rs0, rs1);
+    }
+    // A fragments of this wave's 32 rows (rows >= M read as zero)
+    u32x4_t af[KS];
+    {
+      const uint32_t row = (uint32_t)(m0 + wave * 32 + r32);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) af[ks] = buf_load_b128(rsA, (row * p.lda + (uint32_t)(ks * 16 + 8 * h)) * 2);
+    }
+    // One full wait for the A fragments and the first segments: a wait the
+    // compiler placed for the fragments alone would not know of the segment
+    // loads issued around them.
+    if (!resident) __builtin_amdgcn_s_waitcnt(0);
+    f32x16_t oacc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x16_t{0};
+    float cst = -INFINITY;   // softmax: integer stabiliser of this row
+    float lsum = 0.0f;       // softmax: this lane's part of the unrounded row sum
+
+    for (int lc = 0; lc < nchunks; ++lc) {
+      if (!resident) {
+        // segment lc complete in every thread, all reads of segment lc - 1 done
+        asm volatile("" ::: "memory");
+        wait_vm_lgkm0<(NS - 2) * C::kLoads>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue(lc + NS - 1, rs0, rs1);   // into the buffer of segment lc - 1
+      }
+      segment(smem + (lc % NS) * C::kStage, lc, af, oacc, cst, lsum);
+    }
+    if (!resident) {
+      // the next tile's first segments reuse the ring
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+
+    // ---- normalise and store: oacc[nb][4q + e] is O[m][nb*32 + 8q + 4h + e]
+    float inv = 1.0f;
+    if constexpr (kSoftmax) inv = 1.0f / sum_halves(lsum);
+    const uint32_t row = (uint32_t)(m0 + wave * 32 + r32);
+    const uint32_t es = p.out_f32 ? 4u : 2u;
+    const __amdgpu_buffer_rsrc_t rsO = make_rsrc((uint8_t*)p.O + (size_t)b * p.so * es,
+                                                 (uint32_t)((size_t)p.M * p.ldo * es));
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = nb * 32 + 8 * q + 4 * h;
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = oacc[nb][4 * q + e] * inv;
+        if (p.out_f32) {
+          if (p.o_vec) {
+            const u32x4_t v = {__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3])};
+            buf_store_b128(v, rsO, (row * p.ldo + (uint32_t)n) * 4);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) buf_store_b32(__float_as_uint(y[e]), rsO, (row * p.ldo + (uint32_t)(n + e)) * 4);
+          }
+        } else {
+          if (p.o_vec) {
+            const u32x2_t v = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+            buf_store_b64(v, rsO, (row * p.ldo + (uint32_t)n) * 2);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) buf_store_b16((uint16_t)f32_to_bf16(y[e]), rsO, (row * p.ldo + (uint32_t)(n + e)) * 2);
+          }
+        }
+      }
+  }
+}
+
+// ---- dispatch
+namespace {
+template <bool kSoftmax, bool kB0LK>
+const void* pick_stream_kn(int K, int N) {
+  if (K == 64 && N == 64) return (const void*)&b2b_stream_kernel<4, 2, kSoftmax, kB0LK>;
+  if (K == 64 && N == 128) return (const void*)&b2b_stream_kernel<4, 4, kSoftmax, kB0LK>;
+  if (K == 128 && N == 64) return (const void*)&b2b_stream_kernel<8, 2, kSoftmax, kB0LK>;
+  if (K == 128 && N == 128) return (const void*)&b2b_stream_kernel<8, 4, kSoftmax, kB0LK>;
+  return nullptr;
+}
+}  // namespace
+
+const void* b2b_stream_pick(const B2bParams& p) {
+  if (p.L % kTLC != 0 || p.L < kTLC) return nullptr;
+  const bool sm = p.row_op == 1;
+  if (sm) return p.b0_lk ? pick_stream_kn<true, true>(p.K, p.N) : pick_stream_kn<true, false>(p.K, p.N);
+  return p.b0_lk ? pick_stream_kn<false, true>(p.K, p.N) : pick_stream_kn<false, false>(p.K, p.N);
+}
+
+}  // namespace cf

@@ -80,4 +80,40 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// ----------------------------------------------------------------------------- LDS streaming
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// Raw buffer descriptor words (as make_rsrc builds them) for the asm loads below.
+__device__ inline u32x4_t rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+// 16 bytes per lane from memory straight into LDS at m0 + 16 * lane. Issued
+// from asm so that the compiler neither tracks nor waits for these loads: the
+// kernels order them explicitly with s_waitcnt vmcnt and s_barrier. Vector
+// memory loads complete in issue order, so vmcnt(n) means every such load but
+// the last n issued has landed (pending stores only make the wait stricter).
+__device__ inline void lds_dma16(uint32_t lds_addr, u32x4_t rs, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds_addr), "v"(voff), "s"(rs) : "memory", "m0");
+}
+// s_waitcnt with lgkmcnt(0) and vmcnt(n), expcnt left open (gfx9 encoding).
+template <int N>
+__device__ inline void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+__device__ inline u32x2_t lds_read_tr16(const uint8_t* p) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                         (__attribute__((address_space(3))) i16x4_t*)(lds_u8*)p));
+}
+
+// min over the two lane halves (see max_halves)
+__device__ inline float min_halves(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+
 }  // namespace cf

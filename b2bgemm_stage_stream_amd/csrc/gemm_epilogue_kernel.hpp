@@ -217,32 +217,6 @@ static_assert(kStages * kStageBytes <= 160 * 1024, "LDS ring exceeds 160 KiB");
 __device__ inline int swz64(int row) { return (((row >> 1) ^ (row >> 3)) & 1) | ((row >> 1) & 2); }
 __device__ inline int swz512(int k) { const int j = k & 3; return (2 * j) ^ (4 * j); }
 
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-
-// Raw buffer descriptor words (as make_rsrc builds them) for the asm loads below.
-__device__ inline u32x4_t rsrc_words(const void* base, uint32_t bytes) {
-  const uint64_t a = (uint64_t)base;
-  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
-}
-// 16 bytes per lane from memory straight into LDS at m0 + 16 * lane. Issued
-// from asm so that the compiler neither tracks nor waits for these loads: the
-// ring below orders them explicitly with s_waitcnt vmcnt and s_barrier.
-__device__ inline void lds_dma16(uint32_t lds_addr, u32x4_t rs, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds_addr), "v"(voff), "s"(rs) : "memory", "m0");
-}
-// s_waitcnt with lgkmcnt(0) and vmcnt(n), expcnt left open (gfx9 encoding).
-template <int N>
-__device__ inline void wait_vm_lgkm0() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
-}
-__device__ inline u32x2_t lds_read_tr16(const uint8_t* p) {
-  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                         (__attribute__((address_space(3))) i16x4_t*)(lds_u8*)p));
-}
-
 // `tid` is threadIdx.x passed through an opaque copy made per output tile, so
 // that the per-lane offsets below are computed per tile instead of being
 // hoisted out of the persistent loop (where they would be spilled and reloaded

@@ -104,6 +104,50 @@ def test_shapes(lk, row_op, act, shape):
           what=f"{shape} {row_op}/{act} lk={lk}")
 
 
+@pytest.mark.parametrize("lk", [False, True])
+@pytest.mark.parametrize("row_op,act", [("softmax", "none"), ("none", "relu")])
+@pytest.mark.parametrize("K,N", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_exact_shapes_streamed(K, N, lk, row_op, act):
+    # K, N in {64, 128} and L a multiple of 64 take the LDS-ring kernel; L = 320
+    # is 5 segments (more than the ring holds), batch 3 spreads over XCDs 0..2
+    batch, M, L = 3, 200, 320
+    w, dev, ref = P.inputs("c5_b2b_attention", seed=9, batch=batch, M=M, K=K, L=L, N=N)
+    dev["B1"] = (dev["B1"].float() / np.sqrt(L)).to(torch.bfloat16)
+    ref["B1"] = P.gpu_to_f64(dev["B1"])
+    if not lk:
+        dev["B0"] = dev["B0"].transpose(1, 2).contiguous()
+        ref["B0"] = np.ascontiguousarray(np.swapaxes(ref["B0"], 1, 2))
+    check(dev, ref, lk=lk, alpha=1.0 / np.sqrt(K), act=act, row_op=row_op,
+          what=f"streamed K={K} N={N} lk={lk} {row_op}/{act}")
+
+
+def test_heads_grouped_by_xcd():
+    # per-batch B0/B1 with a batch that is a multiple of 8: the row tiles of one
+    # batch entry are scheduled together (2 tiles per entry, ragged last tile)
+    w, dev, ref = P.inputs("c5_b2b_attention", seed=11, batch=16, M=200, L=192)
+    check(dev, ref, lk=True, alpha=0.125, row_op="softmax", what="16 heads x 200 rows")
+
+
+@pytest.mark.parametrize("L", [128, 640])
+def test_shared_weights_streamed(L):
+    # 2-D B0/B1 shared by the batch: L = 128 stays resident in LDS, L = 640
+    # streams; bias on the ReLU chain, negative alpha on the softmax chain
+    batch, M, K, N = 2, 256, 64, 64
+    w, dev, ref = P.inputs("c4_b2b_mlp_relu", seed=10, batch=batch, M=M, K=K, L=L, N=N)
+    B0, B1 = dev["B0"][0], dev["B1"][0]
+    bias = torch.linspace(-0.5, 0.5, L, device="cuda").to(torch.bfloat16)
+    R = oracle.b2bgemm(ref["A"], ref["B0"][0], ref["B1"][0], alpha=0.5, act="relu", bias=P.gpu_to_f64(bias))
+    O = torch.empty(batch, M, N, dtype=torch.float32, device="cuda")
+    cf.cf_b2bgemm(dev["A"], B0, B1, O, alpha=0.5, act="relu", bias=bias)
+    torch.cuda.synchronize()
+    P.assert_close(P.gpu_to_f64(O), R, P.REL_F_BF16, P.MAX_ABS_BF16, f"shared relu+bias L={L}")
+    B1s = (B1.float() / np.sqrt(L)).to(torch.bfloat16)
+    R = oracle.b2bgemm(ref["A"], ref["B0"][0], P.gpu_to_f64(B1s), alpha=-0.125, row_op="softmax")
+    cf.cf_b2bgemm(dev["A"], B0, B1s, O, alpha=-0.125, row_op="softmax")
+    torch.cuda.synchronize()
+    P.assert_close(P.gpu_to_f64(O), R, P.REL_F_BF16, P.MAX_ABS_BF16, f"shared softmax alpha<0 L={L}")
+
+
 def test_bias_and_shared_weights():
     # a 2-D B0/B1 is shared by every batch; bias per column of S
     w, dev, ref = P.inputs("c4_b2b_mlp_relu", seed=5, batch=3, M=96, K=32, L=96, N=64)

@@ -5,7 +5,7 @@
 // Report major comment 2 (paper Sec. IV-A, Eqs. (2)-(5)) and Fig. 5: S = A.B0 is
 // transformed tile by tile and consumed by the second GEMM from on-chip
 // storage, the contraction over L accumulated segment by segment. One
-// workgroup owns 128 rows of A (4 waves x 32) and walks all of L in 64-wide
+// workgroup owns 128 or 256 rows of A (4 waves x 32 or 64) and walks all of L in 64-wide
 // segments; O stays in registers. The segment arithmetic (operand swap, P
 // packed from the GEMM1 accumulators in the permuted l order, power-of-two
 // online-softmax stabiliser) is the one of the general kernel in b2b.hip.
@@ -28,13 +28,18 @@
 namespace cf {
 namespace {
 
-constexpr int kTBM = 128;     // rows of A per tile
 constexpr int kTLC = 64;      // L segment
 constexpr int kTThreads = 256;
 
-template <int KS, int NB>
+// MB: row blocks of 32 per wave. Two (only where registers allow, K = N = 64)
+// give each wave four independent accumulator chains and let every B0/B1
+// fragment read from LDS feed two MFMAs; one keeps tiles small when there
+// are few rows.
+template <int KS, int NB, int MB_>
 struct TCfg {
   static constexpr int K = 16 * KS, N = 32 * NB;
+  static constexpr int MB = MB_;
+  static constexpr int BM = 128 * MB;                            // rows per tile
   static constexpr int kB0Bytes = kTLC * K * 2;
   static constexpr int kB1Bytes = kTLC * N * 2;
   static constexpr int kStage = kB0Bytes + kB1Bytes;
@@ -54,17 +59,18 @@ __device__ inline int swz_tr256(int r) { return (2 * (r & 3)) ^ (4 * (r & 3)); }
 
 }  // namespace
 
-template <int KS, int NB, bool kSoftmax, bool kB0LK>
+template <int KS, int NB, int MB_, bool kSoftmax, bool kB0LK>
 __global__ __attribute__((amdgpu_flat_work_group_size(kTThreads, kTThreads), amdgpu_waves_per_eu(2, 2)))
 void b2b_stream_kernel(B2bParams p) {
-  using C = TCfg<KS, NB>;
+  using C = TCfg<KS, NB, MB_>;
   constexpr int NS = C::kStages;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::kLds];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, r32 = lane & 31;
-  const int mtiles = (p.M + kTBM - 1) / kTBM;
+  constexpr int MB = C::MB;
+  const int mtiles = (p.M + C::BM - 1) / C::BM;
   const int nchunks = p.L / kTLC;
   const float scale = kSoftmax ? p.alpha * kLog2e : p.alpha;
   const float floor_v = p.act == 1 ? 0.0f : -INFINITY;
@@ -142,15 +148,18 @@ void b2b_stream_kernel(B2bParams p) {
       lds_dma16(st + i * 4096, is_b0[i] ? rs0 : rs1, ok ? goff[i] + (uint32_t)s * gstep[i] : kOutOfRange);
   };
 
-  // one segment: GEMM1, F, GEMM2 on stage buffer st
-  auto segment = [&](const uint8_t* st, int lc, const u32x4_t (&af)[KS], f32x16_t (&oacc)[NB], float& cst,
-                     float& lsum) {
-    f32x16_t sacc[2];
+  // one segment: GEMM1, F, GEMM2 on stage buffer st; row block rb of the wave
+  auto segment = [&](const uint8_t* st, int lc, const u32x4_t (&af)[MB][KS], f32x16_t (&oacc)[MB][NB],
+                     float (&cst)[MB], float (&lsum)[MB]) {
+    f32x16_t sacc[MB][2];
 #pragma unroll
-    for (int lb = 0; lb < 2; ++lb) {
-      sacc[lb] = f32x16_t{0};
+    for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+      for (int lb = 0; lb < 2; ++lb) sacc[rb][lb] = f32x16_t{0};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int lb = 0; lb < 2; ++lb) {
         u32x4_t bf;
         if constexpr (kB0LK) {
           bf = *(const u32x4_t*)(st + b0_rd[ks] + lb * 32 * C::K * 2);
@@ -159,73 +168,77 @@ void b2b_stream_kernel(B2bParams p) {
           const u32x2_t hi = lds_read_tr16(st + b0_rd[lb] + ks * 16 * 128 + 4 * 128);
           bf = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
         }
-        sacc[lb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bf),
-                                                            __builtin_bit_cast(bf16x8_t, af[ks]), sacc[lb], 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb)
+          sacc[rb][lb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bf),
+                                                                  __builtin_bit_cast(bf16x8_t, af[rb][ks]), sacc[rb][lb], 0, 0, 0);
       }
-    }
     // F: register r of block lb holds l = lc*64 + lb*32 + 8(r>>2) + 4h + (r&3)
-    u32x4_t pf[4];
-    if constexpr (kSoftmax) {
-      // row extreme of S (of alpha*S for the stabiliser): max for alpha >= 0, min otherwise
-      float mx;
-      if (scale >= 0.0f) {
-        mx = -INFINITY;
+    u32x4_t pf[MB][4];
 #pragma unroll
-        for (int lb = 0; lb < 2; ++lb)
+    for (int rb = 0; rb < MB; ++rb) {
+      if constexpr (kSoftmax) {
+        // row extreme of S (of alpha*S for the stabiliser): max for alpha >= 0, min otherwise
+        float mx;
+        if (scale >= 0.0f) {
+          mx = -INFINITY;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[lb][r]);
-        mx = max_halves(mx);
-      } else {
-        mx = INFINITY;
+          for (int lb = 0; lb < 2; ++lb)
 #pragma unroll
-        for (int lb = 0; lb < 2; ++lb)
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[rb][lb][r]);
+          mx = max_halves(mx);
+        } else {
+          mx = INFINITY;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fminf(mx, sacc[lb][r]);
-        mx = min_halves(mx);
-      }
-      const float cn = fmaxf(cst, ceilf(mx * scale));
-      if (cn > cst && cst != -INFINITY) {
-        const int sh = (int)(cst - cn);          // exact power-of-two rescale
+          for (int lb = 0; lb < 2; ++lb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[nb][r] = __builtin_amdgcn_ldexpf(oacc[nb][r], sh);
-        lsum = __builtin_amdgcn_ldexpf(lsum, sh);
-      }
-      cst = cn;
-#pragma unroll
-      for (int lb = 0; lb < 2; ++lb) {
-        float e[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          e[r] = fast_exp2(__builtin_fmaf(sacc[lb][r], scale, -cn));
-          lsum += e[r];
+            for (int r = 0; r < 16; ++r) mx = fminf(mx, sacc[rb][lb][r]);
+          mx = min_halves(mx);
         }
+        const float cn = fmaxf(cst[rb], ceilf(mx * scale));
+        if (cn > cst[rb] && cst[rb] != -INFINITY) {
+          const int sh = (int)(cst[rb] - cn);      // exact power-of-two rescale
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+          for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) pf[2 * lb + c][q] = pack_bf16x2(e[8 * c + 2 * q], e[8 * c + 2 * q + 1]);
-      }
-    } else {
+            for (int r = 0; r < 16; ++r) oacc[rb][nb][r] = __builtin_amdgcn_ldexpf(oacc[rb][nb][r], sh);
+          lsum[rb] = __builtin_amdgcn_ldexpf(lsum[rb], sh);
+        }
+        cst[rb] = cn;
 #pragma unroll
-      for (int lb = 0; lb < 2; ++lb) {
-        float x[16];
-        if (p.bias) {
-          const int lbase = lc * kTLC + lb * 32 + 4 * h;
+        for (int lb = 0; lb < 2; ++lb) {
+          float e[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int l = lbase + 8 * (r >> 2) + (r & 3);
-            const float bv = p.bias_f32 ? ((const float*)p.bias)[l] : bf16_to_f32(((const uint16_t*)p.bias)[l]);
-            x[r] = fmaxf(__builtin_fmaf(sacc[lb][r], scale, bv), floor_v);
+            e[r] = fast_exp2(__builtin_fmaf(sacc[rb][lb][r], scale, -cn));
+            lsum[rb] += e[r];
           }
-        } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) x[r] = fmaxf(sacc[lb][r] * scale, floor_v);
+          for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) pf[rb][2 * lb + c][q] = pack_bf16x2(e[8 * c + 2 * q], e[8 * c + 2 * q + 1]);
         }
+      } else {
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int lb = 0; lb < 2; ++lb) {
+          float x[16];
+          if (p.bias) {
+            const int lbase = lc * kTLC + lb * 32 + 4 * h;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) pf[2 * lb + c][q] = pack_bf16x2(x[8 * c + 2 * q], x[8 * c + 2 * q + 1]);
+            for (int r = 0; r < 16; ++r) {
+              const int l = lbase + 8 * (r >> 2) + (r & 3);
+              const float bv = p.bias_f32 ? ((const float*)p.bias)[l] : bf16_to_f32(((const uint16_t*)p.bias)[l]);
+              x[r] = fmaxf(__builtin_fmaf(sacc[rb][lb][r], scale, bv), floor_v);
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[r] = fmaxf(sacc[rb][lb][r] * scale, floor_v);
+          }
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) pf[rb][2 * lb + c][q] = pack_bf16x2(x[8 * c + 2 * q], x[8 * c + 2 * q + 1]);
+        }
       }
     }
     // GEMM2 over the four 16-wide slices of the segment
@@ -236,8 +249,10 @@ void b2b_stream_kernel(B2bParams p) {
         const u32x2_t lo = lds_read_tr16(st + b1_rd[nb] + c * 16 * C::N * 2);
         const u32x2_t hi = lds_read_tr16(st + b1_rd[nb] + c * 16 * C::N * 2 + 8 * C::N * 2);
         const u32x4_t vf = {lo[0], lo[1], hi[0], hi[1]};
-        oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf),
-                                                            __builtin_bit_cast(bf16x8_t, pf[c]), oacc[nb], 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb)
+          oacc[rb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf),
+                                                                  __builtin_bit_cast(bf16x8_t, pf[rb][c]), oacc[rb][nb], 0, 0, 0);
       }
   };
 
@@ -273,7 +288,7 @@ void b2b_stream_kernel(B2bParams p) {
       b = e / mtiles;
       mt = e % mtiles;
     }
-    const int m0 = mt * kTBM;
+    const int m0 = mt * C::BM;
     const uint16_t* Ab = (const uint16_t*)p.A + (size_t)b * p.sa;
     const __amdgpu_buffer_rsrc_t rsA = make_rsrc(Ab, (uint32_t)((size_t)p.M * p.lda * 2));
     const u32x4_t rs0 = rsrc_words((const uint16_t*)p.B0 + (size_t)b * p.sb0,
@@ -284,22 +299,27 @@ void b2b_stream_kernel(B2bParams p) {
 #pragma unroll
       for (int s = 0; s < NS - 1; ++s) issue(s, rs0, rs1);
     }
-    // A fragments of this wave's 32 rows (rows >= M read as zero)
-    u32x4_t af[KS];
-    {
-      const uint32_t row = (uint32_t)(m0 + wave * 32 + r32);
+    // A fragments of this wave's rows (rows >= M read as zero)
+    u32x4_t af[MB][KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) af[ks] = buf_load_b128(rsA, (row * p.lda + (uint32_t)(ks * 16 + 8 * h)) * 2);
+    for (int rb = 0; rb < MB; ++rb) {
+      const uint32_t row = (uint32_t)(m0 + (wave * MB + rb) * 32 + r32);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) af[rb][ks] = buf_load_b128(rsA, (row * p.lda + (uint32_t)(ks * 16 + 8 * h)) * 2);
     }
     // One full wait for the A fragments and the first segments: a wait the
     // compiler placed for the fragments alone would not know of the segment
     // loads issued around them.
     if (!resident) __builtin_amdgcn_s_waitcnt(0);
-    f32x16_t oacc[NB];
+    f32x16_t oacc[MB][NB];
+    float cst[MB], lsum[MB];   // softmax: integer stabiliser of the row, this lane's part of the unrounded row sum
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x16_t{0};
-    float cst = -INFINITY;   // softmax: integer stabiliser of this row
-    float lsum = 0.0f;       // softmax: this lane's part of the unrounded row sum
+    for (int rb = 0; rb < MB; ++rb) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) oacc[rb][nb] = f32x16_t{0};
+      cst[rb] = -INFINITY;
+      lsum[rb] = 0.0f;
+    }
 
     for (int lc = 0; lc < nchunks; ++lc) {
       if (!resident) {
@@ -320,59 +340,68 @@ void b2b_stream_kernel(B2bParams p) {
       asm volatile("" ::: "memory");
     }
 
-    // ---- normalise and store: oacc[nb][4q + e] is O[m][nb*32 + 8q + 4h + e]
-    float inv = 1.0f;
-    if constexpr (kSoftmax) inv = 1.0f / sum_halves(lsum);
-    const uint32_t row = (uint32_t)(m0 + wave * 32 + r32);
+    // ---- normalise and store: oacc[rb][nb][4q + e] is O[m][nb*32 + 8q + 4h + e]
     const uint32_t es = p.out_f32 ? 4u : 2u;
     const __amdgpu_buffer_rsrc_t rsO = make_rsrc((uint8_t*)p.O + (size_t)b * p.so * es,
                                                  (uint32_t)((size_t)p.M * p.ldo * es));
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int rb = 0; rb < MB; ++rb) {
+      float inv = 1.0f;
+      if constexpr (kSoftmax) inv = 1.0f / sum_halves(lsum[rb]);
+      const uint32_t row = (uint32_t)(m0 + (wave * MB + rb) * 32 + r32);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = nb * 32 + 8 * q + 4 * h;
-        float y[4];
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = oacc[nb][4 * q + e] * inv;
-        if (p.out_f32) {
-          if (p.o_vec) {
-            const u32x4_t v = {__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3])};
-            buf_store_b128(v, rsO, (row * p.ldo + (uint32_t)n) * 4);
+        for (int q = 0; q < 4; ++q) {
+          const int n = nb * 32 + 8 * q + 4 * h;
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = oacc[rb][nb][4 * q + e] * inv;
+          if (p.out_f32) {
+            if (p.o_vec) {
+              const u32x4_t v = {__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3])};
+              buf_store_b128(v, rsO, (row * p.ldo + (uint32_t)n) * 4);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) buf_store_b32(__float_as_uint(y[e]), rsO, (row * p.ldo + (uint32_t)(n + e)) * 4);
+            }
           } else {
+            if (p.o_vec) {
+              const u32x2_t v = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+              buf_store_b64(v, rsO, (row * p.ldo + (uint32_t)n) * 2);
+            } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) buf_store_b32(__float_as_uint(y[e]), rsO, (row * p.ldo + (uint32_t)(n + e)) * 4);
-          }
-        } else {
-          if (p.o_vec) {
-            const u32x2_t v = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-            buf_store_b64(v, rsO, (row * p.ldo + (uint32_t)n) * 2);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) buf_store_b16((uint16_t)f32_to_bf16(y[e]), rsO, (row * p.ldo + (uint32_t)(n + e)) * 2);
+              for (int e = 0; e < 4; ++e) buf_store_b16((uint16_t)f32_to_bf16(y[e]), rsO, (row * p.ldo + (uint32_t)(n + e)) * 2);
+            }
           }
         }
-      }
+    }
   }
 }
 
 // ---- dispatch
 namespace {
 template <bool kSoftmax, bool kB0LK>
-const void* pick_stream_kn(int K, int N) {
-  if (K == 64 && N == 64) return (const void*)&b2b_stream_kernel<4, 2, kSoftmax, kB0LK>;
-  if (K == 64 && N == 128) return (const void*)&b2b_stream_kernel<4, 4, kSoftmax, kB0LK>;
-  if (K == 128 && N == 64) return (const void*)&b2b_stream_kernel<8, 2, kSoftmax, kB0LK>;
-  if (K == 128 && N == 128) return (const void*)&b2b_stream_kernel<8, 4, kSoftmax, kB0LK>;
+const void* pick_stream_kn(int K, int N, bool two_blocks) {
+  if (K == 64 && N == 64)
+    return two_blocks ? (const void*)&b2b_stream_kernel<4, 2, 2, kSoftmax, kB0LK>
+                      : (const void*)&b2b_stream_kernel<4, 2, 1, kSoftmax, kB0LK>;
+  if (K == 64 && N == 128) return (const void*)&b2b_stream_kernel<4, 4, 1, kSoftmax, kB0LK>;
+  if (K == 128 && N == 64) return (const void*)&b2b_stream_kernel<8, 2, 1, kSoftmax, kB0LK>;
+  if (K == 128 && N == 128) return (const void*)&b2b_stream_kernel<8, 4, 1, kSoftmax, kB0LK>;
   return nullptr;
 }
 }  // namespace
 
-const void* b2b_stream_pick(const B2bParams& p) {
+const void* b2b_stream_pick(const B2bParams& p, int cus, int* rows_per_tile) {
   if (p.L % kTLC != 0 || p.L < kTLC) return nullptr;
+  // 256-row tiles only when they still give every CU two workgroups
+  const bool two = p.K == 64 && p.N == 64 && (long)p.batch * ((p.M + 255) / 256) >= 2L * cus;
   const bool sm = p.row_op == 1;
-  if (sm) return p.b0_lk ? pick_stream_kn<true, true>(p.K, p.N) : pick_stream_kn<true, false>(p.K, p.N);
-  return p.b0_lk ? pick_stream_kn<false, true>(p.K, p.N) : pick_stream_kn<false, false>(p.K, p.N);
+  const void* k = sm ? (p.b0_lk ? pick_stream_kn<true, true>(p.K, p.N, two) : pick_stream_kn<true, false>(p.K, p.N, two))
+                     : (p.b0_lk ? pick_stream_kn<false, true>(p.K, p.N, two) : pick_stream_kn<false, false>(p.K, p.N, two));
+  if (k && rows_per_tile) *rows_per_tile = two ? 256 : 128;
+  return k;
 }
 
 }  // namespace cf

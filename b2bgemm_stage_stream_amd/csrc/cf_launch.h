@@ -70,8 +70,9 @@ struct B2bParams {
 };
 
 hipError_t launch_b2b(const B2bParams& p, hipStream_t stream);
-// Streamed kernel for exact shapes (K, N in {64, 128}, L a multiple of 64), or null.
-const void* b2b_stream_pick(const B2bParams& p);
+// Streamed kernel for exact shapes (K, N in {64, 128}, L a multiple of 64), or
+// null; *rows_per_tile receives its tile height.
+const void* b2b_stream_pick(const B2bParams& p, int cus, int* rows_per_tile);
 // Returns false when (K, N, row_op, ...) has no kernel instantiation.
 bool b2b_supported(const B2bParams& p);
 

@@ -121,6 +121,19 @@ def test_exact_shapes_streamed(K, N, lk, row_op, act):
           what=f"streamed K={K} N={N} lk={lk} {row_op}/{act}")
 
 
+@pytest.mark.parametrize("lk,row_op,act", [(True, "softmax", "none"), (False, "none", "relu")])
+def test_two_row_blocks_per_wave(lk, row_op, act):
+    # enough 256-row tiles (512 batch entries) for the kernel variant whose
+    # waves own 64 rows; M = 200 leaves every tile ragged
+    w, dev, ref = P.inputs("c5_b2b_attention", seed=12, batch=512, M=200, K=64, L=128, N=64)
+    dev["B1"] = (dev["B1"].float() / np.sqrt(128)).to(torch.bfloat16)
+    ref["B1"] = P.gpu_to_f64(dev["B1"])
+    if not lk:
+        dev["B0"] = dev["B0"].transpose(1, 2).contiguous()
+        ref["B0"] = np.ascontiguousarray(np.swapaxes(ref["B0"], 1, 2))
+    check(dev, ref, lk=lk, alpha=0.125, act=act, row_op=row_op, what=f"512 x 200 rows {row_op}/{act}")
+
+
 def test_heads_grouped_by_xcd():
     # per-batch B0/B1 with a batch that is a multiple of 8: the row tiles of one
     # batch entry are scheduled together (2 tiles per entry, ragged last tile)

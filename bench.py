@@ -4,8 +4,9 @@ MI355X.
 One step = one fused kernel call over the whole workload (inputs already
 resident in HBM). Prints one JSON line:
   value      algorithmic GEMM TFLOP/s of the workload (2*M*N*K per GEMM)
-  roofline   the same kernel against the bf16 dense MFMA peak, with the mean
-             kernel time from HIP events on the launch stream
+  roofline   the same kernel against its bound (bf16 dense MFMA peak, or HBM
+             bandwidth when the workload's flop/byte is below the ridge point),
+             with the mean kernel time from HIP events on the launch stream
   cpu_baseline  the fp64 oracle timed on the host cores on a bounded row sample
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -228,9 +229,17 @@ def main():
 
     flops = flops_of(w)
     value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (kernel_ms * 1e-3) / 1e12
     in_f32 = any(t.dtype == "f32" for t in w.tensors if t.name == "A")
-    peak = PEAK_F32_TFLOPS if in_f32 else PEAK_BF16_TFLOPS
+    peak_flops = PEAK_F32_TFLOPS if in_f32 else PEAK_BF16_TFLOPS
+    # the roofline that bounds the kernel: HBM below the ridge point, MFMA above
+    intensity = flops / bytes_of(w)
+    ridge = peak_flops * 1e12 / (HBM_GBPS * 1e9)
+    if intensity < ridge:
+        bound, unit, peak = "hbm", "GB/s", HBM_GBPS
+        achieved = bytes_of(w) / (kernel_ms * 1e-3) / 1e9
+    else:
+        bound, unit, peak = "mfma", "TFLOP/s", peak_flops
+        achieved = flops / (kernel_ms * 1e-3) / 1e12
     traffic = None
     if os.path.exists(args.traffic) and not args.plain:
         try:
@@ -254,8 +263,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name + ("/identity-epilogue" if args.plain else ""), **w.dims,
                    "out_dtype": w.params.get("out_dtype")},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": traffic},
+        "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "arithmetic_intensity": round(intensity, 1), "ridge": round(ridge, 1)},
         "kernel_ms": round(kernel_ms, 4),
         "algorithmic_bytes": bytes_of(w),
         "intermediate_hbm_bytes": 0,

@@ -95,6 +95,23 @@ def bytes_of(w) -> float:
     return float(tot)
 
 
+def is_f32(w) -> bool:
+    return any(t.dtype == "f32" for t in w.tensors if t.name == "A")
+
+
+def roofline_of(w, kernel_ms: float):
+    """The roofline that bounds the kernel: HBM when the workload's flop/byte is
+    below the ridge point (peak flops / HBM bandwidth), the MFMA peak above it.
+    Returns (bound, unit, peak, achieved, intensity, ridge)."""
+    flops, nbytes = flops_of(w), bytes_of(w)
+    peak_flops = PEAK_F32_TFLOPS if is_f32(w) else PEAK_BF16_TFLOPS
+    intensity = flops / nbytes
+    ridge = peak_flops * 1e12 / (HBM_GBPS * 1e9)
+    if intensity < ridge:
+        return "hbm", "GB/s", HBM_GBPS, nbytes / (kernel_ms * 1e-3) / 1e9, intensity, ridge
+    return "mfma", "TFLOP/s", peak_flops, flops / (kernel_ms * 1e-3) / 1e12, intensity, ridge
+
+
 def make_call(w, dev, torch, cf):
     """Device tensors + a closure launching one fused kernel on the current stream."""
     p = w.params
@@ -229,17 +246,8 @@ def main():
 
     flops = flops_of(w)
     value = flops / (ms_per_step * 1e-3) / 1e12
-    in_f32 = any(t.dtype == "f32" for t in w.tensors if t.name == "A")
-    peak_flops = PEAK_F32_TFLOPS if in_f32 else PEAK_BF16_TFLOPS
-    # the roofline that bounds the kernel: HBM below the ridge point, MFMA above
-    intensity = flops / bytes_of(w)
-    ridge = peak_flops * 1e12 / (HBM_GBPS * 1e9)
-    if intensity < ridge:
-        bound, unit, peak = "hbm", "GB/s", HBM_GBPS
-        achieved = bytes_of(w) / (kernel_ms * 1e-3) / 1e9
-    else:
-        bound, unit, peak = "mfma", "TFLOP/s", peak_flops
-        achieved = flops / (kernel_ms * 1e-3) / 1e12
+    in_f32 = is_f32(w)
+    bound, unit, peak, achieved, intensity, ridge = roofline_of(w, kernel_ms)
     traffic = None
     if os.path.exists(args.traffic) and not args.plain:
         try:

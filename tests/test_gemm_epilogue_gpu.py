@@ -168,6 +168,34 @@ def test_k_zero_and_empty():
                         torch.zeros(4, 16, dtype=torch.bfloat16, device="cuda"), E)
 
 
+def test_exchange_timeout_is_reported_and_recoverable():
+    # A zero spin limit (forced from the host) makes a workgroup give up on
+    # peers that have not published yet: the launch still completes (every
+    # wait is bounded) and the workspace reports the timeout. After a reset and
+    # with the normal limit the same call is exact again.
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=13, M=512, K=256)
+    e = cf.make_epilogue(**epi_of(w, dev))
+    ws = cf.Workspace().get(cf.cf_gemm_epilogue_workspace_size(512, 4096, 256, e))
+    C = torch.empty(512, 4096, dtype=torch.float32, device="cuda")
+    old = cf.cf_set_exchange_timeout_us(0)
+    try:
+        seen = set()
+        for _ in range(3):
+            cf.cf_gemm_epilogue(dev["A"], dev["B"], C, epi=e, workspace=ws)
+            st = cf.cf_workspace_status(ws)
+            assert st in (cf.CF_OK, cf.CF_ERR_DEVICE_TIMEOUT)
+            seen.add(st)
+            if st != cf.CF_OK:
+                cf.cf_workspace_init(ws)
+                assert cf.cf_workspace_status(ws) == cf.CF_OK
+    finally:
+        cf.cf_set_exchange_timeout_us(old)
+    print(f"statuses with a zero spin limit: {sorted(seen)}", flush=True)
+    cf.cf_gemm_epilogue(dev["A"], dev["B"], C, epi=e, workspace=ws)
+    assert cf.cf_workspace_status(ws) == cf.CF_OK
+    P.assert_close(P.gpu_to_f64(C), oracle_of(w, ref), P.REL_F_BF16, P.MAX_ABS_BF16, "after timeout recovery")
+
+
 # ---------------------------------------------------------------------------- structure
 
 def test_deterministic_and_row_local():

@@ -189,12 +189,17 @@ def cpu_baseline(w, raw, target_s: float):
     run(n0)
     t0 = time.perf_counter() - t
     n = int(min(total_units, max(n0, n0 * target_s / max(t0, 1e-6))))
-    t = time.perf_counter()
-    run(n)
-    dt = time.perf_counter() - t
-    tflops = n * unit_flops / dt / 1e12
+    # when the whole workload is quicker than the target, repeat it
+    reps, dt = 0, 0.0
+    while reps == 0 or (n == total_units and dt < target_s and reps < 100):
+        t = time.perf_counter()
+        run(n)
+        dt += time.perf_counter() - t
+        reps += 1
+    tflops = reps * n * unit_flops / dt / 1e12
+    rep_txt = f" x {reps} runs" if reps > 1 else ""
     return {"value": tflops, "unit": "TFLOP/s", "cores": ncores, "kind": "oracle",
-            "sample": f"{n} of {total_units} {what} of the same workload, fp64, {dt:.1f} s"}
+            "sample": f"{n} of {total_units} {what} of the same workload{rep_txt}, fp64, {dt:.1f} s"}
 
 
 def main():

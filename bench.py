@@ -2,7 +2,9 @@
 MI355X.
 
 One step = one fused kernel call over the whole workload (inputs already
-resident in HBM). Prints one JSON line:
+resident in HBM; consecutive steps cycle through copies of the inputs totalling
+at least 512 MiB so that they are read from HBM, not from the last-level
+cache). Prints one JSON line:
   value      algorithmic GEMM TFLOP/s of the workload (2*M*N*K per GEMM)
   roofline   the same kernel against its bound (bf16 dense MFMA peak, or HBM
              bandwidth when the workload's flop/byte is below the ridge point),
@@ -47,6 +49,9 @@ def parse():
                     help="measured HBM bytes per launch (written from rocprofv3 counters)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="calibration: time a plain device copy of MIB MiB (for the byte counters)")
+    ap.add_argument("--rotate-mb", type=int, default=512,
+                    help="cycle through copies of the inputs totalling at least this many MiB, so that they are "
+                         "read from HBM rather than from the 256 MiB last-level cache (0: one set)")
     return ap.parse_args()
 
 
@@ -229,18 +234,24 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
     dev = {t.name: to_dev(raw[t.name], t.dtype) for t in w.tensors}
-    call, out, ws, ws_bytes = make_call(w, dev, torch, cf)
+    in_bytes = sum(v.numel() * v.element_size() for v in dev.values())
+    nset = 1 if args.rotate_mb <= 0 else max(1, min(64, -(-args.rotate_mb * (1 << 20) // in_bytes)))
+    devs = [dev] + [{k: v.clone() for k, v in dev.items()} for _ in range(nset - 1)]
+    calls = []
+    for d_ in devs:
+        call, out, ws, ws_bytes = make_call(w, d_, torch, cf)
+        calls.append(call)
 
-    for _ in range(args.warmup):
-        call()
+    for i in range(max(args.warmup, nset)):
+        calls[i % nset]()
     torch.cuda.synchronize()
     start_ev = torch.cuda.Event(enable_timing=True)
     end_ev = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start_ev.record()
-    for _ in range(args.steps):
-        call()
+    for i in range(args.steps):
+        calls[i % nset]()
     end_ev.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -275,7 +286,7 @@ def main():
         "dtype": "f32" if in_f32 else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name + ("/identity-epilogue" if args.plain else ""), **w.dims,
-                   "out_dtype": w.params.get("out_dtype")},
+                   "out_dtype": w.params.get("out_dtype"), "input_sets": nset, "input_bytes_per_set": in_bytes},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "arithmetic_intensity": round(intensity, 1), "ridge": round(ridge, 1)},
@@ -285,7 +296,7 @@ def main():
         "workspace_bytes": ws_bytes,
     }
     if not args.no_cpu_baseline:
-        del dev, out
+        del dev, devs, calls, out
         line["cpu_baseline"] = cpu_baseline(w, raw, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 

@@ -43,6 +43,9 @@ class cf_epilogue(ctypes.Structure):
         ("gamma", ctypes.c_void_p),
         ("beta", ctypes.c_void_p),
         ("eps", ctypes.c_float),
+        ("x_out", ctypes.c_void_p),
+        ("ld_x_out", ctypes.c_int64),
+        ("x_out_dtype", ctypes.c_int),
     ]
 
 
@@ -122,8 +125,9 @@ def _ptr(t) -> Optional[int]:
 
 
 def make_epilogue(*, alpha: float = 1.0, bias=None, residual=None, act: str = "none",
-                  row_op: str = "none", gamma=None, beta=None, eps: float = 0.0) -> cf_epilogue:
-    """cf_epilogue descriptor from tensors (bias/gamma/beta share one dtype)."""
+                  row_op: str = "none", gamma=None, beta=None, eps: float = 0.0, x_out=None) -> cf_epilogue:
+    """cf_epilogue descriptor from tensors (bias/gamma/beta share one dtype).
+    ``x_out``: optional [M, N] tensor that receives x before the row operation."""
     e = cf_epilogue()
     _lib.cf_epilogue_init(ctypes.byref(e))
     e.alpha = float(alpha)
@@ -144,6 +148,10 @@ def make_epilogue(*, alpha: float = 1.0, bias=None, residual=None, act: str = "n
         e.residual = residual.data_ptr()
         e.ld_residual = _ld(residual)
         e.residual_dtype = _dtype_code(residual)
+    if x_out is not None:
+        e.x_out = x_out.data_ptr()
+        e.ld_x_out = _ld(x_out)
+        e.x_out_dtype = _dtype_code(x_out)
     return e
 
 
@@ -178,7 +186,7 @@ def cf_gemm_epilogue(A, B, C, *, b_is_nk: bool = False, epi: Optional[cf_epilogu
                      workspace=None, stream=None, **epi_kwargs) -> None:
     """C = epilogue(A . B) in one kernel. A [M, K]; B [K, N] (or [N, K] with
     b_is_nk); C [M, N]. The epilogue is ``epi`` or built from keyword
-    arguments (alpha, bias, residual, act, row_op, gamma, beta, eps)."""
+    arguments (alpha, bias, residual, act, row_op, gamma, beta, eps, x_out)."""
     if epi is None:
         epi = make_epilogue(**epi_kwargs)
     elif epi_kwargs:
@@ -187,6 +195,9 @@ def cf_gemm_epilogue(A, B, C, *, b_is_nk: bool = False, epi: Optional[cf_epilogu
     N = B.shape[0] if b_is_nk else B.shape[1]
     if C.shape != (M, N):
         raise ValueError(f"C must be [{M}, {N}]")
+    x_out = epi_kwargs.get("x_out")
+    if x_out is not None and tuple(x_out.shape) != (M, N):
+        raise ValueError(f"x_out must be [{M}, {N}]")
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
                                                            workspace.numel() * workspace.element_size())
     _check(_lib.cf_gemm_epilogue(M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), int(b_is_nk),

@@ -100,6 +100,12 @@ cf_status check_epilogue(const cf_epilogue* epi, int64_t N, bool allow_row_ops_n
     if (epi->ld_residual < N || epi->ld_residual < 1) return CF_ERR_INVALID_ARGUMENT;
     if (!aligned(epi->residual, dsize(epi->residual_dtype))) return CF_ERR_INVALID_ARGUMENT;
   }
+  if (epi->x_out) {
+    if (!allow_residual) return CF_ERR_UNSUPPORTED;
+    if (epi->x_out_dtype != CF_BF16 && epi->x_out_dtype != CF_F32) return CF_ERR_INVALID_ARGUMENT;
+    if (epi->ld_x_out < N || epi->ld_x_out < 1) return CF_ERR_INVALID_ARGUMENT;
+    if (!aligned(epi->x_out, dsize(epi->x_out_dtype))) return CF_ERR_INVALID_ARGUMENT;
+  }
   if (!allow_row_ops_norm) {
     if (epi->row_op == CF_ROW_LAYERNORM || epi->row_op == CF_ROW_RMSNORM) return CF_ERR_UNSUPPORTED;
     if (epi->gamma || epi->beta) return CF_ERR_UNSUPPORTED;
@@ -180,6 +186,9 @@ cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K, const void* A, int64
   }
   const cf_dtype rdt = (epi && epi->residual) ? epi->residual_dtype : CF_BF16;
   if (epi && epi->residual && !fits31(M, kTile, epi->ld_residual, dsize(rdt))) return CF_ERR_UNSUPPORTED;
+  void* const X = epi ? epi->x_out : nullptr;
+  const size_t xs = X ? dsize(epi->x_out_dtype) : 2;
+  if (X && !fits31(M, kTile, epi->ld_x_out, xs)) return CF_ERR_UNSUPPORTED;
   const int row_op = epi ? (int)epi->row_op : 0;
   if (row_op != CF_ROW_NONE && N > 65536) return CF_ERR_UNSUPPORTED;
 
@@ -194,6 +203,7 @@ cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K, const void* A, int64
              aligned(A, 16) && aligned(B, 16) && aligned(C, 16);
   if (epi && epi->residual)
     vec = vec && epi->residual_dtype == CF_BF16 && epi->ld_residual % 8 == 0 && aligned(epi->residual, 16);
+  if (X) vec = vec && epi->ld_x_out % 8 == 0 && aligned(X, 16);
 
   // ---- device
   int dev;
@@ -217,6 +227,10 @@ cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K, const void* A, int64
   p.b_bytes = (uint32_t)(K > 0 ? (uint64_t)(b_is_nk ? N : K) * ldb * es : 0);
   p.c_bytes = (uint32_t)((uint64_t)M * ldc * cs);
   p.r_bytes = (uint32_t)(p.residual ? (uint64_t)M * epi->ld_residual * dsize(rdt) : 0);
+  p.X = X;
+  p.ldx = (uint32_t)(X ? epi->ld_x_out : 0);
+  p.x_bytes = (uint32_t)(X ? (uint64_t)M * epi->ld_x_out * xs : 0);
+  p.x_f32 = X && epi->x_out_dtype == CF_F32;
   p.M = (int)M;
   p.N = (int)N;
   p.K = (int)K;

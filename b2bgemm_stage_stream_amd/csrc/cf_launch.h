@@ -35,6 +35,9 @@ struct GemmEpilogueParams {
   int c_f32;         // 1: fp32 output, 0: bf16
   int vec_f32;       // dtype of bias/gamma/beta: 1 fp32, 0 bf16
   int res_f32;       // dtype of residual
+  void* X;           // optional second output: x before the row operation
+  uint32_t ldx, x_bytes;
+  int x_f32;         // dtype of X: 1 fp32, 0 bf16
   uint32_t* ws_hdr;  // workspace header (NULL when tiles_n == 1 or no row op)
   uint64_t* ws_slots;
   uint64_t spin_ticks;   // wall-clock ticks a strip wait may take

@@ -704,16 +704,23 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
   // ---- stage 2: normalise, affine, cast, store
   // Column group outer, row block inner: the per-column vectors are read
   // from LDS once per group and reused by the 4 row blocks.
-  auto store_pass = [&](auto f32c) {
+  // kX: the second output X (x before the row operation) is 0 absent, 1 bf16,
+  // 2 fp32, 3 decided at run time (general path, one instantiation); it is
+  // stored straight from the registers that hold x
+  const __amdgpu_buffer_rsrc_t rsX = make_rsrc(p.X, p.X ? p.x_bytes : 0u);
+  auto store_pass = [&](auto f32c, auto xc) {
     constexpr bool kOutF32 = decltype(f32c)::value;
+    constexpr int kX = decltype(xc)::value;
     constexpr uint32_t es = kOutF32 ? 4u : 2u;
+    const uint32_t xes = kX == 2 ? 4u : kX == 1 ? 2u : (p.x_f32 ? 4u : 2u);
     float2 st[4];
-    uint32_t rowoff[4];
+    uint32_t rowoff[4], xrowoff[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const int ml = wm * 128 + mb * 32 + r32;
       st[mb] = ROW != 0 ? rstat[ml] : make_float2(0.f, 0.f);
       rowoff[mb] = ((uint32_t)(m0 + ml) * p.ldc + (uint32_t)(n0 + wn * 128 + 4 * h)) * es;
+      if constexpr (kX != 0) xrowoff[mb] = ((uint32_t)(m0 + ml) * p.ldx + (uint32_t)(n0 + wn * 128 + 4 * h)) * xes;
     }
     for_groups([&](int nb, auto qc) {
       constexpr int q = decltype(qc)::value;
@@ -726,6 +733,34 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
       for (int mb = 0; mb < 4; ++mb) {
         float x[4], y[4];
         xgroup(mb, nb, qc, bv, tok, x);
+        if constexpr (kX == 2) {
+          if constexpr (kFast) {
+            const u32x4_t v = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
+            buf_store_b128(v, rsX, xrowoff[mb] + (uint32_t)c * 4);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              buf_store_b32(__float_as_uint(x[e]), rsX, (c + e < ncol) ? xrowoff[mb] + (uint32_t)(c + e) * 4 : kOutOfRange);
+          }
+        } else if constexpr (kX == 1) {
+          if constexpr (kFast) {
+            const u32x2_t v = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+            buf_store_b64(v, rsX, xrowoff[mb] + (uint32_t)c * 2);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              buf_store_b16((uint16_t)f32_to_bf16(x[e]), rsX, (c + e < ncol) ? xrowoff[mb] + (uint32_t)(c + e) * 2 : kOutOfRange);
+          }
+        } else if constexpr (kX == 3) {
+          if (p.X) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t off = (c + e < ncol) ? xrowoff[mb] + (uint32_t)(c + e) * xes : kOutOfRange;
+              if (p.x_f32) buf_store_b32(__float_as_uint(x[e]), rsX, off);
+              else buf_store_b16((uint16_t)f32_to_bf16(x[e]), rsX, off);
+            }
+          }
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if constexpr (ROW == 2) y[e] = __builtin_fmaf((x[e] - st[mb].x) * st[mb].y, g[e], be[e]);
@@ -758,10 +793,20 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
       }
     });
   };
+  using X0 = std::integral_constant<int, 0>;
+  using X1 = std::integral_constant<int, 1>;
+  using X2 = std::integral_constant<int, 2>;
+  using XR = std::integral_constant<int, 3>;
   if (p.c_f32) {
-    store_pass(std::true_type{});
+    if constexpr (!kFast) store_pass(std::true_type{}, XR{});
+    else if (!p.X) store_pass(std::true_type{}, X0{});
+    else if (p.x_f32) store_pass(std::true_type{}, X2{});
+    else store_pass(std::true_type{}, X1{});
   } else {
-    store_pass(std::false_type{});
+    if constexpr (!kFast) store_pass(std::false_type{}, XR{});
+    else if (!p.X) store_pass(std::false_type{}, X0{});
+    else if (p.x_f32) store_pass(std::false_type{}, X2{});
+    else store_pass(std::false_type{}, X1{});
     if constexpr (kFast) {
       // bf16 tile [256][256] from LDS to C: each wave store covers two whole
       // 512-byte row segments; rows >= M fall outside the buffer and are dropped

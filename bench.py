@@ -11,7 +11,7 @@ cache). Prints one JSON line:
              with the mean kernel time from HIP events on the launch stream
   cpu_baseline  the fp64 oracle timed on the host cores on a bounded row sample
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--store-x]
 """
 from __future__ import annotations
 
@@ -49,6 +49,9 @@ def parse():
                     help="measured HBM bytes per launch (written from rocprofv3 counters)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="calibration: time a plain device copy of MIB MiB (for the byte counters)")
+    ap.add_argument("--store-x", action="store_true",
+                    help="GEMM + epilogue workloads: also store x, the input of the row operation, as a second "
+                         "bf16 [M, N] output (e.g. the new residual stream of a pre-norm block)")
     ap.add_argument("--rotate-mb", type=int, default=512,
                     help="cycle through copies of the inputs totalling at least this many MiB, so that they are "
                          "read from HBM rather than from the 256 MiB last-level cache (0: one set)")
@@ -85,9 +88,9 @@ def flops_of(w) -> float:
     return 2.0 * d["batch"] * d["M"] * (d["K"] * d["L"] + d["L"] * d["N"])
 
 
-def bytes_of(w) -> float:
-    """Algorithmic HBM bytes: every input read once, the output written once."""
-    import gen
+def bytes_of(w, store_x: bool = False) -> float:
+    """Algorithmic HBM bytes: every input read once, the output (and X when
+    stored) written once."""
     tot = 0.0
     for t in w.tensors:
         tot += np.prod(w.shape(t)) * (2 if t.dtype == "bf16" else 4)
@@ -95,6 +98,8 @@ def bytes_of(w) -> float:
     out_es = 4 if w.params.get("out_dtype") == "f32" else 2
     if w.kind == "gemm_epilogue":
         tot += d["M"] * d["N"] * out_es
+        if store_x:
+            tot += d["M"] * d["N"] * 2
     else:
         tot += d["batch"] * d["M"] * d["N"] * out_es
     return float(tot)
@@ -104,11 +109,11 @@ def is_f32(w) -> bool:
     return any(t.dtype == "f32" for t in w.tensors if t.name == "A")
 
 
-def roofline_of(w, kernel_ms: float):
+def roofline_of(w, kernel_ms: float, store_x: bool = False):
     """The roofline that bounds the kernel: HBM when the workload's flop/byte is
     below the ridge point (peak flops / HBM bandwidth), the MFMA peak above it.
     Returns (bound, unit, peak, achieved, intensity, ridge)."""
-    flops, nbytes = flops_of(w), bytes_of(w)
+    flops, nbytes = flops_of(w), bytes_of(w, store_x)
     peak_flops = PEAK_F32_TFLOPS if is_f32(w) else PEAK_BF16_TFLOPS
     intensity = flops / nbytes
     ridge = peak_flops * 1e12 / (HBM_GBPS * 1e9)
@@ -117,22 +122,24 @@ def roofline_of(w, kernel_ms: float):
     return "mfma", "TFLOP/s", peak_flops, flops / (kernel_ms * 1e-3) / 1e12, intensity, ridge
 
 
-def make_call(w, dev, torch, cf):
+def make_call(w, dev, torch, cf, store_x: bool = False):
     """Device tensors + a closure launching one fused kernel on the current stream."""
     p = w.params
     out_dt = torch.float32 if p.get("out_dtype") == "f32" else torch.bfloat16
     stream = torch.cuda.current_stream()
     if w.kind == "gemm_epilogue":
         d = w.dims
+        X = torch.empty(d["M"], d["N"], dtype=torch.bfloat16, device="cuda") if store_x else None
         e = cf.make_epilogue(alpha=p["alpha"], bias=dev.get("bias"), residual=dev.get("residual"),
                              act=p["act"], row_op=p["row_op"], gamma=dev.get("gamma", dev.get("weight")),
-                             beta=dev.get("beta"), eps=p.get("eps", 0.0))
+                             beta=dev.get("beta"), eps=p.get("eps", 0.0), x_out=X)
         nbytes = cf.cf_gemm_epilogue_workspace_size(d["M"], d["N"], d["K"], e)
         ws = cf.Workspace("cuda").get(nbytes)
         C = torch.empty(d["M"], d["N"], dtype=out_dt, device="cuda")
 
         def call():
             cf.cf_gemm_epilogue(dev["A"], dev["B"], C, epi=e, workspace=ws, stream=stream)
+        call.keep = X        # the second output lives as long as the closure
         return call, C, ws, nbytes
     d = w.dims
     e = cf.make_epilogue(alpha=p["alpha"], act=p["act"], row_op=p["row_op"])
@@ -222,6 +229,8 @@ def main():
     sys.path.insert(0, os.path.join(ROOT, "tests"))
 
     w = gen.workload(args.workload)
+    if args.store_x and w.kind != "gemm_epilogue":
+        raise SystemExit("--store-x applies to the GEMM + epilogue workloads")
     if args.plain:
         import dataclasses
         w = dataclasses.replace(w, params={**w.params, "row_op": "none", "act": "none"},
@@ -239,7 +248,7 @@ def main():
     devs = [dev] + [{k: v.clone() for k, v in dev.items()} for _ in range(nset - 1)]
     calls = []
     for d_ in devs:
-        call, out, ws, ws_bytes = make_call(w, d_, torch, cf)
+        call, out, ws, ws_bytes = make_call(w, d_, torch, cf, args.store_x)
         calls.append(call)
 
     for i in range(max(args.warmup, nset)):
@@ -263,9 +272,9 @@ def main():
     flops = flops_of(w)
     value = flops / (ms_per_step * 1e-3) / 1e12
     in_f32 = is_f32(w)
-    bound, unit, peak, achieved, intensity, ridge = roofline_of(w, kernel_ms)
+    bound, unit, peak, achieved, intensity, ridge = roofline_of(w, kernel_ms, args.store_x)
     traffic = None
-    if os.path.exists(args.traffic) and not args.plain:
+    if os.path.exists(args.traffic) and not args.plain and not args.store_x:
         try:
             rec = json.load(open(args.traffic))
             if rec.get("kernel_source_hash") == kernel_source_hash():
@@ -285,13 +294,14 @@ def main():
         "vs_baseline": None,
         "dtype": "f32" if in_f32 else "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name + ("/identity-epilogue" if args.plain else ""), **w.dims,
+        "config": {"workload": w.name + ("/identity-epilogue" if args.plain else "")
+                   + ("+x_out" if args.store_x else ""), **w.dims,
                    "out_dtype": w.params.get("out_dtype"), "input_sets": nset, "input_bytes_per_set": in_bytes},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "arithmetic_intensity": round(intensity, 1), "ridge": round(ridge, 1)},
         "kernel_ms": round(kernel_ms, 4),
-        "algorithmic_bytes": bytes_of(w),
+        "algorithmic_bytes": bytes_of(w, args.store_x),
         "intermediate_hbm_bytes": 0,
         "workspace_bytes": ws_bytes,
     }

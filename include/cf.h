@@ -70,7 +70,18 @@ typedef enum {
  *   6. cast to the output dtype (round to nearest even for bf16) and store.
  * bias, gamma and beta are vectors of N elements of dtype `vec_dtype`;
  * residual is an [M, N] matrix of dtype `residual_dtype` with leading
- * dimension ld_residual. */
+ * dimension ld_residual.
+ *
+ * Second output (x_out, optional, cf_gemm_epilogue only): the result of stage
+ * 4, the x that the row operation reads, is also cast to x_out_dtype and
+ * stored to x_out ([M, N], leading dimension ld_x_out, caller-owned device
+ * memory that must not overlap C, A, B or the residual). The epilogue is then
+ * a dataflow graph with two sinks, one on each side of the reduction boundary
+ * (the review's "What carries the argument": the epilogue is split into
+ * chained DAGs at its reductions); a pre-norm transformer block uses it to
+ * keep the new residual stream x = P + residual beside y = RMSNorm(x). In the
+ * stored X only the cast rounds: x is the same fp32 value the row operation
+ * consumes. NULL (the default from cf_epilogue_init) stores nothing. */
 typedef struct cf_epilogue {
   uint32_t struct_size;     /* must be sizeof(cf_epilogue)                        */
   float alpha;
@@ -84,6 +95,9 @@ typedef struct cf_epilogue {
   const void* gamma;
   const void* beta;
   float eps;
+  void* x_out;              /* optional second output: x after stage 4 (see above) */
+  int64_t ld_x_out;         /* leading dimension of x_out in elements, >= N       */
+  cf_dtype x_out_dtype;     /* CF_BF16 or CF_F32                                  */
 } cf_epilogue;
 
 /* Fills *epi with the identity epilogue (alpha 1, no bias/residual/act/row op). */
@@ -121,6 +135,9 @@ cf_status cf_workspace_status(const void* ws, void* stream);
  *   epi     epilogue descriptor (NULL = identity).
  *   ws      workspace of at least cf_gemm_epilogue_workspace_size() bytes,
  *           cleared once by cf_workspace_init(); may be NULL when that size is 0.
+ *   epi->x_out (optional) receives x before the row operation, [M, N] with
+ *           leading dimension epi->ld_x_out >= N, dtype epi->x_out_dtype,
+ *           aligned to its element size; CF_ERR_INVALID_ARGUMENT otherwise.
  * M, N or K may be 0 (nothing is launched when M or N is 0; K = 0 gives P = 0).
  * Row operations need N <= 65536. */
 cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K,
@@ -140,7 +157,8 @@ cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K,
  *   B1  [L, N], leading dimension ldb1, batch stride sb1 (0 = shared).
  *   O   [M, N], leading dimension ldo, batch stride so.
  *   mid epilogue on S: alpha, bias (vector of L), act, and row_op in
- *       {CF_ROW_NONE, CF_ROW_SOFTMAX}; residual/gamma/beta must be NULL.
+ *       {CF_ROW_NONE, CF_ROW_SOFTMAX}; residual/gamma/beta/x_out must be NULL
+ *       (CF_ERR_UNSUPPORTED otherwise: S is never stored).
  * The second GEMM takes P in bf16 (the MFMA operand type); for the softmax the
  * operand is round(2^(t - c)) with t = log2(e) * S and an integer per-row c,
  * and the row sum used for normalisation is taken before rounding.

@@ -155,6 +155,12 @@ def gemm_epilogue(A: np.ndarray, B: np.ndarray, *, alpha: float = 1.0,
     RMSNorm weight when row_op is "rmsnorm".
     """
     X = elementwise_stage(matmul(A, B), alpha, bias, residual, act)
+    return row_stage(X, row_op, gamma, beta, eps)
+
+
+def row_stage(X: np.ndarray, row_op: str, gamma: Optional[np.ndarray] = None,
+              beta: Optional[np.ndarray] = None, eps: float = 0.0) -> np.ndarray:
+    """The stage after the reduction boundary: one row operation on X."""
     if row_op == "none":
         return X
     if row_op == "softmax":
@@ -164,6 +170,21 @@ def gemm_epilogue(A: np.ndarray, B: np.ndarray, *, alpha: float = 1.0,
     if row_op == "rmsnorm":
         return rms_norm(X, gamma, eps)
     raise ValueError(f"unknown row_op {row_op!r}")
+
+
+def gemm_epilogue_with_x(A: np.ndarray, B: np.ndarray, *, alpha: float = 1.0,
+                         bias: Optional[np.ndarray] = None, residual: Optional[np.ndarray] = None,
+                         act: str = "none", row_op: str = "none", gamma: Optional[np.ndarray] = None,
+                         beta: Optional[np.ndarray] = None, eps: float = 0.0):
+    """The same epilogue with two stored results, returned as (Y, X): X is the
+    elementwise stage's output, the tensor the row operation reads, and Y the
+    row operation's output. The review describes the epilogue as chained DAGs
+    cut at its reductions (ComFuse review, "What carries the argument"); a DAG
+    with a sink on each side of the boundary stores both, as a pre-norm block
+    does with its new residual stream X = P + R beside RMSNorm(X). Both are
+    float64 and unrounded."""
+    X = elementwise_stage(matmul(A, B), alpha, bias, residual, act)
+    return row_stage(X, row_op, gamma, beta, eps), X
 
 
 # --------------------------------------------------------------------------- back-to-back GEMM

@@ -216,6 +216,41 @@ def pin_gemm_epilogue_composition(o):
                 _close_dec(gv, wv, rtol=1e-12, atol=1e-13)
 
 
+def pin_two_outputs(o):
+    """(Y, X) of the two-sink epilogue against brute force: X is the elementwise
+    stage (exact rationals), Y the row operation of that X (40-digit decimals)."""
+    rng = np.random.default_rng(11)
+    m, k, n = 3, 5, 4
+    A = _bf16_values(rng, (m, k))
+    B = _bf16_values(rng, (k, n))
+    bias = _bf16_values(rng, (n,))
+    R = _bf16_values(rng, (m, n))
+    g = 1 + 0.1 * _bf16_values(rng, (n,))
+    be = 0.1 * _bf16_values(rng, (n,))
+    alpha = 0.75
+    E = X.mm(X.mat(A), X.mat(B))
+    for act in ("none", "relu"):
+        Xf = [[Fraction(alpha) * E[i][j] + X.F(bias[j]) + X.F(R[i, j]) for j in range(n)] for i in range(m)]
+        if act == "relu":
+            Xf = [[max(v, Fraction(0)) for v in row] for row in Xf]
+        for row_op in ("none", "softmax", "layernorm", "rmsnorm"):
+            Y, Xo = o.gemm_epilogue_with_x(A, B, alpha=alpha, bias=bias, residual=R, act=act,
+                                           row_op=row_op, gamma=g, beta=be, eps=1e-5)
+            for i in range(m):
+                for j in range(n):
+                    assert abs(Fraction(float(Xo[i, j])) - Xf[i][j]) <= Fraction(1, 2 ** 48), (act, row_op, i, j)
+                if row_op == "none":
+                    want = [X.D(v) for v in Xf[i]]
+                elif row_op == "softmax":
+                    want = X.softmax_row(Xf[i])
+                elif row_op == "layernorm":
+                    want = X.layernorm_row(Xf[i], 1e-5, g, be)
+                else:
+                    want = X.rmsnorm_row(Xf[i], 1e-5, g)
+                for gv, wv in zip(Y[i], want):
+                    _close_dec(gv, wv, rtol=1e-12, atol=1e-13)
+
+
 # --------------------------------------------------------------------------- back-to-back GEMM
 
 def pin_b2b_relu(o):
@@ -305,7 +340,7 @@ def pin_b2b_softmax(o):
 
 
 ALL_PINS = [pin_round_bf16, pin_widen_bf16, pin_matmul_exact, pin_stage1_exact, pin_softmax,
-            pin_layernorm, pin_rmsnorm, pin_gemm_epilogue_composition, pin_b2b_relu,
+            pin_layernorm, pin_rmsnorm, pin_gemm_epilogue_composition, pin_two_outputs, pin_b2b_relu,
             pin_b2b_softmax]
 
 

@@ -34,6 +34,9 @@ def test_algorithmic_counts():
     assert bench.flops_of(w) == 2.0 * 8192 * 4096 * 4096
     # A, B, gamma, beta read once (bf16) + the bf16 output written once
     assert bench.bytes_of(w) == 2 * (8192 * 4096 + 4096 * 4096 + 4096 + 4096 + 8192 * 4096)
+    # the second output X of a pre-norm block adds one bf16 [M, N] write
+    w3 = gen.workload("c3_gemm_residual_rmsnorm")
+    assert bench.bytes_of(w3, store_x=True) - bench.bytes_of(w3) == 2 * 16384 * 4096
     w5 = gen.workload("c5_b2b_attention")
     assert bench.flops_of(w5) == 2.0 * 512 * 1024 * (64 * 1024 + 1024 * 64)
 

@@ -97,6 +97,11 @@ def epi(**kw):
     (dict(N=4096, ldb=4096, ldc=4096, epi=epi(row_op=2)), cf.CF_ERR_WORKSPACE),   # needs a workspace
     (dict(N=4096, ldb=4096, ldc=4096, epi=epi(row_op=2), ws=PW + 8, wsb=1 << 22), cf.CF_ERR_WORKSPACE),
     (dict(N=4096, ldb=4096, ldc=4096, epi=epi(row_op=2), ws=PW, wsb=4096), cf.CF_ERR_WORKSPACE),
+    (dict(epi=epi(x_out=PW, ld_x_out=8)), cf.CF_ERR_INVALID_ARGUMENT),                  # ld below N
+    (dict(epi=epi(x_out=PW + 1, ld_x_out=64)), cf.CF_ERR_INVALID_ARGUMENT),             # misaligned bf16
+    (dict(epi=epi(x_out=PW + 2, ld_x_out=64, x_out_dtype=0)), cf.CF_ERR_INVALID_ARGUMENT),   # misaligned f32
+    (dict(epi=epi(x_out=PW, ld_x_out=64, x_out_dtype=7)), cf.CF_ERR_INVALID_ARGUMENT),  # bad dtype
+    (dict(M=1 << 20, epi=epi(x_out=PW, ld_x_out=1024, x_out_dtype=0)), cf.CF_ERR_UNSUPPORTED),  # 4 GiB X
     (dict(M=0), cf.CF_OK),            # empty problems launch nothing
     (dict(N=0), cf.CF_OK),
 ])
@@ -123,6 +128,7 @@ def b2b(batch=1, M=64, K=64, L=64, N=64, A=PA, lda=64, sa=0, B0=PB, ldb0=64, sb0
     (dict(lda=68), cf.CF_ERR_UNSUPPORTED),                          # leading dimension not 16-byte aligned
     (dict(mid=epi(row_op=2)), cf.CF_ERR_UNSUPPORTED),               # LayerNorm between two GEMMs
     (dict(mid=epi(residual=PW, ld_residual=64)), cf.CF_ERR_UNSUPPORTED),
+    (dict(mid=epi(x_out=PW, ld_x_out=64)), cf.CF_ERR_UNSUPPORTED),   # S is never stored
     (dict(batch=0), cf.CF_OK),
 ])
 def test_b2bgemm_argument_checks(kw, status):
@@ -142,5 +148,6 @@ def test_workspace_sizes():
 @pytest.mark.skipif(gpu_present(), reason="would launch on fake pointers; valid calls are covered by the GPU tests")
 def test_valid_calls_report_no_device():
     assert gemm(epi=epi(row_op=1, bias=PW)) == cf.CF_ERR_NO_DEVICE
+    assert gemm(epi=epi(row_op=3, x_out=PW, ld_x_out=64)) == cf.CF_ERR_NO_DEVICE
     assert b2b(mid=epi(row_op=1, alpha=0.125)) == cf.CF_ERR_NO_DEVICE
     assert lib.cf_workspace_init(PW, 4096, None) == cf.CF_ERR_NO_DEVICE

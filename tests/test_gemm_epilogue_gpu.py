@@ -231,3 +231,87 @@ def test_full_size_sampled_rows(name):
     # every row of a LayerNorm/RMSNorm output is finite
     assert torch.isfinite(c16.float()).all()
     print(f"{name} full: relF {r:.2e} maxabs {m:.2e}", flush=True)
+
+
+# ---------------------------------------------------------------------------- second output: x before the row op
+
+def run_x(A, B, out_dtype, x_dtype, **epi):
+    """Like run(), with X (the elementwise stage's result) stored to a second output."""
+    M, N = A.shape[0], B.shape[1]
+    Xo = torch.full((M, N), float("nan"), dtype=x_dtype, device="cuda")
+    C = run(A, B, out_dtype, x_out=Xo, **epi)
+    return C, Xo
+
+
+def check_two_outputs(w, dev, ref, kw, what):
+    p = w.params
+    Yr, Xr = oracle.gemm_epilogue_with_x(
+        ref["A"], ref["B"], alpha=p["alpha"], bias=ref.get("bias"), residual=ref.get("residual"), act=p["act"],
+        row_op=p["row_op"], gamma=ref.get("gamma", ref.get("weight")), beta=ref.get("beta"), eps=p.get("eps", 0.0))
+    y_plain = run(dev["A"], dev["B"], torch.bfloat16, **kw)
+    y32, x32 = run_x(dev["A"], dev["B"], torch.float32, torch.float32, **kw)
+    P.assert_close(P.gpu_to_f64(y32), Yr, P.REL_F_BF16, P.MAX_ABS_BF16, what + " Y f32")
+    P.assert_close(P.gpu_to_f64(x32), Xr, P.REL_F_BF16, P.MAX_ABS_BF16, what + " X f32")
+    y16, x16 = run_x(dev["A"], dev["B"], torch.bfloat16, torch.bfloat16, **kw)
+    # the second sink changes nothing in the first, and stores the same fp32 x rounded once
+    assert torch.equal(y16.view(torch.int16), y_plain.view(torch.int16)), what + ": Y changed by storing X"
+    P.assert_bf16_consistent(y16, y32, Yr, what + " Y bf16")
+    P.assert_bf16_consistent(x16, x32, Xr, what + " X bf16")
+    r, m = P.metrics(P.gpu_to_f64(x32), Xr)
+    print(f"{what}: X relF {r:.2e} maxabs {m:.2e}", flush=True)
+
+
+def test_x_out_residual_rmsnorm_fast_path():
+    # pre-norm block: the new residual stream X = P + R beside Y = RMSNorm(X)
+    w, dev, ref = P.inputs("c3_gemm_residual_rmsnorm", seed=6, M=300, N=1024, K=512)
+    check_two_outputs(w, dev, ref, epi_of(w, dev), "C3-shaped 300x1024x512 + X")
+
+
+@pytest.mark.parametrize("row_op", ["none", "softmax", "layernorm"])
+def test_x_out_with_bias_alpha_relu(row_op):
+    w, dev, ref = P.inputs("c3_gemm_residual_rmsnorm", seed=7, M=256, N=768, K=256)
+    bias = torch.linspace(-0.3, 0.3, 768, device="cuda").to(torch.bfloat16)
+    beta = torch.linspace(-0.1, 0.1, 768, device="cuda").to(torch.bfloat16)
+    import dataclasses
+    w2 = dataclasses.replace(w, params={**w.params, "alpha": 0.5, "act": "relu", "row_op": row_op})
+    dev2 = {**dev, "bias": bias, "beta": beta}
+    ref2 = {**ref, "bias": P.gpu_to_f64(bias), "beta": P.gpu_to_f64(beta)}
+    check_two_outputs(w2, dev2, ref2, epi_of(w2, dev2), f"X with alpha/bias/relu, {row_op}")
+
+
+@pytest.mark.parametrize("shape", [(33, 65, 17), (300, 520, 200), (1, 1000, 9)])
+def test_x_out_general_path(shape):
+    M, N, K = shape
+    w, dev, ref = P.inputs("c3_gemm_residual_rmsnorm", seed=8, M=M, N=N, K=K)
+    check_two_outputs(w, dev, ref, epi_of(w, dev), f"X general path {shape}")
+
+
+def test_x_out_full_size_sampled_rows():
+    w, dev, ref = P.inputs("c3_gemm_residual_rmsnorm", seed=0)
+    rows = np.random.default_rng(1).choice(w.dims["M"], 24, replace=False)
+    rows = np.concatenate([rows, [0, w.dims["M"] - 1]])
+    p = w.params
+    Yr, Xr = oracle.gemm_epilogue_with_x(ref["A"][rows], ref["B"], residual=ref["residual"][rows],
+                                         row_op="rmsnorm", gamma=ref["weight"], eps=p["eps"])
+    y16, x16 = run_x(dev["A"], dev["B"], torch.bfloat16, torch.bfloat16, **epi_of(w, dev))
+    idx = torch.as_tensor(rows, device="cuda")
+    P.assert_bf16_within(P.gpu_to_f64(y16[idx]), Yr, "C3 full Y")
+    P.assert_bf16_within(P.gpu_to_f64(x16[idx]), Xr, "C3 full X")
+    assert not torch.isnan(x16.float()).any(), "X not fully written"
+
+
+# ---------------------------------------------------------------------------- wide strips
+
+@pytest.mark.parametrize("N", [8192, 16384])
+@pytest.mark.parametrize("row_op", ["softmax", "layernorm", "rmsnorm"])
+def test_wide_strips(N, row_op):
+    # strips of 32 and 64 column tiles: every workgroup of a strip merges that
+    # many peers' partial statistics (the C2/C3 strips have 16)
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=9, M=300, N=N, K=128)
+    R = oracle.gemm_epilogue(ref["A"], ref["B"], row_op=row_op, gamma=ref["gamma"],
+                             beta=ref["beta"] if row_op == "layernorm" else None, eps=1e-5)
+    kw = dict(row_op=row_op, gamma=dev["gamma"], beta=dev["beta"] if row_op == "layernorm" else None, eps=1e-5)
+    c32 = run(dev["A"], dev["B"], torch.float32, **kw)
+    P.assert_close(P.gpu_to_f64(c32), R, P.REL_F_BF16, P.MAX_ABS_BF16, f"N={N} {row_op}")
+    c16 = run(dev["A"], dev["B"], torch.bfloat16, **kw)
+    P.assert_bf16_consistent(c16, c32, R, f"N={N} {row_op} bf16")

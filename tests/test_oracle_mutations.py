@@ -47,6 +47,13 @@ MUTATIONS = {
         "r = round_bf16(pt)\n    return r, r.sum(axis=-1, keepdims=True)")],
     "b2b_operand_not_rounded": [("Pm = round_bf16(S) if round_operand else S", "Pm = S")],
     "b2b_keys_layout_ignored": [("B0 = np.swapaxes(B0, -1, -2)", "B0 = B0")],
+    "x_output_after_row_op": [(
+        "    return row_stage(X, row_op, gamma, beta, eps), X\n",
+        "    Y = row_stage(X, row_op, gamma, beta, eps)\n    return Y, Y\n")],
+    "x_output_before_residual": [(
+        "    X = elementwise_stage(matmul(A, B), alpha, bias, residual, act)\n    return row_stage(X, row_op, gamma, beta, eps), X\n",
+        "    X = elementwise_stage(matmul(A, B), alpha, bias, residual, act)\n"
+        "    return row_stage(X, row_op, gamma, beta, eps), elementwise_stage(matmul(A, B), alpha, bias, None, act)\n")],
     "b2b_relu_dropped": [(
         "S = elementwise_stage(matmul(A, B0), alpha, bias, None, act)",
         "S = elementwise_stage(matmul(A, B0), alpha, bias, None, 'none')")],

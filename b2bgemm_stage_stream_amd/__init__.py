@@ -27,6 +27,7 @@ CF_OK, CF_ERR_INVALID_ARGUMENT, CF_ERR_UNSUPPORTED, CF_ERR_WORKSPACE, CF_ERR_NO_
 CF_F32, CF_BF16 = 0, 1
 ACT = {"none": 0, "relu": 1}
 ROW_OP = {"none": 0, "softmax": 1, "layernorm": 2, "rmsnorm": 3}
+MASK = {"none": 0, "causal": 1}
 
 
 class cf_epilogue(ctypes.Structure):
@@ -46,6 +47,7 @@ class cf_epilogue(ctypes.Structure):
         ("x_out", ctypes.c_void_p),
         ("ld_x_out", ctypes.c_int64),
         ("x_out_dtype", ctypes.c_int),
+        ("mask", ctypes.c_int),
     ]
 
 
@@ -125,15 +127,18 @@ def _ptr(t) -> Optional[int]:
 
 
 def make_epilogue(*, alpha: float = 1.0, bias=None, residual=None, act: str = "none",
-                  row_op: str = "none", gamma=None, beta=None, eps: float = 0.0, x_out=None) -> cf_epilogue:
+                  row_op: str = "none", gamma=None, beta=None, eps: float = 0.0, x_out=None,
+                  mask: str = "none") -> cf_epilogue:
     """cf_epilogue descriptor from tensors (bias/gamma/beta share one dtype).
-    ``x_out``: optional [M, N] tensor that receives x before the row operation."""
+    ``x_out``: optional [M, N] tensor that receives x before the row operation.
+    ``mask``: "causal" for the softmax of cf_b2bgemm."""
     e = cf_epilogue()
     _lib.cf_epilogue_init(ctypes.byref(e))
     e.alpha = float(alpha)
     e.act = ACT[act]
     e.row_op = ROW_OP[row_op]
     e.eps = float(eps)
+    e.mask = MASK[mask]
     vecs = [v for v in (bias, gamma, beta) if v is not None]
     if vecs:
         codes = {_dtype_code(v) for v in vecs}

@@ -100,6 +100,8 @@ cf_status check_epilogue(const cf_epilogue* epi, int64_t N, bool allow_row_ops_n
     if (epi->ld_residual < N || epi->ld_residual < 1) return CF_ERR_INVALID_ARGUMENT;
     if (!aligned(epi->residual, dsize(epi->residual_dtype))) return CF_ERR_INVALID_ARGUMENT;
   }
+  if (epi->mask != CF_MASK_NONE && epi->mask != CF_MASK_CAUSAL) return CF_ERR_INVALID_ARGUMENT;
+  if (epi->mask != CF_MASK_NONE && (allow_residual || epi->row_op != CF_ROW_SOFTMAX)) return CF_ERR_UNSUPPORTED;
   if (epi->x_out) {
     if (!allow_residual) return CF_ERR_UNSUPPORTED;
     if (epi->x_out_dtype != CF_BF16 && epi->x_out_dtype != CF_F32) return CF_ERR_INVALID_ARGUMENT;
@@ -328,6 +330,8 @@ cf_status cf_b2bgemm(int64_t batch, int64_t M, int64_t K, int64_t L, int64_t N, 
   p.bias_f32 = (mid && mid->vec_dtype == CF_F32) ? 1 : 0;
   p.b0_lk = b0_is_lk;
   p.o_vec = aligned(O, 16) && ldo % 4 == 0 && so % 4 == 0;
+  p.causal = mid && mid->mask == CF_MASK_CAUSAL;
+  p.coff = (int)(L - M);
   if (!cf::b2b_supported(p)) return CF_ERR_UNSUPPORTED;
 
   int dev;

@@ -73,7 +73,22 @@ __global__ __launch_bounds__(kThreads) void b2b_kernel(B2bParams p) {
 
   for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
     const int b = tile / mtiles;
-    const int m0 = (tile - b * mtiles) * kBM;
+    // causal: work grows with the row tile; rotate it by the round when the
+    // grid is a multiple of the tiles per batch entry (every workgroup then
+    // gets each row position once) and take the tiles that see the most keys
+    // first
+    int mt = tile - b * mtiles;
+    if (p.causal) {
+      if (gridDim.x % mtiles == 0) mt = (mt + tile / (int)gridDim.x) % mtiles;
+      mt = mtiles - 1 - mt;
+    }
+    const int m0 = mt * kBM;
+    // causal: segments past the last key any row of the tile sees are skipped
+    int nch = nchunks;
+    if (p.causal) {
+      const int last = min(m0 + kBM - 1, p.M - 1) + p.coff;
+      nch = last < 0 ? 0 : min(nchunks, last / kLC + 1);
+    }
     const uint16_t* Ab = (const uint16_t*)p.A + (size_t)b * p.sa;
     const uint16_t* B0b = (const uint16_t*)p.B0 + (size_t)b * p.sb0;
     const uint16_t* B1b = (const uint16_t*)p.B1 + (size_t)b * p.sb1;
@@ -221,12 +236,15 @@ __global__ __launch_bounds__(kThreads) void b2b_kernel(B2bParams p) {
     float cst = -INFINITY;   // softmax: integer stabiliser of this row (same in both lane halves)
     float lsum = 0.0f;       // softmax: this lane's part of the unrounded row sum
 
-    load_chunk(0);
-    store_chunk(0);
-    if (nchunks > 1) load_chunk(1);
+    if (nch > 0) {
+      load_chunk(0);
+      store_chunk(0);
+      if (nch > 1) load_chunk(1);
+    }
     __syncthreads();
 
-    for (int lc = 0; lc < nchunks; ++lc) {
+    const int my_row = m0 + wave * 32 + r32;
+    for (int lc = 0; lc < nch; ++lc) {
       const uint8_t* s0 = smem + (lc & 1) * Cfg::kStage;
       const uint8_t* s1 = s0 + Cfg::kB0Bytes;
       // GEMM1: two 32-blocks of l
@@ -242,8 +260,8 @@ __global__ __launch_bounds__(kThreads) void b2b_kernel(B2bParams p) {
         }
       }
       // the next chunk goes to the other LDS buffer while this one is consumed
-      if (lc + 1 < nchunks) store_chunk((lc + 1) & 1);
-      if (lc + 2 < nchunks) load_chunk(lc + 2);
+      if (lc + 1 < nch) store_chunk((lc + 1) & 1);
+      if (lc + 2 < nch) load_chunk(lc + 2);
 
       // F on registers; l of register r of block lb: lc*64 + lb*32 + 8(r>>2) + 4h + (r&3)
       const int lbase = lc * kLC + 4 * h;
@@ -255,7 +273,8 @@ __global__ __launch_bounds__(kThreads) void b2b_kernel(B2bParams p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int l = lbase + lb * 32 + 8 * (r >> 2) + (r & 3);
-            const float t = (kExact || l < p.L) ? sacc[lb][r] * scale : -INFINITY;
+            const bool vis = (kExact || l < p.L) && (!p.causal || l <= my_row + p.coff);
+            const float t = vis ? sacc[lb][r] * scale : -INFINITY;
             sacc[lb][r] = t;
             mx = fmaxf(mx, t);
           }
@@ -322,7 +341,10 @@ __global__ __launch_bounds__(kThreads) void b2b_kernel(B2bParams p) {
 
     // ---- normalise and store: oacc[nb][4q + e] is O[m][nb*32 + 8q + 4h + e]
     float inv = 1.0f;
-    if constexpr (kSoftmax) inv = 1.0f / sum_halves(lsum);
+    if constexpr (kSoftmax) {
+      const float ls = sum_halves(lsum);
+      inv = ls > 0.0f ? 1.0f / ls : 0.0f;   // 0 only for a causal row that sees no key
+    }
     const uint32_t row = (uint32_t)(m0 + wave * 32 + r32);
     const __amdgpu_buffer_rsrc_t rsO = make_rsrc((uint8_t*)p.O + (size_t)b * p.so * (p.out_f32 ? 4 : 2),
                                                  (uint32_t)((size_t)p.M * p.ldo * (p.out_f32 ? 4 : 2)));

@@ -59,7 +59,11 @@ __device__ inline int swz_tr256(int r) { return (2 * (r & 3)) ^ (4 * (r & 3)); }
 
 }  // namespace
 
-template <int KS, int NB, int MB_, bool kSoftmax, bool kB0LK>
+// kCausal (softmax only): key l is visible to row m iff l <= m + p.coff; the
+// segments past the last key a tile's rows see are not computed, the segment
+// on the diagonal is masked per element, and row tiles that see more keys are
+// scheduled first.
+template <int KS, int NB, int MB_, bool kSoftmax, bool kB0LK, bool kCausal = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kTThreads, kTThreads), amdgpu_waves_per_eu(2, 2)))
 void b2b_stream_kernel(B2bParams p) {
   using C = TCfg<KS, NB, MB_>;
@@ -139,18 +143,19 @@ void b2b_stream_kernel(B2bParams p) {
       b1_rd[nb] = (uint32_t)(C::kB0Bytes + (4 * (g >> 1) + (i >> 2)) * RB + 16 * ((4 * nb + c) ^ f) + 8 * (i & 1));
   }
 
-  auto issue = [&](int s, const u32x4_t& rs0, const u32x4_t& rs1) {
+  auto issue = [&](int s, int nseg, const u32x4_t& rs0, const u32x4_t& rs1) {
     const uint32_t st = (uint32_t)__builtin_amdgcn_readfirstlane(
         (int)(lds0 + (uint32_t)((s % NS) * C::kStage + wave * 1024)));
-    const bool ok = s < nchunks;
+    const bool ok = s < nseg;
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i)
       lds_dma16(st + i * 4096, is_b0[i] ? rs0 : rs1, ok ? goff[i] + (uint32_t)s * gstep[i] : kOutOfRange);
   };
 
-  // one segment: GEMM1, F, GEMM2 on stage buffer st; row block rb of the wave
+  // one segment: GEMM1, F, GEMM2 on stage buffer st; row block rb of the wave.
+  // wrow0: first row of this wave (causal masking)
   auto segment = [&](const uint8_t* st, int lc, const u32x4_t (&af)[MB][KS], f32x16_t (&oacc)[MB][NB],
-                     float (&cst)[MB], float (&lsum)[MB]) {
+                     float (&cst)[MB], float (&lsum)[MB], int wrow0) {
     f32x16_t sacc[MB][2];
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb)
@@ -174,6 +179,23 @@ void b2b_stream_kernel(B2bParams p) {
                                                                   __builtin_bit_cast(bf16x8_t, af[rb][ks]), sacc[rb][lb], 0, 0, 0);
       }
     // F: register r of block lb holds l = lc*64 + lb*32 + 8(r>>2) + 4h + (r&3)
+    if constexpr (kCausal) {
+      // the segment reaches past the diagonal for some row of this wave: hide
+      // the invisible keys (their extreme-side infinity drops out of the row
+      // extreme and gives exp2(-inf) = 0)
+      if (lc * kTLC + kTLC - 1 > wrow0 + p.coff) {
+        const float hide = scale >= 0.0f ? -INFINITY : INFINITY;
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb) {
+          const int lim = wrow0 + rb * 32 + r32 + p.coff - (lc * kTLC + 4 * h);   // visible iff l - base <= lim
+#pragma unroll
+          for (int lb = 0; lb < 2; ++lb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (lb * 32 + 8 * (r >> 2) + (r & 3) > lim) sacc[rb][lb][r] = hide;
+        }
+      }
+    }
     u32x4_t pf[MB][4];
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb) {
@@ -205,12 +227,14 @@ void b2b_stream_kernel(B2bParams p) {
           lsum[rb] = __builtin_amdgcn_ldexpf(lsum[rb], sh);
         }
         cst[rb] = cn;
+        // -inf only while a causal row has seen no key; its terms are all 0
+        const float cs = (kCausal && cn == -INFINITY) ? 0.0f : cn;
 #pragma unroll
         for (int lb = 0; lb < 2; ++lb) {
           float e[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            e[r] = fast_exp2(__builtin_fmaf(sacc[rb][lb][r], scale, -cn));
+            e[r] = fast_exp2(__builtin_fmaf(sacc[rb][lb][r], scale, -cs));
             lsum[rb] += e[r];
           }
 #pragma unroll
@@ -263,7 +287,7 @@ void b2b_stream_kernel(B2bParams p) {
     const u32x4_t rs0 = rsrc_words(p.B0, (uint32_t)((size_t)(kB0LK ? p.L : C::K) * p.ldb0 * 2));
     const u32x4_t rs1 = rsrc_words(p.B1, (uint32_t)((size_t)p.L * p.ldb1 * 2));
 #pragma unroll
-    for (int s = 0; s < NS; ++s) issue(s, rs0, rs1);
+    for (int s = 0; s < NS; ++s) issue(s, nchunks, rs0, rs1);
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -288,7 +312,20 @@ void b2b_stream_kernel(B2bParams p) {
       b = e / mtiles;
       mt = e % mtiles;
     }
+    if constexpr (kCausal) {
+      // causal work grows with the row tile: when the stride is a multiple of
+      // the tiles per batch entry, rotate the row tile by the round so that
+      // every workgroup gets each row position once (the tiles of one entry
+      // still run in the same round); tiles that see the most keys first
+      if (estep % mtiles == 0) mt = (mt + e / estep) % mtiles;
+      mt = mtiles - 1 - mt;
+    }
     const int m0 = mt * C::BM;
+    int nseg = nchunks;
+    if constexpr (kCausal) {
+      const int last = min(m0 + C::BM - 1, p.M - 1) + p.coff;
+      nseg = last < 0 ? 0 : min(nchunks, last / kTLC + 1);
+    }
     const uint16_t* Ab = (const uint16_t*)p.A + (size_t)b * p.sa;
     const __amdgpu_buffer_rsrc_t rsA = make_rsrc(Ab, (uint32_t)((size_t)p.M * p.lda * 2));
     const u32x4_t rs0 = rsrc_words((const uint16_t*)p.B0 + (size_t)b * p.sb0,
@@ -297,7 +334,7 @@ void b2b_stream_kernel(B2bParams p) {
 
     if (!resident) {
 #pragma unroll
-      for (int s = 0; s < NS - 1; ++s) issue(s, rs0, rs1);
+      for (int s = 0; s < NS - 1; ++s) issue(s, nseg, rs0, rs1);
     }
     // A fragments of this wave's rows (rows >= M read as zero)
     u32x4_t af[MB][KS];
@@ -321,16 +358,17 @@ void b2b_stream_kernel(B2bParams p) {
       lsum[rb] = 0.0f;
     }
 
-    for (int lc = 0; lc < nchunks; ++lc) {
+    const int wrow0 = m0 + wave * MB * 32;
+    for (int lc = 0; lc < nseg; ++lc) {
       if (!resident) {
         // segment lc complete in every thread, all reads of segment lc - 1 done
         asm volatile("" ::: "memory");
         wait_vm_lgkm0<(NS - 2) * C::kLoads>();
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        issue(lc + NS - 1, rs0, rs1);   // into the buffer of segment lc - 1
+        issue(lc + NS - 1, nseg, rs0, rs1);   // into the buffer of segment lc - 1
       }
-      segment(smem + (lc % NS) * C::kStage, lc, af, oacc, cst, lsum);
+      segment(smem + (lc % NS) * C::kStage, lc, af, oacc, cst, lsum, wrow0);
     }
     if (!resident) {
       // the next tile's first segments reuse the ring
@@ -347,7 +385,10 @@ void b2b_stream_kernel(B2bParams p) {
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb) {
       float inv = 1.0f;
-      if constexpr (kSoftmax) inv = 1.0f / sum_halves(lsum[rb]);
+      if constexpr (kSoftmax) {
+        const float ls = sum_halves(lsum[rb]);
+        inv = ls > 0.0f ? 1.0f / ls : 0.0f;   // 0 only for a causal row that sees no key
+      }
       const uint32_t row = (uint32_t)(m0 + (wave * MB + rb) * 32 + r32);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
@@ -381,14 +422,14 @@ void b2b_stream_kernel(B2bParams p) {
 
 // ---- dispatch
 namespace {
-template <bool kSoftmax, bool kB0LK>
+template <bool kSoftmax, bool kB0LK, bool kCausal = false>
 const void* pick_stream_kn(int K, int N, bool two_blocks) {
   if (K == 64 && N == 64)
-    return two_blocks ? (const void*)&b2b_stream_kernel<4, 2, 2, kSoftmax, kB0LK>
-                      : (const void*)&b2b_stream_kernel<4, 2, 1, kSoftmax, kB0LK>;
-  if (K == 64 && N == 128) return (const void*)&b2b_stream_kernel<4, 4, 1, kSoftmax, kB0LK>;
-  if (K == 128 && N == 64) return (const void*)&b2b_stream_kernel<8, 2, 1, kSoftmax, kB0LK>;
-  if (K == 128 && N == 128) return (const void*)&b2b_stream_kernel<8, 4, 1, kSoftmax, kB0LK>;
+    return two_blocks ? (const void*)&b2b_stream_kernel<4, 2, 2, kSoftmax, kB0LK, kCausal>
+                      : (const void*)&b2b_stream_kernel<4, 2, 1, kSoftmax, kB0LK, kCausal>;
+  if (K == 64 && N == 128) return (const void*)&b2b_stream_kernel<4, 4, 1, kSoftmax, kB0LK, kCausal>;
+  if (K == 128 && N == 64) return (const void*)&b2b_stream_kernel<8, 2, 1, kSoftmax, kB0LK, kCausal>;
+  if (K == 128 && N == 128) return (const void*)&b2b_stream_kernel<8, 4, 1, kSoftmax, kB0LK, kCausal>;
   return nullptr;
 }
 }  // namespace
@@ -398,8 +439,12 @@ const void* b2b_stream_pick(const B2bParams& p, int cus, int* rows_per_tile) {
   // 256-row tiles only when they still give every CU two workgroups
   const bool two = p.K == 64 && p.N == 64 && (long)p.batch * ((p.M + 255) / 256) >= 2L * cus;
   const bool sm = p.row_op == 1;
-  const void* k = sm ? (p.b0_lk ? pick_stream_kn<true, true>(p.K, p.N, two) : pick_stream_kn<true, false>(p.K, p.N, two))
-                     : (p.b0_lk ? pick_stream_kn<false, true>(p.K, p.N, two) : pick_stream_kn<false, false>(p.K, p.N, two));
+  const void* k;
+  if (p.causal)   // keys stored [L, K] (attention); other layouts take the general kernel
+    k = p.b0_lk ? pick_stream_kn<true, true, true>(p.K, p.N, two) : nullptr;
+  else
+    k = sm ? (p.b0_lk ? pick_stream_kn<true, true>(p.K, p.N, two) : pick_stream_kn<true, false>(p.K, p.N, two))
+           : (p.b0_lk ? pick_stream_kn<false, true>(p.K, p.N, two) : pick_stream_kn<false, false>(p.K, p.N, two));
   if (k && rows_per_tile) *rows_per_tile = two ? 256 : 128;
   return k;
 }

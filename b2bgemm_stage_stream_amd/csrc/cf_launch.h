@@ -70,6 +70,8 @@ struct B2bParams {
   int bias_f32;
   int b0_lk;
   int o_vec;     // O base, ldo and batch stride allow 4-element vector stores
+  int causal;    // softmax only: key l visible to row m iff l <= m + coff
+  int coff;      // L - M
 };
 
 hipError_t launch_b2b(const B2bParams& p, hipStream_t stream);

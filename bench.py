@@ -11,7 +11,7 @@ cache). Prints one JSON line:
              with the mean kernel time from HIP events on the launch stream
   cpu_baseline  the fp64 oracle timed on the host cores on a bounded row sample
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--store-x]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--store-x] [--causal]
 """
 from __future__ import annotations
 
@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--store-x", action="store_true",
                     help="GEMM + epilogue workloads: also store x, the input of the row operation, as a second "
                          "bf16 [M, N] output (e.g. the new residual stream of a pre-norm block)")
+    ap.add_argument("--causal", action="store_true",
+                    help="attention workload: causal mask (key l visible to query m iff l <= m + L - M); the "
+                         "algorithmic flops count only the visible (query, key) pairs")
     ap.add_argument("--rotate-mb", type=int, default=512,
                     help="cycle through copies of the inputs totalling at least this many MiB, so that they are "
                          "read from HBM rather than from the 256 MiB last-level cache (0: one set)")
@@ -81,11 +84,17 @@ def copy_probe(mib: int, steps: int):
     print(json.dumps({"copy_probe_bytes_each_way": n * 4, "steps": steps}), flush=True)
 
 
-def flops_of(w) -> float:
+def visible_pairs(M: int, L: int) -> int:
+    """(query, key) pairs a causal mask leaves: row m sees keys 0 .. m + L - M."""
+    return int(sum(min(L, max(0, m + L - M + 1)) for m in range(M)))
+
+
+def flops_of(w, causal: bool = False) -> float:
     d = w.dims
     if w.kind == "gemm_epilogue":
         return 2.0 * d["M"] * d["N"] * d["K"]
-    return 2.0 * d["batch"] * d["M"] * (d["K"] * d["L"] + d["L"] * d["N"])
+    pairs = visible_pairs(d["M"], d["L"]) if causal else d["M"] * d["L"]
+    return 2.0 * d["batch"] * pairs * (d["K"] + d["N"])
 
 
 def bytes_of(w, store_x: bool = False) -> float:
@@ -109,11 +118,11 @@ def is_f32(w) -> bool:
     return any(t.dtype == "f32" for t in w.tensors if t.name == "A")
 
 
-def roofline_of(w, kernel_ms: float, store_x: bool = False):
+def roofline_of(w, kernel_ms: float, store_x: bool = False, causal: bool = False):
     """The roofline that bounds the kernel: HBM when the workload's flop/byte is
     below the ridge point (peak flops / HBM bandwidth), the MFMA peak above it.
     Returns (bound, unit, peak, achieved, intensity, ridge)."""
-    flops, nbytes = flops_of(w), bytes_of(w, store_x)
+    flops, nbytes = flops_of(w, causal), bytes_of(w, store_x)
     peak_flops = PEAK_F32_TFLOPS if is_f32(w) else PEAK_BF16_TFLOPS
     intensity = flops / nbytes
     ridge = peak_flops * 1e12 / (HBM_GBPS * 1e9)
@@ -122,7 +131,7 @@ def roofline_of(w, kernel_ms: float, store_x: bool = False):
     return "mfma", "TFLOP/s", peak_flops, flops / (kernel_ms * 1e-3) / 1e12, intensity, ridge
 
 
-def make_call(w, dev, torch, cf, store_x: bool = False):
+def make_call(w, dev, torch, cf, store_x: bool = False, causal: bool = False):
     """Device tensors + a closure launching one fused kernel on the current stream."""
     p = w.params
     out_dt = torch.float32 if p.get("out_dtype") == "f32" else torch.bfloat16
@@ -142,7 +151,7 @@ def make_call(w, dev, torch, cf, store_x: bool = False):
         call.keep = X        # the second output lives as long as the closure
         return call, C, ws, nbytes
     d = w.dims
-    e = cf.make_epilogue(alpha=p["alpha"], act=p["act"], row_op=p["row_op"])
+    e = cf.make_epilogue(alpha=p["alpha"], act=p["act"], row_op=p["row_op"], mask="causal" if causal else "none")
     O = torch.empty(d["batch"], d["M"], d["N"], dtype=out_dt, device="cuda")
     lk = p["b0_layout"] == "lk"
 
@@ -151,7 +160,7 @@ def make_call(w, dev, torch, cf, store_x: bool = False):
     return call, O, None, 0
 
 
-def cpu_baseline(w, raw, target_s: float):
+def cpu_baseline(w, raw, target_s: float, causal: bool = False):
     """The fp64 oracle on a bounded sample of rows (rows are independent)."""
     import oracle
     ncores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
@@ -180,9 +189,10 @@ def cpu_baseline(w, raw, target_s: float):
 
         def run(rows):   # rows = number of (batch) problems
             oracle.b2bgemm(A[:rows], B0[:rows] if B0.shape[0] > 1 else B0, B1[:rows] if B1.shape[0] > 1 else B1,
-                           alpha=p["alpha"], act=p["act"], row_op=p["row_op"], b0_layout=p["b0_layout"])
+                           alpha=p["alpha"], act=p["act"], row_op=p["row_op"], b0_layout=p["b0_layout"],
+                           causal=causal)
         if d["batch"] > 1:
-            unit_flops = 2.0 * d["M"] * (d["K"] * d["L"] + d["L"] * d["N"])
+            unit_flops = flops_of(w, causal) / d["batch"]
             total_units = d["batch"]
             what = "independent (batch, head) problems"
         else:
@@ -231,6 +241,8 @@ def main():
     w = gen.workload(args.workload)
     if args.store_x and w.kind != "gemm_epilogue":
         raise SystemExit("--store-x applies to the GEMM + epilogue workloads")
+    if args.causal and (w.kind != "b2bgemm" or w.params["row_op"] != "softmax"):
+        raise SystemExit("--causal applies to the attention (softmax B2BGEMM) workload")
     if args.plain:
         import dataclasses
         w = dataclasses.replace(w, params={**w.params, "row_op": "none", "act": "none"},
@@ -248,7 +260,7 @@ def main():
     devs = [dev] + [{k: v.clone() for k, v in dev.items()} for _ in range(nset - 1)]
     calls = []
     for d_ in devs:
-        call, out, ws, ws_bytes = make_call(w, d_, torch, cf, args.store_x)
+        call, out, ws, ws_bytes = make_call(w, d_, torch, cf, args.store_x, args.causal)
         calls.append(call)
 
     for i in range(max(args.warmup, nset)):
@@ -269,12 +281,12 @@ def main():
     kernel_ms = start_ev.elapsed_time(end_ev) / args.steps
     ms_per_step = wall * 1e3 / args.steps
 
-    flops = flops_of(w)
+    flops = flops_of(w, args.causal)
     value = flops / (ms_per_step * 1e-3) / 1e12
     in_f32 = is_f32(w)
-    bound, unit, peak, achieved, intensity, ridge = roofline_of(w, kernel_ms, args.store_x)
+    bound, unit, peak, achieved, intensity, ridge = roofline_of(w, kernel_ms, args.store_x, args.causal)
     traffic = None
-    if os.path.exists(args.traffic) and not args.plain and not args.store_x:
+    if os.path.exists(args.traffic) and not args.plain and not args.store_x and not args.causal:
         try:
             rec = json.load(open(args.traffic))
             if rec.get("kernel_source_hash") == kernel_source_hash():
@@ -295,7 +307,7 @@ def main():
         "dtype": "f32" if in_f32 else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name + ("/identity-epilogue" if args.plain else "")
-                   + ("+x_out" if args.store_x else ""), **w.dims,
+                   + ("+x_out" if args.store_x else "") + ("/causal" if args.causal else ""), **w.dims,
                    "out_dtype": w.params.get("out_dtype"), "input_sets": nset, "input_bytes_per_set": in_bytes},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,
@@ -307,7 +319,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         del dev, devs, calls, out
-        line["cpu_baseline"] = cpu_baseline(w, raw, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(w, raw, args.cpu_seconds, args.causal)
     print(json.dumps(line), flush=True)
 
 

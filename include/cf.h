@@ -58,6 +58,16 @@ typedef enum {
   CF_ROW_RMSNORM = 3    /* y = x / sqrt(mean_n x^2 + eps) * gamma[n]; gamma optional     */
 } cf_row_op;
 
+/* Visibility mask on the scores S of cf_b2bgemm's softmax (ignored nowhere:
+ * any other use is CF_ERR_UNSUPPORTED). */
+typedef enum {
+  CF_MASK_NONE = 0,
+  CF_MASK_CAUSAL = 1    /* key l is visible to query row m iff l <= m + (L - M): the M
+                           queries are the last M of the L positions (for M = L, the
+                           usual lower-triangular self-attention mask). A row that sees
+                           no key (only when M > L) outputs 0.                          */
+} cf_mask;
+
 /* Epilogue descriptor. The stages run in this fixed order on the fp32
  * accumulator of P = A.B (ComFuse review, "What carries the argument":
  * elementwise nodes stream over the accumulator fragments, the reduction is a
@@ -98,6 +108,7 @@ typedef struct cf_epilogue {
   void* x_out;              /* optional second output: x after stage 4 (see above) */
   int64_t ld_x_out;         /* leading dimension of x_out in elements, >= N       */
   cf_dtype x_out_dtype;     /* CF_BF16 or CF_F32                                  */
+  cf_mask mask;             /* cf_b2bgemm with row_op CF_ROW_SOFTMAX only         */
 } cf_epilogue;
 
 /* Fills *epi with the identity epilogue (alpha 1, no bias/residual/act/row op). */
@@ -158,7 +169,11 @@ cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K,
  *   O   [M, N], leading dimension ldo, batch stride so.
  *   mid epilogue on S: alpha, bias (vector of L), act, and row_op in
  *       {CF_ROW_NONE, CF_ROW_SOFTMAX}; residual/gamma/beta/x_out must be NULL
- *       (CF_ERR_UNSUPPORTED otherwise: S is never stored).
+ *       (CF_ERR_UNSUPPORTED otherwise: S is never stored). With row_op
+ *       CF_ROW_SOFTMAX, mask = CF_MASK_CAUSAL hides the scores of keys
+ *       l > m + L - M before the softmax (causal attention; the review's
+ *       Self-Attention workload, Referee Report major comment 3); key segments
+ *       that no row of a tile can see are not computed.
  * The second GEMM takes P in bf16 (the MFMA operand type); for the softmax the
  * operand is round(2^(t - c)) with t = log2(e) * S and an integer per-row c,
  * and the row sum used for normalisation is taken before rounding.

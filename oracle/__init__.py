@@ -202,9 +202,16 @@ def softmax_bf16_operand(S: np.ndarray):
     return round_bf16(pt), pt.sum(axis=-1, keepdims=True)
 
 
+def causal_visible(M: int, L: int) -> np.ndarray:
+    """Boolean [M, L]: key l is visible to query row m iff l <= m + (L - M), the
+    M queries being the last M of the L positions (the lower-triangular mask
+    when M == L)."""
+    return np.arange(L)[None, :] <= np.arange(M)[:, None] + (L - M)
+
+
 def b2bgemm(A: np.ndarray, B0: np.ndarray, B1: np.ndarray, *, alpha: float = 1.0,
             bias: Optional[np.ndarray] = None, act: str = "none", row_op: str = "none",
-            b0_layout: str = "kl", round_operand: bool = True) -> np.ndarray:
+            b0_layout: str = "kl", round_operand: bool = True, causal: bool = False) -> np.ndarray:
     """Back-to-back GEMM O = F(alpha * A . B0 + bias) . B1 (ComFuse review,
     Referee Report major comment 2, paper Sec. IV-A and Eqs. (2)-(5); the
     intermediate S is an [M, L] matrix, L being the page's N1).
@@ -215,6 +222,11 @@ def b2bgemm(A: np.ndarray, B0: np.ndarray, B1: np.ndarray, *, alpha: float = 1.0
     GEMM is rounded to bf16 as described in the module docstring; without it
     the whole computation stays in float64. Leading dims broadcast as batches;
     batches are evaluated one at a time to bound memory.
+
+    ``causal`` (softmax only) hides the scores of invisible keys (see
+    ``causal_visible``) before the softmax, as causal self-attention does (the
+    review's Self-Attention workload, Referee Report major comment 3); a row
+    that sees no key (only when M > L) gives 0.
     """
     A = np.asarray(A, np.float64)
     B0 = np.asarray(B0, np.float64)
@@ -227,14 +239,25 @@ def b2bgemm(A: np.ndarray, B0: np.ndarray, B1: np.ndarray, *, alpha: float = 1.0
         return np.stack([
             b2bgemm(A[i], B0[i] if B0.ndim == 3 else B0, B1[i] if B1.ndim == 3 else B1,
                     alpha=alpha, bias=bias, act=act, row_op=row_op, b0_layout="kl",
-                    round_operand=round_operand)
+                    round_operand=round_operand, causal=causal)
             for i in range(A.shape[0])])
     S = elementwise_stage(matmul(A, B0), alpha, bias, None, act)
+    if causal and row_op != "softmax":
+        raise ValueError("the causal mask applies to the softmax")
     if row_op == "softmax":
-        if round_operand:
-            num, den = softmax_bf16_operand(S)
-            return matmul(num, B1) / den
-        return matmul(row_softmax(S), B1)
+        if causal:
+            vis = causal_visible(S.shape[0], S.shape[1])
+            S = np.where(vis, S, -np.inf)
+            empty = ~vis.any(axis=1)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            if round_operand:
+                num, den = softmax_bf16_operand(S)
+                O = matmul(num, B1) / den
+            else:
+                O = matmul(row_softmax(S), B1)
+        if causal:
+            O[empty] = 0.0
+        return O
     if row_op != "none":
         raise ValueError(f"row_op {row_op!r} is not supported between two GEMMs")
     Pm = round_bf16(S) if round_operand else S

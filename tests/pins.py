@@ -339,9 +339,46 @@ def pin_b2b_softmax(o):
                                            row_op="softmax", b0_layout="lk"))
 
 
+def pin_b2b_causal(o):
+    """Causal softmax B2BGEMM: each row against the brute force of the un-masked
+    computation on the visible prefix of keys only (slicing, not masking), for
+    M < L (queries at the end), M == L and M > L (rows that see nothing give 0)."""
+    rng = np.random.default_rng(12)
+    k, n, alpha = 5, 3, 0.25
+    for m, l in ((3, 6), (5, 5), (6, 4)):
+        A = _bf16_values(rng, (m, k), 2.0)
+        B0 = _bf16_values(rng, (l, k), 2.0)
+        B1 = _bf16_values(rng, (l, n))
+        O = o.b2bgemm(A, B0, B1, alpha=alpha, row_op="softmax", b0_layout="lk", causal=True)
+        Ou = o.b2bgemm(A, B0, B1, alpha=alpha, row_op="softmax", b0_layout="lk", causal=True,
+                       round_operand=False)
+        S = X.mm(X.mat(A), [list(r) for r in zip(*X.mat(B0))])
+        for i in range(m):
+            vis = i + (l - m) + 1              # keys 0 .. i + L - M
+            if vis <= 0:
+                assert np.all(O[i] == 0.0) and np.all(Ou[i] == 0.0), (m, l, i)
+                continue
+            num, den = _softmax_operand_bruteforce([Fraction(alpha) * s for s in S[i][:vis]])
+            p = X.softmax_row([Fraction(alpha) * s for s in S[i][:vis]])
+            for j in range(n):
+                acc = sum((num[q] * X.F(B1[q, j]) for q in range(vis)), Fraction(0))
+                _close_dec(O[i, j], X.CTX.divide(X.D(acc), den), rtol=1e-12, atol=1e-14)
+                want = sum((X.CTX.multiply(p[q], X.D(X.F(B1[q, j]))) for q in range(vis)), Decimal(0))
+                _close_dec(Ou[i, j], want, rtol=1e-12, atol=1e-14)
+        # the first query of a square problem sees only key 0: O[0] = B1[0] exactly (unrounded operand)
+        if m == l:
+            assert np.array_equal(Ou[0], B1[0])
+    # a single query at the end of the sequence sees every key: the unmasked result
+    A = _bf16_values(rng, (1, k))
+    B0 = _bf16_values(rng, (7, k))
+    B1 = _bf16_values(rng, (7, n))
+    assert np.array_equal(o.b2bgemm(A, B0, B1, alpha=alpha, row_op="softmax", b0_layout="lk", causal=True),
+                          o.b2bgemm(A, B0, B1, alpha=alpha, row_op="softmax", b0_layout="lk"))
+
+
 ALL_PINS = [pin_round_bf16, pin_widen_bf16, pin_matmul_exact, pin_stage1_exact, pin_softmax,
             pin_layernorm, pin_rmsnorm, pin_gemm_epilogue_composition, pin_two_outputs, pin_b2b_relu,
-            pin_b2b_softmax]
+            pin_b2b_softmax, pin_b2b_causal]
 
 
 def run_all(o):

@@ -32,15 +32,15 @@ def run(A, B0, B1, out_dtype, *, b0_is_lk, **epi):
     return O
 
 
-def check(dev, ref, *, lk, what, alpha=1.0, act="none", row_op="none", bias=None, bias_ref=None):
-    kw = dict(alpha=alpha, act=act, row_op=row_op, bias=bias)
+def check(dev, ref, *, lk, what, alpha=1.0, act="none", row_op="none", bias=None, bias_ref=None, causal=False):
+    kw = dict(alpha=alpha, act=act, row_op=row_op, bias=bias, mask="causal" if causal else "none")
     R = oracle.b2bgemm(ref["A"], ref["B0"], ref["B1"], alpha=alpha, act=act, row_op=row_op, bias=bias_ref,
-                       b0_layout="lk" if lk else "kl")
+                       b0_layout="lk" if lk else "kl", causal=causal)
     o32 = run(dev["A"], dev["B0"], dev["B1"], torch.float32, b0_is_lk=lk, **kw)
     g = P.gpu_to_f64(o32)
     r, m = P.assert_close(g, R, P.REL_F_BF16, P.MAX_ABS_BF16, what + " f32-out")
     Ru = oracle.b2bgemm(ref["A"], ref["B0"], ref["B1"], alpha=alpha, act=act, row_op=row_op, bias=bias_ref,
-                        b0_layout="lk" if lk else "kl", round_operand=False)
+                        b0_layout="lk" if lk else "kl", round_operand=False, causal=causal)
     ru, _ = P.metrics(g, Ru)
     assert ru <= REL_F_UNROUNDED, f"{what}: relF vs unrounded oracle {ru:.3e}"
     o16 = run(dev["A"], dev["B0"], dev["B1"], torch.bfloat16, b0_is_lk=lk, **kw)
@@ -223,3 +223,56 @@ def test_c5_full_size_sampled_heads():
     r, m = P.assert_close(got, R, P.REL_F_BF16, P.MAX_ABS_BF16, "C5 full size, sampled heads")
     assert torch.isfinite(O).all()
     print(f"C5 full: relF {r:.2e} maxabs {m:.2e}", flush=True)
+
+
+# ---------------------------------------------------------------------------- causal softmax
+
+@pytest.mark.parametrize("M,L", [(256, 256), (200, 640), (384, 320), (1, 192)])
+def test_causal_streamed(M, L):
+    # keys [L, K], K = N = 64, L a multiple of 64: the streamed kernel; M < L puts the
+    # queries at the end, M > L leaves the first M - L rows with no key (output 0)
+    w, dev, ref = P.inputs("c5_b2b_attention", seed=10, batch=3, M=M, L=L)
+    o = check(dev, ref, lk=True, alpha=0.125, row_op="softmax", causal=True, what=f"causal {M}x{L}")
+    if M > L:
+        assert torch.all(o[:, : M - L] == 0)
+
+
+@pytest.mark.parametrize("K,N", [(64, 128), (128, 64), (128, 128)])
+def test_causal_streamed_widths(K, N):
+    w, dev, ref = P.inputs("c5_b2b_attention", seed=11, batch=2, M=192, L=256, K=K, N=N)
+    check(dev, ref, lk=True, alpha=0.125, row_op="softmax", causal=True, what=f"causal K={K} N={N}")
+
+
+def test_causal_two_row_blocks_and_xcd_heads():
+    # 512 heads: 256-row tiles (two row blocks per wave) and heads grouped by XCD
+    w, dev, ref = P.inputs("c5_b2b_attention", seed=12, batch=512, M=256, L=256)
+    check(dev, ref, lk=True, alpha=0.125, row_op="softmax", causal=True, what="causal 512 heads")
+
+
+def test_causal_negative_alpha_large_logits():
+    w, dev, ref = P.inputs("c5_b2b_attention", seed=13, batch=2, M=128, L=320)
+    dev["A"] = (dev["A"].float() * 6).to(torch.bfloat16)
+    ref["A"] = P.gpu_to_f64(dev["A"])
+    check(dev, ref, lk=True, alpha=-0.125, row_op="softmax", causal=True, what="causal alpha<0 x6")
+
+
+@pytest.mark.parametrize("M,L,lk", [(100, 100, True), (70, 150, True), (130, 90, True), (256, 256, False)])
+def test_causal_general_kernel(M, L, lk):
+    # L not a multiple of 64, or keys given [K, L]: the general kernel
+    w, dev, ref = P.inputs("c5_b2b_attention", seed=14, batch=2, M=M, L=L)
+    if not lk:
+        dev["B0"] = dev["B0"].transpose(-1, -2).contiguous()
+        ref["B0"] = np.ascontiguousarray(np.swapaxes(ref["B0"], -1, -2))
+    o = check(dev, ref, lk=lk, alpha=0.125, row_op="softmax", causal=True, what=f"causal general {M}x{L} lk={lk}")
+    if M > L:
+        assert torch.all(o[:, : M - L] == 0)
+
+
+def test_causal_full_size_sampled_heads():
+    w, dev, ref = P.inputs("c5_b2b_attention", seed=0)
+    O = run(dev["A"], dev["B0"], dev["B1"], torch.float32, b0_is_lk=True, alpha=0.125, row_op="softmax",
+            mask="causal")
+    heads = [0, 77, 300, 511]
+    R = oracle.b2bgemm(ref["A"][heads], ref["B0"][heads], ref["B1"][heads], alpha=0.125, row_op="softmax",
+                       b0_layout="lk", causal=True)
+    P.assert_close(P.gpu_to_f64(O[heads]), R, P.REL_F_BF16, P.MAX_ABS_BF16, "causal C5 full size, sampled heads")

@@ -39,6 +39,9 @@ def test_algorithmic_counts():
     assert bench.bytes_of(w3, store_x=True) - bench.bytes_of(w3) == 2 * 16384 * 4096
     w5 = gen.workload("c5_b2b_attention")
     assert bench.flops_of(w5) == 2.0 * 512 * 1024 * (64 * 1024 + 1024 * 64)
+    # causal: row m of a square problem sees m + 1 keys
+    assert bench.flops_of(w5, causal=True) == 2.0 * 512 * (1024 * 1025 // 2) * (64 + 64)
+    assert bench.visible_pairs(3, 5) == 3 + 4 + 5 and bench.visible_pairs(5, 3) == 0 + 0 + 1 + 2 + 3
 
 
 def test_more_than_one_gpu_exits_with_message():

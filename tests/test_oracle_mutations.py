@@ -54,6 +54,13 @@ MUTATIONS = {
         "    X = elementwise_stage(matmul(A, B), alpha, bias, residual, act)\n    return row_stage(X, row_op, gamma, beta, eps), X\n",
         "    X = elementwise_stage(matmul(A, B), alpha, bias, residual, act)\n"
         "    return row_stage(X, row_op, gamma, beta, eps), elementwise_stage(matmul(A, B), alpha, bias, None, act)\n")],
+    "causal_mask_off_by_one": [(
+        "return np.arange(L)[None, :] <= np.arange(M)[:, None] + (L - M)",
+        "return np.arange(L)[None, :] < np.arange(M)[:, None] + (L - M)")],
+    "causal_mask_top_left_aligned": [(
+        "return np.arange(L)[None, :] <= np.arange(M)[:, None] + (L - M)",
+        "return np.arange(L)[None, :] <= np.arange(M)[:, None]")],
+    "causal_mask_ignored": [("            S = np.where(vis, S, -np.inf)\n", "")],
     "b2b_relu_dropped": [(
         "S = elementwise_stage(matmul(A, B0), alpha, bias, None, act)",
         "S = elementwise_stage(matmul(A, B0), alpha, bias, None, 'none')")],

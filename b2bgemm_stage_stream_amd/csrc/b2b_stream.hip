@@ -157,92 +157,129 @@ void b2b_stream_kernel(B2bParams p) {
   auto segment = [&](const uint8_t* st, int lc, const u32x4_t (&af)[MB][KS], f32x16_t (&oacc)[MB][NB],
                      float (&cst)[MB], float (&lsum)[MB], int wrow0) {
     f32x16_t sacc[MB][2];
+    // GEMM1 (S of the segment) and, for causal rows, the hiding of the keys a
+    // row may not see (their extreme-side infinity drops out of the row
+    // extreme and gives exp2(-inf) = 0)
+    auto gemm1 = [&]() {
 #pragma unroll
-    for (int rb = 0; rb < MB; ++rb)
+      for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
-      for (int lb = 0; lb < 2; ++lb) sacc[rb][lb] = f32x16_t{0};
+        for (int lb = 0; lb < 2; ++lb) sacc[rb][lb] = f32x16_t{0};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int lb = 0; lb < 2; ++lb) {
-        u32x4_t bf;
-        if constexpr (kB0LK) {
-          bf = *(const u32x4_t*)(st + b0_rd[ks] + lb * 32 * C::K * 2);
-        } else {
-          const u32x2_t lo = lds_read_tr16(st + b0_rd[lb] + ks * 16 * 128);
-          const u32x2_t hi = lds_read_tr16(st + b0_rd[lb] + ks * 16 * 128 + 4 * 128);
-          bf = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-        }
-#pragma unroll
-        for (int rb = 0; rb < MB; ++rb)
-          sacc[rb][lb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bf),
-                                                                  __builtin_bit_cast(bf16x8_t, af[rb][ks]), sacc[rb][lb], 0, 0, 0);
-      }
-    // F: register r of block lb holds l = lc*64 + lb*32 + 8(r>>2) + 4h + (r&3)
-    if constexpr (kCausal) {
-      // the segment reaches past the diagonal for some row of this wave: hide
-      // the invisible keys (their extreme-side infinity drops out of the row
-      // extreme and gives exp2(-inf) = 0)
-      if (lc * kTLC + kTLC - 1 > wrow0 + p.coff) {
-        const float hide = scale >= 0.0f ? -INFINITY : INFINITY;
-#pragma unroll
-        for (int rb = 0; rb < MB; ++rb) {
-          const int lim = wrow0 + rb * 32 + r32 + p.coff - (lc * kTLC + 4 * h);   // visible iff l - base <= lim
-#pragma unroll
-          for (int lb = 0; lb < 2; ++lb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (lb * 32 + 8 * (r >> 2) + (r & 3) > lim) sacc[rb][lb][r] = hide;
-        }
-      }
-    }
-    u32x4_t pf[MB][4];
-#pragma unroll
-    for (int rb = 0; rb < MB; ++rb) {
-      if constexpr (kSoftmax) {
-        // row extreme of S (of alpha*S for the stabiliser): max for alpha >= 0, min otherwise
-        float mx;
-        if (scale >= 0.0f) {
-          mx = -INFINITY;
-#pragma unroll
-          for (int lb = 0; lb < 2; ++lb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[rb][lb][r]);
-          mx = max_halves(mx);
-        } else {
-          mx = INFINITY;
-#pragma unroll
-          for (int lb = 0; lb < 2; ++lb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fminf(mx, sacc[rb][lb][r]);
-          mx = min_halves(mx);
-        }
-        const float cn = fmaxf(cst[rb], ceilf(mx * scale));
-        if (cn > cst[rb] && cst[rb] != -INFINITY) {
-          const int sh = (int)(cst[rb] - cn);      // exact power-of-two rescale
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[rb][nb][r] = __builtin_amdgcn_ldexpf(oacc[rb][nb][r], sh);
-          lsum[rb] = __builtin_amdgcn_ldexpf(lsum[rb], sh);
-        }
-        cst[rb] = cn;
-        // -inf only while a causal row has seen no key; its terms are all 0
-        const float cs = (kCausal && cn == -INFINITY) ? 0.0f : cn;
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int lb = 0; lb < 2; ++lb) {
-          float e[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            e[r] = fast_exp2(__builtin_fmaf(sacc[rb][lb][r], scale, -cs));
-            lsum[rb] += e[r];
+          u32x4_t bf;
+          if constexpr (kB0LK) {
+            bf = *(const u32x4_t*)(st + b0_rd[ks] + lb * 32 * C::K * 2);
+          } else {
+            const u32x2_t lo = lds_read_tr16(st + b0_rd[lb] + ks * 16 * 128);
+            const u32x2_t hi = lds_read_tr16(st + b0_rd[lb] + ks * 16 * 128 + 4 * 128);
+            bf = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
           }
 #pragma unroll
-          for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) pf[rb][2 * lb + c][q] = pack_bf16x2(e[8 * c + 2 * q], e[8 * c + 2 * q + 1]);
+          for (int rb = 0; rb < MB; ++rb)
+            sacc[rb][lb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bf),
+                                                                    __builtin_bit_cast(bf16x8_t, af[rb][ks]), sacc[rb][lb], 0, 0, 0);
         }
+      // register r of block lb holds l = lc*64 + lb*32 + 8(r>>2) + 4h + (r&3)
+      if constexpr (kCausal) {
+        if (lc * kTLC + kTLC - 1 > wrow0 + p.coff) {   // the segment crosses the diagonal for this wave
+          const float hide = scale >= 0.0f ? -INFINITY : INFINITY;
+#pragma unroll
+          for (int rb = 0; rb < MB; ++rb) {
+            const int lim = wrow0 + rb * 32 + r32 + p.coff - (lc * kTLC + 4 * h);   // visible iff l - base <= lim
+#pragma unroll
+            for (int lb = 0; lb < 2; ++lb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r)
+                if (lb * 32 + 8 * (r >> 2) + (r & 3) > lim) sacc[rb][lb][r] = hide;
+          }
+        }
+      }
+    };
+    u32x4_t pf[MB][4];
+    // softmax, full form: row extreme of S (of alpha*S for the stabiliser: max
+    // for alpha >= 0, min otherwise), raise the integer stabiliser to cover it
+    // with an exact power-of-two rescale of what was accumulated, then the
+    // terms 2^(alpha*log2e*s - c), their row sum and the bf16 operand
+    auto softmax_full = [&](int rb) {
+      float mx;
+      if (scale >= 0.0f) {
+        mx = -INFINITY;
+#pragma unroll
+        for (int lb = 0; lb < 2; ++lb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[rb][lb][r]);
+        mx = max_halves(mx);
       } else {
+        mx = INFINITY;
+#pragma unroll
+        for (int lb = 0; lb < 2; ++lb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fminf(mx, sacc[rb][lb][r]);
+        mx = min_halves(mx);
+      }
+      const float cn = fmaxf(cst[rb], ceilf(mx * scale));
+      if (cn > cst[rb] && cst[rb] != -INFINITY) {
+        const int sh = (int)(cst[rb] - cn);      // exact power-of-two rescale
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[rb][nb][r] = __builtin_amdgcn_ldexpf(oacc[rb][nb][r], sh);
+        lsum[rb] = __builtin_amdgcn_ldexpf(lsum[rb], sh);
+      }
+      cst[rb] = cn;
+    };
+    // the terms with the current stabiliser; -inf only while a causal row has
+    // seen no key, and then every term is 0
+    auto softmax_terms = [&](int rb) {
+      const float cs = (kCausal && cst[rb] == -INFINITY) ? 0.0f : cst[rb];
+#pragma unroll
+      for (int lb = 0; lb < 2; ++lb) {
+        float e[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          e[r] = fast_exp2(__builtin_fmaf(sacc[rb][lb][r], scale, -cs));
+          lsum[rb] += e[r];
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) pf[rb][2 * lb + c][q] = pack_bf16x2(e[8 * c + 2 * q], e[8 * c + 2 * q + 1]);
+      }
+    };
+    if constexpr (kSoftmax) {
+      // Any integer stabiliser gives the same quotient (rounding commutes with
+      // scaling by a power of two), so the row extreme is taken only while a
+      // row has none yet, and when a segment's own terms add up past 2^32; that
+      // segment is then redone from a recomputed S (cheaper than keeping S
+      // live). Otherwise the current stabiliser is kept.
+      bool fresh = false;
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb) fresh |= cst[rb] == -INFINITY;
+      bool full = __builtin_amdgcn_ballot_w64(fresh) != 0;
+#pragma nounroll
+      for (;;) {
+        gemm1();
+        float lprev[MB];
+        bool big = false;
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb) {
+          if (full) softmax_full(rb);
+          lprev[rb] = lsum[rb];
+          softmax_terms(rb);
+          big |= !(lsum[rb] - lprev[rb] <= 0x1p32f);
+        }
+        if (full || __builtin_amdgcn_ballot_w64(big) == 0) break;
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb) lsum[rb] = lprev[rb];
+        full = true;
+      }
+    } else {
+      gemm1();
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb) {
 #pragma unroll
         for (int lb = 0; lb < 2; ++lb) {
           float x[16];

@@ -48,6 +48,7 @@ class cf_epilogue(ctypes.Structure):
         ("ld_x_out", ctypes.c_int64),
         ("x_out_dtype", ctypes.c_int),
         ("mask", ctypes.c_int),
+        ("row_stats", ctypes.c_void_p),
     ]
 
 
@@ -128,10 +129,12 @@ def _ptr(t) -> Optional[int]:
 
 def make_epilogue(*, alpha: float = 1.0, bias=None, residual=None, act: str = "none",
                   row_op: str = "none", gamma=None, beta=None, eps: float = 0.0, x_out=None,
-                  mask: str = "none") -> cf_epilogue:
+                  mask: str = "none", row_stats=None) -> cf_epilogue:
     """cf_epilogue descriptor from tensors (bias/gamma/beta share one dtype).
     ``x_out``: optional [M, N] tensor that receives x before the row operation.
-    ``mask``: "causal" for the softmax of cf_b2bgemm."""
+    ``mask``: "causal" for the softmax of cf_b2bgemm.
+    ``row_stats``: optional contiguous fp32 tensor for the row operation's per-row
+    statistics (log-sum-exp; LayerNorm mean and 1/sigma; RMSNorm 1/rms)."""
     e = cf_epilogue()
     _lib.cf_epilogue_init(ctypes.byref(e))
     e.alpha = float(alpha)
@@ -139,6 +142,11 @@ def make_epilogue(*, alpha: float = 1.0, bias=None, residual=None, act: str = "n
     e.row_op = ROW_OP[row_op]
     e.eps = float(eps)
     e.mask = MASK[mask]
+    if row_stats is not None:
+        import torch
+        if row_stats.dtype != torch.float32 or not row_stats.is_contiguous():
+            raise TypeError("row_stats must be a contiguous float32 tensor")
+        e.row_stats = row_stats.data_ptr()
     vecs = [v for v in (bias, gamma, beta) if v is not None]
     if vecs:
         codes = {_dtype_code(v) for v in vecs}
@@ -203,6 +211,9 @@ def cf_gemm_epilogue(A, B, C, *, b_is_nk: bool = False, epi: Optional[cf_epilogu
     x_out = epi_kwargs.get("x_out")
     if x_out is not None and tuple(x_out.shape) != (M, N):
         raise ValueError(f"x_out must be [{M}, {N}]")
+    st = epi_kwargs.get("row_stats")
+    if st is not None and st.numel() < M * (2 if epi_kwargs.get("row_op") == "layernorm" else 1):
+        raise ValueError("row_stats is too small for M rows")
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
                                                            workspace.numel() * workspace.element_size())
     _check(_lib.cf_gemm_epilogue(M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), int(b_is_nk),
@@ -232,6 +243,9 @@ def cf_b2bgemm(A, B0, B1, O, *, b0_is_lk: bool = False, epi: Optional[cf_epilogu
     _, sb0 = batched(B0)
     _, sb1 = batched(B1)
     _, so = batched(O)
+    st = epi_kwargs.get("row_stats")
+    if st is not None and st.numel() < batch * M:
+        raise ValueError("row_stats is too small for batch * M rows")
     _check(_lib.cf_b2bgemm(batch, M, K, L, N, A.data_ptr(), _ld(A), sa, B0.data_ptr(), _ld(B0), sb0,
                            int(b0_is_lk), B1.data_ptr(), _ld(B1), sb1, O.data_ptr(), _ld(O), so,
                            _dtype_code(A), _dtype_code(O), ctypes.byref(epi), _stream(stream)),

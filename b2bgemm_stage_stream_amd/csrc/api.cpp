@@ -100,6 +100,7 @@ cf_status check_epilogue(const cf_epilogue* epi, int64_t N, bool allow_row_ops_n
     if (epi->ld_residual < N || epi->ld_residual < 1) return CF_ERR_INVALID_ARGUMENT;
     if (!aligned(epi->residual, dsize(epi->residual_dtype))) return CF_ERR_INVALID_ARGUMENT;
   }
+  if (epi->row_stats && (epi->row_op == CF_ROW_NONE || !aligned(epi->row_stats, 4))) return CF_ERR_INVALID_ARGUMENT;
   if (epi->mask != CF_MASK_NONE && epi->mask != CF_MASK_CAUSAL) return CF_ERR_INVALID_ARGUMENT;
   if (epi->mask != CF_MASK_NONE && (allow_residual || epi->row_op != CF_ROW_SOFTMAX)) return CF_ERR_UNSUPPORTED;
   if (epi->x_out) {
@@ -233,6 +234,7 @@ cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K, const void* A, int64
   p.ldx = (uint32_t)(X ? epi->ld_x_out : 0);
   p.x_bytes = (uint32_t)(X ? (uint64_t)M * epi->ld_x_out * xs : 0);
   p.x_f32 = X && epi->x_out_dtype == CF_F32;
+  p.row_stats = epi ? epi->row_stats : nullptr;
   p.M = (int)M;
   p.N = (int)N;
   p.K = (int)K;
@@ -301,6 +303,8 @@ cf_status cf_b2bgemm(int64_t batch, int64_t M, int64_t K, int64_t L, int64_t N, 
   if (!aligned(A, 16) || !aligned(B0, 16) || !aligned(B1, 16) || !aligned(O, os)) return CF_ERR_UNSUPPORTED;
   if (lda % 8 || ldb0 % 8 || ldb1 % 8 || sa % 8 || sb0 % 8 || sb1 % 8) return CF_ERR_UNSUPPORTED;
   if (mid && mid->bias && mid->vec_dtype != CF_BF16 && mid->vec_dtype != CF_F32) return CF_ERR_INVALID_ARGUMENT;
+  // the softmax kernels take the scores alpha * S as they are
+  if (mid && mid->row_op == CF_ROW_SOFTMAX && (mid->bias || mid->act != CF_ACT_NONE)) return CF_ERR_UNSUPPORTED;
   if (batch > INT32_MAX || M > INT32_MAX || L > INT32_MAX || K > INT32_MAX || N > INT32_MAX) return CF_ERR_UNSUPPORTED;
 
   cf::B2bParams p;
@@ -331,6 +335,7 @@ cf_status cf_b2bgemm(int64_t batch, int64_t M, int64_t K, int64_t L, int64_t N, 
   p.b0_lk = b0_is_lk;
   p.o_vec = aligned(O, 16) && ldo % 4 == 0 && so % 4 == 0;
   p.causal = mid && mid->mask == CF_MASK_CAUSAL;
+  p.row_stats = mid ? mid->row_stats : nullptr;
   p.coff = (int)(L - M);
   if (!cf::b2b_supported(p)) return CF_ERR_UNSUPPORTED;
 

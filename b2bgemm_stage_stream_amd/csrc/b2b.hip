@@ -341,11 +341,14 @@ __global__ __launch_bounds__(kThreads) void b2b_kernel(B2bParams p) {
 
     // ---- normalise and store: oacc[nb][4q + e] is O[m][nb*32 + 8q + 4h + e]
     float inv = 1.0f;
+    const uint32_t row = (uint32_t)(m0 + wave * 32 + r32);
     if constexpr (kSoftmax) {
       const float ls = sum_halves(lsum);
       inv = ls > 0.0f ? 1.0f / ls : 0.0f;   // 0 only for a causal row that sees no key
+      // log-sum-exp of the row: sum exp(alpha s) = 2^c * ls
+      if (p.row_stats != nullptr && h == 0 && row < (uint32_t)p.M)
+        p.row_stats[(size_t)b * p.M + row] = ls > 0.0f ? (cst + log2f(ls)) * kLn2 : -INFINITY;
     }
-    const uint32_t row = (uint32_t)(m0 + wave * 32 + r32);
     const __amdgpu_buffer_rsrc_t rsO = make_rsrc((uint8_t*)p.O + (size_t)b * p.so * (p.out_f32 ? 4 : 2),
                                                  (uint32_t)((size_t)p.M * p.ldo * (p.out_f32 ? 4 : 2)));
 #pragma unroll

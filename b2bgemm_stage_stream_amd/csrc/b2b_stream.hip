@@ -422,11 +422,14 @@ void b2b_stream_kernel(B2bParams p) {
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb) {
       float inv = 1.0f;
+      const uint32_t row = (uint32_t)(m0 + (wave * MB + rb) * 32 + r32);
       if constexpr (kSoftmax) {
         const float ls = sum_halves(lsum[rb]);
         inv = ls > 0.0f ? 1.0f / ls : 0.0f;   // 0 only for a causal row that sees no key
+        // log-sum-exp of the row: sum exp(alpha s) = 2^c * ls
+        if (p.row_stats != nullptr && h == 0 && row < (uint32_t)p.M)
+          p.row_stats[(size_t)b * p.M + row] = ls > 0.0f ? (cst[rb] + log2f(ls)) * kLn2 : -INFINITY;
       }
-      const uint32_t row = (uint32_t)(m0 + (wave * MB + rb) * 32 + r32);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll

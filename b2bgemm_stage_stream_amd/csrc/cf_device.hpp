@@ -79,6 +79,7 @@ __device__ inline float max_halves(float v) {
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 // ----------------------------------------------------------------------------- LDS streaming
 typedef short i16x4_t __attribute__((ext_vector_type(4)));

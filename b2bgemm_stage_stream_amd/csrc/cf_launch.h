@@ -38,6 +38,7 @@ struct GemmEpilogueParams {
   void* X;           // optional second output: x before the row operation
   uint32_t ldx, x_bytes;
   int x_f32;         // dtype of X: 1 fp32, 0 bf16
+  float* row_stats;  // optional per-row statistics of the row operation
   uint32_t* ws_hdr;  // workspace header (NULL when tiles_n == 1 or no row op)
   uint64_t* ws_slots;
   uint64_t spin_ticks;   // wall-clock ticks a strip wait may take
@@ -72,6 +73,7 @@ struct B2bParams {
   int o_vec;     // O base, ldo and batch stride allow 4-element vector stores
   int causal;    // softmax only: key l visible to row m iff l <= m + coff
   int coff;      // L - M
+  float* row_stats;   // softmax only, optional: log-sum-exp of each row, [batch][M]
 };
 
 hipError_t launch_b2b(const B2bParams& p, hipStream_t stream);

@@ -697,6 +697,13 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
       else if constexpr (ROW == 2) st = make_float2(a, rsqrtf(b / (float)p.N + p.eps));
       else st = make_float2(rsqrtf(a / (float)p.N + p.eps), 0.0f);
       rstat[ml] = st;
+      // the reduction's own per-row result, stored once per strip (column tile 0)
+      if (p.row_stats != nullptr && tn == 0 && row_ok) {
+        const int m = m0 + ml;
+        if constexpr (ROW == 1) p.row_stats[m] = a + logf(b);   // log-sum-exp: max + ln sum exp(x - max)
+        else if constexpr (ROW == 2) { p.row_stats[2 * m] = a; p.row_stats[2 * m + 1] = st.y; }
+        else p.row_stats[m] = st.x;
+      }
     }
     __syncthreads();
   }

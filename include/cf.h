@@ -91,7 +91,18 @@ typedef enum {
  * chained DAGs at its reductions); a pre-norm transformer block uses it to
  * keep the new residual stream x = P + residual beside y = RMSNorm(x). In the
  * stored X only the cast rounds: x is the same fp32 value the row operation
- * consumes. NULL (the default from cf_epilogue_init) stores nothing. */
+ * consumes. NULL (the default from cf_epilogue_init) stores nothing.
+ *
+ * Row statistics (row_stats, optional, fp32, caller-owned device memory): the
+ * per-row result of the reduction stage itself (the review's "Reading between
+ * the lines": other single-axis reductions such as log-sum-exp), as a
+ * backward pass needs it:
+ *   CF_ROW_SOFTMAX   row_stats[m]         = ln sum_n exp(x[m, n])  (log-sum-exp)
+ *   CF_ROW_LAYERNORM row_stats[2m], [2m+1] = mean, 1 / sqrt(var + eps)
+ *   CF_ROW_RMSNORM   row_stats[m]         = 1 / sqrt(mean_n x^2 + eps)
+ * cf_b2bgemm (softmax only): row_stats[b * M + m] = ln sum_l exp(alpha * S[m, l])
+ * over the visible keys; -inf for a causal row that sees none.
+ * Must be 4-byte aligned; CF_ERR_INVALID_ARGUMENT with CF_ROW_NONE. */
 typedef struct cf_epilogue {
   uint32_t struct_size;     /* must be sizeof(cf_epilogue)                        */
   float alpha;
@@ -109,6 +120,7 @@ typedef struct cf_epilogue {
   int64_t ld_x_out;         /* leading dimension of x_out in elements, >= N       */
   cf_dtype x_out_dtype;     /* CF_BF16 or CF_F32                                  */
   cf_mask mask;             /* cf_b2bgemm with row_op CF_ROW_SOFTMAX only         */
+  float* row_stats;         /* optional fp32 per-row statistics of the row op (see below) */
 } cf_epilogue;
 
 /* Fills *epi with the identity epilogue (alpha 1, no bias/residual/act/row op). */
@@ -170,7 +182,8 @@ cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K,
  *   mid epilogue on S: alpha, bias (vector of L), act, and row_op in
  *       {CF_ROW_NONE, CF_ROW_SOFTMAX}; residual/gamma/beta/x_out must be NULL
  *       (CF_ERR_UNSUPPORTED otherwise: S is never stored). With row_op
- *       CF_ROW_SOFTMAX, mask = CF_MASK_CAUSAL hides the scores of keys
+ *       CF_ROW_SOFTMAX, bias and act must be unset (CF_ERR_UNSUPPORTED: the
+ *       softmax takes alpha * S as it is); mask = CF_MASK_CAUSAL hides the scores of keys
  *       l > m + L - M before the softmax (causal attention; the review's
  *       Self-Attention workload, Referee Report major comment 3); key segments
  *       that no row of a tile can see are not computed.

@@ -172,6 +172,33 @@ def row_stage(X: np.ndarray, row_op: str, gamma: Optional[np.ndarray] = None,
     raise ValueError(f"unknown row_op {row_op!r}")
 
 
+def row_statistics(X: np.ndarray, row_op: str, eps: float = 0.0) -> np.ndarray:
+    """The per-row result of the reduction stage itself (the review's "Reading
+    between the lines" names log-sum-exp among the single-axis reductions the
+    strip locality covers): for the softmax, ln sum_n exp(x) (the row max plus
+    the log of the shifted sum); for LayerNorm, [mean, 1/sqrt(var + eps)] per
+    row (last axis of length 2); for RMSNorm, 1/sqrt(mean(x^2) + eps)."""
+    if row_op == "softmax":
+        mx = X.max(axis=-1, keepdims=True)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            lse = mx + np.log(np.exp(X - mx).sum(axis=-1, keepdims=True))
+        return np.where(np.isneginf(mx), -np.inf, lse)[..., 0]
+    if row_op == "layernorm":
+        mu = X.mean(axis=-1, keepdims=True)
+        var = ((X - mu) * (X - mu)).mean(axis=-1, keepdims=True)
+        return np.concatenate([mu, 1.0 / np.sqrt(var + float(eps))], axis=-1)
+    if row_op == "rmsnorm":
+        return 1.0 / np.sqrt((X * X).mean(axis=-1) + float(eps))
+    raise ValueError(f"row_op {row_op!r} has no row statistics")
+
+
+def gemm_epilogue_row_stats(A: np.ndarray, B: np.ndarray, *, alpha: float = 1.0,
+                            bias: Optional[np.ndarray] = None, residual: Optional[np.ndarray] = None,
+                            act: str = "none", row_op: str = "softmax", eps: float = 0.0) -> np.ndarray:
+    """row_statistics of the elementwise stage's result X = act(alpha A.B + bias + R)."""
+    return row_statistics(elementwise_stage(matmul(A, B), alpha, bias, residual, act), row_op, eps)
+
+
 def gemm_epilogue_with_x(A: np.ndarray, B: np.ndarray, *, alpha: float = 1.0,
                          bias: Optional[np.ndarray] = None, residual: Optional[np.ndarray] = None,
                          act: str = "none", row_op: str = "none", gamma: Optional[np.ndarray] = None,
@@ -207,6 +234,24 @@ def causal_visible(M: int, L: int) -> np.ndarray:
     M queries being the last M of the L positions (the lower-triangular mask
     when M == L)."""
     return np.arange(L)[None, :] <= np.arange(M)[:, None] + (L - M)
+
+
+def b2b_logsumexp(A: np.ndarray, B0: np.ndarray, *, alpha: float = 1.0, b0_layout: str = "kl",
+                  causal: bool = False) -> np.ndarray:
+    """ln sum_l exp(alpha * S[m, l]) over the keys row m sees, S = A . B0 (the
+    softmax's own per-row reduction, as attention's backward pass keeps it);
+    -inf for a causal row that sees no key. Leading dims broadcast as batches."""
+    A = np.asarray(A, np.float64)
+    B0 = np.asarray(B0, np.float64)
+    if b0_layout == "lk":          # keys stored [L, K]
+        B0 = np.moveaxis(B0, -1, -2)
+    if A.ndim == 3:
+        return np.stack([b2b_logsumexp(A[i], B0[i] if B0.ndim == 3 else B0, alpha=alpha, causal=causal)
+                         for i in range(A.shape[0])])
+    S = float(alpha) * matmul(A, B0)
+    if causal:
+        S = np.where(causal_visible(S.shape[0], S.shape[1]), S, -np.inf)
+    return row_statistics(S, "softmax")
 
 
 def b2bgemm(A: np.ndarray, B0: np.ndarray, B1: np.ndarray, *, alpha: float = 1.0,

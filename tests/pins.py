@@ -376,9 +376,74 @@ def pin_b2b_causal(o):
                           o.b2bgemm(A, B0, B1, alpha=alpha, row_op="softmax", b0_layout="lk"))
 
 
+def pin_row_statistics(o):
+    """Log-sum-exp, LayerNorm (mean, 1/sigma) and RMSNorm 1/rms of each row against
+    40-digit decimals and closed forms."""
+    rng = np.random.default_rng(13)
+    Xr = _bf16_values(rng, (3, 7), 3.0)
+    eps = 1e-5
+    for row_op in ("softmax", "layernorm", "rmsnorm"):
+        st = o.row_statistics(Xr, row_op, eps)
+        for i in range(3):
+            xs = [X.D(X.F(v)) for v in Xr[i]]
+            n = X.D(len(xs))
+            if row_op == "softmax":
+                want = [X.CTX.ln(sum((X.dexp(v) for v in xs), Decimal(0)))]
+                got = [st[i]]
+            elif row_op == "layernorm":
+                mu = X.CTX.divide(sum(xs, Decimal(0)), n)
+                var = X.CTX.divide(sum(((v - mu) * (v - mu) for v in xs), Decimal(0)), n)
+                want = [mu, X.CTX.divide(Decimal(1), X.dsqrt(var + X.D(eps)))]
+                got = list(st[i])
+            else:
+                ms = X.CTX.divide(sum((v * v for v in xs), Decimal(0)), n)
+                want = [X.CTX.divide(Decimal(1), X.dsqrt(ms + X.D(eps)))]
+                got = [st[i]]
+            for gv, wv in zip(got, want):
+                _close_dec(gv, wv, rtol=1e-13, atol=1e-14)
+    # closed forms: a constant row c of n values has log-sum-exp c + ln n, mean c and
+    # 1/sigma = 1/sqrt(eps); rmsnorm of c gives 1/sqrt(c^2 + eps)
+    c = np.full((1, 8), 1.25)
+    assert abs(o.row_statistics(c, "softmax")[0] - (1.25 + math.log(8))) < 1e-14
+    ln = o.row_statistics(c, "layernorm", eps)[0]
+    assert ln[0] == 1.25 and abs(ln[1] - 1 / math.sqrt(eps)) < 1e-9
+    assert abs(o.row_statistics(c, "rmsnorm", eps)[0] - 1 / math.sqrt(1.25 ** 2 + eps)) < 1e-14
+    # log-sum-exp is shift-covariant: lse(x + t) = lse(x) + t
+    assert abs(o.row_statistics(Xr + 5.0, "softmax") - o.row_statistics(Xr, "softmax") - 5.0).max() < 1e-13
+    # through the GEMM: the statistics of the elementwise stage's result
+    A = _bf16_values(rng, (3, 4))
+    B = _bf16_values(rng, (4, 6))
+    R = _bf16_values(rng, (3, 6))
+    st = o.gemm_epilogue_row_stats(A, B, alpha=0.5, residual=R, row_op="rmsnorm", eps=eps)
+    E = X.mm(X.mat(A), X.mat(B))
+    for i in range(3):
+        xs = [X.D(Fraction(1, 2) * E[i][j] + X.F(R[i, j])) for j in range(6)]
+        ms = X.CTX.divide(sum((v * v for v in xs), Decimal(0)), X.D(6))
+        _close_dec(st[i], X.CTX.divide(Decimal(1), X.dsqrt(ms + X.D(eps))), rtol=1e-13, atol=1e-14)
+
+
+def pin_b2b_logsumexp(o):
+    """Attention log-sum-exp against brute force on the visible prefix of keys; a
+    causal row that sees no key gives -inf."""
+    rng = np.random.default_rng(14)
+    k, alpha = 5, 0.25
+    for m, l, causal in ((3, 6, True), (4, 4, False), (5, 3, True)):
+        A = _bf16_values(rng, (m, k), 2.0)
+        B0 = _bf16_values(rng, (l, k), 2.0)
+        got = o.b2b_logsumexp(A, B0, alpha=alpha, b0_layout="lk", causal=causal)
+        S = X.mm(X.mat(A), [list(r) for r in zip(*X.mat(B0))])
+        for i in range(m):
+            vis = min(l, i + (l - m) + 1) if causal else l
+            if vis <= 0:
+                assert got[i] == -np.inf
+                continue
+            want = X.CTX.ln(sum((X.dexp(X.D(Fraction(alpha) * S[i][j])) for j in range(vis)), Decimal(0)))
+            _close_dec(got[i], want, rtol=1e-13, atol=1e-14)
+
+
 ALL_PINS = [pin_round_bf16, pin_widen_bf16, pin_matmul_exact, pin_stage1_exact, pin_softmax,
             pin_layernorm, pin_rmsnorm, pin_gemm_epilogue_composition, pin_two_outputs, pin_b2b_relu,
-            pin_b2b_softmax, pin_b2b_causal]
+            pin_b2b_softmax, pin_b2b_causal, pin_row_statistics, pin_b2b_logsumexp]
 
 
 def run_all(o):

@@ -276,3 +276,21 @@ def test_causal_full_size_sampled_heads():
     R = oracle.b2bgemm(ref["A"][heads], ref["B0"][heads], ref["B1"][heads], alpha=0.125, row_op="softmax",
                        b0_layout="lk", causal=True)
     P.assert_close(P.gpu_to_f64(O[heads]), R, P.REL_F_BF16, P.MAX_ABS_BF16, "causal C5 full size, sampled heads")
+
+
+# ---------------------------------------------------------------------------- log-sum-exp of the attention rows
+
+@pytest.mark.parametrize("M,L,causal", [(256, 512, False), (200, 640, True), (384, 320, True), (100, 150, False)])
+def test_attention_logsumexp(M, L, causal):
+    w, dev, ref = P.inputs("c5_b2b_attention", seed=18, batch=3, M=M, L=L)
+    lse = torch.full((3, M), float("nan"), dtype=torch.float32, device="cuda")
+    O = run(dev["A"], dev["B0"], dev["B1"], torch.float32, b0_is_lk=True, alpha=0.125, row_op="softmax",
+            mask="causal" if causal else "none", row_stats=lse)
+    R = oracle.b2b_logsumexp(ref["A"], ref["B0"], alpha=0.125, b0_layout="lk", causal=causal)
+    got = P.gpu_to_f64(lse)
+    fin = np.isfinite(R)
+    assert np.array_equal(np.isfinite(got), fin), "rows without keys must give -inf"
+    assert np.all(got[~fin] == -np.inf)
+    P.assert_close(got[fin], R[fin], 1e-5, 1e-4, f"attention log-sum-exp {M}x{L} causal={causal}")
+    Ro = oracle.b2bgemm(ref["A"], ref["B0"], ref["B1"], alpha=0.125, row_op="softmax", b0_layout="lk", causal=causal)
+    P.assert_close(P.gpu_to_f64(O), Ro, P.REL_F_BF16, P.MAX_ABS_BF16, "output unchanged by storing the statistics")

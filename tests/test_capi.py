@@ -104,6 +104,8 @@ def epi(**kw):
     (dict(M=1 << 20, epi=epi(x_out=PW, ld_x_out=1024, x_out_dtype=0)), cf.CF_ERR_UNSUPPORTED),  # 4 GiB X
     (dict(epi=epi(row_op=1, mask=1)), cf.CF_ERR_UNSUPPORTED),        # masks belong to the B2B softmax
     (dict(epi=epi(mask=3)), cf.CF_ERR_INVALID_ARGUMENT),
+    (dict(epi=epi(row_stats=PW)), cf.CF_ERR_INVALID_ARGUMENT),        # no row op, no statistics
+    (dict(epi=epi(row_op=2, row_stats=PW + 1)), cf.CF_ERR_INVALID_ARGUMENT),
     (dict(M=0), cf.CF_OK),            # empty problems launch nothing
     (dict(N=0), cf.CF_OK),
 ])
@@ -132,6 +134,10 @@ def b2b(batch=1, M=64, K=64, L=64, N=64, A=PA, lda=64, sa=0, B0=PB, ldb0=64, sb0
     (dict(mid=epi(residual=PW, ld_residual=64)), cf.CF_ERR_UNSUPPORTED),
     (dict(mid=epi(x_out=PW, ld_x_out=64)), cf.CF_ERR_UNSUPPORTED),   # S is never stored
     (dict(mid=epi(mask=1)), cf.CF_ERR_UNSUPPORTED),                  # causal needs the softmax
+    (dict(mid=epi(row_op=1, bias=PW)), cf.CF_ERR_UNSUPPORTED),       # softmax takes alpha * S as it is
+    (dict(mid=epi(row_op=1, act=1)), cf.CF_ERR_UNSUPPORTED),
+    (dict(mid=epi(row_stats=PW)), cf.CF_ERR_INVALID_ARGUMENT),       # statistics need a row op
+    (dict(mid=epi(row_op=1, row_stats=PW + 2)), cf.CF_ERR_INVALID_ARGUMENT),
     (dict(mid=epi(row_op=1, mask=2)), cf.CF_ERR_INVALID_ARGUMENT),
     (dict(batch=0), cf.CF_OK),
 ])
@@ -153,6 +159,7 @@ def test_workspace_sizes():
 def test_valid_calls_report_no_device():
     assert gemm(epi=epi(row_op=1, bias=PW)) == cf.CF_ERR_NO_DEVICE
     assert gemm(epi=epi(row_op=3, x_out=PW, ld_x_out=64)) == cf.CF_ERR_NO_DEVICE
+    assert gemm(epi=epi(row_op=1, row_stats=PW)) == cf.CF_ERR_NO_DEVICE
     assert b2b(mid=epi(row_op=1, alpha=0.125)) == cf.CF_ERR_NO_DEVICE
     assert b2b(lk=1, mid=epi(row_op=1, alpha=0.125, mask=1)) == cf.CF_ERR_NO_DEVICE
     assert lib.cf_workspace_init(PW, 4096, None) == cf.CF_ERR_NO_DEVICE

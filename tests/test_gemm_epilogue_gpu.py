@@ -315,3 +315,47 @@ def test_wide_strips(N, row_op):
     P.assert_close(P.gpu_to_f64(c32), R, P.REL_F_BF16, P.MAX_ABS_BF16, f"N={N} {row_op}")
     c16 = run(dev["A"], dev["B"], torch.bfloat16, **kw)
     P.assert_bf16_consistent(c16, c32, R, f"N={N} {row_op} bf16")
+
+
+# ---------------------------------------------------------------------------- row statistics of the reduction
+
+REL_F_STATS, MAX_ABS_STATS = 1e-5, 1e-4   # fp32 statistics of the fp32 x
+
+
+def stats_of(w, dev, ref, row_op, shape_out=torch.bfloat16, **extra):
+    M = dev["A"].shape[0]
+    st = torch.full((M, 2) if row_op == "layernorm" else (M,), float("nan"), dtype=torch.float32, device="cuda")
+    kw = {**epi_of(w, dev), "row_op": row_op, **extra}
+    run(dev["A"], dev["B"], shape_out, row_stats=st, **kw)
+    p = w.params
+    R = oracle.gemm_epilogue_row_stats(ref["A"], ref["B"], alpha=kw.get("alpha", 1.0), bias=ref.get("bias"),
+                                       residual=ref.get("residual"), act=kw.get("act", "none"), row_op=row_op,
+                                       eps=kw.get("eps", 0.0))
+    return P.gpu_to_f64(st), R
+
+
+@pytest.mark.parametrize("row_op", ["softmax", "layernorm", "rmsnorm"])
+def test_row_stats_fast_path(row_op):
+    w, dev, ref = P.inputs("c3_gemm_residual_rmsnorm", seed=15, M=300, N=1024, K=256)
+    got, R = stats_of(w, dev, ref, row_op, eps=1e-5, beta=None)
+    P.assert_close(got, R, REL_F_STATS, MAX_ABS_STATS, f"row stats {row_op}")
+
+
+@pytest.mark.parametrize("shape", [(33, 65, 17), (300, 520, 200)])
+@pytest.mark.parametrize("row_op", ["softmax", "layernorm", "rmsnorm"])
+def test_row_stats_general_path(shape, row_op):
+    M, N, K = shape
+    w, dev, ref = P.inputs("c3_gemm_residual_rmsnorm", seed=16, M=M, N=N, K=K)
+    got, R = stats_of(w, dev, ref, row_op, eps=1e-5, beta=None)
+    P.assert_close(got, R, REL_F_STATS, MAX_ABS_STATS, f"row stats {row_op} {shape}")
+
+
+def test_row_stats_f32_softmax_logsumexp():
+    w, dev, ref = P.inputs("c1_gemm_bias_softmax_f32", seed=17, M=300, N=768, K=96)
+    st = torch.empty(300, dtype=torch.float32, device="cuda")
+    C = run(dev["A"] * 30.0, dev["B"], torch.float32, bias=dev["bias"], row_op="softmax", row_stats=st)
+    R = oracle.gemm_epilogue_row_stats(ref["A"] * 30.0, ref["B"], bias=ref["bias"], row_op="softmax")
+    P.assert_close(P.gpu_to_f64(st), R, REL_F_STATS, MAX_ABS_STATS, "f32 log-sum-exp")
+    # consistency with the stored softmax: y = exp(x - lse)
+    X = oracle.elementwise_stage(oracle.matmul(ref["A"] * 30.0, ref["B"]), bias=ref["bias"])
+    P.assert_close(P.gpu_to_f64(C), np.exp(X - P.gpu_to_f64(st)[:, None]), REL_F_STATS, MAX_ABS_STATS, "y = exp(x - lse)")

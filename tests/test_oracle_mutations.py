@@ -61,6 +61,18 @@ MUTATIONS = {
         "return np.arange(L)[None, :] <= np.arange(M)[:, None] + (L - M)",
         "return np.arange(L)[None, :] <= np.arange(M)[:, None]")],
     "causal_mask_ignored": [("            S = np.where(vis, S, -np.inf)\n", "")],
+    "logsumexp_without_max": [(
+        "lse = mx + np.log(np.exp(X - mx).sum(axis=-1, keepdims=True))",
+        "lse = np.log(np.exp(X - mx).sum(axis=-1, keepdims=True))")],
+    "layernorm_stats_std_not_inverse": [(
+        "return np.concatenate([mu, 1.0 / np.sqrt(var + float(eps))], axis=-1)",
+        "return np.concatenate([mu, np.sqrt(var + float(eps))], axis=-1)")],
+    "rms_stats_drops_eps": [(
+        "return 1.0 / np.sqrt((X * X).mean(axis=-1) + float(eps))",
+        "return 1.0 / np.sqrt((X * X).mean(axis=-1))")],
+    "b2b_lse_keys_layout_ignored": [("        B0 = np.moveaxis(B0, -1, -2)\n", "        pass\n")],
+    "b2b_lse_ignores_alpha": [(
+        "    S = float(alpha) * matmul(A, B0)\n", "    S = matmul(A, B0)\n")],
     "b2b_relu_dropped": [(
         "S = elementwise_stage(matmul(A, B0), alpha, bias, None, act)",
         "S = elementwise_stage(matmul(A, B0), alpha, bias, None, 'none')")],

@@ -26,7 +26,7 @@ CF_OK, CF_ERR_INVALID_ARGUMENT, CF_ERR_UNSUPPORTED, CF_ERR_WORKSPACE, CF_ERR_NO_
     CF_ERR_HIP, CF_ERR_DEVICE_TIMEOUT = range(7)
 CF_F32, CF_BF16 = 0, 1
 ACT = {"none": 0, "relu": 1}
-ROW_OP = {"none": 0, "softmax": 1, "layernorm": 2, "rmsnorm": 3}
+ROW_OP = {"none": 0, "softmax": 1, "layernorm": 2, "rmsnorm": 3, "argmax": 4}
 MASK = {"none": 0, "causal": 1}
 
 
@@ -49,6 +49,7 @@ class cf_epilogue(ctypes.Structure):
         ("x_out_dtype", ctypes.c_int),
         ("mask", ctypes.c_int),
         ("row_stats", ctypes.c_void_p),
+        ("row_index", ctypes.c_void_p),
     ]
 
 
@@ -129,12 +130,14 @@ def _ptr(t) -> Optional[int]:
 
 def make_epilogue(*, alpha: float = 1.0, bias=None, residual=None, act: str = "none",
                   row_op: str = "none", gamma=None, beta=None, eps: float = 0.0, x_out=None,
-                  mask: str = "none", row_stats=None) -> cf_epilogue:
+                  mask: str = "none", row_stats=None, row_index=None) -> cf_epilogue:
     """cf_epilogue descriptor from tensors (bias/gamma/beta share one dtype).
     ``x_out``: optional [M, N] tensor that receives x before the row operation.
     ``mask``: "causal" for the softmax of cf_b2bgemm.
     ``row_stats``: optional contiguous fp32 tensor for the row operation's per-row
-    statistics (log-sum-exp; LayerNorm mean and 1/sigma; RMSNorm 1/rms)."""
+    statistics (log-sum-exp; LayerNorm mean and 1/sigma; RMSNorm 1/rms; the
+    row maximum for argmax). ``row_index``: contiguous int32 [M] tensor that
+    receives each row's argmax column (row_op "argmax")."""
     e = cf_epilogue()
     _lib.cf_epilogue_init(ctypes.byref(e))
     e.alpha = float(alpha)
@@ -147,6 +150,11 @@ def make_epilogue(*, alpha: float = 1.0, bias=None, residual=None, act: str = "n
         if row_stats.dtype != torch.float32 or not row_stats.is_contiguous():
             raise TypeError("row_stats must be a contiguous float32 tensor")
         e.row_stats = row_stats.data_ptr()
+    if row_index is not None:
+        import torch
+        if row_index.dtype != torch.int32 or not row_index.is_contiguous():
+            raise TypeError("row_index must be a contiguous int32 tensor")
+        e.row_index = row_index.data_ptr()
     vecs = [v for v in (bias, gamma, beta) if v is not None]
     if vecs:
         codes = {_dtype_code(v) for v in vecs}
@@ -198,7 +206,7 @@ def cf_workspace_status(ws, stream=None) -> int:
 def cf_gemm_epilogue(A, B, C, *, b_is_nk: bool = False, epi: Optional[cf_epilogue] = None,
                      workspace=None, stream=None, **epi_kwargs) -> None:
     """C = epilogue(A . B) in one kernel. A [M, K]; B [K, N] (or [N, K] with
-    b_is_nk); C [M, N]. The epilogue is ``epi`` or built from keyword
+    b_is_nk); C [M, N] (or None with row_op "argmax"). The epilogue is ``epi`` or built from keyword
     arguments (alpha, bias, residual, act, row_op, gamma, beta, eps, x_out)."""
     if epi is None:
         epi = make_epilogue(**epi_kwargs)
@@ -206,8 +214,11 @@ def cf_gemm_epilogue(A, B, C, *, b_is_nk: bool = False, epi: Optional[cf_epilogu
         raise TypeError("pass either epi or epilogue keywords")
     M, K = A.shape
     N = B.shape[0] if b_is_nk else B.shape[1]
-    if C.shape != (M, N):
+    if C is not None and C.shape != (M, N):
         raise ValueError(f"C must be [{M}, {N}]")
+    ri = epi_kwargs.get("row_index")
+    if ri is not None and ri.numel() < M:
+        raise ValueError("row_index is too small for M rows")
     x_out = epi_kwargs.get("x_out")
     if x_out is not None and tuple(x_out.shape) != (M, N):
         raise ValueError(f"x_out must be [{M}, {N}]")
@@ -216,8 +227,9 @@ def cf_gemm_epilogue(A, B, C, *, b_is_nk: bool = False, epi: Optional[cf_epilogu
         raise ValueError("row_stats is too small for M rows")
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
                                                            workspace.numel() * workspace.element_size())
+    c_ptr, ldc, c_dt = (None, 0, CF_BF16) if C is None else (C.data_ptr(), _ld(C), _dtype_code(C))
     _check(_lib.cf_gemm_epilogue(M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), int(b_is_nk),
-                                 _dtype_code(A), C.data_ptr(), _ld(C), _dtype_code(C), ctypes.byref(epi),
+                                 _dtype_code(A), c_ptr, ldc, c_dt, ctypes.byref(epi),
                                  ws_ptr, ws_bytes, _stream(stream)), "cf_gemm_epilogue")
 
 

@@ -89,7 +89,13 @@ cf_status check_epilogue(const cf_epilogue* epi, int64_t N, bool allow_row_ops_n
   if (epi->struct_size != sizeof(cf_epilogue)) return CF_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(epi->alpha) || !std::isfinite(epi->eps) || epi->eps < 0.0f) return CF_ERR_INVALID_ARGUMENT;
   if (epi->act != CF_ACT_NONE && epi->act != CF_ACT_RELU) return CF_ERR_INVALID_ARGUMENT;
-  if (epi->row_op < CF_ROW_NONE || epi->row_op > CF_ROW_RMSNORM) return CF_ERR_INVALID_ARGUMENT;
+  if (epi->row_op < CF_ROW_NONE || epi->row_op > CF_ROW_ARGMAX) return CF_ERR_INVALID_ARGUMENT;
+  if (epi->row_op == CF_ROW_ARGMAX) {
+    if (!epi->row_index || !aligned(epi->row_index, 4) || epi->gamma || epi->beta) return CF_ERR_INVALID_ARGUMENT;
+    if (!allow_residual) return CF_ERR_UNSUPPORTED;
+  } else if (epi->row_index) {
+    return CF_ERR_INVALID_ARGUMENT;
+  }
   if (!is_dtype(epi->vec_dtype) || !is_dtype(epi->residual_dtype)) return CF_ERR_INVALID_ARGUMENT;
   const size_t vs = dsize(epi->vec_dtype);
   if ((epi->bias && !aligned(epi->bias, vs)) || (epi->gamma && !aligned(epi->gamma, vs)) ||
@@ -173,16 +179,17 @@ cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K, const void* A, int64
   if (st != CF_OK) return st;
   if (M == 0 || N == 0) return CF_OK;
   const size_t es = dsize(ab_dtype), cs = dsize(c_dtype);
-  if (!C || ldc < N) return CF_ERR_INVALID_ARGUMENT;
+  const bool argmax = epi && epi->row_op == CF_ROW_ARGMAX;
+  if (C ? ldc < N : !argmax) return CF_ERR_INVALID_ARGUMENT;
   if (K > 0) {
     if (!A || !B || lda < K) return CF_ERR_INVALID_ARGUMENT;
     if (ldb < (b_is_nk ? K : N)) return CF_ERR_INVALID_ARGUMENT;
     if (!aligned(A, es) || !aligned(B, es)) return CF_ERR_INVALID_ARGUMENT;
   }
-  if (!aligned(C, cs)) return CF_ERR_INVALID_ARGUMENT;
+  if (C && !aligned(C, cs)) return CF_ERR_INVALID_ARGUMENT;
   if (M > INT32_MAX - kTile || N > INT32_MAX - kTile || K > INT32_MAX - kTile) return CF_ERR_UNSUPPORTED;
   // 32-bit buffer offsets: every operand (plus one tile of padding) below 2 GiB
-  if (!fits31(M, kTile, ldc, cs)) return CF_ERR_UNSUPPORTED;
+  if (C && !fits31(M, kTile, ldc, cs)) return CF_ERR_UNSUPPORTED;
   if (K > 0) {
     if (!fits31(M, kTile, lda, es)) return CF_ERR_UNSUPPORTED;
     if (b_is_nk ? !fits31(N, kTile, ldb, es) : !fits31(K, 64, ldb, es)) return CF_ERR_UNSUPPORTED;
@@ -202,8 +209,8 @@ cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K, const void* A, int64
 
   // fast path: 16-byte accesses everywhere, whole column tiles, bf16 (or no) residual
   const int64_t ce = ab_dtype == CF_F32 ? 4 : 8;
-  bool vec = (N % kTile == 0) && (K % ce == 0) && (lda % ce == 0) && (ldb % ce == 0) && (ldc % 8 == 0) &&
-             aligned(A, 16) && aligned(B, 16) && aligned(C, 16);
+  bool vec = (N % kTile == 0) && (K % ce == 0) && (lda % ce == 0) && (ldb % ce == 0) &&
+             (!C || (ldc % 8 == 0 && aligned(C, 16))) && aligned(A, 16) && aligned(B, 16);
   if (epi && epi->residual)
     vec = vec && epi->residual_dtype == CF_BF16 && epi->ld_residual % 8 == 0 && aligned(epi->residual, 16);
   if (X) vec = vec && epi->ld_x_out % 8 == 0 && aligned(X, 16);
@@ -224,17 +231,18 @@ cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K, const void* A, int64
   p.beta = epi ? epi->beta : nullptr;
   p.lda = (uint32_t)(K > 0 ? lda : 0);
   p.ldb = (uint32_t)(K > 0 ? ldb : 0);
-  p.ldc = (uint32_t)ldc;
+  p.ldc = (uint32_t)(C ? ldc : 0);
   p.ldr = (uint32_t)(p.residual ? epi->ld_residual : 0);
   p.a_bytes = (uint32_t)(K > 0 ? (uint64_t)M * lda * es : 0);
   p.b_bytes = (uint32_t)(K > 0 ? (uint64_t)(b_is_nk ? N : K) * ldb * es : 0);
-  p.c_bytes = (uint32_t)((uint64_t)M * ldc * cs);
+  p.c_bytes = (uint32_t)(C ? (uint64_t)M * ldc * cs : 0);
   p.r_bytes = (uint32_t)(p.residual ? (uint64_t)M * epi->ld_residual * dsize(rdt) : 0);
   p.X = X;
   p.ldx = (uint32_t)(X ? epi->ld_x_out : 0);
   p.x_bytes = (uint32_t)(X ? (uint64_t)M * epi->ld_x_out * xs : 0);
   p.x_f32 = X && epi->x_out_dtype == CF_F32;
   p.row_stats = epi ? epi->row_stats : nullptr;
+  p.row_index = epi ? epi->row_index : nullptr;
   p.M = (int)M;
   p.N = (int)N;
   p.K = (int)K;

@@ -39,6 +39,7 @@ struct GemmEpilogueParams {
   uint32_t ldx, x_bytes;
   int x_f32;         // dtype of X: 1 fp32, 0 bf16
   float* row_stats;  // optional per-row statistics of the row operation
+  int32_t* row_index;   // row argmax: column of each row's maximum
   uint32_t* ws_hdr;  // workspace header (NULL when tiles_n == 1 or no row op)
   uint64_t* ws_slots;
   uint64_t spin_ticks;   // wall-clock ticks a strip wait may take

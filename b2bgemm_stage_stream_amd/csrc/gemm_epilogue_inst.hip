@@ -1,7 +1,7 @@
 // One instantiation unit of the GEMM + epilogue kernel. Compiled once per
 // (input dtype, B layout, part): CF_IN_F32 in {0, 1}, CF_B_NK in {0, 1},
-// CF_PART in {0, 1, 2, 3} (fast path for row op CF_PART, with and without
-// bias/residual) or 4 (general path). Splitting the instantiations lets them
+// CF_PART in {0, 1, 2, 3, 4} (fast path for row op CF_PART, with and without
+// bias/residual) or 5 (general path). Splitting the instantiations lets them
 // compile in parallel.
 #include "gemm_epilogue_kernel.hpp"
 
@@ -17,7 +17,7 @@ namespace cf {
 
 // Kernel entry of this unit; `pre` selects the bias/residual variant.
 const void* CF_FN(int pre) {
-#if CF_PART < 4
+#if CF_PART < 5
   if (pre) return (const void*)&gemm_epilogue_kernel<CF_IN_F32 != 0, CF_B_NK != 0, true, CF_PART, true>;
   return (const void*)&gemm_epilogue_kernel<CF_IN_F32 != 0, CF_B_NK != 0, true, CF_PART, false>;
 #else

@@ -421,7 +421,7 @@ __device__ inline float2 halves(float v) {
   return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// ROW: 0 none, 1 softmax, 2 LayerNorm, 3 RMSNorm (cf_row_op).
+// ROW: 0 none, 1 softmax, 2 LayerNorm, 3 RMSNorm, 4 argmax (cf_row_op).
 // kFast: N is a multiple of 256, 16-byte accesses are allowed and the residual
 // (if any) is bf16; otherwise every column is masked against N.
 // kPre: a bias or a residual is present.
@@ -584,7 +584,7 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
         a = mm;
         b = q2;
         (void)cnt_w;
-      } else {
+      } else if constexpr (ROW == 3) {
         float s2 = 0.0f;
         for_groups([&](int nb, auto qc) {
           float x[4];
@@ -597,6 +597,30 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
           tok = s2;
         });
         a = sum_halves(s2);
+      } else {
+        // argmax: a lane visits its columns in increasing order, so a strict >
+        // keeps the first of equal values; the lane halves interleave and are
+        // merged with the column as tie-break (b holds the column's bits)
+        float mx = -INFINITY;
+        int ix = 0x7fffffff;
+        for_groups([&](int nb, auto qc) {
+          constexpr int q = decltype(qc)::value;
+          float x[4];
+          xgroup(mb, nb, qc, bias4(nb, q), tok, x);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (valid(nb, q, e) && x[e] > mx) {
+              mx = x[e];
+              ix = n0 + wn * 128 + nb * 32 + 8 * q + 4 * h + e;
+            }
+          }
+          tok = mx;
+        });
+        const float2 hm = halves(mx), hi = halves(__int_as_float(ix));
+        const int i0 = __float_as_int(hi.x), i1 = __float_as_int(hi.y);
+        const bool take1 = hm.y > hm.x || (hm.y == hm.x && i1 < i0);
+        a = take1 ? hm.y : hm.x;
+        b = __int_as_float(take1 ? i1 : i0);
       }
       if (h == 0) wpart[wn * 256 + wm * 128 + mb * 32 + r32] = make_float2(a, b);
     }
@@ -619,9 +643,13 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
         a = w0.x;
         b = w0.y;
         chan_merge(n, a, b, (float)c1, w1.x, w1.y);
-      } else {
+      } else if constexpr (ROW == 3) {
         a = w0.x + w1.x;
         b = 0.0f;
+      } else {   // argmax: the first column half holds the smaller columns
+        const bool take1 = c1 > 0 && w1.x > w0.x;
+        a = take1 ? w1.x : w0.x;
+        b = take1 ? w1.y : w0.y;
       }
       if (p.ws_hdr != nullptr && row_ok) {
         uint64_t* slots = p.ws_slots + (size_t)strip * p.tiles_n * 512 + 2 * ml;
@@ -633,7 +661,8 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
         // together. The merge then runs in tile order, so every workgroup of
         // the strip computes bit-identical statistics.
         float ra = 0.0f, rb = 0.0f, rn = 0.0f;
-        if constexpr (ROW == 1) ra = -INFINITY;
+        if constexpr (ROW == 1 || ROW == 4) ra = -INFINITY;
+        if constexpr (ROW == 4) rb = __int_as_float(0x7fffffff);
         for (int tb = 0; tb < p.tiles_n; tb += 8) {
           float va[8], vb[8];
           uint32_t need = 0;
@@ -684,8 +713,11 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
               ra = Mn;
             } else if constexpr (ROW == 2) {
               chan_merge(rn, ra, rb, (float)min(kGemmBN, p.N - tt * kGemmBN), va[j], vb[j]);
-            } else {
+            } else if constexpr (ROW == 3) {
               ra += va[j];
+            } else if (va[j] > ra) {   // argmax: tiles in column order, so ties keep the smaller column
+              ra = va[j];
+              rb = vb[j];
             }
           }
         }
@@ -695,14 +727,19 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
       float2 st;
       if constexpr (ROW == 1) st = make_float2(a * kLog2e, 1.0f / b);
       else if constexpr (ROW == 2) st = make_float2(a, rsqrtf(b / (float)p.N + p.eps));
-      else st = make_float2(rsqrtf(a / (float)p.N + p.eps), 0.0f);
+      else if constexpr (ROW == 3) st = make_float2(rsqrtf(a / (float)p.N + p.eps), 0.0f);
+      else st = make_float2(a, b);
       rstat[ml] = st;
       // the reduction's own per-row result, stored once per strip (column tile 0)
-      if (p.row_stats != nullptr && tn == 0 && row_ok) {
+      if (tn == 0 && row_ok) {
         const int m = m0 + ml;
-        if constexpr (ROW == 1) p.row_stats[m] = a + logf(b);   // log-sum-exp: max + ln sum exp(x - max)
-        else if constexpr (ROW == 2) { p.row_stats[2 * m] = a; p.row_stats[2 * m + 1] = st.y; }
-        else p.row_stats[m] = st.x;
+        if constexpr (ROW == 4) p.row_index[m] = __float_as_int(b);
+        if (p.row_stats != nullptr) {
+          if constexpr (ROW == 1) p.row_stats[m] = a + logf(b);   // log-sum-exp: max + ln sum exp(x - max)
+          else if constexpr (ROW == 2) { p.row_stats[2 * m] = a; p.row_stats[2 * m + 1] = st.y; }
+          else if constexpr (ROW == 3) p.row_stats[m] = st.x;
+          else p.row_stats[m] = a;
+        }
       }
     }
     __syncthreads();
@@ -800,6 +837,10 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
       }
     });
   };
+  // argmax without a matrix output (the logits are never written)
+  if constexpr (ROW == 4) {
+    if (p.C == nullptr && p.X == nullptr) return;
+  }
   using X0 = std::integral_constant<int, 0>;
   using X1 = std::integral_constant<int, 1>;
   using X2 = std::integral_constant<int, 2>;
@@ -970,6 +1011,7 @@ void gemm_epilogue_kernel(GemmEpilogueParams p) {
         case 1: epilogue<1, false, true, false>(acc, p, smem, strip, tn, tag, timed_out, tid_t); break;
         case 2: epilogue<2, false, true, false>(acc, p, smem, strip, tn, tag, timed_out, tid_t); break;
         case 3: epilogue<3, false, true, false>(acc, p, smem, strip, tn, tag, timed_out, tid_t); break;
+        case 4: epilogue<4, false, true, false>(acc, p, smem, strip, tn, tag, timed_out, tid_t); break;
         default: epilogue<0, false, true, false>(acc, p, smem, strip, tn, tag, timed_out, tid_t); break;
       }
     }

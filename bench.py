@@ -11,7 +11,7 @@ cache). Prints one JSON line:
              with the mean kernel time from HIP events on the launch stream
   cpu_baseline  the fp64 oracle timed on the host cores on a bounded row sample
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--store-x] [--causal]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--store-x] [--causal] [--argmax]
 """
 from __future__ import annotations
 
@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--store-x", action="store_true",
                     help="GEMM + epilogue workloads: also store x, the input of the row operation, as a second "
                          "bf16 [M, N] output (e.g. the new residual stream of a pre-norm block)")
+    ap.add_argument("--argmax", action="store_true",
+                    help="GEMM + epilogue workloads: replace the row operation by a row argmax and write no "
+                         "[M, N] output (a greedy LM-head step)")
     ap.add_argument("--causal", action="store_true",
                     help="attention workload: causal mask (key l visible to query m iff l <= m + L - M); the "
                          "algorithmic flops count only the visible (query, key) pairs")
@@ -97,16 +100,16 @@ def flops_of(w, causal: bool = False) -> float:
     return 2.0 * d["batch"] * pairs * (d["K"] + d["N"])
 
 
-def bytes_of(w, store_x: bool = False) -> float:
+def bytes_of(w, store_x: bool = False, argmax: bool = False) -> float:
     """Algorithmic HBM bytes: every input read once, the output (and X when
-    stored) written once."""
+    stored) written once; an argmax writes only its index and maximum per row."""
     tot = 0.0
     for t in w.tensors:
         tot += np.prod(w.shape(t)) * (2 if t.dtype == "bf16" else 4)
     d = w.dims
     out_es = 4 if w.params.get("out_dtype") == "f32" else 2
     if w.kind == "gemm_epilogue":
-        tot += d["M"] * d["N"] * out_es
+        tot += d["M"] * 8 if argmax else d["M"] * d["N"] * out_es
         if store_x:
             tot += d["M"] * d["N"] * 2
     else:
@@ -118,11 +121,11 @@ def is_f32(w) -> bool:
     return any(t.dtype == "f32" for t in w.tensors if t.name == "A")
 
 
-def roofline_of(w, kernel_ms: float, store_x: bool = False, causal: bool = False):
+def roofline_of(w, kernel_ms: float, store_x: bool = False, causal: bool = False, argmax: bool = False):
     """The roofline that bounds the kernel: HBM when the workload's flop/byte is
     below the ridge point (peak flops / HBM bandwidth), the MFMA peak above it.
     Returns (bound, unit, peak, achieved, intensity, ridge)."""
-    flops, nbytes = flops_of(w, causal), bytes_of(w, store_x)
+    flops, nbytes = flops_of(w, causal), bytes_of(w, store_x, argmax)
     peak_flops = PEAK_F32_TFLOPS if is_f32(w) else PEAK_BF16_TFLOPS
     intensity = flops / nbytes
     ridge = peak_flops * 1e12 / (HBM_GBPS * 1e9)
@@ -131,7 +134,7 @@ def roofline_of(w, kernel_ms: float, store_x: bool = False, causal: bool = False
     return "mfma", "TFLOP/s", peak_flops, flops / (kernel_ms * 1e-3) / 1e12, intensity, ridge
 
 
-def make_call(w, dev, torch, cf, store_x: bool = False, causal: bool = False):
+def make_call(w, dev, torch, cf, store_x: bool = False, causal: bool = False, argmax: bool = False):
     """Device tensors + a closure launching one fused kernel on the current stream."""
     p = w.params
     out_dt = torch.float32 if p.get("out_dtype") == "f32" else torch.bfloat16
@@ -139,16 +142,24 @@ def make_call(w, dev, torch, cf, store_x: bool = False, causal: bool = False):
     if w.kind == "gemm_epilogue":
         d = w.dims
         X = torch.empty(d["M"], d["N"], dtype=torch.bfloat16, device="cuda") if store_x else None
-        e = cf.make_epilogue(alpha=p["alpha"], bias=dev.get("bias"), residual=dev.get("residual"),
-                             act=p["act"], row_op=p["row_op"], gamma=dev.get("gamma", dev.get("weight")),
-                             beta=dev.get("beta"), eps=p.get("eps", 0.0), x_out=X)
+        if argmax:
+            idx = torch.empty(d["M"], dtype=torch.int32, device="cuda")
+            mx = torch.empty(d["M"], dtype=torch.float32, device="cuda")
+            e = cf.make_epilogue(alpha=p["alpha"], bias=dev.get("bias"), residual=dev.get("residual"),
+                                 act=p["act"], row_op="argmax", row_index=idx, row_stats=mx, x_out=X)
+            C = None
+        else:
+            idx = mx = None
+            e = cf.make_epilogue(alpha=p["alpha"], bias=dev.get("bias"), residual=dev.get("residual"),
+                                 act=p["act"], row_op=p["row_op"], gamma=dev.get("gamma", dev.get("weight")),
+                                 beta=dev.get("beta"), eps=p.get("eps", 0.0), x_out=X)
+            C = torch.empty(d["M"], d["N"], dtype=out_dt, device="cuda")
         nbytes = cf.cf_gemm_epilogue_workspace_size(d["M"], d["N"], d["K"], e)
         ws = cf.Workspace("cuda").get(nbytes)
-        C = torch.empty(d["M"], d["N"], dtype=out_dt, device="cuda")
 
         def call():
             cf.cf_gemm_epilogue(dev["A"], dev["B"], C, epi=e, workspace=ws, stream=stream)
-        call.keep = X        # the second output lives as long as the closure
+        call.keep = (X, idx, mx)   # the extra outputs live as long as the closure
         return call, C, ws, nbytes
     d = w.dims
     e = cf.make_epilogue(alpha=p["alpha"], act=p["act"], row_op=p["row_op"], mask="causal" if causal else "none")
@@ -160,7 +171,7 @@ def make_call(w, dev, torch, cf, store_x: bool = False, causal: bool = False):
     return call, O, None, 0
 
 
-def cpu_baseline(w, raw, target_s: float, causal: bool = False):
+def cpu_baseline(w, raw, target_s: float, causal: bool = False, argmax: bool = False):
     """The fp64 oracle on a bounded sample of rows (rows are independent)."""
     import oracle
     ncores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
@@ -178,9 +189,12 @@ def cpu_baseline(w, raw, target_s: float, causal: bool = False):
         def run(rows):
             A = widen("A")[:rows] if rows < d["M"] else widen("A")
             R = widen("residual")[:rows] if "residual" in raw else None
-            oracle.gemm_epilogue(A, B, alpha=p["alpha"], bias=vec.get("bias"), residual=R, act=p["act"],
-                                 row_op=p["row_op"], gamma=vec.get("gamma", vec.get("weight")),
-                                 beta=vec.get("beta"), eps=p.get("eps", 0.0))
+            if argmax:
+                oracle.gemm_epilogue_argmax(A, B, alpha=p["alpha"], bias=vec.get("bias"), residual=R, act=p["act"])
+            else:
+                oracle.gemm_epilogue(A, B, alpha=p["alpha"], bias=vec.get("bias"), residual=R, act=p["act"],
+                                     row_op=p["row_op"], gamma=vec.get("gamma", vec.get("weight")),
+                                     beta=vec.get("beta"), eps=p.get("eps", 0.0))
         unit_flops = 2.0 * d["N"] * d["K"]          # per row
         total_units = d["M"]
         what = "rows of the output"
@@ -241,6 +255,8 @@ def main():
     w = gen.workload(args.workload)
     if args.store_x and w.kind != "gemm_epilogue":
         raise SystemExit("--store-x applies to the GEMM + epilogue workloads")
+    if args.argmax and w.kind != "gemm_epilogue":
+        raise SystemExit("--argmax applies to the GEMM + epilogue workloads")
     if args.causal and (w.kind != "b2bgemm" or w.params["row_op"] != "softmax"):
         raise SystemExit("--causal applies to the attention (softmax B2BGEMM) workload")
     if args.plain:
@@ -260,7 +276,7 @@ def main():
     devs = [dev] + [{k: v.clone() for k, v in dev.items()} for _ in range(nset - 1)]
     calls = []
     for d_ in devs:
-        call, out, ws, ws_bytes = make_call(w, d_, torch, cf, args.store_x, args.causal)
+        call, out, ws, ws_bytes = make_call(w, d_, torch, cf, args.store_x, args.causal, args.argmax)
         calls.append(call)
 
     for i in range(max(args.warmup, nset)):
@@ -284,9 +300,10 @@ def main():
     flops = flops_of(w, args.causal)
     value = flops / (ms_per_step * 1e-3) / 1e12
     in_f32 = is_f32(w)
-    bound, unit, peak, achieved, intensity, ridge = roofline_of(w, kernel_ms, args.store_x, args.causal)
+    bound, unit, peak, achieved, intensity, ridge = roofline_of(w, kernel_ms, args.store_x, args.causal,
+                                                                args.argmax)
     traffic = None
-    if os.path.exists(args.traffic) and not args.plain and not args.store_x and not args.causal:
+    if os.path.exists(args.traffic) and not (args.plain or args.store_x or args.causal or args.argmax):
         try:
             rec = json.load(open(args.traffic))
             if rec.get("kernel_source_hash") == kernel_source_hash():
@@ -307,19 +324,20 @@ def main():
         "dtype": "f32" if in_f32 else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name + ("/identity-epilogue" if args.plain else "")
-                   + ("+x_out" if args.store_x else "") + ("/causal" if args.causal else ""), **w.dims,
+                   + ("+x_out" if args.store_x else "") + ("/causal" if args.causal else "")
+                   + ("/argmax" if args.argmax else ""), **w.dims,
                    "out_dtype": w.params.get("out_dtype"), "input_sets": nset, "input_bytes_per_set": in_bytes},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "arithmetic_intensity": round(intensity, 1), "ridge": round(ridge, 1)},
         "kernel_ms": round(kernel_ms, 4),
-        "algorithmic_bytes": bytes_of(w, args.store_x),
+        "algorithmic_bytes": bytes_of(w, args.store_x, args.argmax),
         "intermediate_hbm_bytes": 0,
         "workspace_bytes": ws_bytes,
     }
     if not args.no_cpu_baseline:
         del dev, devs, calls, out
-        line["cpu_baseline"] = cpu_baseline(w, raw, args.cpu_seconds, args.causal)
+        line["cpu_baseline"] = cpu_baseline(w, raw, args.cpu_seconds, args.causal, args.argmax)
     print(json.dumps(line), flush=True)
 
 

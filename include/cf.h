@@ -55,7 +55,12 @@ typedef enum {
   CF_ROW_SOFTMAX = 1,   /* y = exp(x - max_n x) / sum_n exp(x - max_n x)                 */
   CF_ROW_LAYERNORM = 2, /* y = (x - mean) / sqrt(var + eps) * gamma[n] + beta[n]; var is
                            the biased (1/N) variance; gamma/beta optional (NULL = 1 / 0) */
-  CF_ROW_RMSNORM = 3    /* y = x / sqrt(mean_n x^2 + eps) * gamma[n]; gamma optional     */
+  CF_ROW_RMSNORM = 3,   /* y = x / sqrt(mean_n x^2 + eps) * gamma[n]; gamma optional     */
+  CF_ROW_ARGMAX = 4     /* cf_gemm_epilogue only: row_index[m] = the smallest n with
+                           x[m, n] = max_n x[m, n] (NaN never wins), row_stats[m] (if
+                           given) = that maximum; y = x is stored only when C != NULL
+                           (C may be NULL: the logits of a greedy LM head are never
+                           written). gamma and beta must be NULL.                      */
 } cf_row_op;
 
 /* Visibility mask on the scores S of cf_b2bgemm's softmax (ignored nowhere:
@@ -100,6 +105,7 @@ typedef enum {
  *   CF_ROW_SOFTMAX   row_stats[m]         = ln sum_n exp(x[m, n])  (log-sum-exp)
  *   CF_ROW_LAYERNORM row_stats[2m], [2m+1] = mean, 1 / sqrt(var + eps)
  *   CF_ROW_RMSNORM   row_stats[m]         = 1 / sqrt(mean_n x^2 + eps)
+ *   CF_ROW_ARGMAX    row_stats[m]         = max_n x[m, n]
  * cf_b2bgemm (softmax only): row_stats[b * M + m] = ln sum_l exp(alpha * S[m, l])
  * over the visible keys; -inf for a causal row that sees none.
  * Must be 4-byte aligned; CF_ERR_INVALID_ARGUMENT with CF_ROW_NONE. */
@@ -121,6 +127,7 @@ typedef struct cf_epilogue {
   cf_dtype x_out_dtype;     /* CF_BF16 or CF_F32                                  */
   cf_mask mask;             /* cf_b2bgemm with row_op CF_ROW_SOFTMAX only         */
   float* row_stats;         /* optional fp32 per-row statistics of the row op (see below) */
+  int32_t* row_index;       /* CF_ROW_ARGMAX: [M] column of each row's maximum (required) */
 } cf_epilogue;
 
 /* Fills *epi with the identity epilogue (alpha 1, no bias/residual/act/row op). */
@@ -153,7 +160,7 @@ cf_status cf_workspace_status(const void* ws, void* stream);
  *   B       [K, N] (b_is_nk = 0) or [N, K] (b_is_nk = 1, the nn.Linear weight
  *           layout) with leading dimension ldb, dtype ab_dtype.
  *   C       [M, N] with leading dimension ldc, dtype c_dtype. Must not overlap
- *           the inputs.
+ *           the inputs. May be NULL (ldc then unused) with CF_ROW_ARGMAX.
  *   ab_dtype CF_BF16 (bf16 MFMA, fp32 accumulation) or CF_F32 (fp32 MFMA).
  *   epi     epilogue descriptor (NULL = identity).
  *   ws      workspace of at least cf_gemm_epilogue_workspace_size() bytes,

@@ -192,6 +192,23 @@ def row_statistics(X: np.ndarray, row_op: str, eps: float = 0.0) -> np.ndarray:
     raise ValueError(f"row_op {row_op!r} has no row statistics")
 
 
+def row_argmax(X: np.ndarray):
+    """(index, value) of each row: the smallest column n with X[m, n] equal to
+    the row maximum, and that maximum (the review's "Reading between the lines"
+    names max for top-k among the single-axis reductions the strip argument
+    covers; top-1 here, ties to the lowest column)."""
+    idx = np.argmax(X, axis=-1)
+    return idx, np.take_along_axis(X, idx[..., None], axis=-1)[..., 0]
+
+
+def gemm_epilogue_argmax(A: np.ndarray, B: np.ndarray, *, alpha: float = 1.0,
+                         bias: Optional[np.ndarray] = None, residual: Optional[np.ndarray] = None,
+                         act: str = "none"):
+    """row_argmax of the elementwise stage's result X = act(alpha A.B + bias + R)
+    (e.g. greedy decoding on an LM head: the logits themselves are not needed)."""
+    return row_argmax(elementwise_stage(matmul(A, B), alpha, bias, residual, act))
+
+
 def gemm_epilogue_row_stats(A: np.ndarray, B: np.ndarray, *, alpha: float = 1.0,
                             bias: Optional[np.ndarray] = None, residual: Optional[np.ndarray] = None,
                             act: str = "none", row_op: str = "softmax", eps: float = 0.0) -> np.ndarray:

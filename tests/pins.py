@@ -441,9 +441,40 @@ def pin_b2b_logsumexp(o):
             _close_dec(got[i], want, rtol=1e-13, atol=1e-14)
 
 
+def pin_row_argmax(o):
+    """Row argmax against an exact brute force (first column attaining the
+    maximum of exact rationals), with exact ties built from duplicated columns."""
+    rng = np.random.default_rng(15)
+    m, k, n = 4, 5, 9
+    A = _bf16_values(rng, (m, k))
+    B = _bf16_values(rng, (k, n))
+    B[:, 6] = B[:, 2]               # column 6 ties column 2 exactly in every row
+    B[:, 8] = B[:, 0]
+    bias = _bf16_values(rng, (n,))
+    bias[6] = bias[2]
+    bias[8] = bias[0]
+    R = np.zeros((m, n))
+    R[1] = 5.0                      # row 1: every column shifted alike
+    E = X.mm(X.mat(A), X.mat(B))
+    for act in ("none", "relu"):
+        idx, val = o.gemm_epilogue_argmax(A, B, alpha=0.5, bias=bias, residual=R, act=act)
+        for i in range(m):
+            xs = [Fraction(1, 2) * E[i][j] + X.F(bias[j]) + X.F(R[i, j]) for j in range(n)]
+            if act == "relu":
+                xs = [max(v, Fraction(0)) for v in xs]
+            best = max(xs)
+            first = xs.index(best)
+            assert int(idx[i]) == first, (act, i, int(idx[i]), first)
+            assert Fraction(float(val[i])) == best
+    # a constant row: column 0; a strictly increasing row: the last column
+    i0, v0 = o.row_argmax(np.full((1, 5), 2.5))
+    i1, v1 = o.row_argmax(np.arange(6.0)[None, :])
+    assert int(i0[0]) == 0 and v0[0] == 2.5 and int(i1[0]) == 5 and v1[0] == 5.0
+
+
 ALL_PINS = [pin_round_bf16, pin_widen_bf16, pin_matmul_exact, pin_stage1_exact, pin_softmax,
             pin_layernorm, pin_rmsnorm, pin_gemm_epilogue_composition, pin_two_outputs, pin_b2b_relu,
-            pin_b2b_softmax, pin_b2b_causal, pin_row_statistics, pin_b2b_logsumexp]
+            pin_b2b_softmax, pin_b2b_causal, pin_row_statistics, pin_b2b_logsumexp, pin_row_argmax]
 
 
 def run_all(o):

@@ -37,6 +37,8 @@ def test_algorithmic_counts():
     # the second output X of a pre-norm block adds one bf16 [M, N] write
     w3 = gen.workload("c3_gemm_residual_rmsnorm")
     assert bench.bytes_of(w3, store_x=True) - bench.bytes_of(w3) == 2 * 16384 * 4096
+    # an argmax writes an index and a maximum per row instead of the [M, N] output
+    assert bench.bytes_of(w, argmax=True) == bench.bytes_of(w) - 2 * 8192 * 4096 + 8 * 8192
     w5 = gen.workload("c5_b2b_attention")
     assert bench.flops_of(w5) == 2.0 * 512 * 1024 * (64 * 1024 + 1024 * 64)
     # causal: row m of a square problem sees m + 1 keys

@@ -105,6 +105,12 @@ def epi(**kw):
     (dict(epi=epi(row_op=1, mask=1)), cf.CF_ERR_UNSUPPORTED),        # masks belong to the B2B softmax
     (dict(epi=epi(mask=3)), cf.CF_ERR_INVALID_ARGUMENT),
     (dict(epi=epi(row_stats=PW)), cf.CF_ERR_INVALID_ARGUMENT),        # no row op, no statistics
+    (dict(epi=epi(row_op=4)), cf.CF_ERR_INVALID_ARGUMENT),            # argmax needs row_index
+    (dict(epi=epi(row_op=4, row_index=PW + 2)), cf.CF_ERR_INVALID_ARGUMENT),
+    (dict(epi=epi(row_op=4, row_index=PW, gamma=PB)), cf.CF_ERR_INVALID_ARGUMENT),
+    (dict(epi=epi(row_op=1, row_index=PW)), cf.CF_ERR_INVALID_ARGUMENT),   # row_index belongs to argmax
+    (dict(epi=epi(row_op=5)), cf.CF_ERR_INVALID_ARGUMENT),
+    (dict(C=None, epi=epi(row_op=3)), cf.CF_ERR_INVALID_ARGUMENT),    # only argmax may omit C
     (dict(epi=epi(row_op=2, row_stats=PW + 1)), cf.CF_ERR_INVALID_ARGUMENT),
     (dict(M=0), cf.CF_OK),            # empty problems launch nothing
     (dict(N=0), cf.CF_OK),
@@ -139,6 +145,7 @@ def b2b(batch=1, M=64, K=64, L=64, N=64, A=PA, lda=64, sa=0, B0=PB, ldb0=64, sb0
     (dict(mid=epi(row_stats=PW)), cf.CF_ERR_INVALID_ARGUMENT),       # statistics need a row op
     (dict(mid=epi(row_op=1, row_stats=PW + 2)), cf.CF_ERR_INVALID_ARGUMENT),
     (dict(mid=epi(row_op=1, mask=2)), cf.CF_ERR_INVALID_ARGUMENT),
+    (dict(mid=epi(row_op=4, row_index=PW)), cf.CF_ERR_UNSUPPORTED),   # argmax between two GEMMs
     (dict(batch=0), cf.CF_OK),
 ])
 def test_b2bgemm_argument_checks(kw, status):
@@ -160,6 +167,7 @@ def test_valid_calls_report_no_device():
     assert gemm(epi=epi(row_op=1, bias=PW)) == cf.CF_ERR_NO_DEVICE
     assert gemm(epi=epi(row_op=3, x_out=PW, ld_x_out=64)) == cf.CF_ERR_NO_DEVICE
     assert gemm(epi=epi(row_op=1, row_stats=PW)) == cf.CF_ERR_NO_DEVICE
+    assert gemm(C=None, ldc=0, epi=epi(row_op=4, row_index=PW)) == cf.CF_ERR_NO_DEVICE
     assert b2b(mid=epi(row_op=1, alpha=0.125)) == cf.CF_ERR_NO_DEVICE
     assert b2b(lk=1, mid=epi(row_op=1, alpha=0.125, mask=1)) == cf.CF_ERR_NO_DEVICE
     assert lib.cf_workspace_init(PW, 4096, None) == cf.CF_ERR_NO_DEVICE

@@ -359,3 +359,80 @@ def test_row_stats_f32_softmax_logsumexp():
     # consistency with the stored softmax: y = exp(x - lse)
     X = oracle.elementwise_stage(oracle.matmul(ref["A"] * 30.0, ref["B"]), bias=ref["bias"])
     P.assert_close(P.gpu_to_f64(C), np.exp(X - P.gpu_to_f64(st)[:, None]), REL_F_STATS, MAX_ABS_STATS, "y = exp(x - lse)")
+
+
+# ---------------------------------------------------------------------------- row argmax
+
+def run_argmax(A, B, with_c, **epi):
+    M, N = A.shape[0], B.shape[1]
+    idx = torch.full((M,), -1, dtype=torch.int32, device="cuda")
+    val = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
+    e = cf.make_epilogue(row_op="argmax", row_index=idx, row_stats=val, **epi)
+    ws = _WS.get(cf.cf_gemm_epilogue_workspace_size(M, N, A.shape[1], e))
+    C = torch.empty(M, N, dtype=torch.float32, device="cuda") if with_c else None
+    cf.cf_gemm_epilogue(A, B, C, epi=e, workspace=ws)
+    torch.cuda.synchronize()
+    if ws is not None:
+        assert cf.cf_workspace_status(ws) == cf.CF_OK
+    return idx, val, C
+
+
+def check_argmax(idx, val, X, what):
+    """The maximum matches; the column is the oracle's wherever the row maximum is
+    separated from the runner-up by more than the fp32 rounding bound, and is
+    otherwise a column within that bound of the maximum (several answers are then
+    correct up to rounding)."""
+    oi, ov = oracle.row_argmax(X)
+    gi = idx.cpu().numpy().astype(np.int64)
+    P.assert_close(P.gpu_to_f64(val), ov, 1e-5, 1e-4, what + " max value")
+    tol = 1e-4 * max(1.0, float(np.abs(X).max()))
+    rows = np.arange(X.shape[0])
+    assert np.all((gi >= 0) & (gi < X.shape[1])), what + ": column out of range"
+    srt = np.sort(X, axis=1)
+    sep = (srt[:, -1] - srt[:, -2]) > tol if X.shape[1] > 1 else np.ones(X.shape[0], bool)
+    bad = int((gi[sep] != oi[sep]).sum())
+    assert bad == 0, f"{what}: {bad} rows with a separated maximum disagree"
+    assert np.all(X[rows, gi] >= ov - tol), what + ": a chosen column is not a maximum"
+
+
+@pytest.mark.parametrize("N", [256, 1024, 4096])
+def test_argmax_fast_path(N):
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=19, M=300, N=N, K=512)
+    X = oracle.elementwise_stage(oracle.matmul(ref["A"], ref["B"]))
+    idx, val, _ = run_argmax(dev["A"], dev["B"], False)
+    check_argmax(idx, val, X, f"argmax N={N}")
+
+
+@pytest.mark.parametrize("shape", [(33, 65, 17), (300, 520, 200), (1, 1000, 9)])
+def test_argmax_general_path_with_logits(shape):
+    M, N, K = shape
+    w, dev, ref = P.inputs("c3_gemm_residual_rmsnorm", seed=20, M=M, N=N, K=K)
+    bias = torch.linspace(-0.3, 0.3, N, device="cuda").to(torch.bfloat16)
+    X = oracle.elementwise_stage(oracle.matmul(ref["A"], ref["B"]), 0.5, P.gpu_to_f64(bias), ref["residual"], "relu")
+    idx, val, C = run_argmax(dev["A"], dev["B"], True, alpha=0.5, bias=bias, residual=dev["residual"], act="relu")
+    check_argmax(idx, val, X, f"argmax {shape}")
+    P.assert_close(P.gpu_to_f64(C), X, P.REL_F_BF16, P.MAX_ABS_BF16, f"argmax {shape}: C = x")
+
+
+@pytest.mark.parametrize("N,cols", [(4096, (5, 700, 3000)), (300, (7, 260, 299))])
+def test_argmax_exact_ties_across_tiles(N, cols):
+    # equal columns of B and equal bias give bit-identical x in every row; a large
+    # bias makes them the row maximum, so the lowest of them must win in every row
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=21, M=260, N=N, K=256)
+    B = dev["B"].clone()
+    for c in cols[1:]:
+        B[:, c] = B[:, cols[0]]
+    bias = torch.zeros(N, device="cuda", dtype=torch.bfloat16)
+    bias[list(cols)] = 50.0
+    idx, val, _ = run_argmax(dev["A"], B, False, bias=bias)
+    assert torch.all(idx == cols[0]), f"ties resolved to {torch.unique(idx).tolist()}"
+
+
+def test_argmax_full_size_sampled_rows():
+    # C2 shape as an LM-head-like greedy step: no logits written
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=0)
+    idx, val, _ = run_argmax(dev["A"], dev["B"], False)
+    rows = np.concatenate([np.random.default_rng(2).choice(w.dims["M"], 30, replace=False), [0, w.dims["M"] - 1]])
+    X = oracle.elementwise_stage(oracle.matmul(ref["A"][rows], ref["B"]))
+    check_argmax(idx[torch.as_tensor(rows, device="cuda")], val[torch.as_tensor(rows, device="cuda")], X,
+                 "argmax C2 full size")

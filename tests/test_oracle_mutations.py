@@ -73,6 +73,10 @@ MUTATIONS = {
     "b2b_lse_keys_layout_ignored": [("        B0 = np.moveaxis(B0, -1, -2)\n", "        pass\n")],
     "b2b_lse_ignores_alpha": [(
         "    S = float(alpha) * matmul(A, B0)\n", "    S = matmul(A, B0)\n")],
+    "argmax_ties_to_last_column": [(
+        "    idx = np.argmax(X, axis=-1)\n",
+        "    idx = X.shape[-1] - 1 - np.argmax(X[..., ::-1], axis=-1)\n")],
+    "argmax_is_argmin": [("    idx = np.argmax(X, axis=-1)\n", "    idx = np.argmin(X, axis=-1)\n")],
     "b2b_relu_dropped": [(
         "S = elementwise_stage(matmul(A, B0), alpha, bias, None, act)",
         "S = elementwise_stage(matmul(A, B0), alpha, bias, None, 'none')")],

@@ -405,7 +405,10 @@ void b2b_stream_kernel(B2bParams p) {
         asm volatile("" ::: "memory");
         issue(lc + NS - 1, nseg, rs0, rs1);   // into the buffer of segment lc - 1
       }
-      segment(smem + (lc % NS) * C::kStage, lc, af, oacc, cst, lsum, wrow0);
+      // causal: a wave whose rows see none of the segment skips its arithmetic
+      // (it still takes part in the workgroup's barriers and loads)
+      if (!kCausal || lc * kTLC <= wrow0 + MB * 32 - 1 + p.coff)
+        segment(smem + (lc % NS) * C::kStage, lc, af, oacc, cst, lsum, wrow0);
     }
     if (!resident) {
       // the next tile's first segments reuse the ring

@@ -1,9 +1,9 @@
 """Lowering of a traced torch subgraph to one fused call.
 
 A small analogue of the front-end the ComFuse review describes (the abstract
-and "What carries the argument": tensor subprograms are lowered automatically
-into fused kernels through a fusion specification, not matched against a fixed
-list of patterns). Here the subprogram is a torch function traced with
+and "What carries the argument": a compiler that turns tensor subprograms into
+fused kernels by itself, through a fusion specification rather than a fixed
+table of patterns). Here the subprogram is a torch function traced with
 torch.fx; every node is placed by its operator and the shapes of its operands
 into the stage stream of one kernel:
 

@@ -340,6 +340,7 @@ cf_status cf_b2bgemm(int64_t batch, int64_t M, int64_t K, int64_t L, int64_t N, 
   p.row_op = mid ? (int)mid->row_op : 0;
   p.out_f32 = out_dtype == CF_F32;
   p.bias_f32 = (mid && mid->vec_dtype == CF_F32) ? 1 : 0;
+  p.bias_vec = p.bias && aligned(p.bias, 4);
   p.b0_lk = b0_is_lk;
   p.o_vec = aligned(O, 16) && ldo % 4 == 0 && so % 4 == 0;
   p.causal = mid && mid->mask == CF_MASK_CAUSAL;

@@ -35,18 +35,23 @@ constexpr int kTThreads = 256;
 // give each wave four independent accumulator chains and let every B0/B1
 // fragment read from LDS feed two MFMAs; one keeps tiles small when there
 // are few rows.
-template <int KS, int NB, int MB_>
+// kBiasEsz: bytes per bias element (0: no bias). A stage then ends with a
+// 256-byte block holding the segment's kTLC bias values.
+template <int KS, int NB, int MB_, int kBiasEsz = 0>
 struct TCfg {
   static constexpr int K = 16 * KS, N = 32 * NB;
   static constexpr int MB = MB_;
   static constexpr int BM = 128 * MB;                            // rows per tile
   static constexpr int kB0Bytes = kTLC * K * 2;
   static constexpr int kB1Bytes = kTLC * N * 2;
-  static constexpr int kStage = kB0Bytes + kB1Bytes;
+  static constexpr int kBiasOff = kB0Bytes + kB1Bytes;
+  static constexpr int kStage = kBiasOff + (kBiasEsz ? 256 : 0);
   static constexpr int kStages = 4 * kStage <= 80 * 1024 ? 4 : 3 * kStage <= 80 * 1024 ? 3 : 2;
   static constexpr int kLds = kStages * kStage;
   static constexpr int kB0Blocks = kB0Bytes / 1024;              // 1 KiB DMA blocks
-  static constexpr int kLoads = kStage / (kTThreads * 16);       // DMA loads per thread per segment
+  static constexpr int kLoads = kBiasOff / (kTThreads * 16);     // B0/B1 DMA loads per thread per segment
+  static constexpr int kLoadsAll = kLoads + (kBiasEsz ? 1 : 0);  // with the bias load
+  static constexpr int kBiasLanes = kTLC * kBiasEsz / 4;         // lanes of the (4-byte) bias load that carry data
 };
 
 // XOR swizzles of the 16-byte chunks of an LDS row (physical = logical ^ f):
@@ -63,10 +68,14 @@ __device__ inline int swz_tr256(int r) { return (2 * (r & 3)) ^ (4 * (r & 3)); }
 // segments past the last key a tile's rows see are not computed, the segment
 // on the diagonal is masked per element, and row tiles that see more keys are
 // scheduled first.
-template <int KS, int NB, int MB_, bool kSoftmax, bool kB0LK, bool kCausal = false>
+// kBias (elementwise F only): S gets a bias per column l, 1 bf16 or 2 fp32.
+// Each wave streams the segment's bias into the stage's bias block with the
+// ring, 4 bytes per lane (all four waves write the same bytes), so every wave
+// issues the same number of ring loads; the bias base must be 4-byte aligned.
+template <int KS, int NB, int MB_, bool kSoftmax, bool kB0LK, bool kCausal = false, int kBias = 0>
 __global__ __attribute__((amdgpu_flat_work_group_size(kTThreads, kTThreads), amdgpu_waves_per_eu(2, 2)))
 void b2b_stream_kernel(B2bParams p) {
-  using C = TCfg<KS, NB, MB_>;
+  using C = TCfg<KS, NB, MB_, kBias == 2 ? 4 : kBias == 1 ? 2 : 0>;
   constexpr int NS = C::kStages;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::kLds];
 
@@ -143,13 +152,17 @@ void b2b_stream_kernel(B2bParams p) {
       b1_rd[nb] = (uint32_t)(C::kB0Bytes + (4 * (g >> 1) + (i >> 2)) * RB + 16 * ((4 * nb + c) ^ f) + 8 * (i & 1));
   }
 
+  const u32x4_t rsb = rsrc_words(p.bias, (uint32_t)p.L * (kBias == 2 ? 4u : 2u));
   auto issue = [&](int s, int nseg, const u32x4_t& rs0, const u32x4_t& rs1) {
-    const uint32_t st = (uint32_t)__builtin_amdgcn_readfirstlane(
-        (int)(lds0 + (uint32_t)((s % NS) * C::kStage + wave * 1024)));
+    const uint32_t sb = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds0 + (uint32_t)((s % NS) * C::kStage)));
+    const uint32_t st = sb + (uint32_t)(wave * 1024);
     const bool ok = s < nseg;
 #pragma unroll
     for (int i = 0; i < C::kLoads; ++i)
       lds_dma16(st + i * 4096, is_b0[i] ? rs0 : rs1, ok ? goff[i] + (uint32_t)s * gstep[i] : kOutOfRange);
+    if constexpr (kBias != 0)
+      lds_dma4(sb + C::kBiasOff, rsb,
+               ok && lane < C::kBiasLanes ? (uint32_t)(s * C::kBiasLanes + lane) * 4u : kOutOfRange);
   };
 
   // one segment: GEMM1, F, GEMM2 on stage buffer st; row block rb of the wave.
@@ -283,12 +296,27 @@ void b2b_stream_kernel(B2bParams p) {
 #pragma unroll
         for (int lb = 0; lb < 2; ++lb) {
           float x[16];
-          if (p.bias) {
-            const int lbase = lc * kTLC + lb * 32 + 4 * h;
+          if constexpr (kBias != 0) {
+            // the lane's columns: four runs j of four l from lb*32 + 4h + 8j
+            uint32_t bwd[16];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int l0 = lb * 32 + 4 * h + 8 * j;
+              if constexpr (kBias == 2) {
+                const u32x4_t v = *(const u32x4_t*)(st + C::kBiasOff + l0 * 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bwd[4 * j + e] = v[e];
+              } else {
+                const u32x2_t v = *(const u32x2_t*)(st + C::kBiasOff + l0 * 2);
+                bwd[4 * j] = v[0] << 16;
+                bwd[4 * j + 1] = v[0] & 0xffff0000u;
+                bwd[4 * j + 2] = v[1] << 16;
+                bwd[4 * j + 3] = v[1] & 0xffff0000u;
+              }
+            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int l = lbase + 8 * (r >> 2) + (r & 3);
-              const float bv = p.bias_f32 ? ((const float*)p.bias)[l] : bf16_to_f32(((const uint16_t*)p.bias)[l]);
+              const float bv = __uint_as_float(bwd[r]);
               x[r] = fmaxf(__builtin_fmaf(sacc[rb][lb][r], scale, bv), floor_v);
             }
           } else {
@@ -381,10 +409,12 @@ void b2b_stream_kernel(B2bParams p) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) af[rb][ks] = buf_load_b128(rsA, (row * p.lda + (uint32_t)(ks * 16 + 8 * h)) * 2);
     }
-    // One full wait for the A fragments and the first segments: a wait the
-    // compiler placed for the fragments alone would not know of the segment
-    // loads issued around them.
-    if (!resident) __builtin_amdgcn_s_waitcnt(0);
+    // One full wait, on every path, for the A fragments (and the first
+    // segments): a wait the compiler placed for the fragments would sit in
+    // the segment loop, run every iteration and also drain the ring loads
+    // issued just before it. The empty asm keeps the fragment loads above it.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
     f32x16_t oacc[MB][NB];
     float cst[MB], lsum[MB];   // softmax: integer stabiliser of the row, this lane's part of the unrounded row sum
 #pragma unroll
@@ -400,7 +430,7 @@ void b2b_stream_kernel(B2bParams p) {
       if (!resident) {
         // segment lc complete in every thread, all reads of segment lc - 1 done
         asm volatile("" ::: "memory");
-        wait_vm_lgkm0<(NS - 2) * C::kLoads>();
+        wait_vm_lgkm0<(NS - 2) * C::kLoadsAll>();
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         issue(lc + NS - 1, nseg, rs0, rs1);   // into the buffer of segment lc - 1
@@ -465,26 +495,35 @@ void b2b_stream_kernel(B2bParams p) {
 
 // ---- dispatch
 namespace {
-template <bool kSoftmax, bool kB0LK, bool kCausal = false>
+template <bool kSoftmax, bool kB0LK, bool kCausal = false, int kBias = 0>
 const void* pick_stream_kn(int K, int N, bool two_blocks) {
   if (K == 64 && N == 64)
-    return two_blocks ? (const void*)&b2b_stream_kernel<4, 2, 2, kSoftmax, kB0LK, kCausal>
-                      : (const void*)&b2b_stream_kernel<4, 2, 1, kSoftmax, kB0LK, kCausal>;
-  if (K == 64 && N == 128) return (const void*)&b2b_stream_kernel<4, 4, 1, kSoftmax, kB0LK, kCausal>;
-  if (K == 128 && N == 64) return (const void*)&b2b_stream_kernel<8, 2, 1, kSoftmax, kB0LK, kCausal>;
-  if (K == 128 && N == 128) return (const void*)&b2b_stream_kernel<8, 4, 1, kSoftmax, kB0LK, kCausal>;
+    return (two_blocks && kBias == 0) ? (const void*)&b2b_stream_kernel<4, 2, 2, kSoftmax, kB0LK, kCausal>
+                                  : (const void*)&b2b_stream_kernel<4, 2, 1, kSoftmax, kB0LK, kCausal, kBias>;
+  if (K == 64 && N == 128) return (const void*)&b2b_stream_kernel<4, 4, 1, kSoftmax, kB0LK, kCausal, kBias>;
+  if (K == 128 && N == 64) return (const void*)&b2b_stream_kernel<8, 2, 1, kSoftmax, kB0LK, kCausal, kBias>;
+  if (K == 128 && N == 128) return (const void*)&b2b_stream_kernel<8, 4, 1, kSoftmax, kB0LK, kCausal, kBias>;
   return nullptr;
 }
 }  // namespace
 
 const void* b2b_stream_pick(const B2bParams& p, int cus, int* rows_per_tile) {
   if (p.L % kTLC != 0 || p.L < kTLC) return nullptr;
-  // 256-row tiles only when they still give every CU two workgroups
-  const bool two = p.K == 64 && p.N == 64 && (long)p.batch * ((p.M + 255) / 256) >= 2L * cus;
+  // a bias the ring loads cannot read takes the general kernel
+  if (p.bias && !p.bias_vec) return nullptr;
+  // 256-row tiles only when they still give every CU two workgroups (and
+  // not with a bias, whose registers they have no room for)
+  const bool two = !p.bias && p.K == 64 && p.N == 64 && (long)p.batch * ((p.M + 255) / 256) >= 2L * cus;
   const bool sm = p.row_op == 1;
   const void* k;
   if (p.causal)   // keys stored [L, K] (attention); other layouts take the general kernel
     k = p.b0_lk ? pick_stream_kn<true, true, true>(p.K, p.N, two) : nullptr;
+  else if (p.bias && p.bias_f32)   // elementwise F only (the softmax takes no bias)
+    k = p.b0_lk ? pick_stream_kn<false, true, false, 2>(p.K, p.N, false)
+                : pick_stream_kn<false, false, false, 2>(p.K, p.N, false);
+  else if (p.bias)
+    k = p.b0_lk ? pick_stream_kn<false, true, false, 1>(p.K, p.N, false)
+                : pick_stream_kn<false, false, false, 1>(p.K, p.N, false);
   else
     k = sm ? (p.b0_lk ? pick_stream_kn<true, true>(p.K, p.N, two) : pick_stream_kn<true, false>(p.K, p.N, two))
            : (p.b0_lk ? pick_stream_kn<false, true>(p.K, p.N, two) : pick_stream_kn<false, false>(p.K, p.N, two));

@@ -99,6 +99,11 @@ __device__ inline void lds_dma16(uint32_t lds_addr, u32x4_t rs, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(lds_addr), "v"(voff), "s"(rs) : "memory", "m0");
 }
+// 4 bytes per lane into LDS at m0 + 4 * lane; ordered like lds_dma16.
+__device__ inline void lds_dma4(uint32_t lds_addr, u32x4_t rs, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(lds_addr), "v"(voff), "s"(rs) : "memory", "m0");
+}
 // s_waitcnt with lgkmcnt(0) and vmcnt(n), expcnt left open (gfx9 encoding).
 template <int N>
 __device__ inline void wait_vm_lgkm0() {

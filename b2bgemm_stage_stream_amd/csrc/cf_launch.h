@@ -70,6 +70,7 @@ struct B2bParams {
   int row_op;
   int out_f32;
   int bias_f32;
+  int bias_vec;      // bias 4-byte aligned: streamed with the B0/B1 segments
   int b0_lk;
   int o_vec;     // O base, ldo and batch stride allow 4-element vector stores
   int causal;    // softmax only: key l visible to row m iff l <= m + coff

@@ -121,6 +121,42 @@ def test_exact_shapes_streamed(K, N, lk, row_op, act):
           what=f"streamed K={K} N={N} lk={lk} {row_op}/{act}")
 
 
+@pytest.mark.parametrize("bias_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("lk", [False, True])
+@pytest.mark.parametrize("K,N,L", [(64, 64, 320), (64, 128, 320), (128, 64, 320), (128, 128, 320), (64, 64, 128)])
+def test_bias_streamed(K, N, L, lk, bias_dtype):
+    # a bias on the ReLU chain travels with the B0/B1 segments through the
+    # LDS ring (per-head weights: streamed; L = 128 with shared weights:
+    # resident); bf16 and fp32 bias vectors
+    batch, M = 3, 200
+    w, dev, ref = P.inputs("c4_b2b_mlp_relu", seed=13, batch=batch, M=M, K=K, L=L, N=N)
+    if lk:   # B0 given as [L, K]
+        dev["B0"] = dev["B0"].transpose(1, 2).contiguous()
+        ref["B0"] = np.ascontiguousarray(np.swapaxes(ref["B0"], 1, 2))
+    if L == 128:   # one 2-D B0/B1 for the whole batch
+        dev["B0"], dev["B1"] = dev["B0"][0], dev["B1"][0]
+        ref["B0"], ref["B1"] = ref["B0"][0], ref["B1"][0]
+    rng = np.random.default_rng(1000 + K + N + L)
+    bias = torch.from_numpy(rng.normal(0.0, 0.5, L)).to(bias_dtype).cuda()
+    check(dev, ref, lk=lk, alpha=0.5, act="relu", bias=bias, bias_ref=P.gpu_to_f64(bias),
+          what=f"bias {str(bias_dtype)[6:]} K={K} N={N} L={L} lk={lk}")
+
+
+@pytest.mark.parametrize("bias_dtype", [torch.bfloat16, torch.float32])
+def test_bias_unaligned(bias_dtype):
+    # a bias one element past an aligned base: fp32 (4-byte aligned) still
+    # streams with the ring, bf16 at an odd element takes the general kernel,
+    # which reads it element by element
+    batch, M, K, L, N = 2, 130, 64, 192, 64
+    w, dev, ref = P.inputs("c4_b2b_mlp_relu", seed=14, batch=batch, M=M, K=K, L=L, N=N)
+    rng = np.random.default_rng(77)
+    buf = torch.from_numpy(rng.normal(0.0, 0.5, L + 1)).to(bias_dtype).cuda()
+    bias = buf[1:]
+    assert bias.data_ptr() % 16 != 0
+    check(dev, ref, lk=False, alpha=0.5, act="relu", bias=bias, bias_ref=P.gpu_to_f64(bias),
+          what=f"unaligned bias {str(bias_dtype)[6:]}")
+
+
 @pytest.mark.parametrize("lk,row_op,act", [(True, "softmax", "none"), (False, "none", "relu")])
 def test_two_row_blocks_per_wave(lk, row_op, act):
     # enough 256-row tiles (512 batch entries) for the kernel variant whose

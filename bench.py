@@ -4,7 +4,11 @@ MI355X.
 One step = one fused kernel call over the whole workload (inputs already
 resident in HBM; consecutive steps cycle through copies of the inputs totalling
 at least 512 MiB so that they are read from HBM, not from the last-level
-cache). Prints one JSON line:
+cache). Before the W warmup steps the same calls run untimed for --settle-s
+seconds: the shader clock climbs over the first tens of milliseconds of
+sustained load (a C2 launch takes 0.33 ms in the first batch and 0.24 ms from
+about the 200th on), and the timed steps are meant to see the sustained state.
+Prints one JSON line:
   value      algorithmic GEMM TFLOP/s of the workload (2*M*N*K per GEMM)
   roofline   the same kernel against its bound (bf16 dense MFMA peak, or HBM
              bandwidth when the workload's flop/byte is below the ridge point),
@@ -39,6 +43,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-s", type=float, default=0.6,
+                    help="untimed seconds of the same calls before the warmup steps, so that the GPU clock has "
+                         "left its idle state (0: none)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -279,6 +286,18 @@ def main():
         call, out, ws, ws_bytes = make_call(w, d_, torch, cf, args.store_x, args.causal, args.argmax)
         calls.append(call)
 
+    # settle: batches of calls (grown to ~20 ms each) until --settle-s has passed
+    settle_steps, batch = 0, 4
+    t_s = time.perf_counter()
+    while time.perf_counter() - t_s < args.settle_s:
+        t_b = time.perf_counter()
+        for _ in range(batch):
+            calls[settle_steps % nset]()
+            settle_steps += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t_b < 0.02 and batch < 4096:
+            batch *= 2
+    settle_s = time.perf_counter() - t_s
     for i in range(max(args.warmup, nset)):
         calls[i % nset]()
     torch.cuda.synchronize()
@@ -317,6 +336,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"seconds": round(settle_s, 3), "steps": settle_steps},
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

@@ -207,9 +207,10 @@ cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K, const void* A, int64
     if (!ws || !aligned(ws, 256) || ws_bytes < plan.ws_bytes) return CF_ERR_WORKSPACE;
   }
 
-  // fast path: 16-byte accesses everywhere, whole column tiles, bf16 (or no) residual
+  // fast path: 16-byte accesses everywhere, bf16 (or no) residual; a ragged
+  // last column tile (N a multiple of 8) takes the masked epilogue
   const int64_t ce = ab_dtype == CF_F32 ? 4 : 8;
-  bool vec = (N % kTile == 0) && (K % ce == 0) && (lda % ce == 0) && (ldb % ce == 0) &&
+  bool vec = (N % 8 == 0) && (K % ce == 0) && (lda % ce == 0) && (ldb % ce == 0) &&
              (!C || (ldc % 8 == 0 && aligned(C, 16))) && aligned(A, 16) && aligned(B, 16);
   if (epi && epi->residual)
     vec = vec && epi->residual_dtype == CF_BF16 && epi->ld_residual % 8 == 0 && aligned(epi->residual, 16);

@@ -422,11 +422,15 @@ __device__ inline float2 halves(float v) {
 }
 
 // ROW: 0 none, 1 softmax, 2 LayerNorm, 3 RMSNorm, 4 argmax (cf_row_op).
-// kFast: N is a multiple of 256, 16-byte accesses are allowed and the residual
-// (if any) is bf16; otherwise every column is masked against N.
+// kFast: 16-byte accesses are allowed, N is a multiple of 8 and the residual
+// (if any) is bf16; otherwise every column is masked against N, element by
+// element.
+// kRagged (with kFast): the column tile extends past N; the row statistics
+// skip the columns >= N and the 16-byte stores of those columns are dropped
+// (N a multiple of 8: a 4- or 8-column group is valid or invalid as a whole).
 // kPre: a bias or a residual is present.
 // kId: alpha == 1 and no activation, so the elementwise stage is P (+ bias + R).
-template <int ROW, bool kFast, bool kPre, bool kId>
+template <int ROW, bool kFast, bool kPre, bool kId, bool kRagged = false>
 __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueParams& p, uint8_t* smem,
                                 int strip, int tn, uint32_t tag, bool& timed_out, int tid) {
   const int lane = tid & 63, wave = tid >> 6;
@@ -524,7 +528,7 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) { f(nb, Q0{}); f(nb, Q1{}); f(nb, Q2{}); f(nb, Q3{}); }
   };
-  auto valid = [&](int nb, int q, int e) { return kFast || (nb * 32 + 8 * q + e < ncol); };
+  auto valid = [&](int nb, int q, int e) { return (kFast && !kRagged) || (nb * 32 + 8 * q + e < ncol); };
 
   float tok = 0.0f;
   if constexpr (ROW != 0) {
@@ -571,11 +575,11 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
             const float d = ok ? x[e] - K : 0.0f;
             s1 += d;
             s2 = __builtin_fmaf(d, d, s2);
-            if constexpr (!kFast) cnt += ok ? 1.0f : 0.0f;
+            if constexpr (!kFast || kRagged) cnt += ok ? 1.0f : 0.0f;
           }
           tok = s2;
         });
-        if constexpr (kFast) cnt = 64.0f;
+        if constexpr (kFast && !kRagged) cnt = 64.0f;
         float mean = cnt > 0.0f ? K + s1 / cnt : 0.0f;
         float m2 = cnt > 0.0f ? fmaxf(s2 - s1 * (s1 / cnt), 0.0f) : 0.0f;
         const float2 hn = halves(cnt), hm = halves(mean), hq = halves(m2);
@@ -777,10 +781,12 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
       for (int mb = 0; mb < 4; ++mb) {
         float x[4], y[4];
         xgroup(mb, nb, qc, bv, tok, x);
+        // ragged tile: the group's 4 columns are valid or invalid together
+        const uint32_t gok = (!kRagged || c < ncol) ? 0u : kOutOfRange;
         if constexpr (kX == 2) {
           if constexpr (kFast) {
             const u32x4_t v = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
-            buf_store_b128(v, rsX, xrowoff[mb] + (uint32_t)c * 4);
+            buf_store_b128(v, rsX, (xrowoff[mb] + (uint32_t)c * 4) | gok);
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -789,7 +795,7 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
         } else if constexpr (kX == 1) {
           if constexpr (kFast) {
             const u32x2_t v = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-            buf_store_b64(v, rsX, xrowoff[mb] + (uint32_t)c * 2);
+            buf_store_b64(v, rsX, (xrowoff[mb] + (uint32_t)c * 2) | gok);
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -816,7 +822,7 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
         if constexpr (kOutF32) {
           if constexpr (kFast) {
             const u32x4_t v = {__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3])};
-            buf_store_b128(v, rsC, rowoff[mb] + (uint32_t)c * 4);
+            buf_store_b128(v, rsC, (rowoff[mb] + (uint32_t)c * 4) | gok);
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -864,15 +870,17 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
       for (int i = 0; i < 32; ++i) {
         const int row = (tid >> 5) + 8 * i;
         const u32x4_t v = *(const u32x4_t*)(smem + kOffRes + row * kResStride + c * 16);
-        buf_store_b128(v, rsC, ((uint32_t)(m0 + row) * p.ldc + (uint32_t)(n0 + c * 8)) * 2u);
+        const uint32_t cok = (!kRagged || n0 + c * 8 < p.N) ? 0u : kOutOfRange;
+        buf_store_b128(v, rsC, (((uint32_t)(m0 + row) * p.ldc + (uint32_t)(n0 + c * 8)) * 2u) | cok);
       }
     }
   }
 }
 
-// kVec (fast path): vector loads, N a multiple of 256, bf16 or no residual; the
-// epilogue is then specialised on kRow (cf_row_op) and kPre (bias/residual
-// present). The general path (kVec false) dispatches on p.row_op at run time.
+// kVec (fast path): vector loads, N a multiple of 8, bf16 or no residual; the
+// epilogue of whole column tiles is then specialised on kRow (cf_row_op) and
+// kPre (bias/residual present). The general path (kVec false) dispatches on
+// p.row_op at run time.
 template <bool kF32, bool kBnk, bool kVec, int kRow, bool kPre>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void gemm_epilogue_kernel(GemmEpilogueParams p) {
@@ -1004,7 +1012,12 @@ void gemm_epilogue_kernel(GemmEpilogueParams p) {
 
     // ------------------------------------------------------------------ epilogue
     if constexpr (kVec) {
-      if (p.alpha == 1.0f && p.act == 0) epilogue<kRow, true, kPre, true>(acc, p, smem, strip, tn, tag, timed_out, tid_t);
+      // the last column tile of a strip may be ragged (N a multiple of 8, not
+      // of 256): its epilogue masks columns against N; the main loop's
+      // accumulators of columns >= N hold whatever the B loads read there,
+      // and the masked epilogue only ever selects them away
+      if (n0 + kGemmBN > p.N) epilogue<kRow, true, kPre, false, true>(acc, p, smem, strip, tn, tag, timed_out, tid_t);
+      else if (p.alpha == 1.0f && p.act == 0) epilogue<kRow, true, kPre, true>(acc, p, smem, strip, tn, tag, timed_out, tid_t);
       else epilogue<kRow, true, kPre, false>(acc, p, smem, strip, tn, tag, timed_out, tid_t);
     } else {
       switch (p.row_op) {

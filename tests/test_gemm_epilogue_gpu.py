@@ -124,6 +124,53 @@ def test_ragged_general_path(row_op, shape):
     P.assert_bf16_consistent(c16, c32, R, f"ragged {shape} {row_op} bf16")
 
 
+@pytest.mark.parametrize("row_op", ["none", "softmax", "layernorm", "rmsnorm"])
+@pytest.mark.parametrize("N,K", [(264, 256), (1000, 200), (4000, 64)])
+def test_ragged_column_tile_fast_path(row_op, N, K):
+    # N a multiple of 8, not of 256: whole column tiles take the fast epilogue
+    # and each strip's last tile its masked variant (8, 232 and 160 valid
+    # columns); K = 256 and 64 stream through the LDS ring, K = 200 takes the
+    # register-staged loop; M = 300 leaves a ragged row strip as well
+    import dataclasses
+    M = 300
+    w, dev, ref = P.inputs("c3_gemm_residual_rmsnorm", seed=21, M=M, N=N, K=K)
+    bias = torch.linspace(-0.3, 0.3, N, device="cuda").to(torch.bfloat16)
+    w2 = dataclasses.replace(w, params={**w.params, "alpha": 0.5, "act": "relu", "row_op": row_op, "eps": 1e-5})
+    dev2, ref2 = {**dev, "bias": bias}, {**ref, "bias": P.gpu_to_f64(bias)}
+    if row_op == "layernorm":
+        beta = torch.linspace(-0.1, 0.1, N, device="cuda").to(torch.bfloat16)
+        dev2["beta"], ref2["beta"] = beta, P.gpu_to_f64(beta)
+    check_two_outputs(w2, dev2, ref2, epi_of(w2, dev2), f"ragged column tile {M}x{N}x{K} {row_op}")
+
+
+@pytest.mark.parametrize("row_op", ["layernorm", "softmax"])
+def test_ragged_column_tile_b_nk(row_op):
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=22, M=256, N=1000, K=256)
+    Bt = dev["B"].t().contiguous()          # [N, K]: rows past N read as zero
+    R = oracle.gemm_epilogue(ref["A"], ref["B"], row_op=row_op, gamma=ref["gamma"], beta=ref["beta"], eps=1e-5)
+    C = run(dev["A"], Bt, torch.float32, b_is_nk=True, row_op=row_op, gamma=dev["gamma"], beta=dev["beta"],
+            eps=1e-5)
+    P.assert_close(P.gpu_to_f64(C), R, P.REL_F_BF16, P.MAX_ABS_BF16, f"ragged column tile, B [N,K], {row_op}")
+
+
+@pytest.mark.parametrize("row_op", ["none", "softmax", "layernorm", "rmsnorm"])
+def test_ragged_column_tile_nan_past_n(row_op):
+    # B is a [K, N] view of a wider buffer whose extra columns hold NaN, so the
+    # ragged tile's accumulators past N are NaN: none of it may reach an output
+    # or a row statistic
+    M, N, K = 300, 1000, 256
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=24, M=M, N=N, K=K)
+    buf = torch.full((K, N + 24), float("nan"), dtype=torch.bfloat16, device="cuda")
+    buf[:, :N] = dev["B"]
+    B = buf[:, :N]
+    beta_d, beta_r = (dev["beta"], ref["beta"]) if row_op == "layernorm" else (None, None)
+    R = oracle.gemm_epilogue(ref["A"], ref["B"], row_op=row_op, gamma=ref["gamma"], beta=beta_r, eps=1e-5)
+    c32 = run(dev["A"], B, torch.float32, row_op=row_op, gamma=dev["gamma"], beta=beta_d, eps=1e-5)
+    P.assert_close(P.gpu_to_f64(c32), R, P.REL_F_BF16, P.MAX_ABS_BF16, f"NaN past N, {row_op}")
+    c16 = run(dev["A"], B, torch.bfloat16, row_op=row_op, gamma=dev["gamma"], beta=beta_d, eps=1e-5)
+    P.assert_bf16_consistent(c16, c32, R, f"NaN past N, {row_op} bf16")
+
+
 @pytest.mark.parametrize("row_op", ["layernorm", "softmax"])
 def test_b_nk_layout(row_op):
     w, dev, ref = P.inputs("c2_gemm_layernorm", seed=4, M=256, N=512, K=256)
@@ -401,6 +448,14 @@ def test_argmax_fast_path(N):
     X = oracle.elementwise_stage(oracle.matmul(ref["A"], ref["B"]))
     idx, val, _ = run_argmax(dev["A"], dev["B"], False)
     check_argmax(idx, val, X, f"argmax N={N}")
+
+
+@pytest.mark.parametrize("N", [264, 1000])
+def test_argmax_ragged_column_tile(N):
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=23, M=300, N=N, K=256)
+    X = oracle.elementwise_stage(oracle.matmul(ref["A"], ref["B"]))
+    idx, val, _ = run_argmax(dev["A"], dev["B"], False)
+    check_argmax(idx, val, X, f"argmax ragged column tile N={N}")
 
 
 @pytest.mark.parametrize("shape", [(33, 65, 17), (300, 520, 200), (1, 1000, 9)])

@@ -44,7 +44,7 @@ import numpy as np
 
 __all__ = [
     "widen_bf16", "round_bf16", "matmul", "elementwise_stage", "relu",
-    "row_softmax", "layer_norm", "rms_norm", "gemm_epilogue",
+    "row_softmax", "layer_norm", "rms_norm", "gemm_epilogue", "gemm_epilogue_two_stage",
     "softmax_bf16_operand", "b2bgemm",
 ]
 
@@ -229,6 +229,23 @@ def gemm_epilogue_with_x(A: np.ndarray, B: np.ndarray, *, alpha: float = 1.0,
     float64 and unrounded."""
     X = elementwise_stage(matmul(A, B), alpha, bias, residual, act)
     return row_stage(X, row_op, gamma, beta, eps), X
+
+
+def gemm_epilogue_two_stage(A: np.ndarray, B: np.ndarray, *, alpha: float = 1.0,
+                            bias: Optional[np.ndarray] = None, residual: Optional[np.ndarray] = None,
+                            act: str = "none", row_op: str = "none", gamma: Optional[np.ndarray] = None,
+                            beta: Optional[np.ndarray] = None, eps: float = 0.0, row_op2: str = "none",
+                            gamma2: Optional[np.ndarray] = None, beta2: Optional[np.ndarray] = None,
+                            eps2: float = 0.0) -> np.ndarray:
+    """An epilogue with two reduction boundaries in sequence. The review
+    describes the epilogue as chained DAGs cut at each reduction (ComFuse
+    review, "What carries the argument"), and names chains of more than one
+    reduction stage as the general case; here the first row operation (with
+    gamma, beta, eps) gives Y from the elementwise stage's X, and the second
+    (with gamma2, beta2, eps2) acts on Y over the same row."""
+    X = elementwise_stage(matmul(A, B), alpha, bias, residual, act)
+    Y = row_stage(X, row_op, gamma, beta, eps)
+    return row_stage(Y, row_op2, gamma2, beta2, eps2)
 
 
 # --------------------------------------------------------------------------- back-to-back GEMM

@@ -251,6 +251,64 @@ def pin_two_outputs(o):
                     _close_dec(gv, wv, rtol=1e-12, atol=1e-13)
 
 
+def pin_two_stage(o):
+    """Two row operations in sequence against brute force (stage 1 and stage 2
+    in 40-digit decimals, stage 2 on stage 1's decimal output) for all nine
+    (softmax, LayerNorm, RMSNorm) pairs, each with its own affine vectors and
+    eps; then closed forms of the compositions on random rows."""
+    rng = np.random.default_rng(29)
+    m, k, n = 3, 4, 5
+    A = _bf16_values(rng, (m, k))
+    B = _bf16_values(rng, (k, n))
+    bias = _bf16_values(rng, (n,))
+    g1, b1 = 1 + 0.1 * _bf16_values(rng, (n,)), 0.1 * _bf16_values(rng, (n,))
+    g2, b2 = 1 + 0.2 * _bf16_values(rng, (n,)), 0.2 * _bf16_values(rng, (n,))
+    E = X.mm(X.mat(A), X.mat(B))
+    Xf = [[Fraction(0.5) * E[i][j] + X.F(bias[j]) for j in range(n)] for i in range(m)]
+
+    def stage(xs_frac, op, g, b, eps):
+        if op == "softmax":
+            return X.softmax_row(xs_frac)
+        if op == "layernorm":
+            return X.layernorm_row(xs_frac, eps, g, b)
+        return X.rmsnorm_row(xs_frac, eps, g)
+
+    ops = ("softmax", "layernorm", "rmsnorm")
+    for op1 in ops:
+        for op2 in ops:
+            Z = o.gemm_epilogue_two_stage(A, B, alpha=0.5, bias=bias, row_op=op1, gamma=g1, beta=b1, eps=1e-3,
+                                          row_op2=op2, gamma2=g2, beta2=b2, eps2=1e-2)
+            for i in range(m):
+                y = [X.dec_to_frac(v) for v in stage(Xf[i], op1, g1, b1, 1e-3)]
+                want = stage(y, op2, g2, b2, 1e-2)
+                for gv, wv in zip(Z[i], want):
+                    _close_dec(gv, wv, rtol=1e-11, atol=1e-12)
+    # closed forms (unit affine): LayerNorm of a LayerNorm output, whose mean is
+    # 0 and variance s2/(s2 + e1), is y / sqrt(s2/(s2 + e1) + e2); RMSNorm of an
+    # RMSNorm output, whose mean square is ms/(ms + e1), is y / sqrt(ms/(ms + e1) + e2);
+    # the softmax of a two-column softmax is the logistic function of 2 p - 1,
+    # p = logistic(x0 - x1)
+    Xr = rng.normal(0.3, 2.0, (6, 7))
+    e1, e2 = 0.5, 0.25
+    Z = o.row_stage(o.row_stage(Xr, "layernorm", eps=e1), "layernorm", eps=e2)
+    mu, s2 = Xr.mean(axis=1, keepdims=True), Xr.var(axis=1, keepdims=True)
+    y = (Xr - mu) / np.sqrt(s2 + e1)
+    assert np.allclose(Z, y / np.sqrt(s2 / (s2 + e1) + e2), rtol=1e-12, atol=1e-13)
+    Z = o.row_stage(o.row_stage(Xr, "rmsnorm", eps=e1), "rmsnorm", eps=e2)
+    ms = (Xr ** 2).mean(axis=1, keepdims=True)
+    y = Xr / np.sqrt(ms + e1)
+    assert np.allclose(Z, y / np.sqrt(ms / (ms + e1) + e2), rtol=1e-12, atol=1e-13)
+    d = rng.normal(0.0, 3.0, 9)
+    Z = o.row_stage(o.row_stage(np.stack([d, np.zeros_like(d)], axis=1), "softmax"), "softmax")
+    p = 1.0 / (1.0 + np.exp(-d))
+    assert np.allclose(Z[:, 0], 1.0 / (1.0 + np.exp(-(2.0 * p - 1.0))), rtol=1e-12, atol=1e-14)
+    # the second stage of "none" is the identity: the single-stage epilogue
+    Z = o.gemm_epilogue_two_stage(A, B, alpha=0.5, bias=bias, row_op="layernorm", gamma=g1, beta=b1, eps=1e-3)
+    for i in range(m):
+        for gv, wv in zip(Z[i], X.layernorm_row(Xf[i], 1e-3, g1, b1)):
+            _close_dec(gv, wv, rtol=1e-12, atol=1e-13)
+
+
 # --------------------------------------------------------------------------- back-to-back GEMM
 
 def pin_b2b_relu(o):
@@ -474,7 +532,8 @@ def pin_row_argmax(o):
 
 ALL_PINS = [pin_round_bf16, pin_widen_bf16, pin_matmul_exact, pin_stage1_exact, pin_softmax,
             pin_layernorm, pin_rmsnorm, pin_gemm_epilogue_composition, pin_two_outputs, pin_b2b_relu,
-            pin_b2b_softmax, pin_b2b_causal, pin_row_statistics, pin_b2b_logsumexp, pin_row_argmax]
+            pin_b2b_softmax, pin_b2b_causal, pin_row_statistics, pin_b2b_logsumexp, pin_row_argmax,
+            pin_two_stage]
 
 
 def run_all(o):

@@ -77,6 +77,18 @@ MUTATIONS = {
         "    idx = np.argmax(X, axis=-1)\n",
         "    idx = X.shape[-1] - 1 - np.argmax(X[..., ::-1], axis=-1)\n")],
     "argmax_is_argmin": [("    idx = np.argmax(X, axis=-1)\n", "    idx = np.argmin(X, axis=-1)\n")],
+    "two_stage_second_on_x": [(
+        "    return row_stage(Y, row_op2, gamma2, beta2, eps2)\n",
+        "    return row_stage(X, row_op2, gamma2, beta2, eps2)\n")],
+    "two_stage_order_swapped": [(
+        "    Y = row_stage(X, row_op, gamma, beta, eps)\n    return row_stage(Y, row_op2, gamma2, beta2, eps2)\n",
+        "    Y = row_stage(X, row_op2, gamma2, beta2, eps2)\n    return row_stage(Y, row_op, gamma, beta, eps)\n")],
+    "two_stage_second_affine_from_first": [(
+        "    return row_stage(Y, row_op2, gamma2, beta2, eps2)\n",
+        "    return row_stage(Y, row_op2, gamma, beta, eps2)\n")],
+    "two_stage_second_eps_from_first": [(
+        "    return row_stage(Y, row_op2, gamma2, beta2, eps2)\n",
+        "    return row_stage(Y, row_op2, gamma2, beta2, eps)\n")],
     "b2b_relu_dropped": [(
         "S = elementwise_stage(matmul(A, B0), alpha, bias, None, act)",
         "S = elementwise_stage(matmul(A, B0), alpha, bias, None, 'none')")],

@@ -50,6 +50,10 @@ class cf_epilogue(ctypes.Structure):
         ("mask", ctypes.c_int),
         ("row_stats", ctypes.c_void_p),
         ("row_index", ctypes.c_void_p),
+        ("row_op2", ctypes.c_int),
+        ("gamma2", ctypes.c_void_p),
+        ("beta2", ctypes.c_void_p),
+        ("eps2", ctypes.c_float),
     ]
 
 
@@ -130,14 +134,17 @@ def _ptr(t) -> Optional[int]:
 
 def make_epilogue(*, alpha: float = 1.0, bias=None, residual=None, act: str = "none",
                   row_op: str = "none", gamma=None, beta=None, eps: float = 0.0, x_out=None,
-                  mask: str = "none", row_stats=None, row_index=None) -> cf_epilogue:
+                  mask: str = "none", row_stats=None, row_index=None, row_op2: str = "none", gamma2=None,
+                  beta2=None, eps2: float = 0.0) -> cf_epilogue:
     """cf_epilogue descriptor from tensors (bias/gamma/beta share one dtype).
     ``x_out``: optional [M, N] tensor that receives x before the row operation.
     ``mask``: "causal" for the softmax of cf_b2bgemm.
     ``row_stats``: optional contiguous fp32 tensor for the row operation's per-row
     statistics (log-sum-exp; LayerNorm mean and 1/sigma; RMSNorm 1/rms; the
     row maximum for argmax). ``row_index``: contiguous int32 [M] tensor that
-    receives each row's argmax column (row_op "argmax")."""
+    receives each row's argmax column (row_op "argmax"). ``row_op2`` (with
+    ``gamma2``, ``beta2``, ``eps2``): a second row stage applied to the first
+    one's output (cf_gemm_epilogue only)."""
     e = cf_epilogue()
     _lib.cf_epilogue_init(ctypes.byref(e))
     e.alpha = float(alpha)
@@ -145,6 +152,8 @@ def make_epilogue(*, alpha: float = 1.0, bias=None, residual=None, act: str = "n
     e.row_op = ROW_OP[row_op]
     e.eps = float(eps)
     e.mask = MASK[mask]
+    e.row_op2 = ROW_OP[row_op2]
+    e.eps2 = float(eps2)
     if row_stats is not None:
         import torch
         if row_stats.dtype != torch.float32 or not row_stats.is_contiguous():
@@ -155,16 +164,17 @@ def make_epilogue(*, alpha: float = 1.0, bias=None, residual=None, act: str = "n
         if row_index.dtype != torch.int32 or not row_index.is_contiguous():
             raise TypeError("row_index must be a contiguous int32 tensor")
         e.row_index = row_index.data_ptr()
-    vecs = [v for v in (bias, gamma, beta) if v is not None]
+    vecs = [v for v in (bias, gamma, beta, gamma2, beta2) if v is not None]
     if vecs:
         codes = {_dtype_code(v) for v in vecs}
         if len(codes) != 1:
-            raise TypeError("bias, gamma and beta must share one dtype")
+            raise TypeError("bias, gamma, beta, gamma2 and beta2 must share one dtype")
         e.vec_dtype = codes.pop()
         for v in vecs:
             if not v.is_contiguous():
                 raise ValueError("bias/gamma/beta must be contiguous")
     e.bias, e.gamma, e.beta = _ptr(bias), _ptr(gamma), _ptr(beta)
+    e.gamma2, e.beta2 = _ptr(gamma2), _ptr(beta2)
     if residual is not None:
         e.residual = residual.data_ptr()
         e.ld_residual = _ld(residual)

@@ -68,6 +68,7 @@ constexpr int64_t kTile = 256;
 struct GemmPlan {
   int64_t tiles_n = 0, strips = 0, tiles = 0;
   bool exchange = false;
+  size_t slot_bytes = 0;   // one stage's exchange slots
   size_t ws_bytes = 0;
 };
 
@@ -78,8 +79,10 @@ GemmPlan plan_gemm(int64_t M, int64_t N, const cf_epilogue* epi) {
   g.tiles = g.tiles_n * g.strips;
   g.exchange = epi && epi->row_op != CF_ROW_NONE && g.tiles_n > 1;
   if (g.exchange) {
+    // one slot set per reduction stage
     const size_t slots = (size_t)g.strips * (size_t)g.tiles_n * (size_t)kTile * 2 * sizeof(uint64_t);
-    g.ws_bytes = cf::kWsHeaderBytes + ((slots + 255) / 256) * 256;
+    g.slot_bytes = ((slots + 255) / 256) * 256;
+    g.ws_bytes = cf::kWsHeaderBytes + g.slot_bytes * (epi->row_op2 != CF_ROW_NONE ? 2 : 1);
   }
   return g;
 }
@@ -118,6 +121,19 @@ cf_status check_epilogue(const cf_epilogue* epi, int64_t N, bool allow_row_ops_n
   if (!allow_row_ops_norm) {
     if (epi->row_op == CF_ROW_LAYERNORM || epi->row_op == CF_ROW_RMSNORM) return CF_ERR_UNSUPPORTED;
     if (epi->gamma || epi->beta) return CF_ERR_UNSUPPORTED;
+  }
+  // second row stage: softmax / LayerNorm / RMSNorm after one of those three
+  if (epi->row_op2 < CF_ROW_NONE || epi->row_op2 > CF_ROW_ARGMAX) return CF_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(epi->eps2) || epi->eps2 < 0.0f) return CF_ERR_INVALID_ARGUMENT;
+  if (epi->row_op2 == CF_ROW_NONE) {
+    if (epi->gamma2 || epi->beta2 || epi->eps2 != 0.0f) return CF_ERR_INVALID_ARGUMENT;
+  } else {
+    if (!allow_residual) return CF_ERR_UNSUPPORTED;
+    const bool norm1 = epi->row_op == CF_ROW_SOFTMAX || epi->row_op == CF_ROW_LAYERNORM || epi->row_op == CF_ROW_RMSNORM;
+    if (!norm1 || epi->row_op2 == CF_ROW_ARGMAX) return CF_ERR_INVALID_ARGUMENT;
+    if (epi->beta2 && epi->row_op2 != CF_ROW_LAYERNORM) return CF_ERR_INVALID_ARGUMENT;
+    if ((epi->gamma2 && !aligned(epi->gamma2, vs)) || (epi->beta2 && !aligned(epi->beta2, vs)))
+      return CF_ERR_INVALID_ARGUMENT;
   }
   return CF_OK;
 }
@@ -215,6 +231,8 @@ cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K, const void* A, int64
   if (epi && epi->residual)
     vec = vec && epi->residual_dtype == CF_BF16 && epi->ld_residual % 8 == 0 && aligned(epi->residual, 16);
   if (X) vec = vec && epi->ld_x_out % 8 == 0 && aligned(X, 16);
+  // two row stages: fast-path layouts only
+  if (epi && epi->row_op2 != CF_ROW_NONE && !vec) return CF_ERR_UNSUPPORTED;
 
   // ---- device
   int dev;
@@ -256,9 +274,14 @@ cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K, const void* A, int64
   p.c_f32 = c_dtype == CF_F32;
   p.vec_f32 = epi ? epi->vec_dtype == CF_F32 : 0;
   p.res_f32 = rdt == CF_F32;
+  p.row_op2 = epi ? (int)epi->row_op2 : 0;
+  p.gamma2 = epi ? epi->gamma2 : nullptr;
+  p.beta2 = epi ? epi->beta2 : nullptr;
+  p.eps2 = epi ? epi->eps2 : 0.0f;
   if (plan.exchange) {
     p.ws_hdr = (uint32_t*)ws;
     p.ws_slots = (uint64_t*)((char*)ws + cf::kWsHeaderBytes);
+    if (p.row_op2 != 0) p.ws_slots2 = (uint64_t*)((char*)ws + cf::kWsHeaderBytes + plan.slot_bytes);
   }
   p.spin_ticks = g_timeout_us.load() * (uint64_t)info.wallclock_khz / 1000u;
 

@@ -40,14 +40,20 @@ struct GemmEpilogueParams {
   int x_f32;         // dtype of X: 1 fp32, 0 bf16
   float* row_stats;  // optional per-row statistics of the row operation
   int32_t* row_index;   // row argmax: column of each row's maximum
+  int row_op2;       // second row stage on the first one's output (0: none)
+  const void* gamma2;
+  const void* beta2;
+  float eps2;
   uint32_t* ws_hdr;  // workspace header (NULL when tiles_n == 1 or no row op)
   uint64_t* ws_slots;
+  uint64_t* ws_slots2;   // the second stage's exchange slots
   uint64_t spin_ticks;   // wall-clock ticks a strip wait may take
 };
 
 // Launches the persistent kernel. in_f32: fp32 inputs (else bf16); b_nk: B
 // stored [N, K]; vec (fast path): 16-byte accesses allowed, N a multiple of
-// 256 and the residual (if any) bf16.
+// 8 and the residual (if any) bf16. p.row_op2 != 0 selects the two-stage
+// instantiations.
 hipError_t launch_gemm_epilogue(const GemmEpilogueParams& p, bool in_f32, bool b_nk, bool vec,
                                 int grid, hipStream_t stream);
 

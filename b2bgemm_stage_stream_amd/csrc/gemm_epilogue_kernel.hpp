@@ -393,6 +393,10 @@ constexpr int kOffRstat = kOffWpart + 4096;      // [256] float2: final row stat
 constexpr int kOffRes = kOffRstat + 2048;        // staged residual tile
 constexpr int kResStride = 528;                  // bytes per staged residual row (256 bf16 + 16 B pad)
 constexpr int kLdsEpilogue = kOffRes + 256 * kResStride;
+// second row stage (two-stage instantiations only): gamma2, beta2 [2][256]
+// f32, then its row statistics [256] float2
+constexpr int kOffTwo = kLdsEpilogue;
+constexpr int kLdsTwo = kOffTwo + 2 * 1024 + 2048;
 
 // Four accumulators of block `blk`, registers 4q..4q+3, read into VGPRs after
 // `tok` is available.
@@ -430,8 +434,11 @@ __device__ inline float2 halves(float v) {
 // (N a multiple of 8: a 4- or 8-column group is valid or invalid as a whole).
 // kPre: a bias or a residual is present.
 // kId: alpha == 1 and no activation, so the elementwise stage is P (+ bias + R).
-template <int ROW, bool kFast, bool kPre, bool kId, bool kRagged = false>
-__device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueParams& p, uint8_t* smem,
+// kTwo (ROW 1-3): a second row stage p.row_op2 (run-time: softmax, LayerNorm,
+// RMSNorm) acts on the first stage's output y over the same row, with its own
+// statistics pass over y and its own strip exchange (slots p.ws_slots2).
+template <int ROW, bool kFast, bool kPre, bool kId, bool kRagged = false, bool kTwo = false>
+__device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueParams& p, uint8_t* smem,
                                 int strip, int tn, uint32_t tag, bool& timed_out, int tid) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -749,6 +756,210 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
     __syncthreads();
   }
 
+  // ---- second row stage (kTwo): statistics of y = stage1(x) per row, a
+  // second strip exchange, then z = stage2(y) in the store pass below
+  float* vg2 = (float*)(smem + kOffTwo);
+  float* vb2 = vg2 + 256;
+  float2* rstat2 = (float2*)(smem + kOffTwo + 2048);
+  const float* vg2_lane = vg2 + wn * 128 + 4 * h;
+  const float* vb2_lane = vb2 + wn * 128 + 4 * h;
+  // stage 1 of one element: softmax st = (max * log2 e, 1 / sum); LayerNorm
+  // (mean, 1 / sqrt(var + eps)); RMSNorm (1 / sqrt(ms + eps), -)
+  auto stage1 = [&](float x, float2 st1, float g, float be) -> float {
+    if constexpr (ROW == 2) return __builtin_fmaf((x - st1.x) * st1.y, g, be);
+    else if constexpr (ROW == 3) return x * st1.x * g;
+    else if constexpr (ROW == 1) return fast_exp2(__builtin_fmaf(x, kLog2e, -st1.x)) * st1.y;
+    else return x;
+  };
+  if constexpr (kTwo && ROW >= 1 && ROW <= 3) {
+    {
+      const int n = n0 + tid;
+      const bool ok = n < p.N;
+      vg2[tid] = (p.gamma2 && ok) ? load_vec(p.gamma2, n, p.vec_f32) : 1.0f;
+      vb2[tid] = (p.beta2 && ok) ? load_vec(p.beta2, n, p.vec_f32) : 0.0f;
+    }
+    float2 s1[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) s1[mb] = rstat[wm * 128 + mb * 32 + r32];
+    auto ygroup = [&](int mb, int nb, auto qc, float (&y)[4]) {
+      constexpr int q = decltype(qc)::value;
+      const int c = nb * 32 + 8 * q;
+      float x[4];
+      xgroup(mb, nb, qc, bias4(nb, q), tok, x);
+      f32x4_t g = {1.f, 1.f, 1.f, 1.f}, be = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (ROW == 2 || ROW == 3) g = *(const f32x4_t*)(vg_lane + c);
+      if constexpr (ROW == 2) be = *(const f32x4_t*)(ve_lane + c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = stage1(x[e], s1[mb], g[e], be[e]);
+    };
+    auto stage2 = [&](auto r2c) {
+      constexpr int R2 = decltype(r2c)::value;
+      // levels 1 and 2 over y, as for the first stage over x
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        float a = 0.0f, b = 0.0f;
+        if constexpr (R2 == 1) {
+          float mx = -INFINITY;
+          for_groups([&](int nb, auto qc) {
+            float y[4];
+            ygroup(mb, nb, qc, y);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mx = valid(nb, decltype(qc)::value, e) ? fmaxf(mx, y[e]) : mx;
+            tok = mx;
+          });
+          mx = max_halves(mx);
+          const float mxs = (mx == -INFINITY) ? 0.0f : mx * kLog2e;
+          float sm = 0.0f;
+          for_groups([&](int nb, auto qc) {
+            float y[4];
+            ygroup(mb, nb, qc, y);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float ex = fast_exp2(__builtin_fmaf(y[e], kLog2e, -mxs));
+              sm += valid(nb, decltype(qc)::value, e) ? ex : 0.0f;
+            }
+            tok = sm;
+          });
+          a = mx;
+          b = sum_halves(sm);
+        } else if constexpr (R2 == 2) {
+          float K = 0.0f, s1s = 0.0f, s2s = 0.0f, cnt = 0.0f;
+          bool first = true;
+          for_groups([&](int nb, auto qc) {
+            float y[4];
+            ygroup(mb, nb, qc, y);
+            if (first) { K = valid(nb, 0, 0) ? y[0] : 0.0f; first = false; }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const bool ok = valid(nb, decltype(qc)::value, e);
+              const float d = ok ? y[e] - K : 0.0f;
+              s1s += d;
+              s2s = __builtin_fmaf(d, d, s2s);
+              cnt += ok ? 1.0f : 0.0f;
+            }
+            tok = s2s;
+          });
+          const float mean = cnt > 0.0f ? K + s1s / cnt : 0.0f;
+          const float m2 = cnt > 0.0f ? fmaxf(s2s - s1s * (s1s / cnt), 0.0f) : 0.0f;
+          const float2 hn = halves(cnt), hm = halves(mean), hq = halves(m2);
+          float nn = hn.x, mm = hm.x, q2 = hq.x;
+          chan_merge(nn, mm, q2, hn.y, hm.y, hq.y);
+          a = mm;
+          b = q2;
+        } else {
+          float sq = 0.0f;
+          for_groups([&](int nb, auto qc) {
+            float y[4];
+            ygroup(mb, nb, qc, y);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float yy = valid(nb, decltype(qc)::value, e) ? y[e] : 0.0f;
+              sq = __builtin_fmaf(yy, yy, sq);
+            }
+            tok = sq;
+          });
+          a = sum_halves(sq);
+        }
+        if (h == 0) wpart[wn * 256 + wm * 128 + mb * 32 + r32] = make_float2(a, b);
+      }
+      __syncthreads();
+      // level 3 over the strip (slots p.ws_slots2), merged in tile order
+      {
+        const int ml = tid;
+        const bool row_ok = m0 + ml < p.M;
+        const float2 w0 = wpart[ml], w1 = wpart[256 + ml];
+        const int c0 = min(max(p.N - n0, 0), 128), c1 = min(max(p.N - n0 - 128, 0), 128);
+        float a, b;
+        if constexpr (R2 == 1) {
+          a = fmaxf(w0.x, w1.x);
+          b = w0.y * fast_exp2((w0.x - a) * kLog2e) + (c1 > 0 ? w1.y * fast_exp2((w1.x - a) * kLog2e) : 0.0f);
+        } else if constexpr (R2 == 2) {
+          float nn = (float)c0;
+          a = w0.x;
+          b = w0.y;
+          chan_merge(nn, a, b, (float)c1, w1.x, w1.y);
+        } else {
+          a = w0.x + w1.x;
+          b = 0.0f;
+        }
+        if (p.ws_hdr != nullptr && row_ok) {
+          uint64_t* slots = p.ws_slots2 + (size_t)strip * p.tiles_n * 512 + 2 * ml;
+          publish(slots + (size_t)tn * 512, a, tag);
+          if constexpr (R2 != 3) publish(slots + (size_t)tn * 512 + 1, b, tag);
+          const uint64_t t0 = wall_clock64();
+          float ra = R2 == 1 ? -INFINITY : 0.0f, rb = 0.0f, rn = 0.0f;
+          for (int tb = 0; tb < p.tiles_n; tb += 8) {
+            float va[8], vb[8];
+            uint32_t need = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              va[j] = a;
+              vb[j] = b;
+              if (tb + j < p.tiles_n && tb + j != tn) need |= 1u << j;
+            }
+            while (need) {
+              uint64_t wa[8], wb[8];
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                wa[j] = wb[j] = 0;
+                if (need & (1u << j)) {
+                  wa[j] = __hip_atomic_load(slots + (size_t)(tb + j) * 512, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                  if constexpr (R2 != 3)
+                    wb[j] = __hip_atomic_load(slots + (size_t)(tb + j) * 512 + 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+                }
+              }
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                const bool ok = (uint32_t)(wa[j] >> 32) == tag && (R2 == 3 || (uint32_t)(wb[j] >> 32) == tag);
+                if ((need & (1u << j)) && ok) {
+                  va[j] = __uint_as_float((uint32_t)wa[j]);
+                  vb[j] = __uint_as_float((uint32_t)wb[j]);
+                  need &= ~(1u << j);
+                }
+              }
+              if (!need) break;
+              if (timed_out || wall_clock64() - t0 > p.spin_ticks) {   // recorded; the values are not used
+                timed_out = true;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                  if (need & (1u << j)) va[j] = vb[j] = 0.0f;
+                break;
+              }
+              __builtin_amdgcn_s_sleep(2);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const int tt = tb + j;
+              if (tt >= p.tiles_n) break;
+              if constexpr (R2 == 1) {
+                const float Mn = fmaxf(ra, va[j]);
+                rb = rb * fast_exp2((ra - Mn) * kLog2e) + vb[j] * fast_exp2((va[j] - Mn) * kLog2e);
+                ra = Mn;
+              } else if constexpr (R2 == 2) {
+                chan_merge(rn, ra, rb, (float)min(kGemmBN, p.N - tt * kGemmBN), va[j], vb[j]);
+              } else {
+                ra += va[j];
+              }
+            }
+          }
+          a = ra;
+          b = rb;
+        }
+        if constexpr (R2 == 1) rstat2[ml] = make_float2(a * kLog2e, 1.0f / b);
+        else if constexpr (R2 == 2) rstat2[ml] = make_float2(a, rsqrtf(b / (float)p.N + p.eps2));
+        else rstat2[ml] = make_float2(rsqrtf(a / (float)p.N + p.eps2), 0.0f);
+      }
+      __syncthreads();
+    };
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    if (p.row_op2 == 1) stage2(I1{});
+    else if (p.row_op2 == 2) stage2(I2{});
+    else stage2(I3{});
+  }
+
   // ---- stage 2: normalise, affine, cast, store
   // Column group outer, row block inner: the per-column vectors are read
   // from LDS once per group and reused by the 4 row blocks.
@@ -761,12 +972,13 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
     constexpr int kX = decltype(xc)::value;
     constexpr uint32_t es = kOutF32 ? 4u : 2u;
     const uint32_t xes = kX == 2 ? 4u : kX == 1 ? 2u : (p.x_f32 ? 4u : 2u);
-    float2 st[4];
+    float2 st[4], st2[4];
     uint32_t rowoff[4], xrowoff[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const int ml = wm * 128 + mb * 32 + r32;
       st[mb] = ROW != 0 ? rstat[ml] : make_float2(0.f, 0.f);
+      st2[mb] = kTwo ? rstat2[ml] : make_float2(0.f, 0.f);
       rowoff[mb] = ((uint32_t)(m0 + ml) * p.ldc + (uint32_t)(n0 + wn * 128 + 4 * h)) * es;
       if constexpr (kX != 0) xrowoff[mb] = ((uint32_t)(m0 + ml) * p.ldx + (uint32_t)(n0 + wn * 128 + 4 * h)) * xes;
     }
@@ -777,6 +989,11 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
       f32x4_t g = {1.f, 1.f, 1.f, 1.f}, be = {0.f, 0.f, 0.f, 0.f};
       if constexpr (ROW == 2 || ROW == 3) g = *(const f32x4_t*)(vg_lane + c);
       if constexpr (ROW == 2) be = *(const f32x4_t*)(ve_lane + c);
+      f32x4_t g2 = {1.f, 1.f, 1.f, 1.f}, b2 = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (kTwo) {
+        g2 = *(const f32x4_t*)(vg2_lane + c);
+        b2 = *(const f32x4_t*)(vb2_lane + c);
+      }
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         float x[4], y[4];
@@ -817,6 +1034,15 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
           else if constexpr (ROW == 3) y[e] = x[e] * st[mb].x * g[e];
           else if constexpr (ROW == 1) y[e] = fast_exp2(__builtin_fmaf(x[e], kLog2e, -st[mb].x)) * st[mb].y;
           else y[e] = x[e];
+        }
+        if constexpr (kTwo) {
+          const int r2 = p.row_op2;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (r2 == 2) y[e] = __builtin_fmaf((y[e] - st2[mb].x) * st2[mb].y, g2[e], b2[e]);
+            else if (r2 == 3) y[e] = y[e] * st2[mb].x * g2[e];
+            else y[e] = fast_exp2(__builtin_fmaf(y[e], kLog2e, -st2[mb].x)) * st2[mb].y;
+          }
         }
         tok = y[3];
         if constexpr (kOutF32) {
@@ -881,11 +1107,12 @@ __device__ inline void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueP
 // epilogue of whole column tiles is then specialised on kRow (cf_row_op) and
 // kPre (bias/residual present). The general path (kVec false) dispatches on
 // p.row_op at run time.
-template <bool kF32, bool kBnk, bool kVec, int kRow, bool kPre>
+template <bool kF32, bool kBnk, bool kVec, int kRow, bool kPre, bool kTwo = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void gemm_epilogue_kernel(GemmEpilogueParams p) {
   constexpr int kLdsMain = 4 * kTileBytes > kStages * kStageBytes ? 4 * kTileBytes : kStages * kStageBytes;
-  constexpr int kLdsBytes = kLdsMain > kLdsEpilogue ? kLdsMain : kLdsEpilogue;
+  constexpr int kLdsEpi = kTwo ? kLdsTwo : kLdsEpilogue;
+  constexpr int kLdsBytes = kLdsMain > kLdsEpi ? kLdsMain : kLdsEpi;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
   constexpr int BK = 8 * In<kF32>::kChunk;
   constexpr int S = In<kF32>::kSize;
@@ -1011,7 +1238,10 @@ void gemm_epilogue_kernel(GemmEpilogueParams p) {
     }
 
     // ------------------------------------------------------------------ epilogue
-    if constexpr (kVec) {
+    if constexpr (kTwo) {   // fast path only (the launcher routes nothing else here)
+      if (n0 + kGemmBN > p.N) epilogue<kRow, true, kPre, false, true, true>(acc, p, smem, strip, tn, tag, timed_out, tid_t);
+      else epilogue<kRow, true, kPre, false, false, true>(acc, p, smem, strip, tn, tag, timed_out, tid_t);
+    } else if constexpr (kVec) {
       // the last column tile of a strip may be ragged (N a multiple of 8, not
       // of 256): its epilogue masks columns against N; the main loop's
       // accumulators of columns >= N hold whatever the B loads read there,

@@ -16,6 +16,7 @@ Prints one JSON line:
   cpu_baseline  the fp64 oracle timed on the host cores on a bounded row sample
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--store-x] [--causal] [--argmax]
+                       [--row2 softmax|layernorm|rmsnorm]
 """
 from __future__ import annotations
 
@@ -62,6 +63,9 @@ def parse():
     ap.add_argument("--argmax", action="store_true",
                     help="GEMM + epilogue workloads: replace the row operation by a row argmax and write no "
                          "[M, N] output (a greedy LM-head step)")
+    ap.add_argument("--row2", choices=["softmax", "layernorm", "rmsnorm"], default=None,
+                    help="GEMM + epilogue workloads: a second row stage on the first one's output (its gamma/beta "
+                         "are the workload's own vectors)")
     ap.add_argument("--causal", action="store_true",
                     help="attention workload: causal mask (key l visible to query m iff l <= m + L - M); the "
                          "algorithmic flops count only the visible (query, key) pairs")
@@ -141,7 +145,7 @@ def roofline_of(w, kernel_ms: float, store_x: bool = False, causal: bool = False
     return "mfma", "TFLOP/s", peak_flops, flops / (kernel_ms * 1e-3) / 1e12, intensity, ridge
 
 
-def make_call(w, dev, torch, cf, store_x: bool = False, causal: bool = False, argmax: bool = False):
+def make_call(w, dev, torch, cf, store_x: bool = False, causal: bool = False, argmax: bool = False, row2=None):
     """Device tensors + a closure launching one fused kernel on the current stream."""
     p = w.params
     out_dt = torch.float32 if p.get("out_dtype") == "f32" else torch.bfloat16
@@ -157,9 +161,13 @@ def make_call(w, dev, torch, cf, store_x: bool = False, causal: bool = False, ar
             C = None
         else:
             idx = mx = None
+            g = dev.get("gamma", dev.get("weight"))
             e = cf.make_epilogue(alpha=p["alpha"], bias=dev.get("bias"), residual=dev.get("residual"),
-                                 act=p["act"], row_op=p["row_op"], gamma=dev.get("gamma", dev.get("weight")),
-                                 beta=dev.get("beta"), eps=p.get("eps", 0.0), x_out=X)
+                                 act=p["act"], row_op=p["row_op"], gamma=g, beta=dev.get("beta"),
+                                 eps=p.get("eps", 0.0), x_out=X, row_op2=row2 or "none",
+                                 gamma2=g if row2 in ("layernorm", "rmsnorm") else None,
+                                 beta2=dev.get("beta") if row2 == "layernorm" else None,
+                                 eps2=p.get("eps", 0.0) if row2 else 0.0)
             C = torch.empty(d["M"], d["N"], dtype=out_dt, device="cuda")
         nbytes = cf.cf_gemm_epilogue_workspace_size(d["M"], d["N"], d["K"], e)
         ws = cf.Workspace("cuda").get(nbytes)
@@ -178,7 +186,7 @@ def make_call(w, dev, torch, cf, store_x: bool = False, causal: bool = False, ar
     return call, O, None, 0
 
 
-def cpu_baseline(w, raw, target_s: float, causal: bool = False, argmax: bool = False):
+def cpu_baseline(w, raw, target_s: float, causal: bool = False, argmax: bool = False, row2=None):
     """The fp64 oracle on a bounded sample of rows (rows are independent)."""
     import oracle
     ncores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
@@ -196,8 +204,15 @@ def cpu_baseline(w, raw, target_s: float, causal: bool = False, argmax: bool = F
         def run(rows):
             A = widen("A")[:rows] if rows < d["M"] else widen("A")
             R = widen("residual")[:rows] if "residual" in raw else None
+            g = vec.get("gamma", vec.get("weight"))
             if argmax:
                 oracle.gemm_epilogue_argmax(A, B, alpha=p["alpha"], bias=vec.get("bias"), residual=R, act=p["act"])
+            elif row2:
+                oracle.gemm_epilogue_two_stage(
+                    A, B, alpha=p["alpha"], bias=vec.get("bias"), residual=R, act=p["act"], row_op=p["row_op"],
+                    gamma=g, beta=vec.get("beta"), eps=p.get("eps", 0.0), row_op2=row2,
+                    gamma2=g if row2 in ("layernorm", "rmsnorm") else None,
+                    beta2=vec.get("beta") if row2 == "layernorm" else None, eps2=p.get("eps", 0.0))
             else:
                 oracle.gemm_epilogue(A, B, alpha=p["alpha"], bias=vec.get("bias"), residual=R, act=p["act"],
                                      row_op=p["row_op"], gamma=vec.get("gamma", vec.get("weight")),
@@ -262,6 +277,8 @@ def main():
     w = gen.workload(args.workload)
     if args.store_x and w.kind != "gemm_epilogue":
         raise SystemExit("--store-x applies to the GEMM + epilogue workloads")
+    if args.row2 and (w.kind != "gemm_epilogue" or args.argmax or w.params["row_op"] == "none"):
+        raise SystemExit("--row2 applies to the GEMM + epilogue workloads with a row operation, without --argmax")
     if args.argmax and w.kind != "gemm_epilogue":
         raise SystemExit("--argmax applies to the GEMM + epilogue workloads")
     if args.causal and (w.kind != "b2bgemm" or w.params["row_op"] != "softmax"):
@@ -283,7 +300,7 @@ def main():
     devs = [dev] + [{k: v.clone() for k, v in dev.items()} for _ in range(nset - 1)]
     calls = []
     for d_ in devs:
-        call, out, ws, ws_bytes = make_call(w, d_, torch, cf, args.store_x, args.causal, args.argmax)
+        call, out, ws, ws_bytes = make_call(w, d_, torch, cf, args.store_x, args.causal, args.argmax, args.row2)
         calls.append(call)
 
     # settle: batches of calls (grown to ~20 ms each) until --settle-s has passed
@@ -322,7 +339,7 @@ def main():
     bound, unit, peak, achieved, intensity, ridge = roofline_of(w, kernel_ms, args.store_x, args.causal,
                                                                 args.argmax)
     traffic = None
-    if os.path.exists(args.traffic) and not (args.plain or args.store_x or args.causal or args.argmax):
+    if os.path.exists(args.traffic) and not (args.plain or args.store_x or args.causal or args.argmax or args.row2):
         try:
             rec = json.load(open(args.traffic))
             if rec.get("kernel_source_hash") == kernel_source_hash():
@@ -345,7 +362,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name + ("/identity-epilogue" if args.plain else "")
                    + ("+x_out" if args.store_x else "") + ("/causal" if args.causal else "")
-                   + ("/argmax" if args.argmax else ""), **w.dims,
+                   + ("/argmax" if args.argmax else "") + (f"/then-{args.row2}" if args.row2 else ""), **w.dims,
                    "out_dtype": w.params.get("out_dtype"), "input_sets": nset, "input_bytes_per_set": in_bytes},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,
@@ -357,7 +374,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         del dev, devs, calls, out
-        line["cpu_baseline"] = cpu_baseline(w, raw, args.cpu_seconds, args.causal, args.argmax)
+        line["cpu_baseline"] = cpu_baseline(w, raw, args.cpu_seconds, args.causal, args.argmax, args.row2)
     print(json.dumps(line), flush=True)
 
 

@@ -108,7 +108,24 @@ typedef enum {
  *   CF_ROW_ARGMAX    row_stats[m]         = max_n x[m, n]
  * cf_b2bgemm (softmax only): row_stats[b * M + m] = ln sum_l exp(alpha * S[m, l])
  * over the visible keys; -inf for a causal row that sees none.
- * Must be 4-byte aligned; CF_ERR_INVALID_ARGUMENT with CF_ROW_NONE. */
+ * Must be 4-byte aligned; CF_ERR_INVALID_ARGUMENT with CF_ROW_NONE.
+ *
+ * Second row stage (row_op2, optional, cf_gemm_epilogue only): a second
+ * reduction boundary in the same epilogue (the review's "What carries the
+ * argument": an epilogue is a chain of DAGs cut at each reduction). With y the
+ * output of the first row operation (after its gamma/beta), C receives
+ *   z = row_op2(y) over the same row, with gamma2, beta2 and eps2
+ * (meanings as for the first stage; vec_dtype for both vector sets). row_op
+ * must then be CF_ROW_SOFTMAX, CF_ROW_LAYERNORM or CF_ROW_RMSNORM and row_op2
+ * one of these three (CF_ERR_INVALID_ARGUMENT otherwise, also for gamma2/beta2
+ * or eps2 set without row_op2 and beta2 without CF_ROW_LAYERNORM). row_stats,
+ * if given, holds the first stage's statistics and x_out the first stage's
+ * input x. The workspace then holds a second set of exchange slots
+ * (cf_gemm_epilogue_workspace_size counts them). Two stages run only where
+ * the fast path does: N, K and every leading dimension multiples of 8 (of 4
+ * for fp32 inputs), 16-byte aligned matrices, no fp32 residual
+ * (CF_ERR_UNSUPPORTED otherwise). cf_b2bgemm: row_op2 must be CF_ROW_NONE
+ * (CF_ERR_UNSUPPORTED). */
 typedef struct cf_epilogue {
   uint32_t struct_size;     /* must be sizeof(cf_epilogue)                        */
   float alpha;
@@ -128,6 +145,10 @@ typedef struct cf_epilogue {
   cf_mask mask;             /* cf_b2bgemm with row_op CF_ROW_SOFTMAX only         */
   float* row_stats;         /* optional fp32 per-row statistics of the row op (see below) */
   int32_t* row_index;       /* CF_ROW_ARGMAX: [M] column of each row's maximum (required) */
+  cf_row_op row_op2;        /* optional second row stage on the first one's output (below) */
+  const void* gamma2;       /* its LayerNorm gamma / RMSNorm weight, N of vec_dtype, or NULL */
+  const void* beta2;        /* its LayerNorm beta, or NULL                               */
+  float eps2;
 } cf_epilogue;
 
 /* Fills *epi with the identity epilogue (alpha 1, no bias/residual/act/row op). */

@@ -112,6 +112,16 @@ def epi(**kw):
     (dict(epi=epi(row_op=5)), cf.CF_ERR_INVALID_ARGUMENT),
     (dict(C=None, epi=epi(row_op=3)), cf.CF_ERR_INVALID_ARGUMENT),    # only argmax may omit C
     (dict(epi=epi(row_op=2, row_stats=PW + 1)), cf.CF_ERR_INVALID_ARGUMENT),
+    (dict(epi=epi(row_op2=1)), cf.CF_ERR_INVALID_ARGUMENT),           # a second stage needs a first
+    (dict(epi=epi(row_op=4, row_index=PW, row_op2=1)), cf.CF_ERR_INVALID_ARGUMENT),   # not after argmax
+    (dict(epi=epi(row_op=2, row_op2=4)), cf.CF_ERR_INVALID_ARGUMENT),  # argmax is no second stage
+    (dict(epi=epi(row_op=2, row_op2=9)), cf.CF_ERR_INVALID_ARGUMENT),
+    (dict(epi=epi(gamma2=PB)), cf.CF_ERR_INVALID_ARGUMENT),           # second-stage vectors without it
+    (dict(epi=epi(eps2=1e-5)), cf.CF_ERR_INVALID_ARGUMENT),
+    (dict(epi=epi(row_op=2, row_op2=1, beta2=PB)), cf.CF_ERR_INVALID_ARGUMENT),   # beta2 belongs to LayerNorm
+    (dict(epi=epi(row_op=2, row_op2=2, eps2=-1.0)), cf.CF_ERR_INVALID_ARGUMENT),
+    (dict(epi=epi(row_op=2, row_op2=2, gamma2=PB + 1)), cf.CF_ERR_INVALID_ARGUMENT),   # misaligned bf16
+    (dict(K=60, epi=epi(row_op=2, row_op2=1)), cf.CF_ERR_UNSUPPORTED),   # two stages: fast-path layouts only
     (dict(M=0), cf.CF_OK),            # empty problems launch nothing
     (dict(N=0), cf.CF_OK),
 ])
@@ -146,6 +156,7 @@ def b2b(batch=1, M=64, K=64, L=64, N=64, A=PA, lda=64, sa=0, B0=PB, ldb0=64, sb0
     (dict(mid=epi(row_op=1, row_stats=PW + 2)), cf.CF_ERR_INVALID_ARGUMENT),
     (dict(mid=epi(row_op=1, mask=2)), cf.CF_ERR_INVALID_ARGUMENT),
     (dict(mid=epi(row_op=4, row_index=PW)), cf.CF_ERR_UNSUPPORTED),   # argmax between two GEMMs
+    (dict(mid=epi(row_op=1, row_op2=2)), cf.CF_ERR_UNSUPPORTED),      # one row stage between two GEMMs
     (dict(batch=0), cf.CF_OK),
 ])
 def test_b2bgemm_argument_checks(kw, status):
@@ -158,6 +169,9 @@ def test_workspace_sizes():
     assert cf.cf_gemm_epilogue_workspace_size(16384, 4096, 11008, epi(row_op=3)) == 512 + 64 * 16 * 256 * 16
     assert cf.cf_gemm_epilogue_workspace_size(8192, 256, 4096, e) == 0        # one column tile per strip
     assert cf.cf_gemm_epilogue_workspace_size(8192, 4096, 4096, epi()) == 0   # no row op
+    # a second row stage exchanges through a second set of slots
+    assert cf.cf_gemm_epilogue_workspace_size(8192, 4096, 4096, epi(row_op=2, row_op2=1)) == \
+        512 + 2 * 32 * 16 * 256 * 16
     assert lib.cf_workspace_init(None, 4096, None) == cf.CF_ERR_WORKSPACE
     assert lib.cf_workspace_init(PW + 16, 4096, None) == cf.CF_ERR_WORKSPACE
 

@@ -171,6 +171,64 @@ def test_ragged_column_tile_nan_past_n(row_op):
     P.assert_bf16_consistent(c16, c32, R, f"NaN past N, {row_op} bf16")
 
 
+# ---------------------------------------------------------------------------- two row stages
+def _vec(rng, n, mu, sd):
+    return torch.from_numpy(rng.normal(mu, sd, n)).to(torch.bfloat16).cuda()
+
+
+def _f64(t):
+    return None if t is None else P.gpu_to_f64(t)
+
+
+@pytest.mark.parametrize("op1,op2", [("layernorm", "softmax"), ("softmax", "layernorm"), ("rmsnorm", "rmsnorm"),
+                                     ("layernorm", "rmsnorm"), ("softmax", "softmax"), ("rmsnorm", "layernorm")])
+@pytest.mark.parametrize("N", [256, 1024, 1000])
+def test_two_row_stages(op1, op2, N):
+    # a second reduction boundary: z = op2(op1(x)), each stage with its own
+    # affine vectors and eps; one column tile (no exchange), four, and four
+    # with a ragged last one per strip; M = 300 leaves a ragged row strip
+    M, K = 300, 256
+    w, dev, ref = P.inputs("c3_gemm_residual_rmsnorm", seed=31, M=M, N=N, K=K)
+    rng = np.random.default_rng(32)
+    bias = _vec(rng, N, 0.0, 0.3)
+    g1 = _vec(rng, N, 1.0, 0.1) if op1 != "softmax" else None
+    b1 = _vec(rng, N, 0.0, 0.1) if op1 == "layernorm" else None
+    g2 = _vec(rng, N, 1.0, 0.2) if op2 != "softmax" else None
+    b2 = _vec(rng, N, 0.0, 0.2) if op2 == "layernorm" else None
+    kw = dict(alpha=0.5, bias=bias, residual=dev["residual"], act="relu", row_op=op1, gamma=g1, beta=b1, eps=1e-5,
+              row_op2=op2, gamma2=g2, beta2=b2, eps2=1e-3)
+    R = oracle.gemm_epilogue_two_stage(ref["A"], ref["B"], alpha=0.5, bias=_f64(bias), residual=ref["residual"],
+                                       act="relu", row_op=op1, gamma=_f64(g1), beta=_f64(b1), eps=1e-5, row_op2=op2,
+                                       gamma2=_f64(g2), beta2=_f64(b2), eps2=1e-3)
+    c32 = run(dev["A"], dev["B"], torch.float32, **kw)
+    r, m = P.assert_close(P.gpu_to_f64(c32), R, P.REL_F_BF16, P.MAX_ABS_BF16, f"{op1} -> {op2} N={N}")
+    c16 = run(dev["A"], dev["B"], torch.bfloat16, **kw)
+    P.assert_bf16_consistent(c16, c32, R, f"{op1} -> {op2} N={N} bf16")
+    print(f"{op1} -> {op2} N={N}: relF {r:.2e} maxabs {m:.2e}", flush=True)
+
+
+def test_two_row_stages_b_nk_with_x_and_stats():
+    # B given [N, K]; the second output X (the first stage's input) and the
+    # first stage's row statistics beside the two-stage result
+    M, N, K = 300, 1024, 512
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=33, M=M, N=N, K=K)
+    rng = np.random.default_rng(34)
+    g2 = _vec(rng, N, 1.0, 0.2)
+    Bt = dev["B"].t().contiguous()
+    Xo = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    st = torch.full((2 * M,), float("nan"), dtype=torch.float32, device="cuda")
+    kw = dict(row_op="layernorm", gamma=dev["gamma"], beta=dev["beta"], eps=1e-5, row_op2="rmsnorm", gamma2=g2,
+              eps2=1e-6, x_out=Xo, row_stats=st)
+    C = run(dev["A"], Bt, torch.float32, b_is_nk=True, **kw)
+    R = oracle.gemm_epilogue_two_stage(ref["A"], ref["B"], row_op="layernorm", gamma=ref["gamma"], beta=ref["beta"],
+                                       eps=1e-5, row_op2="rmsnorm", gamma2=_f64(g2), eps2=1e-6)
+    Xr = oracle.elementwise_stage(oracle.matmul(ref["A"], ref["B"]))
+    P.assert_close(P.gpu_to_f64(C), R, P.REL_F_BF16, P.MAX_ABS_BF16, "LN -> RMS, B [N,K]")
+    P.assert_close(P.gpu_to_f64(Xo), Xr, 1e-5, 1e-4, "X beside two stages")
+    S = oracle.row_statistics(Xr, "layernorm", 1e-5).reshape(-1)
+    P.assert_close(P.gpu_to_f64(st), S, REL_F_STATS, MAX_ABS_STATS, "first-stage statistics beside two stages")
+
+
 @pytest.mark.parametrize("row_op", ["layernorm", "softmax"])
 def test_b_nk_layout(row_op):
     w, dev, ref = P.inputs("c2_gemm_layernorm", seed=4, M=256, N=512, K=256)

@@ -1,9 +1,9 @@
 // One instantiation unit of the GEMM + epilogue kernel. Compiled once per
 // (input dtype, B layout, part): CF_IN_F32 in {0, 1}, CF_B_NK in {0, 1},
 // CF_PART in {0, 1, 2, 3, 4} (fast path for row op CF_PART, with and without
-// bias/residual), 5 (general path) or 6, 7, 8 (two row stages, fast path, the
-// first stage's row op CF_PART - 5). Splitting the instantiations lets them
-// compile in parallel.
+// bias/residual), 5 (general path) or 6 to 14 (two row stages, fast path:
+// first row op 1 + (CF_PART - 6) / 3, second 1 + (CF_PART - 6) % 3).
+// Splitting the instantiations lets them compile in parallel.
 #include "gemm_epilogue_kernel.hpp"
 
 #if !defined(CF_IN_F32) || !defined(CF_B_NK) || !defined(CF_PART)
@@ -16,8 +16,8 @@
 
 namespace cf {
 
-// Kernel entry of this unit; `pre` selects the bias/residual variant (parts
-// 0-4; the two-stage parts take bias and residual at run time).
+// Kernel entry of this unit; `pre` selects the bias/residual variant (every
+// part but the general one).
 const void* CF_FN(int pre) {
 #if CF_PART < 5
   if (pre) return (const void*)&gemm_epilogue_kernel<CF_IN_F32 != 0, CF_B_NK != 0, true, CF_PART, true>;
@@ -26,8 +26,11 @@ const void* CF_FN(int pre) {
   (void)pre;
   return (const void*)&gemm_epilogue_kernel<CF_IN_F32 != 0, CF_B_NK != 0, false, 0, false>;
 #else
-  (void)pre;
-  return (const void*)&gemm_epilogue_kernel<CF_IN_F32 != 0, CF_B_NK != 0, true, CF_PART - 5, true, true>;
+  if (pre)
+    return (const void*)&gemm_epilogue_kernel<CF_IN_F32 != 0, CF_B_NK != 0, true, 1 + (CF_PART - 6) / 3, true,
+                                              1 + (CF_PART - 6) % 3>;
+  return (const void*)&gemm_epilogue_kernel<CF_IN_F32 != 0, CF_B_NK != 0, true, 1 + (CF_PART - 6) / 3, false,
+                                            1 + (CF_PART - 6) % 3>;
 #endif
 }
 

@@ -434,10 +434,12 @@ __device__ inline float2 halves(float v) {
 // (N a multiple of 8: a 4- or 8-column group is valid or invalid as a whole).
 // kPre: a bias or a residual is present.
 // kId: alpha == 1 and no activation, so the elementwise stage is P (+ bias + R).
-// kTwo (ROW 1-3): a second row stage p.row_op2 (run-time: softmax, LayerNorm,
-// RMSNorm) acts on the first stage's output y over the same row, with its own
+// ROW2 (with ROW 1-3): a second row stage (1 softmax, 2 LayerNorm, 3 RMSNorm;
+// 0 none) acts on the first stage's output y over the same row, with its own
 // statistics pass over y and its own strip exchange (slots p.ws_slots2).
-template <int ROW, bool kFast, bool kPre, bool kId, bool kRagged = false, bool kTwo = false>
+// Every choice inside the per-group code is a compile-time one: run-time
+// conditions there cost scalar registers that the epilogue does not have.
+template <int ROW, bool kFast, bool kPre, bool kId, bool kRagged = false, int ROW2 = 0>
 __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueParams& p, uint8_t* smem,
                                 int strip, int tn, uint32_t tag, bool& timed_out, int tid) {
   const int lane = tid & 63, wave = tid >> 6;
@@ -756,7 +758,8 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
     __syncthreads();
   }
 
-  // ---- second row stage (kTwo): statistics of y = stage1(x) per row, a
+  constexpr bool kTwo = ROW2 != 0;
+  // ---- second row stage (ROW2): statistics of y = stage1(x) per row, a
   // second strip exchange, then z = stage2(y) in the store pass below
   float* vg2 = (float*)(smem + kOffTwo);
   float* vb2 = vg2 + 256;
@@ -952,12 +955,7 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
       }
       __syncthreads();
     };
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
-    if (p.row_op2 == 1) stage2(I1{});
-    else if (p.row_op2 == 2) stage2(I2{});
-    else stage2(I3{});
+    stage2(std::integral_constant<int, ROW2>{});
   }
 
   // ---- stage 2: normalise, affine, cast, store
@@ -1036,11 +1034,10 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
           else y[e] = x[e];
         }
         if constexpr (kTwo) {
-          const int r2 = p.row_op2;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            if (r2 == 2) y[e] = __builtin_fmaf((y[e] - st2[mb].x) * st2[mb].y, g2[e], b2[e]);
-            else if (r2 == 3) y[e] = y[e] * st2[mb].x * g2[e];
+            if constexpr (ROW2 == 2) y[e] = __builtin_fmaf((y[e] - st2[mb].x) * st2[mb].y, g2[e], b2[e]);
+            else if constexpr (ROW2 == 3) y[e] = y[e] * st2[mb].x * g2[e];
             else y[e] = fast_exp2(__builtin_fmaf(y[e], kLog2e, -st2[mb].x)) * st2[mb].y;
           }
         }
@@ -1077,6 +1074,7 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
   using X1 = std::integral_constant<int, 1>;
   using X2 = std::integral_constant<int, 2>;
   using XR = std::integral_constant<int, 3>;
+  // (the general path takes X's dtype at run time)
   if (p.c_f32) {
     if constexpr (!kFast) store_pass(std::true_type{}, XR{});
     else if (!p.X) store_pass(std::true_type{}, X0{});
@@ -1107,11 +1105,12 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
 // epilogue of whole column tiles is then specialised on kRow (cf_row_op) and
 // kPre (bias/residual present). The general path (kVec false) dispatches on
 // p.row_op at run time.
-template <bool kF32, bool kBnk, bool kVec, int kRow, bool kPre, bool kTwo = false>
+// kRow2 (with kVec and kRow 1-3): the second row stage, see epilogue's ROW2.
+template <bool kF32, bool kBnk, bool kVec, int kRow, bool kPre, int kRow2 = 0>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void gemm_epilogue_kernel(GemmEpilogueParams p) {
   constexpr int kLdsMain = 4 * kTileBytes > kStages * kStageBytes ? 4 * kTileBytes : kStages * kStageBytes;
-  constexpr int kLdsEpi = kTwo ? kLdsTwo : kLdsEpilogue;
+  constexpr int kLdsEpi = kRow2 != 0 ? kLdsTwo : kLdsEpilogue;
   constexpr int kLdsBytes = kLdsMain > kLdsEpi ? kLdsMain : kLdsEpi;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
   constexpr int BK = 8 * In<kF32>::kChunk;
@@ -1238,9 +1237,11 @@ void gemm_epilogue_kernel(GemmEpilogueParams p) {
     }
 
     // ------------------------------------------------------------------ epilogue
-    if constexpr (kTwo) {   // fast path only (the launcher routes nothing else here)
-      if (n0 + kGemmBN > p.N) epilogue<kRow, true, kPre, false, true, true>(acc, p, smem, strip, tn, tag, timed_out, tid_t);
-      else epilogue<kRow, true, kPre, false, false, true>(acc, p, smem, strip, tn, tag, timed_out, tid_t);
+    if constexpr (kRow2 != 0) {
+      // fast path only (the launcher routes nothing else here); the
+      // column-masked epilogue serves whole and ragged tiles
+      if (p.alpha == 1.0f && p.act == 0) epilogue<kRow, true, kPre, true, true, kRow2>(acc, p, smem, strip, tn, tag, timed_out, tid_t);
+      else epilogue<kRow, true, kPre, false, true, kRow2>(acc, p, smem, strip, tn, tag, timed_out, tid_t);
     } else if constexpr (kVec) {
       // the last column tile of a strip may be ragged (N a multiple of 8, not
       // of 256): its epilogue masks columns against N; the main loop's

@@ -13,6 +13,8 @@ into the stage stream of one kernel:
   boundary (optional, last axis): softmax, layer_norm, rms_norm, or a second
         GEMM that consumes the result (back-to-back GEMM; its first stage may
         be a scale, ReLU or softmax)
+  second boundary (optional, GEMM + epilogue only): softmax, layer_norm or
+        rms_norm of the first one's result
 
 and the stream becomes one ``cf_gemm_epilogue`` or ``cf_b2bgemm`` call. The
 stage-1 value may also be an output of the function (it is then stored as the
@@ -106,6 +108,41 @@ def _single_user(n, outputs) -> Optional[fx.Node]:
     return users[0] if users else None
 
 
+def _place_row_op(u, N, placeholders, plan, stage: str) -> bool:
+    """Places u into the descriptor if it is a row operation over the last axis:
+    row_op/gamma/beta/eps for the first boundary (stage ""), row_op2/gamma2/
+    beta2/eps2 for the second ("2"). False if u is no row operation."""
+    if u is None:
+        return False
+    if (u.op == "call_function" and u.target in _SOFTMAX) or (u.op == "call_method" and u.target == "softmax"):
+        dim = u.kwargs.get("dim", u.args[1] if len(u.args) > 1 else None)
+        if not _last_axis(u, dim):
+            raise NotFusable("softmax over an axis other than the last")
+        plan.epi["row_op" + stage] = "softmax"
+        return True
+    if u.op == "call_function" and u.target in (F.layer_norm, F.rms_norm):
+        shape = u.args[1] if len(u.args) > 1 else u.kwargs["normalized_shape"]
+        if len(shape) != 1:
+            raise NotFusable("the normalisation must be over the last axis only")
+        is_ln = u.target is F.layer_norm
+        names = ("weight", "bias", "eps") if is_ln else ("weight", "eps")
+        vals = dict(zip(names, u.args[2:]))
+        vals.update({k: v for k, v in u.kwargs.items() if k in names})
+        for k, role in (("weight", "gamma"), ("bias", "beta")):
+            t = vals.get(k)
+            if t is None:
+                continue
+            if not (isinstance(t, fx.Node) and t.op == "placeholder" and _shape(t) == (N,)):
+                raise NotFusable(f"the {k} of {u.name} must be an input of shape [N]")
+            plan.tensors[role + stage] = placeholders.index(t)
+        eps = vals.get("eps", 1e-5 if is_ln else None)
+        if eps is None:
+            raise NotFusable("rms_norm without an explicit eps")
+        plan.epi.update({"row_op" + stage: "layernorm" if is_ln else "rmsnorm", "eps" + stage: float(eps)})
+        return True
+    return False
+
+
 def lower(fn: Callable, *example_args) -> "FusedFunction":
     """Trace ``fn`` and lower it to one fused call; the example arguments give
     the shapes (any device; shapes are propagated on meta tensors, so nothing
@@ -168,35 +205,14 @@ def lower(fn: Callable, *example_args) -> "FusedFunction":
         node = x_node = u
 
     plan.epi["alpha"] = float(alpha)
-    # ---- the boundary: a row reduction over the last axis and/or a second GEMM
+    # ---- the boundaries: up to two row reductions over the last axis, and/or a second GEMM
     y_node = node
     u = _single_user(node, outs)
-    if u is not None and ((u.op == "call_function" and u.target in _SOFTMAX) or
-                          (u.op == "call_method" and u.target == "softmax")):
-        dim = u.kwargs.get("dim", u.args[1] if len(u.args) > 1 else None)
-        if not _last_axis(u, dim):
-            raise NotFusable("softmax over an axis other than the last")
-        plan.epi["row_op"] = "softmax"
-        y_node, u = u, _single_user(u, outs)
-    elif u is not None and u.op == "call_function" and u.target in (F.layer_norm, F.rms_norm):
-        shape = u.args[1] if len(u.args) > 1 else u.kwargs["normalized_shape"]
-        if len(shape) != 1:
-            raise NotFusable("the normalisation must be over the last axis only")
-        is_ln = u.target is F.layer_norm
-        names = ("weight", "bias", "eps") if is_ln else ("weight", "eps")
-        vals = dict(zip(names, u.args[2:]))
-        vals.update({k: v for k, v in u.kwargs.items() if k in names})
-        for k, role in (("weight", "gamma"), ("bias", "beta")):
-            t = vals.get(k)
-            if t is None:
-                continue
-            if not (isinstance(t, fx.Node) and t.op == "placeholder" and _shape(t) == (N,)):
-                raise NotFusable(f"the {k} of {u.name} must be an input of shape [N]")
-            plan.tensors[role] = placeholders.index(t)
-        eps = vals.get("eps", 1e-5 if is_ln else None)
-        if eps is None:
-            raise NotFusable("rms_norm without an explicit eps")
-        plan.epi.update(row_op="layernorm" if is_ln else "rmsnorm", eps=float(eps))
+    for stage in ("", "2"):
+        if not _place_row_op(u, N, placeholders, plan, stage):
+            break
+        if stage == "2" and any(o is y_node for o in outs):
+            raise NotFusable("the first row stage's result is not stored beside a second one")
         y_node, u = u, _single_user(u, outs)
     if u is not None and _is_matmul(u):
         if u.args[0] is not y_node:
@@ -204,7 +220,7 @@ def lower(fn: Callable, *example_args) -> "FusedFunction":
         b1, b1_t = _operand(u.args[1], placeholders)
         if b1_t:
             raise NotFusable("the second GEMM's right operand must be stored [L, N]")
-        if plan.epi.get("row_op") not in (None, "softmax") or "residual" in plan.tensors:
+        if plan.epi.get("row_op") not in (None, "softmax") or "row_op2" in plan.epi or "residual" in plan.tensors:
             raise NotFusable("between two GEMMs only a scale, bias, ReLU or softmax may stand")
         if plan.epi.get("row_op") == "softmax" and ("bias" in plan.tensors or "act" in plan.epi):
             raise NotFusable("a softmax between two GEMMs takes the scaled scores as they are")
@@ -247,7 +263,7 @@ class FusedFunction:
         X = torch.empty(M, N, dtype=odt, device=A.device) if "x" in p.outputs else None
         C = torch.empty(M, N, dtype=odt, device=A.device)
         e = make_epilogue(bias=vec.get("bias"), residual=vec.get("residual"), gamma=vec.get("gamma"),
-                          beta=vec.get("beta"), x_out=X, **kw)
+                          beta=vec.get("beta"), gamma2=vec.get("gamma2"), beta2=vec.get("beta2"), x_out=X, **kw)
         if self._ws is None:
             self._ws = Workspace(str(A.device))
         ws = self._ws.get(cf_gemm_epilogue_workspace_size(M, N, A.shape[1], e))

@@ -53,6 +53,23 @@ def test_linear_bias_relu_layernorm():
     check_bf16(y, R, "lowered linear + bias + relu + layernorm")
 
 
+def test_two_row_stages():
+    # LayerNorm then softmax over the same rows, lowered to one call with two
+    # reduction boundaries
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=25, M=300, N=1024, K=256)
+
+    def block(x, wt, g, be):
+        return torch.softmax(F.layer_norm(x @ wt, (wt.shape[1],), g, be, 1e-5), dim=-1)
+
+    args = (dev["A"], dev["B"], dev["gamma"], dev["beta"])
+    f = fuse.lower(block, *args)
+    assert f.plan.epi["row_op2"] == "softmax"
+    y = f(*args, out_dtype=torch.float32)
+    R = oracle.gemm_epilogue_two_stage(ref["A"], ref["B"], row_op="layernorm", gamma=ref["gamma"], beta=ref["beta"],
+                                       eps=1e-5, row_op2="softmax")
+    P.assert_close(P.gpu_to_f64(y), R, P.REL_F_BF16, P.MAX_ABS_BF16, "lowered layernorm -> softmax")
+
+
 def test_attention():
     w, dev, ref = P.inputs("c5_b2b_attention", seed=24, batch=4, M=256, L=320)
 

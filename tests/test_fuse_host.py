@@ -66,13 +66,39 @@ def test_plain_gemm_and_division():
     (lambda x, w: (x @ w).sum(-1), "no place"),
     (lambda x, w: torch.relu(x @ w) * 2.0, "order"),
     (lambda x, w: torch.relu(x @ w) + 1.0, "other than an input"),
-    (lambda x, w: torch.softmax(F.layer_norm(x @ w, (N,)), dim=-1), "no place"),
+    (lambda x, w: torch.softmax(torch.softmax(F.layer_norm(x @ w, (N,)), dim=-1), dim=-1), "no place"),
     (lambda x, w: torch.tanh(x @ w), "no place"),
     (lambda x, w: x + 1.0, "no matrix product"),
 ])
 def test_rejected(fn, why):
     with pytest.raises(fuse.NotFusable, match=why):
         fuse.lower(fn, t(K, K), t(K, N))
+
+
+def test_two_row_stages():
+    # a second row operation on the first one's result: the second boundary
+    def fn(x, w, g, be, g2):
+        y = F.layer_norm(x @ w, (N,), g, be, 1e-5)
+        return F.rms_norm(y, (N,), g2, 1e-6)
+    p = fuse.lower(fn, t(M, K), t(K, N), t(N), t(N), t(N)).plan
+    assert p.epi == {"alpha": 1.0, "row_op": "layernorm", "eps": 1e-5, "row_op2": "rmsnorm", "eps2": 1e-6}
+    assert p.tensors == {"gamma": 2, "beta": 3, "gamma2": 4}
+    p = fuse.lower(lambda x, w: torch.softmax(F.rms_norm(x @ w, (N,), None, 1e-6), dim=-1), t(M, K), t(K, N)).plan
+    assert p.epi["row_op"] == "rmsnorm" and p.epi["row_op2"] == "softmax"
+
+
+def test_two_row_stages_first_result_not_stored():
+    def fn(x, w):
+        y = F.layer_norm(x @ w, (N,))
+        return torch.softmax(y, dim=-1), y
+    with pytest.raises(fuse.NotFusable, match="beside a second"):
+        fuse.lower(fn, t(M, K), t(K, N))
+
+
+def test_two_row_stages_between_gemms_rejected():
+    with pytest.raises(fuse.NotFusable, match="between two GEMMs"):
+        fuse.lower(lambda q, k, v: torch.softmax(torch.softmax(q @ k, dim=-1), dim=-1) @ v,
+                   t(M, K), t(K, N), t(N, 4))
 
 
 def test_transposed_left_operand():

@@ -201,6 +201,29 @@ def row_argmax(X: np.ndarray):
     return idx, np.take_along_axis(X, idx[..., None], axis=-1)[..., 0]
 
 
+def row_topk(X: np.ndarray, k: int):
+    """(index, value) of each row's k largest entries, largest first: the
+    review's "Reading between the lines" names top-k among the single-axis
+    reductions the strip argument covers. Order: value descending, and among
+    equal values the smaller column first (so k = 1 is row_argmax); NaN never
+    enters. Returns int64 [..., k] and float64 [..., k]."""
+    X = np.asarray(X, np.float64)
+    n = X.shape[-1]
+    if not 1 <= k <= n:
+        raise ValueError(f"k = {k} outside 1..{n}")
+    key = np.where(np.isnan(X), -np.inf, X)
+    # a stable sort on the negated values keeps equal values in column order
+    idx = np.argsort(-key, axis=-1, kind="stable")[..., :k]
+    return idx, np.take_along_axis(X, idx, axis=-1)
+
+
+def gemm_epilogue_topk(A: np.ndarray, B: np.ndarray, k: int, *, alpha: float = 1.0,
+                       bias: Optional[np.ndarray] = None, residual: Optional[np.ndarray] = None,
+                       act: str = "none"):
+    """row_topk of the elementwise stage's result X = act(alpha A.B + bias + R)."""
+    return row_topk(elementwise_stage(matmul(A, B), alpha, bias, residual, act), k)
+
+
 def gemm_epilogue_argmax(A: np.ndarray, B: np.ndarray, *, alpha: float = 1.0,
                          bias: Optional[np.ndarray] = None, residual: Optional[np.ndarray] = None,
                          act: str = "none"):

@@ -309,6 +309,36 @@ def pin_two_stage(o):
             _close_dec(gv, wv, rtol=1e-12, atol=1e-13)
 
 
+def pin_row_topk(o):
+    """Top-k against brute force: exact rational x on tiny shapes, every row's
+    candidates compared pairwise (value, then column); duplicated columns of B
+    make exact ties, which must keep column order; k = 1 agrees with argmax."""
+    rng = np.random.default_rng(37)
+    m, kk, n = 4, 3, 9
+    A = _bf16_values(rng, (m, kk))
+    B = _bf16_values(rng, (kk, n))
+    B[:, 6] = B[:, 2]            # columns 2 and 6 equal in every row
+    B[:, 8] = B[:, 2]
+    bias = _bf16_values(rng, (n,))
+    bias[6] = bias[2]
+    bias[8] = bias[2]
+    E = X.mm(X.mat(A), X.mat(B))
+    Xf = [[Fraction(0.75) * E[i][j] + X.F(bias[j]) for j in range(n)] for i in range(m)]
+    for k in (1, 3, 5, 9):
+        idx, val = o.gemm_epilogue_topk(A, B, k, alpha=0.75, bias=bias)
+        assert idx.shape == (m, k) and val.shape == (m, k)
+        for i in range(m):
+            order = sorted(range(n), key=lambda j: (-Xf[i][j], j))[:k]
+            assert [int(v) for v in idx[i]] == order, (k, i, list(idx[i]), order)
+            for j, c in enumerate(order):
+                assert abs(Fraction(float(val[i, j])) - Xf[i][c]) <= Fraction(1, 2 ** 48)
+    ai, av = o.row_argmax(np.array([[1.0, 3.0, 3.0, -2.0]]))
+    ti, tv = o.row_topk(np.array([[1.0, 3.0, 3.0, -2.0]]), 1)
+    assert int(ti[0, 0]) == int(ai[0]) == 1 and tv[0, 0] == av[0] == 3.0
+    ti, tv = o.row_topk(np.array([[np.nan, 2.0, 5.0, 2.0]]), 3)
+    assert [int(v) for v in ti[0]] == [2, 1, 3]
+
+
 # --------------------------------------------------------------------------- back-to-back GEMM
 
 def pin_b2b_relu(o):
@@ -533,7 +563,7 @@ def pin_row_argmax(o):
 ALL_PINS = [pin_round_bf16, pin_widen_bf16, pin_matmul_exact, pin_stage1_exact, pin_softmax,
             pin_layernorm, pin_rmsnorm, pin_gemm_epilogue_composition, pin_two_outputs, pin_b2b_relu,
             pin_b2b_softmax, pin_b2b_causal, pin_row_statistics, pin_b2b_logsumexp, pin_row_argmax,
-            pin_two_stage]
+            pin_two_stage, pin_row_topk]
 
 
 def run_all(o):

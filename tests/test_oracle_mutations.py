@@ -89,6 +89,15 @@ MUTATIONS = {
     "two_stage_second_eps_from_first": [(
         "    return row_stage(Y, row_op2, gamma2, beta2, eps2)\n",
         "    return row_stage(Y, row_op2, gamma2, beta2, eps)\n")],
+    "topk_ties_to_last_column": [(
+        '    idx = np.argsort(-key, axis=-1, kind="stable")[..., :k]\n',
+        '    idx = (n - 1 - np.argsort(-key[..., ::-1], axis=-1, kind="stable"))[..., :k]\n')],
+    "topk_ascending": [(
+        '    idx = np.argsort(-key, axis=-1, kind="stable")[..., :k]\n',
+        '    idx = np.argsort(key, axis=-1, kind="stable")[..., :k]\n')],
+    "topk_one_short": [(
+        '    idx = np.argsort(-key, axis=-1, kind="stable")[..., :k]\n',
+        '    idx = np.argsort(-key, axis=-1, kind="stable")[..., :max(k - 1, 1)]\n')],
     "b2b_relu_dropped": [(
         "S = elementwise_stage(matmul(A, B0), alpha, bias, None, act)",
         "S = elementwise_stage(matmul(A, B0), alpha, bias, None, 'none')")],

@@ -26,7 +26,7 @@ CF_OK, CF_ERR_INVALID_ARGUMENT, CF_ERR_UNSUPPORTED, CF_ERR_WORKSPACE, CF_ERR_NO_
     CF_ERR_HIP, CF_ERR_DEVICE_TIMEOUT = range(7)
 CF_F32, CF_BF16 = 0, 1
 ACT = {"none": 0, "relu": 1}
-ROW_OP = {"none": 0, "softmax": 1, "layernorm": 2, "rmsnorm": 3, "argmax": 4}
+ROW_OP = {"none": 0, "softmax": 1, "layernorm": 2, "rmsnorm": 3, "argmax": 4, "topk": 5}
 MASK = {"none": 0, "causal": 1}
 
 
@@ -54,6 +54,7 @@ class cf_epilogue(ctypes.Structure):
         ("gamma2", ctypes.c_void_p),
         ("beta2", ctypes.c_void_p),
         ("eps2", ctypes.c_float),
+        ("topk", ctypes.c_int32),
     ]
 
 
@@ -135,7 +136,7 @@ def _ptr(t) -> Optional[int]:
 def make_epilogue(*, alpha: float = 1.0, bias=None, residual=None, act: str = "none",
                   row_op: str = "none", gamma=None, beta=None, eps: float = 0.0, x_out=None,
                   mask: str = "none", row_stats=None, row_index=None, row_op2: str = "none", gamma2=None,
-                  beta2=None, eps2: float = 0.0) -> cf_epilogue:
+                  beta2=None, eps2: float = 0.0, topk: int = 0) -> cf_epilogue:
     """cf_epilogue descriptor from tensors (bias/gamma/beta share one dtype).
     ``x_out``: optional [M, N] tensor that receives x before the row operation.
     ``mask``: "causal" for the softmax of cf_b2bgemm.
@@ -144,7 +145,9 @@ def make_epilogue(*, alpha: float = 1.0, bias=None, residual=None, act: str = "n
     row maximum for argmax). ``row_index``: contiguous int32 [M] tensor that
     receives each row's argmax column (row_op "argmax"). ``row_op2`` (with
     ``gamma2``, ``beta2``, ``eps2``): a second row stage applied to the first
-    one's output (cf_gemm_epilogue only)."""
+    one's output (cf_gemm_epilogue only). ``topk``: k (1..8) for row_op "topk",
+    whose ``row_index`` (int32 [M, k]) and ``row_stats`` (fp32 [M, k]) receive
+    each row's k largest columns and values."""
     e = cf_epilogue()
     _lib.cf_epilogue_init(ctypes.byref(e))
     e.alpha = float(alpha)
@@ -153,6 +156,7 @@ def make_epilogue(*, alpha: float = 1.0, bias=None, residual=None, act: str = "n
     e.eps = float(eps)
     e.mask = MASK[mask]
     e.row_op2 = ROW_OP[row_op2]
+    e.topk = int(topk)
     e.eps2 = float(eps2)
     if row_stats is not None:
         import torch
@@ -227,13 +231,14 @@ def cf_gemm_epilogue(A, B, C, *, b_is_nk: bool = False, epi: Optional[cf_epilogu
     if C is not None and C.shape != (M, N):
         raise ValueError(f"C must be [{M}, {N}]")
     ri = epi_kwargs.get("row_index")
-    if ri is not None and ri.numel() < M:
+    kk = int(epi_kwargs.get("topk", 0) or 1)
+    if ri is not None and ri.numel() < M * kk:
         raise ValueError("row_index is too small for M rows")
     x_out = epi_kwargs.get("x_out")
     if x_out is not None and tuple(x_out.shape) != (M, N):
         raise ValueError(f"x_out must be [{M}, {N}]")
     st = epi_kwargs.get("row_stats")
-    if st is not None and st.numel() < M * (2 if epi_kwargs.get("row_op") == "layernorm" else 1):
+    if st is not None and st.numel() < M * (2 if epi_kwargs.get("row_op") == "layernorm" else kk):
         raise ValueError("row_stats is too small for M rows")
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
                                                            workspace.numel() * workspace.element_size())

@@ -79,8 +79,9 @@ GemmPlan plan_gemm(int64_t M, int64_t N, const cf_epilogue* epi) {
   g.tiles = g.tiles_n * g.strips;
   g.exchange = epi && epi->row_op != CF_ROW_NONE && g.tiles_n > 1;
   if (g.exchange) {
-    // one slot set per reduction stage
-    const size_t slots = (size_t)g.strips * (size_t)g.tiles_n * (size_t)kTile * 2 * sizeof(uint64_t);
+    // one slot set per reduction stage; top-k publishes 8 (value, column) pairs per row
+    const size_t words = epi->row_op == CF_ROW_TOPK ? 16 : 2;
+    const size_t slots = (size_t)g.strips * (size_t)g.tiles_n * (size_t)kTile * words * sizeof(uint64_t);
     g.slot_bytes = ((slots + 255) / 256) * 256;
     g.ws_bytes = cf::kWsHeaderBytes + g.slot_bytes * (epi->row_op2 != CF_ROW_NONE ? 2 : 1);
   }
@@ -92,11 +93,17 @@ cf_status check_epilogue(const cf_epilogue* epi, int64_t N, bool allow_row_ops_n
   if (epi->struct_size != sizeof(cf_epilogue)) return CF_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(epi->alpha) || !std::isfinite(epi->eps) || epi->eps < 0.0f) return CF_ERR_INVALID_ARGUMENT;
   if (epi->act != CF_ACT_NONE && epi->act != CF_ACT_RELU) return CF_ERR_INVALID_ARGUMENT;
-  if (epi->row_op < CF_ROW_NONE || epi->row_op > CF_ROW_ARGMAX) return CF_ERR_INVALID_ARGUMENT;
-  if (epi->row_op == CF_ROW_ARGMAX) {
+  if (epi->row_op < CF_ROW_NONE || epi->row_op > CF_ROW_TOPK) return CF_ERR_INVALID_ARGUMENT;
+  if (epi->row_op == CF_ROW_ARGMAX || epi->row_op == CF_ROW_TOPK) {
     if (!epi->row_index || !aligned(epi->row_index, 4) || epi->gamma || epi->beta) return CF_ERR_INVALID_ARGUMENT;
     if (!allow_residual) return CF_ERR_UNSUPPORTED;
   } else if (epi->row_index) {
+    return CF_ERR_INVALID_ARGUMENT;
+  }
+  if (epi->row_op == CF_ROW_TOPK) {
+    if (epi->topk < 1 || epi->topk > 8 || epi->topk > N) return CF_ERR_INVALID_ARGUMENT;
+    if (epi->residual) return CF_ERR_UNSUPPORTED;   // its LDS staging area holds the lists
+  } else if (epi->topk != 0) {
     return CF_ERR_INVALID_ARGUMENT;
   }
   if (!is_dtype(epi->vec_dtype) || !is_dtype(epi->residual_dtype)) return CF_ERR_INVALID_ARGUMENT;
@@ -195,7 +202,7 @@ cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K, const void* A, int64
   if (st != CF_OK) return st;
   if (M == 0 || N == 0) return CF_OK;
   const size_t es = dsize(ab_dtype), cs = dsize(c_dtype);
-  const bool argmax = epi && epi->row_op == CF_ROW_ARGMAX;
+  const bool argmax = epi && (epi->row_op == CF_ROW_ARGMAX || epi->row_op == CF_ROW_TOPK);
   if (C ? ldc < N : !argmax) return CF_ERR_INVALID_ARGUMENT;
   if (K > 0) {
     if (!A || !B || lda < K) return CF_ERR_INVALID_ARGUMENT;
@@ -231,8 +238,8 @@ cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K, const void* A, int64
   if (epi && epi->residual)
     vec = vec && epi->residual_dtype == CF_BF16 && epi->ld_residual % 8 == 0 && aligned(epi->residual, 16);
   if (X) vec = vec && epi->ld_x_out % 8 == 0 && aligned(X, 16);
-  // two row stages: fast-path layouts only
-  if (epi && epi->row_op2 != CF_ROW_NONE && !vec) return CF_ERR_UNSUPPORTED;
+  // two row stages and top-k: fast-path layouts only
+  if (epi && (epi->row_op2 != CF_ROW_NONE || epi->row_op == CF_ROW_TOPK) && !vec) return CF_ERR_UNSUPPORTED;
 
   // ---- device
   int dev;
@@ -274,6 +281,7 @@ cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K, const void* A, int64
   p.c_f32 = c_dtype == CF_F32;
   p.vec_f32 = epi ? epi->vec_dtype == CF_F32 : 0;
   p.res_f32 = rdt == CF_F32;
+  p.topk = epi ? epi->topk : 0;
   p.row_op2 = epi ? (int)epi->row_op2 : 0;
   p.gamma2 = epi ? epi->gamma2 : nullptr;
   p.beta2 = epi ? epi->beta2 : nullptr;

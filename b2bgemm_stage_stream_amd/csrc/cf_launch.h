@@ -39,7 +39,7 @@ struct GemmEpilogueParams {
   uint32_t ldx, x_bytes;
   int x_f32;         // dtype of X: 1 fp32, 0 bf16
   float* row_stats;  // optional per-row statistics of the row operation
-  int32_t* row_index;   // row argmax: column of each row's maximum
+  int32_t* row_index;   // row argmax / top-k: column(s) of each row's maximum (k largest)
   int row_op2;       // second row stage on the first one's output (0: none)
   const void* gamma2;
   const void* beta2;
@@ -48,6 +48,7 @@ struct GemmEpilogueParams {
   uint64_t* ws_slots;
   uint64_t* ws_slots2;   // the second stage's exchange slots
   uint64_t spin_ticks;   // wall-clock ticks a strip wait may take
+  int topk;          // top-k: k (1..8)
 };
 
 // Launches the persistent kernel. in_f32: fp32 inputs (else bf16); b_nk: B

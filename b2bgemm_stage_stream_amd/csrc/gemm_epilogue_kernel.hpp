@@ -408,6 +408,22 @@ __device__ inline void acc_read4(const f32x16_t& blk, float tok, float (&v)[4]) 
       : "a"(blk[4 * Q]), "a"(blk[4 * Q + 1]), "a"(blk[4 * Q + 2]), "a"(blk[4 * Q + 3]), "v"(tok));
 }
 
+// Top-k list of kTopK (value, column) pairs sorted by value descending, equal
+// values by column ascending; insert one candidate (NaN never enters).
+constexpr int kTopK = 8;
+__device__ inline void topk_insert(float (&tv)[kTopK], int (&tc)[kTopK], float cv, int cc) {
+#pragma unroll
+  for (int j = 0; j < kTopK; ++j) {
+    const bool gt = cv > tv[j] || (cv == tv[j] && cc < tc[j]);
+    const float v0 = tv[j];
+    const int c0 = tc[j];
+    tv[j] = gt ? cv : v0;
+    tc[j] = gt ? cc : c0;
+    cv = gt ? v0 : cv;
+    cc = gt ? c0 : cc;
+  }
+}
+
 // (n, mean, M2) merge of two partial statistics (Chan et al.'s pairwise update).
 __device__ inline void chan_merge(float& n, float& mean, float& m2, float nb, float meanb, float m2b) {
   const float nn = n + nb;
@@ -425,7 +441,7 @@ __device__ inline float2 halves(float v) {
   return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// ROW: 0 none, 1 softmax, 2 LayerNorm, 3 RMSNorm, 4 argmax (cf_row_op).
+// ROW: 0 none, 1 softmax, 2 LayerNorm, 3 RMSNorm, 4 argmax, 5 top-k (cf_row_op).
 // kFast: 16-byte accesses are allowed, N is a multiple of 8 and the residual
 // (if any) is bf16; otherwise every column is masked against N, element by
 // element.
@@ -610,6 +626,38 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
           tok = s2;
         });
         a = sum_halves(s2);
+      } else if constexpr (ROW == 5) {
+        // top-k: a lane inserts its columns into a sorted list of kTopK, which
+        // goes to LDS (the residual staging area: top-k takes no residual)
+        float tv[kTopK];
+        int tc[kTopK];
+#pragma unroll
+        for (int j = 0; j < kTopK; ++j) {
+          tv[j] = -INFINITY;
+          tc[j] = 0x7fffffff;
+        }
+        for_groups([&](int nb, auto qc) {
+          constexpr int q = decltype(qc)::value;
+          float x[4];
+          xgroup(mb, nb, qc, bias4(nb, q), tok, x);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool ok = valid(nb, q, e);
+            topk_insert(tv, tc, ok ? x[e] : -INFINITY, ok ? n0 + wn * 128 + nb * 32 + 8 * q + 4 * h + e : 0x7fffffff);
+          }
+          tok = tv[kTopK - 1];
+        });
+        {
+          // lists of [wn][h][row]: the per-row merge below reads all four
+          const int row = wm * 128 + mb * 32 + r32;
+          float* lv = (float*)(smem + kOffRes) + ((wn * 2 + h) * 256 + row) * kTopK;
+          int* lc = (int*)(smem + kOffRes + 4 * 256 * kTopK * 4) + ((wn * 2 + h) * 256 + row) * kTopK;
+#pragma unroll
+          for (int j = 0; j < kTopK; ++j) {
+            lv[j] = tv[j];
+            lc[j] = tc[j];
+          }
+        }
       } else {
         // argmax: a lane visits its columns in increasing order, so a strict >
         // keeps the first of equal values; the lane halves interleave and are
@@ -635,14 +683,80 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
         a = take1 ? hm.y : hm.x;
         b = __int_as_float(take1 ? i1 : i0);
       }
-      if (h == 0) wpart[wn * 256 + wm * 128 + mb * 32 + r32] = make_float2(a, b);
+      if constexpr (ROW != 5)
+        if (h == 0) wpart[wn * 256 + wm * 128 + mb * 32 + r32] = make_float2(a, b);
     }
     __syncthreads();
 
     // ---- one thread per row: merge the two wave partials, then (reduction
     // level 3) exchange with the other column tiles of the strip and merge all
     // of them in tile order
-    {
+    if constexpr (ROW == 5) {
+      // top-k: merge the two waves' lists, then the strip's: every tile
+      // publishes its list (16 tagged words per row) and merges all of them
+      const int ml = tid;
+      const bool row_ok = m0 + ml < p.M;
+      const float* lv = (const float*)(smem + kOffRes);
+      const int* lc = (const int*)(smem + kOffRes + 4 * 256 * kTopK * 4);
+      float tv[kTopK];
+      int tc[kTopK];
+#pragma unroll
+      for (int j = 0; j < kTopK; ++j) {
+        tv[j] = lv[ml * kTopK + j];
+        tc[j] = lc[ml * kTopK + j];
+      }
+      // the other lane half and the other wave's two halves
+      for (int l = 1; l < 4; ++l)
+#pragma unroll
+        for (int j = 0; j < kTopK; ++j) topk_insert(tv, tc, lv[(l * 256 + ml) * kTopK + j], lc[(l * 256 + ml) * kTopK + j]);
+      if (p.ws_hdr != nullptr && row_ok) {
+        uint64_t* slots = p.ws_slots + (size_t)strip * p.tiles_n * (256 * 2 * kTopK) + (size_t)ml * 2 * kTopK;
+#pragma unroll
+        for (int j = 0; j < kTopK; ++j) {
+          publish(slots + (size_t)tn * (256 * 2 * kTopK) + j, tv[j], tag);
+          publish(slots + (size_t)tn * (256 * 2 * kTopK) + kTopK + j, __int_as_float(tc[j]), tag);
+        }
+        // the peers' lists go into this tile's own (the order of a total
+        // order's insertions does not change the result)
+        const uint64_t t0 = wall_clock64();
+        for (int tt = 0; tt < p.tiles_n; ++tt) {
+          if (tt != tn) {
+            float pv[kTopK];
+            int pc[kTopK];
+            const uint64_t* ps = slots + (size_t)tt * (256 * 2 * kTopK);
+            for (;;) {
+              bool all = true;
+#pragma unroll
+              for (int j = 0; j < 2 * kTopK; ++j) {
+                const uint64_t w = __hip_atomic_load(ps + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                all = all && (uint32_t)(w >> 32) == tag;
+                if (j < kTopK) pv[j] = __uint_as_float((uint32_t)w);
+                else pc[j - kTopK] = (int)(uint32_t)w;
+              }
+              if (all) break;
+              if (timed_out || wall_clock64() - t0 > p.spin_ticks) {   // recorded; the values are not used
+                timed_out = true;
+                break;
+              }
+              __builtin_amdgcn_s_sleep(2);
+            }
+#pragma unroll
+            for (int j = 0; j < kTopK; ++j) topk_insert(tv, tc, pv[j], pc[j]);
+          }
+        }
+      }
+      // the row's k largest, stored once per strip (column tile 0)
+      if (tn == 0 && row_ok) {
+        const int m = m0 + ml;
+#pragma unroll
+        for (int j = 0; j < kTopK; ++j) {
+          if (j < p.topk) {
+            p.row_index[(size_t)m * p.topk + j] = tc[j];
+            if (p.row_stats != nullptr) p.row_stats[(size_t)m * p.topk + j] = tv[j];
+          }
+        }
+      }
+    } else {
       const int ml = tid;
       const bool row_ok = m0 + ml < p.M;
       const float2 w0 = wpart[ml], w1 = wpart[256 + ml];
@@ -1066,8 +1180,8 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
       }
     });
   };
-  // argmax without a matrix output (the logits are never written)
-  if constexpr (ROW == 4) {
+  // argmax / top-k without a matrix output (the logits are never written)
+  if constexpr (ROW == 4 || ROW == 5) {
     if (p.C == nullptr && p.X == nullptr) return;
   }
   using X0 = std::integral_constant<int, 0>;

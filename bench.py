@@ -16,7 +16,7 @@ Prints one JSON line:
   cpu_baseline  the fp64 oracle timed on the host cores on a bounded row sample
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--store-x] [--causal] [--argmax]
-                       [--row2 softmax|layernorm|rmsnorm]
+                       [--row2 softmax|layernorm|rmsnorm] [--topk K]
 """
 from __future__ import annotations
 
@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--store-x", action="store_true",
                     help="GEMM + epilogue workloads: also store x, the input of the row operation, as a second "
                          "bf16 [M, N] output (e.g. the new residual stream of a pre-norm block)")
+    ap.add_argument("--topk", type=int, default=0, metavar="K",
+                    help="GEMM + epilogue workloads without a residual: replace the row operation by each row's "
+                         "K largest (columns and values; no logits written)")
     ap.add_argument("--argmax", action="store_true",
                     help="GEMM + epilogue workloads: replace the row operation by a row argmax and write no "
                          "[M, N] output (a greedy LM-head step)")
@@ -111,7 +114,7 @@ def flops_of(w, causal: bool = False) -> float:
     return 2.0 * d["batch"] * pairs * (d["K"] + d["N"])
 
 
-def bytes_of(w, store_x: bool = False, argmax: bool = False) -> float:
+def bytes_of(w, store_x: bool = False, argmax: bool = False, topk: int = 0) -> float:
     """Algorithmic HBM bytes: every input read once, the output (and X when
     stored) written once; an argmax writes only its index and maximum per row."""
     tot = 0.0
@@ -120,7 +123,7 @@ def bytes_of(w, store_x: bool = False, argmax: bool = False) -> float:
     d = w.dims
     out_es = 4 if w.params.get("out_dtype") == "f32" else 2
     if w.kind == "gemm_epilogue":
-        tot += d["M"] * 8 if argmax else d["M"] * d["N"] * out_es
+        tot += d["M"] * 8 * (topk or 1) if (argmax or topk) else d["M"] * d["N"] * out_es
         if store_x:
             tot += d["M"] * d["N"] * 2
     else:
@@ -132,11 +135,11 @@ def is_f32(w) -> bool:
     return any(t.dtype == "f32" for t in w.tensors if t.name == "A")
 
 
-def roofline_of(w, kernel_ms: float, store_x: bool = False, causal: bool = False, argmax: bool = False):
+def roofline_of(w, kernel_ms: float, store_x: bool = False, causal: bool = False, argmax: bool = False, topk: int = 0):
     """The roofline that bounds the kernel: HBM when the workload's flop/byte is
     below the ridge point (peak flops / HBM bandwidth), the MFMA peak above it.
     Returns (bound, unit, peak, achieved, intensity, ridge)."""
-    flops, nbytes = flops_of(w, causal), bytes_of(w, store_x, argmax)
+    flops, nbytes = flops_of(w, causal), bytes_of(w, store_x, argmax, topk)
     peak_flops = PEAK_F32_TFLOPS if is_f32(w) else PEAK_BF16_TFLOPS
     intensity = flops / nbytes
     ridge = peak_flops * 1e12 / (HBM_GBPS * 1e9)
@@ -145,7 +148,8 @@ def roofline_of(w, kernel_ms: float, store_x: bool = False, causal: bool = False
     return "mfma", "TFLOP/s", peak_flops, flops / (kernel_ms * 1e-3) / 1e12, intensity, ridge
 
 
-def make_call(w, dev, torch, cf, store_x: bool = False, causal: bool = False, argmax: bool = False, row2=None):
+def make_call(w, dev, torch, cf, store_x: bool = False, causal: bool = False, argmax: bool = False, row2=None,
+              topk: int = 0):
     """Device tensors + a closure launching one fused kernel on the current stream."""
     p = w.params
     out_dt = torch.float32 if p.get("out_dtype") == "f32" else torch.bfloat16
@@ -153,7 +157,13 @@ def make_call(w, dev, torch, cf, store_x: bool = False, causal: bool = False, ar
     if w.kind == "gemm_epilogue":
         d = w.dims
         X = torch.empty(d["M"], d["N"], dtype=torch.bfloat16, device="cuda") if store_x else None
-        if argmax:
+        if topk:
+            idx = torch.empty(d["M"], topk, dtype=torch.int32, device="cuda")
+            mx = torch.empty(d["M"], topk, dtype=torch.float32, device="cuda")
+            e = cf.make_epilogue(alpha=p["alpha"], bias=dev.get("bias"), act=p["act"], row_op="topk", topk=topk,
+                                 row_index=idx, row_stats=mx, x_out=X)
+            C = None
+        elif argmax:
             idx = torch.empty(d["M"], dtype=torch.int32, device="cuda")
             mx = torch.empty(d["M"], dtype=torch.float32, device="cuda")
             e = cf.make_epilogue(alpha=p["alpha"], bias=dev.get("bias"), residual=dev.get("residual"),
@@ -186,7 +196,7 @@ def make_call(w, dev, torch, cf, store_x: bool = False, causal: bool = False, ar
     return call, O, None, 0
 
 
-def cpu_baseline(w, raw, target_s: float, causal: bool = False, argmax: bool = False, row2=None):
+def cpu_baseline(w, raw, target_s: float, causal: bool = False, argmax: bool = False, row2=None, topk: int = 0):
     """The fp64 oracle on a bounded sample of rows (rows are independent)."""
     import oracle
     ncores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
@@ -205,7 +215,9 @@ def cpu_baseline(w, raw, target_s: float, causal: bool = False, argmax: bool = F
             A = widen("A")[:rows] if rows < d["M"] else widen("A")
             R = widen("residual")[:rows] if "residual" in raw else None
             g = vec.get("gamma", vec.get("weight"))
-            if argmax:
+            if topk:
+                oracle.gemm_epilogue_topk(A, B, topk, alpha=p["alpha"], bias=vec.get("bias"), act=p["act"])
+            elif argmax:
                 oracle.gemm_epilogue_argmax(A, B, alpha=p["alpha"], bias=vec.get("bias"), residual=R, act=p["act"])
             elif row2:
                 oracle.gemm_epilogue_two_stage(
@@ -279,6 +291,9 @@ def main():
         raise SystemExit("--store-x applies to the GEMM + epilogue workloads")
     if args.row2 and (w.kind != "gemm_epilogue" or args.argmax or w.params["row_op"] == "none"):
         raise SystemExit("--row2 applies to the GEMM + epilogue workloads with a row operation, without --argmax")
+    if args.topk and (w.kind != "gemm_epilogue" or "residual" in {t.name for t in w.tensors} or args.argmax
+                      or args.row2 or not 1 <= args.topk <= 8):
+        raise SystemExit("--topk K (1..8) applies to the GEMM + epilogue workloads without a residual, alone")
     if args.argmax and w.kind != "gemm_epilogue":
         raise SystemExit("--argmax applies to the GEMM + epilogue workloads")
     if args.causal and (w.kind != "b2bgemm" or w.params["row_op"] != "softmax"):
@@ -300,7 +315,8 @@ def main():
     devs = [dev] + [{k: v.clone() for k, v in dev.items()} for _ in range(nset - 1)]
     calls = []
     for d_ in devs:
-        call, out, ws, ws_bytes = make_call(w, d_, torch, cf, args.store_x, args.causal, args.argmax, args.row2)
+        call, out, ws, ws_bytes = make_call(w, d_, torch, cf, args.store_x, args.causal, args.argmax, args.row2,
+                                            args.topk)
         calls.append(call)
 
     # settle: batches of calls (grown to ~20 ms each) until --settle-s has passed
@@ -337,9 +353,10 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     in_f32 = is_f32(w)
     bound, unit, peak, achieved, intensity, ridge = roofline_of(w, kernel_ms, args.store_x, args.causal,
-                                                                args.argmax)
+                                                                args.argmax, args.topk)
     traffic = None
-    if os.path.exists(args.traffic) and not (args.plain or args.store_x or args.causal or args.argmax or args.row2):
+    if os.path.exists(args.traffic) and not (args.plain or args.store_x or args.causal or args.argmax or args.row2
+                                             or args.topk):
         try:
             rec = json.load(open(args.traffic))
             if rec.get("kernel_source_hash") == kernel_source_hash():
@@ -362,19 +379,20 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name + ("/identity-epilogue" if args.plain else "")
                    + ("+x_out" if args.store_x else "") + ("/causal" if args.causal else "")
-                   + ("/argmax" if args.argmax else "") + (f"/then-{args.row2}" if args.row2 else ""), **w.dims,
+                   + ("/argmax" if args.argmax else "") + (f"/then-{args.row2}" if args.row2 else "")
+                   + (f"/top-{args.topk}" if args.topk else ""), **w.dims,
                    "out_dtype": w.params.get("out_dtype"), "input_sets": nset, "input_bytes_per_set": in_bytes},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "arithmetic_intensity": round(intensity, 1), "ridge": round(ridge, 1)},
         "kernel_ms": round(kernel_ms, 4),
-        "algorithmic_bytes": bytes_of(w, args.store_x, args.argmax),
+        "algorithmic_bytes": bytes_of(w, args.store_x, args.argmax, args.topk),
         "intermediate_hbm_bytes": 0,
         "workspace_bytes": ws_bytes,
     }
     if not args.no_cpu_baseline:
         del dev, devs, calls, out
-        line["cpu_baseline"] = cpu_baseline(w, raw, args.cpu_seconds, args.causal, args.argmax, args.row2)
+        line["cpu_baseline"] = cpu_baseline(w, raw, args.cpu_seconds, args.causal, args.argmax, args.row2, args.topk)
     print(json.dumps(line), flush=True)
 
 

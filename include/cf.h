@@ -56,11 +56,18 @@ typedef enum {
   CF_ROW_LAYERNORM = 2, /* y = (x - mean) / sqrt(var + eps) * gamma[n] + beta[n]; var is
                            the biased (1/N) variance; gamma/beta optional (NULL = 1 / 0) */
   CF_ROW_RMSNORM = 3,   /* y = x / sqrt(mean_n x^2 + eps) * gamma[n]; gamma optional     */
-  CF_ROW_ARGMAX = 4     /* cf_gemm_epilogue only: row_index[m] = the smallest n with
+  CF_ROW_ARGMAX = 4,    /* cf_gemm_epilogue only: row_index[m] = the smallest n with
                            x[m, n] = max_n x[m, n] (NaN never wins), row_stats[m] (if
                            given) = that maximum; y = x is stored only when C != NULL
                            (C may be NULL: the logits of a greedy LM head are never
                            written). gamma and beta must be NULL.                      */
+  CF_ROW_TOPK = 5       /* cf_gemm_epilogue only: the topk (1..8, <= N) largest x of
+                           each row, largest first, equal values by column ascending
+                           (NaN never enters; topk = 1 is CF_ROW_ARGMAX):
+                           row_index[m * topk + j] = their columns, row_stats[m * topk
+                           + j] (if given) = their values. C as for argmax (may be
+                           NULL). gamma, beta and residual must be NULL; fast-path
+                           layouts only (CF_ERR_UNSUPPORTED otherwise).             */
 } cf_row_op;
 
 /* Visibility mask on the scores S of cf_b2bgemm's softmax (ignored nowhere:
@@ -149,6 +156,7 @@ typedef struct cf_epilogue {
   const void* gamma2;       /* its LayerNorm gamma / RMSNorm weight, N of vec_dtype, or NULL */
   const void* beta2;        /* its LayerNorm beta, or NULL                               */
   float eps2;
+  int32_t topk;             /* CF_ROW_TOPK: k (1..8); 0 otherwise                  */
 } cf_epilogue;
 
 /* Fills *epi with the identity epilogue (alpha 1, no bias/residual/act/row op). */

@@ -109,7 +109,6 @@ def epi(**kw):
     (dict(epi=epi(row_op=4, row_index=PW + 2)), cf.CF_ERR_INVALID_ARGUMENT),
     (dict(epi=epi(row_op=4, row_index=PW, gamma=PB)), cf.CF_ERR_INVALID_ARGUMENT),
     (dict(epi=epi(row_op=1, row_index=PW)), cf.CF_ERR_INVALID_ARGUMENT),   # row_index belongs to argmax
-    (dict(epi=epi(row_op=5)), cf.CF_ERR_INVALID_ARGUMENT),
     (dict(C=None, epi=epi(row_op=3)), cf.CF_ERR_INVALID_ARGUMENT),    # only argmax may omit C
     (dict(epi=epi(row_op=2, row_stats=PW + 1)), cf.CF_ERR_INVALID_ARGUMENT),
     (dict(epi=epi(row_op2=1)), cf.CF_ERR_INVALID_ARGUMENT),           # a second stage needs a first
@@ -122,6 +121,15 @@ def epi(**kw):
     (dict(epi=epi(row_op=2, row_op2=2, eps2=-1.0)), cf.CF_ERR_INVALID_ARGUMENT),
     (dict(epi=epi(row_op=2, row_op2=2, gamma2=PB + 1)), cf.CF_ERR_INVALID_ARGUMENT),   # misaligned bf16
     (dict(K=60, epi=epi(row_op=2, row_op2=1)), cf.CF_ERR_UNSUPPORTED),   # two stages: fast-path layouts only
+    (dict(epi=epi(row_op=5, topk=4)), cf.CF_ERR_INVALID_ARGUMENT),            # top-k needs row_index
+    (dict(epi=epi(row_op=5, row_index=PW, topk=0)), cf.CF_ERR_INVALID_ARGUMENT),
+    (dict(epi=epi(row_op=5, row_index=PW, topk=9)), cf.CF_ERR_INVALID_ARGUMENT),   # k <= 8
+    (dict(N=4, ldb=4, ldc=4, epi=epi(row_op=5, row_index=PW, topk=5)), cf.CF_ERR_INVALID_ARGUMENT),   # k <= N
+    (dict(epi=epi(row_op=5, row_index=PW, topk=4, gamma=PB)), cf.CF_ERR_INVALID_ARGUMENT),
+    (dict(epi=epi(row_op=5, row_index=PW, topk=4, residual=PW, ld_residual=64)), cf.CF_ERR_UNSUPPORTED),
+    (dict(K=60, epi=epi(row_op=5, row_index=PW, topk=4)), cf.CF_ERR_UNSUPPORTED),   # fast-path layouts only
+    (dict(epi=epi(row_op=2, topk=4)), cf.CF_ERR_INVALID_ARGUMENT),            # topk belongs to CF_ROW_TOPK
+    (dict(epi=epi(row_op=6)), cf.CF_ERR_INVALID_ARGUMENT),
     (dict(M=0), cf.CF_OK),            # empty problems launch nothing
     (dict(N=0), cf.CF_OK),
 ])
@@ -157,6 +165,7 @@ def b2b(batch=1, M=64, K=64, L=64, N=64, A=PA, lda=64, sa=0, B0=PB, ldb0=64, sb0
     (dict(mid=epi(row_op=1, mask=2)), cf.CF_ERR_INVALID_ARGUMENT),
     (dict(mid=epi(row_op=4, row_index=PW)), cf.CF_ERR_UNSUPPORTED),   # argmax between two GEMMs
     (dict(mid=epi(row_op=1, row_op2=2)), cf.CF_ERR_UNSUPPORTED),      # one row stage between two GEMMs
+    (dict(mid=epi(row_op=5, row_index=PW, topk=2)), cf.CF_ERR_UNSUPPORTED),   # top-k between two GEMMs
     (dict(batch=0), cf.CF_OK),
 ])
 def test_b2bgemm_argument_checks(kw, status):
@@ -169,6 +178,9 @@ def test_workspace_sizes():
     assert cf.cf_gemm_epilogue_workspace_size(16384, 4096, 11008, epi(row_op=3)) == 512 + 64 * 16 * 256 * 16
     assert cf.cf_gemm_epilogue_workspace_size(8192, 256, 4096, e) == 0        # one column tile per strip
     assert cf.cf_gemm_epilogue_workspace_size(8192, 4096, 4096, epi()) == 0   # no row op
+    # top-k exchanges 8 (value, column) pairs per row
+    assert cf.cf_gemm_epilogue_workspace_size(8192, 4096, 4096, epi(row_op=5, row_index=PW, topk=4)) == \
+        512 + 32 * 16 * 256 * 16 * 8
     # a second row stage exchanges through a second set of slots
     assert cf.cf_gemm_epilogue_workspace_size(8192, 4096, 4096, epi(row_op=2, row_op2=1)) == \
         512 + 2 * 32 * 16 * 256 * 16

@@ -527,6 +527,83 @@ def test_argmax_general_path_with_logits(shape):
     P.assert_close(P.gpu_to_f64(C), X, P.REL_F_BF16, P.MAX_ABS_BF16, f"argmax {shape}: C = x")
 
 
+def run_topk(A, B, k, with_c, **epi):
+    M, N = A.shape[0], B.shape[1]
+    idx = torch.full((M, k), -1, dtype=torch.int32, device="cuda")
+    val = torch.full((M, k), float("nan"), dtype=torch.float32, device="cuda")
+    e = cf.make_epilogue(row_op="topk", topk=k, row_index=idx, row_stats=val, **epi)
+    ws = _WS.get(cf.cf_gemm_epilogue_workspace_size(M, N, A.shape[1], e))
+    C = torch.empty(M, N, dtype=torch.float32, device="cuda") if with_c else None
+    cf.cf_gemm_epilogue(A, B, C, epi=e, workspace=ws)
+    torch.cuda.synchronize()
+    if ws is not None:
+        assert cf.cf_workspace_status(ws) == cf.CF_OK
+    return idx, val, C
+
+
+def check_topk(idx, val, X, k, what):
+    """The k values match the oracle's rank by rank; the columns are the
+    oracle's wherever the k + 1 largest values of the row are separated by more
+    than the fp32 rounding bound, and otherwise distinct columns whose exact
+    values lie within that bound of the oracle's value of the same rank."""
+    oi, ov = oracle.row_topk(X, k)
+    gi = idx.cpu().numpy().astype(np.int64)
+    P.assert_close(P.gpu_to_f64(val), ov, 1e-5, 1e-4, what + " values")
+    tol = 1e-4 * max(1.0, float(np.abs(X).max()))
+    assert np.all((gi >= 0) & (gi < X.shape[1])), what + ": column out of range"
+    assert all(len(set(r)) == k for r in gi.tolist()), what + ": repeated column"
+    rows = np.arange(X.shape[0])[:, None]
+    assert np.all(np.abs(X[rows, gi] - ov) <= tol), what + ": a chosen column is not of its rank"
+    srt = -np.sort(-X, axis=1)[:, :min(k + 1, X.shape[1])]
+    sep = np.all(np.abs(np.diff(srt, axis=1)) > tol, axis=1)
+    bad = int((gi[sep] != oi[sep]).any(axis=1).sum())
+    assert bad == 0, f"{what}: {bad} rows with separated values disagree"
+
+
+@pytest.mark.parametrize("k", [1, 4, 8])
+@pytest.mark.parametrize("N", [256, 1000, 4096])
+def test_topk(N, k):
+    # one column tile per strip (no exchange), four with a ragged one, sixteen
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=41, M=300, N=N, K=256)
+    X = oracle.elementwise_stage(oracle.matmul(ref["A"], ref["B"]))
+    idx, val, _ = run_topk(dev["A"], dev["B"], k, False)
+    check_topk(idx, val, X, k, f"top-{k} N={N}")
+
+
+def test_topk_with_logits_bias_relu():
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=42, M=300, N=1000, K=256)
+    bias = torch.linspace(-0.3, 0.3, 1000, device="cuda").to(torch.bfloat16)
+    X = oracle.elementwise_stage(oracle.matmul(ref["A"], ref["B"]), 0.5, P.gpu_to_f64(bias), None, "relu")
+    idx, val, C = run_topk(dev["A"], dev["B"], 5, True, alpha=0.5, bias=bias, act="relu")
+    check_topk(idx, val, X, 5, "top-5 of relu logits")
+    P.assert_close(P.gpu_to_f64(C), X, P.REL_F_BF16, P.MAX_ABS_BF16, "top-5: C = x")
+
+
+def test_topk_exact_ties_across_tiles():
+    # five equal columns (duplicated B columns, equal bias) that are the row
+    # maximum in every row: the top-3 are the three lowest of them, in order
+    M, N, K = 256, 4096, 256
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=43, M=M, N=N, K=K)
+    cols = (5, 700, 3000, 3001, 4095)
+    B = dev["B"].clone()
+    for c in cols[1:]:
+        B[:, c] = B[:, cols[0]]
+    bias = torch.zeros(N, device="cuda").to(torch.bfloat16)
+    bias[list(cols)] = 50.0
+    idx, val, _ = run_topk(dev["A"], B, 3, False, bias=bias)
+    got = idx.cpu().numpy()
+    assert np.all(got == np.array(cols[:3])[None, :]), got[:4]
+    v = val.cpu().numpy()
+    assert np.all(v[:, 0] == v[:, 1]) and np.all(v[:, 1] == v[:, 2])
+
+
+def test_topk_one_is_argmax():
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=44, M=300, N=1000, K=256)
+    i1, v1, _ = run_topk(dev["A"], dev["B"], 1, False)
+    ia, va, _ = run_argmax(dev["A"], dev["B"], False)
+    assert torch.equal(i1[:, 0], ia) and torch.equal(v1[:, 0], va)
+
+
 @pytest.mark.parametrize("N,cols", [(4096, (5, 700, 3000)), (300, (7, 260, 299))])
 def test_argmax_exact_ties_across_tiles(N, cols):
     # equal columns of B and equal bias give bit-identical x in every row; a large

@@ -196,8 +196,11 @@ def row_argmax(X: np.ndarray):
     """(index, value) of each row: the smallest column n with X[m, n] equal to
     the row maximum, and that maximum (the review's "Reading between the lines"
     names max for top-k among the single-axis reductions the strip argument
-    covers; top-1 here, ties to the lowest column)."""
-    idx = np.argmax(X, axis=-1)
+    covers; top-1 here, ties to the lowest column). A NaN ranks as -inf: it
+    never wins over a number, and a row of NaN and -inf only gives column 0."""
+    X = np.asarray(X, np.float64)
+    key = np.where(np.isnan(X), -np.inf, X)
+    idx = np.argmax(key, axis=-1)
     return idx, np.take_along_axis(X, idx[..., None], axis=-1)[..., 0]
 
 
@@ -205,8 +208,8 @@ def row_topk(X: np.ndarray, k: int):
     """(index, value) of each row's k largest entries, largest first: the
     review's "Reading between the lines" names top-k among the single-axis
     reductions the strip argument covers. Order: value descending, and among
-    equal values the smaller column first (so k = 1 is row_argmax); NaN never
-    enters. Returns int64 [..., k] and float64 [..., k]."""
+    equal values the smaller column first (so k = 1 is row_argmax); a NaN ranks
+    as -inf at its own column. Returns int64 [..., k] and float64 [..., k]."""
     X = np.asarray(X, np.float64)
     n = X.shape[-1]
     if not 1 <= k <= n:

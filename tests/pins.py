@@ -337,6 +337,9 @@ def pin_row_topk(o):
     assert int(ti[0, 0]) == int(ai[0]) == 1 and tv[0, 0] == av[0] == 3.0
     ti, tv = o.row_topk(np.array([[np.nan, 2.0, 5.0, 2.0]]), 3)
     assert [int(v) for v in ti[0]] == [2, 1, 3]
+    # NaN ranks as -inf at its own column: behind every number, level with -inf
+    ti, tv = o.row_topk(np.array([[-np.inf, np.nan, 1.0, -np.inf, np.inf]]), 5)
+    assert [int(v) for v in ti[0]] == [4, 2, 0, 1, 3]
 
 
 # --------------------------------------------------------------------------- back-to-back GEMM
@@ -558,6 +561,11 @@ def pin_row_argmax(o):
     i0, v0 = o.row_argmax(np.full((1, 5), 2.5))
     i1, v1 = o.row_argmax(np.arange(6.0)[None, :])
     assert int(i0[0]) == 0 and v0[0] == 2.5 and int(i1[0]) == 5 and v1[0] == 5.0
+    # NaN ranks as -inf: it never beats a number, and rows of NaN and -inf
+    # alone give their first column
+    ni, _ = o.row_argmax(np.array([[np.nan, 2.0, 5.0, 5.0], [np.nan, np.nan, np.nan, np.nan],
+                                   [-np.inf, np.nan, -np.inf, -np.inf], [1.0, np.nan, np.inf, np.nan]]))
+    assert [int(v) for v in ni] == [2, 0, 0, 2], list(ni)
 
 
 ALL_PINS = [pin_round_bf16, pin_widen_bf16, pin_matmul_exact, pin_stage1_exact, pin_softmax,

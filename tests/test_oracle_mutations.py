@@ -74,9 +74,10 @@ MUTATIONS = {
     "b2b_lse_ignores_alpha": [(
         "    S = float(alpha) * matmul(A, B0)\n", "    S = matmul(A, B0)\n")],
     "argmax_ties_to_last_column": [(
-        "    idx = np.argmax(X, axis=-1)\n",
-        "    idx = X.shape[-1] - 1 - np.argmax(X[..., ::-1], axis=-1)\n")],
-    "argmax_is_argmin": [("    idx = np.argmax(X, axis=-1)\n", "    idx = np.argmin(X, axis=-1)\n")],
+        "    idx = np.argmax(key, axis=-1)\n",
+        "    idx = X.shape[-1] - 1 - np.argmax(key[..., ::-1], axis=-1)\n")],
+    "argmax_is_argmin": [("    idx = np.argmax(key, axis=-1)\n", "    idx = np.argmin(key, axis=-1)\n")],
+    "argmax_nan_wins": [("    idx = np.argmax(key, axis=-1)\n", "    idx = np.argmax(X, axis=-1)\n")],
     "two_stage_second_on_x": [(
         "    return row_stage(Y, row_op2, gamma2, beta2, eps2)\n",
         "    return row_stage(X, row_op2, gamma2, beta2, eps2)\n")],
@@ -95,6 +96,9 @@ MUTATIONS = {
     "topk_ascending": [(
         '    idx = np.argsort(-key, axis=-1, kind="stable")[..., :k]\n',
         '    idx = np.argsort(key, axis=-1, kind="stable")[..., :k]\n')],
+    "topk_nan_not_ranked_as_minus_inf": [(
+        '    idx = np.argsort(-key, axis=-1, kind="stable")[..., :k]\n',
+        '    idx = np.argsort(-X, axis=-1, kind="stable")[..., :k]\n')],
     "topk_one_short": [(
         '    idx = np.argsort(-key, axis=-1, kind="stable")[..., :k]\n',
         '    idx = np.argsort(-key, axis=-1, kind="stable")[..., :max(k - 1, 1)]\n')],

@@ -408,19 +408,65 @@ __device__ inline void acc_read4(const f32x16_t& blk, float tok, float (&v)[4]) 
       : "a"(blk[4 * Q]), "a"(blk[4 * Q + 1]), "a"(blk[4 * Q + 2]), "a"(blk[4 * Q + 3]), "v"(tok));
 }
 
-// Top-k list of kTopK (value, column) pairs sorted by value descending, equal
-// values by column ascending; insert one candidate (NaN never enters).
+// Top-k lists: kTopK (value, column) pairs sorted by value descending, equal
+// values by column ascending. An empty entry is (-inf, kNoColumn); it ranks
+// below every real entry, -inf included. NaN is mapped to -inf by the caller.
 constexpr int kTopK = 8;
-__device__ inline void topk_insert(float (&tv)[kTopK], int (&tc)[kTopK], float cv, int cc) {
+constexpr int kNoColumn = 0x7fffffff;
+
+// Inserts a candidate whose column is larger than every column the list holds
+// (a lane visits its columns in increasing order), so an equal value never
+// moves ahead. Once it is in, every later entry moves down one place (the
+// entry carried down ranks before the next one even where their values are
+// equal). kMaybeEmpty: the list may still hold empty entries, which any
+// candidate with a column displaces. Selects only: no branches.
+template <bool kMaybeEmpty>
+__device__ inline void topk_insert_next(float (&tv)[kTopK], int (&tc)[kTopK], float cv, int cc) {
+  bool in = false;
 #pragma unroll
   for (int j = 0; j < kTopK; ++j) {
-    const bool gt = cv > tv[j] || (cv == tv[j] && cc < tc[j]);
+    bool gt = in | (cv > tv[j]);
+    if constexpr (kMaybeEmpty) gt = gt | (tc[j] == kNoColumn);
+    in = gt;
     const float v0 = tv[j];
     const int c0 = tc[j];
     tv[j] = gt ? cv : v0;
     tc[j] = gt ? cc : c0;
     cv = gt ? v0 : cv;
     cc = gt ? c0 : cc;
+  }
+}
+
+// (va, ca) ranks before (vb, cb): larger value, or equal value and smaller column.
+__device__ inline bool topk_before(float va, int ca, float vb, int cb) {
+  return (va > vb) | ((va == vb) & (ca < cb));
+}
+
+// Merges list (bv, bc) into (tv, tc), keeping the kTopK best of the union: the
+// elementwise better of a[i] and b[kTopK-1-i] is the union's best kTopK as a
+// bitonic sequence, which three half-cleaner stages sort.
+__device__ inline void topk_merge(float (&tv)[kTopK], int (&tc)[kTopK], const float (&bv)[kTopK],
+                                  const int (&bc)[kTopK]) {
+#pragma unroll
+  for (int i = 0; i < kTopK; ++i) {
+    const bool b = topk_before(bv[kTopK - 1 - i], bc[kTopK - 1 - i], tv[i], tc[i]);
+    tv[i] = b ? bv[kTopK - 1 - i] : tv[i];
+    tc[i] = b ? bc[kTopK - 1 - i] : tc[i];
+  }
+#pragma unroll
+  for (int d = kTopK / 2; d > 0; d >>= 1) {
+#pragma unroll
+    for (int i = 0; i < kTopK; ++i) {
+      if ((i & d) == 0) {
+        const bool sw = topk_before(tv[i + d], tc[i + d], tv[i], tc[i]);
+        const float v0 = tv[i], v1 = tv[i + d];
+        const int c0 = tc[i], c1 = tc[i + d];
+        tv[i] = sw ? v1 : v0;
+        tc[i] = sw ? c1 : c0;
+        tv[i + d] = sw ? v0 : v1;
+        tc[i + d] = sw ? c0 : c1;
+      }
+    }
   }
 }
 
@@ -476,7 +522,8 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
     vgamma[tid] = (p.gamma && ok) ? load_vec(p.gamma, n, p.vec_f32) : 1.0f;
     vbeta[tid] = (p.beta && ok) ? load_vec(p.beta, n, p.vec_f32) : 0.0f;
   }
-  const bool has_res = p.residual != nullptr;
+  // top-k takes no residual (its lists use the residual staging area)
+  const bool has_res = ROW != 5 && p.residual != nullptr;
   const __amdgpu_buffer_rsrc_t rsR = make_rsrc(p.residual, has_res ? p.r_bytes : 0u);
   if (kFast && has_res) {
     // stage the bf16 residual tile [256][256] in LDS with coalesced 16-byte loads;
@@ -627,14 +674,15 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
         });
         a = sum_halves(s2);
       } else if constexpr (ROW == 5) {
-        // top-k: a lane inserts its columns into a sorted list of kTopK, which
-        // goes to LDS (the residual staging area: top-k takes no residual)
+        // top-k: a lane inserts its columns, in increasing order, into a sorted
+        // list of kTopK, which goes to LDS (the residual staging area: top-k
+        // takes no residual)
         float tv[kTopK];
         int tc[kTopK];
 #pragma unroll
         for (int j = 0; j < kTopK; ++j) {
           tv[j] = -INFINITY;
-          tc[j] = 0x7fffffff;
+          tc[j] = kNoColumn;
         }
         for_groups([&](int nb, auto qc) {
           constexpr int q = decltype(qc)::value;
@@ -643,7 +691,13 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const bool ok = valid(nb, q, e);
-            topk_insert(tv, tc, ok ? x[e] : -INFINITY, ok ? n0 + wn * 128 + nb * 32 + 8 * q + 4 * h + e : 0x7fffffff);
+            // NaN ranks as -inf; a column past N stays out
+            const float cv = ok ? fmaxf(x[e], -INFINITY) : -INFINITY;
+            const int cc = ok ? n0 + wn * 128 + nb * 32 + 8 * q + 4 * h + e : kNoColumn;
+            // empty entries remain only among the first kTopK candidates (past
+            // those, only columns beyond N, which come last, leave entries empty)
+            if (nb * 16 + q * 4 + e < kTopK) topk_insert_next<true>(tv, tc, cv, cc);
+            else topk_insert_next<false>(tv, tc, cv, cc);
           }
           tok = tv[kTopK - 1];
         });
@@ -660,19 +714,26 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
         }
       } else {
         // argmax: a lane visits its columns in increasing order, so a strict >
-        // keeps the first of equal values; the lane halves interleave and are
-        // merged with the column as tie-break (b holds the column's bits)
+        // keeps the first of equal values; its first column is taken whatever
+        // its value (NaN ranks as -inf), so a row of -inf still names a column.
+        // The lane halves interleave and are merged with the column as
+        // tie-break (b holds the column's bits)
         float mx = -INFINITY;
-        int ix = 0x7fffffff;
+        int ix = kNoColumn;
         for_groups([&](int nb, auto qc) {
           constexpr int q = decltype(qc)::value;
           float x[4];
           xgroup(mb, nb, qc, bias4(nb, q), tok, x);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            if (valid(nb, q, e) && x[e] > mx) {
-              mx = x[e];
-              ix = n0 + wn * 128 + nb * 32 + 8 * q + 4 * h + e;
+            const float xv = fmaxf(x[e], -INFINITY);
+            const int c = n0 + wn * 128 + nb * 32 + 8 * q + 4 * h + e;
+            if (nb == 0 && q == 0 && e == 0) {   // columns past N come last
+              mx = valid(nb, q, e) ? xv : -INFINITY;
+              ix = valid(nb, q, e) ? c : kNoColumn;
+            } else if (valid(nb, q, e) && xv > mx) {
+              mx = xv;
+              ix = c;
             }
           }
           tok = mx;
@@ -692,8 +753,10 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
     // level 3) exchange with the other column tiles of the strip and merge all
     // of them in tile order
     if constexpr (ROW == 5) {
-      // top-k: merge the two waves' lists, then the strip's: every tile
-      // publishes its list (16 tagged words per row) and merges all of them
+      // top-k: merge the four lists of the tile (two lane halves of two
+      // waves), then the strip's: column tile 0 stores the result, so the
+      // other tiles publish their lists (16 tagged words per row) and go on,
+      // and tile 0 merges them all
       const int ml = tid;
       const bool row_ok = m0 + ml < p.M;
       const float* lv = (const float*)(smem + kOffRes);
@@ -705,22 +768,27 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
         tv[j] = lv[ml * kTopK + j];
         tc[j] = lc[ml * kTopK + j];
       }
-      // the other lane half and the other wave's two halves
-      for (int l = 1; l < 4; ++l)
-#pragma unroll
-        for (int j = 0; j < kTopK; ++j) topk_insert(tv, tc, lv[(l * 256 + ml) * kTopK + j], lc[(l * 256 + ml) * kTopK + j]);
-      if (p.ws_hdr != nullptr && row_ok) {
-        uint64_t* slots = p.ws_slots + (size_t)strip * p.tiles_n * (256 * 2 * kTopK) + (size_t)ml * 2 * kTopK;
+      for (int l = 1; l < 4; ++l) {
+        float bv[kTopK];
+        int bc[kTopK];
 #pragma unroll
         for (int j = 0; j < kTopK; ++j) {
-          publish(slots + (size_t)tn * (256 * 2 * kTopK) + j, tv[j], tag);
-          publish(slots + (size_t)tn * (256 * 2 * kTopK) + kTopK + j, __int_as_float(tc[j]), tag);
+          bv[j] = lv[(l * 256 + ml) * kTopK + j];
+          bc[j] = lc[(l * 256 + ml) * kTopK + j];
         }
-        // the peers' lists go into this tile's own (the order of a total
-        // order's insertions does not change the result)
-        const uint64_t t0 = wall_clock64();
-        for (int tt = 0; tt < p.tiles_n; ++tt) {
-          if (tt != tn) {
+        topk_merge(tv, tc, bv, bc);
+      }
+      if (p.ws_hdr != nullptr && row_ok) {
+        uint64_t* slots = p.ws_slots + (size_t)strip * p.tiles_n * (256 * 2 * kTopK) + (size_t)ml * 2 * kTopK;
+        if (tn != 0) {
+#pragma unroll
+          for (int j = 0; j < kTopK; ++j) {
+            publish(slots + (size_t)tn * (256 * 2 * kTopK) + j, tv[j], tag);
+            publish(slots + (size_t)tn * (256 * 2 * kTopK) + kTopK + j, __int_as_float(tc[j]), tag);
+          }
+        } else {
+          const uint64_t t0 = wall_clock64();
+          for (int tt = 1; tt < p.tiles_n; ++tt) {
             float pv[kTopK];
             int pc[kTopK];
             const uint64_t* ps = slots + (size_t)tt * (256 * 2 * kTopK);
@@ -729,7 +797,7 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
 #pragma unroll
               for (int j = 0; j < 2 * kTopK; ++j) {
                 const uint64_t w = __hip_atomic_load(ps + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                all = all && (uint32_t)(w >> 32) == tag;
+                all = all & ((uint32_t)(w >> 32) == tag);
                 if (j < kTopK) pv[j] = __uint_as_float((uint32_t)w);
                 else pc[j - kTopK] = (int)(uint32_t)w;
               }
@@ -740,8 +808,7 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
               }
               __builtin_amdgcn_s_sleep(2);
             }
-#pragma unroll
-            for (int j = 0; j < kTopK; ++j) topk_insert(tv, tc, pv[j], pc[j]);
+            topk_merge(tv, tc, pv, pc);
           }
         }
       }
@@ -842,7 +909,7 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
               chan_merge(rn, ra, rb, (float)min(kGemmBN, p.N - tt * kGemmBN), va[j], vb[j]);
             } else if constexpr (ROW == 3) {
               ra += va[j];
-            } else if (va[j] > ra) {   // argmax: tiles in column order, so ties keep the smaller column
+            } else if (tt == 0 || va[j] > ra) {   // argmax: tiles in column order, so ties keep the smaller column
               ra = va[j];
               rb = vb[j];
             }

@@ -57,13 +57,15 @@ typedef enum {
                            the biased (1/N) variance; gamma/beta optional (NULL = 1 / 0) */
   CF_ROW_RMSNORM = 3,   /* y = x / sqrt(mean_n x^2 + eps) * gamma[n]; gamma optional     */
   CF_ROW_ARGMAX = 4,    /* cf_gemm_epilogue only: row_index[m] = the smallest n with
-                           x[m, n] = max_n x[m, n] (NaN never wins), row_stats[m] (if
-                           given) = that maximum; y = x is stored only when C != NULL
+                           x[m, n] = max_n x[m, n], a NaN ranking as -inf (a row of
+                           NaN and -inf gives 0), row_stats[m] (if given) = that
+                           maximum (-inf for a NaN); y = x is stored only when C != NULL
                            (C may be NULL: the logits of a greedy LM head are never
                            written). gamma and beta must be NULL.                      */
   CF_ROW_TOPK = 5       /* cf_gemm_epilogue only: the topk (1..8, <= N) largest x of
                            each row, largest first, equal values by column ascending
-                           (NaN never enters; topk = 1 is CF_ROW_ARGMAX):
+                           (a NaN ranks as -inf at its own column and is reported
+                           as -inf; topk = 1 is CF_ROW_ARGMAX):
                            row_index[m * topk + j] = their columns, row_stats[m * topk
                            + j] (if given) = their values. C as for argmax (may be
                            NULL). gamma, beta and residual must be NULL; fast-path

@@ -597,6 +597,59 @@ def test_topk_exact_ties_across_tiles():
     assert np.all(v[:, 0] == v[:, 1]) and np.all(v[:, 1] == v[:, 2])
 
 
+def test_topk_nonfinite():
+    # +inf bias columns rank first, in column order; a NaN row ranks every
+    # column as -inf, so its top-k are the lowest columns with value -inf; a row
+    # whose only finite values are two columns fills the rest with the lowest
+    # -inf columns (empty list entries must give way to real -inf ones, across
+    # lanes and column tiles, with a ragged last tile)
+    M, N, K = 256, 1000, 256
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=45, M=M, N=N, K=K)
+    A = dev["A"].clone()
+    A[7] = float("nan")
+    bias = torch.zeros(N, device="cuda", dtype=torch.float32)
+    bias[[3, 511, 998]] = float("inf")
+    idx, val, _ = run_topk(A, dev["B"], 3, False, bias=bias)
+    got, v = idx.cpu().numpy(), val.cpu().numpy()
+    others = np.arange(M) != 7
+    assert np.all(got[others] == np.array([3, 511, 998])[None, :]), got[:2]
+    assert np.all(v[others] == np.inf)
+    assert list(got[7]) == [0, 1, 2] and np.all(v[7] == -np.inf), (got[7], v[7])
+
+    bias = torch.full((N,), float("-inf"), device="cuda", dtype=torch.bfloat16)
+    bias[[17, 900]] = 0.0
+    idx, val, _ = run_topk(A, dev["B"], 5, False, bias=bias)
+    got, v = idx.cpu().numpy(), val.cpu().numpy()
+    Aref = ref["A"].copy()
+    Aref[7] = np.nan
+    X = oracle.elementwise_stage(oracle.matmul(Aref, ref["B"]), 1.0, P.gpu_to_f64(bias), None, "none")
+    oi, ov = oracle.row_topk(X, 5)
+    assert np.array_equal(got, oi), np.argwhere(got != oi)[:4]
+    fin = np.isfinite(ov)
+    assert np.all(np.abs(v[fin] - ov[fin]) <= 1e-4 * np.maximum(1.0, np.abs(ov[fin])))
+    assert np.all(v[~fin] == -np.inf)
+    assert list(got[7]) == [0, 1, 2, 3, 4]
+    assert all(sorted(r[:2]) == [17, 900] and list(r[2:]) == [0, 1, 2] for r in got[others])
+
+
+@pytest.mark.parametrize("N", [1000, 4096])
+def test_topk_relu_zero_ties(N):
+    # ReLU clamps all but two columns to exactly 0: the top-8 are those two,
+    # then the six lowest zero columns in column order (equal values behind an
+    # insertion keep their order within every lane's list)
+    M, K = 256, 256
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=47, M=M, N=N, K=K)
+    bias = torch.full((N,), -50.0, device="cuda", dtype=torch.bfloat16)
+    bias[[17, N - 100]] = 50.0
+    idx, val, _ = run_topk(dev["A"], dev["B"], 8, False, bias=bias, act="relu")
+    X = oracle.elementwise_stage(oracle.matmul(ref["A"], ref["B"]), 1.0, P.gpu_to_f64(bias), None, "relu")
+    oi, ov = oracle.row_topk(X, 8)
+    got = idx.cpu().numpy()
+    assert np.array_equal(got, oi), np.argwhere(got != oi)[:4]
+    assert all(list(r[2:]) == [0, 1, 2, 3, 4, 5] for r in got)
+    P.assert_close(P.gpu_to_f64(val), ov, 1e-5, 1e-4, "relu top-8 values")
+
+
 def test_topk_one_is_argmax():
     w, dev, ref = P.inputs("c2_gemm_layernorm", seed=44, M=300, N=1000, K=256)
     i1, v1, _ = run_topk(dev["A"], dev["B"], 1, False)
@@ -616,6 +669,32 @@ def test_argmax_exact_ties_across_tiles(N, cols):
     bias[list(cols)] = 50.0
     idx, val, _ = run_argmax(dev["A"], B, False, bias=bias)
     assert torch.all(idx == cols[0]), f"ties resolved to {torch.unique(idx).tolist()}"
+
+
+@pytest.mark.parametrize("N", [1000, 300])
+def test_argmax_nonfinite(N):
+    # a NaN row ranks every column as -inf and names column 0; with -inf bias
+    # on all but two columns the maximum is the larger of those two; with -inf
+    # everywhere every row names column 0 (never an out-of-range column)
+    M, K = 256, 256
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=46, M=M, N=N, K=K)
+    A = dev["A"].clone()
+    A[7] = float("nan")
+    Aref = ref["A"].copy()
+    Aref[7] = np.nan
+    bias = torch.full((N,), float("-inf"), device="cuda", dtype=torch.bfloat16)
+    bias[[17, N - 100]] = 0.0
+    idx, val, _ = run_argmax(A, dev["B"], False, bias=bias)
+    X = oracle.elementwise_stage(oracle.matmul(Aref, ref["B"]), 1.0, P.gpu_to_f64(bias), None, "none")
+    oi, ov = oracle.row_argmax(X)
+    got, v = idx.cpu().numpy(), val.cpu().numpy()
+    assert np.array_equal(got, oi), np.argwhere(got != oi)[:4]
+    assert got[7] == 0 and v[7] == -np.inf
+    fin = np.isfinite(ov)
+    assert np.all(np.abs(v[fin] - ov[fin]) <= 1e-4 * np.maximum(1.0, np.abs(ov[fin])))
+    bias[:] = float("-inf")
+    idx, val, _ = run_argmax(A, dev["B"], False, bias=bias)
+    assert torch.all(idx == 0) and torch.all(val == float("-inf"))
 
 
 def test_argmax_full_size_sampled_rows():

@@ -416,25 +416,28 @@ constexpr int kNoColumn = 0x7fffffff;
 
 // Inserts a candidate whose column is larger than every column the list holds
 // (a lane visits its columns in increasing order), so an equal value never
-// moves ahead. Once it is in, every later entry moves down one place (the
-// entry carried down ranks before the next one even where their values are
-// equal). kMaybeEmpty: the list may still hold empty entries, which any
-// candidate with a column displaces. Selects only: no branches.
+// moves ahead. Every position is updated at once from the old list: g[j] says
+// the candidate ranks before entry j (monotone in j), entry j becomes the
+// candidate where g[j] first holds and entry j-1 after that; its value is the
+// median of (old j, candidate, old j-1), which is that choice for a sorted
+// list. kMaybeEmpty: the list may still hold empty entries, which any
+// candidate with a column displaces. No branches and no chain through the
+// positions.
 template <bool kMaybeEmpty>
 __device__ inline void topk_insert_next(float (&tv)[kTopK], int (&tc)[kTopK], float cv, int cc) {
-  bool in = false;
+  bool g[kTopK];
 #pragma unroll
   for (int j = 0; j < kTopK; ++j) {
-    bool gt = in | (cv > tv[j]);
-    if constexpr (kMaybeEmpty) gt = gt | (tc[j] == kNoColumn);
-    in = gt;
-    const float v0 = tv[j];
-    const int c0 = tc[j];
-    tv[j] = gt ? cv : v0;
-    tc[j] = gt ? cc : c0;
-    cv = gt ? v0 : cv;
-    cc = gt ? c0 : cc;
+    g[j] = cv > tv[j];
+    if constexpr (kMaybeEmpty) g[j] = g[j] | (tc[j] == kNoColumn);
   }
+#pragma unroll
+  for (int j = kTopK - 1; j > 0; --j) {
+    tc[j] = g[j] ? (g[j - 1] ? tc[j - 1] : cc) : tc[j];
+    tv[j] = __builtin_amdgcn_fmed3f(tv[j], cv, tv[j - 1]);
+  }
+  tc[0] = g[0] ? cc : tc[0];
+  tv[0] = fmaxf(tv[0], cv);
 }
 
 // (va, ca) ranks before (vb, cb): larger value, or equal value and smaller column.
@@ -787,28 +790,54 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
             publish(slots + (size_t)tn * (256 * 2 * kTopK) + kTopK + j, __int_as_float(tc[j]), tag);
           }
         } else {
+          // the peers' lists, kPeers tiles at a time with all their loads in
+          // flight together, merged in tile order
+          constexpr int kPeers = 2;
           const uint64_t t0 = wall_clock64();
-          for (int tt = 1; tt < p.tiles_n; ++tt) {
-            float pv[kTopK];
-            int pc[kTopK];
-            const uint64_t* ps = slots + (size_t)tt * (256 * 2 * kTopK);
-            for (;;) {
-              bool all = true;
+          for (int tb = 1; tb < p.tiles_n; tb += kPeers) {
+            uint64_t w[kPeers][2 * kTopK];
+            uint32_t need = 0;
 #pragma unroll
-              for (int j = 0; j < 2 * kTopK; ++j) {
-                const uint64_t w = __hip_atomic_load(ps + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                all = all & ((uint32_t)(w >> 32) == tag);
-                if (j < kTopK) pv[j] = __uint_as_float((uint32_t)w);
-                else pc[j - kTopK] = (int)(uint32_t)w;
+            for (int i = 0; i < kPeers; ++i)
+              if (tb + i < p.tiles_n) need |= 1u << i;
+            const uint32_t have = need;
+            while (need) {
+#pragma unroll
+              for (int i = 0; i < kPeers; ++i) {
+                if (need & (1u << i)) {
+                  const uint64_t* ps = slots + (size_t)(tb + i) * (256 * 2 * kTopK);
+#pragma unroll
+                  for (int j = 0; j < 2 * kTopK; ++j)
+                    w[i][j] = __hip_atomic_load(ps + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
               }
-              if (all) break;
+#pragma unroll
+              for (int i = 0; i < kPeers; ++i) {
+                bool all = true;
+#pragma unroll
+                for (int j = 0; j < 2 * kTopK; ++j) all = all & ((uint32_t)(w[i][j] >> 32) == tag);
+                if (all) need &= ~(1u << i);
+              }
+              if (!need) break;
               if (timed_out || wall_clock64() - t0 > p.spin_ticks) {   // recorded; the values are not used
                 timed_out = true;
                 break;
               }
               __builtin_amdgcn_s_sleep(2);
             }
-            topk_merge(tv, tc, pv, pc);
+#pragma unroll
+            for (int i = 0; i < kPeers; ++i) {
+              if (have & (1u << i)) {
+                float pv[kTopK];
+                int pc[kTopK];
+#pragma unroll
+                for (int j = 0; j < kTopK; ++j) {
+                  pv[j] = __uint_as_float((uint32_t)w[i][j]);
+                  pc[j] = (int)(uint32_t)w[i][kTopK + j];
+                }
+                topk_merge(tv, tc, pv, pc);
+              }
+            }
           }
         }
       }

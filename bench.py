@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--b-nk", action="store_true",
+                    help="GEMM + epilogue with B stored [N, K] (the nn.Linear weight layout), b_is_nk")
     ap.add_argument("--plain", action="store_true",
                     help="diagnostic: same GEMM with the identity epilogue (not the headline workload)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
@@ -149,7 +151,7 @@ def roofline_of(w, kernel_ms: float, store_x: bool = False, causal: bool = False
 
 
 def make_call(w, dev, torch, cf, store_x: bool = False, causal: bool = False, argmax: bool = False, row2=None,
-              topk: int = 0):
+              topk: int = 0, b_nk: bool = False):
     """Device tensors + a closure launching one fused kernel on the current stream."""
     p = w.params
     out_dt = torch.float32 if p.get("out_dtype") == "f32" else torch.bfloat16
@@ -183,7 +185,7 @@ def make_call(w, dev, torch, cf, store_x: bool = False, causal: bool = False, ar
         ws = cf.Workspace("cuda").get(nbytes)
 
         def call():
-            cf.cf_gemm_epilogue(dev["A"], dev["B"], C, epi=e, workspace=ws, stream=stream)
+            cf.cf_gemm_epilogue(dev["A"], dev["B"], C, b_is_nk=b_nk, epi=e, workspace=ws, stream=stream)
         call.keep = (X, idx, mx)   # the extra outputs live as long as the closure
         return call, C, ws, nbytes
     d = w.dims
@@ -310,13 +312,17 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
     dev = {t.name: to_dev(raw[t.name], t.dtype) for t in w.tensors}
+    if args.b_nk:
+        if w.kind != "gemm_epilogue":
+            raise SystemExit("--b-nk applies to the GEMM + epilogue workloads")
+        dev["B"] = dev["B"].t().contiguous()
     in_bytes = sum(v.numel() * v.element_size() for v in dev.values())
     nset = 1 if args.rotate_mb <= 0 else max(1, min(64, -(-args.rotate_mb * (1 << 20) // in_bytes)))
     devs = [dev] + [{k: v.clone() for k, v in dev.items()} for _ in range(nset - 1)]
     calls = []
     for d_ in devs:
         call, out, ws, ws_bytes = make_call(w, d_, torch, cf, args.store_x, args.causal, args.argmax, args.row2,
-                                            args.topk)
+                                            args.topk, args.b_nk)
         calls.append(call)
 
     # settle: batches of calls (grown to ~20 ms each) until --settle-s has passed
@@ -356,7 +362,7 @@ def main():
                                                                 args.argmax, args.topk)
     traffic = None
     if os.path.exists(args.traffic) and not (args.plain or args.store_x or args.causal or args.argmax or args.row2
-                                             or args.topk):
+                                             or args.topk or args.b_nk):
         try:
             rec = json.load(open(args.traffic))
             if rec.get("kernel_source_hash") == kernel_source_hash():
@@ -380,7 +386,7 @@ def main():
         "config": {"workload": w.name + ("/identity-epilogue" if args.plain else "")
                    + ("+x_out" if args.store_x else "") + ("/causal" if args.causal else "")
                    + ("/argmax" if args.argmax else "") + (f"/then-{args.row2}" if args.row2 else "")
-                   + (f"/top-{args.topk}" if args.topk else ""), **w.dims,
+                   + (f"/top-{args.topk}" if args.topk else "") + ("/B[N,K]" if args.b_nk else ""), **w.dims,
                    "out_dtype": w.params.get("out_dtype"), "input_sets": nset, "input_bytes_per_set": in_bytes},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,

@@ -527,14 +527,14 @@ def test_argmax_general_path_with_logits(shape):
     P.assert_close(P.gpu_to_f64(C), X, P.REL_F_BF16, P.MAX_ABS_BF16, f"argmax {shape}: C = x")
 
 
-def run_topk(A, B, k, with_c, **epi):
-    M, N = A.shape[0], B.shape[1]
+def run_topk(A, B, k, with_c, b_is_nk=False, **epi):
+    M, N = A.shape[0], (B.shape[0] if b_is_nk else B.shape[1])
     idx = torch.full((M, k), -1, dtype=torch.int32, device="cuda")
     val = torch.full((M, k), float("nan"), dtype=torch.float32, device="cuda")
     e = cf.make_epilogue(row_op="topk", topk=k, row_index=idx, row_stats=val, **epi)
     ws = _WS.get(cf.cf_gemm_epilogue_workspace_size(M, N, A.shape[1], e))
     C = torch.empty(M, N, dtype=torch.float32, device="cuda") if with_c else None
-    cf.cf_gemm_epilogue(A, B, C, epi=e, workspace=ws)
+    cf.cf_gemm_epilogue(A, B, C, b_is_nk=b_is_nk, epi=e, workspace=ws)
     torch.cuda.synchronize()
     if ws is not None:
         assert cf.cf_workspace_status(ws) == cf.CF_OK
@@ -648,6 +648,25 @@ def test_topk_relu_zero_ties(N):
     assert np.array_equal(got, oi), np.argwhere(got != oi)[:4]
     assert all(list(r[2:]) == [0, 1, 2, 3, 4, 5] for r in got)
     P.assert_close(P.gpu_to_f64(val), ov, 1e-5, 1e-4, "relu top-8 values")
+
+
+def test_topk_full_size_sampled_rows():
+    # C2 shape (8192 x 4096 x 4096, sixteen column tiles per strip), top-8 of
+    # sampled rows, in the launch configuration bench.py times
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=0)
+    idx, val, _ = run_topk(dev["A"], dev["B"], 8, False)
+    rows = np.concatenate([np.random.default_rng(3).choice(w.dims["M"], 24, replace=False), [0, w.dims["M"] - 1]])
+    X = oracle.elementwise_stage(oracle.matmul(ref["A"][rows], ref["B"]))
+    r = torch.as_tensor(rows, device="cuda")
+    check_topk(idx[r], val[r], X, 8, "top-8 C2 full size")
+
+
+def test_topk_b_nk():
+    # B given [N, K] (the nn.Linear weight layout), ragged last column tile
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=48, M=300, N=1000, K=256)
+    X = oracle.elementwise_stage(oracle.matmul(ref["A"], ref["B"]))
+    idx, val, _ = run_topk(dev["A"], dev["B"].t().contiguous(), 8, False, b_is_nk=True)
+    check_topk(idx, val, X, 8, "top-8 B[N,K]")
 
 
 def test_topk_one_is_argmax():

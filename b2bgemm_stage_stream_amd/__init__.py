@@ -104,29 +104,46 @@ def _check(status: int, where: str):
 
 
 # ----------------------------------------------------------------------------- helpers
+_DTYPE_CODES = None
+
+
 def _dtype_code(t) -> int:
-    import torch
-    if t.dtype == torch.float32:
-        return CF_F32
-    if t.dtype == torch.bfloat16:
-        return CF_BF16
-    raise TypeError(f"unsupported dtype {t.dtype}")
+    global _DTYPE_CODES
+    if _DTYPE_CODES is None:
+        import torch
+        _DTYPE_CODES = {torch.float32: CF_F32, torch.bfloat16: CF_BF16}
+    code = _DTYPE_CODES.get(t.dtype)
+    if code is None:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return code
 
 
 def _ld(t) -> int:
     """Leading dimension (row stride in elements) of a row-major 2-D (or batched) tensor."""
-    if t.dim() < 2:
+    st = t.stride()
+    if len(st) < 2:
         raise ValueError("expected a matrix")
-    if t.stride(-1) != 1:
+    if st[-1] != 1:
         raise ValueError("the last dimension must be contiguous")
-    return t.stride(-2)
+    return st[-2]
+
+
+_RAW_STREAM = None
 
 
 def _stream(stream) -> Optional[int]:
+    """The HIP stream handle: `stream` itself (a torch stream or a handle), or
+    torch's current stream on the current device. The raw-handle query skips
+    building a stream object on every launch."""
+    global _RAW_STREAM
+    if stream is not None:
+        return getattr(stream, "cuda_stream", stream)
     import torch
-    if stream is None:
-        return torch.cuda.current_stream().cuda_stream
-    return getattr(stream, "cuda_stream", stream)
+    if _RAW_STREAM is None:
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        _RAW_STREAM = (lambda: raw(torch.cuda.current_device())) if raw is not None else \
+            (lambda: torch.cuda.current_stream().cuda_stream)
+    return _RAW_STREAM()
 
 
 def _ptr(t) -> Optional[int]:
@@ -258,18 +275,16 @@ def cf_b2bgemm(A, B0, B1, O, *, b0_is_lk: bool = False, epi: Optional[cf_epilogu
     elif epi_kwargs:
         raise TypeError("pass either epi or epilogue keywords")
 
-    def batched(t):
-        return (t.shape[0], t.stride(0)) if t.dim() == 3 else (None, 0)
+    def bstride(t):
+        st = t.stride()
+        return st[0] if len(st) == 3 else 0
 
-    batch, sa = batched(A)
-    if batch is None:
-        batch = 1
-    M, K = A.shape[-2:]
+    ash = A.shape
+    batch = ash[0] if len(ash) == 3 else 1
+    M, K = ash[-2], ash[-1]
     L = B0.shape[-2] if b0_is_lk else B0.shape[-1]
     N = B1.shape[-1]
-    _, sb0 = batched(B0)
-    _, sb1 = batched(B1)
-    _, so = batched(O)
+    sa, sb0, sb1, so = bstride(A), bstride(B0), bstride(B1), bstride(O)
     st = epi_kwargs.get("row_stats")
     if st is not None and st.numel() < batch * M:
         raise ValueError("row_stats is too small for batch * M rows")

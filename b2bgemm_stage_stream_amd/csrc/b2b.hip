@@ -430,15 +430,14 @@ bool b2b_supported(const B2bParams& p) {
 }
 
 hipError_t launch_b2b(const B2bParams& p, hipStream_t stream) {
-  int dev = 0, cus = 0, per_cu = 0;
+  int cus = 0, per_cu = 0;
   hipError_t e;
-  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+  if ((e = device_cus_cached(&cus)) != hipSuccess) return e;
   int bm = kBM;
   const void* ks = b2b_stream_pick(p, cus, &bm);
   const void* k = ks ? ks : pick(p);
   if (!k) return hipErrorNotSupported;
-  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, 0)) != hipSuccess) return e;
+  if ((e = blocks_per_cu_cached(k, kThreads, &per_cu)) != hipSuccess) return e;
   const long tiles = (long)p.batch * ((p.M + bm - 1) / bm);
   const long cap = (long)(per_cu > 0 ? per_cu : 1) * cus;
   long g = tiles < cap ? tiles : cap;

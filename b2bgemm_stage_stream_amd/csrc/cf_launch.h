@@ -58,6 +58,11 @@ struct GemmEpilogueParams {
 hipError_t launch_gemm_epilogue(const GemmEpilogueParams& p, bool in_f32, bool b_nk, bool vec,
                                 int grid, hipStream_t stream);
 
+// Workgroups of `kernel` with `threads` threads that fit on one compute unit
+// of the current device, and the device's compute units; both cached.
+hipError_t blocks_per_cu_cached(const void* kernel, int threads, int* n);
+hipError_t device_cus_cached(int* cus);
+
 // Workgroups of the GEMM + epilogue kernel that fit on one compute unit.
 int gemm_epilogue_blocks_per_cu(const GemmEpilogueParams& p, bool in_f32, bool b_nk, bool vec);
 

@@ -2,7 +2,66 @@
 // and the workspace clear kernel.
 #include "cf_launch.h"
 
+#include <mutex>
+
 namespace cf {
+
+// The occupancy query and the device attribute read cost microseconds of host
+// time, which small launches would pay on every call; both are fixed per
+// (device, kernel), so they are cached. A full table leaves new entries
+// uncached (still correct).
+namespace {
+struct OccEntry {
+  const void* k;
+  int dev, threads, n;
+};
+std::mutex g_occ_mu;
+OccEntry g_occ[512];
+int g_occ_used = 0;
+int g_cus[64];   // 0: not read yet
+}  // namespace
+
+hipError_t blocks_per_cu_cached(const void* k, int threads, int* n) {
+  *n = 0;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  {
+    std::lock_guard<std::mutex> g(g_occ_mu);
+    for (int i = 0; i < g_occ_used; ++i)
+      if (g_occ[i].k == k && g_occ[i].dev == dev && g_occ[i].threads == threads) {
+        *n = g_occ[i].n;
+        return hipSuccess;
+      }
+  }
+  int v = 0;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k, threads, 0)) != hipSuccess) return e;
+  std::lock_guard<std::mutex> g(g_occ_mu);
+  if (g_occ_used < (int)(sizeof(g_occ) / sizeof(g_occ[0]))) g_occ[g_occ_used++] = OccEntry{k, dev, threads, v};
+  *n = v;
+  return hipSuccess;
+}
+
+hipError_t device_cus_cached(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < 64) {
+    std::lock_guard<std::mutex> g(g_occ_mu);
+    if (g_cus[dev] > 0) {
+      *cus = g_cus[dev];
+      return hipSuccess;
+    }
+  }
+  int v = 0;
+  if ((e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+  if (dev >= 0 && dev < 64) {
+    std::lock_guard<std::mutex> g(g_occ_mu);
+    g_cus[dev] = v;
+  }
+  *cus = v;
+  return hipSuccess;
+}
 
 #define CF_DECL_PARTS(F, N)                      \
   const void* cf_ge_kernels_##F##_##N##_0(int);  \
@@ -47,9 +106,9 @@ static const void* pick(const GemmEpilogueParams& p, bool in_f32, bool b_nk, boo
 }
 
 int gemm_epilogue_blocks_per_cu(const GemmEpilogueParams& p, bool in_f32, bool b_nk, bool vec) {
+  const void* k = pick(p, in_f32, b_nk, vec);
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pick(p, in_f32, b_nk, vec), 256, 0) != hipSuccess)
-    return 0;
+  if (k == nullptr || blocks_per_cu_cached(k, 256, &n) != hipSuccess) return 0;
   return n;
 }
 

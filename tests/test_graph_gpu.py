@@ -89,3 +89,14 @@ def test_row_stats_with_second_output():
     P.assert_close(P.gpu_to_f64(Y), P.gpu_to_f64(X * st[:, None] * w32), 1e-6, 1e-5, "y from stored x and rstd")
     R = oracle.gemm_epilogue_row_stats(ref["A"], ref["B"], residual=ref["residual"], row_op="rmsnorm", eps=1e-6)
     P.assert_close(P.gpu_to_f64(st), R, 1e-5, 1e-4, "rstd")
+
+
+def test_launch_stream_is_torch_current_stream():
+    # launches without an explicit stream go to torch's current stream, on the
+    # default stream and inside a side-stream context
+    assert cf._stream(None) == torch.cuda.current_stream().cuda_stream
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        assert cf._stream(None) == s.cuda_stream == torch.cuda.current_stream().cuda_stream
+    assert cf._stream(None) == torch.cuda.current_stream().cuda_stream
+    assert cf._stream(s) == s.cuda_stream

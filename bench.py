@@ -298,6 +298,8 @@ def main():
         raise SystemExit("--topk K (1..8) applies to the GEMM + epilogue workloads without a residual, alone")
     if args.argmax and w.kind != "gemm_epilogue":
         raise SystemExit("--argmax applies to the GEMM + epilogue workloads")
+    if args.b_nk and w.kind != "gemm_epilogue":
+        raise SystemExit("--b-nk applies to the GEMM + epilogue workloads")
     if args.causal and (w.kind != "b2bgemm" or w.params["row_op"] != "softmax"):
         raise SystemExit("--causal applies to the attention (softmax B2BGEMM) workload")
     if args.plain:
@@ -313,8 +315,6 @@ def main():
 
     dev = {t.name: to_dev(raw[t.name], t.dtype) for t in w.tensors}
     if args.b_nk:
-        if w.kind != "gemm_epilogue":
-            raise SystemExit("--b-nk applies to the GEMM + epilogue workloads")
         dev["B"] = dev["B"].t().contiguous()
     in_bytes = sum(v.numel() * v.element_size() for v in dev.values())
     nset = 1 if args.rotate_mb <= 0 else max(1, min(64, -(-args.rotate_mb * (1 << 20) // in_bytes)))

@@ -51,3 +51,15 @@ def test_more_than_one_gpu_exits_with_message():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+@pytest.mark.parametrize("flags", [["--workload", "c4_b2b_mlp_relu", "--b-nk"],
+                                   ["--workload", "c4_b2b_mlp_relu", "--argmax"],
+                                   ["--workload", "c3_gemm_residual_rmsnorm", "--topk", "4"],
+                                   ["--topk", "9"]])
+def test_flags_outside_their_workloads_exit_with_message(flags):
+    # rejected before any device work, so this runs without a GPU
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")] + flags, capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode != 0
+    assert "applies to" in r.stderr, r.stderr[-500:]

@@ -35,7 +35,7 @@ def _units():
         units.append((os.path.join(CSRC, f), os.path.join(BUILD, os.path.splitext(f)[0] + ".o"), []))
     for in_f32 in (0, 1):
         for b_nk in (0, 1):
-            for part in range(16):
+            for part in range(17):
                 obj = os.path.join(BUILD, f"gemm_epilogue_inst_{in_f32}_{b_nk}_{part}.o")
                 units.append((os.path.join(CSRC, "gemm_epilogue_inst.hip"), obj,
                               [f"-DCF_IN_F32={in_f32}", f"-DCF_B_NK={b_nk}", f"-DCF_PART={part}"]))

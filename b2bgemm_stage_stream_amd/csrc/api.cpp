@@ -222,7 +222,9 @@ cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K, const void* A, int64
   void* const X = epi ? epi->x_out : nullptr;
   const size_t xs = X ? dsize(epi->x_out_dtype) : 2;
   if (X && !fits31(M, kTile, epi->ld_x_out, xs)) return CF_ERR_UNSUPPORTED;
-  const int row_op = epi ? (int)epi->row_op : 0;
+  // top-1 is the row argmax (same order, ties and NaN ranking, same outputs)
+  const int row_op = (epi && epi->row_op == CF_ROW_TOPK && epi->topk == 1) ? (int)CF_ROW_ARGMAX
+                     : epi ? (int)epi->row_op : 0;
   if (row_op != CF_ROW_NONE && N > 65536) return CF_ERR_UNSUPPORTED;
 
   const GemmPlan plan = plan_gemm(M, N, epi);

@@ -79,18 +79,19 @@ hipError_t device_cus_cached(int* cus) {
   const void* cf_ge_kernels_##F##_##N##_12(int);  \
   const void* cf_ge_kernels_##F##_##N##_13(int);  \
   const void* cf_ge_kernels_##F##_##N##_14(int);  \
-  const void* cf_ge_kernels_##F##_##N##_15(int);
+  const void* cf_ge_kernels_##F##_##N##_15(int); \
+  const void* cf_ge_kernels_##F##_##N##_16(int);
 CF_DECL_PARTS(0, 0)
 CF_DECL_PARTS(0, 1)
 CF_DECL_PARTS(1, 0)
 CF_DECL_PARTS(1, 1)
 
 typedef const void* (*PartFn)(int);
-static const PartFn kParts[2][2][16] = {
-    {{cf_ge_kernels_0_0_0, cf_ge_kernels_0_0_1, cf_ge_kernels_0_0_2, cf_ge_kernels_0_0_3, cf_ge_kernels_0_0_4, cf_ge_kernels_0_0_5, cf_ge_kernels_0_0_6, cf_ge_kernels_0_0_7, cf_ge_kernels_0_0_8, cf_ge_kernels_0_0_9, cf_ge_kernels_0_0_10, cf_ge_kernels_0_0_11, cf_ge_kernels_0_0_12, cf_ge_kernels_0_0_13, cf_ge_kernels_0_0_14, cf_ge_kernels_0_0_15},
-     {cf_ge_kernels_0_1_0, cf_ge_kernels_0_1_1, cf_ge_kernels_0_1_2, cf_ge_kernels_0_1_3, cf_ge_kernels_0_1_4, cf_ge_kernels_0_1_5, cf_ge_kernels_0_1_6, cf_ge_kernels_0_1_7, cf_ge_kernels_0_1_8, cf_ge_kernels_0_1_9, cf_ge_kernels_0_1_10, cf_ge_kernels_0_1_11, cf_ge_kernels_0_1_12, cf_ge_kernels_0_1_13, cf_ge_kernels_0_1_14, cf_ge_kernels_0_1_15}},
-    {{cf_ge_kernels_1_0_0, cf_ge_kernels_1_0_1, cf_ge_kernels_1_0_2, cf_ge_kernels_1_0_3, cf_ge_kernels_1_0_4, cf_ge_kernels_1_0_5, cf_ge_kernels_1_0_6, cf_ge_kernels_1_0_7, cf_ge_kernels_1_0_8, cf_ge_kernels_1_0_9, cf_ge_kernels_1_0_10, cf_ge_kernels_1_0_11, cf_ge_kernels_1_0_12, cf_ge_kernels_1_0_13, cf_ge_kernels_1_0_14, cf_ge_kernels_1_0_15},
-     {cf_ge_kernels_1_1_0, cf_ge_kernels_1_1_1, cf_ge_kernels_1_1_2, cf_ge_kernels_1_1_3, cf_ge_kernels_1_1_4, cf_ge_kernels_1_1_5, cf_ge_kernels_1_1_6, cf_ge_kernels_1_1_7, cf_ge_kernels_1_1_8, cf_ge_kernels_1_1_9, cf_ge_kernels_1_1_10, cf_ge_kernels_1_1_11, cf_ge_kernels_1_1_12, cf_ge_kernels_1_1_13, cf_ge_kernels_1_1_14, cf_ge_kernels_1_1_15}}};
+static const PartFn kParts[2][2][17] = {
+    {{cf_ge_kernels_0_0_0, cf_ge_kernels_0_0_1, cf_ge_kernels_0_0_2, cf_ge_kernels_0_0_3, cf_ge_kernels_0_0_4, cf_ge_kernels_0_0_5, cf_ge_kernels_0_0_6, cf_ge_kernels_0_0_7, cf_ge_kernels_0_0_8, cf_ge_kernels_0_0_9, cf_ge_kernels_0_0_10, cf_ge_kernels_0_0_11, cf_ge_kernels_0_0_12, cf_ge_kernels_0_0_13, cf_ge_kernels_0_0_14, cf_ge_kernels_0_0_15, cf_ge_kernels_0_0_16},
+     {cf_ge_kernels_0_1_0, cf_ge_kernels_0_1_1, cf_ge_kernels_0_1_2, cf_ge_kernels_0_1_3, cf_ge_kernels_0_1_4, cf_ge_kernels_0_1_5, cf_ge_kernels_0_1_6, cf_ge_kernels_0_1_7, cf_ge_kernels_0_1_8, cf_ge_kernels_0_1_9, cf_ge_kernels_0_1_10, cf_ge_kernels_0_1_11, cf_ge_kernels_0_1_12, cf_ge_kernels_0_1_13, cf_ge_kernels_0_1_14, cf_ge_kernels_0_1_15, cf_ge_kernels_0_1_16}},
+    {{cf_ge_kernels_1_0_0, cf_ge_kernels_1_0_1, cf_ge_kernels_1_0_2, cf_ge_kernels_1_0_3, cf_ge_kernels_1_0_4, cf_ge_kernels_1_0_5, cf_ge_kernels_1_0_6, cf_ge_kernels_1_0_7, cf_ge_kernels_1_0_8, cf_ge_kernels_1_0_9, cf_ge_kernels_1_0_10, cf_ge_kernels_1_0_11, cf_ge_kernels_1_0_12, cf_ge_kernels_1_0_13, cf_ge_kernels_1_0_14, cf_ge_kernels_1_0_15, cf_ge_kernels_1_0_16},
+     {cf_ge_kernels_1_1_0, cf_ge_kernels_1_1_1, cf_ge_kernels_1_1_2, cf_ge_kernels_1_1_3, cf_ge_kernels_1_1_4, cf_ge_kernels_1_1_5, cf_ge_kernels_1_1_6, cf_ge_kernels_1_1_7, cf_ge_kernels_1_1_8, cf_ge_kernels_1_1_9, cf_ge_kernels_1_1_10, cf_ge_kernels_1_1_11, cf_ge_kernels_1_1_12, cf_ge_kernels_1_1_13, cf_ge_kernels_1_1_14, cf_ge_kernels_1_1_15, cf_ge_kernels_1_1_16}}};
 
 static const void* pick(const GemmEpilogueParams& p, bool in_f32, bool b_nk, bool vec) {
   // two row stages: fast path only, one part per (first, second) row op
@@ -100,7 +101,8 @@ static const void* pick(const GemmEpilogueParams& p, bool in_f32, bool b_nk, boo
                     (p.bias != nullptr || p.residual != nullptr) ? 1 : 0)
               : nullptr;
   }
-  if (p.row_op == 5) return vec ? kParts[in_f32][b_nk][15]((p.bias != nullptr) ? 1 : 0) : nullptr;   // top-k
+  if (p.row_op == 5)   // top-k: lists of 4 when k <= 4, else of 8
+    return vec ? kParts[in_f32][b_nk][p.topk <= 4 ? 16 : 15]((p.bias != nullptr) ? 1 : 0) : nullptr;
   const int part = vec ? p.row_op : 5;
   return kParts[in_f32][b_nk][part]((p.bias != nullptr || p.residual != nullptr) ? 1 : 0);
 }

@@ -2,8 +2,8 @@
 // (input dtype, B layout, part): CF_IN_F32 in {0, 1}, CF_B_NK in {0, 1},
 // CF_PART in {0, 1, 2, 3, 4} (fast path for row op CF_PART, with and without
 // bias/residual), 5 (general path), 6 to 14 (two row stages, fast path:
-// first row op 1 + (CF_PART - 6) / 3, second 1 + (CF_PART - 6) % 3) or 15
-// (top-k, fast path).
+// first row op 1 + (CF_PART - 6) / 3, second 1 + (CF_PART - 6) % 3), 15 (top-k, fast path) or 16 (top-k with
+// k <= 4, fast path).
 // Splitting the instantiations lets them compile in parallel.
 #include "gemm_epilogue_kernel.hpp"
 
@@ -26,9 +26,9 @@ const void* CF_FN(int pre) {
 #elif CF_PART == 5
   (void)pre;
   return (const void*)&gemm_epilogue_kernel<CF_IN_F32 != 0, CF_B_NK != 0, false, 0, false>;
-#elif CF_PART == 15
-  if (pre) return (const void*)&gemm_epilogue_kernel<CF_IN_F32 != 0, CF_B_NK != 0, true, 5, true>;
-  return (const void*)&gemm_epilogue_kernel<CF_IN_F32 != 0, CF_B_NK != 0, true, 5, false>;
+#elif CF_PART == 15 || CF_PART == 16
+  if (pre) return (const void*)&gemm_epilogue_kernel<CF_IN_F32 != 0, CF_B_NK != 0, true, CF_PART - 10, true>;
+  return (const void*)&gemm_epilogue_kernel<CF_IN_F32 != 0, CF_B_NK != 0, true, CF_PART - 10, false>;
 #else
   if (pre)
     return (const void*)&gemm_epilogue_kernel<CF_IN_F32 != 0, CF_B_NK != 0, true, 1 + (CF_PART - 6) / 3, true,

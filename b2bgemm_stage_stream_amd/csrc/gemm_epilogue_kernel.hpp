@@ -408,10 +408,10 @@ __device__ inline void acc_read4(const f32x16_t& blk, float tok, float (&v)[4]) 
       : "a"(blk[4 * Q]), "a"(blk[4 * Q + 1]), "a"(blk[4 * Q + 2]), "a"(blk[4 * Q + 3]), "v"(tok));
 }
 
-// Top-k lists: kTopK (value, column) pairs sorted by value descending, equal
-// values by column ascending. An empty entry is (-inf, kNoColumn); it ranks
-// below every real entry, -inf included. NaN is mapped to -inf by the caller.
-constexpr int kTopK = 8;
+// Top-k lists: L (value, column) pairs sorted by value descending, equal
+// values by column ascending (L = 8, or 4 when k <= 4). An empty entry is
+// (-inf, kNoColumn); it ranks below every real entry, -inf included. NaN is
+// mapped to -inf by the caller.
 constexpr int kNoColumn = 0x7fffffff;
 
 // Inserts a candidate whose column is larger than every column the list holds
@@ -423,16 +423,16 @@ constexpr int kNoColumn = 0x7fffffff;
 // list. kMaybeEmpty: the list may still hold empty entries, which any
 // candidate with a column displaces. No branches and no chain through the
 // positions.
-template <bool kMaybeEmpty>
-__device__ inline void topk_insert_next(float (&tv)[kTopK], int (&tc)[kTopK], float cv, int cc) {
-  bool g[kTopK];
+template <bool kMaybeEmpty, int L>
+__device__ inline void topk_insert_next(float (&tv)[L], int (&tc)[L], float cv, int cc) {
+  bool g[L];
 #pragma unroll
-  for (int j = 0; j < kTopK; ++j) {
+  for (int j = 0; j < L; ++j) {
     g[j] = cv > tv[j];
     if constexpr (kMaybeEmpty) g[j] = g[j] | (tc[j] == kNoColumn);
   }
 #pragma unroll
-  for (int j = kTopK - 1; j > 0; --j) {
+  for (int j = L - 1; j > 0; --j) {
     tc[j] = g[j] ? (g[j - 1] ? tc[j - 1] : cc) : tc[j];
     tv[j] = __builtin_amdgcn_fmed3f(tv[j], cv, tv[j - 1]);
   }
@@ -445,21 +445,21 @@ __device__ inline bool topk_before(float va, int ca, float vb, int cb) {
   return (va > vb) | ((va == vb) & (ca < cb));
 }
 
-// Merges list (bv, bc) into (tv, tc), keeping the kTopK best of the union: the
-// elementwise better of a[i] and b[kTopK-1-i] is the union's best kTopK as a
-// bitonic sequence, which three half-cleaner stages sort.
-__device__ inline void topk_merge(float (&tv)[kTopK], int (&tc)[kTopK], const float (&bv)[kTopK],
-                                  const int (&bc)[kTopK]) {
+// Merges list (bv, bc) into (tv, tc), keeping the L best of the union: the
+// elementwise better of a[i] and b[L-1-i] is the union's best L as a bitonic
+// sequence, which log2(L) half-cleaner stages sort.
+template <int L>
+__device__ inline void topk_merge(float (&tv)[L], int (&tc)[L], const float (&bv)[L], const int (&bc)[L]) {
 #pragma unroll
-  for (int i = 0; i < kTopK; ++i) {
-    const bool b = topk_before(bv[kTopK - 1 - i], bc[kTopK - 1 - i], tv[i], tc[i]);
-    tv[i] = b ? bv[kTopK - 1 - i] : tv[i];
-    tc[i] = b ? bc[kTopK - 1 - i] : tc[i];
+  for (int i = 0; i < L; ++i) {
+    const bool b = topk_before(bv[L - 1 - i], bc[L - 1 - i], tv[i], tc[i]);
+    tv[i] = b ? bv[L - 1 - i] : tv[i];
+    tc[i] = b ? bc[L - 1 - i] : tc[i];
   }
 #pragma unroll
-  for (int d = kTopK / 2; d > 0; d >>= 1) {
+  for (int d = L / 2; d > 0; d >>= 1) {
 #pragma unroll
-    for (int i = 0; i < kTopK; ++i) {
+    for (int i = 0; i < L; ++i) {
       if ((i & d) == 0) {
         const bool sw = topk_before(tv[i + d], tc[i + d], tv[i], tc[i]);
         const float v0 = tv[i], v1 = tv[i + d];
@@ -490,7 +490,7 @@ __device__ inline float2 halves(float v) {
   return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// ROW: 0 none, 1 softmax, 2 LayerNorm, 3 RMSNorm, 4 argmax, 5 top-k (cf_row_op).
+// ROW: 0 none, 1 softmax, 2 LayerNorm, 3 RMSNorm, 4 argmax, 5 top-k (cf_row_op); 6 top-k with k <= 4.
 // kFast: 16-byte accesses are allowed, N is a multiple of 8 and the residual
 // (if any) is bf16; otherwise every column is masked against N, element by
 // element.
@@ -507,6 +507,9 @@ __device__ inline float2 halves(float v) {
 template <int ROW, bool kFast, bool kPre, bool kId, bool kRagged = false, int ROW2 = 0>
 __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&acc)[4][4], const GemmEpilogueParams& p, uint8_t* smem,
                                 int strip, int tn, uint32_t tag, bool& timed_out, int tid) {
+  // top-k (ROW 5: lists of 8; ROW 6: lists of 4, for k <= 4)
+  constexpr bool kTop = ROW == 5 || ROW == 6;
+  constexpr int kL = ROW == 6 ? 4 : 8;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, r32 = lane & 31;
@@ -526,7 +529,7 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
     vbeta[tid] = (p.beta && ok) ? load_vec(p.beta, n, p.vec_f32) : 0.0f;
   }
   // top-k takes no residual (its lists use the residual staging area)
-  const bool has_res = ROW != 5 && p.residual != nullptr;
+  const bool has_res = !kTop && p.residual != nullptr;
   const __amdgpu_buffer_rsrc_t rsR = make_rsrc(p.residual, has_res ? p.r_bytes : 0u);
   if (kFast && has_res) {
     // stage the bf16 residual tile [256][256] in LDS with coalesced 16-byte loads;
@@ -676,14 +679,14 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
           tok = s2;
         });
         a = sum_halves(s2);
-      } else if constexpr (ROW == 5) {
+      } else if constexpr (kTop) {
         // top-k: a lane inserts its columns, in increasing order, into a sorted
-        // list of kTopK, which goes to LDS (the residual staging area: top-k
+        // list of kL, which goes to LDS (the residual staging area: top-k
         // takes no residual)
-        float tv[kTopK];
-        int tc[kTopK];
+        float tv[kL];
+        int tc[kL];
 #pragma unroll
-        for (int j = 0; j < kTopK; ++j) {
+        for (int j = 0; j < kL; ++j) {
           tv[j] = -INFINITY;
           tc[j] = kNoColumn;
         }
@@ -697,20 +700,20 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
             // NaN ranks as -inf; a column past N stays out
             const float cv = ok ? fmaxf(x[e], -INFINITY) : -INFINITY;
             const int cc = ok ? n0 + wn * 128 + nb * 32 + 8 * q + 4 * h + e : kNoColumn;
-            // empty entries remain only among the first kTopK candidates (past
+            // empty entries remain only among the first kL candidates (past
             // those, only columns beyond N, which come last, leave entries empty)
-            if (nb * 16 + q * 4 + e < kTopK) topk_insert_next<true>(tv, tc, cv, cc);
+            if (nb * 16 + q * 4 + e < kL) topk_insert_next<true>(tv, tc, cv, cc);
             else topk_insert_next<false>(tv, tc, cv, cc);
           }
-          tok = tv[kTopK - 1];
+          tok = tv[kL - 1];
         });
         {
           // lists of [wn][h][row]: the per-row merge below reads all four
           const int row = wm * 128 + mb * 32 + r32;
-          float* lv = (float*)(smem + kOffRes) + ((wn * 2 + h) * 256 + row) * kTopK;
-          int* lc = (int*)(smem + kOffRes + 4 * 256 * kTopK * 4) + ((wn * 2 + h) * 256 + row) * kTopK;
+          float* lv = (float*)(smem + kOffRes) + ((wn * 2 + h) * 256 + row) * kL;
+          int* lc = (int*)(smem + kOffRes + 4 * 256 * kL * 4) + ((wn * 2 + h) * 256 + row) * kL;
 #pragma unroll
-          for (int j = 0; j < kTopK; ++j) {
+          for (int j = 0; j < kL; ++j) {
             lv[j] = tv[j];
             lc[j] = tc[j];
           }
@@ -747,7 +750,7 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
         a = take1 ? hm.y : hm.x;
         b = __int_as_float(take1 ? i1 : i0);
       }
-      if constexpr (ROW != 5)
+      if constexpr (!kTop)
         if (h == 0) wpart[wn * 256 + wm * 128 + mb * 32 + r32] = make_float2(a, b);
     }
     __syncthreads();
@@ -755,7 +758,7 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
     // ---- one thread per row: merge the two wave partials, then (reduction
     // level 3) exchange with the other column tiles of the strip and merge all
     // of them in tile order
-    if constexpr (ROW == 5) {
+    if constexpr (kTop) {
       // top-k: merge the four lists of the tile (two lane halves of two
       // waves), then the strip's: column tile 0 stores the result, so the
       // other tiles publish their lists (16 tagged words per row) and go on,
@@ -763,31 +766,31 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
       const int ml = tid;
       const bool row_ok = m0 + ml < p.M;
       const float* lv = (const float*)(smem + kOffRes);
-      const int* lc = (const int*)(smem + kOffRes + 4 * 256 * kTopK * 4);
-      float tv[kTopK];
-      int tc[kTopK];
+      const int* lc = (const int*)(smem + kOffRes + 4 * 256 * kL * 4);
+      float tv[kL];
+      int tc[kL];
 #pragma unroll
-      for (int j = 0; j < kTopK; ++j) {
-        tv[j] = lv[ml * kTopK + j];
-        tc[j] = lc[ml * kTopK + j];
+      for (int j = 0; j < kL; ++j) {
+        tv[j] = lv[ml * kL + j];
+        tc[j] = lc[ml * kL + j];
       }
       for (int l = 1; l < 4; ++l) {
-        float bv[kTopK];
-        int bc[kTopK];
+        float bv[kL];
+        int bc[kL];
 #pragma unroll
-        for (int j = 0; j < kTopK; ++j) {
-          bv[j] = lv[(l * 256 + ml) * kTopK + j];
-          bc[j] = lc[(l * 256 + ml) * kTopK + j];
+        for (int j = 0; j < kL; ++j) {
+          bv[j] = lv[(l * 256 + ml) * kL + j];
+          bc[j] = lc[(l * 256 + ml) * kL + j];
         }
         topk_merge(tv, tc, bv, bc);
       }
       if (p.ws_hdr != nullptr && row_ok) {
-        uint64_t* slots = p.ws_slots + (size_t)strip * p.tiles_n * (256 * 2 * kTopK) + (size_t)ml * 2 * kTopK;
+        uint64_t* slots = p.ws_slots + (size_t)strip * p.tiles_n * (256 * 2 * kL) + (size_t)ml * 2 * kL;
         if (tn != 0) {
 #pragma unroll
-          for (int j = 0; j < kTopK; ++j) {
-            publish(slots + (size_t)tn * (256 * 2 * kTopK) + j, tv[j], tag);
-            publish(slots + (size_t)tn * (256 * 2 * kTopK) + kTopK + j, __int_as_float(tc[j]), tag);
+          for (int j = 0; j < kL; ++j) {
+            publish(slots + (size_t)tn * (256 * 2 * kL) + j, tv[j], tag);
+            publish(slots + (size_t)tn * (256 * 2 * kL) + kL + j, __int_as_float(tc[j]), tag);
           }
         } else {
           // the peers' lists, kPeers tiles at a time with all their loads in
@@ -795,7 +798,7 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
           constexpr int kPeers = 2;
           const uint64_t t0 = wall_clock64();
           for (int tb = 1; tb < p.tiles_n; tb += kPeers) {
-            uint64_t w[kPeers][2 * kTopK];
+            uint64_t w[kPeers][2 * kL];
             uint32_t need = 0;
 #pragma unroll
             for (int i = 0; i < kPeers; ++i)
@@ -805,9 +808,9 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
 #pragma unroll
               for (int i = 0; i < kPeers; ++i) {
                 if (need & (1u << i)) {
-                  const uint64_t* ps = slots + (size_t)(tb + i) * (256 * 2 * kTopK);
+                  const uint64_t* ps = slots + (size_t)(tb + i) * (256 * 2 * kL);
 #pragma unroll
-                  for (int j = 0; j < 2 * kTopK; ++j)
+                  for (int j = 0; j < 2 * kL; ++j)
                     w[i][j] = __hip_atomic_load(ps + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
               }
@@ -815,7 +818,7 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
               for (int i = 0; i < kPeers; ++i) {
                 bool all = true;
 #pragma unroll
-                for (int j = 0; j < 2 * kTopK; ++j) all = all & ((uint32_t)(w[i][j] >> 32) == tag);
+                for (int j = 0; j < 2 * kL; ++j) all = all & ((uint32_t)(w[i][j] >> 32) == tag);
                 if (all) need &= ~(1u << i);
               }
               if (!need) break;
@@ -828,12 +831,12 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
 #pragma unroll
             for (int i = 0; i < kPeers; ++i) {
               if (have & (1u << i)) {
-                float pv[kTopK];
-                int pc[kTopK];
+                float pv[kL];
+                int pc[kL];
 #pragma unroll
-                for (int j = 0; j < kTopK; ++j) {
+                for (int j = 0; j < kL; ++j) {
                   pv[j] = __uint_as_float((uint32_t)w[i][j]);
-                  pc[j] = (int)(uint32_t)w[i][kTopK + j];
+                  pc[j] = (int)(uint32_t)w[i][kL + j];
                 }
                 topk_merge(tv, tc, pv, pc);
               }
@@ -845,7 +848,7 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
       if (tn == 0 && row_ok) {
         const int m = m0 + ml;
 #pragma unroll
-        for (int j = 0; j < kTopK; ++j) {
+        for (int j = 0; j < kL; ++j) {
           if (j < p.topk) {
             p.row_index[(size_t)m * p.topk + j] = tc[j];
             if (p.row_stats != nullptr) p.row_stats[(size_t)m * p.topk + j] = tv[j];
@@ -1277,7 +1280,7 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
     });
   };
   // argmax / top-k without a matrix output (the logits are never written)
-  if constexpr (ROW == 4 || ROW == 5) {
+  if constexpr (ROW == 4 || kTop) {
     if (p.C == nullptr && p.X == nullptr) return;
   }
   using X0 = std::integral_constant<int, 0>;

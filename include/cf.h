@@ -69,7 +69,8 @@ typedef enum {
                            row_index[m * topk + j] = their columns, row_stats[m * topk
                            + j] (if given) = their values. C as for argmax (may be
                            NULL). gamma, beta and residual must be NULL; fast-path
-                           layouts only (CF_ERR_UNSUPPORTED otherwise).             */
+                           layouts only (CF_ERR_UNSUPPORTED otherwise). topk = 1
+                           runs as CF_ROW_ARGMAX; topk <= 4 keeps shorter lists.    */
 } cf_row_op;
 
 /* Visibility mask on the scores S of cf_b2bgemm's softmax (ignored nowhere:

@@ -560,9 +560,10 @@ def check_topk(idx, val, X, k, what):
     assert bad == 0, f"{what}: {bad} rows with separated values disagree"
 
 
-@pytest.mark.parametrize("k", [1, 4, 8])
+@pytest.mark.parametrize("k", [1, 2, 4, 5, 8])
 @pytest.mark.parametrize("N", [256, 1000, 4096])
 def test_topk(N, k):
+    # k = 1 runs as the argmax, k <= 4 on lists of 4, k > 4 on lists of 8
     # one column tile per strip (no exchange), four with a ragged one, sixteen
     w, dev, ref = P.inputs("c2_gemm_layernorm", seed=41, M=300, N=N, K=256)
     X = oracle.elementwise_stage(oracle.matmul(ref["A"], ref["B"]))

@@ -79,7 +79,7 @@ GemmPlan plan_gemm(int64_t M, int64_t N, const cf_epilogue* epi) {
   g.tiles = g.tiles_n * g.strips;
   g.exchange = epi && epi->row_op != CF_ROW_NONE && g.tiles_n > 1;
   if (g.exchange) {
-    // one slot set per reduction stage; top-k publishes 8 (value, column) pairs per row
+    // one slot set per reduction stage; top-k publishes up to 8 (value, column) pairs per row
     const size_t words = epi->row_op == CF_ROW_TOPK ? 16 : 2;
     const size_t slots = (size_t)g.strips * (size_t)g.tiles_n * (size_t)kTile * words * sizeof(uint64_t);
     g.slot_bytes = ((slots + 255) / 256) * 256;

@@ -761,7 +761,7 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
     if constexpr (kTop) {
       // top-k: merge the four lists of the tile (two lane halves of two
       // waves), then the strip's: column tile 0 stores the result, so the
-      // other tiles publish their lists (16 tagged words per row) and go on,
+      // other tiles publish their lists (2 kL tagged words per row) and go on,
       // and tile 0 merges them all
       const int ml = tid;
       const bool row_ok = m0 + ml < p.M;

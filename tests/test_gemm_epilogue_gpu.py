@@ -662,12 +662,14 @@ def test_topk_full_size_sampled_rows():
     check_topk(idx[r], val[r], X, 8, "top-8 C2 full size")
 
 
-def test_topk_b_nk():
-    # B given [N, K] (the nn.Linear weight layout), ragged last column tile
+@pytest.mark.parametrize("k", [3, 8])
+def test_topk_b_nk(k):
+    # B given [N, K] (the nn.Linear weight layout), ragged last column tile;
+    # lists of 4 (k = 3) and of 8
     w, dev, ref = P.inputs("c2_gemm_layernorm", seed=48, M=300, N=1000, K=256)
     X = oracle.elementwise_stage(oracle.matmul(ref["A"], ref["B"]))
-    idx, val, _ = run_topk(dev["A"], dev["B"].t().contiguous(), 8, False, b_is_nk=True)
-    check_topk(idx, val, X, 8, "top-8 B[N,K]")
+    idx, val, _ = run_topk(dev["A"], dev["B"].t().contiguous(), k, False, b_is_nk=True)
+    check_topk(idx, val, X, k, f"top-{k} B[N,K]")
 
 
 def test_topk_one_is_argmax():

@@ -3,8 +3,9 @@
 Thin ctypes marshalling over the C ABI in ``include/cf.h`` (``libcf.so`` built
 from ``csrc/`` by ``build_lib.py``). The functions keep the C names; they take
 torch tensors only to read device pointers, strides and the current HIP
-stream. Every computation runs in the library's kernels: there is no fallback,
-and importing this package fails loudly when ``libcf.so`` is missing.
+stream. Every computation runs in the library's kernels: there is no fallback.
+Importing the package builds ``libcf.so`` first when it is missing or was
+built from other sources (hipcc, gfx950), and fails loudly when it cannot.
 """
 from __future__ import annotations
 
@@ -12,12 +13,14 @@ import ctypes
 import os
 from typing import Optional
 
-_HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libcf.so")
+from . import build_lib as _build_lib
 
-if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with "
-                      "`python -m b2bgemm_stage_stream_amd.build_lib` (or __graft_entry__.build())")
+LIB_PATH = _build_lib.LIB
+
+try:
+    _build_lib.ensure_built()
+except Exception as exc:   # no hipcc, or a compile error: no library, no package
+    raise ImportError(f"cannot build {LIB_PATH}: {exc}") from exc
 
 _lib = ctypes.CDLL(LIB_PATH)
 

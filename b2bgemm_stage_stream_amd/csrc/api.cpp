@@ -240,8 +240,9 @@ cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K, const void* A, int64
   if (epi && epi->residual)
     vec = vec && epi->residual_dtype == CF_BF16 && epi->ld_residual % 8 == 0 && aligned(epi->residual, 16);
   if (X) vec = vec && epi->ld_x_out % 8 == 0 && aligned(X, 16);
-  // two row stages and top-k: fast-path layouts only
-  if (epi && (epi->row_op2 != CF_ROW_NONE || epi->row_op == CF_ROW_TOPK) && !vec) return CF_ERR_UNSUPPORTED;
+  // two row stages and top-k (k > 1): fast-path layouts and bf16 inputs only
+  if (epi && (epi->row_op2 != CF_ROW_NONE || row_op == CF_ROW_TOPK) && (!vec || ab_dtype != CF_BF16))
+    return CF_ERR_UNSUPPORTED;
 
   // ---- device
   int dev;

@@ -63,48 +63,73 @@ hipError_t device_cus_cached(int* cus) {
   return hipSuccess;
 }
 
-#define CF_DECL_PARTS(F, N)                      \
-  const void* cf_ge_kernels_##F##_##N##_0(int);  \
-  const void* cf_ge_kernels_##F##_##N##_1(int);  \
-  const void* cf_ge_kernels_##F##_##N##_2(int);  \
-  const void* cf_ge_kernels_##F##_##N##_3(int);  \
-  const void* cf_ge_kernels_##F##_##N##_4(int);  \
-  const void* cf_ge_kernels_##F##_##N##_5(int);  \
-  const void* cf_ge_kernels_##F##_##N##_6(int);  \
-  const void* cf_ge_kernels_##F##_##N##_7(int);  \
-  const void* cf_ge_kernels_##F##_##N##_8(int);  \
-  const void* cf_ge_kernels_##F##_##N##_9(int);  \
-  const void* cf_ge_kernels_##F##_##N##_10(int);  \
-  const void* cf_ge_kernels_##F##_##N##_11(int);  \
-  const void* cf_ge_kernels_##F##_##N##_12(int);  \
-  const void* cf_ge_kernels_##F##_##N##_13(int);  \
-  const void* cf_ge_kernels_##F##_##N##_14(int);  \
-  const void* cf_ge_kernels_##F##_##N##_15(int); \
-  const void* cf_ge_kernels_##F##_##N##_16(int);
-CF_DECL_PARTS(0, 0)
-CF_DECL_PARTS(0, 1)
-CF_DECL_PARTS(1, 0)
-CF_DECL_PARTS(1, 1)
+// Instantiation units (gemm_epilogue_inst.hip): parts 0-9 for both input
+// dtypes, parts 10-20 (two row stages, top-k) for bf16 inputs only.
+#define CF_DECL10(F, N)                                                                              \
+  const void* cf_ge_kernels_##F##_##N##_0(int);                                                      \
+  const void* cf_ge_kernels_##F##_##N##_1(int);                                                      \
+  const void* cf_ge_kernels_##F##_##N##_2(int);                                                      \
+  const void* cf_ge_kernels_##F##_##N##_3(int);                                                      \
+  const void* cf_ge_kernels_##F##_##N##_4(int);                                                      \
+  const void* cf_ge_kernels_##F##_##N##_5(int);                                                      \
+  const void* cf_ge_kernels_##F##_##N##_6(int);                                                      \
+  const void* cf_ge_kernels_##F##_##N##_7(int);                                                      \
+  const void* cf_ge_kernels_##F##_##N##_8(int);                                                      \
+  const void* cf_ge_kernels_##F##_##N##_9(int);
+#define CF_DECL_BF16_EXTRA(N)                                                                        \
+  const void* cf_ge_kernels_0_##N##_10(int);                                                         \
+  const void* cf_ge_kernels_0_##N##_11(int);                                                         \
+  const void* cf_ge_kernels_0_##N##_12(int);                                                         \
+  const void* cf_ge_kernels_0_##N##_13(int);                                                         \
+  const void* cf_ge_kernels_0_##N##_14(int);                                                         \
+  const void* cf_ge_kernels_0_##N##_15(int);                                                         \
+  const void* cf_ge_kernels_0_##N##_16(int);                                                         \
+  const void* cf_ge_kernels_0_##N##_17(int);                                                         \
+  const void* cf_ge_kernels_0_##N##_18(int);                                                         \
+  const void* cf_ge_kernels_0_##N##_19(int);                                                         \
+  const void* cf_ge_kernels_0_##N##_20(int);
+CF_DECL10(0, 0)
+CF_DECL10(0, 1)
+CF_DECL10(1, 0)
+CF_DECL10(1, 1)
+CF_DECL_BF16_EXTRA(0)
+CF_DECL_BF16_EXTRA(1)
 
 typedef const void* (*PartFn)(int);
-static const PartFn kParts[2][2][17] = {
-    {{cf_ge_kernels_0_0_0, cf_ge_kernels_0_0_1, cf_ge_kernels_0_0_2, cf_ge_kernels_0_0_3, cf_ge_kernels_0_0_4, cf_ge_kernels_0_0_5, cf_ge_kernels_0_0_6, cf_ge_kernels_0_0_7, cf_ge_kernels_0_0_8, cf_ge_kernels_0_0_9, cf_ge_kernels_0_0_10, cf_ge_kernels_0_0_11, cf_ge_kernels_0_0_12, cf_ge_kernels_0_0_13, cf_ge_kernels_0_0_14, cf_ge_kernels_0_0_15, cf_ge_kernels_0_0_16},
-     {cf_ge_kernels_0_1_0, cf_ge_kernels_0_1_1, cf_ge_kernels_0_1_2, cf_ge_kernels_0_1_3, cf_ge_kernels_0_1_4, cf_ge_kernels_0_1_5, cf_ge_kernels_0_1_6, cf_ge_kernels_0_1_7, cf_ge_kernels_0_1_8, cf_ge_kernels_0_1_9, cf_ge_kernels_0_1_10, cf_ge_kernels_0_1_11, cf_ge_kernels_0_1_12, cf_ge_kernels_0_1_13, cf_ge_kernels_0_1_14, cf_ge_kernels_0_1_15, cf_ge_kernels_0_1_16}},
-    {{cf_ge_kernels_1_0_0, cf_ge_kernels_1_0_1, cf_ge_kernels_1_0_2, cf_ge_kernels_1_0_3, cf_ge_kernels_1_0_4, cf_ge_kernels_1_0_5, cf_ge_kernels_1_0_6, cf_ge_kernels_1_0_7, cf_ge_kernels_1_0_8, cf_ge_kernels_1_0_9, cf_ge_kernels_1_0_10, cf_ge_kernels_1_0_11, cf_ge_kernels_1_0_12, cf_ge_kernels_1_0_13, cf_ge_kernels_1_0_14, cf_ge_kernels_1_0_15, cf_ge_kernels_1_0_16},
-     {cf_ge_kernels_1_1_0, cf_ge_kernels_1_1_1, cf_ge_kernels_1_1_2, cf_ge_kernels_1_1_3, cf_ge_kernels_1_1_4, cf_ge_kernels_1_1_5, cf_ge_kernels_1_1_6, cf_ge_kernels_1_1_7, cf_ge_kernels_1_1_8, cf_ge_kernels_1_1_9, cf_ge_kernels_1_1_10, cf_ge_kernels_1_1_11, cf_ge_kernels_1_1_12, cf_ge_kernels_1_1_13, cf_ge_kernels_1_1_14, cf_ge_kernels_1_1_15, cf_ge_kernels_1_1_16}}};
+constexpr int kNumParts = 21;
+#define CF_ROW10(F, N)                                                                               \
+  cf_ge_kernels_##F##_##N##_0, cf_ge_kernels_##F##_##N##_1, cf_ge_kernels_##F##_##N##_2,             \
+      cf_ge_kernels_##F##_##N##_3, cf_ge_kernels_##F##_##N##_4, cf_ge_kernels_##F##_##N##_5,         \
+      cf_ge_kernels_##F##_##N##_6, cf_ge_kernels_##F##_##N##_7, cf_ge_kernels_##F##_##N##_8,         \
+      cf_ge_kernels_##F##_##N##_9
+#define CF_ROW_EXTRA(N)                                                                              \
+  cf_ge_kernels_0_##N##_10, cf_ge_kernels_0_##N##_11, cf_ge_kernels_0_##N##_12,                      \
+      cf_ge_kernels_0_##N##_13, cf_ge_kernels_0_##N##_14, cf_ge_kernels_0_##N##_15,                  \
+      cf_ge_kernels_0_##N##_16, cf_ge_kernels_0_##N##_17, cf_ge_kernels_0_##N##_18,                  \
+      cf_ge_kernels_0_##N##_19, cf_ge_kernels_0_##N##_20
+static const PartFn kParts[2][2][kNumParts] = {
+    {{CF_ROW10(0, 0), CF_ROW_EXTRA(0)}, {CF_ROW10(0, 1), CF_ROW_EXTRA(1)}},
+    {{CF_ROW10(1, 0)}, {CF_ROW10(1, 1)}}};   // fp32 inputs: parts 10-20 absent (null)
 
+static const void* part(bool in_f32, bool b_nk, int i, int pre) {
+  const PartFn f = kParts[in_f32][b_nk][i];
+  return f ? f(pre) : nullptr;
+}
+
+// Null when no instantiation serves the combination (the C ABI refuses those
+// before it gets here).
 static const void* pick(const GemmEpilogueParams& p, bool in_f32, bool b_nk, bool vec) {
   // two row stages: fast path only, one part per (first, second) row op
   if (p.row_op2 != 0) {
     const bool ok = vec && p.row_op >= 1 && p.row_op <= 3 && p.row_op2 >= 1 && p.row_op2 <= 3;
-    return ok ? kParts[in_f32][b_nk][6 + 3 * (p.row_op - 1) + (p.row_op2 - 1)](
-                    (p.bias != nullptr || p.residual != nullptr) ? 1 : 0)
+    return ok ? part(in_f32, b_nk, 10 + 3 * (p.row_op - 1) + (p.row_op2 - 1),
+                     (p.bias != nullptr || p.residual != nullptr) ? 1 : 0)
               : nullptr;
   }
   if (p.row_op == 5)   // top-k: lists of 4 when k <= 4, else of 8
-    return vec ? kParts[in_f32][b_nk][p.topk <= 4 ? 16 : 15]((p.bias != nullptr) ? 1 : 0) : nullptr;
-  const int part = vec ? p.row_op : 5;
-  return kParts[in_f32][b_nk][part]((p.bias != nullptr || p.residual != nullptr) ? 1 : 0);
+    return vec ? part(in_f32, b_nk, p.topk <= 4 ? 20 : 19, (p.bias != nullptr) ? 1 : 0) : nullptr;
+  if (p.row_op < 0 || p.row_op > 4) return nullptr;
+  return part(in_f32, b_nk, vec ? p.row_op : 5 + p.row_op, (p.bias != nullptr || p.residual != nullptr) ? 1 : 0);
 }
 
 int gemm_epilogue_blocks_per_cu(const GemmEpilogueParams& p, bool in_f32, bool b_nk, bool vec) {
@@ -116,8 +141,10 @@ int gemm_epilogue_blocks_per_cu(const GemmEpilogueParams& p, bool in_f32, bool b
 
 hipError_t launch_gemm_epilogue(const GemmEpilogueParams& p, bool in_f32, bool b_nk, bool vec, int grid,
                                 hipStream_t stream) {
+  const void* k = pick(p, in_f32, b_nk, vec);
+  if (k == nullptr) return hipErrorInvalidDeviceFunction;
   void* args[] = {(void*)&p};
-  return hipLaunchKernel(pick(p, in_f32, b_nk, vec), dim3(grid), dim3(256), args, 0, stream);
+  return hipLaunchKernel(k, dim3(grid), dim3(256), args, 0, stream);
 }
 
 // Clears a workspace with a fill kernel (no hipMemsetAsync, so the call can be

@@ -1316,8 +1316,8 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
 
 // kVec (fast path): vector loads, N a multiple of 8, bf16 or no residual; the
 // epilogue of whole column tiles is then specialised on kRow (cf_row_op) and
-// kPre (bias/residual present). The general path (kVec false) dispatches on
-// p.row_op at run time.
+// kPre (bias/residual present). The general path (kVec false) is specialised
+// on kRow only and masks every access element by element.
 // kRow2 (with kVec and kRow 1-3): the second row stage, see epilogue's ROW2.
 template <bool kF32, bool kBnk, bool kVec, int kRow, bool kPre, int kRow2 = 0>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
@@ -1464,13 +1464,7 @@ void gemm_epilogue_kernel(GemmEpilogueParams p) {
       else if (p.alpha == 1.0f && p.act == 0) epilogue<kRow, true, kPre, true>(acc, p, smem, strip, tn, tag, timed_out, tid_t);
       else epilogue<kRow, true, kPre, false>(acc, p, smem, strip, tn, tag, timed_out, tid_t);
     } else {
-      switch (p.row_op) {
-        case 1: epilogue<1, false, true, false>(acc, p, smem, strip, tn, tag, timed_out, tid_t); break;
-        case 2: epilogue<2, false, true, false>(acc, p, smem, strip, tn, tag, timed_out, tid_t); break;
-        case 3: epilogue<3, false, true, false>(acc, p, smem, strip, tn, tag, timed_out, tid_t); break;
-        case 4: epilogue<4, false, true, false>(acc, p, smem, strip, tn, tag, timed_out, tid_t); break;
-        default: epilogue<0, false, true, false>(acc, p, smem, strip, tn, tag, timed_out, tid_t); break;
-      }
+      epilogue<kRow, false, true, false>(acc, p, smem, strip, tn, tag, timed_out, tid_t);
     }
     __syncthreads();   // the next tile's operand stores reuse this LDS
   }

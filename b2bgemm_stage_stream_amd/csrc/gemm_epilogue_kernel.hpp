@@ -797,6 +797,7 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
           // flight together, merged in tile order
           constexpr int kPeers = 2;
           const uint64_t t0 = wall_clock64();
+          bool lost = false;   // a peer's list never arrived: the row's results become NaN (index -1)
           for (int tb = 1; tb < p.tiles_n; tb += kPeers) {
             uint64_t w[kPeers][2 * kL];
             uint32_t need = 0;
@@ -822,8 +823,9 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
                 if (all) need &= ~(1u << i);
               }
               if (!need) break;
-              if (timed_out || wall_clock64() - t0 > p.spin_ticks) {   // recorded; the values are not used
+              if (timed_out || wall_clock64() - t0 > p.spin_ticks) {   // recorded in the workspace header
                 timed_out = true;
+                lost = true;
                 break;
               }
               __builtin_amdgcn_s_sleep(2);
@@ -840,6 +842,13 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
                 }
                 topk_merge(tv, tc, pv, pc);
               }
+            }
+          }
+          if (lost) {
+#pragma unroll
+            for (int j = 0; j < kL; ++j) {
+              tv[j] = __int_as_float(0x7fc00000);
+              tc[j] = -1;
             }
           }
         }
@@ -889,6 +898,7 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
         float ra = 0.0f, rb = 0.0f, rn = 0.0f;
         if constexpr (ROW == 1 || ROW == 4) ra = -INFINITY;
         if constexpr (ROW == 4) rb = __int_as_float(0x7fffffff);
+        bool lost = false;   // a peer's partial never arrived: the row's results become NaN (index -1)
         for (int tb = 0; tb < p.tiles_n; tb += 8) {
           float va[8], vb[8];
           uint32_t need = 0;
@@ -920,8 +930,9 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
               }
             }
             if (!need) break;
-            if (timed_out || wall_clock64() - t0 > p.spin_ticks) {   // recorded; the values are not used
+            if (timed_out || wall_clock64() - t0 > p.spin_ticks) {   // recorded in the workspace header
               timed_out = true;
+              lost = true;
 #pragma unroll
               for (int j = 0; j < 8; ++j)
                 if (need & (1u << j)) va[j] = vb[j] = 0.0f;
@@ -949,6 +960,10 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
         }
         a = ra;
         b = rb;
+        if (lost) {
+          a = __int_as_float(0x7fc00000);
+          b = ROW == 4 ? __int_as_float(-1) : __int_as_float(0x7fc00000);
+        }
       }
       float2 st;
       if constexpr (ROW == 1) st = make_float2(a * kLog2e, 1.0f / b);
@@ -1104,6 +1119,7 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
           if constexpr (R2 != 3) publish(slots + (size_t)tn * 512 + 1, b, tag);
           const uint64_t t0 = wall_clock64();
           float ra = R2 == 1 ? -INFINITY : 0.0f, rb = 0.0f, rn = 0.0f;
+          bool lost = false;   // a peer's partial never arrived: the row's results become NaN
           for (int tb = 0; tb < p.tiles_n; tb += 8) {
             float va[8], vb[8];
             uint32_t need = 0;
@@ -1135,8 +1151,9 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
                 }
               }
               if (!need) break;
-              if (timed_out || wall_clock64() - t0 > p.spin_ticks) {   // recorded; the values are not used
+              if (timed_out || wall_clock64() - t0 > p.spin_ticks) {   // recorded in the workspace header
                 timed_out = true;
+                lost = true;
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
                   if (need & (1u << j)) va[j] = vb[j] = 0.0f;
@@ -1161,6 +1178,7 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
           }
           a = ra;
           b = rb;
+          if (lost) a = b = __int_as_float(0x7fc00000);
         }
         if constexpr (R2 == 1) rstat2[ml] = make_float2(a * kLog2e, 1.0f / b);
         else if constexpr (R2 == 2) rstat2[ml] = make_float2(a, rsqrtf(b / (float)p.N + p.eps2));

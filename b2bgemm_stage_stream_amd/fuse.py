@@ -241,14 +241,22 @@ def lower(fn: Callable, *example_args) -> "FusedFunction":
 
 
 class FusedFunction:
-    """Callable running a lowered plan on new arguments of the traced shapes."""
+    """Callable running a lowered plan on new arguments of the traced shapes.
+
+    A row reduction over several column tiles waits for the partial statistics
+    of the other workgroups of its row strip. If some of them never run
+    alongside (another kernel holds the compute units), the wait gives up after
+    the exchange time limit: the rows concerned come out as NaN and the
+    workspace records the timeout. ``check=True`` waits for the call and raises
+    RuntimeError in that case."""
 
     def __init__(self, plan: Plan):
         self.plan = plan
         self._ws = None
 
-    def __call__(self, *args, out_dtype=None):
-        from . import Workspace, cf_b2bgemm, cf_gemm_epilogue, make_epilogue, cf_gemm_epilogue_workspace_size
+    def __call__(self, *args, out_dtype=None, check: bool = False):
+        from . import (CF_OK, Workspace, cf_b2bgemm, cf_gemm_epilogue, cf_gemm_epilogue_workspace_size,
+                       cf_status_string, cf_workspace_status, make_epilogue)
         p = self.plan
         A, B = args[p.a], args[p.b]
         odt = out_dtype or A.dtype
@@ -268,6 +276,10 @@ class FusedFunction:
             self._ws = Workspace(str(A.device))
         ws = self._ws.get(cf_gemm_epilogue_workspace_size(M, N, A.shape[1], e))
         cf_gemm_epilogue(A, B, C, b_is_nk=p.b_transposed, epi=e, workspace=ws)
+        if check and ws is not None:
+            st = cf_workspace_status(ws)
+            if st != CF_OK:
+                raise RuntimeError(f"fused call failed on the device: {cf_status_string(st)}")
         res = {"y": C, "x": X}
         outs = tuple(res[o] for o in p.outputs)
         return outs[0] if len(outs) == 1 else outs

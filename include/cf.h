@@ -181,8 +181,12 @@ cf_status cf_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Reads the workspace error word (blocking copy; call after the stream has
  * synchronised). Returns CF_ERR_DEVICE_TIMEOUT if a strip exchange wait timed
- * out since the last cf_workspace_init (outputs of that call are invalid),
- * otherwise CF_OK. */
+ * out since the last cf_workspace_init, otherwise CF_OK. The rows whose wait
+ * timed out are NaN in every output of that call (row_index -1), so a timeout
+ * is visible in the results without this check. Waits time out only when the
+ * workgroups of one row strip do not run at the same time: the grid never
+ * exceeds the kernel's co-resident capacity, but kernels of other streams or
+ * processes on the same GPU can hold compute units meanwhile. */
 cf_status cf_workspace_status(const void* ws, void* stream);
 
 /* C[M,N] = epilogue(A[M,K] . B) -- one fused kernel; P is never written to
@@ -250,8 +254,9 @@ int cf_last_hip_error(void);
 const char* cf_version(void);
 
 /* Upper bound, in microseconds, of each strip-exchange wait (default 2e6).
- * A wait that exceeds it records CF_ERR_DEVICE_TIMEOUT in the workspace and
- * lets the kernel finish. Returns the previous value. */
+ * A wait that exceeds it records CF_ERR_DEVICE_TIMEOUT in the workspace,
+ * makes the rows concerned NaN and lets the kernel finish. Returns the
+ * previous value. */
 uint64_t cf_set_exchange_timeout_us(uint64_t us);
 
 #ifdef __cplusplus

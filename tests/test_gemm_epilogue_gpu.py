@@ -282,14 +282,23 @@ def test_exchange_timeout_is_reported_and_recoverable():
     e = cf.make_epilogue(**epi_of(w, dev))
     ws = cf.Workspace().get(cf.cf_gemm_epilogue_workspace_size(512, 4096, 256, e))
     C = torch.empty(512, 4096, dtype=torch.float32, device="cuda")
+    R = oracle_of(w, ref)
     old = cf.cf_set_exchange_timeout_us(0)
     try:
         seen = set()
         for _ in range(3):
+            C.fill_(0.0)
             cf.cf_gemm_epilogue(dev["A"], dev["B"], C, epi=e, workspace=ws)
             st = cf.cf_workspace_status(ws)
             assert st in (cf.CF_OK, cf.CF_ERR_DEVICE_TIMEOUT)
             seen.add(st)
+            # a row segment whose peers' statistics never arrived is NaN, every
+            # other element is exact; NaN appears exactly when a timeout is reported
+            G = P.gpu_to_f64(C)
+            nan = np.isnan(G)
+            assert nan.any() == (st == cf.CF_ERR_DEVICE_TIMEOUT)
+            ok = ~nan
+            assert np.abs(G[ok] - R[ok]).max(initial=0.0) <= P.MAX_ABS_BF16
             if st != cf.CF_OK:
                 cf.cf_workspace_init(ws)
                 assert cf.cf_workspace_status(ws) == cf.CF_OK

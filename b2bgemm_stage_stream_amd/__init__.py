@@ -75,6 +75,9 @@ _lib.cf_workspace_status.restype = _int
 _lib.cf_gemm_epilogue.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _int, _int, _vp, _i64, _int,
                                   _EPI_P, _vp, _sz, _vp]
 _lib.cf_gemm_epilogue.restype = _int
+_lib.cf_gemm_epilogue_noalloc.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _int, _int, _vp, _i64, _int,
+                                          _EPI_P, _vp]
+_lib.cf_gemm_epilogue_noalloc.restype = _int
 _lib.cf_b2bgemm.argtypes = [_i64, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _int,
                             _vp, _i64, _i64, _vp, _i64, _i64, _int, _int, _EPI_P, _vp]
 _lib.cf_b2bgemm.restype = _int
@@ -88,7 +91,7 @@ _lib.cf_set_exchange_timeout_us.argtypes = [ctypes.c_uint64]
 _lib.cf_set_exchange_timeout_us.restype = ctypes.c_uint64
 
 EXPORTED = ["cf_epilogue_init", "cf_gemm_epilogue_workspace_size", "cf_workspace_init",
-            "cf_workspace_status", "cf_gemm_epilogue", "cf_b2bgemm", "cf_status_string",
+            "cf_workspace_status", "cf_gemm_epilogue", "cf_gemm_epilogue_noalloc", "cf_b2bgemm", "cf_status_string",
             "cf_last_hip_error", "cf_version", "cf_set_exchange_timeout_us"]
 
 
@@ -266,6 +269,23 @@ def cf_gemm_epilogue(A, B, C, *, b_is_nk: bool = False, epi: Optional[cf_epilogu
     _check(_lib.cf_gemm_epilogue(M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), int(b_is_nk),
                                  _dtype_code(A), c_ptr, ldc, c_dt, ctypes.byref(epi),
                                  ws_ptr, ws_bytes, _stream(stream)), "cf_gemm_epilogue")
+
+
+def cf_gemm_epilogue_noalloc(A, B, C, *, b_is_nk: bool = False, epi: Optional[cf_epilogue] = None,
+                             stream=None) -> None:
+    """cf_gemm_epilogue without a workspace argument: the library's static
+    per-GPU scratch (16 MiB) serves the strip exchange, so nothing is
+    allocated. Calls that overlap on one GPU race."""
+    if epi is None:
+        epi = make_epilogue()
+    M, K = A.shape
+    N = B.shape[0] if b_is_nk else B.shape[1]
+    if C is not None and C.shape != (M, N):
+        raise ValueError(f"C must be [{M}, {N}]")
+    c_ptr, ldc, c_dt = (None, 0, CF_BF16) if C is None else (C.data_ptr(), _ld(C), _dtype_code(C))
+    _check(_lib.cf_gemm_epilogue_noalloc(M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), int(b_is_nk),
+                                         _dtype_code(A), c_ptr, ldc, c_dt, ctypes.byref(epi), _stream(stream)),
+           "cf_gemm_epilogue_noalloc")
 
 
 def cf_b2bgemm(A, B0, B1, O, *, b0_is_lk: bool = False, epi: Optional[cf_epilogue] = None,

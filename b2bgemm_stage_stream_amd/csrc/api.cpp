@@ -191,9 +191,51 @@ cf_status cf_workspace_status(const void* ws, void* stream) {
   return err ? CF_ERR_DEVICE_TIMEOUT : CF_OK;
 }
 
-cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-                           int64_t ldb, int b_is_nk, cf_dtype ab_dtype, void* C, int64_t ldc, cf_dtype c_dtype,
-                           const cf_epilogue* epi, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+// Scratch of the allocation-free entry point: one static device array per GPU
+// the library runs on, held until the process ends. Host code never uses the
+// array's name as an address (on the host it is only a stand-in for the
+// symbol): the device address comes from hipGetSymbolAddress, once per device.
+static constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+struct ScratchDevice {
+  void* ptr = nullptr;    // device address of `scratch` on this device
+  bool cleared = false;   // the clear kernel has been enqueued once
+};
+std::mutex g_scratch_mu;
+ScratchDevice g_scratch[64];
+
+// The current device's scratch address; its first use on a device enqueues a
+// clear of the whole array on `stream` (the exchange protocol needs a zeroed
+// epoch word and zeroed slots once).
+cf_status scratch_of_device(int dev, hipStream_t stream, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchDevice& sd = g_scratch[dev];
+  if (sd.ptr == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (ptr == nullptr || !aligned(ptr, 256)) return CF_ERR_WORKSPACE;
+    sd.ptr = ptr;
+  }
+  if (!sd.cleared) {
+    const hipError_t e = cf::launch_workspace_clear(sd.ptr, kScratchBytes, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    sd.cleared = true;
+  }
+  *out = sd.ptr;
+  return CF_OK;
+}
+
+// cf_gemm_epilogue, with the caller's workspace (use_scratch false) or the
+// library's static scratch (use_scratch true; ws and ws_bytes are ignored).
+cf_status gemm_epilogue_run(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                            int64_t ldb, int b_is_nk, cf_dtype ab_dtype, void* C, int64_t ldc, cf_dtype c_dtype,
+                            const cf_epilogue* epi, void* ws, size_t ws_bytes, void* stream, bool use_scratch) {
   // ---- argument checks (no HIP calls)
   if (M < 0 || N < 0 || K < 0) return CF_ERR_INVALID_ARGUMENT;
   if (!is_dtype(ab_dtype) || !is_dtype(c_dtype)) return CF_ERR_INVALID_ARGUMENT;
@@ -229,7 +271,11 @@ cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K, const void* A, int64
 
   const GemmPlan plan = plan_gemm(M, N, epi);
   if (plan.exchange) {
-    if (!ws || !aligned(ws, 256) || ws_bytes < plan.ws_bytes) return CF_ERR_WORKSPACE;
+    if (use_scratch) {
+      if (plan.ws_bytes > kScratchBytes) return CF_ERR_WORKSPACE;
+    } else if (!ws || !aligned(ws, 256) || ws_bytes < plan.ws_bytes) {
+      return CF_ERR_WORKSPACE;
+    }
   }
 
   // fast path: 16-byte accesses everywhere, bf16 (or no) residual; a ragged
@@ -248,6 +294,10 @@ cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K, const void* A, int64
   int dev;
   DeviceInfo info;
   if ((st = current_device(&dev, &info)) != CF_OK) return st;
+  if (use_scratch && plan.exchange) {
+    if ((st = scratch_of_device(dev, (hipStream_t)stream, &ws)) != CF_OK) return st;
+    ws_bytes = kScratchBytes;
+  }
 
   cf::GemmEpilogueParams p;
   std::memset(&p, 0, sizeof(p));
@@ -326,6 +376,24 @@ cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K, const void* A, int64
   }
   hipError_t e = cf::launch_gemm_epilogue(p, in_f32, b_is_nk != 0, vec, (int)grid, (hipStream_t)stream);
   return e == hipSuccess ? CF_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                           int64_t ldb, int b_is_nk, cf_dtype ab_dtype, void* C, int64_t ldc, cf_dtype c_dtype,
+                           const cf_epilogue* epi, void* ws, size_t ws_bytes, void* stream) {
+  return gemm_epilogue_run(M, N, K, A, lda, B, ldb, b_is_nk, ab_dtype, C, ldc, c_dtype, epi, ws, ws_bytes, stream,
+                           false);
+}
+
+cf_status cf_gemm_epilogue_noalloc(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                                   int64_t ldb, int b_is_nk, cf_dtype ab_dtype, void* C, int64_t ldc,
+                                   cf_dtype c_dtype, const cf_epilogue* epi, void* stream) {
+  return gemm_epilogue_run(M, N, K, A, lda, B, ldb, b_is_nk, ab_dtype, C, ldc, c_dtype, epi, nullptr, 0, stream,
+                           true);
 }
 
 cf_status cf_b2bgemm(int64_t batch, int64_t M, int64_t K, int64_t L, int64_t N, const void* A, int64_t lda,

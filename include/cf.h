@@ -212,6 +212,25 @@ cf_status cf_gemm_epilogue(int64_t M, int64_t N, int64_t K,
                            void* C, int64_t ldc, cf_dtype c_dtype,
                            const cf_epilogue* epi, void* ws, size_t ws_bytes, void* stream);
 
+/* cf_gemm_epilogue without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, kernels, results and
+ * errors as cf_gemm_epilogue, minus ws/ws_bytes: the strip exchange uses a
+ * static device array of the library (16 MiB = 16777216 bytes per GPU, held
+ * by each GPU the library runs on until the process ends). A problem whose
+ * cf_gemm_epilogue_workspace_size() exceeds 16 MiB returns CF_ERR_WORKSPACE
+ * before any HIP call. The first call on a device enqueues a clear of the
+ * array on `stream`; no call allocates or frees memory. All calls on one GPU
+ * share that array: calls that overlap in time on one GPU (concurrent
+ * streams, or threads) race and must be serialised by the caller. A strip
+ * exchange that times out leaves the rows concerned NaN (as in
+ * cf_gemm_epilogue); its status word is not readable through this entry. */
+cf_status cf_gemm_epilogue_noalloc(int64_t M, int64_t N, int64_t K,
+                                   const void* A, int64_t lda,
+                                   const void* B, int64_t ldb, int b_is_nk, cf_dtype ab_dtype,
+                                   void* C, int64_t ldc, cf_dtype c_dtype,
+                                   const cf_epilogue* epi, void* stream);
+
 /* Back-to-back GEMM, one fused kernel per call (ComFuse review, Referee Report
  * major comment 2, paper Sec. IV-A, Eqs. (2)-(5); Fig. 5):
  *   S = alpha * A . B0 (+ bias[l]),  P = F(S),  O = P . B1

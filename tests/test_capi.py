@@ -197,3 +197,27 @@ def test_valid_calls_report_no_device():
     assert b2b(mid=epi(row_op=1, alpha=0.125)) == cf.CF_ERR_NO_DEVICE
     assert b2b(lk=1, mid=epi(row_op=1, alpha=0.125, mask=1)) == cf.CF_ERR_NO_DEVICE
     assert lib.cf_workspace_init(PW, 4096, None) == cf.CF_ERR_NO_DEVICE
+
+
+def noalloc(M=64, N=64, K=64, A=PA, lda=64, B=PB, ldb=64, nk=0, abt=1, C=PC, ldc=64, ct=1, epi=None):
+    return lib.cf_gemm_epilogue_noalloc(M, N, K, A, lda, B, ldb, nk, abt, C, ldc, ct,
+                                        ctypes.byref(epi) if epi is not None else None, None)
+
+
+def test_noalloc_argument_checks():
+    # the same checks as cf_gemm_epilogue, before any HIP call
+    assert noalloc(M=-1) == cf.CF_ERR_INVALID_ARGUMENT
+    assert noalloc(lda=63) == cf.CF_ERR_INVALID_ARGUMENT
+    assert noalloc(epi=epi(row_op=9)) == cf.CF_ERR_INVALID_ARGUMENT
+    assert noalloc(M=0) == cf.CF_OK
+    # beyond the 16 MiB scratch: top-8 over 8192 x 4096 needs 16 MiB of slots + the header
+    big = epi(row_op=5, row_index=PW, topk=8)
+    assert cf.cf_gemm_epilogue_workspace_size(8192, 4096, 64, big) > (16 << 20)
+    assert noalloc(M=8192, N=4096, ldb=4096, C=None, ldc=0, epi=big) == cf.CF_ERR_WORKSPACE
+    # C3's RMSNorm exchange (4 MiB) fits
+    assert cf.cf_gemm_epilogue_workspace_size(16384, 4096, 64, epi(row_op=3)) <= (16 << 20)
+
+
+@pytest.mark.skipif(gpu_present(), reason="would launch on fake pointers; valid calls are covered by the GPU tests")
+def test_noalloc_valid_call_reports_no_device():
+    assert noalloc(N=4096, ldb=4096, ldc=4096, epi=epi(row_op=2)) == cf.CF_ERR_NO_DEVICE

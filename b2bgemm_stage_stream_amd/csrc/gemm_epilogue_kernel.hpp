@@ -785,12 +785,14 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
         topk_merge(tv, tc, bv, bc);
       }
       if (p.ws_hdr != nullptr && row_ok) {
-        uint64_t* slots = p.ws_slots + (size_t)strip * p.tiles_n * (256 * 2 * kL) + (size_t)ml * 2 * kL;
+        // word j of row ml of tile t at t * (256 * 2 kL) + j * 256 + ml: each
+        // store instruction writes whole contiguous lines
+        uint64_t* slots = p.ws_slots + (size_t)strip * p.tiles_n * (256 * 2 * kL) + (size_t)ml;
         if (tn != 0) {
 #pragma unroll
           for (int j = 0; j < kL; ++j) {
-            publish(slots + (size_t)tn * (256 * 2 * kL) + j, tv[j], tag);
-            publish(slots + (size_t)tn * (256 * 2 * kL) + kL + j, __int_as_float(tc[j]), tag);
+            publish(slots + (size_t)tn * (256 * 2 * kL) + j * 256, tv[j], tag);
+            publish(slots + (size_t)tn * (256 * 2 * kL) + (kL + j) * 256, __int_as_float(tc[j]), tag);
           }
         } else {
           // the peers' lists, kPeers tiles at a time with all their loads in
@@ -812,7 +814,7 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
                   const uint64_t* ps = slots + (size_t)(tb + i) * (256 * 2 * kL);
 #pragma unroll
                   for (int j = 0; j < 2 * kL; ++j)
-                    w[i][j] = __hip_atomic_load(ps + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    w[i][j] = __hip_atomic_load(ps + j * 256, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
               }
 #pragma unroll
@@ -887,9 +889,11 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
         b = take1 ? w1.y : w0.y;
       }
       if (p.ws_hdr != nullptr && row_ok) {
-        uint64_t* slots = p.ws_slots + (size_t)strip * p.tiles_n * 512 + 2 * ml;
+        // word w (0: a, 1: b) of row ml of tile t at t * 512 + w * 256 + ml, so
+        // that each store instruction writes whole contiguous lines
+        uint64_t* slots = p.ws_slots + (size_t)strip * p.tiles_n * 512 + ml;
         publish(slots + (size_t)tn * 512, a, tag);
-        if constexpr (ROW != 3) publish(slots + (size_t)tn * 512 + 1, b, tag);
+        if constexpr (ROW != 3) publish(slots + (size_t)tn * 512 + 256, b, tag);
         const uint64_t t0 = wall_clock64();
         // The peers' words are fetched 8 column tiles at a time with all loads
         // in flight together, and the words not yet published are polled again
@@ -916,7 +920,7 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
               if (need & (1u << j)) {
                 wa[j] = __hip_atomic_load(slots + (size_t)(tb + j) * 512, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if constexpr (ROW != 3)
-                  wb[j] = __hip_atomic_load(slots + (size_t)(tb + j) * 512 + 1, __ATOMIC_RELAXED,
+                  wb[j] = __hip_atomic_load(slots + (size_t)(tb + j) * 512 + 256, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);
               }
             }
@@ -1114,9 +1118,9 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
           b = 0.0f;
         }
         if (p.ws_hdr != nullptr && row_ok) {
-          uint64_t* slots = p.ws_slots2 + (size_t)strip * p.tiles_n * 512 + 2 * ml;
+          uint64_t* slots = p.ws_slots2 + (size_t)strip * p.tiles_n * 512 + ml;   // layout as in stage 1
           publish(slots + (size_t)tn * 512, a, tag);
-          if constexpr (R2 != 3) publish(slots + (size_t)tn * 512 + 1, b, tag);
+          if constexpr (R2 != 3) publish(slots + (size_t)tn * 512 + 256, b, tag);
           const uint64_t t0 = wall_clock64();
           float ra = R2 == 1 ? -INFINITY : 0.0f, rb = 0.0f, rn = 0.0f;
           bool lost = false;   // a peer's partial never arrived: the row's results become NaN
@@ -1137,7 +1141,7 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
                 if (need & (1u << j)) {
                   wa[j] = __hip_atomic_load(slots + (size_t)(tb + j) * 512, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                   if constexpr (R2 != 3)
-                    wb[j] = __hip_atomic_load(slots + (size_t)(tb + j) * 512 + 1, __ATOMIC_RELAXED,
+                    wb[j] = __hip_atomic_load(slots + (size_t)(tb + j) * 512 + 256, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT);
                 }
               }

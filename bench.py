@@ -36,7 +36,8 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (published)
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 (published)
 HBM_GBPS = 8000.0
 
-DEFAULT_WORKLOAD = "c2_gemm_layernorm"
+# the largest workload (16384 x 11008 x 4096 GEMM + residual + RMSNorm)
+DEFAULT_WORKLOAD = "c3_gemm_residual_rmsnorm"
 
 
 def parse():
@@ -59,6 +60,9 @@ def parse():
                     help="measured HBM bytes per launch (written from rocprofv3 counters)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="calibration: time a plain device copy of MIB MiB (for the byte counters)")
+    ap.add_argument("--ingest-counters", default=None, metavar="DIR",
+                    help="no GPU: read the rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv files under DIR "
+                         "(fetch_<workload>/, write_<workload>/, fetch_copy/, write_copy/) and write --traffic")
     ap.add_argument("--store-x", action="store_true",
                     help="GEMM + epilogue workloads: also store x, the input of the row operation, as a second "
                          "bf16 [M, N] output (e.g. the new residual stream of a pre-norm block)")
@@ -89,6 +93,73 @@ def kernel_source_hash() -> str:
         with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
+
+
+def _counter_rows(d: str):
+    """(kernel name, counter name, value) of every dispatch in the rocprofv3
+    counter-collection csv files under d."""
+    import csv
+    import glob
+    out = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                out.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"]), r.get("Dispatch_Id")))
+    return out
+
+
+def _per_dispatch(d: str, counter: str, match):
+    """Mean counter value per dispatch of the kernels whose name satisfies
+    `match`, and the most frequent such kernel name."""
+    rows = [r for r in _counter_rows(d) if r[1] == counter and match(r[0])]
+    if not rows:
+        raise SystemExit(f"no {counter} values for the kernel under {d}")
+    per = {}
+    for name, _, v, disp in rows:
+        per.setdefault((name, disp), 0.0)
+        per[(name, disp)] += v           # summed over the counter's instances
+    names = {}
+    for (name, _), _v in per.items():
+        names[name] = names.get(name, 0) + 1
+    top = max(names, key=names.get)
+    vals = [v for (name, _), v in per.items() if name == top]
+    return float(np.mean(vals)), top, len(vals)
+
+
+def ingest_counters(d: str, out_path: str) -> dict:
+    """profiles/traffic.json from the FETCH_SIZE / WRITE_SIZE runs: per-dispatch
+    KiB of each workload's fused kernel, scaled by what the same counters read
+    for a plain copy of known size (copy probe), and the sources they were
+    taken on (their hash)."""
+    def is_cf(n):
+        return "cf::" in n and "workspace_clear" not in n
+
+    def is_copy(n):
+        return "cf::" not in n
+
+    probe = json.load(open(os.path.join(d, "copy_probe.json")))
+    nbytes = probe["copy_probe_bytes_each_way"]
+    fk, _, _ = _per_dispatch(os.path.join(d, "fetch_copy"), "FETCH_SIZE", is_copy)
+    wk, _, _ = _per_dispatch(os.path.join(d, "write_copy"), "WRITE_SIZE", is_copy)
+    rec = {"kernel_source_hash": kernel_source_hash(),
+           "copy_probe": {"bytes_each_way": nbytes, "fetch_kib": fk, "write_kib": wk},
+           "factor_fetch": nbytes / (fk * 1024.0), "factor_write": nbytes / (wk * 1024.0),
+           "note": "HBM-side bytes per launch = counter KiB * 1024 * factor; the factors make a plain copy of "
+                   "known size read and write exactly its size",
+           "workloads": {}}
+    for sub in sorted(os.listdir(d)):
+        if not sub.startswith("fetch_") or sub == "fetch_copy":
+            continue
+        name = sub[len("fetch_"):]
+        f, kname, nd = _per_dispatch(os.path.join(d, sub), "FETCH_SIZE", is_cf)
+        w_, kname2, _ = _per_dispatch(os.path.join(d, "write_" + name), "WRITE_SIZE", is_cf)
+        rec["workloads"][name] = {"kernel": kname, "dispatches": nd, "fetch_kib": f, "write_kib": w_,
+                                  "fetch_bytes": f * 1024.0 * rec["factor_fetch"],
+                                  "write_bytes": w_ * 1024.0 * rec["factor_write"]}
+    with open(out_path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    return rec
 
 
 def copy_probe(mib: int, steps: int):
@@ -131,6 +202,19 @@ def bytes_of(w, store_x: bool = False, argmax: bool = False, topk: int = 0) -> f
     else:
         tot += d["batch"] * d["M"] * d["N"] * out_es
     return float(tot)
+
+
+def output_bytes(w, store_x: bool = False, argmax: bool = False, topk: int = 0) -> float:
+    """Bytes the kernel must write: the output (and X when stored); an argmax
+    or top-k writes only its indices and values per row."""
+    d = w.dims
+    out_es = 4 if w.params.get("out_dtype") == "f32" else 2
+    if w.kind == "gemm_epilogue":
+        tot = d["M"] * 8 * (topk or 1) if (argmax or topk) else d["M"] * d["N"] * out_es
+        if store_x:
+            tot += d["M"] * d["N"] * 2
+        return float(tot)
+    return float(d["batch"] * d["M"] * d["N"] * out_es)
 
 
 def is_f32(w) -> bool:
@@ -198,10 +282,43 @@ def make_call(w, dev, torch, cf, store_x: bool = False, causal: bool = False, ar
     return call, O, None, 0
 
 
+def host_cpu():
+    """CPU model, physical cores and logical CPUs of this host, from /proc/cpuinfo."""
+    model, phys = None, set()
+    cur = {}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f.read().splitlines() + [""]:
+                if not line.strip():
+                    if "core id" in cur:
+                        phys.add((cur.get("physical id", "0"), cur["core id"]))
+                    cur = {}
+                    continue
+                k, _, v = line.partition(":")
+                cur[k.strip()] = v.strip()
+                if k.strip() == "model name" and model is None:
+                    model = v.strip()
+    except OSError:
+        pass
+    return {"cpu_model": model, "physical_cores": len(phys) or None, "logical_cpus": os.cpu_count()}
+
+
+def blas_threads() -> int:
+    """Threads numpy's BLAS (the oracle's matmul) runs with."""
+    try:
+        import threadpoolctl
+        n = [i["num_threads"] for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+
 def cpu_baseline(w, raw, target_s: float, causal: bool = False, argmax: bool = False, row2=None, topk: int = 0):
-    """The fp64 oracle on a bounded sample of rows (rows are independent)."""
+    """The fp64 oracle on a bounded sample of rows (rows are independent). The
+    inputs are widened to fp64 once, outside the timed runs."""
     import oracle
-    ncores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     p = w.params
     d = w.dims
 
@@ -212,10 +329,12 @@ def cpu_baseline(w, raw, target_s: float, causal: bool = False, argmax: bool = F
     if w.kind == "gemm_epilogue":
         B = widen("B")
         vec = {k: widen(k) for k in ("bias", "gamma", "beta", "weight") if k in raw}
+        A_all = widen("A")
+        R_all = widen("residual") if "residual" in raw else None
 
         def run(rows):
-            A = widen("A")[:rows] if rows < d["M"] else widen("A")
-            R = widen("residual")[:rows] if "residual" in raw else None
+            A = A_all[:rows]
+            R = R_all[:rows] if R_all is not None else None
             g = vec.get("gamma", vec.get("weight"))
             if topk:
                 oracle.gemm_epilogue_topk(A, B, topk, alpha=p["alpha"], bias=vec.get("bias"), act=p["act"])
@@ -270,12 +389,17 @@ def cpu_baseline(w, raw, target_s: float, causal: bool = False, argmax: bool = F
         reps += 1
     tflops = reps * n * unit_flops / dt / 1e12
     rep_txt = f" x {reps} runs" if reps > 1 else ""
-    return {"value": tflops, "unit": "TFLOP/s", "cores": ncores, "kind": "oracle",
-            "sample": f"{n} of {total_units} {what} of the same workload{rep_txt}, fp64, {dt:.1f} s"}
+    return {"value": tflops, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{n} of {total_units} {what} of the same workload{rep_txt}, fp64, {dt:.1f} s",
+            **host_cpu()}
 
 
 def main():
     args = parse()
+    if args.ingest_counters:
+        rec = ingest_counters(args.ingest_counters, args.traffic)
+        print(json.dumps(rec["workloads"], indent=1))
+        return
     if args.copy_probe:
         copy_probe(args.copy_probe, args.steps)
         return
@@ -360,15 +484,23 @@ def main():
     in_f32 = is_f32(w)
     bound, unit, peak, achieved, intensity, ridge = roofline_of(w, kernel_ms, args.store_x, args.causal,
                                                                 args.argmax, args.topk)
-    traffic = None
+    # HBM-side bytes per launch from the byte counters, when they were taken on
+    # these kernel sources and this exact workload; the unfused intermediate's
+    # share is what the kernel writes beyond its output and the exchange
+    # workspace
+    traffic = intermediate = None
+    out_bytes = output_bytes(w, args.store_x, args.argmax, args.topk)
     if os.path.exists(args.traffic) and not (args.plain or args.store_x or args.causal or args.argmax or args.row2
                                              or args.topk or args.b_nk):
         try:
             rec = json.load(open(args.traffic))
             if rec.get("kernel_source_hash") == kernel_source_hash():
-                traffic = rec.get("bytes_per_launch", {}).get(args.workload)
-        except (OSError, ValueError):
-            traffic = None
+                t = rec.get("workloads", {}).get(args.workload)
+                if t:
+                    traffic = round(t["fetch_bytes"] + t["write_bytes"])
+                    intermediate = round(t["write_bytes"] - out_bytes - (ws_bytes or 0))
+        except (OSError, ValueError, KeyError):
+            traffic = intermediate = None
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -393,7 +525,8 @@ def main():
                      "arithmetic_intensity": round(intensity, 1), "ridge": round(ridge, 1)},
         "kernel_ms": round(kernel_ms, 4),
         "algorithmic_bytes": bytes_of(w, args.store_x, args.argmax, args.topk),
-        "intermediate_hbm_bytes": 0,
+        "intermediate_hbm_bytes": intermediate,
+        "output_bytes": out_bytes,
         "workspace_bytes": ws_bytes,
     }
     if not args.no_cpu_baseline:

@@ -3,9 +3,16 @@ against the fp64 oracle, through the C ABI.
 
 The oracle mirrors the one rounding the fused kernel must make: the second
 GEMM's left operand in bf16 (round_operand=True). The unrounded oracle is
-checked too, against a bar derived from that rounding (bf16 unit roundoff
-2^-9 on every operand element gives a relative Frobenius error of order 1e-3;
-the bar is 1e-2)."""
+checked too, against a bar derived from that rounding: round-to-nearest-even
+to bf16 (8 significant bits) moves each operand element by at most 2^-9 of
+its value, uniformly, so by 2^-9/sqrt(3) = 1.1e-3 of it in the rms; the
+second GEMM averages these independent errors over L terms with weights of
+both signs, which leaves the relative Frobenius error of O of that order
+(measured 1.5e-3 to 1.7e-3). The bar is 3e-3, below any error of twice the
+rounding's own size."""
+import concurrent.futures
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -19,7 +26,7 @@ import b2bgemm_stage_stream_amd as cf   # noqa: E402
 import oracle                           # noqa: E402
 import parity as P                      # noqa: E402
 
-REL_F_UNROUNDED = 1e-2
+REL_F_UNROUNDED = 3e-3
 
 
 def run(A, B0, B1, out_dtype, *, b0_is_lk, **epi):
@@ -47,6 +54,21 @@ def check(dev, ref, *, lk, what, alpha=1.0, act="none", row_op="none", bias=None
     P.assert_bf16_consistent(o16, o32, R, what + " bf16-out")
     print(f"{what}: relF {r:.2e} maxabs {m:.2e} (unrounded oracle relF {ru:.2e})", flush=True)
     return o32
+
+
+def oracle_heads(ref, heads_per_call=16, **kw):
+    """oracle.b2bgemm of every (batch, head) problem of ref, evaluated in
+    groups of heads on a few host threads (the problems are independent)."""
+    nb = ref["A"].shape[0]
+
+    def part(i):
+        sl = slice(i, min(nb, i + heads_per_call))
+        B0 = ref["B0"][sl] if ref["B0"].ndim == 3 else ref["B0"]
+        B1 = ref["B1"][sl] if ref["B1"].ndim == 3 else ref["B1"]
+        return oracle.b2bgemm(ref["A"][sl], B0, B1, **kw)
+
+    with concurrent.futures.ThreadPoolExecutor(min(16, os.cpu_count() or 4)) as ex:
+        return np.concatenate(list(ex.map(part, range(0, nb, heads_per_call))))
 
 
 # ---------------------------------------------------------------------------- the two workloads
@@ -239,25 +261,23 @@ def test_deterministic():
 
 # ---------------------------------------------------------------------------- full sizes, sampled
 
-def test_c4_full_size_sampled_rows():
+def test_c4_full_size_all_rows():
     w, dev, ref = P.inputs("c4_b2b_mlp_relu", seed=0)
     O = run(dev["A"], dev["B0"], dev["B1"], torch.float32, b0_is_lk=False, act="relu")
-    rows = np.sort(np.random.default_rng(1).choice(w.dims["M"], 2048, replace=False))
-    R = oracle.b2bgemm(ref["A"][:, rows], ref["B0"], ref["B1"], act="relu")
-    got = P.gpu_to_f64(O[:, torch.as_tensor(rows, device="cuda")])
-    r, m = P.assert_close(got, R, P.REL_F_BF16, P.MAX_ABS_BF16, "C4 full size, sampled rows")
+    R = oracle.b2bgemm(ref["A"], ref["B0"], ref["B1"], act="relu")
+    r, m = P.assert_close(P.gpu_to_f64(O), R, P.REL_F_BF16, P.MAX_ABS_BF16, "C4 full size")
+    o16 = run(dev["A"], dev["B0"], dev["B1"], torch.bfloat16, b0_is_lk=False, act="relu")
+    P.assert_bf16_consistent(o16, O, R, "C4 full size bf16")
     print(f"C4 full: relF {r:.2e} maxabs {m:.2e}", flush=True)
 
 
-def test_c5_full_size_sampled_heads():
+def test_c5_full_size_all_heads():
     w, dev, ref = P.inputs("c5_b2b_attention", seed=0)
     O = run(dev["A"], dev["B0"], dev["B1"], torch.float32, b0_is_lk=True, alpha=0.125, row_op="softmax")
-    heads = np.array([0, 1, 255, 511])
-    R = oracle.b2bgemm(ref["A"][heads], ref["B0"][heads], ref["B1"][heads], alpha=0.125, row_op="softmax",
-                       b0_layout="lk")
-    got = P.gpu_to_f64(O[torch.as_tensor(heads, device="cuda")])
-    r, m = P.assert_close(got, R, P.REL_F_BF16, P.MAX_ABS_BF16, "C5 full size, sampled heads")
-    assert torch.isfinite(O).all()
+    R = oracle_heads(ref, alpha=0.125, row_op="softmax", b0_layout="lk")
+    r, m = P.assert_close(P.gpu_to_f64(O), R, P.REL_F_BF16, P.MAX_ABS_BF16, "C5 full size, all heads")
+    o16 = run(dev["A"], dev["B0"], dev["B1"], torch.bfloat16, b0_is_lk=True, alpha=0.125, row_op="softmax")
+    P.assert_bf16_consistent(o16, O, R, "C5 full size bf16")
     print(f"C5 full: relF {r:.2e} maxabs {m:.2e}", flush=True)
 
 
@@ -304,14 +324,12 @@ def test_causal_general_kernel(M, L, lk):
         assert torch.all(o[:, : M - L] == 0)
 
 
-def test_causal_full_size_sampled_heads():
+def test_causal_full_size_all_heads():
     w, dev, ref = P.inputs("c5_b2b_attention", seed=0)
     O = run(dev["A"], dev["B0"], dev["B1"], torch.float32, b0_is_lk=True, alpha=0.125, row_op="softmax",
             mask="causal")
-    heads = [0, 77, 300, 511]
-    R = oracle.b2bgemm(ref["A"][heads], ref["B0"][heads], ref["B1"][heads], alpha=0.125, row_op="softmax",
-                       b0_layout="lk", causal=True)
-    P.assert_close(P.gpu_to_f64(O[heads]), R, P.REL_F_BF16, P.MAX_ABS_BF16, "causal C5 full size, sampled heads")
+    R = oracle_heads(ref, alpha=0.125, row_op="softmax", b0_layout="lk", causal=True)
+    P.assert_close(P.gpu_to_f64(O), R, P.REL_F_BF16, P.MAX_ABS_BF16, "causal C5 full size, all heads")
 
 
 # ---------------------------------------------------------------------------- log-sum-exp of the attention rows

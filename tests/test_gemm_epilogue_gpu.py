@@ -85,7 +85,7 @@ def test_f32_row_ops_multi_tile(row_op):
                              gamma=P.gpu_to_f64(g), beta=P.gpu_to_f64(b), eps=1e-5, act="relu")
     C = run(dev["A"], dev["B"], torch.float32, bias=dev["bias"], row_op=row_op, gamma=g, beta=b,
             eps=1e-5, act="relu")
-    P.assert_close(P.gpu_to_f64(C), R, P.REL_F_F32 * 10, P.MAX_ABS_F32 * 10, f"f32 {row_op}")
+    P.assert_close(P.gpu_to_f64(C), R, P.REL_F_F32, P.MAX_ABS_F32, f"f32 {row_op}")
 
 
 # ---------------------------------------------------------------------------- bf16 path
@@ -329,21 +329,16 @@ def test_deterministic_and_row_local():
 # ---------------------------------------------------------------------------- full sizes, sampled rows
 
 @pytest.mark.parametrize("name", ["c2_gemm_layernorm", "c3_gemm_residual_rmsnorm"])
-def test_full_size_sampled_rows(name):
+def test_full_size_all_rows(name):
+    # the full workload in the launch configuration bench.py times: every row
+    # (every strip of the exchange) against the oracle, fp32 and bf16 outputs
     w, dev, ref = P.inputs(name, seed=0)
-    rows = np.random.default_rng(0).choice(w.dims["M"], 48, replace=False)
-    rows = np.concatenate([rows, [0, w.dims["M"] - 1]])
-    R = oracle_of(w, ref, rows)
+    R = oracle_of(w, ref)
     kw = epi_of(w, dev)
     c32 = run(dev["A"], dev["B"], torch.float32, **kw)
-    got = P.gpu_to_f64(c32[torch.as_tensor(rows, device="cuda")])
-    r, m = P.assert_close(got, R, P.REL_F_BF16, P.MAX_ABS_BF16, f"{name} full size, sampled rows")
-    del c32
+    r, m = P.assert_close(P.gpu_to_f64(c32), R, P.REL_F_BF16, P.MAX_ABS_BF16, f"{name} full size")
     c16 = run(dev["A"], dev["B"], torch.bfloat16, **kw)
-    g16 = P.gpu_to_f64(c16[torch.as_tensor(rows, device="cuda")])
-    P.assert_bf16_within(g16, R, f"{name} full size bf16")
-    # every row of a LayerNorm/RMSNorm output is finite
-    assert torch.isfinite(c16.float()).all()
+    P.assert_bf16_consistent(c16, c32, R, f"{name} full size bf16")
     print(f"{name} full: relF {r:.2e} maxabs {m:.2e}", flush=True)
 
 
@@ -400,18 +395,15 @@ def test_x_out_general_path(shape):
     check_two_outputs(w, dev, ref, epi_of(w, dev), f"X general path {shape}")
 
 
-def test_x_out_full_size_sampled_rows():
+def test_x_out_full_size_all_rows():
     w, dev, ref = P.inputs("c3_gemm_residual_rmsnorm", seed=0)
-    rows = np.random.default_rng(1).choice(w.dims["M"], 24, replace=False)
-    rows = np.concatenate([rows, [0, w.dims["M"] - 1]])
     p = w.params
-    Yr, Xr = oracle.gemm_epilogue_with_x(ref["A"][rows], ref["B"], residual=ref["residual"][rows],
-                                         row_op="rmsnorm", gamma=ref["weight"], eps=p["eps"])
+    Yr, Xr = oracle.gemm_epilogue_with_x(ref["A"], ref["B"], residual=ref["residual"], row_op="rmsnorm",
+                                         gamma=ref["weight"], eps=p["eps"])
     y16, x16 = run_x(dev["A"], dev["B"], torch.bfloat16, torch.bfloat16, **epi_of(w, dev))
-    idx = torch.as_tensor(rows, device="cuda")
-    P.assert_bf16_within(P.gpu_to_f64(y16[idx]), Yr, "C3 full Y")
-    P.assert_bf16_within(P.gpu_to_f64(x16[idx]), Xr, "C3 full X")
-    assert not torch.isnan(x16.float()).any(), "X not fully written"
+    P.assert_bf16_within(P.gpu_to_f64(y16), Yr, "C3 full Y")
+    P.assert_bf16_within(P.gpu_to_f64(x16), Xr, "C3 full X")
+    assert P.metrics(P.gpu_to_f64(x16), oracle.round_bf16(Xr))[0] <= P.REL_F_BF16
 
 
 # ---------------------------------------------------------------------------- wide strips
@@ -660,15 +652,13 @@ def test_topk_relu_zero_ties(N):
     P.assert_close(P.gpu_to_f64(val), ov, 1e-5, 1e-4, "relu top-8 values")
 
 
-def test_topk_full_size_sampled_rows():
+def test_topk_full_size_all_rows():
     # C2 shape (8192 x 4096 x 4096, sixteen column tiles per strip), top-8 of
-    # sampled rows, in the launch configuration bench.py times
+    # every row, in the launch configuration bench.py times
     w, dev, ref = P.inputs("c2_gemm_layernorm", seed=0)
     idx, val, _ = run_topk(dev["A"], dev["B"], 8, False)
-    rows = np.concatenate([np.random.default_rng(3).choice(w.dims["M"], 24, replace=False), [0, w.dims["M"] - 1]])
-    X = oracle.elementwise_stage(oracle.matmul(ref["A"][rows], ref["B"]))
-    r = torch.as_tensor(rows, device="cuda")
-    check_topk(idx[r], val[r], X, 8, "top-8 C2 full size")
+    X = oracle.elementwise_stage(oracle.matmul(ref["A"], ref["B"]))
+    check_topk(idx, val, X, 8, "top-8 C2 full size")
 
 
 @pytest.mark.parametrize("k", [3, 8])
@@ -728,11 +718,9 @@ def test_argmax_nonfinite(N):
     assert torch.all(idx == 0) and torch.all(val == float("-inf"))
 
 
-def test_argmax_full_size_sampled_rows():
+def test_argmax_full_size_all_rows():
     # C2 shape as an LM-head-like greedy step: no logits written
     w, dev, ref = P.inputs("c2_gemm_layernorm", seed=0)
     idx, val, _ = run_argmax(dev["A"], dev["B"], False)
-    rows = np.concatenate([np.random.default_rng(2).choice(w.dims["M"], 30, replace=False), [0, w.dims["M"] - 1]])
-    X = oracle.elementwise_stage(oracle.matmul(ref["A"][rows], ref["B"]))
-    check_argmax(idx[torch.as_tensor(rows, device="cuda")], val[torch.as_tensor(rows, device="cuda")], X,
-                 "argmax C2 full size")
+    X = oracle.elementwise_stage(oracle.matmul(ref["A"], ref["B"]))
+    check_argmax(idx, val, X, "argmax C2 full size")

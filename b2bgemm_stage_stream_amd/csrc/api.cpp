@@ -11,6 +11,7 @@
 #include <mutex>
 
 #include "cf_launch.h"
+#include "cf_plan.h"
 
 namespace {
 
@@ -52,98 +53,13 @@ cf_status current_device(int* dev_out, DeviceInfo* info) {
   return CF_OK;
 }
 
-bool is_dtype(int d) { return d == CF_F32 || d == CF_BF16; }
-size_t dsize(cf_dtype d) { return d == CF_F32 ? 4 : 2; }
-bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+using cf::check_epilogue;
+using cf::GemmPlan;
+using cf::plan_gemm;
 
-// Bytes spanned by `rows` rows of leading dimension ld (elements of size es),
-// padded by `pad_rows` rows so that out-of-range tile rows stay below 2^31.
-bool fits31(int64_t rows, int64_t pad_rows, int64_t ld, size_t es) {
-  const long double b = (long double)(rows + pad_rows) * (long double)ld * (long double)es;
-  return b < 2147483648.0L;
-}
-
-constexpr int64_t kTile = 256;
-
-struct GemmPlan {
-  int64_t tiles_n = 0, strips = 0, tiles = 0;
-  bool exchange = false;
-  size_t slot_bytes = 0;   // one stage's exchange slots
-  size_t ws_bytes = 0;
-};
-
-GemmPlan plan_gemm(int64_t M, int64_t N, const cf_epilogue* epi) {
-  GemmPlan g;
-  g.tiles_n = (N + kTile - 1) / kTile;
-  g.strips = (M + kTile - 1) / kTile;
-  g.tiles = g.tiles_n * g.strips;
-  g.exchange = epi && epi->row_op != CF_ROW_NONE && g.tiles_n > 1;
-  if (g.exchange) {
-    // one slot set per reduction stage; top-k publishes up to 8 (value, column) pairs per row
-    const size_t words = epi->row_op == CF_ROW_TOPK ? 16 : 2;
-    const size_t slots = (size_t)g.strips * (size_t)g.tiles_n * (size_t)kTile * words * sizeof(uint64_t);
-    g.slot_bytes = ((slots + 255) / 256) * 256;
-    g.ws_bytes = cf::kWsHeaderBytes + g.slot_bytes * (epi->row_op2 != CF_ROW_NONE ? 2 : 1);
-  }
-  return g;
-}
-
-cf_status check_epilogue(const cf_epilogue* epi, int64_t N, bool allow_row_ops_norm, bool allow_residual) {
-  if (!epi) return CF_OK;
-  if (epi->struct_size != sizeof(cf_epilogue)) return CF_ERR_INVALID_ARGUMENT;
-  if (!std::isfinite(epi->alpha) || !std::isfinite(epi->eps) || epi->eps < 0.0f) return CF_ERR_INVALID_ARGUMENT;
-  if (epi->act != CF_ACT_NONE && epi->act != CF_ACT_RELU) return CF_ERR_INVALID_ARGUMENT;
-  if (epi->row_op < CF_ROW_NONE || epi->row_op > CF_ROW_TOPK) return CF_ERR_INVALID_ARGUMENT;
-  if (epi->row_op == CF_ROW_ARGMAX || epi->row_op == CF_ROW_TOPK) {
-    if (!epi->row_index || !aligned(epi->row_index, 4) || epi->gamma || epi->beta) return CF_ERR_INVALID_ARGUMENT;
-    if (!allow_residual) return CF_ERR_UNSUPPORTED;
-  } else if (epi->row_index) {
-    return CF_ERR_INVALID_ARGUMENT;
-  }
-  if (epi->row_op == CF_ROW_TOPK) {
-    if (epi->topk < 1 || epi->topk > 8 || epi->topk > N) return CF_ERR_INVALID_ARGUMENT;
-    if (epi->residual) return CF_ERR_UNSUPPORTED;   // its LDS staging area holds the lists
-  } else if (epi->topk != 0) {
-    return CF_ERR_INVALID_ARGUMENT;
-  }
-  if (!is_dtype(epi->vec_dtype) || !is_dtype(epi->residual_dtype)) return CF_ERR_INVALID_ARGUMENT;
-  const size_t vs = dsize(epi->vec_dtype);
-  if ((epi->bias && !aligned(epi->bias, vs)) || (epi->gamma && !aligned(epi->gamma, vs)) ||
-      (epi->beta && !aligned(epi->beta, vs)))
-    return CF_ERR_INVALID_ARGUMENT;
-  if (epi->residual) {
-    if (!allow_residual) return CF_ERR_UNSUPPORTED;
-    if (epi->ld_residual < N || epi->ld_residual < 1) return CF_ERR_INVALID_ARGUMENT;
-    if (!aligned(epi->residual, dsize(epi->residual_dtype))) return CF_ERR_INVALID_ARGUMENT;
-  }
-  if (epi->row_stats && (epi->row_op == CF_ROW_NONE || !aligned(epi->row_stats, 4))) return CF_ERR_INVALID_ARGUMENT;
-  if (epi->mask != CF_MASK_NONE && epi->mask != CF_MASK_CAUSAL) return CF_ERR_INVALID_ARGUMENT;
-  if (epi->mask != CF_MASK_NONE && (allow_residual || epi->row_op != CF_ROW_SOFTMAX)) return CF_ERR_UNSUPPORTED;
-  if (epi->x_out) {
-    if (!allow_residual) return CF_ERR_UNSUPPORTED;
-    if (epi->x_out_dtype != CF_BF16 && epi->x_out_dtype != CF_F32) return CF_ERR_INVALID_ARGUMENT;
-    if (epi->ld_x_out < N || epi->ld_x_out < 1) return CF_ERR_INVALID_ARGUMENT;
-    if (!aligned(epi->x_out, dsize(epi->x_out_dtype))) return CF_ERR_INVALID_ARGUMENT;
-  }
-  if (!allow_row_ops_norm) {
-    if (epi->row_op == CF_ROW_LAYERNORM || epi->row_op == CF_ROW_RMSNORM) return CF_ERR_UNSUPPORTED;
-    if (epi->gamma || epi->beta) return CF_ERR_UNSUPPORTED;
-  }
-  // second row stage: softmax / LayerNorm / RMSNorm after one of those three
-  if (epi->row_op2 < CF_ROW_NONE || epi->row_op2 > CF_ROW_ARGMAX) return CF_ERR_INVALID_ARGUMENT;
-  if (!std::isfinite(epi->eps2) || epi->eps2 < 0.0f) return CF_ERR_INVALID_ARGUMENT;
-  if (epi->row_op2 == CF_ROW_NONE) {
-    if (epi->gamma2 || epi->beta2 || epi->eps2 != 0.0f) return CF_ERR_INVALID_ARGUMENT;
-  } else {
-    if (!allow_residual) return CF_ERR_UNSUPPORTED;
-    const bool norm1 = epi->row_op == CF_ROW_SOFTMAX || epi->row_op == CF_ROW_LAYERNORM || epi->row_op == CF_ROW_RMSNORM;
-    if (!norm1 || epi->row_op2 == CF_ROW_ARGMAX) return CF_ERR_INVALID_ARGUMENT;
-    if (epi->beta2 && epi->row_op2 != CF_ROW_LAYERNORM) return CF_ERR_INVALID_ARGUMENT;
-    if ((epi->gamma2 && !aligned(epi->gamma2, vs)) || (epi->beta2 && !aligned(epi->beta2, vs)))
-      return CF_ERR_INVALID_ARGUMENT;
-  }
-  return CF_OK;
-}
+bool aligned(const void* p, size_t a) { return cf::plan_aligned(p, a); }
+bool is_dtype(int d) { return cf::plan_is_dtype(d); }
+size_t dsize(cf_dtype d) { return cf::plan_dsize(d); }
 
 }  // namespace
 
@@ -237,58 +153,17 @@ cf_status gemm_epilogue_run(int64_t M, int64_t N, int64_t K, const void* A, int6
                             int64_t ldb, int b_is_nk, cf_dtype ab_dtype, void* C, int64_t ldc, cf_dtype c_dtype,
                             const cf_epilogue* epi, void* ws, size_t ws_bytes, void* stream, bool use_scratch) {
   // ---- argument checks (no HIP calls)
-  if (M < 0 || N < 0 || K < 0) return CF_ERR_INVALID_ARGUMENT;
-  if (!is_dtype(ab_dtype) || !is_dtype(c_dtype)) return CF_ERR_INVALID_ARGUMENT;
-  if (b_is_nk != 0 && b_is_nk != 1) return CF_ERR_INVALID_ARGUMENT;
-  cf_status st = check_epilogue(epi, N, true, true);
-  if (st != CF_OK) return st;
-  if (M == 0 || N == 0) return CF_OK;
+  cf::GemmChecked chk;
+  cf_status st = cf::check_gemm(M, N, K, A, lda, B, ldb, b_is_nk, cf::ev(ab_dtype), C, ldc, cf::ev(c_dtype), epi, ws,
+                                use_scratch ? kScratchBytes : ws_bytes, !use_scratch, &chk);
+  if (st != CF_OK || chk.empty) return st;
+  const GemmPlan& plan = chk.plan;
+  const int row_op = chk.row_op;
+  const bool vec = chk.vec;
   const size_t es = dsize(ab_dtype), cs = dsize(c_dtype);
-  const bool argmax = epi && (epi->row_op == CF_ROW_ARGMAX || epi->row_op == CF_ROW_TOPK);
-  if (C ? ldc < N : !argmax) return CF_ERR_INVALID_ARGUMENT;
-  if (K > 0) {
-    if (!A || !B || lda < K) return CF_ERR_INVALID_ARGUMENT;
-    if (ldb < (b_is_nk ? K : N)) return CF_ERR_INVALID_ARGUMENT;
-    if (!aligned(A, es) || !aligned(B, es)) return CF_ERR_INVALID_ARGUMENT;
-  }
-  if (C && !aligned(C, cs)) return CF_ERR_INVALID_ARGUMENT;
-  if (M > INT32_MAX - kTile || N > INT32_MAX - kTile || K > INT32_MAX - kTile) return CF_ERR_UNSUPPORTED;
-  // 32-bit buffer offsets: every operand (plus one tile of padding) below 2 GiB
-  if (C && !fits31(M, kTile, ldc, cs)) return CF_ERR_UNSUPPORTED;
-  if (K > 0) {
-    if (!fits31(M, kTile, lda, es)) return CF_ERR_UNSUPPORTED;
-    if (b_is_nk ? !fits31(N, kTile, ldb, es) : !fits31(K, 64, ldb, es)) return CF_ERR_UNSUPPORTED;
-  }
   const cf_dtype rdt = (epi && epi->residual) ? epi->residual_dtype : CF_BF16;
-  if (epi && epi->residual && !fits31(M, kTile, epi->ld_residual, dsize(rdt))) return CF_ERR_UNSUPPORTED;
   void* const X = epi ? epi->x_out : nullptr;
   const size_t xs = X ? dsize(epi->x_out_dtype) : 2;
-  if (X && !fits31(M, kTile, epi->ld_x_out, xs)) return CF_ERR_UNSUPPORTED;
-  // top-1 is the row argmax (same order, ties and NaN ranking, same outputs)
-  const int row_op = (epi && epi->row_op == CF_ROW_TOPK && epi->topk == 1) ? (int)CF_ROW_ARGMAX
-                     : epi ? (int)epi->row_op : 0;
-  if (row_op != CF_ROW_NONE && N > 65536) return CF_ERR_UNSUPPORTED;
-
-  const GemmPlan plan = plan_gemm(M, N, epi);
-  if (plan.exchange) {
-    if (use_scratch) {
-      if (plan.ws_bytes > kScratchBytes) return CF_ERR_WORKSPACE;
-    } else if (!ws || !aligned(ws, 256) || ws_bytes < plan.ws_bytes) {
-      return CF_ERR_WORKSPACE;
-    }
-  }
-
-  // fast path: 16-byte accesses everywhere, bf16 (or no) residual; a ragged
-  // last column tile (N a multiple of 8) takes the masked epilogue
-  const int64_t ce = ab_dtype == CF_F32 ? 4 : 8;
-  bool vec = (N % 8 == 0) && (K % ce == 0) && (lda % ce == 0) && (ldb % ce == 0) &&
-             (!C || (ldc % 8 == 0 && aligned(C, 16))) && aligned(A, 16) && aligned(B, 16);
-  if (epi && epi->residual)
-    vec = vec && epi->residual_dtype == CF_BF16 && epi->ld_residual % 8 == 0 && aligned(epi->residual, 16);
-  if (X) vec = vec && epi->ld_x_out % 8 == 0 && aligned(X, 16);
-  // two row stages and top-k (k > 1): fast-path layouts and bf16 inputs only
-  if (epi && (epi->row_op2 != CF_ROW_NONE || row_op == CF_ROW_TOPK) && (!vec || ab_dtype != CF_BF16))
-    return CF_ERR_UNSUPPORTED;
 
   // ---- device
   int dev;
@@ -349,31 +224,11 @@ cf_status gemm_epilogue_run(int64_t M, int64_t N, int64_t K, const void* A, int6
   const bool in_f32 = ab_dtype == CF_F32;
   const int per_cu = cf::gemm_epilogue_blocks_per_cu(p, in_f32, b_is_nk != 0, vec);
   if (per_cu <= 0) return hip_fail(hipGetLastError());
-  const int64_t cap = (int64_t)per_cu * info.cus;
-  int64_t grid;
-  if (plan.exchange) {
-    // every strip must be processed by co-resident workgroups in one round
-    if (plan.tiles_n > cap) return CF_ERR_UNSUPPORTED;
-    grid = std::min<int64_t>(plan.tiles, (cap / plan.tiles_n) * plan.tiles_n);
-  } else {
-    grid = std::min<int64_t>(plan.tiles, cap);
-  }
-  // XCD rectangles: a round of `grid` tiles is (grid / tiles_n) strips x
-  // tiles_n columns; split it into 8 equal a x b rectangles with a + b minimal.
-  if (grid % 8 == 0 && grid % plan.tiles_n == 0) {
-    const int64_t S = grid / plan.tiles_n, per = grid / 8;
-    int64_t best = 0;
-    for (int64_t a = 1; a <= S; ++a) {
-      if (S % a || per % a) continue;
-      const int64_t b = per / a;
-      if (plan.tiles_n % b || (S / a) * (plan.tiles_n / b) != 8) continue;
-      if (!best || a + b < best + per / best) best = a;
-    }
-    if (best) {
-      p.xcd_a = (int)best;
-      p.xcd_b = (int)(per / best);
-    }
-  }
+  cf::GridPlan gp;
+  if ((st = cf::plan_grid(plan, per_cu, info.cus, &gp)) != CF_OK) return st;
+  const int64_t grid = gp.grid;
+  p.xcd_a = gp.xcd_a;
+  p.xcd_b = gp.xcd_b;
   hipError_t e = cf::launch_gemm_epilogue(p, in_f32, b_is_nk != 0, vec, (int)grid, (hipStream_t)stream);
   return e == hipSuccess ? CF_OK : hip_fail(e);
 }
@@ -401,7 +256,7 @@ cf_status cf_b2bgemm(int64_t batch, int64_t M, int64_t K, int64_t L, int64_t N, 
                      int64_t ldb1, int64_t sb1, void* O, int64_t ldo, int64_t so, cf_dtype in_dtype,
                      cf_dtype out_dtype, const cf_epilogue* mid, void* stream) {
   if (batch < 0 || M < 0 || K < 0 || L < 0 || N < 0) return CF_ERR_INVALID_ARGUMENT;
-  if (!is_dtype(in_dtype) || !is_dtype(out_dtype)) return CF_ERR_INVALID_ARGUMENT;
+  if (!is_dtype(cf::ev(in_dtype)) || !is_dtype(cf::ev(out_dtype))) return CF_ERR_INVALID_ARGUMENT;
   if (b0_is_lk != 0 && b0_is_lk != 1) return CF_ERR_INVALID_ARGUMENT;
   if (sa < 0 || sb0 < 0 || sb1 < 0 || so < 0) return CF_ERR_INVALID_ARGUMENT;
   cf_status st = check_epilogue(mid, L, false, false);

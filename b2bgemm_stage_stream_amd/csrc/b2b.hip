@@ -11,6 +11,12 @@
 // That is the same segmented sum, evaluated sequentially, with no exchange
 // between workgroups at all.
 //
+// Any K and N: GEMM1 runs over K in blocks of 16*KS (one pipeline step per
+// (segment, k-block), the A fragments of a block reloaded per step when there
+// is more than one), and O is split into column blocks of 32*NB, each its own
+// workgroup tile; a tile recomputes S and F for its column block (the softmax
+// evaluates the same online sequence in every block, so the blocks agree).
+//
 // Per wave (32 rows m):
 //   GEMM1: S^T[l][m] = sum_k B0^T[l][k] A^T[k][m] with v_mfma_f32_32x32x16_bf16
 //          (src0 = B0 chunk rows l, src1 = A rows m), so every accumulator
@@ -57,7 +63,8 @@ struct B2bCfg {
 
 }  // namespace
 
-// kExact: K == 16*KS, N == 32*NB and L a multiple of 64 (no column masks).
+// kExact: K == 16*KS, N == 32*NB and L a multiple of 64 (no column masks, one
+// k-block, one column block).
 template <int KS, int NB, bool kSoftmax, bool kB0LK, bool kExact>
 __global__ __launch_bounds__(kThreads) void b2b_kernel(B2bParams p) {
   using Cfg = B2bCfg<KS, NB, kSoftmax, kB0LK>;
@@ -66,23 +73,27 @@ __global__ __launch_bounds__(kThreads) void b2b_kernel(B2bParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, r32 = lane & 31;
   const int mtiles = (p.M + kBM - 1) / kBM;
-  const int tiles = p.batch * mtiles;
+  const int nblocks = kExact ? 1 : (p.N + 32 * NB - 1) / (32 * NB);   // column blocks of O
+  const int tiles = p.batch * mtiles * nblocks;
   const int nchunks = (p.L + kLC - 1) / kLC;
+  const int nkb = kExact ? 1 : (p.K + 16 * KS - 1) / (16 * KS);       // k-blocks of GEMM1
   const float scale = kSoftmax ? p.alpha * kLog2e : p.alpha;
   const float floor_v = p.act == 1 ? 0.0f : -INFINITY;
 
   for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
-    const int b = tile / mtiles;
+    const int nbk = tile % nblocks, rest = tile / nblocks;
+    const int b = rest / mtiles;
     // causal: work grows with the row tile; rotate it by the round when the
     // grid is a multiple of the tiles per batch entry (every workgroup then
     // gets each row position once) and take the tiles that see the most keys
     // first
-    int mt = tile - b * mtiles;
+    int mt = rest - b * mtiles;
     if (p.causal) {
-      if (gridDim.x % mtiles == 0) mt = (mt + tile / (int)gridDim.x) % mtiles;
+      if (nblocks == 1 && gridDim.x % mtiles == 0) mt = (mt + tile / (int)gridDim.x) % mtiles;
       mt = mtiles - 1 - mt;
     }
     const int m0 = mt * kBM;
+    const int n0 = nbk * 32 * NB;   // first column of O in this tile
     // causal: segments past the last key any row of the tile sees are skipped
     int nch = nchunks;
     if (p.causal) {
@@ -97,13 +108,14 @@ __global__ __launch_bounds__(kThreads) void b2b_kernel(B2bParams p) {
         make_rsrc(B0b, (uint32_t)((size_t)(kB0LK ? p.L : p.K) * p.ldb0 * 2));
     const __amdgpu_buffer_rsrc_t rsB1 = make_rsrc(B1b, (uint32_t)((size_t)p.L * p.ldb1 * 2));
 
-    // ---- A fragments of this wave's 32 rows (rows >= M read as zero, k >= K masked)
+    // ---- A fragments of this wave's 32 rows in k-block kb (rows >= M read as
+    // zero, k >= K masked)
     u32x4_t af[KS];
-    {
+    auto load_a = [&](int kb) {
       const uint32_t row = (uint32_t)(m0 + wave * 32 + r32);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int k = ks * 16 + 8 * h;
+        const int k = kb * 16 * KS + ks * 16 + 8 * h;
         if (kExact || k + 8 <= p.K) {
           af[ks] = buf_load_b128(rsA, (row * p.lda + (uint32_t)k) * 2);
         } else {
@@ -117,7 +129,8 @@ __global__ __launch_bounds__(kThreads) void b2b_kernel(B2bParams p) {
           af[ks] = v;
         }
       }
-    }
+    };
+    load_a(0);
 
     // ---- chunk staging: global -> registers -> LDS (B0 chunk as [l][k], B1^T as [n][perm l])
     // B0 [L][K] (lk): 64 x 2KS chunks of 16 B, thread t takes chunks t + 256 i.
@@ -145,13 +158,16 @@ __global__ __launch_bounds__(kThreads) void b2b_kernel(B2bParams p) {
       return v;
     };
 
-    auto load_chunk = [&](int lc) {
-      const int l0 = lc * kLC;
+    // pipeline step st = (segment st / nkb, k-block st % nkb): the B0 block of
+    // that segment and k-block, and with the last k-block the B1 segment
+    auto load_chunk = [&](int st) {
+      const int lc = st / nkb, kb = st - lc * nkb;
+      const int l0 = lc * kLC, k0 = kb * 16 * KS;
       if constexpr (kB0LK) {
 #pragma unroll
         for (int i = 0; i < kB0Regs; ++i) {
           const int id = tid + kThreads * i;
-          r0[i] = (id < kB0Chunks) ? piece(rsB0, l0 + id / (2 * KS), (id % (2 * KS)) * 8, p.ldb0, p.K)
+          r0[i] = (id < kB0Chunks) ? piece(rsB0, l0 + id / (2 * KS), k0 + (id % (2 * KS)) * 8, p.ldb0, p.K)
                                    : u32x4_t{0u, 0u, 0u, 0u};
         }
       } else {
@@ -161,18 +177,20 @@ __global__ __launch_bounds__(kThreads) void b2b_kernel(B2bParams p) {
           const int kq = blk / (kLC / 8), lg = blk % (kLC / 8);
 #pragma unroll
           for (int i = 0; i < 4; ++i)   // rows k >= K read as zero (range check)
-            r0[4 * bi + i] = (blk < kB0Blocks) ? piece(rsB0, kq * 4 + i, l0 + lg * 8, p.ldb0, p.L)
+            r0[4 * bi + i] = (blk < kB0Blocks) ? piece(rsB0, k0 + kq * 4 + i, l0 + lg * 8, p.ldb0, p.L)
                                                : u32x4_t{0u, 0u, 0u, 0u};
         }
       }
+      if (kb == nkb - 1) {
 #pragma unroll
-      for (int bi = 0; bi < kB1Regs / 4; ++bi) {
-        const int blk = tid + kThreads * bi;
-        const int lq = blk / (NB * 4), ng = blk % (NB * 4);
+        for (int bi = 0; bi < kB1Regs / 4; ++bi) {
+          const int blk = tid + kThreads * bi;
+          const int lq = blk / (NB * 4), ng = blk % (NB * 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)     // rows l >= L read as zero (range check)
-          r1[4 * bi + i] = (blk < kB1Blocks) ? piece(rsB1, l0 + lq * 4 + i, ng * 8, p.ldb1, p.N)
-                                             : u32x4_t{0u, 0u, 0u, 0u};
+          for (int i = 0; i < 4; ++i)   // rows l >= L read as zero (range check), columns >= N as zero
+            r1[4 * bi + i] = (blk < kB1Blocks) ? piece(rsB1, l0 + lq * 4 + i, n0 + ng * 8, p.ldb1, p.N)
+                                               : u32x4_t{0u, 0u, 0u, 0u};
+        }
       }
     };
 
@@ -189,7 +207,8 @@ __global__ __launch_bounds__(kThreads) void b2b_kernel(B2bParams p) {
       return o;
     };
 
-    auto store_chunk = [&](int buf) {
+    auto store_chunk = [&](int buf, int st) {
+      const bool with_b1 = st % nkb == nkb - 1;
       uint8_t* s0 = smem + buf * Cfg::kStage;
       uint8_t* s1 = s0 + Cfg::kB0Bytes;
       if constexpr (kB0LK) {
@@ -215,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void b2b_kernel(B2bParams p) {
 #pragma unroll
       for (int bi = 0; bi < kB1Regs / 4; ++bi) {
         const int blk = tid + kThreads * bi;
-        if (blk < kB1Blocks) {
+        if (with_b1 && blk < kB1Blocks) {
           const int lq = blk / (NB * 4), ng = blk % (NB * 4);
           // The block holds l' = 4 sub + i (i = 0..3) of 16-chunk c16. Position of
           // l' in the permuted order: 8 ((l' >> 2) & 1) + 4 (l' >> 3) + (l' & 3)
@@ -236,22 +255,25 @@ __global__ __launch_bounds__(kThreads) void b2b_kernel(B2bParams p) {
     float cst = -INFINITY;   // softmax: integer stabiliser of this row (same in both lane halves)
     float lsum = 0.0f;       // softmax: this lane's part of the unrounded row sum
 
-    if (nch > 0) {
+    const int nsteps = nch * nkb;
+    if (nsteps > 0) {
       load_chunk(0);
-      store_chunk(0);
-      if (nch > 1) load_chunk(1);
+      store_chunk(0, 0);
+      if (nsteps > 1) load_chunk(1);
     }
     __syncthreads();
 
     const int my_row = m0 + wave * 32 + r32;
-    for (int lc = 0; lc < nch; ++lc) {
-      const uint8_t* s0 = smem + (lc & 1) * Cfg::kStage;
+    f32x16_t sacc[2];
+    for (int stp = 0; stp < nsteps; ++stp) {
+      const int lc = stp / nkb, kb = stp - lc * nkb;
+      const uint8_t* s0 = smem + (stp & 1) * Cfg::kStage;
       const uint8_t* s1 = s0 + Cfg::kB0Bytes;
-      // GEMM1: two 32-blocks of l
-      f32x16_t sacc[2];
+      if (nkb > 1 && stp > 0) load_a(kb);
+      // GEMM1: two 32-blocks of l, accumulated over the k-blocks
 #pragma unroll
       for (int lb = 0; lb < 2; ++lb) {
-        sacc[lb] = f32x16_t{0};
+        if (kb == 0) sacc[lb] = f32x16_t{0};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const u32x4_t bf = *(const u32x4_t*)(s0 + swz(lb * 32 + r32, 2 * ks + h, Cfg::kB0Cpr));
@@ -259,9 +281,13 @@ __global__ __launch_bounds__(kThreads) void b2b_kernel(B2bParams p) {
                                                               __builtin_bit_cast(bf16x8_t, af[ks]), sacc[lb], 0, 0, 0);
         }
       }
-      // the next chunk goes to the other LDS buffer while this one is consumed
-      if (lc + 1 < nch) store_chunk((lc + 1) & 1);
-      if (lc + 2 < nch) load_chunk(lc + 2);
+      // the next step's blocks go to the other LDS buffer while this one is consumed
+      if (stp + 1 < nsteps) store_chunk((stp + 1) & 1, stp + 1);
+      if (stp + 2 < nsteps) load_chunk(stp + 2);
+      if (kb != nkb - 1) {
+        __syncthreads();
+        continue;
+      }
 
       // F on registers; l of register r of block lb: lc*64 + lb*32 + 8(r>>2) + 4h + (r&3)
       const int lbase = lc * kLC + 4 * h;
@@ -346,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void b2b_kernel(B2bParams p) {
       const float ls = sum_halves(lsum);
       inv = ls > 0.0f ? 1.0f / ls : 0.0f;   // 0 only for a causal row that sees no key
       // log-sum-exp of the row: sum exp(alpha s) = 2^c * ls
-      if (p.row_stats != nullptr && h == 0 && row < (uint32_t)p.M)
+      if (p.row_stats != nullptr && nbk == 0 && h == 0 && row < (uint32_t)p.M)
         p.row_stats[(size_t)b * p.M + row] = ls > 0.0f ? (cst + log2f(ls)) * kLn2 : -INFINITY;
     }
     const __amdgpu_buffer_rsrc_t rsO = make_rsrc((uint8_t*)p.O + (size_t)b * p.so * (p.out_f32 ? 4 : 2),
@@ -355,7 +381,7 @@ __global__ __launch_bounds__(kThreads) void b2b_kernel(B2bParams p) {
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = nb * 32 + 8 * q + 4 * h;
+        const int n = n0 + nb * 32 + 8 * q + 4 * h;
         float y[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) y[e] = oacc[nb][4 * q + e] * inv;
@@ -402,8 +428,9 @@ const void* pick_kn(int KS, int NB, bool exact) {
   return nullptr;
 }
 
-int ks_of(int K) { return K <= 16 ? 1 : K <= 32 ? 2 : K <= 64 ? 4 : K <= 128 ? 8 : 0; }
-int nb_of(int N) { return N <= 32 ? 1 : N <= 64 ? 2 : N <= 128 ? 4 : 0; }
+// K above 128 runs in k-blocks of 128, N above 128 in column blocks of 128
+int ks_of(int K) { return K <= 16 ? 1 : K <= 32 ? 2 : K <= 64 ? 4 : 8; }
+int nb_of(int N) { return N <= 32 ? 1 : N <= 64 ? 2 : 4; }
 
 const void* pick(const B2bParams& p) {
   const int KS = ks_of(p.K), NB = nb_of(p.N);
@@ -419,11 +446,10 @@ const void* pick(const B2bParams& p) {
 bool b2b_supported(const B2bParams& p) {
   if (p.row_op != 0 && p.row_op != 1) return false;
   if (p.K < 1 || p.L < 1 || p.N < 1) return false;
-  if (p.K > 128 || p.N > 128) return false;
   // 32-bit buffer offsets within one batch
   const uint64_t lim = 1ull << 31;
   if ((uint64_t)(p.M + kBM) * p.lda * 2 >= lim) return false;
-  if ((uint64_t)(p.b0_lk ? p.L + kLC : p.K) * p.ldb0 * 2 >= lim) return false;
+  if ((uint64_t)(p.b0_lk ? p.L + kLC : p.K + 128) * p.ldb0 * 2 >= lim) return false;
   if ((uint64_t)(p.L + kLC) * p.ldb1 * 2 >= lim) return false;
   if ((uint64_t)(p.M + kBM) * p.ldo * 4 >= lim) return false;
   return pick(p) != nullptr;
@@ -438,7 +464,9 @@ hipError_t launch_b2b(const B2bParams& p, hipStream_t stream) {
   const void* k = ks ? ks : pick(p);
   if (!k) return hipErrorNotSupported;
   if ((e = blocks_per_cu_cached(k, kThreads, &per_cu)) != hipSuccess) return e;
-  const long tiles = (long)p.batch * ((p.M + bm - 1) / bm);
+  // the general kernel's tiles also run over the column blocks of O
+  const long nblocks = ks ? 1 : (p.N + 32 * nb_of(p.N) - 1) / (32 * nb_of(p.N));
+  const long tiles = (long)p.batch * ((p.M + bm - 1) / bm) * nblocks;
   const long cap = (long)(per_cu > 0 ? per_cu : 1) * cus;
   long g = tiles < cap ? tiles : cap;
   if (ks && g >= 8) g -= g % 8;   // the streamed kernel maps workgroups to XCDs in groups of 8

@@ -4,12 +4,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "cf_plan.h"
+
 namespace cf {
 
 // Workspace header words (uint32 index into the header); the header is
 // kWsHeaderBytes long and followed by the partial-statistics slots.
 enum : int { kHdrEpoch = 0, kHdrDone = 32, kHdrError = 64 };
-constexpr size_t kWsHeaderBytes = 512;
 
 // Output tile of one workgroup in the GEMM + epilogue kernel.
 constexpr int kGemmBM = 256;

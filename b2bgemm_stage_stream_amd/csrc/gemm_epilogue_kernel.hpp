@@ -1370,13 +1370,7 @@ void gemm_epilogue_kernel(GemmEpilogueParams p) {
     // XCDs (workgroup w on XCD w % 8); in a full round each XCD takes an
     // xcd_a x xcd_b rectangle of (strip, column) tiles so that its workgroups
     // share A strips and B panels in that XCD's L2.
-    int tile = base + (int)blockIdx.x;
-    if (p.xcd_a > 0 && base + (int)gridDim.x <= p.tiles) {
-      const int x = (int)blockIdx.x & 7, i = (int)blockIdx.x >> 3;
-      const int rects_n = p.tiles_n / p.xcd_b;
-      const int rx = x / rects_n, ry = x - rx * rects_n;
-      tile = (base / p.tiles_n + rx * p.xcd_a + i / p.xcd_b) * p.tiles_n + ry * p.xcd_b + i % p.xcd_b;
-    }
+    const int tile = round_tile(base, (int)blockIdx.x, (int)gridDim.x, p.tiles, p.tiles_n, p.xcd_a, p.xcd_b);
     if (tile >= p.tiles) break;
     const int strip = tile / p.tiles_n, tn = tile - strip * p.tiles_n;
     const int m0 = strip * kGemmBM, n0 = tn * kGemmBN;

@@ -8,6 +8,9 @@ cache). Before the W warmup steps the same calls run untimed for --settle-s
 seconds: the shader clock climbs over the first tens of milliseconds of
 sustained load (a C2 launch takes 0.33 ms in the first batch and 0.24 ms from
 about the 200th on), and the timed steps are meant to see the sustained state.
+The K timed launches are captured once into a HIP graph and replayed as one
+(--eager: launched one by one from Python), so that a small kernel's time is
+not the host's per-call cost.
 Prints one JSON line:
   value      algorithmic GEMM TFLOP/s of the workload (2*M*N*K per GEMM)
   roofline   the same kernel against its bound (bf16 dense MFMA peak, or HBM
@@ -78,6 +81,9 @@ def parse():
     ap.add_argument("--causal", action="store_true",
                     help="attention workload: causal mask (key l visible to query m iff l <= m + L - M); the "
                          "algorithmic flops count only the visible (query, key) pairs")
+    ap.add_argument("--eager", action="store_true",
+                    help="time K eager launches from Python instead of one replay of a HIP graph that holds the "
+                         "K launches (the graph removes the host's per-launch cost from the timed region)")
     ap.add_argument("--rotate-mb", type=int, default=512,
                     help="cycle through copies of the inputs totalling at least this many MiB, so that they are "
                          "read from HBM rather than from the 256 MiB last-level cache (0: one set)")
@@ -239,7 +245,7 @@ def make_call(w, dev, torch, cf, store_x: bool = False, causal: bool = False, ar
     """Device tensors + a closure launching one fused kernel on the current stream."""
     p = w.params
     out_dt = torch.float32 if p.get("out_dtype") == "f32" else torch.bfloat16
-    stream = torch.cuda.current_stream()
+    stream = None   # torch's current stream at call time (a graph's capture stream while capturing)
     if w.kind == "gemm_epilogue":
         d = w.dims
         X = torch.empty(d["M"], d["N"], dtype=torch.bfloat16, device="cuda") if store_x else None
@@ -464,13 +470,29 @@ def main():
     for i in range(max(args.warmup, nset)):
         calls[i % nset]()
     torch.cuda.synchronize()
+    graph = None
+    if not args.eager:
+        # the K timed launches, captured once (same kernels and arguments as
+        # the eager calls) and replayed as one graph on the launch stream
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(args.steps):
+                calls[i % nset]()
+        torch.cuda.synchronize()
+        graph.replay()   # untimed first replay
+        torch.cuda.synchronize()
     start_ev = torch.cuda.Event(enable_timing=True)
     end_ev = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start_ev.record()
-    for i in range(args.steps):
-        calls[i % nset]()
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            calls[i % nset]()
     end_ev.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -509,6 +531,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "settle": {"seconds": round(settle_s, 3), "steps": settle_steps},
+        "timing": "eager launches" if args.eager else "one HIP graph replay of the K launches",
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

@@ -253,8 +253,10 @@ cf_status cf_gemm_epilogue_noalloc(int64_t M, int64_t N, int64_t K,
  * operand is round(2^(t - c)) with t = log2(e) * S and an integer per-row c,
  * and the row sum used for normalisation is taken before rounding.
  * in_dtype must be CF_BF16; out_dtype CF_BF16 or CF_F32.
- * Supported sizes: K, N in {16, 32, 64, 128} (softmax: K, N in {64, 128});
- * any M, L and batch. */
+ * Any M, K, L, N and batch (each batch entry's operands below 2 GiB). K above
+ * 128 is contracted in blocks of 128; N above 128 is computed in column
+ * blocks of 128, each of which evaluates S and F again (the softmax gives
+ * identical terms in every block). */
 cf_status cf_b2bgemm(int64_t batch, int64_t M, int64_t K, int64_t L, int64_t N,
                      const void* A, int64_t lda, int64_t sa,
                      const void* B0, int64_t ldb0, int64_t sb0, int b0_is_lk,

@@ -127,6 +127,58 @@ def test_shapes(lk, row_op, act, shape):
 
 
 @pytest.mark.parametrize("lk", [False, True])
+@pytest.mark.parametrize("row_op,act", [("none", "relu"), ("softmax", "none")])
+@pytest.mark.parametrize("shape", [(1, 300, 512, 256, 128), (2, 200, 512, 128, 256), (1, 1000, 256, 512, 64),
+                                   (2, 77, 200, 150, 300), (1, 130, 130, 64, 129), (3, 65, 1024, 96, 520)])
+def test_wide_k_and_n(lk, row_op, act, shape):
+    # K above 128 (k-blocks of 128) and N above 128 (column blocks of 128),
+    # among them the pages' DLRM bottom-MLP feature widths 512 / 256 / 128,
+    # ragged K, L, N and rows
+    batch, M, K, L, N = shape
+    w, dev, ref = P.inputs("c5_b2b_attention", seed=15, batch=batch, M=M, K=K, L=L, N=N)
+    dev["B1"] = (dev["B1"].float() / np.sqrt(L)).to(torch.bfloat16)
+    ref["B1"] = P.gpu_to_f64(dev["B1"])
+    if not lk:   # B0 given as [K, L]
+        dev["B0"] = dev["B0"].transpose(1, 2).contiguous()
+        ref["B0"] = np.ascontiguousarray(np.swapaxes(ref["B0"], 1, 2))
+    dev = {k: padded(v) for k, v in dev.items()}
+    check(dev, ref, lk=lk, alpha=1.0 / np.sqrt(K), act=act, row_op=row_op,
+          what=f"wide {shape} {row_op}/{act} lk={lk}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_wide_attention_logsumexp_and_bias(causal):
+    # head dim 256 (K = N = 256): the softmax terms and the log-sum-exp must
+    # agree across the two column blocks of O
+    w, dev, ref = P.inputs("c5_b2b_attention", seed=16, batch=2, M=192, K=256, L=320, N=256)
+    lse = torch.full((2, 192), float("nan"), dtype=torch.float32, device="cuda")
+    O = run(dev["A"], dev["B0"], dev["B1"], torch.float32, b0_is_lk=True, alpha=1 / 16, row_op="softmax",
+            mask="causal" if causal else "none", row_stats=lse)
+    R = oracle.b2bgemm(ref["A"], ref["B0"], ref["B1"], alpha=1 / 16, row_op="softmax", b0_layout="lk",
+                       causal=causal)
+    P.assert_close(P.gpu_to_f64(O), R, P.REL_F_BF16, P.MAX_ABS_BF16, f"head dim 256 causal={causal}")
+    Rl = oracle.b2b_logsumexp(ref["A"], ref["B0"], alpha=1 / 16, b0_layout="lk", causal=causal)
+    P.assert_close(P.gpu_to_f64(lse), Rl, 1e-5, 1e-4, "head dim 256 log-sum-exp")
+
+
+def test_wide_mlp_with_bias_dlrm_widths():
+    # bottom-MLP layer pair 512 -> 256 -> 128 with a bias and ReLU between.
+    # The MLP workload's W0 ~ N(0, 1/8) is scaled for K = 64; alpha = 1/sqrt(8)
+    # keeps S of the same order at K = 512. (S itself is accumulated in fp32
+    # and rounded to bf16 for the second GEMM, as the oracle mirrors; where an
+    # fp32 S lies within its rounding error of a bf16 rounding boundary the
+    # two roundings pick neighbouring values, and one bf16 step of S grows
+    # with |S|, so an unscaled S of order 8 would spend the max-abs bar on such
+    # ties alone.)
+    batch, M, K, L, N = 1, 4096, 512, 256, 128
+    w, dev, ref = P.inputs("c4_b2b_mlp_relu", seed=17, batch=batch, M=M, K=K, L=L, N=N)
+    rng = np.random.default_rng(17)
+    bias = torch.from_numpy(rng.normal(0.0, 0.5, L)).to(torch.bfloat16).cuda()
+    check(dev, ref, lk=False, alpha=float(np.float32(1 / np.sqrt(8))), act="relu", bias=bias,
+          bias_ref=P.gpu_to_f64(bias), what="DLRM 512-256-128 + bias")
+
+
+@pytest.mark.parametrize("lk", [False, True])
 @pytest.mark.parametrize("row_op,act", [("softmax", "none"), ("none", "relu")])
 @pytest.mark.parametrize("K,N", [(64, 64), (64, 128), (128, 64), (128, 128)])
 def test_exact_shapes_streamed(K, N, lk, row_op, act):

@@ -151,8 +151,6 @@ def b2b(batch=1, M=64, K=64, L=64, N=64, A=PA, lda=64, sa=0, B0=PB, ldb0=64, sb0
     (dict(ldo=8), cf.CF_ERR_INVALID_ARGUMENT),
     (dict(sa=-8), cf.CF_ERR_INVALID_ARGUMENT),
     (dict(it=0), cf.CF_ERR_UNSUPPORTED),                            # fp32 inputs
-    (dict(K=256, lda=256, ldb0=64), cf.CF_ERR_UNSUPPORTED),         # K > 128
-    (dict(N=200, ldb1=200, ldo=200), cf.CF_ERR_UNSUPPORTED),        # N > 128
     (dict(lda=68), cf.CF_ERR_UNSUPPORTED),                          # leading dimension not 16-byte aligned
     (dict(mid=epi(row_op=2)), cf.CF_ERR_UNSUPPORTED),               # LayerNorm between two GEMMs
     (dict(mid=epi(residual=PW, ld_residual=64)), cf.CF_ERR_UNSUPPORTED),
@@ -196,6 +194,8 @@ def test_valid_calls_report_no_device():
     assert gemm(C=None, ldc=0, epi=epi(row_op=4, row_index=PW)) == cf.CF_ERR_NO_DEVICE
     assert b2b(mid=epi(row_op=1, alpha=0.125)) == cf.CF_ERR_NO_DEVICE
     assert b2b(lk=1, mid=epi(row_op=1, alpha=0.125, mask=1)) == cf.CF_ERR_NO_DEVICE
+    assert b2b(K=512, lda=512, ldb0=64) == cf.CF_ERR_NO_DEVICE           # K above 128: k-blocks
+    assert b2b(N=200, ldb1=200, ldo=200) == cf.CF_ERR_NO_DEVICE          # N above 128: column blocks
     assert lib.cf_workspace_init(PW, 4096, None) == cf.CF_ERR_NO_DEVICE
 
 

@@ -83,9 +83,12 @@ def units() -> list[tuple[str, str, list[str]]]:
 
 
 def source_hash() -> str:
-    """Hash of every source and header the library is built from, and of the flags."""
+    """Hash of every source and header the library is built from, and of the
+    flags (with the tree's own include directories by name, so that a copy of
+    the tree at another path has the same hash)."""
     h = hashlib.sha256()
-    h.update(repr((FLAGS, LINK_FLAGS, list(PARTS_ALL), list(PARTS_BF16))).encode())
+    flags = [{INCLUDE: "<include>", CSRC: "<csrc>"}.get(f, f) for f in FLAGS]
+    h.update(repr((flags, LINK_FLAGS, list(PARTS_ALL), list(PARTS_BF16))).encode())
     for d in (CSRC, INCLUDE):
         for f in sorted(os.listdir(d)):
             p = os.path.join(d, f)

@@ -17,6 +17,8 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 std::atomic<uint64_t> g_timeout_us{2000000};
+// strips of at least this many column tiles exchange leader-follower (0: never)
+std::atomic<int> g_lf_tiles{CF_DEFAULT_LEADER_TILES};
 
 struct DeviceInfo {
   bool valid = false;
@@ -220,6 +222,7 @@ cf_status gemm_epilogue_run(int64_t M, int64_t N, int64_t K, const void* A, int6
     if (p.row_op2 != 0) p.ws_slots2 = (uint64_t*)((char*)ws + cf::kWsHeaderBytes + plan.slot_bytes);
   }
   p.spin_ticks = g_timeout_us.load() * (uint64_t)info.wallclock_khz / 1000u;
+  p.lf_tiles = g_lf_tiles.load();
 
   const bool in_f32 = ab_dtype == CF_F32;
   const int per_cu = cf::gemm_epilogue_blocks_per_cu(p, in_f32, b_is_nk != 0, vec);
@@ -331,5 +334,9 @@ int cf_last_hip_error(void) { return g_last_hip_error; }
 const char* cf_version(void) { return "cf 0.1.0 (gfx950)"; }
 
 uint64_t cf_set_exchange_timeout_us(uint64_t us) { return g_timeout_us.exchange(us); }
+
+int cf_set_exchange_leader_tiles(int min_tiles) {
+  return min_tiles < 0 ? g_lf_tiles.load() : g_lf_tiles.exchange(min_tiles);
+}
 
 }  // extern "C"

@@ -50,6 +50,7 @@ struct GemmEpilogueParams {
   uint64_t* ws_slots2;   // the second stage's exchange slots
   uint64_t spin_ticks;   // wall-clock ticks a strip wait may take
   int topk;          // top-k: k (1..8)
+  int lf_tiles;      // leader-follower exchange for strips of at least this many tiles (0: never)
 };
 
 // Launches the persistent kernel. in_f32: fp32 inputs (else bf16); b_nk: B

@@ -888,12 +888,46 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
         a = take1 ? w1.x : w0.x;
         b = take1 ? w1.y : w0.y;
       }
-      if (p.ws_hdr != nullptr && row_ok) {
-        // word w (0: a, 1: b) of row ml of tile t at t * 512 + w * 256 + ml, so
-        // that each store instruction writes whole contiguous lines
+      // Leader-follower mode (strips of at least p.lf_tiles tiles): column
+      // tile 0 merges every partial and publishes the merged statistics in its
+      // own slot; the other tiles publish their partials and read only that.
+      // Peer-to-peer mode: every tile reads every partial. Both merge in tile
+      // order, so the statistics are bit-identical either way.
+      const bool lf = p.lf_tiles > 0 && p.tiles_n >= p.lf_tiles;
+      if (p.ws_hdr != nullptr && row_ok && lf && tn != 0) {
         uint64_t* slots = p.ws_slots + (size_t)strip * p.tiles_n * 512 + ml;
         publish(slots + (size_t)tn * 512, a, tag);
         if constexpr (ROW != 3) publish(slots + (size_t)tn * 512 + 256, b, tag);
+        const uint64_t t0 = wall_clock64();
+        bool lost = false;
+        for (;;) {
+          const uint64_t wa = __hip_atomic_load(slots, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          uint64_t wb = 0;
+          if constexpr (ROW != 3) wb = __hip_atomic_load(slots + 256, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if ((uint32_t)(wa >> 32) == tag && (ROW == 3 || (uint32_t)(wb >> 32) == tag)) {
+            a = __uint_as_float((uint32_t)wa);
+            b = __uint_as_float((uint32_t)wb);
+            break;
+          }
+          if (timed_out || wall_clock64() - t0 > p.spin_ticks) {   // recorded in the workspace header
+            timed_out = true;
+            lost = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+        if (lost) {
+          a = __int_as_float(0x7fc00000);
+          b = ROW == 4 ? __int_as_float(-1) : __int_as_float(0x7fc00000);
+        }
+      } else if (p.ws_hdr != nullptr && row_ok) {
+        // word w (0: a, 1: b) of row ml of tile t at t * 512 + w * 256 + ml, so
+        // that each store instruction writes whole contiguous lines
+        uint64_t* slots = p.ws_slots + (size_t)strip * p.tiles_n * 512 + ml;
+        if (!lf) {   // the leader's own slot carries the merged result instead
+          publish(slots + (size_t)tn * 512, a, tag);
+          if constexpr (ROW != 3) publish(slots + (size_t)tn * 512 + 256, b, tag);
+        }
         const uint64_t t0 = wall_clock64();
         // The peers' words are fetched 8 column tiles at a time with all loads
         // in flight together, and the words not yet published are polled again
@@ -967,6 +1001,10 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
         if (lost) {
           a = __int_as_float(0x7fc00000);
           b = ROW == 4 ? __int_as_float(-1) : __int_as_float(0x7fc00000);
+        }
+        if (lf) {   // the leader (tn == 0) hands the merged statistics to its followers
+          publish(slots, a, tag);
+          if constexpr (ROW != 3) publish(slots + 256, b, tag);
         }
       }
       float2 st;

@@ -81,6 +81,11 @@ def parse():
     ap.add_argument("--causal", action="store_true",
                     help="attention workload: causal mask (key l visible to query m iff l <= m + L - M); the "
                          "algorithmic flops count only the visible (query, key) pairs")
+    ap.add_argument("--dims", default="",
+                    help="diagnostic: override workload dims, e.g. M=2048,N=16384 (the line then names them)")
+    ap.add_argument("--leader-tiles", type=int, default=-1, metavar="T",
+                    help="strips of at least T column tiles exchange leader-follower (0: never; default: the "
+                         "library's setting)")
     ap.add_argument("--eager", action="store_true",
                     help="time K eager launches from Python instead of one replay of a HIP graph that holds the "
                          "K launches (the graph removes the host's per-launch cost from the timed region)")
@@ -418,7 +423,10 @@ def main():
     import gen
     sys.path.insert(0, os.path.join(ROOT, "tests"))
 
-    w = gen.workload(args.workload)
+    dims = {k: int(v) for k, v in (kv.split("=") for kv in args.dims.split(",") if kv)}
+    w = gen.workload(args.workload, **dims)
+    if args.leader_tiles >= 0:
+        cf.cf_set_exchange_leader_tiles(args.leader_tiles)
     if args.store_x and w.kind != "gemm_epilogue":
         raise SystemExit("--store-x applies to the GEMM + epilogue workloads")
     if args.row2 and (w.kind != "gemm_epilogue" or args.argmax or w.params["row_op"] == "none"):
@@ -513,7 +521,7 @@ def main():
     traffic = intermediate = None
     out_bytes = output_bytes(w, args.store_x, args.argmax, args.topk)
     if os.path.exists(args.traffic) and not (args.plain or args.store_x or args.causal or args.argmax or args.row2
-                                             or args.topk or args.b_nk):
+                                             or args.topk or args.b_nk or args.dims):
         try:
             rec = json.load(open(args.traffic))
             if rec.get("kernel_source_hash") == kernel_source_hash():
@@ -538,7 +546,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32" if in_f32 else "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name + ("/identity-epilogue" if args.plain else "")
+        "config": {"workload": w.name + (f"@{args.dims}" if args.dims else "") + ("/identity-epilogue" if args.plain else "")
                    + ("+x_out" if args.store_x else "") + ("/causal" if args.causal else "")
                    + ("/argmax" if args.argmax else "") + (f"/then-{args.row2}" if args.row2 else "")
                    + (f"/top-{args.topk}" if args.topk else "") + ("/B[N,K]" if args.b_nk else ""), **w.dims,
@@ -547,6 +555,7 @@ def main():
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "arithmetic_intensity": round(intensity, 1), "ridge": round(ridge, 1)},
         "kernel_ms": round(kernel_ms, 4),
+        "exchange_leader_tiles": cf.cf_set_exchange_leader_tiles(-1),
         "algorithmic_bytes": bytes_of(w, args.store_x, args.argmax, args.topk),
         "intermediate_hbm_bytes": intermediate,
         "output_bytes": out_bytes,

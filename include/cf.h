@@ -280,6 +280,26 @@ const char* cf_version(void);
  * previous value. */
 uint64_t cf_set_exchange_timeout_us(uint64_t us);
 
+/* Default of cf_set_exchange_leader_tiles (strips of this many column tiles
+ * or more exchange leader-follower). */
+#define CF_DEFAULT_LEADER_TILES 33
+
+/* Aggregation mode of the strip exchange (ComFuse review, Referee Report minor
+ * comment 4 on Sec. III-A and "Assumptions & free parameters": a dual-mode
+ * scheme, peer-to-peer or leader-follower, switched at a strip width C_N the
+ * pages leave open). In peer-to-peer mode every workgroup of a row strip reads
+ * every other workgroup's per-row partial statistics; in leader-follower mode
+ * the workgroup of column tile 0 merges them all and publishes the merged
+ * statistics, which the others read. Both merge in column-tile order, so the
+ * outputs are bit-identical; the mode changes only the exchange's traffic
+ * (tiles^2 against 2 tiles partials per strip) and latency (one hop against
+ * two). Strips of at least `min_tiles` column tiles of 256 use
+ * leader-follower, narrower ones peer-to-peer; 0 means never (C_N here, the
+ * default CF_DEFAULT_LEADER_TILES). A negative value changes nothing.
+ * Returns the previous value. Process-wide; applies to the first row stage
+ * (a second row stage and top-k keep their own schemes). */
+int cf_set_exchange_leader_tiles(int min_tiles);
+
 #ifdef __cplusplus
 }
 #endif

@@ -80,3 +80,9 @@ def test_stamp_follows_content_not_file_times(tmp_path):
 def test_built_library_is_current():
     bl = load_builder(__import__("pathlib").Path(ROOT))
     assert bl.up_to_date(), "libcf.so is older than the sources: rebuild it"
+
+
+def test_hash_does_not_depend_on_the_tree_path(tmp_path):
+    a = load_builder(clean_copy(tmp_path / "one"))
+    b = load_builder(clean_copy(tmp_path / "two" / "deeper"))
+    assert a.source_hash() == b.source_hash()

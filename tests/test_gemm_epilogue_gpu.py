@@ -273,7 +273,16 @@ def test_k_zero_and_empty():
                         torch.zeros(4, 16, dtype=torch.bfloat16, device="cuda"), E)
 
 
-def test_exchange_timeout_is_reported_and_recoverable():
+@pytest.fixture(params=["peer-to-peer", "leader-follower"])
+def exchange_mode(request):
+    """Runs a test with every strip exchanging peer-to-peer, then with every
+    strip of two or more tiles exchanging leader-follower."""
+    old = cf.cf_set_exchange_leader_tiles(0 if request.param == "peer-to-peer" else 2)
+    yield request.param
+    cf.cf_set_exchange_leader_tiles(old)
+
+
+def test_exchange_timeout_is_reported_and_recoverable(exchange_mode):
     # A zero spin limit (forced from the host) makes a workgroup give up on
     # peers that have not published yet: the launch still completes (every
     # wait is bounded) and the workspace reports the timeout. After a reset and
@@ -404,6 +413,37 @@ def test_x_out_full_size_all_rows():
     P.assert_bf16_within(P.gpu_to_f64(y16), Yr, "C3 full Y")
     P.assert_bf16_within(P.gpu_to_f64(x16), Xr, "C3 full X")
     assert P.metrics(P.gpu_to_f64(x16), oracle.round_bf16(Xr))[0] <= P.REL_F_BF16
+
+
+# ---------------------------------------------------------------------------- leader-follower exchange
+
+@pytest.mark.parametrize("N,M", [(512, 300), (4096, 300), (8192, 300), (16384, 300), (65536, 64)])
+@pytest.mark.parametrize("row_op", ["softmax", "layernorm", "rmsnorm", "argmax"])
+def test_leader_follower_equals_peer_to_peer(N, M, row_op):
+    # the two aggregation modes merge the same partials in the same order:
+    # bit-identical outputs (and row statistics), both within the oracle's bars
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=19, M=M, N=N, K=128)
+    X = oracle.elementwise_stage(oracle.matmul(ref["A"], ref["B"]))
+    outs = {}
+    for mode, tiles in (("p2p", 0), ("lf", 2)):
+        old = cf.cf_set_exchange_leader_tiles(tiles)
+        try:
+            if row_op == "argmax":
+                outs[mode] = run_argmax(dev["A"], dev["B"], False)[:2]
+            else:
+                st = torch.full((M, 2) if row_op == "layernorm" else (M,), float("nan"), device="cuda")
+                C = run(dev["A"], dev["B"], torch.float32, row_op=row_op, gamma=dev["gamma"],
+                        beta=dev["beta"] if row_op == "layernorm" else None, eps=1e-5, row_stats=st)
+                outs[mode] = (C, st)
+        finally:
+            cf.cf_set_exchange_leader_tiles(old)
+    for a, b in zip(outs["p2p"], outs["lf"]):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"N={N} {row_op}: modes differ"
+    if row_op == "argmax":
+        check_argmax(outs["lf"][0], outs["lf"][1], X, f"leader-follower argmax N={N}")
+    else:
+        R = oracle.row_stage(X, row_op, ref["gamma"], ref["beta"] if row_op == "layernorm" else None, 1e-5)
+        P.assert_close(P.gpu_to_f64(outs["lf"][0]), R, P.REL_F_BF16, P.MAX_ABS_BF16, f"leader-follower {row_op} N={N}")
 
 
 # ---------------------------------------------------------------------------- wide strips

@@ -45,7 +45,8 @@ import numpy as np
 __all__ = [
     "widen_bf16", "round_bf16", "matmul", "elementwise_stage", "relu",
     "row_softmax", "layer_norm", "rms_norm", "gemm_epilogue", "gemm_epilogue_two_stage",
-    "softmax_bf16_operand", "b2bgemm",
+    "softmax_bf16_operand", "b2bgemm", "column_stage", "column_statistics", "gemm_epilogue_columns",
+    "gemm_epilogue_column_stats",
 ]
 
 _LOG2E = 1.0 / math.log(2.0)
@@ -272,6 +273,73 @@ def gemm_epilogue_two_stage(A: np.ndarray, B: np.ndarray, *, alpha: float = 1.0,
     X = elementwise_stage(matmul(A, B), alpha, bias, residual, act)
     Y = row_stage(X, row_op, gamma, beta, eps)
     return row_stage(Y, row_op2, gamma2, beta2, eps2)
+
+
+# --------------------------------------------------------------------------- column reductions
+
+def column_stage(X: np.ndarray, col_op: str, gamma: Optional[np.ndarray] = None,
+                 beta: Optional[np.ndarray] = None, eps: float = 0.0) -> np.ndarray:
+    """A reduction along the other dimension: the operation runs over the rows m
+    of each column n. The review notes that Eq. (1)'s strip argument covers a
+    column-dimension reduction through the complementary strip, the tiles
+    T_{m,n} that share n (ComFuse review, Referee Report major comment 1 on
+    Sec. III). Textbook forms, as for the rows: softmax over m with the column
+    maximum subtracted; LayerNorm with the biased variance over m and eps inside
+    the root, then gamma[n] * x_hat + beta[n] (a per-column affine, as a batch
+    normalisation over the rows has); RMSNorm x / sqrt(mean_m(x^2) + eps) * w[n]."""
+    X = np.asarray(X, np.float64)
+    if col_op == "softmax":
+        mx = X.max(axis=-2, keepdims=True)
+        e = np.exp(X - mx)
+        return e / e.sum(axis=-2, keepdims=True)
+    if col_op == "layernorm":
+        mu = X.mean(axis=-2, keepdims=True)
+        d = X - mu
+        var = (d * d).mean(axis=-2, keepdims=True)
+        Y = d / np.sqrt(var + float(eps))
+    elif col_op == "rmsnorm":
+        ms = (X * X).mean(axis=-2, keepdims=True)
+        Y = X / np.sqrt(ms + float(eps))
+        beta = None
+    else:
+        raise ValueError(f"unknown col_op {col_op!r}")
+    if gamma is not None:
+        Y = Y * np.asarray(gamma, np.float64)
+    if beta is not None:
+        Y = Y + np.asarray(beta, np.float64)
+    return Y
+
+
+def column_statistics(X: np.ndarray, col_op: str, eps: float = 0.0) -> np.ndarray:
+    """The per-column result of a column reduction: log-sum-exp over m for the
+    softmax; [mean, 1/sqrt(var + eps)] for LayerNorm (last axis of length 2);
+    1/sqrt(mean_m(x^2) + eps) for RMSNorm."""
+    X = np.asarray(X, np.float64)
+    if col_op == "softmax":
+        mx = X.max(axis=-2)
+        return mx + np.log(np.exp(X - mx[..., None, :]).sum(axis=-2))
+    if col_op == "layernorm":
+        mu = X.mean(axis=-2)
+        var = ((X - mu[..., None, :]) ** 2).mean(axis=-2)
+        return np.stack([mu, 1.0 / np.sqrt(var + float(eps))], axis=-1)
+    if col_op == "rmsnorm":
+        return 1.0 / np.sqrt((X * X).mean(axis=-2) + float(eps))
+    raise ValueError(f"col_op {col_op!r} has no column statistics")
+
+
+def gemm_epilogue_columns(A: np.ndarray, B: np.ndarray, *, alpha: float = 1.0,
+                          bias: Optional[np.ndarray] = None, residual: Optional[np.ndarray] = None,
+                          act: str = "none", col_op: str = "softmax", gamma: Optional[np.ndarray] = None,
+                          beta: Optional[np.ndarray] = None, eps: float = 0.0) -> np.ndarray:
+    """GEMM, the elementwise stage, then one column reduction (column_stage)."""
+    return column_stage(elementwise_stage(matmul(A, B), alpha, bias, residual, act), col_op, gamma, beta, eps)
+
+
+def gemm_epilogue_column_stats(A: np.ndarray, B: np.ndarray, *, alpha: float = 1.0,
+                               bias: Optional[np.ndarray] = None, residual: Optional[np.ndarray] = None,
+                               act: str = "none", col_op: str = "softmax", eps: float = 0.0) -> np.ndarray:
+    """column_statistics of the elementwise stage's result."""
+    return column_statistics(elementwise_stage(matmul(A, B), alpha, bias, residual, act), col_op, eps)
 
 
 # --------------------------------------------------------------------------- back-to-back GEMM

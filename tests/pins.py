@@ -568,10 +568,88 @@ def pin_row_argmax(o):
     assert [int(v) for v in ni] == [2, 0, 0, 2], list(ni)
 
 
+def pin_column_ops(o):
+    """Column reductions against brute force on each column (the exact row
+    routines applied to the column's values), closed forms and invariants."""
+    rng = np.random.default_rng(21)
+    Xm = rng.standard_normal((7, 5)) * 2 + 1
+    eps = 1e-5
+    gamma = rng.standard_normal(5)
+    beta = rng.standard_normal(5)
+    # softmax over m: every column sums to 1, a per-column shift changes nothing
+    Ys = o.column_stage(Xm, "softmax")
+    assert np.all(np.abs(Ys.sum(0) - 1) <= 7 * 1e-15)
+    assert np.allclose(o.column_stage(Xm + rng.standard_normal((1, 5)) * 40, "softmax"), Ys, rtol=1e-12, atol=0)
+    # large logits in a column must not overflow (the column maximum is subtracted)
+    big = np.array([[1000.0, 0.5], [999.0, 0.25], [990.0, -1.0]])
+    yb = o.column_stage(big, "softmax")
+    for j in range(2):
+        for g, w in zip(yb[:, j], X.softmax_row([Fraction(v) for v in big[:, j]])):
+            _close_dec(g, w)
+    # LayerNorm over m: zero column mean, variance var / (var + eps) before the affine step
+    Yl = o.column_stage(Xm, "layernorm", None, None, eps)
+    assert np.all(np.abs(Yl.mean(0)) <= 1e-14)
+    for j in range(5):
+        xs = [X.F(v) for v in Xm[:, j]]
+        mu = sum(xs, Fraction(0)) / len(xs)
+        var = sum(((x - mu) ** 2 for x in xs), Fraction(0)) / len(xs)
+        assert math.isclose(float(np.mean(Yl[:, j] ** 2)), float(var / (var + X.F(eps))), rel_tol=1e-13)
+    # a constant column -> beta of that column
+    Xc = Xm.copy()
+    Xc[:, 2] = 3.5
+    assert np.allclose(o.column_stage(Xc, "layernorm", gamma, beta, eps)[:, 2], beta[2], rtol=0, atol=1e-15)
+    # 40-digit brute force, column by column, with the per-column affine vectors
+    Z = rng.standard_normal((4, 3)) * 2
+    for op in ("softmax", "layernorm", "rmsnorm"):
+        g3 = None if op == "softmax" else gamma[:3]
+        b3 = beta[:3] if op == "layernorm" else None
+        Y = o.column_stage(Z, op, g3, b3, eps)
+        for j in range(3):
+            col = [X.F(v) for v in Z[:, j]]
+            if op == "softmax":
+                want = X.softmax_row(col)
+            elif op == "layernorm":
+                want = X.layernorm_row(col, eps, [gamma[j]] * 4, [beta[j]] * 4)
+            else:
+                want = X.rmsnorm_row(col, eps, [gamma[j]] * 4)
+            for i in range(4):
+                _close_dec(Y[i, j], want[i], rtol=1e-12, atol=1e-14)
+    # statistics: log-sum-exp, (mean, 1/sigma) and 1/rms of each column
+    for op in ("softmax", "layernorm", "rmsnorm"):
+        st = o.column_statistics(Z, op, eps)
+        for j in range(3):
+            xs = [X.D(X.F(v)) for v in Z[:, j]]
+            n = X.D(len(xs))
+            if op == "softmax":
+                want, got = [X.CTX.ln(sum((X.dexp(v) for v in xs), Decimal(0)))], [st[j]]
+            elif op == "layernorm":
+                mu = X.CTX.divide(sum(xs, Decimal(0)), n)
+                var = X.CTX.divide(sum(((v - mu) * (v - mu) for v in xs), Decimal(0)), n)
+                want, got = [mu, X.CTX.divide(Decimal(1), X.dsqrt(var + X.D(eps)))], list(st[j])
+            else:
+                ms = X.CTX.divide(sum((v * v for v in xs), Decimal(0)), n)
+                want, got = [X.CTX.divide(Decimal(1), X.dsqrt(ms + X.D(eps)))], [st[j]]
+            for gv, wv in zip(got, want):
+                _close_dec(gv, wv, rtol=1e-13, atol=1e-14)
+    # through the GEMM with alpha, bias, residual and ReLU: exact x, then the column op
+    A = _bf16_values(rng, (5, 4))
+    B = _bf16_values(rng, (4, 3))
+    R = _bf16_values(rng, (5, 3))
+    bias = _bf16_values(rng, (3,))
+    Yg = o.gemm_epilogue_columns(A, B, alpha=0.5, bias=bias, residual=R, act="relu", col_op="rmsnorm",
+                                 gamma=gamma[:3], eps=eps)
+    E = X.mm(X.mat(A), X.mat(B))
+    for j in range(3):
+        col = [max(Fraction(1, 2) * E[i][j] + X.F(bias[j]) + X.F(R[i, j]), Fraction(0)) for i in range(5)]
+        want = X.rmsnorm_row(col, eps, [gamma[j]] * 5)
+        for i in range(5):
+            _close_dec(Yg[i, j], want[i], rtol=1e-12, atol=1e-14)
+
+
 ALL_PINS = [pin_round_bf16, pin_widen_bf16, pin_matmul_exact, pin_stage1_exact, pin_softmax,
             pin_layernorm, pin_rmsnorm, pin_gemm_epilogue_composition, pin_two_outputs, pin_b2b_relu,
             pin_b2b_softmax, pin_b2b_causal, pin_row_statistics, pin_b2b_logsumexp, pin_row_argmax,
-            pin_two_stage, pin_row_topk]
+            pin_two_stage, pin_row_topk, pin_column_ops]
 
 
 def run_all(o):

@@ -16,14 +16,15 @@ MUTATIONS = {
         "var = (d * d).mean(axis=-1, keepdims=True)",
         "var = (d * d).sum(axis=-1, keepdims=True) / (X.shape[-1] - 1)")],
     "layernorm_eps_outside_root": [(
-        "Y = d / np.sqrt(var + float(eps))", "Y = d / (np.sqrt(var) + float(eps))")],
+        "\n    Y = d / np.sqrt(var + float(eps))", "\n    Y = d / (np.sqrt(var) + float(eps))")],
     "layernorm_drops_beta": [(
-        "Y = Y + np.asarray(beta, np.float64)", "Y = Y")],
-    "rmsnorm_drops_eps": [("Y = X / np.sqrt(ms + float(eps))", "Y = X / np.sqrt(ms)")],
+        "    if beta is not None:\n        Y = Y + np.asarray(beta, np.float64)\n    return Y\n\n\ndef rms_norm",
+        "    return Y\n\n\ndef rms_norm")],
+    "rmsnorm_drops_eps": [("\n    Y = X / np.sqrt(ms + float(eps))", "\n    Y = X / np.sqrt(ms)")],
     "rmsnorm_centres_rows": [(
         "ms = (X * X).mean(axis=-1, keepdims=True)",
         "ms = ((X - X.mean(axis=-1, keepdims=True)) ** 2).mean(axis=-1, keepdims=True)")],
-    "softmax_without_max_shift": [("e = np.exp(X - mx)", "e = np.exp(X)")],
+    "softmax_without_max_shift": [("\n    e = np.exp(X - mx)", "\n    e = np.exp(X)")],
     "bias_per_row": [(
         "X = X + np.asarray(bias, np.float64)[..., None, :]",
         "X = X + np.asarray(bias, np.float64)[..., :, None]")],
@@ -102,6 +103,31 @@ MUTATIONS = {
     "topk_one_short": [(
         '    idx = np.argsort(-key, axis=-1, kind="stable")[..., :k]\n',
         '    idx = np.argsort(-key, axis=-1, kind="stable")[..., :max(k - 1, 1)]\n')],
+    "column_softmax_over_rows": [(
+        "        return e / e.sum(axis=-2, keepdims=True)\n", "        return e / e.sum(axis=-1, keepdims=True)\n")],
+    "column_softmax_without_max_shift": [(
+        "        mx = X.max(axis=-2, keepdims=True)\n        e = np.exp(X - mx)\n",
+        "        mx = X.max(axis=-2, keepdims=True)\n        e = np.exp(X)\n")],
+    "column_layernorm_unbiased_variance": [(
+        "        var = (d * d).mean(axis=-2, keepdims=True)\n",
+        "        var = (d * d).sum(axis=-2, keepdims=True) / (X.shape[-2] - 1)\n")],
+    "column_layernorm_mean_over_columns": [(
+        "        mu = X.mean(axis=-2, keepdims=True)\n        d = X - mu\n",
+        "        mu = X.mean(axis=-1, keepdims=True)\n        d = X - mu\n")],
+    "column_rmsnorm_drops_eps": [(
+        "        Y = X / np.sqrt(ms + float(eps))\n        beta = None\n",
+        "        Y = X / np.sqrt(ms)\n        beta = None\n")],
+    "column_affine_per_row": [(
+        "    if gamma is not None:\n        Y = Y * np.asarray(gamma, np.float64)\n    if beta is not None:\n"
+        "        Y = Y + np.asarray(beta, np.float64)\n    return Y\n\n\ndef column_statistics",
+        "    if gamma is not None:\n        Y = Y * np.asarray(gamma, np.float64)[:Y.shape[0], None]\n    if beta is not None:\n"
+        "        Y = Y + np.asarray(beta, np.float64)\n    return Y\n\n\ndef column_statistics")],
+    "column_stats_lse_drops_max": [(
+        "        return mx + np.log(np.exp(X - mx[..., None, :]).sum(axis=-2))",
+        "        return np.log(np.exp(X - mx[..., None, :]).sum(axis=-2))")],
+    "column_stats_rms_over_rows": [(
+        "        return 1.0 / np.sqrt((X * X).mean(axis=-2) + float(eps))",
+        "        return 1.0 / np.sqrt((X * X).mean(axis=-1) + float(eps))")],
     "b2b_relu_dropped": [(
         "S = elementwise_stage(matmul(A, B0), alpha, bias, None, act)",
         "S = elementwise_stage(matmul(A, B0), alpha, bias, None, 'none')")],

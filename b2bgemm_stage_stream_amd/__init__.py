@@ -31,6 +31,7 @@ CF_F32, CF_BF16 = 0, 1
 ACT = {"none": 0, "relu": 1}
 ROW_OP = {"none": 0, "softmax": 1, "layernorm": 2, "rmsnorm": 3, "argmax": 4, "topk": 5}
 MASK = {"none": 0, "causal": 1}
+AXIS = {"row": 0, "column": 1}
 
 
 class cf_epilogue(ctypes.Structure):
@@ -58,6 +59,7 @@ class cf_epilogue(ctypes.Structure):
         ("beta2", ctypes.c_void_p),
         ("eps2", ctypes.c_float),
         ("topk", ctypes.c_int32),
+        ("axis", ctypes.c_int),
     ]
 
 
@@ -161,7 +163,7 @@ def _ptr(t) -> Optional[int]:
 def make_epilogue(*, alpha: float = 1.0, bias=None, residual=None, act: str = "none",
                   row_op: str = "none", gamma=None, beta=None, eps: float = 0.0, x_out=None,
                   mask: str = "none", row_stats=None, row_index=None, row_op2: str = "none", gamma2=None,
-                  beta2=None, eps2: float = 0.0, topk: int = 0) -> cf_epilogue:
+                  beta2=None, eps2: float = 0.0, topk: int = 0, axis: str = "row") -> cf_epilogue:
     """cf_epilogue descriptor from tensors (bias/gamma/beta share one dtype).
     ``x_out``: optional [M, N] tensor that receives x before the row operation.
     ``mask``: "causal" for the softmax of cf_b2bgemm.
@@ -172,9 +174,12 @@ def make_epilogue(*, alpha: float = 1.0, bias=None, residual=None, act: str = "n
     ``gamma2``, ``beta2``, ``eps2``): a second row stage applied to the first
     one's output (cf_gemm_epilogue only). ``topk``: k (1..8) for row_op "topk",
     whose ``row_index`` (int32 [M, k]) and ``row_stats`` (fp32 [M, k]) receive
-    each row's k largest columns and values."""
+    each row's k largest columns and values. ``axis``: "column" makes the row
+    operation (softmax, layernorm, rmsnorm) reduce over the rows of each
+    column instead (row_stats then holds per-column statistics)."""
     e = cf_epilogue()
     _lib.cf_epilogue_init(ctypes.byref(e))
+    e.axis = AXIS[axis]
     e.alpha = float(alpha)
     e.act = ACT[act]
     e.row_op = ROW_OP[row_op]
@@ -269,8 +274,9 @@ def cf_gemm_epilogue(A, B, C, *, b_is_nk: bool = False, epi: Optional[cf_epilogu
     if x_out is not None and tuple(x_out.shape) != (M, N):
         raise ValueError(f"x_out must be [{M}, {N}]")
     st = epi_kwargs.get("row_stats")
-    if st is not None and st.numel() < M * (2 if epi_kwargs.get("row_op") == "layernorm" else kk):
-        raise ValueError("row_stats is too small for M rows")
+    per = N if epi_kwargs.get("axis") == "column" else M
+    if st is not None and st.numel() < per * (2 if epi_kwargs.get("row_op") == "layernorm" else kk):
+        raise ValueError("row_stats is too small for the rows (columns) it covers")
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
                                                            workspace.numel() * workspace.element_size())
     c_ptr, ldc, c_dt = (None, 0, CF_BF16) if C is None else (C.data_ptr(), _ld(C), _dtype_code(C))

@@ -45,8 +45,8 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 LINK_FLAGS = [f"--offload-arch={ARCH}", "-shared", "-fPIC"]
 
 # Instantiation parts of the GEMM + epilogue kernel (gemm_epilogue_inst.hip):
-# 0-9 for both input dtypes, 10-20 for bf16 inputs only.
-PARTS_ALL = range(10)
+# 0-9 and 21-23 for both input dtypes, 10-20 for bf16 inputs only.
+PARTS_ALL = list(range(10)) + [21, 22, 23]
 PARTS_BF16 = range(10, 21)
 
 Log = Callable[[str], None]

@@ -204,6 +204,9 @@ cf_status gemm_epilogue_run(int64_t M, int64_t N, int64_t K, const void* A, int6
   p.K = (int)K;
   p.tiles_n = (int)plan.tiles_n;
   p.tiles = (int)plan.tiles;
+  p.col = plan.col ? 1 : 0;
+  p.group = (int)plan.group;
+  p.strips = (int)plan.strips;
   p.alpha = epi ? epi->alpha : 1.0f;
   p.eps = epi ? epi->eps : 0.0f;
   p.act = epi ? (int)epi->act : 0;

@@ -50,7 +50,10 @@ struct GemmEpilogueParams {
   uint64_t* ws_slots2;   // the second stage's exchange slots
   uint64_t spin_ticks;   // wall-clock ticks a strip wait may take
   int topk;          // top-k: k (1..8)
-  int lf_tiles;      // leader-follower exchange for strips of at least this many tiles (0: never)
+  int lf_tiles;      // leader-follower exchange for groups of at least this many tiles (0: never)
+  int col;           // the row op reduces over the rows m of each column (column reduction)
+  int group;         // tiles per exchange group: tiles_n (row strips) or strips (tile columns)
+  int strips;        // row strips
 };
 
 // Launches the persistent kernel. in_f32: fp32 inputs (else bf16); b_nk: B

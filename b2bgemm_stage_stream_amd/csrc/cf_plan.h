@@ -52,6 +52,8 @@ inline bool fits31(int64_t rows, int64_t pad_rows, int64_t ld, size_t es) {
 
 struct GemmPlan {
   int64_t tiles_n = 0, strips = 0, tiles = 0;
+  bool col = false;        // a column reduction: groups are tile columns
+  int64_t group = 0;       // tiles per exchange group (tiles_n, or strips for a column reduction)
   bool exchange = false;
   size_t slot_bytes = 0;   // one stage's exchange slots
   size_t ws_bytes = 0;
@@ -63,7 +65,9 @@ inline GemmPlan plan_gemm(int64_t M, int64_t N, const cf_epilogue* epi) {
   g.tiles_n = (N + kPlanTile - 1) / kPlanTile;
   g.strips = (M + kPlanTile - 1) / kPlanTile;
   g.tiles = g.tiles_n * g.strips;
-  g.exchange = epi && ev(epi->row_op) != CF_ROW_NONE && g.tiles_n > 1;
+  g.col = epi && ev(epi->axis) == CF_AXIS_COLUMN;
+  g.group = g.col ? g.strips : g.tiles_n;
+  g.exchange = epi && ev(epi->row_op) != CF_ROW_NONE && g.group > 1;
   if (g.exchange) {
     // one slot set per reduction stage; top-k publishes up to 8 (value, column) pairs per row
     const size_t words = ev(epi->row_op) == CF_ROW_TOPK ? 16 : 2;
@@ -115,6 +119,17 @@ inline cf_status check_epilogue(const cf_epilogue* epi, int64_t N, bool allow_ro
   if (!allow_row_ops_norm) {
     if (ev(epi->row_op) == CF_ROW_LAYERNORM || ev(epi->row_op) == CF_ROW_RMSNORM) return CF_ERR_UNSUPPORTED;
     if (epi->gamma || epi->beta) return CF_ERR_UNSUPPORTED;
+  }
+  // reduction axis: a column reduction takes softmax, LayerNorm or RMSNorm
+  // alone (one stage), in cf_gemm_epilogue only
+  const int axis = ev(epi->axis);
+  if (axis != CF_AXIS_ROW && axis != CF_AXIS_COLUMN) return CF_ERR_INVALID_ARGUMENT;
+  if (axis == CF_AXIS_COLUMN) {
+    const int op = ev(epi->row_op);
+    if (op == CF_ROW_NONE) return CF_ERR_INVALID_ARGUMENT;
+    if (!allow_residual) return CF_ERR_UNSUPPORTED;
+    if (op != CF_ROW_SOFTMAX && op != CF_ROW_LAYERNORM && op != CF_ROW_RMSNORM) return CF_ERR_UNSUPPORTED;
+    if (ev(epi->row_op2) != CF_ROW_NONE) return CF_ERR_UNSUPPORTED;
   }
   // second row stage: softmax / LayerNorm / RMSNorm after one of those three
   if (ev(epi->row_op2) < CF_ROW_NONE || ev(epi->row_op2) > CF_ROW_ARGMAX) return CF_ERR_INVALID_ARGUMENT;
@@ -181,9 +196,9 @@ inline cf_status check_gemm(int64_t M, int64_t N, int64_t K, const void* A, int6
   // top-1 is the row argmax (same order, ties and NaN ranking, same outputs)
   const int row_op = (epi && ev(epi->row_op) == CF_ROW_TOPK && epi->topk == 1) ? (int)CF_ROW_ARGMAX
                      : epi ? (int)ev(epi->row_op) : 0;
-  if (row_op != CF_ROW_NONE && N > 65536) return CF_ERR_UNSUPPORTED;
-
   const GemmPlan plan = plan_gemm(M, N, epi);
+  // an exchange group is at most 256 tiles (a row strip of N, or a tile column of M)
+  if (row_op != CF_ROW_NONE && (plan.col ? M : N) > 65536) return CF_ERR_UNSUPPORTED;
   if (plan.exchange) {
     if (plan.ws_bytes > ws_limit) return CF_ERR_WORKSPACE;
     if (need_ws_ptr && (!ws || !plan_aligned(ws, 256))) return CF_ERR_WORKSPACE;
@@ -197,9 +212,11 @@ inline cf_status check_gemm(int64_t M, int64_t N, int64_t K, const void* A, int6
   if (epi && epi->residual)
     vec = vec && ev(epi->residual_dtype) == CF_BF16 && epi->ld_residual % 8 == 0 && plan_aligned(epi->residual, 16);
   if (X) vec = vec && epi->ld_x_out % 8 == 0 && plan_aligned(X, 16);
-  // two row stages and top-k (k > 1): fast-path layouts and bf16 inputs only
+  // two row stages and top-k (k > 1): fast-path layouts and bf16 inputs only;
+  // column reductions: fast-path layouts
   if (epi && (ev(epi->row_op2) != CF_ROW_NONE || row_op == CF_ROW_TOPK) && (!vec || ab_dtype != CF_BF16))
     return CF_ERR_UNSUPPORTED;
+  if (plan.col && !vec) return CF_ERR_UNSUPPORTED;
   out->plan = plan;
   out->row_op = row_op;
   out->vec = vec;
@@ -214,29 +231,30 @@ struct GridPlan {
 };
 
 // per_cu workgroups of the kernel fit on each of `cus` compute units. With an
-// exchange, a round of the persistent grid is a whole number of strips, all
-// resident at once, so every strip's tiles run together: a strip wider than
-// the resident capacity is refused. Workgroup w runs on XCD w % 8; a full
-// round of `grid` tiles is cut into 8 equal a x b rectangles (a strips by b
-// columns, a + b smallest), one per XCD, so that an XCD's workgroups share A
-// strips and B column panels in its L2.
+// exchange, a round of the persistent grid is a whole number of exchange
+// groups (row strips, or tile columns for a column reduction), all resident
+// at once, so every group's tiles run together: a group wider than the
+// resident capacity is refused. Workgroup w runs on XCD w % 8; a full round
+// of `grid` tiles is cut into 8 equal a x b rectangles (a groups by b members,
+// a + b smallest), one per XCD, so that an XCD's workgroups share A strips
+// and B column panels in its L2.
 inline cf_status plan_grid(const GemmPlan& g, int64_t per_cu, int64_t cus, GridPlan* out) {
   if (per_cu <= 0 || cus <= 0) return CF_ERR_UNSUPPORTED;
   const int64_t cap = per_cu * cus;
   GridPlan r;
   if (g.exchange) {
-    if (g.tiles_n > cap) return CF_ERR_UNSUPPORTED;
-    r.grid = g.tiles < (cap / g.tiles_n) * g.tiles_n ? g.tiles : (cap / g.tiles_n) * g.tiles_n;
+    if (g.group > cap) return CF_ERR_UNSUPPORTED;
+    r.grid = g.tiles < (cap / g.group) * g.group ? g.tiles : (cap / g.group) * g.group;
   } else {
     r.grid = g.tiles < cap ? g.tiles : cap;
   }
-  if (r.grid % 8 == 0 && r.grid % g.tiles_n == 0) {
-    const int64_t S = r.grid / g.tiles_n, per = r.grid / 8;
+  if (r.grid % 8 == 0 && r.grid % g.group == 0) {
+    const int64_t S = r.grid / g.group, per = r.grid / 8;
     int64_t best = 0;
     for (int64_t a = 1; a <= S; ++a) {
       if (S % a || per % a) continue;
       const int64_t b = per / a;
-      if (g.tiles_n % b || (S / a) * (g.tiles_n / b) != 8) continue;
+      if (g.group % b || (S / a) * (g.group / b) != 8) continue;
       if (!best || a + b < best + per / best) best = a;
     }
     if (best) {
@@ -248,11 +266,13 @@ inline cf_status plan_grid(const GemmPlan& g, int64_t per_cu, int64_t cus, GridP
   return CF_OK;
 }
 
-// Output tile of workgroup `bid` in the round that starts at tile `base`
-// (tiles numbered strip-major: tile = strip * tiles_n + column tile). A full
-// round with XCD rectangles gives XCD x = bid % 8 the rectangle (rx, ry) of
-// the round's strips x columns; otherwise tiles go in plain order. A result
-// >= tiles means the workgroup has no tile left.
+// Tile of workgroup `bid` in the round that starts at tile `base`, tiles
+// numbered group by group (tile = group * tiles_n + member; tiles_n here is
+// the group width: column tiles per row strip, or row strips per tile column
+// for a column reduction). A full round with XCD rectangles gives XCD x =
+// bid % 8 the rectangle (rx, ry) of the round's groups x members; otherwise
+// tiles go in plain order. A result >= tiles means the workgroup has no tile
+// left.
 CF_HD inline int round_tile(int base, int bid, int grid, int tiles, int tiles_n, int xcd_a, int xcd_b) {
   if (xcd_a > 0 && base + grid <= tiles) {
     const int x = bid & 7, i = bid >> 3;

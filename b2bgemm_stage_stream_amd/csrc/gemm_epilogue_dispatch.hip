@@ -88,15 +88,23 @@ hipError_t device_cus_cached(int* cus) {
   const void* cf_ge_kernels_0_##N##_18(int);                                                         \
   const void* cf_ge_kernels_0_##N##_19(int);                                                         \
   const void* cf_ge_kernels_0_##N##_20(int);
+#define CF_DECL_COL(F, N)                                                                            \
+  const void* cf_ge_kernels_##F##_##N##_21(int);                                                     \
+  const void* cf_ge_kernels_##F##_##N##_22(int);                                                     \
+  const void* cf_ge_kernels_##F##_##N##_23(int);
 CF_DECL10(0, 0)
 CF_DECL10(0, 1)
 CF_DECL10(1, 0)
 CF_DECL10(1, 1)
 CF_DECL_BF16_EXTRA(0)
 CF_DECL_BF16_EXTRA(1)
+CF_DECL_COL(0, 0)
+CF_DECL_COL(0, 1)
+CF_DECL_COL(1, 0)
+CF_DECL_COL(1, 1)
 
 typedef const void* (*PartFn)(int);
-constexpr int kNumParts = 21;
+constexpr int kNumParts = 24;
 #define CF_ROW10(F, N)                                                                               \
   cf_ge_kernels_##F##_##N##_0, cf_ge_kernels_##F##_##N##_1, cf_ge_kernels_##F##_##N##_2,             \
       cf_ge_kernels_##F##_##N##_3, cf_ge_kernels_##F##_##N##_4, cf_ge_kernels_##F##_##N##_5,         \
@@ -107,9 +115,12 @@ constexpr int kNumParts = 21;
       cf_ge_kernels_0_##N##_13, cf_ge_kernels_0_##N##_14, cf_ge_kernels_0_##N##_15,                  \
       cf_ge_kernels_0_##N##_16, cf_ge_kernels_0_##N##_17, cf_ge_kernels_0_##N##_18,                  \
       cf_ge_kernels_0_##N##_19, cf_ge_kernels_0_##N##_20
+#define CF_ROW_COL(F, N) cf_ge_kernels_##F##_##N##_21, cf_ge_kernels_##F##_##N##_22, cf_ge_kernels_##F##_##N##_23
+#define CF_NULL11 nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr
 static const PartFn kParts[2][2][kNumParts] = {
-    {{CF_ROW10(0, 0), CF_ROW_EXTRA(0)}, {CF_ROW10(0, 1), CF_ROW_EXTRA(1)}},
-    {{CF_ROW10(1, 0)}, {CF_ROW10(1, 1)}}};   // fp32 inputs: parts 10-20 absent (null)
+    {{CF_ROW10(0, 0), CF_ROW_EXTRA(0), CF_ROW_COL(0, 0)}, {CF_ROW10(0, 1), CF_ROW_EXTRA(1), CF_ROW_COL(0, 1)}},
+    // fp32 inputs: parts 10-20 absent (null)
+    {{CF_ROW10(1, 0), CF_NULL11, CF_ROW_COL(1, 0)}, {CF_ROW10(1, 1), CF_NULL11, CF_ROW_COL(1, 1)}}};
 
 static const void* part(bool in_f32, bool b_nk, int i, int pre) {
   const PartFn f = kParts[in_f32][b_nk][i];
@@ -125,6 +136,10 @@ static const void* pick(const GemmEpilogueParams& p, bool in_f32, bool b_nk, boo
     return ok ? part(in_f32, b_nk, 10 + 3 * (p.row_op - 1) + (p.row_op2 - 1),
                      (p.bias != nullptr || p.residual != nullptr) ? 1 : 0)
               : nullptr;
+  }
+  if (p.col) {   // column reductions: fast path, parts 21-23 for softmax, LayerNorm, RMSNorm
+    const bool ok = vec && p.row_op >= 1 && p.row_op <= 3;
+    return ok ? part(in_f32, b_nk, 20 + p.row_op, (p.bias != nullptr || p.residual != nullptr) ? 1 : 0) : nullptr;
   }
   if (p.row_op == 5)   // top-k: lists of 4 when k <= 4, else of 8
     return vec ? part(in_f32, b_nk, p.topk <= 4 ? 20 : 19, (p.bias != nullptr) ? 1 : 0) : nullptr;

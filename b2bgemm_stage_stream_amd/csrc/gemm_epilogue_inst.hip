@@ -6,13 +6,15 @@
 //   10 to 18  two row stages, fast path: first row op 1 + (CF_PART - 10) / 3,
 //             second 1 + (CF_PART - 10) % 3 (bf16 inputs only);
 //   19        top-k with lists of 8, fast path (bf16 inputs only);
-//   20        top-k with lists of 4 (k <= 4), fast path (bf16 inputs only).
+//   20        top-k with lists of 4 (k <= 4), fast path (bf16 inputs only);
+//   21 to 23  column reductions (softmax, LayerNorm, RMSNorm over the rows
+//             of each column), fast path.
 #include "gemm_epilogue_kernel.hpp"
 
 #if !defined(CF_IN_F32) || !defined(CF_B_NK) || !defined(CF_PART)
 #error "CF_IN_F32, CF_B_NK and CF_PART must be defined"
 #endif
-#if CF_IN_F32 && CF_PART >= 10
+#if CF_IN_F32 && CF_PART >= 10 && CF_PART <= 20
 #error "two-stage and top-k parts are built for bf16 inputs only"
 #endif
 
@@ -35,8 +37,12 @@ const void* CF_FN(int pre) {
 #elif CF_PART < 19
   if (pre) return (const void*)&gemm_epilogue_kernel<kF, kN, true, 1 + (CF_PART - 10) / 3, true, 1 + (CF_PART - 10) % 3>;
   return (const void*)&gemm_epilogue_kernel<kF, kN, true, 1 + (CF_PART - 10) / 3, false, 1 + (CF_PART - 10) % 3>;
-#else
+#elif CF_PART < 21
   // epilogue ROW 5: lists of 8; ROW 6: lists of 4
+  if (pre) return (const void*)&gemm_epilogue_kernel<kF, kN, true, CF_PART - 14, true>;
+  return (const void*)&gemm_epilogue_kernel<kF, kN, true, CF_PART - 14, false>;
+#else
+  // epilogue ROW 7, 8, 9: column softmax, LayerNorm, RMSNorm
   if (pre) return (const void*)&gemm_epilogue_kernel<kF, kN, true, CF_PART - 14, true>;
   return (const void*)&gemm_epilogue_kernel<kF, kN, true, CF_PART - 14, false>;
 #endif

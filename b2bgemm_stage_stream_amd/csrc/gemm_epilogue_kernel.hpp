@@ -484,6 +484,14 @@ __device__ inline void chan_merge(float& n, float& mean, float& m2, float nb, fl
   n = nn;
 }
 
+// Lane l receives the value of lane l ^ X of its own 32-lane half
+// (ds_swizzle in bit-mask mode: and 0x1f, or 0, xor X).
+template <int X>
+__device__ inline float xor_lanes(float v) {
+  static_assert(X > 0 && X < 32, "xor within a 32-lane half");
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1f | (X << 10)));
+}
+
 // Values of the two lane halves: .x from lane (l & 31), .y from lane (l | 32).
 __device__ inline float2 halves(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -510,6 +518,11 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
   // top-k (ROW 5: lists of 8; ROW 6: lists of 4, for k <= 4)
   constexpr bool kTop = ROW == 5 || ROW == 6;
   constexpr int kL = ROW == 6 ? 4 : 8;
+  // column reductions (ROW 7, 8, 9: softmax, LayerNorm, RMSNorm over the rows
+  // m of each column n): the statistics are per column, and the exchange runs
+  // over the tiles of the tile column (the complementary strip)
+  constexpr bool kCol = ROW >= 7 && ROW <= 9;
+  constexpr int R = kCol ? ROW - 6 : ROW;   // the reduction's operation (1-3 as for rows)
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, r32 = lane & 31;
@@ -611,6 +624,91 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
   float tok = 0.0f;
   if constexpr (ROW != 0) {
     const int cnt_w = min(max(p.N - (n0 + wn * 128), 0), 128);
+    if constexpr (kCol) {
+      // ---- column reduction, levels 1 and 2: over the 4 rows a lane holds
+      // of each of its columns (one per row block), then over the 32 lanes of
+      // its half (xor butterfly; the two halves hold different columns), then,
+      // below, over the two waves that share the columns (wm 0 and 1). Rows
+      // >= M are left out. Partial per column: softmax (max, sum exp(x -
+      // max)); LayerNorm (mean, M2), from sums shifted by a value K of the
+      // column (the half's first row) so that the lane merges are plain sums;
+      // RMSNorm sum x^2.
+      bool rok[4];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) rok[mb] = m0 + wm * 128 + mb * 32 + r32 < p.M;
+      // merge of (a, b, n) with a partner's (oa, ob, on)
+      auto merge = [&](float& a, float& b, float& n, float oa, float ob, float on) {
+        if constexpr (R == 1) {
+          const float mx = fmaxf(a, oa);
+          const float sa = a == -INFINITY ? 0.0f : b * fast_exp2((a - mx) * kLog2e);
+          const float sb = oa == -INFINITY ? 0.0f : ob * fast_exp2((oa - mx) * kLog2e);
+          a = mx;
+          b = sa + sb;
+        } else if constexpr (R == 2) {
+          a += oa;
+          b += ob;
+          n += on;
+        } else {
+          a += oa;
+        }
+      };
+      auto butterfly = [&](float& a, float& b, float& n) {
+        auto step = [&](auto xc) {
+          constexpr int X = decltype(xc)::value;
+          const float oa = xor_lanes<X>(a);
+          const float ob = R == 3 ? 0.0f : xor_lanes<X>(b);
+          const float on = R == 2 ? xor_lanes<X>(n) : 0.0f;
+          merge(a, b, n, oa, ob, on);
+        };
+        step(std::integral_constant<int, 16>{});
+        step(std::integral_constant<int, 8>{});
+        step(std::integral_constant<int, 4>{});
+        step(std::integral_constant<int, 2>{});
+        step(std::integral_constant<int, 1>{});
+      };
+      for_groups([&](int nb, auto qc) {
+        constexpr int q = decltype(qc)::value;
+        const f32x4_t bv = bias4(nb, q);
+        float xv[4][4];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          xgroup(mb, nb, qc, bv, tok, xv[mb]);
+          tok = xv[mb][3];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float a = 0.0f, b = 0.0f, n = 0.0f;
+          if constexpr (R == 1) {
+            a = -INFINITY;
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) a = rok[mb] ? fmaxf(a, xv[mb][e]) : a;
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) b += rok[mb] ? fast_exp2((xv[mb][e] - a) * kLog2e) : 0.0f;
+          } else if constexpr (R == 2) {
+            // K: the column's value in the half's lane 0 (row m0 + wm*128, valid)
+            const float K = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(xv[0][e]), 0));
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+              const float d = rok[mb] ? xv[mb][e] - K : 0.0f;
+              n += rok[mb] ? 1.0f : 0.0f;
+              a += d;
+              b = __builtin_fmaf(d, d, b);
+            }
+            butterfly(a, b, n);
+            // (mean, M2) of the column's rows in this wave
+            const float mean = n > 0.0f ? K + a / n : 0.0f;
+            b = n > 0.0f ? fmaxf(b - a * (a / n), 0.0f) : 0.0f;
+            a = mean;
+          } else {
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) a = rok[mb] ? __builtin_fmaf(xv[mb][e], xv[mb][e], a) : a;
+          }
+          if constexpr (R != 2) butterfly(a, b, n);
+          tok = a;
+          if (r32 == 0) wpart[wm * 256 + wn * 128 + nb * 32 + 8 * q + 4 * h + e] = make_float2(a, b);
+        }
+      });
+    } else {
     // ---- reduction levels 1 and 2 (in-lane, lane halves, then the two waves sharing rows)
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
@@ -753,6 +851,7 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
       if constexpr (!kTop)
         if (h == 0) wpart[wn * 256 + wm * 128 + mb * 32 + r32] = make_float2(a, b);
     }
+    }   // row reductions
     __syncthreads();
 
     // ---- one thread per row: merge the two wave partials, then (reduction
@@ -867,20 +966,28 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
         }
       }
     } else {
+      // thread ml: row ml of the tile (row reductions) or its column ml
+      // (column reductions). The exchange group: the tiles of the row strip,
+      // or of the tile column; G members, this tile is member `me` of group
+      // `gi`, and a statistic covers `total` elements
       const int ml = tid;
-      const bool row_ok = m0 + ml < p.M;
+      const bool row_ok = kCol ? n0 + ml < p.N : m0 + ml < p.M;
       const float2 w0 = wpart[ml], w1 = wpart[256 + ml];
-      const int c0 = min(max(p.N - n0, 0), 128), c1 = min(max(p.N - n0 - 128, 0), 128);
+      const int ext = kCol ? p.M - m0 : p.N - n0;
+      const int c0 = min(max(ext, 0), 128), c1 = min(max(ext - 128, 0), 128);
+      const int G = kCol ? p.strips : p.tiles_n;
+      const int me = kCol ? strip : tn, gi = kCol ? tn : strip;
+      const int total = kCol ? p.M : p.N;
       float a, b;
-      if constexpr (ROW == 1) {
+      if constexpr (R == 1) {
         a = fmaxf(w0.x, w1.x);
         b = w0.y * fast_exp2((w0.x - a) * kLog2e) + (c1 > 0 ? w1.y * fast_exp2((w1.x - a) * kLog2e) : 0.0f);
-      } else if constexpr (ROW == 2) {
+      } else if constexpr (R == 2) {
         float n = (float)c0;
         a = w0.x;
         b = w0.y;
         chan_merge(n, a, b, (float)c1, w1.x, w1.y);
-      } else if constexpr (ROW == 3) {
+      } else if constexpr (R == 3) {
         a = w0.x + w1.x;
         b = 0.0f;
       } else {   // argmax: the first column half holds the smaller columns
@@ -893,18 +1000,18 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
       // own slot; the other tiles publish their partials and read only that.
       // Peer-to-peer mode: every tile reads every partial. Both merge in tile
       // order, so the statistics are bit-identical either way.
-      const bool lf = p.lf_tiles > 0 && p.tiles_n >= p.lf_tiles;
-      if (p.ws_hdr != nullptr && row_ok && lf && tn != 0) {
-        uint64_t* slots = p.ws_slots + (size_t)strip * p.tiles_n * 512 + ml;
-        publish(slots + (size_t)tn * 512, a, tag);
-        if constexpr (ROW != 3) publish(slots + (size_t)tn * 512 + 256, b, tag);
+      const bool lf = p.lf_tiles > 0 && G >= p.lf_tiles;
+      if (p.ws_hdr != nullptr && row_ok && lf && me != 0) {
+        uint64_t* slots = p.ws_slots + (size_t)gi * G * 512 + ml;
+        publish(slots + (size_t)me * 512, a, tag);
+        if constexpr (R != 3) publish(slots + (size_t)me * 512 + 256, b, tag);
         const uint64_t t0 = wall_clock64();
         bool lost = false;
         for (;;) {
           const uint64_t wa = __hip_atomic_load(slots, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           uint64_t wb = 0;
-          if constexpr (ROW != 3) wb = __hip_atomic_load(slots + 256, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if ((uint32_t)(wa >> 32) == tag && (ROW == 3 || (uint32_t)(wb >> 32) == tag)) {
+          if constexpr (R != 3) wb = __hip_atomic_load(slots + 256, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if ((uint32_t)(wa >> 32) == tag && (R == 3 || (uint32_t)(wb >> 32) == tag)) {
             a = __uint_as_float((uint32_t)wa);
             b = __uint_as_float((uint32_t)wb);
             break;
@@ -923,10 +1030,10 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
       } else if (p.ws_hdr != nullptr && row_ok) {
         // word w (0: a, 1: b) of row ml of tile t at t * 512 + w * 256 + ml, so
         // that each store instruction writes whole contiguous lines
-        uint64_t* slots = p.ws_slots + (size_t)strip * p.tiles_n * 512 + ml;
+        uint64_t* slots = p.ws_slots + (size_t)gi * G * 512 + ml;
         if (!lf) {   // the leader's own slot carries the merged result instead
-          publish(slots + (size_t)tn * 512, a, tag);
-          if constexpr (ROW != 3) publish(slots + (size_t)tn * 512 + 256, b, tag);
+          publish(slots + (size_t)me * 512, a, tag);
+          if constexpr (R != 3) publish(slots + (size_t)me * 512 + 256, b, tag);
         }
         const uint64_t t0 = wall_clock64();
         // The peers' words are fetched 8 column tiles at a time with all loads
@@ -934,17 +1041,17 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
         // together. The merge then runs in tile order, so every workgroup of
         // the strip computes bit-identical statistics.
         float ra = 0.0f, rb = 0.0f, rn = 0.0f;
-        if constexpr (ROW == 1 || ROW == 4) ra = -INFINITY;
+        if constexpr (R == 1 || ROW == 4) ra = -INFINITY;
         if constexpr (ROW == 4) rb = __int_as_float(0x7fffffff);
         bool lost = false;   // a peer's partial never arrived: the row's results become NaN (index -1)
-        for (int tb = 0; tb < p.tiles_n; tb += 8) {
+        for (int tb = 0; tb < G; tb += 8) {
           float va[8], vb[8];
           uint32_t need = 0;
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             va[j] = a;
             vb[j] = b;
-            if (tb + j < p.tiles_n && tb + j != tn) need |= 1u << j;
+            if (tb + j < G && tb + j != me) need |= 1u << j;
           }
           while (need) {
             uint64_t wa[8], wb[8];
@@ -953,14 +1060,14 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
               wa[j] = wb[j] = 0;
               if (need & (1u << j)) {
                 wa[j] = __hip_atomic_load(slots + (size_t)(tb + j) * 512, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if constexpr (ROW != 3)
+                if constexpr (R != 3)
                   wb[j] = __hip_atomic_load(slots + (size_t)(tb + j) * 512 + 256, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);
               }
             }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-              const bool ok = (uint32_t)(wa[j] >> 32) == tag && (ROW == 3 || (uint32_t)(wb[j] >> 32) == tag);
+              const bool ok = (uint32_t)(wa[j] >> 32) == tag && (R == 3 || (uint32_t)(wb[j] >> 32) == tag);
               if ((need & (1u << j)) && ok) {
                 va[j] = __uint_as_float((uint32_t)wa[j]);
                 vb[j] = __uint_as_float((uint32_t)wb[j]);
@@ -981,14 +1088,14 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int tt = tb + j;
-            if (tt >= p.tiles_n) break;
-            if constexpr (ROW == 1) {
+            if (tt >= G) break;
+            if constexpr (R == 1) {
               const float Mn = fmaxf(ra, va[j]);
               rb = rb * fast_exp2((ra - Mn) * kLog2e) + vb[j] * fast_exp2((va[j] - Mn) * kLog2e);
               ra = Mn;
-            } else if constexpr (ROW == 2) {
-              chan_merge(rn, ra, rb, (float)min(kGemmBN, p.N - tt * kGemmBN), va[j], vb[j]);
-            } else if constexpr (ROW == 3) {
+            } else if constexpr (R == 2) {
+              chan_merge(rn, ra, rb, (float)min(kGemmBN, total - tt * kGemmBN), va[j], vb[j]);
+            } else if constexpr (R == 3) {
               ra += va[j];
             } else if (tt == 0 || va[j] > ra) {   // argmax: tiles in column order, so ties keep the smaller column
               ra = va[j];
@@ -1002,25 +1109,26 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
           a = __int_as_float(0x7fc00000);
           b = ROW == 4 ? __int_as_float(-1) : __int_as_float(0x7fc00000);
         }
-        if (lf) {   // the leader (tn == 0) hands the merged statistics to its followers
+        if (lf) {   // the leader (me == 0) hands the merged statistics to its followers
           publish(slots, a, tag);
-          if constexpr (ROW != 3) publish(slots + 256, b, tag);
+          if constexpr (R != 3) publish(slots + 256, b, tag);
         }
       }
       float2 st;
-      if constexpr (ROW == 1) st = make_float2(a * kLog2e, 1.0f / b);
-      else if constexpr (ROW == 2) st = make_float2(a, rsqrtf(b / (float)p.N + p.eps));
-      else if constexpr (ROW == 3) st = make_float2(rsqrtf(a / (float)p.N + p.eps), 0.0f);
+      if constexpr (R == 1) st = make_float2(a * kLog2e, 1.0f / b);
+      else if constexpr (R == 2) st = make_float2(a, rsqrtf(b / (float)total + p.eps));
+      else if constexpr (R == 3) st = make_float2(rsqrtf(a / (float)total + p.eps), 0.0f);
       else st = make_float2(a, b);
       rstat[ml] = st;
-      // the reduction's own per-row result, stored once per strip (column tile 0)
-      if (tn == 0 && row_ok) {
-        const int m = m0 + ml;
+      // the reduction's own per-row (per-column) result, stored once per
+      // exchange group (by its member 0)
+      if (me == 0 && row_ok) {
+        const int m = kCol ? n0 + ml : m0 + ml;
         if constexpr (ROW == 4) p.row_index[m] = __float_as_int(b);
         if (p.row_stats != nullptr) {
-          if constexpr (ROW == 1) p.row_stats[m] = a + logf(b);   // log-sum-exp: max + ln sum exp(x - max)
-          else if constexpr (ROW == 2) { p.row_stats[2 * m] = a; p.row_stats[2 * m + 1] = st.y; }
-          else if constexpr (ROW == 3) p.row_stats[m] = st.x;
+          if constexpr (R == 1) p.row_stats[m] = a + logf(b);   // log-sum-exp: max + ln sum exp(x - max)
+          else if constexpr (R == 2) { p.row_stats[2 * m] = a; p.row_stats[2 * m + 1] = st.y; }
+          else if constexpr (R == 3) p.row_stats[m] = st.x;
           else p.row_stats[m] = a;
         }
       }
@@ -1248,7 +1356,7 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const int ml = wm * 128 + mb * 32 + r32;
-      st[mb] = ROW != 0 ? rstat[ml] : make_float2(0.f, 0.f);
+      st[mb] = (ROW != 0 && !kCol) ? rstat[ml] : make_float2(0.f, 0.f);
       st2[mb] = kTwo ? rstat2[ml] : make_float2(0.f, 0.f);
       rowoff[mb] = ((uint32_t)(m0 + ml) * p.ldc + (uint32_t)(n0 + wn * 128 + 4 * h)) * es;
       if constexpr (kX != 0) xrowoff[mb] = ((uint32_t)(m0 + ml) * p.ldx + (uint32_t)(n0 + wn * 128 + 4 * h)) * xes;
@@ -1258,8 +1366,17 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
       const int c = nb * 32 + 8 * q;
       const f32x4_t bv = bias4(nb, q);
       f32x4_t g = {1.f, 1.f, 1.f, 1.f}, be = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (ROW == 2 || ROW == 3) g = *(const f32x4_t*)(vg_lane + c);
-      if constexpr (ROW == 2) be = *(const f32x4_t*)(ve_lane + c);
+      if constexpr (R == 2 || R == 3) g = *(const f32x4_t*)(vg_lane + c);
+      if constexpr (R == 2) be = *(const f32x4_t*)(ve_lane + c);
+      // column reductions: the statistics of the group's 4 columns
+      f32x4_t csx = {0.f, 0.f, 0.f, 0.f}, csy = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (kCol) {
+        const float* rs_lane = (const float*)rstat + 2 * (wn * 128 + 4 * h);
+        const f32x4_t s01 = *(const f32x4_t*)(rs_lane + 2 * c);
+        const f32x4_t s23 = *(const f32x4_t*)(rs_lane + 2 * c + 4);
+        csx = f32x4_t{s01[0], s01[2], s23[0], s23[2]};
+        csy = f32x4_t{s01[1], s01[3], s23[1], s23[3]};
+      }
       f32x4_t g2 = {1.f, 1.f, 1.f, 1.f}, b2 = {0.f, 0.f, 0.f, 0.f};
       if constexpr (kTwo) {
         g2 = *(const f32x4_t*)(vg2_lane + c);
@@ -1301,7 +1418,10 @@ __device__ inline __attribute__((always_inline)) void epilogue(const f32x16_t (&
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          if constexpr (ROW == 2) y[e] = __builtin_fmaf((x[e] - st[mb].x) * st[mb].y, g[e], be[e]);
+          if constexpr (kCol && R == 2) y[e] = __builtin_fmaf((x[e] - csx[e]) * csy[e], g[e], be[e]);
+          else if constexpr (kCol && R == 3) y[e] = x[e] * csx[e] * g[e];
+          else if constexpr (kCol) y[e] = fast_exp2(__builtin_fmaf(x[e], kLog2e, -csx[e])) * csy[e];
+          else if constexpr (ROW == 2) y[e] = __builtin_fmaf((x[e] - st[mb].x) * st[mb].y, g[e], be[e]);
           else if constexpr (ROW == 3) y[e] = x[e] * st[mb].x * g[e];
           else if constexpr (ROW == 1) y[e] = fast_exp2(__builtin_fmaf(x[e], kLog2e, -st[mb].x)) * st[mb].y;
           else y[e] = x[e];
@@ -1408,9 +1528,13 @@ void gemm_epilogue_kernel(GemmEpilogueParams p) {
     // XCDs (workgroup w on XCD w % 8); in a full round each XCD takes an
     // xcd_a x xcd_b rectangle of (strip, column) tiles so that its workgroups
     // share A strips and B panels in that XCD's L2.
-    const int tile = round_tile(base, (int)blockIdx.x, (int)gridDim.x, p.tiles, p.tiles_n, p.xcd_a, p.xcd_b);
+    const int tile = round_tile(base, (int)blockIdx.x, (int)gridDim.x, p.tiles, p.group, p.xcd_a, p.xcd_b);
     if (tile >= p.tiles) break;
-    const int strip = tile / p.tiles_n, tn = tile - strip * p.tiles_n;
+    // tiles are numbered group by group: strip-major for row reductions (a
+    // group is a row strip), column-major for column reductions (a group is
+    // a tile column)
+    const int grp = tile / p.group, mbr = tile - grp * p.group;
+    const int strip = p.col ? mbr : grp, tn = p.col ? grp : mbr;
     const int m0 = strip * kGemmBM, n0 = tn * kGemmBN;
 
     f32x16_t acc[4][4];

@@ -83,6 +83,18 @@ typedef enum {
                            no key (only when M > L) outputs 0.                          */
 } cf_mask;
 
+/* The axis a row operation (softmax, LayerNorm, RMSNorm) reduces over.
+ * CF_AXIS_ROW: over the columns n of each row m (the default). CF_AXIS_COLUMN:
+ * over the rows m of each column n, through the tiles that share n -- the
+ * complementary strip of the review's Eq. (1) argument (ComFuse review,
+ * Referee Report major comment 1 on Sec. III). gamma/beta stay per column n;
+ * row_stats then holds one statistic per column ([N], or [N, 2] for
+ * LayerNorm). Column reductions: cf_gemm_epilogue with row_op softmax,
+ * LayerNorm or RMSNorm, no second row stage, fast-path layouts (N a multiple
+ * of 8, 16-byte aligned operands, leading dimensions multiples of 8 elements)
+ * and M <= 65536; CF_ERR_UNSUPPORTED otherwise. */
+typedef enum { CF_AXIS_ROW = 0, CF_AXIS_COLUMN = 1 } cf_axis;
+
 /* Epilogue descriptor. The stages run in this fixed order on the fp32
  * accumulator of P = A.B (ComFuse review, "What carries the argument":
  * elementwise nodes stream over the accumulator fragments, the reduction is a
@@ -160,6 +172,7 @@ typedef struct cf_epilogue {
   const void* beta2;        /* its LayerNorm beta, or NULL                               */
   float eps2;
   int32_t topk;             /* CF_ROW_TOPK: k (1..8); 0 otherwise                  */
+  cf_axis axis;             /* the row op's reduction axis (CF_AXIS_ROW unless set) */
 } cf_epilogue;
 
 /* Fills *epi with the identity epilogue (alpha 1, no bias/residual/act/row op). */
@@ -280,9 +293,12 @@ const char* cf_version(void);
  * previous value. */
 uint64_t cf_set_exchange_timeout_us(uint64_t us);
 
-/* Default of cf_set_exchange_leader_tiles (strips of this many column tiles
- * or more exchange leader-follower). */
-#define CF_DEFAULT_LEADER_TILES 33
+/* Default of cf_set_exchange_leader_tiles: 0, peer-to-peer for every strip.
+ * On MI355X leader-follower measured slower at every strip width tried (16 to
+ * 256 column tiles, K = 256 and 2048): its followers wait for two exchange
+ * latencies, while the extra partials peer-to-peer reads come from L2 and the
+ * last-level cache. */
+#define CF_DEFAULT_LEADER_TILES 0
 
 /* Aggregation mode of the strip exchange (ComFuse review, Referee Report minor
  * comment 4 on Sec. III-A and "Assumptions & free parameters": a dual-mode
@@ -293,11 +309,12 @@ uint64_t cf_set_exchange_timeout_us(uint64_t us);
  * statistics, which the others read. Both merge in column-tile order, so the
  * outputs are bit-identical; the mode changes only the exchange's traffic
  * (tiles^2 against 2 tiles partials per strip) and latency (one hop against
- * two). Strips of at least `min_tiles` column tiles of 256 use
- * leader-follower, narrower ones peer-to-peer; 0 means never (C_N here, the
- * default CF_DEFAULT_LEADER_TILES). A negative value changes nothing.
- * Returns the previous value. Process-wide; applies to the first row stage
- * (a second row stage and top-k keep their own schemes). */
+ * two). Exchange groups (row strips, or tile columns for a column
+ * reduction) of at least `min_tiles` tiles of 256 use leader-follower,
+ * narrower ones peer-to-peer; 0 means never (C_N here; default
+ * CF_DEFAULT_LEADER_TILES). A negative value changes nothing. Returns the
+ * previous value. Process-wide; applies to the first row stage (a second row
+ * stage and top-k keep their own schemes). */
 int cf_set_exchange_leader_tiles(int min_tiles);
 
 #ifdef __cplusplus

@@ -57,13 +57,15 @@ static cf_epilogue make_epi(cf_row_op op) {
   return e;
 }
 
-static void check_plan(int64_t M, int64_t N, cf_row_op op, int64_t per_cu, int64_t cus) {
+static void check_plan(int64_t M, int64_t N, cf_row_op op, int64_t per_cu, int64_t cus, bool col = false) {
   cf_epilogue e = make_epi(op);
+  setv(e.axis, col ? CF_AXIS_COLUMN : CF_AXIS_ROW);
   const cf::GemmPlan g = cf::plan_gemm(M, N, &e);
+  CHECK(g.group == (col ? g.strips : g.tiles_n), "group width");
   cf::GridPlan gp;
   const cf_status st = cf::plan_grid(g, per_cu, cus, &gp);
   const int64_t cap = per_cu * cus;
-  if (g.exchange && g.tiles_n > cap) {
+  if (g.exchange && g.group > cap) {
     CHECK(st == CF_ERR_UNSUPPORTED, "M=%lld N=%lld cap=%lld: strip wider than capacity not refused",
           (long long)M, (long long)N, (long long)cap);
     return;
@@ -72,10 +74,10 @@ static void check_plan(int64_t M, int64_t N, cf_row_op op, int64_t per_cu, int64
   if (st != CF_OK) return;
   CHECK(gp.grid >= 1 && gp.grid <= cap && gp.grid <= g.tiles, "grid %lld outside [1, min(cap %lld, tiles %lld)]",
         (long long)gp.grid, (long long)cap, (long long)g.tiles);
-  if (g.exchange) CHECK(gp.grid % g.tiles_n == 0, "grid %lld not whole strips of %lld", (long long)gp.grid, (long long)g.tiles_n);
+  if (g.exchange) CHECK(gp.grid % g.group == 0, "grid %lld not whole groups of %lld", (long long)gp.grid, (long long)g.group);
   // the persistent loop
   std::vector<int> seen((size_t)g.tiles, 0);
-  const int grid = (int)gp.grid, tiles = (int)g.tiles, tn = (int)g.tiles_n;
+  const int grid = (int)gp.grid, tiles = (int)g.tiles, tn = (int)g.group;
   for (int base = 0; base < tiles; base += grid) {
     std::vector<std::set<int64_t>> xs(8), ys(8);
     std::vector<int> xcount(8, 0);
@@ -87,9 +89,10 @@ static void check_plan(int64_t M, int64_t N, cf_row_op op, int64_t per_cu, int64
       ++seen[(size_t)t];
       CHECK(t >= base && t < base + grid, "tile %d outside its round [%d, %d)", t, base, base + grid);
       if (g.exchange) {
-        // the strip of t lies entirely inside this round
+        // the exchange group of t (a row strip, or a tile column) lies
+        // entirely inside this round
         const int s0 = (t / tn) * tn;
-        CHECK(s0 >= base && s0 + tn <= base + grid, "strip of tile %d split across rounds", t);
+        CHECK(s0 >= base && s0 + tn <= base + grid, "group of tile %d split across rounds", t);
       }
       xs[bid & 7].insert(t / tn);
       ys[bid & 7].insert(t % tn);
@@ -145,6 +148,7 @@ static void fuzz_checks(unsigned seed, int n) {
     e.row_stats = (rng() % 4 == 0) ? (float*)(base + pick({0, 2})) : nullptr;
     e.row_index = (rng() % 3 == 0) ? (int32_t*)(base + pick({0, 2})) : nullptr;
     setv(e.row_op2, pick({0, 0, 1, 2, 3, 4, 9}));
+    setv(e.axis, pick({0, 0, 1, 5}));
     e.eps2 = (rng() & 1) ? 0.0f : 1e-6f;
     e.topk = (int32_t)pick({0, 1, 4, 8, 9});
     const int64_t M = pick({0, 1, 255, 256, 8192, -1, 1ll << 31});
@@ -164,6 +168,8 @@ static void fuzz_checks(unsigned seed, int n) {
     CHECK(st >= CF_OK && st <= CF_ERR_DEVICE_TIMEOUT, "status %d out of range", (int)st);
     if (st == CF_OK && !out.empty) {
       CHECK(M > 0 && N > 0, "accepted an empty or negative shape");
+      if (out.plan.col) CHECK(out.vec && out.row_op >= CF_ROW_SOFTMAX && out.row_op <= CF_ROW_RMSNORM,
+                              "column reduction accepted outside its fast-path row ops");
       CHECK(out.plan.tiles == ((M + 255) / 256) * ((N + 255) / 256), "tile count");
     }
   }
@@ -177,11 +183,14 @@ int main() {
   int n = 0;
   for (int64_t M : Ms)
     for (int64_t N : Ns)
-      for (const auto& d : devs)
+      for (const auto& d : devs) {
         for (cf_row_op op : ops) {
           check_plan(M, N, op, d[0], d[1]);
           ++n;
         }
+        check_plan(M, N, CF_ROW_SOFTMAX, d[0], d[1], true);   // column reduction: tile-column groups
+        ++n;
+      }
   fuzz_checks(1234, 200000);
   if (g_fail) {
     std::fprintf(stderr, "%d failures\n", g_fail);

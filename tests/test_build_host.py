@@ -42,7 +42,7 @@ def test_builder_loads_without_library(tmp_path):
     parts = {tuple(d.split("=")[1] for d in u[2]) for u in us if u[2]}
     for f32 in ("0", "1"):
         for nk in ("0", "1"):
-            want = set(range(10)) | (set(range(10, 21)) if f32 == "0" else set())
+            want = set(range(10)) | {21, 22, 23} | (set(range(10, 21)) if f32 == "0" else set())
             assert {int(p) for a, b, p in parts if (a, b) == (f32, nk)} == want
 
 

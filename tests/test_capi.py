@@ -130,6 +130,13 @@ def epi(**kw):
     (dict(K=60, epi=epi(row_op=5, row_index=PW, topk=4)), cf.CF_ERR_UNSUPPORTED),   # fast-path layouts only
     (dict(epi=epi(row_op=2, topk=4)), cf.CF_ERR_INVALID_ARGUMENT),            # topk belongs to CF_ROW_TOPK
     (dict(epi=epi(row_op=6)), cf.CF_ERR_INVALID_ARGUMENT),
+    (dict(epi=epi(row_op=1, axis=5)), cf.CF_ERR_INVALID_ARGUMENT),     # no such axis
+    (dict(epi=epi(axis=1)), cf.CF_ERR_INVALID_ARGUMENT),               # a column axis needs a row op
+    (dict(epi=epi(row_op=4, row_index=PW, axis=1)), cf.CF_ERR_UNSUPPORTED),   # argmax over columns
+    (dict(epi=epi(row_op=2, row_op2=1, axis=1)), cf.CF_ERR_UNSUPPORTED),      # one column stage
+    (dict(K=60, epi=epi(row_op=1, axis=1)), cf.CF_ERR_UNSUPPORTED),   # column reductions: fast path only
+    (dict(M=70000, epi=epi(row_op=3, axis=1)), cf.CF_ERR_UNSUPPORTED),   # a tile column of more than 256 tiles
+    (dict(M=4096, epi=epi(row_op=2, axis=1)), cf.CF_ERR_WORKSPACE),   # 16 strips exchange: needs a workspace
     (dict(M=0), cf.CF_OK),            # empty problems launch nothing
     (dict(N=0), cf.CF_OK),
 ])
@@ -164,6 +171,7 @@ def b2b(batch=1, M=64, K=64, L=64, N=64, A=PA, lda=64, sa=0, B0=PB, ldb0=64, sb0
     (dict(mid=epi(row_op=4, row_index=PW)), cf.CF_ERR_UNSUPPORTED),   # argmax between two GEMMs
     (dict(mid=epi(row_op=1, row_op2=2)), cf.CF_ERR_UNSUPPORTED),      # one row stage between two GEMMs
     (dict(mid=epi(row_op=5, row_index=PW, topk=2)), cf.CF_ERR_UNSUPPORTED),   # top-k between two GEMMs
+    (dict(mid=epi(row_op=1, axis=1)), cf.CF_ERR_UNSUPPORTED),        # S's columns are never all on chip
     (dict(batch=0), cf.CF_OK),
 ])
 def test_b2bgemm_argument_checks(kw, status):
@@ -179,6 +187,9 @@ def test_workspace_sizes():
     # top-k exchanges 8 (value, column) pairs per row
     assert cf.cf_gemm_epilogue_workspace_size(8192, 4096, 4096, epi(row_op=5, row_index=PW, topk=4)) == \
         512 + 32 * 16 * 256 * 16 * 8
+    # a column reduction exchanges over the tile columns: the same slots
+    assert cf.cf_gemm_epilogue_workspace_size(8192, 4096, 4096, epi(row_op=2, axis=1)) == 512 + 32 * 16 * 256 * 16
+    assert cf.cf_gemm_epilogue_workspace_size(256, 4096, 4096, epi(row_op=2, axis=1)) == 0   # one strip
     # a second row stage exchanges through a second set of slots
     assert cf.cf_gemm_epilogue_workspace_size(8192, 4096, 4096, epi(row_op=2, row_op2=1)) == \
         512 + 2 * 32 * 16 * 256 * 16

@@ -446,6 +446,90 @@ def test_leader_follower_equals_peer_to_peer(N, M, row_op):
         P.assert_close(P.gpu_to_f64(outs["lf"][0]), R, P.REL_F_BF16, P.MAX_ABS_BF16, f"leader-follower {row_op} N={N}")
 
 
+# ---------------------------------------------------------------------------- column reductions
+
+def check_columns(w, dev, ref, col_op, what, b_is_nk=False, **extra):
+    """A column reduction (softmax / LayerNorm / RMSNorm over the rows of each
+    column) against the oracle: fp32 and bf16 outputs and the per-column
+    statistics."""
+    M, N = w.dims["M"], w.dims["N"]
+    g = dev.get("gamma", dev.get("weight"))
+    gr = ref.get("gamma", ref.get("weight"))
+    ln = col_op == "layernorm"
+    st = torch.full((N, 2) if ln else (N,), float("nan"), dtype=torch.float32, device="cuda")
+    kw = dict(row_op=col_op, axis="column", gamma=None if col_op == "softmax" else g,
+              beta=dev["beta"] if ln else None, eps=1e-5, row_stats=st, **extra)
+    B = dev["B"].t().contiguous() if b_is_nk else dev["B"]
+    c32 = run(dev["A"], B, torch.float32, b_is_nk=b_is_nk, **kw)
+    rkw = dict(alpha=extra.get("alpha", 1.0), act=extra.get("act", "none"),
+               bias=None if extra.get("bias") is None else P.gpu_to_f64(extra["bias"]),
+               residual=None if extra.get("residual") is None else P.gpu_to_f64(extra["residual"]))
+    R = oracle.gemm_epilogue_columns(ref["A"], ref["B"], col_op=col_op, gamma=None if col_op == "softmax" else gr,
+                                     beta=ref["beta"] if ln else None, eps=1e-5, **rkw)
+    r, m = P.assert_close(P.gpu_to_f64(c32), R, P.REL_F_BF16, P.MAX_ABS_BF16, what + " f32-out")
+    Rs = oracle.gemm_epilogue_column_stats(ref["A"], ref["B"], col_op=col_op, eps=1e-5, **rkw)
+    P.assert_close(P.gpu_to_f64(st), Rs, 1e-5, 1e-4, what + " column statistics")
+    kw["row_stats"] = None
+    c16 = run(dev["A"], B, torch.bfloat16, b_is_nk=b_is_nk, **kw)
+    P.assert_bf16_consistent(c16, c32, R, what + " bf16-out")
+    print(f"{what}: relF {r:.2e} maxabs {m:.2e}", flush=True)
+    return c32
+
+
+@pytest.mark.parametrize("col_op", ["softmax", "layernorm", "rmsnorm"])
+@pytest.mark.parametrize("shape", [(256, 512, 128), (700, 768, 256), (1000, 264, 64), (2048, 1024, 512),
+                                   (8192, 512, 64)])
+def test_column_reductions(col_op, shape):
+    # one row strip, ragged strips and column tiles, 32 strips per tile column
+    M, N, K = shape
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=31, M=M, N=N, K=K)
+    check_columns(w, dev, ref, col_op, f"column {col_op} {shape}")
+
+
+@pytest.mark.parametrize("col_op", ["softmax", "layernorm", "rmsnorm"])
+def test_column_reductions_with_epilogue_and_nk(col_op):
+    # alpha, bias, residual and ReLU before the column reduction; B given [N, K]
+    w, dev, ref = P.inputs("c3_gemm_residual_rmsnorm", seed=32, M=600, N=1024, K=256)
+    dev["gamma"], ref["gamma"] = dev["weight"], ref["weight"]
+    beta = torch.linspace(-0.2, 0.2, 1024, device="cuda").to(torch.bfloat16)
+    bias = torch.linspace(-0.5, 0.5, 1024, device="cuda").to(torch.bfloat16)
+    dev["beta"], ref["beta"] = beta, P.gpu_to_f64(beta)
+    check_columns(w, dev, ref, col_op, f"column {col_op} + alpha/bias/residual/relu, B[N,K]", b_is_nk=True,
+                  alpha=0.5, bias=bias, residual=dev["residual"], act="relu")
+
+
+def test_column_softmax_fp32_inputs_and_large_logits():
+    w, dev, ref = P.inputs("c1_gemm_bias_softmax_f32", seed=33, M=700, N=512, K=96)
+    dev["A"] = dev["A"] * 40.0
+    ref["A"] = P.gpu_to_f64(dev["A"])
+    g = torch.ones(512, device="cuda")
+    st = torch.empty(512, dtype=torch.float32, device="cuda")
+    C = run(dev["A"], dev["B"], torch.float32, row_op="softmax", axis="column", bias=dev["bias"], row_stats=st)
+    R = oracle.gemm_epilogue_columns(ref["A"], ref["B"], bias=ref["bias"], col_op="softmax")
+    P.assert_close(P.gpu_to_f64(C), R, P.REL_F_F32, P.MAX_ABS_F32, "fp32 column softmax, logits x40")
+    del g
+
+
+def test_column_reduction_modes_and_locality():
+    # leader-follower equals peer-to-peer bit for bit; column n of the output
+    # depends on column n of B only (the transposed Eq. (1) locality)
+    w, dev, ref = P.inputs("c2_gemm_layernorm", seed=34, M=4096, N=768, K=256)
+    kw = dict(row_op="layernorm", axis="column", gamma=dev["gamma"], beta=dev["beta"], eps=1e-5)
+    outs = []
+    for tiles in (0, 2):
+        old = cf.cf_set_exchange_leader_tiles(tiles)
+        try:
+            outs.append(run(dev["A"], dev["B"], torch.bfloat16, **kw))
+        finally:
+            cf.cf_set_exchange_leader_tiles(old)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    B2 = dev["B"].clone()
+    B2[:, 77] = -B2[:, 77] * 2
+    c2 = run(dev["A"], B2, torch.bfloat16, **kw)
+    diff = (c2.view(torch.int16) != outs[0].view(torch.int16)).any(dim=0).cpu().numpy()
+    assert diff[77] and diff.sum() == 1
+
+
 # ---------------------------------------------------------------------------- wide strips
 
 @pytest.mark.parametrize("N", [8192, 16384])

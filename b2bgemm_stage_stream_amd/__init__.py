@@ -93,10 +93,13 @@ _lib.cf_set_exchange_timeout_us.argtypes = [ctypes.c_uint64]
 _lib.cf_set_exchange_timeout_us.restype = ctypes.c_uint64
 _lib.cf_set_exchange_leader_tiles.argtypes = [_int]
 _lib.cf_set_exchange_leader_tiles.restype = _int
+_lib.cf_set_b2b_pingpong.argtypes = [_int]
+_lib.cf_set_b2b_pingpong.restype = _int
 
 EXPORTED = ["cf_epilogue_init", "cf_gemm_epilogue_workspace_size", "cf_workspace_init",
             "cf_workspace_status", "cf_gemm_epilogue", "cf_gemm_epilogue_noalloc", "cf_b2bgemm", "cf_status_string",
-            "cf_last_hip_error", "cf_version", "cf_set_exchange_timeout_us", "cf_set_exchange_leader_tiles"]
+            "cf_last_hip_error", "cf_version", "cf_set_exchange_timeout_us", "cf_set_exchange_leader_tiles",
+            "cf_set_b2b_pingpong"]
 
 
 class CfError(RuntimeError):
@@ -237,6 +240,12 @@ def cf_set_exchange_leader_tiles(min_tiles: int) -> int:
     """Strips of at least ``min_tiles`` column tiles exchange leader-follower
     (0: never); returns the previous setting."""
     return int(_lib.cf_set_exchange_leader_tiles(int(min_tiles)))
+
+
+def cf_set_b2b_pingpong(on: int) -> int:
+    """Selects (1) or deselects (0) the ping-pong schedule of cf_b2bgemm's
+    softmax; a negative value only reads it. Returns the previous value."""
+    return int(_lib.cf_set_b2b_pingpong(int(on)))
 
 
 def cf_gemm_epilogue_workspace_size(M: int, N: int, K: int, epi: Optional[cf_epilogue] = None) -> int:

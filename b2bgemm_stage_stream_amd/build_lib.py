@@ -99,8 +99,24 @@ def source_hash() -> str:
     return h.hexdigest()
 
 
-def _unit_hash(src_hash: str, src: str, defs: list[str]) -> str:
-    return hashlib.sha256(repr((src_hash, os.path.basename(src), defs)).encode()).hexdigest()
+def _unit_hash(src: str, defs: list[str]) -> str:
+    """Hash of what one object file is built from: the flags, every header
+    (any file that is not itself a translation unit), the unit's own source
+    and its defines. Translation units include headers only, so a change to
+    one .hip file rebuilds that file's objects alone."""
+    h = hashlib.sha256()
+    flags = [{INCLUDE: "<include>", CSRC: "<csrc>"}.get(f, f) for f in FLAGS]
+    h.update(repr((flags, defs, os.path.basename(src))).encode())
+    for d in (CSRC, INCLUDE):
+        for f in sorted(os.listdir(d)):
+            p = os.path.join(d, f)
+            if os.path.isfile(p) and not f.endswith((".hip", ".cpp")):
+                h.update(f.encode() + b"\0")
+                with open(p, "rb") as fh:
+                    h.update(fh.read())
+    with open(src, "rb") as fh:
+        h.update(fh.read())
+    return h.hexdigest()
 
 
 def _read(path: str) -> str:
@@ -156,7 +172,7 @@ def build(jobs: Optional[int] = None, force: bool = True, log: Log = _stderr) ->
     src_hash = source_hash()
     todo, objs = [], []
     for src, obj, defs in units():
-        st = _unit_hash(src_hash, src, defs)
+        st = _unit_hash(src, defs)
         objs.append(obj)
         if force or not os.path.exists(obj) or _read(obj + ".stamp") != st:
             todo.append((src, obj, defs, st))

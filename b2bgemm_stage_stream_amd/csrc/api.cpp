@@ -19,6 +19,7 @@ thread_local int g_last_hip_error = 0;
 std::atomic<uint64_t> g_timeout_us{2000000};
 // strips of at least this many column tiles exchange leader-follower (0: never)
 std::atomic<int> g_lf_tiles{CF_DEFAULT_LEADER_TILES};
+std::atomic<int> g_b2b_pingpong{0};
 
 struct DeviceInfo {
   bool valid = false;
@@ -310,6 +311,7 @@ cf_status cf_b2bgemm(int64_t batch, int64_t M, int64_t K, int64_t L, int64_t N, 
   p.causal = mid && mid->mask == CF_MASK_CAUSAL;
   p.row_stats = mid ? mid->row_stats : nullptr;
   p.coff = (int)(L - M);
+  p.pingpong = g_b2b_pingpong.load();
   if (!cf::b2b_supported(p)) return CF_ERR_UNSUPPORTED;
 
   int dev;
@@ -340,6 +342,10 @@ uint64_t cf_set_exchange_timeout_us(uint64_t us) { return g_timeout_us.exchange(
 
 int cf_set_exchange_leader_tiles(int min_tiles) {
   return min_tiles < 0 ? g_lf_tiles.load() : g_lf_tiles.exchange(min_tiles);
+}
+
+int cf_set_b2b_pingpong(int on) {
+  return on < 0 ? g_b2b_pingpong.load() : g_b2b_pingpong.exchange(on ? 1 : 0);
 }
 
 }  // extern "C"

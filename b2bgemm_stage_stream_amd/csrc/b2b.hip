@@ -459,11 +459,11 @@ hipError_t launch_b2b(const B2bParams& p, hipStream_t stream) {
   int cus = 0, per_cu = 0;
   hipError_t e;
   if ((e = device_cus_cached(&cus)) != hipSuccess) return e;
-  int bm = kBM;
-  const void* ks = b2b_stream_pick(p, cus, &bm);
+  int bm = kBM, threads = kThreads;
+  const void* ks = b2b_stream_pick(p, cus, &bm, &threads);
   const void* k = ks ? ks : pick(p);
   if (!k) return hipErrorNotSupported;
-  if ((e = blocks_per_cu_cached(k, kThreads, &per_cu)) != hipSuccess) return e;
+  if ((e = blocks_per_cu_cached(k, threads, &per_cu)) != hipSuccess) return e;
   // the general kernel's tiles also run over the column blocks of O
   const long nblocks = ks ? 1 : (p.N + 32 * nb_of(p.N) - 1) / (32 * nb_of(p.N));
   const long tiles = (long)p.batch * ((p.M + bm - 1) / bm) * nblocks;
@@ -472,7 +472,7 @@ hipError_t launch_b2b(const B2bParams& p, hipStream_t stream) {
   if (ks && g >= 8) g -= g % 8;   // the streamed kernel maps workgroups to XCDs in groups of 8
   const int grid = (int)g;
   void* args[] = {(void*)&p};
-  return hipLaunchKernel(k, dim3(grid), dim3(kThreads), args, 0, stream);
+  return hipLaunchKernel(k, dim3(grid), dim3(threads), args, 0, stream);
 }
 
 }  // namespace cf

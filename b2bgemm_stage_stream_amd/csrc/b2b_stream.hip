@@ -62,6 +62,63 @@ __device__ inline int swz_rows256(int r) { return r & 15; }                     
 __device__ inline int swz_tr128(int r) { return 2 * (r & 3); }                  // transposed reads, 128-B rows
 __device__ inline int swz_tr256(int r) { return (2 * (r & 3)) ^ (4 * (r & 3)); }  // transposed reads, 256-B rows
 
+// Softmax of one 32-row block whose S^T accumulators s[lb] hold l = lb*32 +
+// 8(r >> 2) + 4h + (r & 3) of row m = lane & 31. Full form: the row extreme
+// of S (max for alpha >= 0, min otherwise, so that it is the extreme of
+// alpha*S), and the integer stabiliser cs raised to cover it with an exact
+// power-of-two rescale of what was accumulated (o and the lane's row-sum part
+// ls).
+template <int NB>
+__device__ inline void sm_full_rb(const f32x16_t (&s)[2], f32x16_t (&o)[NB], float& cs, float& ls, float scale) {
+  float mx;
+  if (scale >= 0.0f) {
+    mx = -INFINITY;
+#pragma unroll
+    for (int lb = 0; lb < 2; ++lb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[lb][r]);
+    mx = max_halves(mx);
+  } else {
+    mx = INFINITY;
+#pragma unroll
+    for (int lb = 0; lb < 2; ++lb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fminf(mx, s[lb][r]);
+    mx = min_halves(mx);
+  }
+  const float cn = fmaxf(cs, ceilf(mx * scale));
+  if (cn > cs && cs != -INFINITY) {
+    const int sh = (int)(cs - cn);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[nb][r] = __builtin_amdgcn_ldexpf(o[nb][r], sh);
+    ls = __builtin_amdgcn_ldexpf(ls, sh);
+  }
+  cs = cn;
+}
+// The terms 2^(scale*s - cs) of one row block, added to the lane's row-sum part
+// unrounded, and packed to bf16 as the GEMM2 operand (k-slot order of the
+// accumulator registers). cs = -inf only while a causal row has seen no key;
+// every term is 0 then.
+template <bool kCausal>
+__device__ inline void sm_terms_rb(const f32x16_t (&s)[2], u32x4_t (&pfr)[4], float cs, float& ls, float scale) {
+  const float c0 = (kCausal && cs == -INFINITY) ? 0.0f : cs;
+#pragma unroll
+  for (int lb = 0; lb < 2; ++lb) {
+    float e[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      e[r] = fast_exp2(__builtin_fmaf(s[lb][r], scale, -c0));
+      ls += e[r];
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) pfr[2 * lb + c][q] = pack_bf16x2(e[8 * c + 2 * q], e[8 * c + 2 * q + 1]);
+  }
+}
+
 }  // namespace
 
 // kCausal (softmax only): key l is visible to row m iff l <= m + p.coff; the
@@ -173,7 +230,11 @@ void b2b_stream_kernel(B2bParams p) {
     // GEMM1 (S of the segment) and, for causal rows, the hiding of the keys a
     // row may not see (their extreme-side infinity drops out of the row
     // extreme and gives exp2(-inf) = 0)
+    // The MFMA blocks run at raised wave priority: the SIMD's other wave (of
+    // the CU's other workgroup) is then the one that waits while its softmax
+    // fills the issue slots the MFMAs leave free.
     auto gemm1 = [&]() {
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
@@ -195,6 +256,7 @@ void b2b_stream_kernel(B2bParams p) {
             sacc[rb][lb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bf),
                                                                     __builtin_bit_cast(bf16x8_t, af[rb][ks]), sacc[rb][lb], 0, 0, 0);
         }
+      __builtin_amdgcn_s_setprio(0);
       // register r of block lb holds l = lc*64 + lb*32 + 8(r>>2) + 4h + (r&3)
       if constexpr (kCausal) {
         if (lc * kTLC + kTLC - 1 > wrow0 + p.coff) {   // the segment crosses the diagonal for this wave
@@ -212,56 +274,10 @@ void b2b_stream_kernel(B2bParams p) {
       }
     };
     u32x4_t pf[MB][4];
-    // softmax, full form: row extreme of S (of alpha*S for the stabiliser: max
-    // for alpha >= 0, min otherwise), raise the integer stabiliser to cover it
-    // with an exact power-of-two rescale of what was accumulated, then the
-    // terms 2^(alpha*log2e*s - c), their row sum and the bf16 operand
-    auto softmax_full = [&](int rb) {
-      float mx;
-      if (scale >= 0.0f) {
-        mx = -INFINITY;
-#pragma unroll
-        for (int lb = 0; lb < 2; ++lb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[rb][lb][r]);
-        mx = max_halves(mx);
-      } else {
-        mx = INFINITY;
-#pragma unroll
-        for (int lb = 0; lb < 2; ++lb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fminf(mx, sacc[rb][lb][r]);
-        mx = min_halves(mx);
-      }
-      const float cn = fmaxf(cst[rb], ceilf(mx * scale));
-      if (cn > cst[rb] && cst[rb] != -INFINITY) {
-        const int sh = (int)(cst[rb] - cn);      // exact power-of-two rescale
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[rb][nb][r] = __builtin_amdgcn_ldexpf(oacc[rb][nb][r], sh);
-        lsum[rb] = __builtin_amdgcn_ldexpf(lsum[rb], sh);
-      }
-      cst[rb] = cn;
-    };
-    // the terms with the current stabiliser; -inf only while a causal row has
-    // seen no key, and then every term is 0
-    auto softmax_terms = [&](int rb) {
-      const float cs = (kCausal && cst[rb] == -INFINITY) ? 0.0f : cst[rb];
-#pragma unroll
-      for (int lb = 0; lb < 2; ++lb) {
-        float e[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          e[r] = fast_exp2(__builtin_fmaf(sacc[rb][lb][r], scale, -cs));
-          lsum[rb] += e[r];
-        }
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) pf[rb][2 * lb + c][q] = pack_bf16x2(e[8 * c + 2 * q], e[8 * c + 2 * q + 1]);
-      }
-    };
+    // softmax of row block rb: full form (row extreme, stabiliser raised with
+    // an exact rescale) and the terms with the current stabiliser
+    auto softmax_full = [&](int rb) { sm_full_rb<NB>(sacc[rb], oacc[rb], cst[rb], lsum[rb], scale); };
+    auto softmax_terms = [&](int rb) { sm_terms_rb<kCausal>(sacc[rb], pf[rb], cst[rb], lsum[rb], scale); };
     if constexpr (kSoftmax) {
       // Any integer stabiliser gives the same quotient (rounding commutes with
       // scaling by a power of two), so the row extreme is taken only while a
@@ -331,6 +347,7 @@ void b2b_stream_kernel(B2bParams p) {
       }
     }
     // GEMM2 over the four 16-wide slices of the segment
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -343,6 +360,7 @@ void b2b_stream_kernel(B2bParams p) {
           oacc[rb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf),
                                                                   __builtin_bit_cast(bf16x8_t, pf[rb][c]), oacc[rb][nb], 0, 0, 0);
       }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- B0/B1 shared by the batch and no longer than the ring: load once
@@ -493,6 +511,378 @@ void b2b_stream_kernel(B2bParams p) {
   }
 }
 
+// ---- ping-pong schedule (softmax, no mask, no bias; selected by cf_set_b2b_pingpong)
+//
+// The softmax of a segment is vector ALU work (an exp per score, slower to
+// issue than other vector instructions) about as long as the segment's MFMAs,
+// and one wave can only start it once its GEMM1 MFMAs have drained. Here a
+// workgroup
+// of eight waves runs as two groups of four, waves w and w + 4 sharing a SIMD,
+// and every wave alternates an MFMA phase (GEMM2 of the previous segment,
+// GEMM1 of this one) and a vector phase (the softmax terms). Group 1 runs one
+// phase behind group 0 and a workgroup barrier closes every phase, so on each
+// SIMD one wave feeds the matrix core while the other computes exponentials
+// (the alternating MFMA/vector wave groups of the method's ping-pong pipeline,
+// ComFuse review, "Assumptions & free parameters", Sec. III-C). One workgroup
+// fills a CU: 512 rows per tile (64 per wave); the tile's A rows sit in LDS
+// (in registers they spilled) beside the ring of B0/B1 segments, which both
+// groups share and which streams the segments of the workgroup's successive
+// tiles as one sequence.
+constexpr int kPWaves = 8;
+constexpr int kPThreads = 64 * kPWaves;
+
+template <int KS, int NB, bool kB0LK>
+__global__ __attribute__((amdgpu_flat_work_group_size(kPThreads, kPThreads), amdgpu_waves_per_eu(2, 2)))
+void b2b_pp_kernel(B2bParams p) {
+  constexpr int K = 16 * KS, N = 32 * NB;
+  constexpr int MB = 2, BM = kPWaves * MB * 32;
+  constexpr int kB0Bytes = kTLC * K * 2, kB1Bytes = kTLC * N * 2;
+  constexpr int kStage = kB0Bytes + kB1Bytes;
+  constexpr int kB0Blocks = kB0Bytes / 1024;
+  constexpr int kLoads = kStage / (kPThreads * 16);        // ring loads per thread per segment
+  static_assert(kLoads * kPThreads * 16 == kStage, "whole 1 KiB blocks per wave");
+  // LDS: the ring of NS segments, then the tile's A rows (K * 2 bytes each,
+  // 16-byte chunks XOR-swizzled by row like B0 given [L][K])
+  constexpr int kABytes = BM * K * 2;
+  constexpr int kAOff = 160 * 1024 - kABytes;
+  constexpr int NS = kAOff / kStage < 8 ? kAOff / kStage : 8;
+  static_assert(NS >= 4, "ring of at least four segments");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NS * kStage + kABytes];
+  constexpr int kA = NS * kStage;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int h = lane >> 5, r32 = lane & 31;
+  const int mtiles = (p.M + BM - 1) / BM;
+  const int nchunks = p.L / kTLC;
+  const float scale = p.alpha * kLog2e;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)smem;
+
+  // ring plan: load i of wave w fills 1 KiB block q = 8 i + w of a stage (B0
+  // blocks first); the global offsets are recomputed at every issue (a few
+  // integer instructions) rather than held in registers across the loop
+  auto ring_off = [&](int i, int s) -> uint32_t {
+    const int q = kPWaves * i + wave;
+    if (q < kB0Blocks) {
+      if constexpr (kB0LK) {
+        constexpr int cpr = K / 8, rpb = 1024 / (K * 2);
+        const int row = q * rpb + lane / cpr, ph = lane % cpr;
+        const int lg = ph ^ (K == 64 ? swz_rows128(row) : swz_rows256(row));
+        return ((uint32_t)(row + s * kTLC) * p.ldb0 + (uint32_t)(8 * lg)) * 2u;
+      } else {
+        const int row = q * 8 + lane / 8, ph = lane % 8;
+        const int lg = ph ^ swz_tr128(row);
+        return ((uint32_t)row * p.ldb0 + (uint32_t)(8 * lg + s * kTLC)) * 2u;
+      }
+    }
+    constexpr int cpr = N / 8, rpb = 1024 / (N * 2);
+    const int qb = q - kB0Blocks;
+    const int row = qb * rpb + lane / cpr, ph = lane % cpr;
+    const int lg = ph ^ (N == 64 ? swz_tr128(row) : swz_tr256(row));
+    return ((uint32_t)(row + s * kTLC) * p.ldb1 + (uint32_t)(8 * lg)) * 2u;
+  };
+  // segment s (ok: it exists) into ring buffer slot `slot`
+  auto issue = [&](int slot, int s, bool ok, const u32x4_t& rs0, const u32x4_t& rs1) {
+    const uint32_t sb = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds0 + (uint32_t)(slot * kStage)));
+    const uint32_t st = sb + (uint32_t)(wave * 1024);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i)
+      lds_dma16(st + i * kPWaves * 1024, kPWaves * i + wave < kB0Blocks ? rs0 : rs1, ok ? ring_off(i, s) : kOutOfRange);
+  };
+
+  // fragment read offsets within a stage (as in b2b_stream_kernel)
+  uint32_t b0_rd[kB0LK ? KS : 2];
+  if constexpr (kB0LK) {
+    constexpr int RB = K * 2;
+    const int f = K == 64 ? swz_rows128(r32) : swz_rows256(r32);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) b0_rd[ks] = (uint32_t)(r32 * RB + 16 * ((2 * ks + h) ^ f));
+  } else {
+    const int g = lane >> 4, i = lane & 15;
+    const int f = swz_tr128(i >> 2);
+    const int c = 2 * (g & 1) + ((i & 3) >> 1);
+#pragma unroll
+    for (int lb = 0; lb < 2; ++lb)
+      b0_rd[lb] = (uint32_t)((8 * (g >> 1) + (i >> 2)) * 128 + 16 * ((4 * lb + c) ^ f) + 8 * (i & 1));
+  }
+  uint32_t b1_rd[NB];
+  {
+    constexpr int RB = N * 2;
+    const int g = lane >> 4, i = lane & 15;
+    const int f = N == 64 ? swz_tr128(i >> 2) : swz_tr256(i >> 2);
+    const int c = 2 * (g & 1) + ((i & 3) >> 1);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      b1_rd[nb] = (uint32_t)(kB0Bytes + (4 * (g >> 1) + (i >> 2)) * RB + 16 * ((4 * nb + c) ^ f) + 8 * (i & 1));
+  }
+  // A fragment of row block rb, k step ks: row wave*64 + rb*32 + (lane & 31),
+  // 8 k from ks*16 + 8h
+  uint32_t a_rd[KS];
+  {
+    const int f = K == 64 ? swz_rows128(r32) : swz_rows256(r32);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      a_rd[ks] = (uint32_t)(kA + (wave * MB * 32 + r32) * K * 2 + 16 * ((2 * ks + h) ^ f));
+  }
+  auto afrag = [&](int rb, int ks) -> u32x4_t { return *(const u32x4_t*)(smem + a_rd[ks] + rb * 32 * K * 2); };
+  auto b0frag = [&](const uint8_t* st, int ks, int lb) -> u32x4_t {
+    if constexpr (kB0LK) {
+      return *(const u32x4_t*)(st + b0_rd[ks] + lb * 32 * K * 2);
+    } else {
+      const u32x2_t lo = lds_read_tr16(st + b0_rd[lb] + ks * 16 * 128);
+      const u32x2_t hi = lds_read_tr16(st + b0_rd[lb] + ks * 16 * 128 + 4 * 128);
+      return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+    }
+  };
+  auto b1frag = [&](const uint8_t* st, int c, int nb) -> u32x4_t {
+    const u32x2_t lo = lds_read_tr16(st + b1_rd[nb] + c * 16 * N * 2);
+    const u32x2_t hi = lds_read_tr16(st + b1_rd[nb] + c * 16 * N * 2 + 8 * N * 2);
+    return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+  };
+  auto mfma = [](const u32x4_t& b, const u32x4_t& a, const f32x16_t& acc) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, b),
+                                                    __builtin_bit_cast(bf16x8_t, a), acc, 0, 0, 0);
+  };
+
+  // ---- B0/B1 shared by the batch and no longer than the ring: load once
+  const bool shared = p.batch == 1 || (p.sb0 == 0 && p.sb1 == 0);
+  const bool resident = shared && nchunks <= NS;
+  if (resident) {
+    const u32x4_t rs0 = rsrc_words(p.B0, (uint32_t)((size_t)(kB0LK ? p.L : K) * p.ldb0 * 2));
+    const u32x4_t rs1 = rsrc_words(p.B1, (uint32_t)((size_t)p.L * p.ldb1 * 2));
+#pragma unroll
+    for (int s = 0; s < NS; ++s) issue(s, s, s < nchunks, rs0, rs1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+
+  // ---- tile schedule (as in b2b_stream_kernel)
+  const int G = (int)gridDim.x;
+  const bool by_xcd = !shared && mtiles > 1 && (p.batch & 7) == 0 && (G & 7) == 0;
+  const int x = (int)blockIdx.x & 7;
+  const int per_x = by_xcd ? (x < p.batch ? (p.batch - x + 7) / 8 : 0) * mtiles : p.batch * mtiles;
+  const int e0 = by_xcd ? (int)blockIdx.x >> 3 : (int)blockIdx.x;
+  const int estep = by_xcd ? G >> 3 : G;
+
+  const int ntiles = per_x > e0 ? (per_x - e0 + estep - 1) / estep : 0;   // tiles of this workgroup
+  const int nseg = nchunks;
+  auto tile_b = [&](int t) { const int e = e0 + t * estep; return by_xcd ? x + 8 * (e / mtiles) : e / mtiles; };
+  auto tile_m0 = [&](int t) { return (e0 + t * estep) % mtiles * BM; };
+  // The ring streams the segments of all this workgroup's tiles as one
+  // sequence: segment s of tile t is element t * nseg + s, in slot (t * nseg +
+  // s) % NS, so the next tile's first segments arrive during the current
+  // tile's last phases. (it, is): tile and segment of the next element to issue.
+  int it = 0, is = 0, gnext = 0;
+  auto issue_next = [&]() {
+    const bool ok = it < ntiles;
+    const int b = ok ? tile_b(it) : 0;
+    const u32x4_t rs0 = rsrc_words((const uint16_t*)p.B0 + (size_t)b * p.sb0,
+                                   (uint32_t)((size_t)(kB0LK ? p.L : K) * p.ldb0 * 2));
+    const u32x4_t rs1 = rsrc_words((const uint16_t*)p.B1 + (size_t)b * p.sb1, (uint32_t)((size_t)p.L * p.ldb1 * 2));
+    issue(gnext % NS, is, ok, rs0, rs1);
+    ++gnext;
+    if (++is == nseg) { is = 0; ++it; }
+  };
+  // this wave's MB*32 rows of A of tile t into LDS, 1 KiB (K == 64: 8 rows)
+  // per load; rows past M read as zero
+  auto load_a = [&](int t) {
+    const uint16_t* Ab = (const uint16_t*)p.A + (size_t)tile_b(t) * p.sa;
+    const int m0 = tile_m0(t);
+    const u32x4_t rsAw = rsrc_words(Ab, (uint32_t)((size_t)p.M * p.lda * 2));
+    constexpr int cpr = K / 8, rpl = 64 / cpr, nld = MB * 32 / rpl;
+    const uint32_t ab = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds0 + kA + wave * MB * 32 * K * 2));
+#pragma unroll
+    for (int i = 0; i < nld; ++i) {
+      const int rl = i * rpl + lane / cpr, ph = lane % cpr;   // row within the wave's rows
+      const int lg = ph ^ (K == 64 ? swz_rows128(rl) : swz_rows256(rl));
+      const int row = m0 + wave * MB * 32 + rl;
+      lds_dma16(ab + i * 1024, rsAw, row < p.M ? ((uint32_t)row * p.lda + (uint32_t)(8 * lg)) * 2u : kOutOfRange);
+    }
+  };
+  if (ntiles > 0) {
+    if (!resident) {
+      for (int s = 0; s < NS - 2; ++s) issue_next();
+    }
+    load_a(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int b = tile_b(t);
+    const int m0 = tile_m0(t);
+    const int sbase = resident ? 0 : t * nseg;   // ring element of the tile's segment 0
+    f32x16_t oacc[MB][NB];
+    f32x16_t sacc[MB][2];
+    u32x4_t pf[MB][4];
+    float cst[MB], lsum[MB];
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) oacc[rb][nb] = f32x16_t{0};
+      cst[rb] = -INFINITY;
+      lsum[rb] = 0.0f;
+    }
+
+    // Phases: group 0 runs GEMM1(0), softmax(0), GEMM2(0)+GEMM1(1), ...,
+    // softmax(nseg-1), GEMM2(nseg-1) in phases 0 .. 2 nseg, group 1 the same
+    // one phase later; a workgroup barrier opens every phase (2 nseg + 2 of
+    // them, each wave passes all). Stage s is read in phases 2s .. 2s + 3, so
+    // at the start of phase 2i (i >= 0) segment i has to be in and the stage
+    // of segment i - 2 is refilled with segment i + NS - 2.
+    auto phase = [&](int k) {
+      asm volatile("" ::: "memory");
+      if (!resident && (k & 1) == 0 && k < 2 * nseg) {
+        wait_vm_lgkm0<(NS - 3) * kLoads>();   // segment k / 2 landed in this wave's share
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        issue_next();                         // element sbase + k / 2 + NS - 2
+      } else {
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      }
+    };
+    // The MFMA phase: GEMM2 of segment j2 (if j2 >= 0) and GEMM1 of segment j1
+    // (if j1 >= 0), at raised wave priority. The B1 fragments are read first;
+    // each GEMM2 MFMA is then followed by one of GEMM1's LDS reads, so that
+    // GEMM1's operands are in when its MFMAs start.
+    auto mphase = [&](int j2, int j1) {
+      __builtin_amdgcn_s_setprio(1);
+      u32x4_t vf[4][NB], bf[KS][2], fa[MB][KS];
+      if (j2 >= 0) {
+        const uint8_t* st = smem + ((sbase + j2) % NS) * kStage;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) vf[c][nb] = b1frag(st, c, nb);
+      }
+      if (j1 >= 0) {
+        const uint8_t* st = smem + ((sbase + j1) % NS) * kStage;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+          for (int lb = 0; lb < 2; ++lb) bf[ks][lb] = b0frag(st, ks, lb);
+#pragma unroll
+          for (int rb = 0; rb < MB; ++rb) fa[rb][ks] = afrag(rb, ks);
+        }
+      }
+      if (j2 >= 0) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int rb = 0; rb < MB; ++rb) oacc[rb][nb] = mfma(vf[c][nb], pf[rb][c], oacc[rb][nb]);
+      }
+      if (j1 >= 0) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int lb = 0; lb < 2; ++lb)
+#pragma unroll
+            for (int rb = 0; rb < MB; ++rb)
+              sacc[rb][lb] = mfma(bf[ks][lb], fa[rb][ks], ks == 0 ? f32x16_t{0} : sacc[rb][lb]);
+      }
+      if (j2 >= 0 && j1 >= 0) {
+        // 16 LDS reads (B1), then 16 x (GEMM2 MFMA, one GEMM1 read), then GEMM1
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+    };
+    // softmax of a segment: the row extreme only while a row has no
+    // stabiliser yet, or when the segment's terms add up past 2^32 (the block
+    // is then redone with it; S is still in registers)
+    auto softmax = [&]() {
+      bool fresh = false;
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb) fresh |= cst[rb] == -INFINITY;
+      const bool full = __builtin_amdgcn_ballot_w64(fresh) != 0;
+      float lprev[MB];
+      bool big = false;
+#pragma unroll
+      for (int rb = 0; rb < MB; ++rb) {
+        if (full) sm_full_rb<NB>(sacc[rb], oacc[rb], cst[rb], lsum[rb], scale);
+        lprev[rb] = lsum[rb];
+        sm_terms_rb<false>(sacc[rb], pf[rb], cst[rb], lsum[rb], scale);
+        big |= !(lsum[rb] - lprev[rb] <= 0x1p32f);
+      }
+      if (!full && __builtin_amdgcn_ballot_w64(big) != 0) {
+#pragma unroll
+        for (int rb = 0; rb < MB; ++rb) {
+          lsum[rb] = lprev[rb];
+          sm_full_rb<NB>(sacc[rb], oacc[rb], cst[rb], lsum[rb], scale);
+          sm_terms_rb<false>(sacc[rb], pf[rb], cst[rb], lsum[rb], scale);
+        }
+      }
+    };
+    if (grp == 1) phase(0);
+    phase(grp);
+    mphase(-1, 0);
+    for (int j = 1; j < nseg; ++j) {
+      phase(2 * j - 1 + grp);
+      softmax();
+      phase(2 * j + grp);
+      mphase(j - 1, j);
+    }
+    phase(2 * nseg - 1 + grp);
+    if (t + 1 < ntiles) load_a(t + 1);   // this wave's last GEMM1 of the tile is done
+    softmax();
+    phase(2 * nseg + grp);
+    mphase(nseg - 1, -1);
+    if (grp == 0) phase(2 * nseg + 1);
+
+    // ---- normalise and store: oacc[rb][nb][4q + e] is O[m][nb*32 + 8q + 4h + e]
+    const uint32_t es = p.out_f32 ? 4u : 2u;
+    const __amdgpu_buffer_rsrc_t rsO = make_rsrc((uint8_t*)p.O + (size_t)b * p.so * es,
+                                                 (uint32_t)((size_t)p.M * p.ldo * es));
+#pragma unroll
+    for (int rb = 0; rb < MB; ++rb) {
+      const uint32_t row = (uint32_t)(m0 + (wave * MB + rb) * 32 + r32);
+      const float ls = sum_halves(lsum[rb]);
+      const float inv = ls > 0.0f ? 1.0f / ls : 0.0f;
+      if (p.row_stats != nullptr && h == 0 && row < (uint32_t)p.M)
+        p.row_stats[(size_t)b * p.M + row] = ls > 0.0f ? (cst[rb] + log2f(ls)) * kLn2 : -INFINITY;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = nb * 32 + 8 * q + 4 * h;
+          float y[4];
+#pragma unroll
+          for (int ee = 0; ee < 4; ++ee) y[ee] = oacc[rb][nb][4 * q + ee] * inv;
+          if (p.out_f32) {
+            if (p.o_vec) {
+              const u32x4_t v = {__float_as_uint(y[0]), __float_as_uint(y[1]), __float_as_uint(y[2]), __float_as_uint(y[3])};
+              buf_store_b128(v, rsO, (row * p.ldo + (uint32_t)n) * 4);
+            } else {
+#pragma unroll
+              for (int ee = 0; ee < 4; ++ee) buf_store_b32(__float_as_uint(y[ee]), rsO, (row * p.ldo + (uint32_t)(n + ee)) * 4);
+            }
+          } else {
+            if (p.o_vec) {
+              const u32x2_t v = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+              buf_store_b64(v, rsO, (row * p.ldo + (uint32_t)n) * 2);
+            } else {
+#pragma unroll
+              for (int ee = 0; ee < 4; ++ee) buf_store_b16((uint16_t)f32_to_bf16(y[ee]), rsO, (row * p.ldo + (uint32_t)(n + ee)) * 2);
+            }
+          }
+        }
+    }
+    // the next tile's A rows in (its first phase's barrier follows)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+}
+
 // ---- dispatch
 namespace {
 template <bool kSoftmax, bool kB0LK, bool kCausal = false, int kBias = 0>
@@ -507,10 +897,19 @@ const void* pick_stream_kn(int K, int N, bool two_blocks) {
 }
 }  // namespace
 
-const void* b2b_stream_pick(const B2bParams& p, int cus, int* rows_per_tile) {
+const void* b2b_stream_pick(const B2bParams& p, int cus, int* rows_per_tile, int* threads) {
   if (p.L % kTLC != 0 || p.L < kTLC) return nullptr;
   // a bias the ring loads cannot read takes the general kernel
   if (p.bias && !p.bias_vec) return nullptr;
+  if (threads) *threads = kTThreads;
+  // the ping-pong schedule (when selected): softmax without mask, K = N = 64,
+  // and 512-row tiles enough for one workgroup on every CU
+  if (p.pingpong && p.row_op == 1 && !p.causal && !p.bias && p.K == 64 && p.N == 64 &&
+      (long)p.batch * ((p.M + 511) / 512) >= cus) {
+    if (rows_per_tile) *rows_per_tile = 512;
+    if (threads) *threads = kPThreads;
+    return p.b0_lk ? (const void*)&b2b_pp_kernel<4, 2, true> : (const void*)&b2b_pp_kernel<4, 2, false>;
+  }
   // 256-row tiles only when they still give every CU two workgroups (and
   // not with a bias, whose registers they have no room for)
   const bool two = !p.bias && p.K == 64 && p.N == 64 && (long)p.batch * ((p.M + 255) / 256) >= 2L * cus;

@@ -93,12 +93,14 @@ struct B2bParams {
   int causal;    // softmax only: key l visible to row m iff l <= m + coff
   int coff;      // L - M
   float* row_stats;   // softmax only, optional: log-sum-exp of each row, [batch][M]
+  int pingpong;        // softmax: the ping-pong schedule where it applies (cf_set_b2b_pingpong)
 };
 
 hipError_t launch_b2b(const B2bParams& p, hipStream_t stream);
 // Streamed kernel for exact shapes (K, N in {64, 128}, L a multiple of 64), or
-// null; *rows_per_tile receives its tile height.
-const void* b2b_stream_pick(const B2bParams& p, int cus, int* rows_per_tile);
+// null; *rows_per_tile receives its tile height and *threads its workgroup
+// size.
+const void* b2b_stream_pick(const B2bParams& p, int cus, int* rows_per_tile, int* threads);
 // Returns false when (K, N, row_op, ...) has no kernel instantiation.
 bool b2b_supported(const B2bParams& p);
 

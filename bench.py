@@ -83,6 +83,9 @@ def parse():
                          "algorithmic flops count only the visible (query, key) pairs")
     ap.add_argument("--dims", default="",
                     help="diagnostic: override workload dims, e.g. M=2048,N=16384 (the line then names them)")
+    ap.add_argument("--pingpong", action="store_true",
+                    help="attention workload: the ping-pong schedule of the softmax B2BGEMM "
+                         "(cf_set_b2b_pingpong; two wave groups per CU alternating MFMA and softmax phases)")
     ap.add_argument("--leader-tiles", type=int, default=-1, metavar="T",
                     help="strips of at least T column tiles exchange leader-follower (0: never; default: the "
                          "library's setting)")
@@ -427,6 +430,8 @@ def main():
     w = gen.workload(args.workload, **dims)
     if args.leader_tiles >= 0:
         cf.cf_set_exchange_leader_tiles(args.leader_tiles)
+    if args.pingpong:
+        cf.cf_set_b2b_pingpong(1)
     if args.store_x and w.kind != "gemm_epilogue":
         raise SystemExit("--store-x applies to the GEMM + epilogue workloads")
     if args.row2 and (w.kind != "gemm_epilogue" or args.argmax or w.params["row_op"] == "none"):
@@ -556,6 +561,7 @@ def main():
                      "arithmetic_intensity": round(intensity, 1), "ridge": round(ridge, 1)},
         "kernel_ms": round(kernel_ms, 4),
         "exchange_leader_tiles": cf.cf_set_exchange_leader_tiles(-1),
+        "b2b_pingpong": cf.cf_set_b2b_pingpong(-1),
         "algorithmic_bytes": bytes_of(w, args.store_x, args.argmax, args.topk),
         "intermediate_hbm_bytes": intermediate,
         "output_bytes": out_bytes,

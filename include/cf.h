@@ -317,6 +317,21 @@ uint64_t cf_set_exchange_timeout_us(uint64_t us);
  * stage and top-k keep their own schemes). */
 int cf_set_exchange_leader_tiles(int min_tiles);
 
+/* Schedule of cf_b2bgemm's softmax (ComFuse review, "Assumptions & free
+ * parameters": the Sec. III-C PingPong pipeline, two groups alternating
+ * tensor-core and CUDA-core work). on = 1 selects, where it applies (row_op
+ * CF_ROW_SOFTMAX without mask, K = N = 64, at least one 512-row tile per CU),
+ * a workgroup of eight waves per CU whose two groups of four alternate an
+ * MFMA phase and a softmax phase, a workgroup barrier between phases, with the
+ * A rows and the B0/B1 segments in LDS. on = 0 (the default) keeps two
+ * independent four-wave workgroups per CU whose MFMA blocks run at raised
+ * wave priority. Both give the same results up to the order of the row-sum
+ * additions. On MI355X at batch 512, M = L = 1024, the ping-pong schedule
+ * measured no faster (each phase waits at the barrier for the slowest of eight
+ * waves, and the softmax phase alone takes about as long as both MFMA GEMMs).
+ * A negative value changes nothing. Returns the previous value. Process-wide. */
+int cf_set_b2b_pingpong(int on);
+
 #ifdef __cplusplus
 }
 #endif

@@ -400,3 +400,78 @@ def test_attention_logsumexp(M, L, causal):
     P.assert_close(got[fin], R[fin], 1e-5, 1e-4, f"attention log-sum-exp {M}x{L} causal={causal}")
     Ro = oracle.b2bgemm(ref["A"], ref["B0"], ref["B1"], alpha=0.125, row_op="softmax", b0_layout="lk", causal=causal)
     P.assert_close(P.gpu_to_f64(O), Ro, P.REL_F_BF16, P.MAX_ABS_BF16, "output unchanged by storing the statistics")
+
+
+# ---------------------------------------------------------------------------- ping-pong schedule
+# With cf_set_b2b_pingpong(1), the softmax without mask and bias at K = N = 64
+# runs with 512-row tiles, two groups of four waves alternating MFMA and
+# softmax phases, once there are at least as many 512-row tiles as CUs
+# (batch * ceil(M / 512) >= 256 on MI355X).
+
+@pytest.fixture
+def pingpong():
+    old = cf.cf_set_b2b_pingpong(1)
+    yield
+    cf.cf_set_b2b_pingpong(old)
+
+
+def pp_inputs(seed, batch, M, L, lk=True, scale_a=1.0):
+    w, dev, ref = P.inputs("c5_b2b_attention", seed=seed, batch=batch, M=M, L=L)
+    if scale_a != 1.0:
+        dev["A"] = (dev["A"].float() * scale_a).to(torch.bfloat16)
+        ref["A"] = P.gpu_to_f64(dev["A"])
+    dev["B1"] = (dev["B1"].float() / np.sqrt(L / 64)).to(torch.bfloat16)
+    ref["B1"] = P.gpu_to_f64(dev["B1"])
+    if not lk:
+        dev["B0"] = dev["B0"].transpose(1, 2).contiguous()
+        ref["B0"] = np.ascontiguousarray(np.swapaxes(ref["B0"], 1, 2))
+    return dev, ref
+
+
+@pytest.mark.parametrize("lk", [True, False])
+@pytest.mark.parametrize("M,L", [(100, 64), (100, 192), (37, 448), (512, 128), (600, 320)])
+def test_ping_pong_per_head(pingpong, lk, M, L):
+    # ragged 512-row tiles; one segment, several, and more than the ring holds;
+    # a workgroup's tiles stream through the ring back to back
+    batch = 256 if M <= 512 else 128
+    dev, ref = pp_inputs(20, batch, M, L, lk)
+    check(dev, ref, lk=lk, alpha=0.125, row_op="softmax", what=f"ping-pong {batch}x{M}x{L} lk={lk}")
+
+
+@pytest.mark.parametrize("L", [320, 640])
+def test_ping_pong_shared_weights(pingpong, L):
+    # 2-D B0/B1 shared by the batch: L = 320 stays resident in LDS, L = 640 streams
+    batch, M = 256, 96
+    dev, ref = pp_inputs(21, batch, M, L)
+    R = oracle.b2bgemm(ref["A"], ref["B0"][0], ref["B1"][0], alpha=0.125, row_op="softmax", b0_layout="lk")
+    O = run(dev["A"], dev["B0"][0], dev["B1"][0], torch.float32, b0_is_lk=True, alpha=0.125, row_op="softmax")
+    P.assert_close(P.gpu_to_f64(O), R, P.REL_F_BF16, P.MAX_ABS_BF16, f"ping-pong shared weights L={L}")
+
+
+@pytest.mark.parametrize("alpha", [0.125, -0.125])
+def test_ping_pong_large_logits_and_logsumexp(pingpong, alpha):
+    # logits of several hundred: the stabiliser is raised within the stream
+    # (the redo of a segment whose terms pass 2^32), either sign of alpha
+    batch, M, L = 256, 64, 384
+    dev, ref = pp_inputs(22, batch, M, L, scale_a=6.0)
+    lse = torch.full((batch, M), float("nan"), dtype=torch.float32, device="cuda")
+    O = run(dev["A"], dev["B0"], dev["B1"], torch.float32, b0_is_lk=True, alpha=alpha, row_op="softmax",
+            row_stats=lse)
+    R = oracle.b2bgemm(ref["A"], ref["B0"], ref["B1"], alpha=alpha, row_op="softmax", b0_layout="lk")
+    P.assert_close(P.gpu_to_f64(O), R, P.REL_F_BF16, P.MAX_ABS_BF16, f"ping-pong x6 logits alpha={alpha}")
+    Rl = oracle.b2b_logsumexp(ref["A"], ref["B0"], alpha=alpha, b0_layout="lk")
+    P.assert_close(P.gpu_to_f64(lse), Rl, 1e-5, 1e-4, f"ping-pong log-sum-exp alpha={alpha}")
+
+
+def test_ping_pong_full_size_all_heads(pingpong):
+    # the attention workload (batch 32 x 16 heads, M = L = 1024) on the ping-pong
+    # schedule, every row against the oracle, and against the default schedule
+    w, dev, ref = P.inputs("c5_b2b_attention", seed=0)
+    O = run(dev["A"], dev["B0"], dev["B1"], torch.float32, b0_is_lk=True, alpha=0.125, row_op="softmax")
+    R = oracle_heads(ref, alpha=0.125, row_op="softmax", b0_layout="lk")
+    r, m = P.assert_close(P.gpu_to_f64(O), R, P.REL_F_BF16, P.MAX_ABS_BF16, "C5 ping-pong, all heads")
+    cf.cf_set_b2b_pingpong(0)
+    O0 = run(dev["A"], dev["B0"], dev["B1"], torch.float32, b0_is_lk=True, alpha=0.125, row_op="softmax")
+    d = float((O - O0).abs().max())
+    assert d <= 1e-5, f"schedules differ by {d:.2e} (only the row-sum order may differ)"
+    print(f"C5 ping-pong full: relF {r:.2e} maxabs {m:.2e}; max |pp - default| {d:.1e}", flush=True)

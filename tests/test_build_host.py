@@ -86,3 +86,24 @@ def test_hash_does_not_depend_on_the_tree_path(tmp_path):
     a = load_builder(clean_copy(tmp_path / "one"))
     b = load_builder(clean_copy(tmp_path / "two" / "deeper"))
     assert a.source_hash() == b.source_hash()
+
+
+def test_unit_stamps_follow_their_own_source_and_the_headers(tmp_path):
+    repo = clean_copy(tmp_path)
+    bl = load_builder(repo)
+    us = bl.units()
+    before = {obj: bl._unit_hash(src, defs) for src, obj, defs in us}
+    # the same unit at another path has the same stamp
+    other = load_builder(clean_copy(tmp_path / "elsewhere"))
+    assert [other._unit_hash(s, d) for s, _, d in other.units()] == list(before.values())
+    # one translation unit edited: its objects alone go stale
+    with open(os.path.join(bl.CSRC, "b2b_stream.hip"), "a") as f:
+        f.write("\n// edited\n")
+    after = {obj: bl._unit_hash(src, defs) for src, obj, defs in us}
+    stale = {os.path.basename(o) for o in before if before[o] != after[o]}
+    assert stale == {"b2b_stream.o"}
+    # a header edited: every object goes stale
+    with open(os.path.join(bl.INCLUDE, "cf.h"), "a") as f:
+        f.write("\n// edited\n")
+    again = {obj: bl._unit_hash(src, defs) for src, obj, defs in us}
+    assert all(again[o] != after[o] for o in after)

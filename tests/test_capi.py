@@ -58,6 +58,12 @@ def test_status_strings_and_version():
     assert "gfx950" in cf.cf_version()
     old = cf.cf_set_exchange_timeout_us(1234)
     assert cf.cf_set_exchange_timeout_us(old) == 1234
+    assert cf.cf_set_exchange_leader_tiles(-1) == cf.cf_set_exchange_leader_tiles(-1)
+    prev = cf.cf_set_b2b_pingpong(1)
+    assert prev == 0   # off unless selected
+    assert cf.cf_set_b2b_pingpong(-1) == 1   # a negative value only reads it
+    assert cf.cf_set_b2b_pingpong(prev) == 1
+    assert cf.cf_set_b2b_pingpong(-1) == 0
 
 
 def gemm(M=64, N=64, K=64, A=PA, lda=64, B=PB, ldb=64, nk=0, abt=1, C=PC, ldc=64, ct=1, epi=None, ws=None,

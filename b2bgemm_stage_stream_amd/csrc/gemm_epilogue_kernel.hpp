@@ -1558,6 +1558,12 @@ void gemm_epilogue_kernel(GemmEpilogueParams p) {
       }
     }
     if (!streamed) {
+    // the register-staged loop's lane offsets also come from the per-tile
+    // copy, so that they are not computed once before the tile loop and kept
+    // (spilled) through the streamed path
+    const int tid = tid_t, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int h = lane >> 5, r32 = lane & 31;
     u32x4_t ra[8], rb[8];
     // per-thread byte offsets at k = 0 and the per-k-tile steps
     const uint32_t a_off0 = ((uint32_t)(m0 + (tid >> 3)) * p.lda + (uint32_t)((tid & 7) * In<kF32>::kChunk)) * S;

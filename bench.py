@@ -83,6 +83,11 @@ def parse():
                          "algorithmic flops count only the visible (query, key) pairs")
     ap.add_argument("--dims", default="",
                     help="diagnostic: override workload dims, e.g. M=2048,N=16384 (the line then names them)")
+    ap.add_argument("--column", action="store_true",
+                    help="GEMM + epilogue workloads: the row operation over the rows of each column instead "
+                         "(cf_epilogue.axis = column; the complementary strip exchange)")
+    ap.add_argument("--row-stats", action="store_true",
+                    help="GEMM + epilogue workloads: also store the reduction's per-row (per-column) statistics")
     ap.add_argument("--pingpong", action="store_true",
                     help="attention workload: the ping-pong schedule of the softmax B2BGEMM "
                          "(cf_set_b2b_pingpong; two wave groups per CU alternating MFMA and softmax phases)")
@@ -249,7 +254,7 @@ def roofline_of(w, kernel_ms: float, store_x: bool = False, causal: bool = False
 
 
 def make_call(w, dev, torch, cf, store_x: bool = False, causal: bool = False, argmax: bool = False, row2=None,
-              topk: int = 0, b_nk: bool = False):
+              topk: int = 0, b_nk: bool = False, column: bool = False, row_stats: bool = False):
     """Device tensors + a closure launching one fused kernel on the current stream."""
     p = w.params
     out_dt = torch.float32 if p.get("out_dtype") == "f32" else torch.bfloat16
@@ -270,11 +275,14 @@ def make_call(w, dev, torch, cf, store_x: bool = False, causal: bool = False, ar
                                  act=p["act"], row_op="argmax", row_index=idx, row_stats=mx, x_out=X)
             C = None
         else:
-            idx = mx = None
+            idx = None
             g = dev.get("gamma", dev.get("weight"))
+            per = (d["N"] if column else d["M"]) * (2 if p["row_op"] == "layernorm" else 1)
+            mx = torch.empty(per, dtype=torch.float32, device="cuda") if row_stats else None
             e = cf.make_epilogue(alpha=p["alpha"], bias=dev.get("bias"), residual=dev.get("residual"),
                                  act=p["act"], row_op=p["row_op"], gamma=g, beta=dev.get("beta"),
-                                 eps=p.get("eps", 0.0), x_out=X, row_op2=row2 or "none",
+                                 eps=p.get("eps", 0.0), x_out=X, row_op2=row2 or "none", row_stats=mx,
+                                 axis="column" if column else "row",
                                  gamma2=g if row2 in ("layernorm", "rmsnorm") else None,
                                  beta2=dev.get("beta") if row2 == "layernorm" else None,
                                  eps2=p.get("eps", 0.0) if row2 else 0.0)
@@ -439,6 +447,9 @@ def main():
     if args.topk and (w.kind != "gemm_epilogue" or "residual" in {t.name for t in w.tensors} or args.argmax
                       or args.row2 or not 1 <= args.topk <= 8):
         raise SystemExit("--topk K (1..8) applies to the GEMM + epilogue workloads without a residual, alone")
+    if (args.column or args.row_stats) and (w.kind != "gemm_epilogue" or args.argmax or args.topk or args.row2
+                                            or w.params["row_op"] == "none"):
+        raise SystemExit("--column and --row-stats apply to the GEMM + epilogue workloads' own row operation")
     if args.argmax and w.kind != "gemm_epilogue":
         raise SystemExit("--argmax applies to the GEMM + epilogue workloads")
     if args.b_nk and w.kind != "gemm_epilogue":
@@ -465,7 +476,7 @@ def main():
     calls = []
     for d_ in devs:
         call, out, ws, ws_bytes = make_call(w, d_, torch, cf, args.store_x, args.causal, args.argmax, args.row2,
-                                            args.topk, args.b_nk)
+                                            args.topk, args.b_nk, args.column, args.row_stats)
         calls.append(call)
 
     # settle: batches of calls (grown to ~20 ms each) until --settle-s has passed
@@ -526,7 +537,7 @@ def main():
     traffic = intermediate = None
     out_bytes = output_bytes(w, args.store_x, args.argmax, args.topk)
     if os.path.exists(args.traffic) and not (args.plain or args.store_x or args.causal or args.argmax or args.row2
-                                             or args.topk or args.b_nk or args.dims):
+                                             or args.topk or args.b_nk or args.dims or args.column or args.row_stats):
         try:
             rec = json.load(open(args.traffic))
             if rec.get("kernel_source_hash") == kernel_source_hash():
@@ -554,6 +565,7 @@ def main():
         "config": {"workload": w.name + (f"@{args.dims}" if args.dims else "") + ("/identity-epilogue" if args.plain else "")
                    + ("+x_out" if args.store_x else "") + ("/causal" if args.causal else "")
                    + ("/argmax" if args.argmax else "") + (f"/then-{args.row2}" if args.row2 else "")
+                   + ("/over-columns" if args.column else "") + ("/row-stats" if args.row_stats else "")
                    + (f"/top-{args.topk}" if args.topk else "") + ("/B[N,K]" if args.b_nk else ""), **w.dims,
                    "out_dtype": w.params.get("out_dtype"), "input_sets": nset, "input_bytes_per_set": in_bytes},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,

@@ -88,6 +88,9 @@ def parse():
                          "(cf_epilogue.axis = column; the complementary strip exchange)")
     ap.add_argument("--row-stats", action="store_true",
                     help="GEMM + epilogue workloads: also store the reduction's per-row (per-column) statistics")
+    ap.add_argument("--via-fuse", action="store_true",
+                    help="time the workload written as a torch function and lowered by fuse.lower onto one fused "
+                         "call (the front-end's path) instead of the direct call")
     ap.add_argument("--pingpong", action="store_true",
                     help="attention workload: the ping-pong schedule of the softmax B2BGEMM "
                          "(cf_set_b2b_pingpong; two wave groups per CU alternating MFMA and softmax phases)")
@@ -251,6 +254,42 @@ def roofline_of(w, kernel_ms: float, store_x: bool = False, causal: bool = False
     if intensity < ridge:
         return "hbm", "GB/s", HBM_GBPS, nbytes / (kernel_ms * 1e-3) / 1e9, intensity, ridge
     return "mfma", "TFLOP/s", peak_flops, flops / (kernel_ms * 1e-3) / 1e12, intensity, ridge
+
+
+def fuse_call(w, dev, torch):
+    """The workload as a torch function, lowered by fuse.lower; a closure running the lowered call."""
+    import torch.nn.functional as F
+    from b2bgemm_stage_stream_amd import fuse
+    p, d = w.params, w.dims
+    if w.name == "c2_gemm_layernorm":
+        n, eps = d["N"], p["eps"]
+
+        def fn(a, b, g, be):
+            return F.layer_norm(a @ b, (n,), g, be, eps)
+        args = (dev["A"], dev["B"], dev["gamma"], dev["beta"])
+    elif w.name == "c3_gemm_residual_rmsnorm":
+        n, eps = d["N"], p["eps"]
+
+        def fn(a, b, r, g):
+            return F.rms_norm(a @ b + r, (n,), g, eps)
+        args = (dev["A"], dev["B"], dev["residual"], dev["weight"])
+    elif w.name == "c4_b2b_mlp_relu":
+        def fn(x, w0, w1):
+            return torch.relu(x @ w0) @ w1
+        args = (dev["A"], dev["B0"], dev["B1"])
+    elif w.name == "c5_b2b_attention":
+        alpha = p["alpha"]
+
+        def fn(q, k, v):
+            return torch.softmax((q @ k.transpose(-1, -2)) * alpha, dim=-1) @ v
+        args = (dev["A"], dev["B0"], dev["B1"])
+    else:
+        raise SystemExit(f"--via-fuse: no torch form of {w.name}")
+    run = fuse.lower(fn, *args)
+
+    def call():
+        call.last = run(*args)
+    return call
 
 
 def make_call(w, dev, torch, cf, store_x: bool = False, causal: bool = False, argmax: bool = False, row2=None,
@@ -447,6 +486,9 @@ def main():
     if args.topk and (w.kind != "gemm_epilogue" or "residual" in {t.name for t in w.tensors} or args.argmax
                       or args.row2 or not 1 <= args.topk <= 8):
         raise SystemExit("--topk K (1..8) applies to the GEMM + epilogue workloads without a residual, alone")
+    if args.via_fuse and (args.store_x or args.causal or args.argmax or args.row2 or args.topk or args.b_nk
+                          or args.column or args.row_stats or args.plain or args.dims):
+        raise SystemExit("--via-fuse times the workload as it is, with no other variant flag")
     if (args.column or args.row_stats) and (w.kind != "gemm_epilogue" or args.argmax or args.topk or args.row2
                                             or w.params["row_op"] == "none"):
         raise SystemExit("--column and --row-stats apply to the GEMM + epilogue workloads' own row operation")
@@ -475,8 +517,11 @@ def main():
     devs = [dev] + [{k: v.clone() for k, v in dev.items()} for _ in range(nset - 1)]
     calls = []
     for d_ in devs:
-        call, out, ws, ws_bytes = make_call(w, d_, torch, cf, args.store_x, args.causal, args.argmax, args.row2,
-                                            args.topk, args.b_nk, args.column, args.row_stats)
+        if args.via_fuse:
+            call, ws, ws_bytes = fuse_call(w, d_, torch), None, 0
+        else:
+            call, out, ws, ws_bytes = make_call(w, d_, torch, cf, args.store_x, args.causal, args.argmax, args.row2,
+                                                args.topk, args.b_nk, args.column, args.row_stats)
         calls.append(call)
 
     # settle: batches of calls (grown to ~20 ms each) until --settle-s has passed
@@ -537,7 +582,8 @@ def main():
     traffic = intermediate = None
     out_bytes = output_bytes(w, args.store_x, args.argmax, args.topk)
     if os.path.exists(args.traffic) and not (args.plain or args.store_x or args.causal or args.argmax or args.row2
-                                             or args.topk or args.b_nk or args.dims or args.column or args.row_stats):
+                                             or args.topk or args.b_nk or args.dims or args.column or args.row_stats
+                                             or args.via_fuse):
         try:
             rec = json.load(open(args.traffic))
             if rec.get("kernel_source_hash") == kernel_source_hash():
@@ -566,6 +612,7 @@ def main():
                    + ("+x_out" if args.store_x else "") + ("/causal" if args.causal else "")
                    + ("/argmax" if args.argmax else "") + (f"/then-{args.row2}" if args.row2 else "")
                    + ("/over-columns" if args.column else "") + ("/row-stats" if args.row_stats else "")
+                   + ("/via-fuse" if args.via_fuse else "")
                    + (f"/top-{args.topk}" if args.topk else "") + ("/B[N,K]" if args.b_nk else ""), **w.dims,
                    "out_dtype": w.params.get("out_dtype"), "input_sets": nset, "input_bytes_per_set": in_bytes},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,

@@ -578,7 +578,8 @@ def main():
     # HBM-side bytes per launch from the byte counters, when they were taken on
     # these kernel sources and this exact workload; the unfused intermediate's
     # share is what the kernel writes beyond its output and the exchange
-    # workspace
+    # workspace (0 when the writes come to less: workspace lines still held in
+    # the caches when the counters were read)
     traffic = intermediate = None
     out_bytes = output_bytes(w, args.store_x, args.argmax, args.topk)
     if os.path.exists(args.traffic) and not (args.plain or args.store_x or args.causal or args.argmax or args.row2
@@ -590,7 +591,7 @@ def main():
                 t = rec.get("workloads", {}).get(args.workload)
                 if t:
                     traffic = round(t["fetch_bytes"] + t["write_bytes"])
-                    intermediate = round(t["write_bytes"] - out_bytes - (ws_bytes or 0))
+                    intermediate = max(0, round(t["write_bytes"] - out_bytes - (ws_bytes or 0)))
         except (OSError, ValueError, KeyError):
             traffic = intermediate = None
     line = {

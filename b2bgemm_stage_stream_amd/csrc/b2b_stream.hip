@@ -366,6 +366,162 @@ void b2b_stream_kernel(B2bParams p) {
   // ---- B0/B1 shared by the batch and no longer than the ring: load once
   const bool shared = p.batch == 1 || (p.sb0 == 0 && p.sb1 == 0);
   const bool resident = shared && nchunks <= NS;
+
+  if constexpr (!kSoftmax && !kCausal && kBias == 0 && MB == 1) {
+    if (resident && nchunks == NS) {
+      // All of B0 and B1 in LDS and an elementwise F (the MLP form), one row
+      // block per wave:
+      //  * the first tile's A rows are requested together with the weights, and
+      //    each tile requests the next tile's rows before its own arithmetic;
+      //  * the segments are software-pipelined inside the wave: GEMM1 of
+      //    segment j + 1 is issued between the vector instructions that
+      //    transform segment j, so the matrix core runs while the wave packs;
+      //  * after the weights are in, the waves share no barrier.
+      const u32x4_t rs0 = rsrc_words(p.B0, (uint32_t)((size_t)(kB0LK ? p.L : C::K) * p.ldb0 * 2));
+      const u32x4_t rs1 = rsrc_words(p.B1, (uint32_t)((size_t)p.L * p.ldb1 * 2));
+#pragma unroll
+      for (int s = 0; s < NS; ++s) issue(s, nchunks, rs0, rs1);
+      const int G = (int)gridDim.x;
+      const int ntile = p.batch * mtiles;
+      // A fragments of tile e for this wave's 32 rows (zero when !ok or past M)
+      auto a_load = [&](int e, bool ok, u32x4_t (&af)[KS]) {
+        const int b = e / mtiles, mt = e - b * mtiles;
+        const __amdgpu_buffer_rsrc_t rsA = make_rsrc((const uint16_t*)p.A + (size_t)b * p.sa,
+                                                     (uint32_t)((size_t)p.M * p.lda * 2));
+        const uint32_t row = (uint32_t)(mt * C::BM + wave * 32 + r32);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          af[ks] = buf_load_b128(rsA, ok ? (row * p.lda + (uint32_t)(ks * 16 + 8 * h)) * 2 : kOutOfRange);
+      };
+      u32x4_t af[KS];
+      int e = (int)blockIdx.x;
+      a_load(e, e < ntile, af);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      // GEMM1 of segment sg (B0 fragments from stage sg) into sx
+      auto g1 = [&](int sg, f32x16_t (&sx)[2]) {
+        const uint8_t* st = smem + sg * C::kStage;
+        u32x4_t bf[KS][2];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int lb = 0; lb < 2; ++lb) {
+            if constexpr (kB0LK) {
+              bf[ks][lb] = *(const u32x4_t*)(st + b0_rd[ks] + lb * 32 * C::K * 2);
+            } else {
+              const u32x2_t lo = lds_read_tr16(st + b0_rd[lb] + ks * 16 * 128);
+              const u32x2_t hi = lds_read_tr16(st + b0_rd[lb] + ks * 16 * 128 + 4 * 128);
+              bf[ks][lb] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+            }
+          }
+#pragma unroll
+        for (int lb = 0; lb < 2; ++lb) sx[lb] = f32x16_t{0};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int lb = 0; lb < 2; ++lb)
+            sx[lb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bf[ks][lb]),
+                                                             __builtin_bit_cast(bf16x8_t, af[ks]), sx[lb], 0, 0, 0);
+      };
+      // F of one segment (the arithmetic of the other path) packed as GEMM2's operand
+      auto tf = [&](const f32x16_t (&sx)[2], u32x4_t (&pf)[4]) {
+#pragma unroll
+        for (int lb = 0; lb < 2; ++lb) {
+          float x[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) x[r] = fmaxf(sx[lb][r] * scale, floor_v);
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) pf[2 * lb + c][q] = pack_bf16x2(x[8 * c + 2 * q], x[8 * c + 2 * q + 1]);
+        }
+      };
+      // GEMM2 of segment sg (B1 fragments from stage sg) into o
+      auto g2 = [&](int sg, const u32x4_t (&pf)[4], f32x16_t (&o)[NB]) {
+        const uint8_t* st = smem + sg * C::kStage;
+        u32x4_t vf[4][NB];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const u32x2_t lo = lds_read_tr16(st + b1_rd[nb] + c * 16 * C::N * 2);
+            const u32x2_t hi = lds_read_tr16(st + b1_rd[nb] + c * 16 * C::N * 2 + 8 * C::N * 2);
+            vf[c][nb] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+          }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf[c][nb]),
+                                                            __builtin_bit_cast(bf16x8_t, pf[c]), o[nb], 0, 0, 0);
+      };
+      for (; e < ntile; e += G) {
+        const int en = e + G;
+        u32x4_t an[KS];
+        a_load(en < ntile ? en : e, en < ntile, an);
+        f32x16_t oacc[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x16_t{0};
+        f32x16_t s0[2], s1[2];
+        u32x4_t pf[4];
+        g1(0, s0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          f32x16_t (&cur)[2] = (j & 1) ? s1 : s0;
+          f32x16_t (&nxt)[2] = (j & 1) ? s0 : s1;
+          if (j + 1 < NS) {
+            g1(j + 1, nxt);
+            tf(cur, pf);
+            // GEMM1's fragment reads first, then its MFMAs one at a time
+            // between the transform's vector instructions (80 per segment)
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS * (kB0LK ? 1 : 2), 0);
+#pragma unroll
+            for (int i = 0; i < 2 * KS; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, 80 / (2 * KS), 0);
+            }
+          } else {
+            tf(cur, pf);
+          }
+          g2(j, pf, oacc);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        const int b = e / mtiles, mt = e - b * mtiles;
+        const uint32_t es = p.out_f32 ? 4u : 2u;
+        const __amdgpu_buffer_rsrc_t rsO = make_rsrc((uint8_t*)p.O + (size_t)b * p.so * es,
+                                                     (uint32_t)((size_t)p.M * p.ldo * es));
+        const uint32_t row = (uint32_t)(mt * C::BM + wave * 32 + r32);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {   // oacc[nb][4q + k] is O[row][nb*32 + 8q + 4h + k]
+            const int n = nb * 32 + 8 * q + 4 * h;
+            const f32x4_t y = {oacc[nb][4 * q], oacc[nb][4 * q + 1], oacc[nb][4 * q + 2], oacc[nb][4 * q + 3]};
+            if (p.out_f32) {
+              if (p.o_vec) {
+                buf_store_b128(__builtin_bit_cast(u32x4_t, y), rsO, (row * p.ldo + (uint32_t)n) * 4);
+              } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) buf_store_b32(__float_as_uint(y[k]), rsO, (row * p.ldo + (uint32_t)(n + k)) * 4);
+              }
+            } else {
+              if (p.o_vec) {
+                buf_store_b64(u32x2_t{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])}, rsO, (row * p.ldo + (uint32_t)n) * 2);
+              } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) buf_store_b16((uint16_t)f32_to_bf16(y[k]), rsO, (row * p.ldo + (uint32_t)(n + k)) * 2);
+              }
+            }
+          }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) af[ks] = an[ks];
+      }
+      return;
+    }
+  }
   if (resident) {
     const u32x4_t rs0 = rsrc_words(p.B0, (uint32_t)((size_t)(kB0LK ? p.L : C::K) * p.ldb0 * 2));
     const u32x4_t rs1 = rsrc_words(p.B1, (uint32_t)((size_t)p.L * p.ldb1 * 2));

@@ -271,6 +271,29 @@ def test_shared_weights_streamed(L):
     P.assert_close(P.gpu_to_f64(O), R, P.REL_F_BF16, P.MAX_ABS_BF16, f"shared softmax alpha<0 L={L}")
 
 
+@pytest.mark.parametrize("K,N,L", [(64, 64, 256), (64, 128, 192), (128, 64, 192), (128, 128, 128)])
+def test_mlp_resident_weights_several_tiles_per_workgroup(K, N, L):
+    # B0 and B1 resident in LDS (L as long as the ring) with an elementwise F:
+    # more 128-row tiles than co-resident workgroups, so a workgroup takes
+    # several tiles and loads the next tile's A rows during the current one;
+    # the last tile is ragged
+    # (alpha = 64 / K, a power of two, keeps the scores at the workload's unit
+    # variance when K = 128)
+    M = 65536 + 64 * 128 + 37
+    w, dev, ref = P.inputs("c4_b2b_mlp_relu", seed=19, M=M, K=K, L=L, N=N)
+    check(dev, ref, lk=False, alpha=64.0 / K, act="relu", what=f"MLP {M} rows K={K} N={N} L={L}")
+    # 2-D weights shared by a batch of 3 (tiles of one workgroup cross batch
+    # entries), identity F with alpha != 1
+    batch, Mb, alpha = 3, 30005, 0.75 * 64.0 / K
+    w, dev, ref = P.inputs("c4_b2b_mlp_relu", seed=20, batch=batch, M=Mb, K=K, L=L, N=N)
+    R = oracle.b2bgemm(ref["A"], ref["B0"][0], ref["B1"][0], alpha=alpha)
+    O = torch.empty(batch, Mb, N, dtype=torch.float32, device="cuda")
+    cf.cf_b2bgemm(dev["A"], dev["B0"][0], dev["B1"][0], O, alpha=alpha)
+    torch.cuda.synchronize()
+    r, m = P.assert_close(P.gpu_to_f64(O), R, P.REL_F_BF16, P.MAX_ABS_BF16, f"shared weights, batch {batch}")
+    print(f"shared weights batch {batch} x {Mb}: relF {r:.2e} maxabs {m:.2e}", flush=True)
+
+
 def test_bias_and_shared_weights():
     # a 2-D B0/B1 is shared by every batch; bias per column of S
     w, dev, ref = P.inputs("c4_b2b_mlp_relu", seed=5, batch=3, M=96, K=32, L=96, N=64)

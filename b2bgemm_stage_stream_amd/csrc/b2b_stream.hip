@@ -366,162 +366,6 @@ void b2b_stream_kernel(B2bParams p) {
   // ---- B0/B1 shared by the batch and no longer than the ring: load once
   const bool shared = p.batch == 1 || (p.sb0 == 0 && p.sb1 == 0);
   const bool resident = shared && nchunks <= NS;
-
-  if constexpr (!kSoftmax && !kCausal && kBias == 0 && MB == 1) {
-    if (resident && nchunks == NS) {
-      // All of B0 and B1 in LDS and an elementwise F (the MLP form), one row
-      // block per wave:
-      //  * the first tile's A rows are requested together with the weights, and
-      //    each tile requests the next tile's rows before its own arithmetic;
-      //  * the segments are software-pipelined inside the wave: GEMM1 of
-      //    segment j + 1 is issued between the vector instructions that
-      //    transform segment j, so the matrix core runs while the wave packs;
-      //  * after the weights are in, the waves share no barrier.
-      const u32x4_t rs0 = rsrc_words(p.B0, (uint32_t)((size_t)(kB0LK ? p.L : C::K) * p.ldb0 * 2));
-      const u32x4_t rs1 = rsrc_words(p.B1, (uint32_t)((size_t)p.L * p.ldb1 * 2));
-#pragma unroll
-      for (int s = 0; s < NS; ++s) issue(s, nchunks, rs0, rs1);
-      const int G = (int)gridDim.x;
-      const int ntile = p.batch * mtiles;
-      // A fragments of tile e for this wave's 32 rows (zero when !ok or past M)
-      auto a_load = [&](int e, bool ok, u32x4_t (&af)[KS]) {
-        const int b = e / mtiles, mt = e - b * mtiles;
-        const __amdgpu_buffer_rsrc_t rsA = make_rsrc((const uint16_t*)p.A + (size_t)b * p.sa,
-                                                     (uint32_t)((size_t)p.M * p.lda * 2));
-        const uint32_t row = (uint32_t)(mt * C::BM + wave * 32 + r32);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          af[ks] = buf_load_b128(rsA, ok ? (row * p.lda + (uint32_t)(ks * 16 + 8 * h)) * 2 : kOutOfRange);
-      };
-      u32x4_t af[KS];
-      int e = (int)blockIdx.x;
-      a_load(e, e < ntile, af);
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_waitcnt(0);
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      // GEMM1 of segment sg (B0 fragments from stage sg) into sx
-      auto g1 = [&](int sg, f32x16_t (&sx)[2]) {
-        const uint8_t* st = smem + sg * C::kStage;
-        u32x4_t bf[KS][2];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-          for (int lb = 0; lb < 2; ++lb) {
-            if constexpr (kB0LK) {
-              bf[ks][lb] = *(const u32x4_t*)(st + b0_rd[ks] + lb * 32 * C::K * 2);
-            } else {
-              const u32x2_t lo = lds_read_tr16(st + b0_rd[lb] + ks * 16 * 128);
-              const u32x2_t hi = lds_read_tr16(st + b0_rd[lb] + ks * 16 * 128 + 4 * 128);
-              bf[ks][lb] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-            }
-          }
-#pragma unroll
-        for (int lb = 0; lb < 2; ++lb) sx[lb] = f32x16_t{0};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-          for (int lb = 0; lb < 2; ++lb)
-            sx[lb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bf[ks][lb]),
-                                                             __builtin_bit_cast(bf16x8_t, af[ks]), sx[lb], 0, 0, 0);
-      };
-      // F of one segment (the arithmetic of the other path) packed as GEMM2's operand
-      auto tf = [&](const f32x16_t (&sx)[2], u32x4_t (&pf)[4]) {
-#pragma unroll
-        for (int lb = 0; lb < 2; ++lb) {
-          float x[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) x[r] = fmaxf(sx[lb][r] * scale, floor_v);
-#pragma unroll
-          for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) pf[2 * lb + c][q] = pack_bf16x2(x[8 * c + 2 * q], x[8 * c + 2 * q + 1]);
-        }
-      };
-      // GEMM2 of segment sg (B1 fragments from stage sg) into o
-      auto g2 = [&](int sg, const u32x4_t (&pf)[4], f32x16_t (&o)[NB]) {
-        const uint8_t* st = smem + sg * C::kStage;
-        u32x4_t vf[4][NB];
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const u32x2_t lo = lds_read_tr16(st + b1_rd[nb] + c * 16 * C::N * 2);
-            const u32x2_t hi = lds_read_tr16(st + b1_rd[nb] + c * 16 * C::N * 2 + 8 * C::N * 2);
-            vf[c][nb] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-          }
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf[c][nb]),
-                                                            __builtin_bit_cast(bf16x8_t, pf[c]), o[nb], 0, 0, 0);
-      };
-      for (; e < ntile; e += G) {
-        const int en = e + G;
-        u32x4_t an[KS];
-        a_load(en < ntile ? en : e, en < ntile, an);
-        f32x16_t oacc[NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x16_t{0};
-        f32x16_t s0[2], s1[2];
-        u32x4_t pf[4];
-        g1(0, s0);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < NS; ++j) {
-          f32x16_t (&cur)[2] = (j & 1) ? s1 : s0;
-          f32x16_t (&nxt)[2] = (j & 1) ? s0 : s1;
-          if (j + 1 < NS) {
-            g1(j + 1, nxt);
-            tf(cur, pf);
-            // GEMM1's fragment reads first, then its MFMAs one at a time
-            // between the transform's vector instructions (80 per segment)
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS * (kB0LK ? 1 : 2), 0);
-#pragma unroll
-            for (int i = 0; i < 2 * KS; ++i) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(0x002, 80 / (2 * KS), 0);
-            }
-          } else {
-            tf(cur, pf);
-          }
-          g2(j, pf, oacc);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        const int b = e / mtiles, mt = e - b * mtiles;
-        const uint32_t es = p.out_f32 ? 4u : 2u;
-        const __amdgpu_buffer_rsrc_t rsO = make_rsrc((uint8_t*)p.O + (size_t)b * p.so * es,
-                                                     (uint32_t)((size_t)p.M * p.ldo * es));
-        const uint32_t row = (uint32_t)(mt * C::BM + wave * 32 + r32);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {   // oacc[nb][4q + k] is O[row][nb*32 + 8q + 4h + k]
-            const int n = nb * 32 + 8 * q + 4 * h;
-            const f32x4_t y = {oacc[nb][4 * q], oacc[nb][4 * q + 1], oacc[nb][4 * q + 2], oacc[nb][4 * q + 3]};
-            if (p.out_f32) {
-              if (p.o_vec) {
-                buf_store_b128(__builtin_bit_cast(u32x4_t, y), rsO, (row * p.ldo + (uint32_t)n) * 4);
-              } else {
-#pragma unroll
-                for (int k = 0; k < 4; ++k) buf_store_b32(__float_as_uint(y[k]), rsO, (row * p.ldo + (uint32_t)(n + k)) * 4);
-              }
-            } else {
-              if (p.o_vec) {
-                buf_store_b64(u32x2_t{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])}, rsO, (row * p.ldo + (uint32_t)n) * 2);
-              } else {
-#pragma unroll
-                for (int k = 0; k < 4; ++k) buf_store_b16((uint16_t)f32_to_bf16(y[k]), rsO, (row * p.ldo + (uint32_t)(n + k)) * 2);
-              }
-            }
-          }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) af[ks] = an[ks];
-      }
-      return;
-    }
-  }
   if (resident) {
     const u32x4_t rs0 = rsrc_words(p.B0, (uint32_t)((size_t)(kB0LK ? p.L : C::K) * p.ldb0 * 2));
     const u32x4_t rs1 = rsrc_words(p.B1, (uint32_t)((size_t)p.L * p.ldb1 * 2));
@@ -664,6 +508,246 @@ void b2b_stream_kernel(B2bParams p) {
           }
         }
     }
+  }
+}
+
+// ---- elementwise F with B0 and B1 resident in LDS (the MLP form)
+//
+// B0 and B1 are shared by the batch and exactly as long as the ring (L = 256
+// for K = N = 64, 192 with one width 128, 128 with both), F is elementwise
+// without bias. The weights are loaded once per workgroup; then each wave
+// runs its own 32-row blocks with no further barrier:
+//  * the first tile's A rows are requested together with the weights, and
+//    each tile requests the next tile's rows before its own arithmetic;
+//  * the segments are software-pipelined inside the wave: GEMM1 of segment
+//    j + 1 is issued between the vector instructions that transform segment j
+//    into GEMM2's operand, so the matrix core runs while the wave packs.
+// The arithmetic and its order are those of b2b_stream_kernel. Built with
+// four waves (two workgroups per CU); one eight-wave workgroup per CU, which
+// loads the weights into LDS once per CU instead of twice, measured slower.
+template <int KS, int NB, bool kB0LK, int kWaves>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kWaves, 64 * kWaves), amdgpu_waves_per_eu(2, 2)))
+void b2b_mlp_kernel(B2bParams p) {
+  using C = TCfg<KS, NB, 1>;
+  constexpr int NS = C::kStages;            // segments of L (the host checks L == NS * kTLC)
+  constexpr int BM = 32 * kWaves;           // rows per tile, 32 per wave
+  constexpr int kThreads = 64 * kWaves;
+  constexpr int kLoads = C::kStage / (kThreads * 16);
+  static_assert(kLoads * kThreads * 16 == C::kStage, "whole 1 KiB blocks per wave");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::kLds];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, r32 = lane & 31;
+  const int mtiles = (p.M + BM - 1) / BM;
+  const int ntile = p.batch * mtiles;
+  const float scale = p.alpha;
+  const float floor_v = p.act == 1 ? 0.0f : -INFINITY;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)smem;
+
+  // ---- the weights: load i of wave w fills 1 KiB block q = kWaves i + w of
+  // stage s (B0 blocks first), the layouts and swizzles of b2b_stream_kernel
+  auto w_off = [&](int i, int s) -> uint32_t {
+    const int q = kWaves * i + wave;
+    if (q < C::kB0Blocks) {
+      if constexpr (kB0LK) {
+        constexpr int cpr = C::K / 8, rpb = 1024 / (C::K * 2);
+        const int row = q * rpb + lane / cpr, ph = lane % cpr;
+        const int lg = ph ^ (C::K == 64 ? swz_rows128(row) : swz_rows256(row));
+        return ((uint32_t)(row + s * kTLC) * p.ldb0 + (uint32_t)(8 * lg)) * 2u;
+      } else {
+        const int row = q * 8 + lane / 8, ph = lane % 8;
+        const int lg = ph ^ swz_tr128(row);
+        return ((uint32_t)row * p.ldb0 + (uint32_t)(8 * lg + s * kTLC)) * 2u;
+      }
+    }
+    constexpr int cpr = C::N / 8, rpb = 1024 / (C::N * 2);
+    const int qb = q - C::kB0Blocks;
+    const int row = qb * rpb + lane / cpr, ph = lane % cpr;
+    const int lg = ph ^ (C::N == 64 ? swz_tr128(row) : swz_tr256(row));
+    return ((uint32_t)(row + s * kTLC) * p.ldb1 + (uint32_t)(8 * lg)) * 2u;
+  };
+  {
+    const u32x4_t rs0 = rsrc_words(p.B0, (uint32_t)((size_t)(kB0LK ? p.L : C::K) * p.ldb0 * 2));
+    const u32x4_t rs1 = rsrc_words(p.B1, (uint32_t)((size_t)p.L * p.ldb1 * 2));
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const uint32_t st = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds0 + (uint32_t)(s * C::kStage))) +
+                          (uint32_t)(wave * 1024);
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i)
+        lds_dma16(st + i * kWaves * 1024, kWaves * i + wave < C::kB0Blocks ? rs0 : rs1, w_off(i, s));
+    }
+  }
+
+  // ---- fragment read offsets within a stage (as in b2b_stream_kernel)
+  uint32_t b0_rd[kB0LK ? KS : 2];
+  if constexpr (kB0LK) {
+    constexpr int RB = C::K * 2;
+    const int f = C::K == 64 ? swz_rows128(r32) : swz_rows256(r32);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) b0_rd[ks] = (uint32_t)(r32 * RB + 16 * ((2 * ks + h) ^ f));
+  } else {
+    const int g = lane >> 4, i = lane & 15;
+    const int f = swz_tr128(i >> 2);
+    const int c = 2 * (g & 1) + ((i & 3) >> 1);
+#pragma unroll
+    for (int lb = 0; lb < 2; ++lb)
+      b0_rd[lb] = (uint32_t)((8 * (g >> 1) + (i >> 2)) * 128 + 16 * ((4 * lb + c) ^ f) + 8 * (i & 1));
+  }
+  uint32_t b1_rd[NB];
+  {
+    constexpr int RB = C::N * 2;
+    const int g = lane >> 4, i = lane & 15;
+    const int f = C::N == 64 ? swz_tr128(i >> 2) : swz_tr256(i >> 2);
+    const int c = 2 * (g & 1) + ((i & 3) >> 1);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      b1_rd[nb] = (uint32_t)(C::kB0Bytes + (4 * (g >> 1) + (i >> 2)) * RB + 16 * ((4 * nb + c) ^ f) + 8 * (i & 1));
+  }
+
+  // A fragments of tile e for this wave's 32 rows (zero when !ok or past M)
+  auto a_load = [&](int e, bool ok, u32x4_t (&af)[KS]) {
+    const int b = e / mtiles, mt = e - b * mtiles;
+    const __amdgpu_buffer_rsrc_t rsA = make_rsrc((const uint16_t*)p.A + (size_t)b * p.sa,
+                                                 (uint32_t)((size_t)p.M * p.lda * 2));
+    const uint32_t row = (uint32_t)(mt * BM + wave * 32 + r32);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      af[ks] = buf_load_b128(rsA, ok ? (row * p.lda + (uint32_t)(ks * 16 + 8 * h)) * 2 : kOutOfRange);
+  };
+  u32x4_t af[KS];
+  const int G = (int)gridDim.x;
+  int e = (int)blockIdx.x;
+  a_load(e, e < ntile, af);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  // GEMM1 of segment sg (B0 fragments from stage sg) into sx
+  auto g1 = [&](int sg, f32x16_t (&sx)[2]) {
+    const uint8_t* st = smem + sg * C::kStage;
+    u32x4_t bf[KS][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int lb = 0; lb < 2; ++lb) {
+        if constexpr (kB0LK) {
+          bf[ks][lb] = *(const u32x4_t*)(st + b0_rd[ks] + lb * 32 * C::K * 2);
+        } else {
+          const u32x2_t lo = lds_read_tr16(st + b0_rd[lb] + ks * 16 * 128);
+          const u32x2_t hi = lds_read_tr16(st + b0_rd[lb] + ks * 16 * 128 + 4 * 128);
+          bf[ks][lb] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        }
+      }
+#pragma unroll
+    for (int lb = 0; lb < 2; ++lb) sx[lb] = f32x16_t{0};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int lb = 0; lb < 2; ++lb)
+        sx[lb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bf[ks][lb]),
+                                                         __builtin_bit_cast(bf16x8_t, af[ks]), sx[lb], 0, 0, 0);
+  };
+  // F of one segment packed as GEMM2's operand: register r of block lb holds
+  // l = lb*32 + 8(r>>2) + 4h + (r&3), packed in the k-slot order of GEMM2
+  auto tf = [&](const f32x16_t (&sx)[2], u32x4_t (&pf)[4]) {
+#pragma unroll
+    for (int lb = 0; lb < 2; ++lb) {
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = fmaxf(sx[lb][r] * scale, floor_v);
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pf[2 * lb + c][q] = pack_bf16x2(x[8 * c + 2 * q], x[8 * c + 2 * q + 1]);
+    }
+  };
+  // GEMM2 of segment sg (B1 fragments from stage sg) into o
+  auto g2 = [&](int sg, const u32x4_t (&pf)[4], f32x16_t (&o)[NB]) {
+    const uint8_t* st = smem + sg * C::kStage;
+    u32x4_t vf[4][NB];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const u32x2_t lo = lds_read_tr16(st + b1_rd[nb] + c * 16 * C::N * 2);
+        const u32x2_t hi = lds_read_tr16(st + b1_rd[nb] + c * 16 * C::N * 2 + 8 * C::N * 2);
+        vf[c][nb] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+      }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vf[c][nb]),
+                                                        __builtin_bit_cast(bf16x8_t, pf[c]), o[nb], 0, 0, 0);
+  };
+
+  for (; e < ntile; e += G) {
+    const int en = e + G;
+    u32x4_t an[KS];
+    a_load(en < ntile ? en : e, en < ntile, an);
+    f32x16_t oacc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) oacc[nb] = f32x16_t{0};
+    f32x16_t s0[2], s1[2];
+    u32x4_t pf[4];
+    g1(0, s0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      f32x16_t (&cur)[2] = (j & 1) ? s1 : s0;
+      f32x16_t (&nxt)[2] = (j & 1) ? s0 : s1;
+      if (j + 1 < NS) {
+        g1(j + 1, nxt);
+        tf(cur, pf);
+        // GEMM1's fragment reads first, then its MFMAs one at a time between
+        // the transform's vector instructions (80 per segment)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS * (kB0LK ? 1 : 2), 0);
+#pragma unroll
+        for (int i = 0; i < 2 * KS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 80 / (2 * KS), 0);
+        }
+      } else {
+        tf(cur, pf);
+      }
+      g2(j, pf, oacc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- store: oacc[nb][4q + k] is O[row][nb*32 + 8q + 4h + k] (rows past M
+    // are dropped by the range check)
+    const int b = e / mtiles, mt = e - b * mtiles;
+    const uint32_t es = p.out_f32 ? 4u : 2u;
+    const __amdgpu_buffer_rsrc_t rsO = make_rsrc((uint8_t*)p.O + (size_t)b * p.so * es,
+                                                 (uint32_t)((size_t)p.M * p.ldo * es));
+    const uint32_t row = (uint32_t)(mt * BM + wave * 32 + r32);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = nb * 32 + 8 * q + 4 * h;
+        const f32x4_t y = {oacc[nb][4 * q], oacc[nb][4 * q + 1], oacc[nb][4 * q + 2], oacc[nb][4 * q + 3]};
+        if (p.out_f32) {
+          if (p.o_vec) {
+            buf_store_b128(__builtin_bit_cast(u32x4_t, y), rsO, (row * p.ldo + (uint32_t)n) * 4);
+          } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) buf_store_b32(__float_as_uint(y[k]), rsO, (row * p.ldo + (uint32_t)(n + k)) * 4);
+          }
+        } else {
+          if (p.o_vec) {
+            buf_store_b64(u32x2_t{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])}, rsO, (row * p.ldo + (uint32_t)n) * 2);
+          } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) buf_store_b16((uint16_t)f32_to_bf16(y[k]), rsO, (row * p.ldo + (uint32_t)(n + k)) * 2);
+          }
+        }
+      }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) af[ks] = an[ks];
   }
 }
 
@@ -1051,6 +1135,21 @@ const void* pick_stream_kn(int K, int N, bool two_blocks) {
   if (K == 128 && N == 128) return (const void*)&b2b_stream_kernel<8, 4, 1, kSoftmax, kB0LK, kCausal, kBias>;
   return nullptr;
 }
+
+template <int KS, int NB>
+const void* pick_mlp_kn(const B2bParams& p, int* rows_per_tile, int* threads) {
+  if (p.L != TCfg<KS, NB, 1>::kStages * kTLC) return nullptr;
+  if (rows_per_tile) *rows_per_tile = 128;
+  if (threads) *threads = kTThreads;
+  return p.b0_lk ? (const void*)&b2b_mlp_kernel<KS, NB, true, 4> : (const void*)&b2b_mlp_kernel<KS, NB, false, 4>;
+}
+const void* pick_mlp(const B2bParams& p, int* rows_per_tile, int* threads) {
+  if (p.K == 64 && p.N == 64) return pick_mlp_kn<4, 2>(p, rows_per_tile, threads);
+  if (p.K == 64 && p.N == 128) return pick_mlp_kn<4, 4>(p, rows_per_tile, threads);
+  if (p.K == 128 && p.N == 64) return pick_mlp_kn<8, 2>(p, rows_per_tile, threads);
+  if (p.K == 128 && p.N == 128) return pick_mlp_kn<8, 4>(p, rows_per_tile, threads);
+  return nullptr;
+}
 }  // namespace
 
 const void* b2b_stream_pick(const B2bParams& p, int cus, int* rows_per_tile, int* threads) {
@@ -1065,6 +1164,12 @@ const void* b2b_stream_pick(const B2bParams& p, int cus, int* rows_per_tile, int
     if (rows_per_tile) *rows_per_tile = 512;
     if (threads) *threads = kPThreads;
     return p.b0_lk ? (const void*)&b2b_pp_kernel<4, 2, true> : (const void*)&b2b_pp_kernel<4, 2, false>;
+  }
+  // elementwise F without bias, B0/B1 shared by the batch and exactly one ring
+  // long: the MLP kernel (128-row tiles)
+  if (p.row_op == 0 && !p.causal && !p.bias && (p.batch == 1 || (p.sb0 == 0 && p.sb1 == 0))) {
+    const void* k = pick_mlp(p, rows_per_tile, threads);
+    if (k) return k;
   }
   // 256-row tiles only when they still give every CU two workgroups (and
   // not with a bias, whose registers they have no room for)

@@ -62,6 +62,67 @@ __device__ inline int swz_rows256(int r) { return r & 15; }                     
 __device__ inline int swz_tr128(int r) { return 2 * (r & 3); }                  // transposed reads, 128-B rows
 __device__ inline int swz_tr256(int r) { return (2 * (r & 3)) ^ (4 * (r & 3)); }  // transposed reads, 256-B rows
 
+// Per-lane LDS read offsets within a stage (B0 segment, then B1 segment):
+//  b0_rd: GEMM1's operand B0^T, rows l = lb*32 + (lane & 31), k-slots 8h..8h+7
+//         of step ks; one offset per ks for B0 given [L][K] (16-byte row
+//         reads), one per lb for B0 given [K][L] (transposed reads);
+//  b1_rd: GEMM2's operand B1^T, rows n = nb*32 + (lane & 31), k-slots = l in
+//         the permuted order: half 0 reads rows c16*16 + 4h + 0..3, half 1 rows +8.
+template <int KS, int NB, bool kB0LK>
+__device__ inline void stage_read_offsets(int lane, uint32_t (&b0_rd)[kB0LK ? KS : 2], uint32_t (&b1_rd)[NB]) {
+  constexpr int K = 16 * KS, N = 32 * NB, kB0Bytes = kTLC * K * 2;
+  const int h = lane >> 5, r32 = lane & 31;
+  if constexpr (kB0LK) {
+    constexpr int RB = K * 2;
+    const int f = K == 64 ? swz_rows128(r32) : swz_rows256(r32);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) b0_rd[ks] = (uint32_t)(r32 * RB + 16 * ((2 * ks + h) ^ f));
+  } else {
+    // [k][l]: lane 16g + i reads row ks*16 + 8(g>>1) + 4 half + i/4, columns
+    // lb*32 + 16(g&1) + 4(i&3) .. +3; one base per lb
+    const int g = lane >> 4, i = lane & 15;
+    const int f = swz_tr128(i >> 2);
+    const int c = 2 * (g & 1) + ((i & 3) >> 1);
+#pragma unroll
+    for (int lb = 0; lb < 2; ++lb)
+      b0_rd[lb] = (uint32_t)((8 * (g >> 1) + (i >> 2)) * 128 + 16 * ((4 * lb + c) ^ f) + 8 * (i & 1));
+  }
+  constexpr int RB = N * 2;
+  const int g = lane >> 4, i = lane & 15;
+  const int f = N == 64 ? swz_tr128(i >> 2) : swz_tr256(i >> 2);
+  const int c = 2 * (g & 1) + ((i & 3) >> 1);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+    b1_rd[nb] = (uint32_t)(kB0Bytes + (4 * (g >> 1) + (i >> 2)) * RB + 16 * ((4 * nb + c) ^ f) + 8 * (i & 1));
+}
+
+// Global byte offset, within B0 or B1, of the 16 bytes that lane `lane` of
+// wave `wave` loads into 1 KiB block q = kWaves*i + wave of the stage holding
+// segment s (B0 blocks first, then B1), in the swizzled layouts that
+// stage_read_offsets reads.
+template <int KS, int NB, bool kB0LK, int kWaves>
+__device__ inline uint32_t seg_load_off(const B2bParams& p, int wave, int lane, int i, int s) {
+  constexpr int K = 16 * KS, N = 32 * NB, kB0Blocks = kTLC * K * 2 / 1024;
+  const int q = kWaves * i + wave;
+  if (q < kB0Blocks) {
+    if constexpr (kB0LK) {             // rows l of K * 2 bytes
+      constexpr int cpr = K / 8, rpb = 1024 / (K * 2);
+      const int row = q * rpb + lane / cpr, ph = lane % cpr;
+      const int lg = ph ^ (K == 64 ? swz_rows128(row) : swz_rows256(row));
+      return ((uint32_t)(row + s * kTLC) * p.ldb0 + (uint32_t)(8 * lg)) * 2u;
+    } else {                           // rows k of 64 l (128 bytes)
+      const int row = q * 8 + lane / 8, ph = lane % 8;
+      const int lg = ph ^ swz_tr128(row);
+      return ((uint32_t)row * p.ldb0 + (uint32_t)(8 * lg + s * kTLC)) * 2u;
+    }
+  }
+  constexpr int cpr = N / 8, rpb = 1024 / (N * 2);   // B1 rows l of N * 2 bytes
+  const int qb = q - kB0Blocks;
+  const int row = qb * rpb + lane / cpr, ph = lane % cpr;
+  const int lg = ph ^ (N == 64 ? swz_tr128(row) : swz_tr256(row));
+  return ((uint32_t)(row + s * kTLC) * p.ldb1 + (uint32_t)(8 * lg)) * 2u;
+}
+
 // Softmax of one 32-row block whose S^T accumulators s[lb] hold l = lb*32 +
 // 8(r >> 2) + 4h + (r & 3) of row m = lane & 31. Full form: the row extreme
 // of S (max for alpha >= 0, min otherwise, so that it is the extreme of
@@ -147,67 +208,20 @@ void b2b_stream_kernel(B2bParams p) {
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)smem;
 
   // ---- DMA plan: load i of wave w fills 1 KiB block q = 4 i + w of a stage
-  // (B0 blocks first). Per load: global byte offset at segment 0 (batch entry
-  // base excluded), the per-segment step, and the region.
+  // (B0 blocks first); per load the global byte offset at segment 0 (batch
+  // entry base excluded) and the per-segment step, uniform over the wave
   uint32_t goff[C::kLoads], gstep[C::kLoads];
   bool is_b0[C::kLoads];
 #pragma unroll
   for (int i = 0; i < C::kLoads; ++i) {
-    const int q = 4 * i + wave;
-    is_b0[i] = q < C::kB0Blocks;
-    if (q < C::kB0Blocks) {
-      if constexpr (kB0LK) {            // rows l of K * 2 bytes
-        constexpr int cpr = C::K / 8, rpb = 1024 / (C::K * 2);
-        const int row = q * rpb + lane / cpr, ph = lane % cpr;
-        const int lg = ph ^ (C::K == 64 ? swz_rows128(row) : swz_rows256(row));
-        goff[i] = ((uint32_t)row * p.ldb0 + (uint32_t)(8 * lg)) * 2u;
-        gstep[i] = (uint32_t)kTLC * p.ldb0 * 2u;
-      } else {                          // rows k of 64 l (128 bytes)
-        const int row = q * 8 + lane / 8, ph = lane % 8;
-        const int lg = ph ^ swz_tr128(row);
-        goff[i] = ((uint32_t)row * p.ldb0 + (uint32_t)(8 * lg)) * 2u;
-        gstep[i] = kTLC * 2u;
-      }
-    } else {                            // B1 rows l of N * 2 bytes
-      constexpr int cpr = C::N / 8, rpb = 1024 / (C::N * 2);
-      const int qb = q - C::kB0Blocks;
-      const int row = qb * rpb + lane / cpr, ph = lane % cpr;
-      const int lg = ph ^ (C::N == 64 ? swz_tr128(row) : swz_tr256(row));
-      goff[i] = ((uint32_t)row * p.ldb1 + (uint32_t)(8 * lg)) * 2u;
-      gstep[i] = (uint32_t)kTLC * p.ldb1 * 2u;
-    }
+    is_b0[i] = (kTThreads / 64) * i + wave < C::kB0Blocks;
+    goff[i] = seg_load_off<KS, NB, kB0LK, kTThreads / 64>(p, wave, lane, i, 0);
+    gstep[i] = is_b0[i] ? (kB0LK ? (uint32_t)kTLC * p.ldb0 * 2u : kTLC * 2u) : (uint32_t)kTLC * p.ldb1 * 2u;
   }
 
   // ---- LDS read offsets (within a stage)
-  // GEMM1 operand B0^T rows l = lb*32 + r32, k-slots 8h..8h+7 of step ks
-  uint32_t b0_rd[kB0LK ? KS : 2];
-  if constexpr (kB0LK) {
-    constexpr int RB = C::K * 2;
-    const int f = C::K == 64 ? swz_rows128(r32) : swz_rows256(r32);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) b0_rd[ks] = (uint32_t)(r32 * RB + 16 * ((2 * ks + h) ^ f));
-  } else {
-    // [k][l]: lane 16g + i reads row ks*16 + 8(g>>1) + 4 half + i/4, columns
-    // lb*32 + 16(g&1) + 4(i&3) .. +3; one base per lb
-    const int g = lane >> 4, i = lane & 15;
-    const int f = swz_tr128(i >> 2);
-    const int c = 2 * (g & 1) + ((i & 3) >> 1);
-#pragma unroll
-    for (int lb = 0; lb < 2; ++lb)
-      b0_rd[lb] = (uint32_t)((8 * (g >> 1) + (i >> 2)) * 128 + 16 * ((4 * lb + c) ^ f) + 8 * (i & 1));
-  }
-  // GEMM2 operand B1^T rows n = nb*32 + (lane & 31), k-slots = l in the
-  // permuted order: half 0 reads rows c16*16 + 4h + 0..3, half 1 rows +8
-  uint32_t b1_rd[NB];
-  {
-    constexpr int RB = C::N * 2;
-    const int g = lane >> 4, i = lane & 15;
-    const int f = C::N == 64 ? swz_tr128(i >> 2) : swz_tr256(i >> 2);
-    const int c = 2 * (g & 1) + ((i & 3) >> 1);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      b1_rd[nb] = (uint32_t)(C::kB0Bytes + (4 * (g >> 1) + (i >> 2)) * RB + 16 * ((4 * nb + c) ^ f) + 8 * (i & 1));
-  }
+  uint32_t b0_rd[kB0LK ? KS : 2], b1_rd[NB];
+  stage_read_offsets<KS, NB, kB0LK>(lane, b0_rd, b1_rd);
 
   const u32x4_t rsb = rsrc_words(p.bias, (uint32_t)p.L * (kBias == 2 ? 4u : 2u));
   auto issue = [&](int s, int nseg, const u32x4_t& rs0, const u32x4_t& rs1) {
@@ -547,26 +561,6 @@ void b2b_mlp_kernel(B2bParams p) {
 
   // ---- the weights: load i of wave w fills 1 KiB block q = kWaves i + w of
   // stage s (B0 blocks first), the layouts and swizzles of b2b_stream_kernel
-  auto w_off = [&](int i, int s) -> uint32_t {
-    const int q = kWaves * i + wave;
-    if (q < C::kB0Blocks) {
-      if constexpr (kB0LK) {
-        constexpr int cpr = C::K / 8, rpb = 1024 / (C::K * 2);
-        const int row = q * rpb + lane / cpr, ph = lane % cpr;
-        const int lg = ph ^ (C::K == 64 ? swz_rows128(row) : swz_rows256(row));
-        return ((uint32_t)(row + s * kTLC) * p.ldb0 + (uint32_t)(8 * lg)) * 2u;
-      } else {
-        const int row = q * 8 + lane / 8, ph = lane % 8;
-        const int lg = ph ^ swz_tr128(row);
-        return ((uint32_t)row * p.ldb0 + (uint32_t)(8 * lg + s * kTLC)) * 2u;
-      }
-    }
-    constexpr int cpr = C::N / 8, rpb = 1024 / (C::N * 2);
-    const int qb = q - C::kB0Blocks;
-    const int row = qb * rpb + lane / cpr, ph = lane % cpr;
-    const int lg = ph ^ (C::N == 64 ? swz_tr128(row) : swz_tr256(row));
-    return ((uint32_t)(row + s * kTLC) * p.ldb1 + (uint32_t)(8 * lg)) * 2u;
-  };
   {
     const u32x4_t rs0 = rsrc_words(p.B0, (uint32_t)((size_t)(kB0LK ? p.L : C::K) * p.ldb0 * 2));
     const u32x4_t rs1 = rsrc_words(p.B1, (uint32_t)((size_t)p.L * p.ldb1 * 2));
@@ -576,35 +570,14 @@ void b2b_mlp_kernel(B2bParams p) {
                           (uint32_t)(wave * 1024);
 #pragma unroll
       for (int i = 0; i < kLoads; ++i)
-        lds_dma16(st + i * kWaves * 1024, kWaves * i + wave < C::kB0Blocks ? rs0 : rs1, w_off(i, s));
+        lds_dma16(st + i * kWaves * 1024, kWaves * i + wave < C::kB0Blocks ? rs0 : rs1,
+                  seg_load_off<KS, NB, kB0LK, kWaves>(p, wave, lane, i, s));
     }
   }
 
-  // ---- fragment read offsets within a stage (as in b2b_stream_kernel)
-  uint32_t b0_rd[kB0LK ? KS : 2];
-  if constexpr (kB0LK) {
-    constexpr int RB = C::K * 2;
-    const int f = C::K == 64 ? swz_rows128(r32) : swz_rows256(r32);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) b0_rd[ks] = (uint32_t)(r32 * RB + 16 * ((2 * ks + h) ^ f));
-  } else {
-    const int g = lane >> 4, i = lane & 15;
-    const int f = swz_tr128(i >> 2);
-    const int c = 2 * (g & 1) + ((i & 3) >> 1);
-#pragma unroll
-    for (int lb = 0; lb < 2; ++lb)
-      b0_rd[lb] = (uint32_t)((8 * (g >> 1) + (i >> 2)) * 128 + 16 * ((4 * lb + c) ^ f) + 8 * (i & 1));
-  }
-  uint32_t b1_rd[NB];
-  {
-    constexpr int RB = C::N * 2;
-    const int g = lane >> 4, i = lane & 15;
-    const int f = C::N == 64 ? swz_tr128(i >> 2) : swz_tr256(i >> 2);
-    const int c = 2 * (g & 1) + ((i & 3) >> 1);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      b1_rd[nb] = (uint32_t)(C::kB0Bytes + (4 * (g >> 1) + (i >> 2)) * RB + 16 * ((4 * nb + c) ^ f) + 8 * (i & 1));
-  }
+  // ---- fragment read offsets within a stage
+  uint32_t b0_rd[kB0LK ? KS : 2], b1_rd[NB];
+  stage_read_offsets<KS, NB, kB0LK>(lane, b0_rd, b1_rd);
 
   // A fragments of tile e for this wave's 32 rows (zero when !ok or past M)
   auto a_load = [&](int e, bool ok, u32x4_t (&af)[KS]) {
@@ -802,26 +775,7 @@ void b2b_pp_kernel(B2bParams p) {
   // ring plan: load i of wave w fills 1 KiB block q = 8 i + w of a stage (B0
   // blocks first); the global offsets are recomputed at every issue (a few
   // integer instructions) rather than held in registers across the loop
-  auto ring_off = [&](int i, int s) -> uint32_t {
-    const int q = kPWaves * i + wave;
-    if (q < kB0Blocks) {
-      if constexpr (kB0LK) {
-        constexpr int cpr = K / 8, rpb = 1024 / (K * 2);
-        const int row = q * rpb + lane / cpr, ph = lane % cpr;
-        const int lg = ph ^ (K == 64 ? swz_rows128(row) : swz_rows256(row));
-        return ((uint32_t)(row + s * kTLC) * p.ldb0 + (uint32_t)(8 * lg)) * 2u;
-      } else {
-        const int row = q * 8 + lane / 8, ph = lane % 8;
-        const int lg = ph ^ swz_tr128(row);
-        return ((uint32_t)row * p.ldb0 + (uint32_t)(8 * lg + s * kTLC)) * 2u;
-      }
-    }
-    constexpr int cpr = N / 8, rpb = 1024 / (N * 2);
-    const int qb = q - kB0Blocks;
-    const int row = qb * rpb + lane / cpr, ph = lane % cpr;
-    const int lg = ph ^ (N == 64 ? swz_tr128(row) : swz_tr256(row));
-    return ((uint32_t)(row + s * kTLC) * p.ldb1 + (uint32_t)(8 * lg)) * 2u;
-  };
+  auto ring_off = [&](int i, int s) { return seg_load_off<KS, NB, kB0LK, kPWaves>(p, wave, lane, i, s); };
   // segment s (ok: it exists) into ring buffer slot `slot`
   auto issue = [&](int slot, int s, bool ok, const u32x4_t& rs0, const u32x4_t& rs1) {
     const uint32_t sb = (uint32_t)__builtin_amdgcn_readfirstlane((int)(lds0 + (uint32_t)(slot * kStage)));
@@ -831,31 +785,9 @@ void b2b_pp_kernel(B2bParams p) {
       lds_dma16(st + i * kPWaves * 1024, kPWaves * i + wave < kB0Blocks ? rs0 : rs1, ok ? ring_off(i, s) : kOutOfRange);
   };
 
-  // fragment read offsets within a stage (as in b2b_stream_kernel)
-  uint32_t b0_rd[kB0LK ? KS : 2];
-  if constexpr (kB0LK) {
-    constexpr int RB = K * 2;
-    const int f = K == 64 ? swz_rows128(r32) : swz_rows256(r32);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) b0_rd[ks] = (uint32_t)(r32 * RB + 16 * ((2 * ks + h) ^ f));
-  } else {
-    const int g = lane >> 4, i = lane & 15;
-    const int f = swz_tr128(i >> 2);
-    const int c = 2 * (g & 1) + ((i & 3) >> 1);
-#pragma unroll
-    for (int lb = 0; lb < 2; ++lb)
-      b0_rd[lb] = (uint32_t)((8 * (g >> 1) + (i >> 2)) * 128 + 16 * ((4 * lb + c) ^ f) + 8 * (i & 1));
-  }
-  uint32_t b1_rd[NB];
-  {
-    constexpr int RB = N * 2;
-    const int g = lane >> 4, i = lane & 15;
-    const int f = N == 64 ? swz_tr128(i >> 2) : swz_tr256(i >> 2);
-    const int c = 2 * (g & 1) + ((i & 3) >> 1);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      b1_rd[nb] = (uint32_t)(kB0Bytes + (4 * (g >> 1) + (i >> 2)) * RB + 16 * ((4 * nb + c) ^ f) + 8 * (i & 1));
-  }
+  // fragment read offsets within a stage
+  uint32_t b0_rd[kB0LK ? KS : 2], b1_rd[NB];
+  stage_read_offsets<KS, NB, kB0LK>(lane, b0_rd, b1_rd);
   // A fragment of row block rb, k step ks: row wave*64 + rb*32 + (lane & 31),
   // 8 k from ks*16 + 8h
   uint32_t a_rd[KS];

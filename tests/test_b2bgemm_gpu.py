@@ -271,8 +271,18 @@ def test_shared_weights_streamed(L):
     P.assert_close(P.gpu_to_f64(O), R, P.REL_F_BF16, P.MAX_ABS_BF16, f"shared softmax alpha<0 L={L}")
 
 
+def mlp_inputs(seed, lk, **dims):
+    """The MLP workload's inputs; with lk, B0 given as [L, K] (transposed copy)."""
+    w, dev, ref = P.inputs("c4_b2b_mlp_relu", seed=seed, **dims)
+    if lk:
+        dev["B0"] = dev["B0"].transpose(1, 2).contiguous()
+        ref["B0"] = np.ascontiguousarray(np.swapaxes(ref["B0"], 1, 2))
+    return dev, ref
+
+
+@pytest.mark.parametrize("lk", [False, True])
 @pytest.mark.parametrize("K,N,L", [(64, 64, 256), (64, 128, 192), (128, 64, 192), (128, 128, 128)])
-def test_mlp_resident_weights_several_tiles_per_workgroup(K, N, L):
+def test_mlp_resident_weights_several_tiles_per_workgroup(K, N, L, lk):
     # B0 and B1 resident in LDS (L as long as the ring) with an elementwise F:
     # more 128-row tiles than co-resident workgroups, so a workgroup takes
     # several tiles and loads the next tile's A rows during the current one;
@@ -280,15 +290,15 @@ def test_mlp_resident_weights_several_tiles_per_workgroup(K, N, L):
     # (alpha = 64 / K, a power of two, keeps the scores at the workload's unit
     # variance when K = 128)
     M = 65536 + 64 * 128 + 37
-    w, dev, ref = P.inputs("c4_b2b_mlp_relu", seed=19, M=M, K=K, L=L, N=N)
-    check(dev, ref, lk=False, alpha=64.0 / K, act="relu", what=f"MLP {M} rows K={K} N={N} L={L}")
+    dev, ref = mlp_inputs(19, lk, M=M, K=K, L=L, N=N)
+    check(dev, ref, lk=lk, alpha=64.0 / K, act="relu", what=f"MLP {M} rows K={K} N={N} L={L} lk={lk}")
     # 2-D weights shared by a batch of 3 (tiles of one workgroup cross batch
     # entries), identity F with alpha != 1
     batch, Mb, alpha = 3, 30005, 0.75 * 64.0 / K
-    w, dev, ref = P.inputs("c4_b2b_mlp_relu", seed=20, batch=batch, M=Mb, K=K, L=L, N=N)
-    R = oracle.b2bgemm(ref["A"], ref["B0"][0], ref["B1"][0], alpha=alpha)
+    dev, ref = mlp_inputs(20, lk, batch=batch, M=Mb, K=K, L=L, N=N)
+    R = oracle.b2bgemm(ref["A"], ref["B0"][0], ref["B1"][0], alpha=alpha, b0_layout="lk" if lk else "kl")
     O = torch.empty(batch, Mb, N, dtype=torch.float32, device="cuda")
-    cf.cf_b2bgemm(dev["A"], dev["B0"][0], dev["B1"][0], O, alpha=alpha)
+    cf.cf_b2bgemm(dev["A"], dev["B0"][0], dev["B1"][0], O, b0_is_lk=lk, alpha=alpha)
     torch.cuda.synchronize()
     r, m = P.assert_close(P.gpu_to_f64(O), R, P.REL_F_BF16, P.MAX_ABS_BF16, f"shared weights, batch {batch}")
     print(f"shared weights batch {batch} x {Mb}: relF {r:.2e} maxabs {m:.2e}", flush=True)

@@ -525,6 +525,8 @@ void b2b_stream_kernel(B2bParams p) {
   }
 }
 
+typedef short i16x2_t __attribute__((ext_vector_type(2)));
+
 // ---- elementwise F with B0 and B1 resident in LDS (the MLP form)
 //
 // B0 and B1 are shared by the batch and exactly as long as the ring (L = 256
@@ -536,10 +538,14 @@ void b2b_stream_kernel(B2bParams p) {
 //  * the segments are software-pipelined inside the wave: GEMM1 of segment
 //    j + 1 is issued between the vector instructions that transform segment j
 //    into GEMM2's operand, so the matrix core runs while the wave packs.
-// The arithmetic and its order are those of b2b_stream_kernel. Built with
-// four waves (two workgroups per CU); one eight-wave workgroup per CU, which
-// loads the weights into LDS once per CU instead of twice, measured slower.
-template <int KS, int NB, bool kB0LK, int kWaves>
+// The arithmetic and its order are those of b2b_stream_kernel, except that F
+// is applied after the bf16 rounding: kRelu takes the ReLU of the rounded
+// pair as a 16-bit signed max with 0 (rounding keeps the sign, so this is the
+// rounding of the ReLU; a negative value or -0 becomes +0, a NaN keeps its
+// sign's side), and kUnit (alpha = 1) skips the scaling. Built with four
+// waves (two workgroups per CU); one eight-wave workgroup per CU, which loads
+// the weights into LDS once per CU instead of twice, measured slower.
+template <int KS, int NB, bool kB0LK, int kWaves, bool kUnit, bool kRelu>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kWaves, 64 * kWaves), amdgpu_waves_per_eu(2, 2)))
 void b2b_mlp_kernel(B2bParams p) {
   using C = TCfg<KS, NB, 1>;
@@ -556,7 +562,6 @@ void b2b_mlp_kernel(B2bParams p) {
   const int mtiles = (p.M + BM - 1) / BM;
   const int ntile = p.batch * mtiles;
   const float scale = p.alpha;
-  const float floor_v = p.act == 1 ? 0.0f : -INFINITY;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)smem;
 
   // ---- the weights: load i of wave w fills 1 KiB block q = kWaves i + w of
@@ -627,16 +632,19 @@ void b2b_mlp_kernel(B2bParams p) {
   // l = lb*32 + 8(r>>2) + 4h + (r&3), packed in the k-slot order of GEMM2
   auto tf = [&](const f32x16_t (&sx)[2], u32x4_t (&pf)[4]) {
 #pragma unroll
-    for (int lb = 0; lb < 2; ++lb) {
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = fmaxf(sx[lb][r] * scale, floor_v);
+    for (int lb = 0; lb < 2; ++lb)
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) pf[2 * lb + c][q] = pack_bf16x2(x[8 * c + 2 * q], x[8 * c + 2 * q + 1]);
-    }
+        for (int q = 0; q < 4; ++q) {
+          const float x0 = sx[lb][8 * c + 2 * q], x1 = sx[lb][8 * c + 2 * q + 1];
+          uint32_t v = kUnit ? pack_bf16x2(x0, x1) : pack_bf16x2(x0 * scale, x1 * scale);
+          if constexpr (kRelu)
+            v = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(i16x2_t, v), i16x2_t{0, 0}));
+          pf[2 * lb + c][q] = v;
+        }
   };
+  constexpr int kTfValu = (kUnit ? 0 : 32) + 16 + (kRelu ? 16 : 0);   // vector instructions of tf
   // GEMM2 of segment sg (B1 fragments from stage sg) into o
   auto g2 = [&](int sg, const u32x4_t (&pf)[4], f32x16_t (&o)[NB]) {
     const uint8_t* st = smem + sg * C::kStage;
@@ -676,12 +684,12 @@ void b2b_mlp_kernel(B2bParams p) {
         g1(j + 1, nxt);
         tf(cur, pf);
         // GEMM1's fragment reads first, then its MFMAs one at a time between
-        // the transform's vector instructions (80 per segment)
+        // the transform's vector instructions
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS * (kB0LK ? 1 : 2), 0);
 #pragma unroll
         for (int i = 0; i < 2 * KS; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 80 / (2 * KS), 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, (kTfValu + 2 * KS - 1) / (2 * KS), 0);
         }
       } else {
         tf(cur, pf);
@@ -1068,12 +1076,19 @@ const void* pick_stream_kn(int K, int N, bool two_blocks) {
   return nullptr;
 }
 
+template <int KS, int NB, bool kUnit, bool kRelu>
+const void* pick_mlp_f(const B2bParams& p) {
+  return p.b0_lk ? (const void*)&b2b_mlp_kernel<KS, NB, true, 4, kUnit, kRelu>
+                 : (const void*)&b2b_mlp_kernel<KS, NB, false, 4, kUnit, kRelu>;
+}
 template <int KS, int NB>
 const void* pick_mlp_kn(const B2bParams& p, int* rows_per_tile, int* threads) {
   if (p.L != TCfg<KS, NB, 1>::kStages * kTLC) return nullptr;
   if (rows_per_tile) *rows_per_tile = 128;
   if (threads) *threads = kTThreads;
-  return p.b0_lk ? (const void*)&b2b_mlp_kernel<KS, NB, true, 4> : (const void*)&b2b_mlp_kernel<KS, NB, false, 4>;
+  const bool unit = p.alpha == 1.0f, relu = p.act == 1;
+  if (unit) return relu ? pick_mlp_f<KS, NB, true, true>(p) : pick_mlp_f<KS, NB, true, false>(p);
+  return relu ? pick_mlp_f<KS, NB, false, true>(p) : pick_mlp_f<KS, NB, false, false>(p);
 }
 const void* pick_mlp(const B2bParams& p, int* rows_per_tile, int* threads) {
   if (p.K == 64 && p.N == 64) return pick_mlp_kn<4, 2>(p, rows_per_tile, threads);

@@ -306,22 +306,23 @@ def test_mlp_resident_weights_several_tiles_per_workgroup(K, N, L, lk):
 
 @pytest.mark.parametrize("M", [1, 37, 129])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_mlp_resident_weights_few_rows_and_strided_output(M, out_dtype):
+@pytest.mark.parametrize("act", ["relu", "none"])
+def test_mlp_resident_weights_few_rows_and_strided_output(M, out_dtype, act):
     # the MLP kernel on one partial tile (and one full tile plus one row),
     # writing O through a row stride of 67 elements, which takes the element
-    # stores instead of the 8- or 16-byte ones
+    # stores instead of the 8- or 16-byte ones; alpha = 1 with and without ReLU
     K, L, N = 64, 256, 64
     dev, ref = mlp_inputs(21, False, M=M, K=K, L=L, N=N)
-    R = oracle.b2bgemm(ref["A"], ref["B0"], ref["B1"], act="relu")
+    R = oracle.b2bgemm(ref["A"], ref["B0"], ref["B1"], act=act)
     buf = torch.full((1, M, 67), float("nan"), dtype=out_dtype, device="cuda")
     O = buf[..., :N]
-    cf.cf_b2bgemm(dev["A"], dev["B0"], dev["B1"], O, act="relu")
+    cf.cf_b2bgemm(dev["A"], dev["B0"], dev["B1"], O, act=act)
     torch.cuda.synchronize()
     assert torch.isnan(buf[..., N:].float()).all(), "a store landed past column N"
     if out_dtype == torch.float32:
         P.assert_close(P.gpu_to_f64(O), R, P.REL_F_BF16, P.MAX_ABS_BF16, f"MLP {M} rows, strided O")
     else:
-        o32 = run(dev["A"], dev["B0"], dev["B1"], torch.float32, b0_is_lk=False, act="relu")
+        o32 = run(dev["A"], dev["B0"], dev["B1"], torch.float32, b0_is_lk=False, act=act)
         P.assert_bf16_consistent(O.contiguous(), o32, R, f"MLP {M} rows, strided bf16 O")
 
 

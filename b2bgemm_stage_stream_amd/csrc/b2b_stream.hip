@@ -1118,9 +1118,12 @@ const void* b2b_stream_pick(const B2bParams& p, int cus, int* rows_per_tile, int
     const void* k = pick_mlp(p, rows_per_tile, threads);
     if (k) return k;
   }
-  // 256-row tiles only when they still give every CU two workgroups (and
-  // not with a bias, whose registers they have no room for)
-  const bool two = !p.bias && p.K == 64 && p.N == 64 && (long)p.batch * ((p.M + 255) / 256) >= 2L * cus;
+  // 256-row tiles only when they still give every CU two workgroups, not
+  // with a bias (whose registers they have no room for), and not with the
+  // causal mask (128-row tiles skip more of the masked work: fewer of their
+  // waves sit out a segment on the diagonal, measured about 4 % faster on the
+  // attention workload)
+  const bool two = !p.bias && !p.causal && p.K == 64 && p.N == 64 && (long)p.batch * ((p.M + 255) / 256) >= 2L * cus;
   const bool sm = p.row_op == 1;
   const void* k;
   if (p.causal)   // keys stored [L, K] (attention); other layouts take the general kernel

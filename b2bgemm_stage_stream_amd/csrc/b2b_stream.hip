@@ -1067,9 +1067,12 @@ void b2b_pp_kernel(B2bParams p) {
 namespace {
 template <bool kSoftmax, bool kB0LK, bool kCausal = false, int kBias = 0>
 const void* pick_stream_kn(int K, int N, bool two_blocks) {
-  if (K == 64 && N == 64)
-    return (two_blocks && kBias == 0) ? (const void*)&b2b_stream_kernel<4, 2, 2, kSoftmax, kB0LK, kCausal>
-                                  : (const void*)&b2b_stream_kernel<4, 2, 1, kSoftmax, kB0LK, kCausal, kBias>;
+  if (K == 64 && N == 64) {
+    // two row blocks per wave: never with a bias or the causal mask
+    if constexpr (kBias == 0 && !kCausal)
+      if (two_blocks) return (const void*)&b2b_stream_kernel<4, 2, 2, kSoftmax, kB0LK, kCausal>;
+    return (const void*)&b2b_stream_kernel<4, 2, 1, kSoftmax, kB0LK, kCausal, kBias>;
+  }
   if (K == 64 && N == 128) return (const void*)&b2b_stream_kernel<4, 4, 1, kSoftmax, kB0LK, kCausal, kBias>;
   if (K == 128 && N == 64) return (const void*)&b2b_stream_kernel<8, 2, 1, kSoftmax, kB0LK, kCausal, kBias>;
   if (K == 128 && N == 128) return (const void*)&b2b_stream_kernel<8, 4, 1, kSoftmax, kB0LK, kCausal, kBias>;

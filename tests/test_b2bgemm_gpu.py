@@ -406,8 +406,9 @@ def test_causal_streamed_widths(K, N):
     check(dev, ref, lk=True, alpha=0.125, row_op="softmax", causal=True, what=f"causal K={K} N={N}")
 
 
-def test_causal_two_row_blocks_and_xcd_heads():
-    # 512 heads: 256-row tiles (two row blocks per wave) and heads grouped by XCD
+def test_causal_many_heads_xcd_grouped():
+    # 512 heads: enough tiles for every CU, heads grouped by XCD (the causal
+    # mask takes 128-row tiles, one row block per wave, at any head count)
     w, dev, ref = P.inputs("c5_b2b_attention", seed=12, batch=512, M=256, L=256)
     check(dev, ref, lk=True, alpha=0.125, row_op="softmax", causal=True, what="causal 512 heads")
 

@@ -1076,6 +1076,14 @@ const void* pick_stream_kn(int K, int N, bool two_blocks) {
   if (K == 64 && N == 128) return (const void*)&b2b_stream_kernel<4, 4, 1, kSoftmax, kB0LK, kCausal, kBias>;
   if (K == 128 && N == 64) return (const void*)&b2b_stream_kernel<8, 2, 1, kSoftmax, kB0LK, kCausal, kBias>;
   if (K == 128 && N == 128) return (const void*)&b2b_stream_kernel<8, 4, 1, kSoftmax, kB0LK, kCausal, kBias>;
+  // the wider GEMM1 (the DLRM widths): A's fragments for all of K stay in
+  // registers (64 or 128 VGPRs a wave, so one wave per SIMD at K = 512) and
+  // the ring holds two segments
+  if (K == 256 && N == 64) return (const void*)&b2b_stream_kernel<16, 2, 1, kSoftmax, kB0LK, kCausal, kBias>;
+  if (K == 256 && N == 128) return (const void*)&b2b_stream_kernel<16, 4, 1, kSoftmax, kB0LK, kCausal, kBias>;
+  if (K == 512 && N == 64) return (const void*)&b2b_stream_kernel<32, 2, 1, kSoftmax, kB0LK, kCausal, kBias>;
+  if constexpr (kBias == 0)   // two 80 KiB stages fill the LDS; no room for a bias block
+    if (K == 512 && N == 128) return (const void*)&b2b_stream_kernel<32, 4, 1, kSoftmax, kB0LK, kCausal, kBias>;
   return nullptr;
 }
 

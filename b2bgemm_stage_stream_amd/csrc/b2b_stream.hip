@@ -1082,6 +1082,10 @@ const void* pick_stream_kn(int K, int N, bool two_blocks) {
   if (K == 256 && N == 64) return (const void*)&b2b_stream_kernel<16, 2, 1, kSoftmax, kB0LK, kCausal, kBias>;
   if (K == 256 && N == 128) return (const void*)&b2b_stream_kernel<16, 4, 1, kSoftmax, kB0LK, kCausal, kBias>;
   if (K == 512 && N == 64) return (const void*)&b2b_stream_kernel<32, 2, 1, kSoftmax, kB0LK, kCausal, kBias>;
+  // N = 256 where two stages fit the LDS (K = 64 keeps the general kernel: its
+  // softmax instantiations spill at two waves per SIMD)
+  if (K == 128 && N == 256) return (const void*)&b2b_stream_kernel<8, 8, 1, kSoftmax, kB0LK, kCausal, kBias>;
+  if (K == 256 && N == 256) return (const void*)&b2b_stream_kernel<16, 8, 1, kSoftmax, kB0LK, kCausal, kBias>;
   if constexpr (kBias == 0)   // two 80 KiB stages fill the LDS; no room for a bias block
     if (K == 512 && N == 128) return (const void*)&b2b_stream_kernel<32, 4, 1, kSoftmax, kB0LK, kCausal, kBias>;
   return nullptr;

@@ -129,10 +129,14 @@ def test_shapes(lk, row_op, act, shape):
 @pytest.mark.parametrize("lk", [False, True])
 @pytest.mark.parametrize("row_op,act", [("none", "relu"), ("softmax", "none")])
 @pytest.mark.parametrize("shape", [(1, 300, 512, 256, 128), (2, 200, 512, 128, 256), (1, 1000, 256, 512, 64),
-                                   (2, 77, 200, 150, 300), (1, 130, 130, 64, 129), (3, 65, 1024, 96, 520)])
+                                   (2, 77, 200, 150, 300), (1, 130, 130, 64, 129), (3, 65, 1024, 96, 520),
+                                   (1, 300, 512, 192, 64), (2, 150, 128, 256, 256), (1, 200, 256, 128, 128),
+                                   (1, 257, 256, 320, 256)])
 def test_wide_k_and_n(lk, row_op, act, shape):
-    # K above 128 (k-blocks of 128) and N above 128 (column blocks of 128),
-    # among them the pages' DLRM bottom-MLP feature widths 512 / 256 / 128,
+    # K above 128 and N above 128, among them the pages' DLRM bottom-MLP
+    # feature widths 512 / 256 / 128: the streamed kernel for K = 256 or 512
+    # with N = 64 or 128 and for K = 128 or 256 with N = 256 (L a multiple of
+    # 64), the general kernel (k-blocks and column blocks of 128) otherwise;
     # ragged K, L, N and rows
     batch, M, K, L, N = shape
     w, dev, ref = P.inputs("c5_b2b_attention", seed=15, batch=batch, M=M, K=K, L=L, N=N)

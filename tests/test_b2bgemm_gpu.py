@@ -404,7 +404,7 @@ def test_causal_streamed(M, L):
         assert torch.all(o[:, : M - L] == 0)
 
 
-@pytest.mark.parametrize("K,N", [(64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("K,N", [(64, 128), (128, 64), (128, 128), (256, 128), (512, 64), (128, 256)])
 def test_causal_streamed_widths(K, N):
     w, dev, ref = P.inputs("c5_b2b_attention", seed=11, batch=2, M=192, L=256, K=K, N=N)
     check(dev, ref, lk=True, alpha=0.125, row_op="softmax", causal=True, what=f"causal K={K} N={N}")

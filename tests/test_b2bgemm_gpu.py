@@ -165,21 +165,24 @@ def test_wide_attention_logsumexp_and_bias(causal):
     P.assert_close(P.gpu_to_f64(lse), Rl, 1e-5, 1e-4, "head dim 256 log-sum-exp")
 
 
-def test_wide_mlp_with_bias_dlrm_widths():
-    # bottom-MLP layer pair 512 -> 256 -> 128 with a bias and ReLU between.
+@pytest.mark.parametrize("K,N", [(512, 128), (512, 64), (256, 128), (256, 256)])
+def test_wide_mlp_with_bias_dlrm_widths(K, N):
+    # bottom-MLP layer pairs K -> 256 -> N with a bias and ReLU between (512 ->
+    # 256 -> 128 the pages' widths; K = 512 with N = 128 takes the general
+    # kernel, the others the streamed one with its bias block).
     # The MLP workload's W0 ~ N(0, 1/8) is scaled for K = 64; alpha = 1/sqrt(8)
-    # keeps S of the same order at K = 512. (S itself is accumulated in fp32
+    # (sqrt(K / 64) in general) keeps S of the same order at K = 512. (S itself is accumulated in fp32
     # and rounded to bf16 for the second GEMM, as the oracle mirrors; where an
     # fp32 S lies within its rounding error of a bf16 rounding boundary the
     # two roundings pick neighbouring values, and one bf16 step of S grows
     # with |S|, so an unscaled S of order 8 would spend the max-abs bar on such
     # ties alone.)
-    batch, M, K, L, N = 1, 4096, 512, 256, 128
+    batch, M, L = 1, 4096, 256
     w, dev, ref = P.inputs("c4_b2b_mlp_relu", seed=17, batch=batch, M=M, K=K, L=L, N=N)
     rng = np.random.default_rng(17)
     bias = torch.from_numpy(rng.normal(0.0, 0.5, L)).to(torch.bfloat16).cuda()
-    check(dev, ref, lk=False, alpha=float(np.float32(1 / np.sqrt(8))), act="relu", bias=bias,
-          bias_ref=P.gpu_to_f64(bias), what="DLRM 512-256-128 + bias")
+    check(dev, ref, lk=False, alpha=float(np.float32(1 / np.sqrt(K / 64))), act="relu", bias=bias,
+          bias_ref=P.gpu_to_f64(bias), what=f"DLRM {K}-256-{N} + bias")
 
 
 @pytest.mark.parametrize("lk", [False, True])
